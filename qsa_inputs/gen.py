@@ -1,0 +1,117 @@
+"""Host (numpy) implementation of the counter-based input generator.
+
+See the package docstring for the definition. Nothing here knows about
+attention, pooling or selection.
+"""
+from __future__ import annotations
+
+import statistics
+
+import numpy as np
+
+G = 0x9E3779B97F4A7C15  # SplitMix64 increment (golden-ratio constant)
+H = 0xD1B54A32D192ED03  # odd multiplier used only to spread stream ids
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+_MASK = (1 << 64) - 1
+
+# Tensor kinds, used to derive independent streams per (layer, sequence).
+KIND = {
+    "q": 1, "q_idx": 2, "k": 3, "v": 4, "raw_key": 5, "w_idx": 6,
+    "latent": 7, "scores": 8, "misc": 9,
+}
+
+
+def mix64(z: np.ndarray) -> np.ndarray:
+    """SplitMix64 output function on a uint64 array (wrapping arithmetic)."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        z = z ^ (z >> np.uint64(31))
+    return z
+
+
+def _mix64_int(z: int) -> int:
+    z &= _MASK
+    z = ((z ^ (z >> 30)) * 0xBF58476D1CE4E5B9) & _MASK
+    z = ((z ^ (z >> 27)) * 0x94D049BB133111EB) & _MASK
+    return z ^ (z >> 31)
+
+
+def stream_key(seed: int, stream: int) -> int:
+    return _mix64_int(((seed * G) & _MASK) ^ ((stream * H) & _MASK))
+
+
+def config_seed(config_id: int) -> int:
+    """Fixed seed per workload: 0x51A5EED0 + workload number."""
+    return 0x51A5EED0 + int(config_id)
+
+
+def stream_id(layer: int, seq: int, kind: str, salt: int = 0) -> int:
+    """Stream number of one tensor of one (layer, sequence) unit."""
+    return ((((int(salt) * 256 + int(layer)) * 65536 + int(seq)) * 16) + KIND[kind]) & _MASK
+
+
+def words(seed: int, stream: int, word_index: np.ndarray) -> np.ndarray:
+    """The SplitMix64 outputs with the given indices (0-based) of one stream."""
+    key = np.uint64(stream_key(seed, stream))
+    wi = np.asarray(word_index, dtype=np.uint64)
+    with np.errstate(over="ignore"):
+        return mix64(key + (wi + np.uint64(1)) * np.uint64(G))
+
+
+def codes(seed: int, stream: int, index: np.ndarray) -> np.ndarray:
+    """16-bit codes of the given element indices of one stream."""
+    idx = np.asarray(index, dtype=np.uint64)
+    u = words(seed, stream, idx >> np.uint64(2))
+    shift = np.uint64(48) - np.uint64(16) * (idx & np.uint64(3))
+    return ((u >> shift) & np.uint64(0xFFFF)).astype(np.uint16)
+
+
+def _f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    u = np.asarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    u = u + np.uint64(0x7FFF) + ((u >> np.uint64(16)) & np.uint64(1))
+    return (u >> np.uint64(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+_TABLE = None
+
+
+def normal_table() -> np.ndarray:
+    """65536 bf16 bit patterns: N(0,1) quantiles at (c + 0.5) / 65536."""
+    global _TABLE
+    if _TABLE is None:
+        nd = statistics.NormalDist()
+        q = np.array([nd.inv_cdf((c + 0.5) / 65536.0) for c in range(65536)], dtype=np.float64)
+        _TABLE = _f32_to_bf16_bits(q.astype(np.float32))
+        _TABLE.setflags(write=False)
+    return _TABLE
+
+
+def normal_bf16(seed: int, stream: int, start: int, count: int = None, index=None) -> np.ndarray:
+    """bf16 bit patterns of elements [start, start+count) (or the given indices)."""
+    if index is None:
+        index = np.arange(start, start + count, dtype=np.uint64)
+    return normal_table()[codes(seed, stream, index)]
+
+
+def uniform_f32(seed: int, stream: int, count: int, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
+    """fp32 values on a 2**-24 grid of [lo, hi) (exactly representable)."""
+    u = words(seed, stream, np.arange(count, dtype=np.uint64))
+    frac = (u >> np.uint64(40)).astype(np.float64) / float(1 << 24)
+    return (lo + (hi - lo) * frac).astype(np.float32)
+
+
+def tie_heavy_f32(seed: int, stream: int, count: int, levels: int = 64) -> np.ndarray:
+    """fp32 values drawn from a few levels (many exact ties, includes -0.0 and +0.0)."""
+    u = words(seed, stream, np.arange(count, dtype=np.uint64))
+    lev = (u >> np.uint64(40)).astype(np.int64) % levels - levels // 2
+    out = (lev.astype(np.float32) * np.float32(0.25))
+    neg0 = ((u >> np.uint64(8)) & np.uint64(7)) == 0
+    out[(lev == 0) & neg0] = np.float32(-0.0)
+    return out
