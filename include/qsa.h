@@ -1,0 +1,238 @@
+/*
+ * qsa.h -- C ABI of libqsa: indexer-selected sparse attention over pooled
+ * block keys, hand-written HIP for gfx950 (one GPU).
+ *
+ * The method (described in prose on the pages cited below; no formulas are
+ * printed there):
+ *   - every history block of `block` tokens has one pooled indexer key;
+ *   - each query scores every complete block with its indexer query, keeps
+ *     the `topk` best blocks plus the trailing tokens of the incomplete last
+ *     block (all tokens when there are at most `topk` complete blocks);
+ *   - it gathers only those K/V rows and runs softmax attention over them;
+ *   - prefill walks history tiles in the outer loop and merges the partial
+ *     softmax results by log-sum-exp.
+ * Sources: "3090x3で 314 万コンテキスト" (sections "なぜ", "カーネルを書き換え
+ * ずに済む", "VRAM に残す必要があるもの", "ちなみにこの欠点"); "GLM-5.3 最適化
+ * 第2部：16基のH200上でのPCP、DCP、およびHybrid HiSparse" (sections "PCP",
+ * "DCP", footnote 1); "125B MoE を 3090 3 枚で運用する vLLM 最適化編"
+ * (section 3.3, ties in top-k go to the smaller id).
+ *
+ * Conventions for every entry point:
+ *   - Pointers marked (device) are device memory owned by the caller; the
+ *     library never allocates, frees or keeps them. Pointers marked (host)
+ *     are read before the call returns.
+ *   - Each call validates its arguments on the host, then enqueues its
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream) and returns
+ *     without synchronising. Nothing is launched when validation fails.
+ *   - bf16 arrays are raw bit patterns (uint16) and must be 16-byte aligned;
+ *     fp32 / int32 arrays must be 16-byte aligned as well.
+ *   - Per-query context lengths `q_ctx` live in device memory (so a captured
+ *     graph can be replayed as positions advance); `max_ctx` is a host-side
+ *     upper bound used to size launches and validate buffers. A q_ctx entry
+ *     outside [0, max_ctx] is a caller error: kernels clamp it into range
+ *     (so no access leaves the buffers) and the results for that query are
+ *     unspecified. Setting QSA_VALIDATE=1 in the environment makes each call
+ *     copy q_ctx / q_seq back and return QSA_ERR_ARG instead (synchronising).
+ *   - Setting QSA_SYNC_CHECK=1 makes each call synchronise its stream and
+ *     return QSA_ERR_LAUNCH if a kernel failed.
+ *   - Results are bit-identical from run to run (no floating-point atomics).
+ *   - Calls keep no global mutable state and may be issued from several
+ *     threads on different streams.
+ */
+#ifndef QSA_H
+#define QSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t qsa_bf16;      /* bf16 bit pattern */
+typedef void*    qsa_stream_t;  /* hipStream_t */
+
+typedef enum {
+  QSA_OK = 0,
+  QSA_ERR_ARG = 1,          /* null or misaligned pointer, negative size, short stride */
+  QSA_ERR_UNSUPPORTED = 2,  /* well-formed but outside the compiled shapes */
+  QSA_ERR_WORKSPACE = 3,    /* workspace smaller than the matching *_workspace_bytes() */
+  QSA_ERR_LAUNCH = 4,       /* a kernel launch (or, with QSA_SYNC_CHECK=1, a kernel) failed */
+  QSA_ERR_DEVICE = 5        /* no usable gfx950 device */
+} qsa_status;
+
+/* Indexer / selection parameters.
+ *   variant A (pooled block keys):   block 4, topk 512,  idx_dim 128, idx_heads 1
+ *   variant B (token keys, MLA-like): block 1, topk 2048, idx_dim 64,  idx_heads 4
+ * Supported: block in {1, 4}; 1 <= topk <= 2048; (idx_dim, idx_heads) in
+ * {(128, 1), (64, 4)}. */
+typedef struct {
+  int32_t block;
+  int32_t topk;
+  int32_t idx_dim;
+  int32_t idx_heads;
+} qsa_sel_cfg;
+
+/* Attention shape. Query head h reads kv head h / (hq / hkv).
+ * Supported: (hq, hkv, dk, dv) = (16, 2, 256, 256) [variant A] and
+ * (64, 1, 576, 512) [variant B, V = first dv columns of the K row]. */
+typedef struct {
+  int32_t hq;
+  int32_t hkv;
+  int32_t dk;
+  int32_t dv;
+  float scale;   /* softmax scale applied to q.k (1/16 for dk = 256) */
+} qsa_attn_cfg;
+
+/* K/V cache of one layer for several sequences (device).
+ * Element d of the K row of (sequence s, token t, kv head g) is
+ *   k[s * seq_stride + t * tok_stride + g * head_stride + d]
+ * and likewise for v (v may equal k: the MLA latent row serves as both).
+ * Strides are in elements and must be multiples of 8; `capacity` is the
+ * number of token rows each sequence holds (every query needs
+ * q_ctx <= capacity). The pages' gather kernel uses
+ * [token][kv_head][head_dim] ("カーネルを書き換えずに済む"): tok_stride =
+ * hkv * dk, head_stride = dk. */
+typedef struct {
+  const qsa_bf16* k;
+  const qsa_bf16* v;
+  int64_t seq_stride;
+  int64_t tok_stride;
+  int64_t head_stride;
+  int64_t capacity;
+} qsa_kv;
+
+/* ---------------------------------------------------------------- A1 ----
+ * qsa_pool_keys: pooled indexer keys for the complete blocks of tokens
+ * [tok_begin, tok_end) of n_seq sequences.
+ *   pooled[s][b][d] = bf16_rne( mean_{j < block} raw[s][block*b + j][d] )
+ * i.e. the exact mean rounded once to bf16 (nearest, ties to even); exact
+ * whenever the block's nonzero values lie within a factor 2^44 of each
+ * other. ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの": one
+ * pooled key of 128 bf16 per block; the mean is the workload's definition.)
+ *   raw    (device) bf16 [n_seq][raw_seq_stride]: token t of sequence s at
+ *          raw + s*raw_seq_stride + t*dim.
+ *   pooled (device) bf16 [n_seq][pooled_seq_stride]: block b at
+ *          pooled + s*pooled_seq_stride + b*dim.
+ *   tok_begin must be a multiple of block; blocks b in
+ *   [tok_begin/block, tok_end/block) are written, nothing else.
+ *   dim must be a multiple of 8, at most 1024. */
+qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride,
+                         qsa_bf16* pooled, int64_t pooled_seq_stride,
+                         int32_t n_seq, int64_t tok_begin, int64_t tok_end,
+                         int32_t dim, int32_t block, qsa_stream_t stream);
+
+/* ---------------------------------------------------------------- A2 ----
+ * qsa_index_scores: indexer scores of every candidate block for nq queries.
+ * Query i reads the keys of sequence q_seq[i] and has n_i = q_ctx[i] / block
+ * candidates; for b < n_i:
+ *   variant A (idx_heads 1): scores[i][b] = q_idx[i] . keys[b]
+ *   variant B (idx_heads H): scores[i][b] = sum_h w_idx[i][h] * max(0, q_idx[i][h] . keys[b])
+ * accumulated in fp32. Entries b >= n_i are not written.
+ * ("VRAM に残す必要があるもの": every pooled key is scored at every step;
+ * "GLM-5.3 ...", "PCP": a token-level indexer scores all earlier tokens.)
+ *   q_seq  (device) int32 [nq], or NULL: every query reads sequence 0
+ *          (a prefill chunk; enables the MFMA query-tile path).
+ *   q_ctx  (device) int32 [nq] visible tokens per query (its own included).
+ *   q_idx  (device) bf16 [nq][idx_heads][idx_dim].
+ *   w_idx  (device) fp32 [nq][idx_heads]; NULL when idx_heads == 1.
+ *   keys   (device) bf16: key b of sequence s at keys + s*keys_seq_stride + b*idx_dim
+ *          (pooled block keys for block 4, per-token keys for block 1).
+ *   scores (device) fp32 [nq][ld_scores], ld_scores >= max_ctx / block. */
+qsa_status qsa_index_scores(const qsa_sel_cfg* cfg, int32_t nq,
+                            const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                            const qsa_bf16* q_idx, const float* w_idx,
+                            const qsa_bf16* keys, int64_t keys_seq_stride,
+                            float* scores, int64_t ld_scores, qsa_stream_t stream);
+
+/* ---------------------------------------------------------------- A3 ----
+ * qsa_topk_blocks: the blocks each query attends.
+ * With n_i = q_ctx[i] / block candidates: if n_i <= topk every block is
+ * selected; otherwise the topk blocks ranked first by (score descending,
+ * block index ascending), -0.0 ranking equal to +0.0. Scores must be finite.
+ * ("3090x3で 314 万コンテキスト", "なぜ": fixed budget, full history below
+ * 4*topk + 3 tokens; "125B MoE ...", 3.3: equal values go to the smaller id.)
+ *   sel   (device) int32 [nq][topk]: row i holds n_sel[i] ascending block
+ *         indices, then -1 up to topk.
+ *   n_sel (device) int32 [nq] = min(n_i, topk).
+ *   ws    (device) workspace of at least qsa_topk_workspace_bytes(cfg, nq,
+ *         max_ctx) bytes, contents ignored on entry (may be NULL if that is 0). */
+qsa_status qsa_topk_blocks(const qsa_sel_cfg* cfg, int32_t nq,
+                           const int32_t* q_ctx, int32_t max_ctx,
+                           const float* scores, int64_t ld_scores,
+                           int32_t* sel, int32_t* n_sel,
+                           void* ws, size_t ws_bytes, qsa_stream_t stream);
+
+size_t qsa_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx);
+
+/* ---------------------------------------------------------------- A4 ----
+ * qsa_sparse_decode: softmax attention of each query over its selected
+ * tokens, split into n_split partial results.
+ * The token list of query i is, in ascending order: the `block` tokens of
+ * each selected block sel[i][0..n_sel[i]), then the trailing tokens
+ * [block * (q_ctx[i]/block), q_ctx[i]). Split j covers list positions
+ * [j*L/n_split, (j+1)*L/n_split) with L the list length. For head h, kv
+ * head g = h / (hq/hkv):
+ *   z_t = scale * q[i][h] . k[t][g],  lse = ln sum_t exp(z_t),
+ *   O   = sum_t exp(z_t - lse) v[t][g][0..dv)
+ * An empty split gives O = 0, lse = -inf. ("なぜ": only the selected K/V
+ * rows are read; "カーネルを書き換えずに済む": rows addressed per token and
+ * kv head.)
+ *   q        (device) bf16 [nq][hq][dk].
+ *   o_part   (device) fp32 [n_split][nq][hq][dv];
+ *   lse_part (device) fp32 [n_split][nq][hq] (natural log).
+ *   1 <= n_split <= 256. Combine the splits with qsa_lse_merge. */
+qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
+                             int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
+                             int32_t max_ctx, const qsa_bf16* q, const qsa_kv* kv,
+                             const int32_t* sel, const int32_t* n_sel, int32_t n_split,
+                             float* o_part, float* lse_part, qsa_stream_t stream);
+
+/* ---------------------------------------------------------------- A6 ----
+ * qsa_sparse_prefill: the same attention restricted to one history tile:
+ * query i attends the tokens of its list that lie in [tile_begin, tile_end)
+ * and writes one partial (O, lse); a query with no token in the tile gets
+ * O = 0, lse = -inf. Partials of consecutive tiles merged with
+ * qsa_lse_merge equal the untiled result (up to rounding).
+ * ("3090x3で 314 万コンテキスト", "ちなみにこの欠点": history in fixed tiles in
+ * the outer loop, all queries computed per tile, partial softmax results
+ * merged across tiles.)
+ *   q_seq may be NULL (all queries in sequence 0).
+ *   tile_begin must be a multiple of block and 0 <= tile_begin <= tile_end.
+ *   o_part (device) fp32 [nq][hq][dv]; lse_part (device) fp32 [nq][hq]. */
+qsa_status qsa_sparse_prefill(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
+                              int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
+                              int32_t max_ctx, const qsa_bf16* q, const qsa_kv* kv,
+                              const int32_t* sel, const int32_t* n_sel,
+                              int64_t tile_begin, int64_t tile_end,
+                              float* o_part, float* lse_part, qsa_stream_t stream);
+
+/* ---------------------------------------------------------------- A5 ----
+ * qsa_lse_merge: combine n_part partial softmax results per row.
+ *   lse = M + ln sum_p exp(lse_p - M), M = max_p lse_p;
+ *   O   = sum_p exp(lse_p - lse) O_p; partials with lse_p = -inf add nothing;
+ *   rows whose partials are all empty get O = 0, lse = -inf.
+ * ("GLM-5.3 ...", "DCP": partial attention combined by log-sum-exp.)
+ *   o_parts   (device) fp32: partial p, row r at o_parts + p*o_part_stride + r*dv.
+ *   lse_parts (device) fp32: lse_parts + p*lse_part_stride + r.
+ *   o_out (device, fp32 [rows][dv]), o_out_bf16 (device, bf16 [rows][dv],
+ *   nearest-even of the fp32 value) and lse_out (device, fp32 [rows]) may
+ *   each be NULL. 1 <= n_part <= 4096; dv a multiple of 4, at most 1024. */
+qsa_status qsa_lse_merge(int32_t n_part, int64_t rows, int32_t dv,
+                         const float* o_parts, int64_t o_part_stride,
+                         const float* lse_parts, int64_t lse_part_stride,
+                         float* o_out, qsa_bf16* o_out_bf16, float* lse_out,
+                         qsa_stream_t stream);
+
+/* ------------------------------------------------------------- misc ---- */
+const char* qsa_status_string(qsa_status s);
+/* Message of the last failed call on this thread ("" if none). */
+const char* qsa_last_error(void);
+/* Library version: major * 10000 + minor * 100 + patch. */
+int32_t qsa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QSA_H */

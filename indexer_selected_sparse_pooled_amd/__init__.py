@@ -1,0 +1,12 @@
+"""Indexer-selected sparse attention over pooled block keys, MI355X (gfx950).
+
+The computation lives in libqsa.so (hand-written HIP, C ABI in
+include/qsa.h); ``qsa`` is its thin binding and ``pipeline`` chains the
+calls into a decode layer and a tiled prefill chunk.
+"""
+from . import qsa  # noqa: F401
+from .qsa import (  # noqa: F401
+    ATTN_A, ATTN_B, SEL_A, SEL_B, AttnCfg, QsaError, SelCfg, make_kv, qsa_index_scores,
+    qsa_lse_merge, qsa_pool_keys, qsa_sparse_decode, qsa_sparse_prefill, qsa_topk_blocks,
+    qsa_topk_workspace_bytes, qsa_version, topk_workspace,
+)

@@ -1,0 +1,332 @@
+// C ABI of libqsa (declared in include/qsa.h): argument validation on the
+// host, then kernel launches on the caller's stream. No entry point
+// allocates memory or synchronises unless QSA_VALIDATE / QSA_SYNC_CHECK ask.
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <vector>
+
+#include "../../include/qsa.h"
+#include "kernels.hpp"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+qsa_status fail(qsa_status s, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+  return s;
+}
+
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Per-device record of the architecture check: 0 unknown, 1 gfx950, 2 other.
+std::atomic<int> g_arch_ok[64];
+
+qsa_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_DEVICE, "no HIP device");
+  if (dev < 0 || dev >= 64) return fail(QSA_ERR_DEVICE, "device index %d out of range", dev);
+  int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+  if (st == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return fail(QSA_ERR_DEVICE, "hipGetDeviceProperties failed");
+    st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+    g_arch_ok[dev].store(st, std::memory_order_relaxed);
+  }
+  if (st != 1) return fail(QSA_ERR_DEVICE, "device %d is not gfx950", dev);
+  return QSA_OK;
+}
+
+qsa_status finish(hipError_t e, hipStream_t s, const char* what) {
+  if (e != hipSuccess) return fail(QSA_ERR_LAUNCH, "%s: launch failed: %s", what, hipGetErrorString(e));
+  if (env_on("QSA_SYNC_CHECK")) {
+    hipError_t e2 = hipStreamSynchronize(s);
+    if (e2 == hipSuccess) e2 = hipGetLastError();
+    if (e2 != hipSuccess) return fail(QSA_ERR_LAUNCH, "%s: kernel failed: %s", what, hipGetErrorString(e2));
+  }
+  g_err[0] = 0;
+  return QSA_OK;
+}
+
+// Optional synchronous check of the device-side per-query arrays.
+qsa_status validate_queries(int nq, const int32_t* q_seq, const int32_t* q_ctx, int max_ctx, hipStream_t s) {
+  if (!env_on("QSA_VALIDATE") || nq <= 0) return QSA_OK;
+  std::vector<int32_t> h(nq);
+  if (hipMemcpyAsync(h.data(), q_ctx, sizeof(int32_t) * nq, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return fail(QSA_ERR_ARG, "QSA_VALIDATE: cannot read q_ctx");
+  for (int i = 0; i < nq; i++)
+    if (h[i] < 0 || h[i] > max_ctx) return fail(QSA_ERR_ARG, "q_ctx[%d] = %d outside [0, max_ctx = %d]", i, h[i], max_ctx);
+  if (q_seq) {
+    if (hipMemcpyAsync(h.data(), q_seq, sizeof(int32_t) * nq, hipMemcpyDeviceToHost, s) != hipSuccess ||
+        hipStreamSynchronize(s) != hipSuccess)
+      return fail(QSA_ERR_ARG, "QSA_VALIDATE: cannot read q_seq");
+    for (int i = 0; i < nq; i++)
+      if (h[i] < 0) return fail(QSA_ERR_ARG, "q_seq[%d] = %d is negative", i, h[i]);
+  }
+  return QSA_OK;
+}
+
+qsa_status check_sel_cfg(const qsa_sel_cfg* c) {
+  if (!c) return fail(QSA_ERR_ARG, "sel_cfg is NULL");
+  if (c->block != 1 && c->block != 4) return fail(QSA_ERR_UNSUPPORTED, "block %d not in {1, 4}", c->block);
+  if (c->topk < 1 || c->topk > 2048) return fail(QSA_ERR_UNSUPPORTED, "topk %d not in [1, 2048]", c->topk);
+  const bool a = c->idx_dim == 128 && c->idx_heads == 1;
+  const bool b = c->idx_dim == 64 && c->idx_heads == 4;
+  if (!a && !b) return fail(QSA_ERR_UNSUPPORTED, "(idx_dim, idx_heads) = (%d, %d) not supported", c->idx_dim, c->idx_heads);
+  return QSA_OK;
+}
+
+qsa_status check_attn(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, const int32_t* q_ctx, int max_ctx,
+                      const qsa_bf16* q, const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel,
+                      const float* o_part, const float* lse_part) {
+  qsa_status st = check_sel_cfg(sc);
+  if (st != QSA_OK) return st;
+  if (!ac) return fail(QSA_ERR_ARG, "attn_cfg is NULL");
+  if (!kv) return fail(QSA_ERR_ARG, "kv is NULL");
+  if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
+  if (ac->hq <= 0 || ac->hkv <= 0 || ac->hq % ac->hkv != 0) return fail(QSA_ERR_ARG, "hq %% hkv != 0");
+  if (!(ac->hq == 16 && ac->hkv == 2 && ac->dk == 256 && ac->dv == 256))
+    return fail(QSA_ERR_UNSUPPORTED, "attention shape (hq %d, hkv %d, dk %d, dv %d) not compiled", ac->hq, ac->hkv,
+                ac->dk, ac->dv);
+  if (!(ac->scale > 0.f) || !(ac->scale < 1e30f)) return fail(QSA_ERR_ARG, "scale must be positive and finite");
+  if (nq == 0) return QSA_OK;
+  if (!q_ctx || !q || !kv->k || !kv->v || !sel || !n_sel || !o_part || !lse_part)
+    return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o_part) || !aligned16(sel))
+    return fail(QSA_ERR_ARG, "q, k, v, sel and o_part must be 16-byte aligned");
+  if (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 || kv->head_stride < 0 ||
+      kv->seq_stride < 0)
+    return fail(QSA_ERR_ARG, "kv strides must be non-negative multiples of 8");
+  if (int64_t(ac->hkv - 1) * kv->head_stride + ac->dk > kv->tok_stride)
+    return fail(QSA_ERR_ARG, "tok_stride too small for hkv heads of dk");
+  if (kv->capacity < max_ctx) return fail(QSA_ERR_ARG, "kv capacity %lld < max_ctx %d", (long long)kv->capacity, max_ctx);
+  return QSA_OK;
+}
+
+qsa::AttendArgs attend_args(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, const int32_t* q_seq,
+                            const int32_t* q_ctx, int max_ctx, const qsa_bf16* q, const qsa_kv* kv,
+                            const int32_t* sel, const int32_t* n_sel, int n_split, int64_t t0, int64_t t1,
+                            float* o_part, float* lse_part) {
+  qsa::AttendArgs a{};
+  a.q_seq = q_seq;
+  a.q_ctx = q_ctx;
+  a.max_ctx = max_ctx;
+  a.nq = nq;
+  a.hq = ac->hq;
+  a.hkv = ac->hkv;
+  a.dk = ac->dk;
+  a.dv = ac->dv;
+  a.scale = ac->scale;
+  a.q = q;
+  a.k = kv->k;
+  a.v = kv->v;
+  a.seq_stride = kv->seq_stride;
+  a.tok_stride = kv->tok_stride;
+  a.head_stride = kv->head_stride;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.topk = sc->topk;
+  a.block = sc->block;
+  a.n_split = n_split;
+  a.tile_begin = t0;
+  a.tile_end = t1;
+  a.o_part = o_part;
+  a.lse_part = lse_part;
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride, qsa_bf16* pooled, int64_t pooled_seq_stride,
+                         int32_t n_seq, int64_t tok_begin, int64_t tok_end, int32_t dim, int32_t block,
+                         qsa_stream_t stream) {
+  if (block != 1 && block != 4) return fail(QSA_ERR_UNSUPPORTED, "block %d not in {1, 4}", block);
+  if (dim < 8 || dim > 1024 || dim % 8) return fail(QSA_ERR_UNSUPPORTED, "dim %d must be a multiple of 8 in [8, 1024]", dim);
+  if (n_seq < 0 || tok_begin < 0 || tok_end < tok_begin) return fail(QSA_ERR_ARG, "bad n_seq or token range");
+  if (tok_begin % block) return fail(QSA_ERR_ARG, "tok_begin must be a multiple of block");
+  const int64_t b0 = tok_begin / block, b1 = tok_end / block;
+  if (n_seq == 0 || b1 <= b0) return QSA_OK;
+  if (!raw || !pooled) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(raw) || !aligned16(pooled)) return fail(QSA_ERR_ARG, "raw and pooled must be 16-byte aligned");
+  if (raw_seq_stride % 8 || pooled_seq_stride % 8) return fail(QSA_ERR_ARG, "strides must be multiples of 8");
+  if (n_seq > 1 && (raw_seq_stride < b1 * block * dim || pooled_seq_stride < b1 * dim))
+    return fail(QSA_ERR_ARG, "sequence strides too small");
+  if (n_seq > 65535) return fail(QSA_ERR_UNSUPPORTED, "n_seq > 65535");
+  qsa_status st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(qsa::launch_pool(raw, raw_seq_stride, pooled, pooled_seq_stride, n_seq, b0, b1 - b0, dim, block, s), s,
+                "qsa_pool_keys");
+}
+
+qsa_status qsa_index_scores(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
+                            int32_t max_ctx, const qsa_bf16* q_idx, const float* w_idx, const qsa_bf16* keys,
+                            int64_t keys_seq_stride, float* scores, int64_t ld_scores, qsa_stream_t stream) {
+  qsa_status st = check_sel_cfg(cfg);
+  if (st != QSA_OK) return st;
+  if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
+  if (nq == 0) return QSA_OK;
+  if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
+  if (!q_ctx || !q_idx || !keys || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (cfg->idx_heads > 1 && !w_idx) return fail(QSA_ERR_ARG, "w_idx required when idx_heads > 1");
+  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx, keys and scores must be 16-byte aligned");
+  const int64_t nmax = int64_t(max_ctx) / cfg->block;
+  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / block = %lld", (long long)ld_scores, (long long)nmax);
+  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
+  if (q_seq && keys_seq_stride < nmax * cfg->idx_dim) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / block keys");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::ScoreArgs a{};
+  a.q_seq = q_seq;
+  a.q_ctx = q_ctx;
+  a.max_ctx = max_ctx;
+  a.nq = nq;
+  a.block = cfg->block;
+  a.idx_dim = cfg->idx_dim;
+  a.idx_heads = cfg->idx_heads;
+  a.q_idx = q_idx;
+  a.w_idx = w_idx;
+  a.keys = keys;
+  a.keys_ss = keys_seq_stride;
+  a.scores = scores;
+  a.ld = ld_scores;
+  return finish(qsa::launch_scores(a, s), s, "qsa_index_scores");
+}
+
+size_t qsa_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx) {
+  if (!cfg || cfg->block <= 0 || cfg->topk <= 0 || nq <= 0 || max_ctx <= 0) return 0;
+  return qsa::plan_topk(nq, max_ctx, cfg->block, cfg->topk).ws_bytes;
+}
+
+qsa_status qsa_topk_blocks(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_ctx, int32_t max_ctx,
+                           const float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, void* ws,
+                           size_t ws_bytes, qsa_stream_t stream) {
+  qsa_status st = check_sel_cfg(cfg);
+  if (st != QSA_OK) return st;
+  if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
+  if (nq == 0) return QSA_OK;
+  if (nq > 1000000) return fail(QSA_ERR_UNSUPPORTED, "nq too large");
+  if (!q_ctx || !scores || !sel || !n_sel) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(scores) || !aligned16(sel)) return fail(QSA_ERR_ARG, "scores and sel must be 16-byte aligned");
+  const int64_t nmax = int64_t(max_ctx) / cfg->block;
+  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores < max_ctx / block");
+  if (nmax > 8388608) return fail(QSA_ERR_UNSUPPORTED, "more than 8388608 candidates per query");
+  const qsa::TopkPlan plan = qsa::plan_topk(nq, max_ctx, cfg->block, cfg->topk);
+  if (plan.chunked && nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535 with more than 32768 candidates");
+  if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+  if (ws && !aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, nullptr, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::TopkArgs a{};
+  a.q_ctx = q_ctx;
+  a.max_ctx = max_ctx;
+  a.nq = nq;
+  a.block = cfg->block;
+  a.topk = cfg->topk;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.sel = sel;
+  a.n_sel = n_sel;
+  a.ws = ws;
+  return finish(qsa::launch_topk(a, plan, s), s, "qsa_topk_blocks");
+}
+
+qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q,
+                             const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel, int32_t n_split,
+                             float* o_part, float* lse_part, qsa_stream_t stream) {
+  qsa_status st = check_attn(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel, o_part, lse_part);
+  if (st != QSA_OK) return st;
+  if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
+  if (nq == 0) return QSA_OK;
+  if (int64_t(nq) * n_split > 0x7FFFFFFF) return fail(QSA_ERR_UNSUPPORTED, "nq * n_split too large");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  const qsa::AttendArgs a = attend_args(sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q, kv, sel, n_sel, n_split, 0,
+                                        int64_t(max_ctx), o_part, lse_part);
+  return finish(qsa::launch_attend(a, s), s, "qsa_sparse_decode");
+}
+
+qsa_status qsa_sparse_prefill(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                              const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q,
+                              const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel, int64_t tile_begin,
+                              int64_t tile_end, float* o_part, float* lse_part, qsa_stream_t stream) {
+  qsa_status st = check_attn(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel, o_part, lse_part);
+  if (st != QSA_OK) return st;
+  if (tile_begin < 0 || tile_end < tile_begin) return fail(QSA_ERR_ARG, "bad tile range");
+  if (tile_begin % sel_cfg->block) return fail(QSA_ERR_ARG, "tile_begin must be a multiple of block");
+  if (tile_end % sel_cfg->block && tile_end < max_ctx)
+    return fail(QSA_ERR_ARG, "tile_end must be a multiple of block (or >= max_ctx)");
+  if (nq == 0) return QSA_OK;
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  const qsa::AttendArgs a = attend_args(sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q, kv, sel, n_sel, 1,
+                                        tile_begin, tile_end, o_part, lse_part);
+  return finish(qsa::launch_attend(a, s), s, "qsa_sparse_prefill");
+}
+
+qsa_status qsa_lse_merge(int32_t n_part, int64_t rows, int32_t dv, const float* o_parts, int64_t o_part_stride,
+                         const float* lse_parts, int64_t lse_part_stride, float* o_out, qsa_bf16* o_out_bf16,
+                         float* lse_out, qsa_stream_t stream) {
+  if (n_part < 1 || n_part > 4096) return fail(QSA_ERR_ARG, "n_part %d not in [1, 4096]", n_part);
+  if (rows < 0) return fail(QSA_ERR_ARG, "negative rows");
+  if (dv < 4 || dv > 1024 || dv % 4) return fail(QSA_ERR_UNSUPPORTED, "dv %d must be a multiple of 4 in [4, 1024]", dv);
+  if (rows == 0) return QSA_OK;
+  if (!o_parts || !lse_parts) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(o_parts) || (o_out && !aligned16(o_out)) || (o_out_bf16 && !aligned16(o_out_bf16)))
+    return fail(QSA_ERR_ARG, "o_parts, o_out and o_out_bf16 must be 16-byte aligned");
+  if (n_part > 1 && (o_part_stride < rows * dv || lse_part_stride < rows || o_part_stride % 4))
+    return fail(QSA_ERR_ARG, "partial strides too small");
+  if (rows > int64_t(0x7FFFFFFF) * 4) return fail(QSA_ERR_UNSUPPORTED, "too many rows");
+  qsa_status st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(qsa::launch_merge(n_part, rows, dv, o_parts, o_part_stride, lse_parts, lse_part_stride, o_out,
+                                  o_out_bf16, lse_out, s),
+                s, "qsa_lse_merge");
+}
+
+const char* qsa_status_string(qsa_status s) {
+  switch (s) {
+    case QSA_OK: return "ok";
+    case QSA_ERR_ARG: return "invalid argument";
+    case QSA_ERR_UNSUPPORTED: return "unsupported shape";
+    case QSA_ERR_WORKSPACE: return "workspace too small";
+    case QSA_ERR_LAUNCH: return "launch failed";
+    case QSA_ERR_DEVICE: return "no usable gfx950 device";
+  }
+  return "unknown status";
+}
+
+const char* qsa_last_error(void) { return g_err; }
+
+int32_t qsa_version(void) { return 100; }
+
+}  // extern "C"

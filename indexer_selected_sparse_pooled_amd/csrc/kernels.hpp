@@ -1,0 +1,80 @@
+// Host-side launchers of the libqsa kernels. Arguments are validated by the
+// C-ABI layer (api.hip) before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace qsa {
+
+hipError_t launch_pool(const uint16_t* raw, int64_t raw_ss, uint16_t* pooled, int64_t pooled_ss,
+                       int n_seq, int64_t b0, int64_t nb, int dim, int block, hipStream_t s);
+
+struct ScoreArgs {
+  const int* q_seq;   // nullable
+  const int* q_ctx;
+  int max_ctx;
+  int nq;
+  int block;
+  int idx_dim;
+  int idx_heads;
+  const uint16_t* q_idx;
+  const float* w_idx;  // nullable when idx_heads == 1
+  const uint16_t* keys;
+  int64_t keys_ss;
+  float* scores;
+  int64_t ld;
+};
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t s);
+
+struct TopkArgs {
+  const int* q_ctx;
+  int max_ctx;
+  int nq;
+  int block;
+  int topk;
+  const float* scores;
+  int64_t ld;
+  int* sel;
+  int* n_sel;
+  void* ws;
+};
+// Workspace layout of the chunked (large-context) path.
+struct TopkPlan {
+  bool chunked;      // false: every query fits the LDS path
+  int chunk;         // scores per chunk
+  int n_chunks;      // chunks per query at max_ctx
+  int list_len;      // candidates kept per chunk
+  size_t ws_bytes;
+};
+TopkPlan plan_topk(int nq, int max_ctx, int block, int topk);
+hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t s);
+
+struct AttendArgs {
+  const int* q_seq;  // nullable
+  const int* q_ctx;
+  int max_ctx;
+  int nq;
+  int hq, hkv, dk, dv;
+  float scale;
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  int64_t seq_stride, tok_stride, head_stride;
+  const int* sel;
+  const int* n_sel;
+  int topk;
+  int block;
+  int n_split;
+  int64_t tile_begin, tile_end;
+  float* o_part;
+  float* lse_part;
+};
+hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, int64_t o_ps,
+                        const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,
+                        float* lse_out, hipStream_t s);
+
+}  // namespace qsa

@@ -1,0 +1,301 @@
+// A2: indexer scores of every candidate block.
+// "3090x3で 314 万コンテキスト", section "VRAM に残す必要があるもの": the
+// pooled keys (128 x bf16 per block) are the only read that grows with the
+// context and are scanned in full at every decode step, so the decode
+// kernel is a bandwidth-bound stream: each wave reads 64 consecutive keys
+// (16 KiB) with 16-byte non-temporal loads, 16 lanes per key row, and folds
+// the 16 partial dot products of a lane group with a transposing butterfly
+// (15 lane exchanges per 16 keys instead of 60).
+// "GLM-5.3 最適化 第2部", section "PCP": the token-level indexer of the
+// MLA-like variant scores every earlier token with several heads; the score
+// is the weighted sum of the heads' ReLU'd dot products.
+// A prefill chunk (all queries in one sequence) uses MFMA 16x16x32 bf16
+// tiles: 16 queries x 16 keys x 32 dims per instruction.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qsa {
+namespace {
+
+__device__ __forceinline__ float dot8(u32x4 k, u32x4 q) {
+  float acc = 0.f;
+  acc = dot2(k[0], q[0], acc);
+  acc = dot2(k[1], q[1], acc);
+  acc = dot2(k[2], q[2], acc);
+  acc = dot2(k[3], q[3], acc);
+  return acc;
+}
+
+// Variant A decode: 128-d keys, one head. A wave owns 64 consecutive keys
+// per tile; lane (g = lane/16, c = lane%16) loads dims [8c, 8c+8) of keys
+// 4k+g (k = 0..15) and after the butterfly holds the score of key 4c+g.
+template <int TPW>
+__global__ __launch_bounds__(256) void scores_gemv_a(ScoreArgs a) {
+  const int i = blockIdx.y;
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int64_t n = clamp_ctx(a.q_ctx[i], a.max_ctx) / a.block;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
+  const int64_t wg0 = int64_t(blockIdx.x) * (4 * TPW * 64);
+  if (wg0 >= n) return;
+  const u32x4 qv = ld16(a.q_idx + int64_t(i) * 128 + 8 * c);
+  const uint16_t* kb = a.keys + int64_t(seq) * a.keys_ss;
+  float* out = a.scores + int64_t(i) * a.ld;
+  for (int t = 0; t < TPW; t++) {
+    const int64_t tile0 = wg0 + int64_t(wave * TPW + t) * 64;
+    if (tile0 >= n) break;
+    u32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      const int64_t blk = tile0 + 4 * k + g;
+      v[k] = blk < n ? ld16_nt(kb + blk * 128 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    }
+    float p[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) p[k] = dot8(v[k], qv);
+    // transposing butterfly over the 16 lanes of a group
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      const bool up = c & 8;
+      const float keep = up ? p[j + 8] : p[j];
+      const float send = up ? p[j] : p[j + 8];
+      p[j] = keep + __shfl_xor(send, 8);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; j++) {
+      const bool up = c & 4;
+      const float keep = up ? p[j + 4] : p[j];
+      const float send = up ? p[j] : p[j + 4];
+      p[j] = keep + __shfl_xor(send, 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const bool up = c & 2;
+      const float keep = up ? p[j + 2] : p[j];
+      const float send = up ? p[j] : p[j + 2];
+      p[j] = keep + __shfl_xor(send, 2);
+    }
+    {
+      const bool up = c & 1;
+      const float keep = up ? p[1] : p[0];
+      const float send = up ? p[0] : p[1];
+      p[0] = keep + __shfl_xor(send, 1);
+    }
+    const int64_t blk = tile0 + 4 * c + g;
+    if (blk < n) out[blk] = p[0];
+  }
+}
+
+// Variant B decode: 64-d token keys, 4 indexer heads, ReLU-weighted sum.
+// A wave owns 128 consecutive keys (16 KiB); lane (g = lane/8, c = lane%8)
+// loads dims [8c, 8c+8) of keys 8k+g; after the butterfly over the 8 lanes
+// of a group it holds the 4 head dots of keys 8(2c+j)+g, j = 0, 1.
+__global__ __launch_bounds__(256) void scores_gemv_b(ScoreArgs a) {
+  const int i = blockIdx.y;
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int64_t n = clamp_ctx(a.q_ctx[i], a.max_ctx) / a.block;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = lane >> 3, c = lane & 7;
+  const int64_t tile0 = (int64_t(blockIdx.x) * 4 + wave) * 128;
+  if (tile0 >= n) return;
+  u32x4 qv[4];
+  float w[4];
+#pragma unroll
+  for (int h = 0; h < 4; h++) {
+    qv[h] = ld16(a.q_idx + (int64_t(i) * 4 + h) * 64 + 8 * c);
+    w[h] = a.w_idx[int64_t(i) * 4 + h];
+  }
+  const uint16_t* kb = a.keys + int64_t(seq) * a.keys_ss;
+  float p[16][4];
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const int64_t tok = tile0 + 8 * k + g;
+    const u32x4 v = tok < n ? ld16_nt(kb + tok * 64 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int h = 0; h < 4; h++) p[k][h] = dot8(v, qv[h]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const bool up = c & 4;
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      const float keep = up ? p[j + 8][h] : p[j][h];
+      const float send = up ? p[j][h] : p[j + 8][h];
+      p[j][h] = keep + __shfl_xor(send, 4);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; j++) {
+    const bool up = c & 2;
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      const float keep = up ? p[j + 4][h] : p[j][h];
+      const float send = up ? p[j][h] : p[j + 4][h];
+      p[j][h] = keep + __shfl_xor(send, 2);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const bool up = c & 1;
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      const float keep = up ? p[j + 2][h] : p[j][h];
+      const float send = up ? p[j][h] : p[j + 2][h];
+      p[j][h] = keep + __shfl_xor(send, 1);
+    }
+  }
+  float* out = a.scores + int64_t(i) * a.ld;
+#pragma unroll
+  for (int j = 0; j < 2; j++) {
+    const int64_t tok = tile0 + 8 * (2 * c + j) + g;
+    float s = 0.f;
+#pragma unroll
+    for (int h = 0; h < 4; h++) s += w[h] * fmaxf(p[j][h], 0.f);
+    if (tok < n) out[tok] = s;
+  }
+}
+
+// Largest candidate count among the 64 queries of a work-group.
+__device__ __forceinline__ int64_t wg_max_n(const ScoreArgs& a, int q0, int* red) {
+  int n = 0;
+  if (threadIdx.x < 64) {
+    const int q = q0 + threadIdx.x;
+    n = q < a.nq ? clamp_ctx(a.q_ctx[q], a.max_ctx) / a.block : 0;
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) n = max(n, __shfl_xor(n, m));
+    if (threadIdx.x == 0) red[0] = n;
+  }
+  __syncthreads();
+  return red[0];
+}
+
+// Prefill chunk, variant A: work-group = 64 queries (16 per wave) x 128 keys.
+// MFMA 16x16x32 bf16: A = q_idx rows, B = key rows (dims contiguous).
+__global__ __launch_bounds__(256) void scores_gemm_a(ScoreArgs a) {
+  __shared__ int red[1];
+  const int q0 = blockIdx.y * 64;
+  const int64_t b0 = int64_t(blockIdx.x) * 128;
+  const int64_t nmax = wg_max_n(a, q0, red);
+  if (b0 >= nmax) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = lane >> 4;
+  const int qa_row = q0 + 16 * wave + r;
+  bf16x8 qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) {
+    u32x4 w = qa_row < a.nq ? ld16(a.q_idx + int64_t(qa_row) * 128 + 32 * ks + 8 * kq)
+                            : u32x4{0u, 0u, 0u, 0u};
+    qa[ks] = as_bf16x8(w);
+  }
+  int64_t nrow[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int q = q0 + 16 * wave + 4 * kq + e;
+    nrow[e] = q < a.nq ? clamp_ctx(a.q_ctx[q], a.max_ctx) / a.block : 0;
+  }
+  for (int nt = 0; nt < 8; nt++) {
+    const int64_t blk = b0 + 16 * nt + r;
+    if (b0 + 16 * nt >= nmax) break;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      u32x4 w = blk < nmax ? ld16(a.keys + blk * 128 + 32 * ks + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], as_bf16x8(w), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int q = q0 + 16 * wave + 4 * kq + e;
+      if (blk < nrow[e]) a.scores[int64_t(q) * a.ld + blk] = acc[e];
+    }
+  }
+}
+
+// Prefill chunk, variant B: 4 heads x 64 dims, score = sum_h w_h relu(dot_h).
+__global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
+  __shared__ int red[1];
+  const int q0 = blockIdx.y * 64;
+  const int64_t b0 = int64_t(blockIdx.x) * 128;
+  const int64_t nmax = wg_max_n(a, q0, red);
+  if (b0 >= nmax) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = lane >> 4;
+  const int qa_row = q0 + 16 * wave + r;
+  bf16x8 qa[4][2];
+#pragma unroll
+  for (int h = 0; h < 4; h++)
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      u32x4 w = qa_row < a.nq ? ld16(a.q_idx + (int64_t(qa_row) * 4 + h) * 64 + 32 * ks + 8 * kq)
+                              : u32x4{0u, 0u, 0u, 0u};
+      qa[h][ks] = as_bf16x8(w);
+    }
+  int64_t nrow[4];
+  float wr[4][4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int q = q0 + 16 * wave + 4 * kq + e;
+    nrow[e] = q < a.nq ? clamp_ctx(a.q_ctx[q], a.max_ctx) / a.block : 0;
+#pragma unroll
+    for (int h = 0; h < 4; h++) wr[e][h] = q < a.nq ? a.w_idx[int64_t(q) * 4 + h] : 0.f;
+  }
+  for (int nt = 0; nt < 8; nt++) {
+    const int64_t tok = b0 + 16 * nt + r;
+    if (b0 + 16 * nt >= nmax) break;
+    bf16x8 kb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      u32x4 w = tok < nmax ? ld16(a.keys + tok * 64 + 32 * ks + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      kb[ks] = as_bf16x8(w);
+    }
+    float s[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 4; h++) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], kb[0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], kb[1], acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; e++) s[e] += wr[e][h] * fmaxf(acc[e], 0.f);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int q = q0 + 16 * wave + 4 * kq + e;
+      if (tok < nrow[e]) a.scores[int64_t(q) * a.ld + tok] = s[e];
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  const int64_t nmax = int64_t(a.max_ctx) / a.block;
+  if (nmax <= 0) return hipSuccess;
+  const bool chunk = a.q_seq == nullptr && a.nq >= 16;
+  if (a.idx_heads == 1) {
+    if (chunk) {
+      dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
+      hipLaunchKernelGGL(scores_gemm_a, grid, dim3(256), 0, s, a);
+    } else {
+      const int64_t per_wg1 = 256;  // keys per work-group with one tile per wave
+      const int64_t wgs1 = ((nmax + per_wg1 - 1) / per_wg1) * a.nq;
+      if (wgs1 >= 8192) {
+        dim3 grid(unsigned((nmax + 511) / 512), unsigned(a.nq));
+        hipLaunchKernelGGL(scores_gemv_a<2>, grid, dim3(256), 0, s, a);
+      } else {
+        dim3 grid(unsigned((nmax + 255) / 256), unsigned(a.nq));
+        hipLaunchKernelGGL(scores_gemv_a<1>, grid, dim3(256), 0, s, a);
+      }
+    }
+  } else {
+    if (chunk) {
+      dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
+      hipLaunchKernelGGL(scores_gemm_b, grid, dim3(256), 0, s, a);
+    } else {
+      dim3 grid(unsigned((nmax + 511) / 512), unsigned(a.nq));
+      hipLaunchKernelGGL(scores_gemv_b, grid, dim3(256), 0, s, a);
+    }
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qsa

@@ -1,0 +1,119 @@
+"""The hot path as a chain of libqsa calls.
+
+A decode layer is A2 -> A3 -> A4 -> A5 (scores, top-k, split attention,
+merge); a prefill chunk is A2 -> A3 -> A6 per history tile -> A5. Buffers
+are allocated once with torch and reused; every step runs in libqsa's
+kernels, enqueued on one stream with no host synchronisation, so a whole
+layer or chunk can be captured in a HIP graph.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import qsa
+
+
+@dataclass
+class DecodeBuffers:
+    scores: torch.Tensor    # [nq, max_ctx / block] fp32
+    sel: torch.Tensor       # [nq, topk] int32
+    n_sel: torch.Tensor     # [nq] int32
+    ws: torch.Tensor        # top-k workspace (or None)
+    o_part: torch.Tensor    # [n_split, nq, hq, dv] fp32
+    lse_part: torch.Tensor  # [n_split, nq, hq] fp32
+    o: torch.Tensor         # [nq, hq, dv] fp32
+    o_bf16: torch.Tensor    # [nq, hq, dv] bf16
+    lse: torch.Tensor       # [nq, hq] fp32
+    n_split: int
+
+
+def default_n_split(nq: int, hkv: int, budget_tokens: int) -> int:
+    """Splits per (query, kv head): enough work-groups to cover the chip
+    (about 512), at least 64 tokens each."""
+    want = max(1, -(-512 // max(1, nq * hkv)))
+    most = max(1, budget_tokens // 64)
+    return int(min(want, most, 256))
+
+
+def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") -> DecodeBuffers:
+    nmax = max(1, max_ctx // sel_cfg.block)
+    if n_split is None:
+        n_split = default_n_split(nq, attn_cfg.hkv, sel_cfg.topk * sel_cfg.block + sel_cfg.block - 1)
+    f32 = dict(dtype=torch.float32, device=device)
+    return DecodeBuffers(
+        scores=torch.empty(nq, nmax, **f32),
+        sel=torch.empty(nq, sel_cfg.topk, dtype=torch.int32, device=device),
+        n_sel=torch.empty(nq, dtype=torch.int32, device=device),
+        ws=qsa.topk_workspace(sel_cfg, nq, max_ctx, device),
+        o_part=torch.empty(n_split, nq, attn_cfg.hq, attn_cfg.dv, **f32),
+        lse_part=torch.empty(n_split, nq, attn_cfg.hq, **f32),
+        o=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, **f32),
+        o_bf16=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, dtype=torch.bfloat16, device=device),
+        lse=torch.empty(nq, attn_cfg.hq, **f32),
+        n_split=n_split,
+    )
+
+
+def decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: DecodeBuffers,
+                 q_seq=None, w_idx=None, stream=None) -> None:
+    """One decode layer for nq queries (one per sequence): results in bufs.o / o_bf16 / lse."""
+    qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=q_seq, w_idx=w_idx,
+                         stream=stream)
+    qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
+    qsa.qsa_sparse_decode(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, bufs.n_split,
+                          bufs.o_part, bufs.lse_part, q_seq=q_seq, stream=stream)
+    qsa.qsa_lse_merge(bufs.o_part, bufs.lse_part, o_out=bufs.o, o_out_bf16=bufs.o_bf16, lse_out=bufs.lse,
+                      stream=stream)
+
+
+@dataclass
+class PrefillBuffers:
+    scores: torch.Tensor      # [nq, max_ctx / block] fp32
+    sel: torch.Tensor
+    n_sel: torch.Tensor
+    ws: torch.Tensor
+    o_tiles: torch.Tensor     # [n_tiles, nq, hq, dv] fp32
+    lse_tiles: torch.Tensor   # [n_tiles, nq, hq] fp32
+    o: torch.Tensor
+    o_bf16: torch.Tensor
+    lse: torch.Tensor
+    tiles: list
+
+
+def history_tiles(ctx_max: int, tile: int):
+    """[k*tile, (k+1)*tile) clipped to [0, ctx_max)."""
+    return [(a, min(a + tile, ctx_max)) for a in range(0, ctx_max, tile)]
+
+
+def prefill_buffers(sel_cfg, attn_cfg, nq, max_ctx, tile, device="cuda") -> PrefillBuffers:
+    nmax = max(1, max_ctx // sel_cfg.block)
+    tiles = history_tiles(max_ctx, tile)
+    f32 = dict(dtype=torch.float32, device=device)
+    return PrefillBuffers(
+        scores=torch.empty(nq, nmax, **f32),
+        sel=torch.empty(nq, sel_cfg.topk, dtype=torch.int32, device=device),
+        n_sel=torch.empty(nq, dtype=torch.int32, device=device),
+        ws=qsa.topk_workspace(sel_cfg, nq, max_ctx, device),
+        o_tiles=torch.empty(len(tiles), nq, attn_cfg.hq, attn_cfg.dv, **f32),
+        lse_tiles=torch.empty(len(tiles), nq, attn_cfg.hq, **f32),
+        o=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, **f32),
+        o_bf16=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, dtype=torch.bfloat16, device=device),
+        lse=torch.empty(nq, attn_cfg.hq, **f32),
+        tiles=tiles,
+    )
+
+
+def prefill_chunk(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: PrefillBuffers,
+                  w_idx=None, stream=None) -> None:
+    """A chunk of queries of one sequence: selection, then the history tiles
+    in the outer loop (one attention call per tile), then the merge."""
+    qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=None, w_idx=w_idx,
+                         stream=stream)
+    qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
+    for t, (a, b) in enumerate(bufs.tiles):
+        qsa.qsa_sparse_prefill(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, a, b,
+                               bufs.o_tiles[t], bufs.lse_tiles[t], stream=stream)
+    qsa.qsa_lse_merge(bufs.o_tiles, bufs.lse_tiles, o_out=bufs.o, o_out_bf16=bufs.o_bf16, lse_out=bufs.lse,
+                      stream=stream)

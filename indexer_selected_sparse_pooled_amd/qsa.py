@@ -1,0 +1,239 @@
+"""Python binding of libqsa (argument marshalling only).
+
+Every function here has the name of the C entry point it calls (declared in
+include/qsa.h), takes torch tensors that already live on the GPU, reads
+their pointers and strides, and calls the library on the given (or current)
+torch stream. No arithmetic of the method happens here; if libqsa.so is
+missing the first call raises instead of falling back to anything else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libqsa.so")
+
+QSA_OK = 0
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape", 3: "workspace too small",
+          4: "launch failed", 5: "no usable gfx950 device"}
+
+
+class QsaError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__(f"{fn}: {STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+class SelCfg(ctypes.Structure):
+    _fields_ = [("block", ctypes.c_int32), ("topk", ctypes.c_int32),
+                ("idx_dim", ctypes.c_int32), ("idx_heads", ctypes.c_int32)]
+
+
+class AttnCfg(ctypes.Structure):
+    _fields_ = [("hq", ctypes.c_int32), ("hkv", ctypes.c_int32), ("dk", ctypes.c_int32),
+                ("dv", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class KV(ctypes.Structure):
+    _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("seq_stride", ctypes.c_int64),
+                ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
+                ("capacity", ctypes.c_int64)]
+
+
+# The two parameter sets of the pages (variant A: pooled 4-token blocks,
+# variant B: token-level indexer with an MLA-like shared latent).
+SEL_A = SelCfg(4, 512, 128, 1)
+ATTN_A = AttnCfg(16, 2, 256, 256, 1.0 / 16.0)
+SEL_B = SelCfg(1, 2048, 64, 4)
+ATTN_B = AttnCfg(64, 1, 576, 512, 1.0 / 24.0)
+
+_lib = None
+
+_vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+_SIGS = {
+    "qsa_pool_keys": [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _i32, _vp],
+    "qsa_index_scores": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
+    "qsa_topk_blocks": [_vp, _i32, _vp, _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
+    "qsa_topk_workspace_bytes": [_vp, _i32, _i32],
+    "qsa_sparse_decode": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp],
+    "qsa_sparse_prefill": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
+    "qsa_lse_merge": [_i32, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
+    "qsa_status_string": [_i32],
+    "qsa_last_error": [],
+    "qsa_version": [],
+}
+_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
+        "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
+EXPORTS = tuple(_SIGS)
+
+
+def lib():
+    """The loaded libqsa (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with indexer_selected_sparse_pooled_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, args in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = _RES.get(name, ctypes.c_int)
+        _lib = L
+    return _lib
+
+
+def _check(fn, status):
+    if status != QSA_OK:
+        raise QsaError(fn, status, lib().qsa_last_error().decode())
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _dev(t, dtypes, name):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA tensor")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+_BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_F32 = (torch.float32,)
+_I32 = (torch.int32,)
+
+
+def _rowmajor_tail(t, name, n):
+    """Require the last n dims of t to be densely packed (row-major)."""
+    expect = 1
+    for d in range(t.dim() - 1, t.dim() - 1 - n, -1):
+        if t.size(d) > 1 and t.stride(d) != expect:
+            raise ValueError(f"{name}: the last {n} dims must be contiguous")
+        expect *= t.size(d)
+
+
+def qsa_version() -> int:
+    return lib().qsa_version()
+
+
+def qsa_pool_keys(raw, pooled, tok_begin=0, tok_end=None, block=4, stream=None):
+    """raw: [n_seq, n_tok, dim] bf16; pooled: [n_seq, n_blk, dim] bf16."""
+    n_seq, n_tok, dim = raw.shape
+    _rowmajor_tail(raw, "raw", 2)
+    _rowmajor_tail(pooled, "pooled", 2)
+    if tok_end is None:
+        tok_end = n_tok
+    if tok_end > n_tok or (tok_end // block) > pooled.shape[1] or pooled.shape[0] != n_seq or pooled.shape[2] != dim:
+        raise ValueError("qsa_pool_keys: shapes do not cover the token range")
+    _check("qsa_pool_keys", lib().qsa_pool_keys(
+        _dev(raw, _BF16, "raw"), raw.stride(0), _dev(pooled, _BF16, "pooled"), pooled.stride(0),
+        n_seq, tok_begin, tok_end, dim, block, _stream(stream)))
+
+
+def qsa_index_scores(cfg, q_ctx, max_ctx, q_idx, keys, scores, q_seq=None, w_idx=None, stream=None):
+    """q_ctx: [nq] int32; q_idx: [nq, heads, dim] bf16; keys: [n_seq, n_keys, dim] bf16;
+    scores: [nq, ld] fp32; q_seq: [nq] int32 or None; w_idx: [nq, heads] fp32 or None."""
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(q_idx, "q_idx", 3)
+    _rowmajor_tail(keys, "keys", 2)
+    _rowmajor_tail(scores, "scores", 1)
+    if max_ctx // cfg.block > keys.shape[1]:
+        raise ValueError("qsa_index_scores: keys hold fewer than max_ctx / block rows")
+    _check("qsa_index_scores", lib().qsa_index_scores(
+        ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
+        _dev(q_idx, _BF16, "q_idx"), _dev(w_idx, _F32, "w_idx"), _dev(keys, _BF16, "keys"),
+        keys.stride(0), _dev(scores, _F32, "scores"), scores.stride(0), _stream(stream)))
+
+
+def qsa_topk_workspace_bytes(cfg, nq, max_ctx) -> int:
+    return int(lib().qsa_topk_workspace_bytes(ctypes.byref(cfg), nq, max_ctx))
+
+
+def topk_workspace(cfg, nq, max_ctx, device="cuda"):
+    """A workspace tensor of the size qsa_topk_blocks needs (or None)."""
+    n = qsa_topk_workspace_bytes(cfg, nq, max_ctx)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device) if n else None
+
+
+def qsa_topk_blocks(cfg, q_ctx, max_ctx, scores, sel, n_sel, ws=None, stream=None):
+    """scores: [nq, ld] fp32; sel: [nq, topk] int32; n_sel: [nq] int32; ws: uint8 tensor."""
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(scores, "scores", 1)
+    if sel.shape != (nq, cfg.topk) or not sel.is_contiguous():
+        raise ValueError("qsa_topk_blocks: sel must be a contiguous [nq, topk] tensor")
+    ws_ptr = None if ws is None else ctypes.c_void_p(ws.data_ptr())
+    ws_n = 0 if ws is None else ws.numel() * ws.element_size()
+    _check("qsa_topk_blocks", lib().qsa_topk_blocks(
+        ctypes.byref(cfg), nq, _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(scores, _F32, "scores"),
+        scores.stride(0), _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), ws_ptr, ws_n,
+        _stream(stream)))
+
+
+def make_kv(k, v=None):
+    """KV descriptor of k, v: [n_seq, capacity, hkv, d] bf16 (v defaults to k)."""
+    if v is None:
+        v = k
+    for t, name in ((k, "k"), (v, "v")):
+        if t.dim() != 4 or t.stride(3) != 1:
+            raise ValueError(f"{name} must be [n_seq, capacity, hkv, d] with unit last stride")
+    if k.stride()[:3] != v.stride()[:3] or k.shape[:2] != v.shape[:2]:
+        raise ValueError("k and v must share their sequence, token and head strides")
+    kv = KV(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), k.stride(0), k.stride(1),
+            k.stride(2), k.shape[1])
+    kv._keep = (k, v)
+    return kv
+
+
+def qsa_sparse_decode(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, n_split, o_part, lse_part,
+                      q_seq=None, stream=None):
+    """q: [nq, hq, dk] bf16; kv: make_kv(...); o_part: [n_split, nq, hq, dv] fp32;
+    lse_part: [n_split, nq, hq] fp32."""
+    nq = q_ctx.shape[0]
+    if not q.is_contiguous() or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("q, o_part and lse_part must be contiguous")
+    if tuple(o_part.shape) != (n_split, nq, attn_cfg.hq, attn_cfg.dv):
+        raise ValueError("o_part must be [n_split, nq, hq, dv]")
+    if tuple(lse_part.shape) != (n_split, nq, attn_cfg.hq):
+        raise ValueError("lse_part must be [n_split, nq, hq]")
+    _check("qsa_sparse_decode", lib().qsa_sparse_decode(
+        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"),
+        _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q, _BF16, "q"), ctypes.byref(kv),
+        _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_part, _F32, "o_part"),
+        _dev(lse_part, _F32, "lse_part"), _stream(stream)))
+
+
+def qsa_sparse_prefill(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, tile_begin, tile_end,
+                       o_part, lse_part, q_seq=None, stream=None):
+    """q: [nq, hq, dk] bf16; o_part: [nq, hq, dv] fp32; lse_part: [nq, hq] fp32."""
+    nq = q_ctx.shape[0]
+    if not q.is_contiguous() or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("q, o_part and lse_part must be contiguous")
+    if tuple(o_part.shape[-3:]) != (nq, attn_cfg.hq, attn_cfg.dv) or tuple(lse_part.shape[-2:]) != (nq, attn_cfg.hq):
+        raise ValueError("o_part must end in [nq, hq, dv] and lse_part in [nq, hq]")
+    _check("qsa_sparse_prefill", lib().qsa_sparse_prefill(
+        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"),
+        _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q, _BF16, "q"), ctypes.byref(kv),
+        _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), tile_begin, tile_end,
+        _dev(o_part, _F32, "o_part"), _dev(lse_part, _F32, "lse_part"), _stream(stream)))
+
+
+def qsa_lse_merge(o_parts, lse_parts, o_out=None, o_out_bf16=None, lse_out=None, stream=None):
+    """o_parts: [P, rows..., dv] fp32 (contiguous rows); lse_parts: [P, rows...] fp32."""
+    n_part = o_parts.shape[0]
+    dv = o_parts.shape[-1]
+    rows = lse_parts[0].numel()
+    if o_parts[0].numel() != rows * dv:
+        raise ValueError("o_parts and lse_parts disagree on the number of rows")
+    _rowmajor_tail(o_parts, "o_parts", o_parts.dim() - 1)
+    _rowmajor_tail(lse_parts, "lse_parts", lse_parts.dim() - 1)
+    _check("qsa_lse_merge", lib().qsa_lse_merge(
+        n_part, rows, dv, _dev(o_parts, _F32, "o_parts"), o_parts.stride(0),
+        _dev(lse_parts, _F32, "lse_parts"), lse_parts.stride(0), _dev(o_out, _F32, "o_out"),
+        _dev(o_out_bf16, _BF16, "o_out_bf16"), _dev(lse_out, _F32, "lse_out"), _stream(stream)))

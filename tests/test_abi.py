@@ -1,0 +1,76 @@
+"""The C ABI library loads on a CPU-only host and exports every entry point
+that include/qsa.h declares; argument checks that need no device work."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qsa.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qsa_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from indexer_selected_sparse_pooled_amd import qsa
+    if not os.path.exists(qsa.LIB_PATH):
+        pytest.fail("libqsa.so is not built (run __graft_entry__.build())")
+    return qsa.lib()
+
+
+def test_header_declares_the_five_operations():
+    names = _declared()
+    for n in ("qsa_index_scores", "qsa_topk_blocks", "qsa_sparse_decode", "qsa_sparse_prefill", "qsa_lse_merge"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from indexer_selected_sparse_pooled_amd import qsa
+    for name in _declared():
+        assert hasattr(lib, name), name
+        assert name in qsa.EXPORTS, f"binding has no signature for {name}"
+
+
+def test_status_strings_and_version(lib):
+    assert lib.qsa_version() == 100
+    assert lib.qsa_status_string(0) == b"ok"
+    assert lib.qsa_status_string(3) == b"workspace too small"
+
+
+def test_validation_happens_before_any_device_call(lib):
+    from indexer_selected_sparse_pooled_amd import qsa
+    # unsupported block: rejected on the host, no GPU needed
+    st = lib.qsa_pool_keys(None, 0, None, 0, 1, 0, 8, 128, 3, None)
+    assert st == 2 and b"block" in lib.qsa_last_error()
+    # unsupported top-k
+    cfg = qsa.SelCfg(4, 4096, 128, 1)
+    st = lib.qsa_topk_blocks(ctypes.byref(cfg), 1, None, 100, None, 100, None, None, None, 0, None)
+    assert st == 2
+    # empty work is a no-op that succeeds without touching the device
+    st = lib.qsa_index_scores(ctypes.byref(qsa.SEL_A), 0, None, None, 0, None, None, None, 0, None, 0, None)
+    assert st == 0
+    st = lib.qsa_lse_merge(1, 0, 256, None, 0, None, 0, None, None, None, None)
+    assert st == 0
+    # negative sizes
+    st = lib.qsa_lse_merge(0, 4, 256, None, 0, None, 0, None, None, None, None)
+    assert st == 1
+    # attention shape not compiled
+    bad = qsa.AttnCfg(8, 2, 128, 128, 0.1)
+    kv = qsa.KV()
+    st = lib.qsa_sparse_decode(ctypes.byref(qsa.SEL_A), ctypes.byref(bad), 1, None, None, 10, None,
+                               ctypes.byref(kv), None, None, 1, None, None, None)
+    assert st == 2
+
+
+def test_topk_workspace_query(lib):
+    from indexer_selected_sparse_pooled_amd import qsa
+    # small contexts need no workspace; 1M-token contexts need the chunk lists
+    assert qsa.qsa_topk_workspace_bytes(qsa.SEL_A, 4, 8192) == 0
+    big = qsa.qsa_topk_workspace_bytes(qsa.SEL_A, 4, 1048320)
+    assert big > 0 and big % 16 == 0
