@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the indexer-selected sparse-attention hot path on one MI355X.
+
+Headline (``value``): decode steps/s at 1,048,320-token context, batch 4,
+12 sparse-attention layers run in sequence (each layer: pooled-key scan,
+top-512 block selection, sparse attention over the 2,048 selected tokens in
+splits, log-sum-exp merge). One step = all 12 layers for the 4 sequences,
+captured once in a HIP graph and replayed. Inputs (K, V, raw and pooled
+indexer keys, queries) are seeded, synthetic and resident in HBM before the
+timed region.
+
+Also reported: HBM GB/s of the step (algorithmic bytes), the prefill chunk
+(4096 queries after a 60,000-token history, 8192-token history tiles, and
+1024-token tiles) in query tokens/s, the roofline of the dominant kernel
+(the pooled-key scan) with its launch duration timed by HIP events on the
+launch stream, and the CPU oracle timed on the host on a bounded sample.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "sparse-attn decode steps/s + HBM GB/s at 1M ctx; prefill query tok/s"
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+
+DECODE = dict(name="decode L=1048320 B=4 12 layers, 16 q heads / 2 kv heads, head_dim 256, top-512 of 4-token blocks",
+              config_id=3, ctx=1048320, batch=4, layers=12)
+PREFILL = dict(name="prefill 4096 queries after a 60000-token history, 8192-token tiles", config_id=4,
+               history=60000, chunk=4096, tiles=(8192, 1024))
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def fill(t, seed, stream):
+    from qsa_inputs.gpu import fill_normal_bf16
+    fill_normal_bf16(t, seed, stream)
+
+
+def build_decode(pkg, pipeline, qi, torch):
+    """Device-resident inputs of the 1M-context decode workload."""
+    L, B, NL = DECODE["ctx"], DECODE["batch"], DECODE["layers"]
+    seed = qi.config_seed(DECODE["config_id"])
+    dev = "cuda"
+    layers = []
+    t0 = time.time()
+    for l in range(NL):
+        raw = torch.empty(B, L, 128, dtype=torch.bfloat16, device=dev)
+        k = torch.empty(B, L, 2, 256, dtype=torch.bfloat16, device=dev)
+        v = torch.empty(B, L, 2, 256, dtype=torch.bfloat16, device=dev)
+        q = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=dev)
+        q_idx = torch.empty(B, 1, 128, dtype=torch.bfloat16, device=dev)
+        for s in range(B):
+            fill(raw[s], seed, qi.stream_id(l, s, "raw_key"))
+            fill(k[s], seed, qi.stream_id(l, s, "k"))
+            fill(v[s], seed, qi.stream_id(l, s, "v"))
+            fill(q[s], seed, qi.stream_id(l, s, "q"))
+            fill(q_idx[s], seed, qi.stream_id(l, s, "q_idx"))
+        pooled = torch.empty(B, L // 4, 128, dtype=torch.bfloat16, device=dev)
+        layers.append(dict(raw=raw, k=k, v=v, q=q, q_idx=q_idx, pooled=pooled, kv=pkg.make_kv(k, v)))
+        torch.cuda.synchronize()
+        log(f"decode inputs: layer {l + 1}/{NL} filled ({time.time() - t0:.1f} s)")
+    # pooling happens when a block completes (append time), not per step
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for lay in layers:
+        pkg.qsa_pool_keys(lay["raw"], lay["pooled"], block=4)
+    ev1.record()
+    torch.cuda.synchronize()
+    pool_ms = ev0.elapsed_time(ev1)
+    q_ctx = torch.full((B,), L, dtype=torch.int32, device=dev)
+    q_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    return layers, q_ctx, q_seq, pool_ms
+
+
+def time_graph(torch, fn, steps, warmup):
+    """Capture fn in a graph, replay warmup + steps times; ms per replay."""
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # eager run once (also checks the calls)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        fn()
+    for _ in range(warmup):
+        g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(steps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return e0.elapsed_time(e1) / steps, wall, g
+
+
+def time_launches(torch, fn, reps):
+    """Average duration of one call of fn (HIP events on the current stream)."""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
+    layers, q_ctx, q_seq, pool_ms = build_decode(pkg, pipeline, qi, torch)
+    L, B = DECODE["ctx"], DECODE["batch"]
+    bufs = [pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, B, L) for _ in layers]
+
+    def step():
+        for lay, bf in zip(layers, bufs):
+            pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay["q_idx"], lay["pooled"], lay["q"], lay["kv"],
+                                  bf, q_seq=q_seq)
+
+    ms, wall, graph = time_graph(torch, step, steps, warmup)
+    unit_bytes = bm.decode_unit_bytes(L)
+    step_bytes = unit_bytes * B * len(layers)
+    # per-kernel durations, each timed alone over every layer (HIP events, launch stream)
+    b0, lay0 = bufs[0], layers[0]
+    reps = max(10, steps)
+
+    def scan_only():
+        for lay, bf in zip(layers, bufs):
+            pkg.qsa_index_scores(pkg.SEL_A, q_ctx, L, lay["q_idx"], lay["pooled"], bf.scores, q_seq=q_seq)
+
+    scan_ms = time_launches(torch, scan_only, reps) / len(layers)
+    topk_ms = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, L, b0.scores, b0.sel, b0.n_sel,
+                                                               b0.ws), reps)
+    attn_ms = time_launches(torch, lambda: pkg.qsa_sparse_decode(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"],
+                                                                 lay0["kv"], b0.sel, b0.n_sel, b0.n_split, b0.o_part,
+                                                                 b0.lse_part, q_seq=q_seq), reps)
+    merge_ms = time_launches(torch, lambda: pkg.qsa_lse_merge(b0.o_part, b0.lse_part, o_out=b0.o,
+                                                              o_out_bf16=b0.o_bf16, lse_out=b0.lse), reps)
+    scan_launch_bytes = B * (bm.scan_bytes(L) + 128 * 2)
+    scan_gbs = scan_launch_bytes / (scan_ms * 1e-3) / 1e9
+    del graph
+    return dict(ms=ms, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
+                n_split=bufs[0].n_split, scan_ms=scan_ms, topk_ms=topk_ms, attn_ms=attn_ms, merge_ms=merge_ms,
+                scan_launch_bytes=scan_launch_bytes, scan_gbs=scan_gbs, layers=layers, bufs=bufs)
+
+
+def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
+    H, C = PREFILL["history"], PREFILL["chunk"]
+    ctx_max = H + C
+    seed = qi.config_seed(PREFILL["config_id"])
+    dev = "cuda"
+    raw = torch.empty(1, ctx_max, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(1, ctx_max, 2, 256, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(1, ctx_max, 2, 256, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(C, 16, 256, dtype=torch.bfloat16, device=dev)
+    q_idx = torch.empty(C, 1, 128, dtype=torch.bfloat16, device=dev)
+    fill(raw, seed, qi.stream_id(0, 0, "raw_key"))
+    fill(k, seed, qi.stream_id(0, 0, "k"))
+    fill(v, seed, qi.stream_id(0, 0, "v"))
+    fill(q, seed, qi.stream_id(0, 0, "q"))
+    fill(q_idx, seed, qi.stream_id(0, 0, "q_idx"))
+    pooled = torch.empty(1, ctx_max // 4, 128, dtype=torch.bfloat16, device=dev)
+    pkg.qsa_pool_keys(raw, pooled, block=4)
+    kv = pkg.make_kv(k, v)
+    ctxs = list(range(H + 1, H + C + 1))
+    q_ctx = torch.tensor(ctxs, dtype=torch.int32, device=dev)
+    flops = bm.prefill_flops(ctxs)
+    out = {}
+    for tile in PREFILL["tiles"]:
+        bufs = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, C, ctx_max, tile)
+
+        def chunk():
+            pipeline.prefill_chunk(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q_idx, pooled, q, kv, bufs)
+
+        ms, wall, g = time_graph(torch, chunk, max(3, steps // 5), max(1, warmup))
+        out[tile] = dict(ms=ms, tok_s=C / (ms * 1e-3), tflops=flops["total"] / (ms * 1e-3) / 1e12)
+        del g, bufs
+        log(f"prefill tile {tile}: {ms:.3f} ms/chunk")
+    return out, flops
+
+
+def cpu_baseline(qi, orc, bm):
+    """The oracle on one (layer, sequence) unit of the decode workload: scan of
+    262,080 pooled keys, top-512 selection, attention over the 2,048 selected
+    tokens (input generation and pooling excluded), repeated for about 10 s
+    (a step has 48 such units; steps/s is scaled accordingly)."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    L = DECODE["ctx"]
+    seed = qi.config_seed(DECODE["config_id"])
+    t0 = time.time()
+    raw = qi.normal_bf16(seed, qi.stream_id(0, 0, "raw_key"), 0, L * 128).reshape(L, 128)
+    pooled = orc.pool_keys(raw, 4)
+    del raw
+    q_idx = qi.normal_bf16(seed, qi.stream_id(0, 0, "q_idx"), 0, 128)
+    q = qi.normal_bf16(seed, qi.stream_id(0, 0, "q"), 0, 16 * 256).reshape(16, 256)
+    # the selection does not change between repetitions: generate the K/V rows it reads once
+    s0 = orc.index_scores(q_idx, pooled, L // 4)
+    toks0 = orc.selected_tokens(orc.select_blocks(s0, L, 4, 512), L, 4)
+    idx = (toks0[:, None, None] * 512 + np.arange(2)[None, :, None] * 256 + np.arange(256)[None, None, :])
+    k_rows = qi.normal_bf16(seed, qi.stream_id(0, 0, "k"), 0, index=idx.reshape(-1).astype(np.uint64))
+    v_rows = qi.normal_bf16(seed, qi.stream_id(0, 0, "v"), 0, index=idx.reshape(-1).astype(np.uint64))
+    k_rows, v_rows = k_rows.reshape(-1, 2, 256), v_rows.reshape(-1, 2, 256)
+    row_of = {int(t): r for r, t in enumerate(toks0)}
+    prep_s = time.time() - t0
+    # repeat the unit for about 10 s of CPU work (at least 16 times)
+    reps = 0
+    t0 = time.perf_counter()
+    while reps < 16 or (time.perf_counter() - t0 < 10.0 and reps < 2000):
+        reps += 1
+        s = orc.index_scores(q_idx, pooled, L // 4)
+        sel = orc.select_blocks(s, L, 4, 512)
+        toks = orc.selected_tokens(sel, L, 4)
+        rows = np.array([row_of[int(t)] for t in toks])
+        o, lse = orc.attend(q, k_rows, v_rows, rows, 1.0 / 16)
+    dt = time.perf_counter() - t0
+    unit_s = dt / reps
+    return dict(value=1.0 / (unit_s * DECODE["batch"] * DECODE["layers"]), unit="steps/s", cores=int(cores),
+                kind="oracle",
+                sample=(f"one (layer, sequence) unit of the 1M-context decode step (scan of 262,080 pooled keys, "
+                        f"top-512, attention over 2,048 tokens; K/V rows it reads are generated by index beforehand), "
+                        f"run {reps} times (a step has 48 such units); {unit_s * 1e3:.1f} ms per unit; "
+                        f"input generation and pooling excluded ({prep_s:.1f} s)"),
+                seconds=dt)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "The decode step would shard by sequence and layer, one GPU per shard; run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+
+    import indexer_selected_sparse_pooled_amd as pkg
+    import qsa_inputs as qi
+    from indexer_selected_sparse_pooled_amd import bytemodel as bm
+    from indexer_selected_sparse_pooled_amd import pipeline
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    pkg.qsa.lib()  # fails loudly if libqsa.so is missing
+    torch.cuda.set_device(0)
+
+    t_all = time.time()
+    dec = run_decode(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
+    log(f"decode: {dec['ms']:.4f} ms/step, scan {dec['scan_ms'] * 1e3:.1f} us/launch")
+    del dec["layers"], dec["bufs"]
+    torch.cuda.empty_cache()
+    pre, pflops = run_prefill(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
+
+    from oracle import qsa_oracle as orc
+    cpu = cpu_baseline(qi, orc, bm)
+    log(f"cpu baseline: {cpu['value']:.4f} steps/s ({cpu['seconds']:.1f} s)")
+
+    steps_s = 1e3 / dec["ms"]
+    hbm_gbs = dec["step_bytes"] / (dec["ms"] * 1e-3) / 1e9
+    t8 = pre[8192]
+    line = {
+        "metric": METRIC,
+        "value": round(steps_s, 3),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(dec["ms"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic: seeded SplitMix64 inverse-CDF N(0,1) bf16, device-resident",
+        "config": {"workload": DECODE["name"], "ctx": DECODE["ctx"], "batch": DECODE["batch"],
+                   "layers": DECODE["layers"], "n_split": dec["n_split"], "graph": True},
+        "hbm_gbs": round(hbm_gbs, 1),
+        "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
+        "step_bytes": dec["step_bytes"],
+        "breakdown_us_per_layer": {"scan": round(dec["scan_ms"] * 1e3, 2), "topk": round(dec["topk_ms"] * 1e3, 2),
+                                   "attend": round(dec["attn_ms"] * 1e3, 2),
+                                   "merge": round(dec["merge_ms"] * 1e3, 2)},
+        "pool_ms_all_layers": round(dec["pool_ms"], 3),
+        "prefill": {"workload": PREFILL["name"], "tok_s": round(t8["tok_s"], 1), "ms_per_chunk": round(t8["ms"], 4),
+                    "tflops": round(t8["tflops"], 2), "mfma_frac": round(t8["tflops"] / BF16_PEAK_TFLOPS, 5),
+                    "useful_gflop": round(pflops["total"] / 1e9, 2),
+                    "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)}},
+        "roofline": {"kernel": "scores_gemv_a (pooled-key scan)", "bound": "hbm",
+                     "achieved": round(dec["scan_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec["scan_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["scan_ms"] * 1e3, 3)},
+        "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "wall_s": round(time.time() - t_all, 1),
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

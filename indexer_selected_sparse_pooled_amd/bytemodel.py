@@ -1,0 +1,56 @@
+"""Algorithmic bytes and FLOPs of the hot path (host-side arithmetic only).
+
+Decode unit = one query (one sequence) in one layer: the pooled-key scan
+(every complete block's key), the indexer query, the gathered K/V rows of
+the selected tokens, the query and the bf16 output. Scores and selections
+are intermediates and are not counted. ("3090x3で 314 万コンテキスト": the
+K/V read per layer is |S| x head_dim x 2 B x 2 (K and V) x kv heads, section
+"なぜ"; the scan reads blocks x 128 x 2 B per layer, section
+"VRAM に残す必要があるもの".)
+"""
+from __future__ import annotations
+
+BF16 = 2
+
+
+def attended_tokens(ctx: int, block: int = 4, topk: int = 512) -> int:
+    nblk = ctx // block
+    return ctx if nblk <= topk else topk * block + ctx % block
+
+
+def scan_bytes(ctx: int, block: int = 4, idx_dim: int = 128) -> int:
+    return (ctx // block) * idx_dim * BF16
+
+
+def kv_bytes(n_tokens: int, hkv: int = 2, d: int = 256) -> int:
+    return n_tokens * hkv * d * BF16 * 2
+
+
+def decode_unit_bytes(ctx: int, block: int = 4, topk: int = 512, idx_dim: int = 128, hq: int = 16,
+                      hkv: int = 2, d: int = 256) -> int:
+    s = attended_tokens(ctx, block, topk)
+    return (scan_bytes(ctx, block, idx_dim) + idx_dim * BF16 + kv_bytes(s, hkv, d)
+            + hq * d * BF16 + hq * d * BF16)
+
+
+def decode_unit_flops(ctx: int, block: int = 4, topk: int = 512, idx_dim: int = 128, hq: int = 16,
+                      d: int = 256) -> int:
+    s = attended_tokens(ctx, block, topk)
+    return 2 * idx_dim * (ctx // block) + 2 * hq * s * (d + d)
+
+
+def prefill_flops(ctxs, block: int = 4, topk: int = 512, idx_dim: int = 128, hq: int = 16, dk: int = 256,
+                  dv: int = 256) -> dict:
+    """Useful FLOPs of a prefill chunk: attention over each query's selected
+    tokens plus the indexer scores of every candidate block."""
+    att = sum(2 * hq * attended_tokens(c, block, topk) * (dk + dv) for c in ctxs)
+    idx = sum(2 * idx_dim * (c // block) for c in ctxs)
+    return {"attention": att, "indexer": idx, "total": att + idx}
+
+
+def per_token_bytes(layers: int = 12, idx_dim: int = 128, block: int = 4, hkv: int = 2, d: int = 256) -> dict:
+    """Memory per context token over all sparse layers: the pooled key
+    (kept next to the GPU) and the K, V and raw indexer key rows."""
+    pooled = layers * idx_dim * BF16 / block
+    rows = layers * (2 * hkv * d * BF16 + idx_dim * BF16)
+    return {"pooled": pooled, "kv_and_raw_keys": rows}

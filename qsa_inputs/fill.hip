@@ -22,14 +22,24 @@ __global__ __launch_bounds__(256) void fill_kernel(uint64_t key, uint64_t start,
                                                    const uint16_t* __restrict__ table,
                                                    uint16_t* __restrict__ out) {
   const int64_t stride = int64_t(gridDim.x) * blockDim.x;
+  // 8-byte stores need the word's first element 8-byte aligned in `out`
+  const bool aligned = (start & 3u) == 0 && (reinterpret_cast<uintptr_t>(out) & 7u) == 0;
   // elements [start, start + n): word w covers elements 4w .. 4w+3
   const uint64_t w0 = start >> 2;
   const uint64_t w1 = (start + uint64_t(n) + 3) >> 2;
   for (uint64_t w = w0 + uint64_t(blockIdx.x) * blockDim.x + threadIdx.x; w < w1; w += uint64_t(stride)) {
     const uint64_t u = mix64(key + (w + 1) * kG);
+    const uint64_t e0 = 4 * w;
+    if (aligned && e0 >= start && e0 + 4 <= start + uint64_t(n)) {
+      // whole word inside the range: one 8-byte store
+      const uint64_t v = uint64_t(table[(u >> 48) & 0xFFFFu]) | (uint64_t(table[(u >> 32) & 0xFFFFu]) << 16) |
+                         (uint64_t(table[(u >> 16) & 0xFFFFu]) << 32) | (uint64_t(table[u & 0xFFFFu]) << 48);
+      *reinterpret_cast<uint64_t*>(out + (e0 - start)) = v;
+      continue;
+    }
 #pragma unroll
     for (int l = 0; l < 4; l++) {
-      const uint64_t e = 4 * w + l;
+      const uint64_t e = e0 + l;
       if (e >= start && e < start + uint64_t(n)) out[e - start] = table[(u >> (48 - 16 * l)) & 0xFFFFu];
     }
   }

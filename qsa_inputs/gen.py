@@ -53,12 +53,33 @@ def stream_id(layer: int, seq: int, kind: str, salt: int = 0) -> int:
     return ((((int(salt) * 256 + int(layer)) * 65536 + int(seq)) * 16) + KIND[kind]) & _MASK
 
 
+def _mix64_inplace(z: np.ndarray, t: np.ndarray) -> None:
+    """mix64 applied in place to z (t: scratch of the same shape)."""
+    np.right_shift(z, np.uint64(30), out=t)
+    np.bitwise_xor(z, t, out=z)
+    np.multiply(z, _M1, out=z)
+    np.right_shift(z, np.uint64(27), out=t)
+    np.bitwise_xor(z, t, out=z)
+    np.multiply(z, _M2, out=z)
+    np.right_shift(z, np.uint64(31), out=t)
+    np.bitwise_xor(z, t, out=z)
+
+
 def words(seed: int, stream: int, word_index: np.ndarray) -> np.ndarray:
     """The SplitMix64 outputs with the given indices (0-based) of one stream."""
     key = np.uint64(stream_key(seed, stream))
-    wi = np.asarray(word_index, dtype=np.uint64)
-    with np.errstate(over="ignore"):
-        return mix64(key + (wi + np.uint64(1)) * np.uint64(G))
+    wi = np.asarray(word_index, dtype=np.uint64).reshape(-1)
+    out = np.empty(wi.size, dtype=np.uint64)
+    chunk = 1 << 20
+    t = np.empty(min(chunk, max(1, wi.size)), dtype=np.uint64)
+    for a in range(0, wi.size, chunk):
+        z = out[a:a + chunk]
+        tt = t[: z.size]
+        np.add(wi[a:a + chunk], np.uint64(1), out=z)
+        np.multiply(z, np.uint64(G), out=z)
+        np.add(z, key, out=z)
+        _mix64_inplace(z, tt)
+    return out.reshape(np.shape(word_index))
 
 
 def codes(seed: int, stream: int, index: np.ndarray) -> np.ndarray:
@@ -93,10 +114,20 @@ def normal_table() -> np.ndarray:
     return _TABLE
 
 
+def _codes_range(seed: int, stream: int, start: int, count: int) -> np.ndarray:
+    """16-bit codes of elements [start, start + count): each word hashed once."""
+    w0, w1 = start >> 2, (start + count + 3) >> 2
+    u = words(seed, stream, np.arange(w0, w1, dtype=np.uint64))
+    # little-endian uint16 view of a word holds lanes 3, 2, 1, 0 (lane 0 = most significant)
+    c = u.view(np.uint16).reshape(-1, 4)[:, ::-1].reshape(-1)
+    off = start - 4 * w0
+    return c[off: off + count]
+
+
 def normal_bf16(seed: int, stream: int, start: int, count: int = None, index=None) -> np.ndarray:
     """bf16 bit patterns of elements [start, start+count) (or the given indices)."""
     if index is None:
-        index = np.arange(start, start + count, dtype=np.uint64)
+        return normal_table()[_codes_range(seed, stream, start, count)]
     return normal_table()[codes(seed, stream, index)]
 
 
