@@ -127,26 +127,38 @@ __global__ __launch_bounds__(256) void attend_a(AttendArgs a) {
 
   for (int64_t pb = P0; pb < P1; pb += TT) {
     const int cnt = int((P1 - pb) < TT ? (P1 - pb) : TT);
+    // token positions first, then every K and V load of the tile, so that
+    // all of them are in flight together
+    const int c = tid & 31;
+    int64_t vtok[TT / 8];
+#pragma unroll
+    for (int ps = 0; ps < TT / 8; ps++) {
+      const int row = ps * 8 + (tid >> 5);
+      vtok[ps] = row < cnt ? lv.tok(pb + row) : -1;
+    }
+    const int rr = 16 * wave + r;
+    const bool valid = rr < cnt;
+    const int64_t kt = lv.tok(pb + (valid ? rr : 0));
+    u32x4 vw[TT / 8];
+#pragma unroll
+    for (int ps = 0; ps < TT / 8; ps++)
+      vw[ps] = vtok[ps] >= 0 ? ld16(vbase + vtok[ps] * a.tok_stride + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    bf16x8 kb[DK_A / 32];
+    {
+      const uint16_t* krow = kbase + kt * a.tok_stride + 8 * kq;
+#pragma unroll
+      for (int ks = 0; ks < DK_A / 32; ks++) kb[ks] = as_bf16x8(ld16(krow + 32 * ks));
+    }
     // V tile -> LDS: 8 passes of 8 rows x 32 chunks of 16 bytes
 #pragma unroll
     for (int ps = 0; ps < TT / 8; ps++) {
       const int row = ps * 8 + (tid >> 5);
-      const int c = tid & 31;
-      u32x4 w = {0u, 0u, 0u, 0u};
-      if (row < cnt) w = ld16(vbase + lv.tok(pb + row) * a.tok_stride + 8 * c);
       u32x2* dst = reinterpret_cast<u32x2*>(vsh + row * VSTR + 8 * c);
-      dst[0] = u32x2{w[0], w[1]};
-      dst[1] = u32x2{w[2], w[3]};
+      dst[0] = u32x2{vw[ps][0], vw[ps][1]};
+      dst[1] = u32x2{vw[ps][2], vw[ps][3]};
     }
     // S for tokens 16*wave .. 16*wave+15
     {
-      const int rr = 16 * wave + r;
-      const bool valid = rr < cnt;
-      const int64_t t = lv.tok(pb + (valid ? rr : 0));
-      const uint16_t* krow = kbase + t * a.tok_stride + 8 * kq;
-      bf16x8 kb[DK_A / 32];
-#pragma unroll
-      for (int ks = 0; ks < DK_A / 32; ks++) kb[ks] = as_bf16x8(ld16(krow + 32 * ks));
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < DK_A / 32; ks++)

@@ -3,7 +3,8 @@
 // context is computed separately and the partial results are combined with
 // log-sum-exp; "3090x3で 314 万コンテキスト", section "ちなみにこの欠点":
 // prefill merges the softmax partials of consecutive history tiles.
-// One wave per output row; each lane owns 4 consecutive dims per 256.
+// One wave per output row; each lane owns 4 consecutive dims per 256; the
+// partials' weights are computed once (one lane each) and broadcast.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -26,22 +27,41 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, in
     for (int p = lane; p < n_part; p += 64) tot += expf(l[p * lps + row] - mx);
   tot = wave_sum(tot);
   const float lse = mx == -INFINITY ? -INFINITY : mx + logf(tot);
-  for (int d0 = 4 * lane; d0 < dv; d0 += 256) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (mx != -INFINITY) {
-      for (int p = 0; p < n_part; p++) {
-        const float lp = l[p * lps + row];
-        if (lp == -INFINITY) continue;
-        const float w = expf(lp - lse);
-        const f32x4 v = *reinterpret_cast<const f32x4*>(o + p * ops + row * dv + d0);
-        acc += w * v;
+  const int nd = (dv + 255) / 256;  // 256 dims per pass of the wave (4 per lane)
+  f32x4 acc[4];
+#pragma unroll
+  for (int c = 0; c < 4; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (mx != -INFINITY) {
+    for (int p0 = 0; p0 < n_part; p0 += 64) {
+      // weight of partial p0 + lane, then broadcast one partial at a time
+      const int p = p0 + lane;
+      const float w_lane = p < n_part ? expf(l[p * lps + row] - lse) : 0.f;
+      const int cnt = min(64, n_part - p0);
+#pragma unroll 8
+      for (int pp = 0; pp < cnt; pp++) {
+        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), pp));
+        const float* src = o + (p0 + pp) * ops + row * dv + 4 * lane;
+#pragma unroll
+        for (int c = 0; c < 4; c++) {
+          if (c < nd && 256 * c + 4 * lane < dv) {
+            // loads are unconditional so that several partials are in flight;
+            // an empty partial (lse = -inf, weight 0) adds nothing
+            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 256 * c);
+            if (w != 0.f) acc[c] += w * v;
+          }
+        }
       }
     }
-    if (oo) *reinterpret_cast<f32x4*>(oo + row * dv + d0) = acc;
+  }
+#pragma unroll
+  for (int c = 0; c < 4; c++) {
+    const int d0 = 256 * c + 4 * lane;
+    if (c >= nd || d0 >= dv) continue;
+    if (oo) *reinterpret_cast<f32x4*>(oo + row * dv + d0) = acc[c];
     if (ob) {
       u32x2 pk;
-      pk[0] = uint32_t(f32_to_bf16(acc[0])) | (uint32_t(f32_to_bf16(acc[1])) << 16);
-      pk[1] = uint32_t(f32_to_bf16(acc[2])) | (uint32_t(f32_to_bf16(acc[3])) << 16);
+      pk[0] = uint32_t(f32_to_bf16(acc[c][0])) | (uint32_t(f32_to_bf16(acc[c][1])) << 16);
+      pk[1] = uint32_t(f32_to_bf16(acc[c][2])) | (uint32_t(f32_to_bf16(acc[c][3])) << 16);
       *reinterpret_cast<u32x2*>(ob + row * dv + d0) = pk;
     }
   }
