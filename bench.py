@@ -2,9 +2,9 @@
 """Benchmark of the indexer-selected sparse-attention hot path on one MI355X.
 
 Headline (``value``): decode steps/s at 1,048,320-token context, batch 4,
-12 sparse-attention layers run in sequence (each layer: pooled-key scan,
-top-512 block selection, sparse attention over the 2,048 selected tokens in
-splits, log-sum-exp merge). One step = all 12 layers for the 4 sequences,
+12 sparse-attention layers run in sequence (each layer: pooled-key scan
+and exact top-512 block selection in one launch, sparse attention over the
+2,048 selected tokens in splits, log-sum-exp merge). One step = all 12 layers for the 4 sequences,
 captured once in a HIP graph and replayed. Inputs (K, V, raw and pooled
 indexer keys, queries) are seeded, synthetic and resident in HBM before the
 timed region.
@@ -12,7 +12,7 @@ timed region.
 Also reported: HBM GB/s of the step (algorithmic bytes), the prefill chunk
 (4096 queries after a 60,000-token history, 8192-token history tiles, and
 1024-token tiles) in query tokens/s, the roofline of the dominant kernel
-(the pooled-key scan) with its launch duration timed by HIP events on the
+(the pooled-key scan with the top-k) with its launch duration timed by HIP events on the
 launch stream, and the CPU oracle timed on the host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
@@ -139,13 +139,12 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
     b0, lay0 = bufs[0], layers[0]
     reps = max(10, steps)
 
-    def scan_only():
+    def scan_select_only():
         for lay, bf in zip(layers, bufs):
-            pkg.qsa_index_scores(pkg.SEL_A, q_ctx, L, lay["q_idx"], lay["pooled"], bf.scores, q_seq=q_seq)
+            pkg.qsa_index_topk(pkg.SEL_A, q_ctx, L, lay["q_idx"], lay["pooled"], bf.scores, bf.sel, bf.n_sel,
+                               bf.itk_ws, q_seq=q_seq)
 
-    scan_ms = time_launches(torch, scan_only, reps) / len(layers)
-    topk_ms = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, L, b0.scores, b0.sel, b0.n_sel,
-                                                               b0.ws), reps)
+    scan_ms = time_launches(torch, scan_select_only, reps) / len(layers)
     attn_ms = time_launches(torch, lambda: pkg.qsa_sparse_decode(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"],
                                                                  lay0["kv"], b0.sel, b0.n_sel, b0.n_split, b0.o_part,
                                                                  b0.lse_part, q_seq=q_seq), reps)
@@ -155,7 +154,7 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
     scan_gbs = scan_launch_bytes / (scan_ms * 1e-3) / 1e9
     del graph
     return dict(ms=ms, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
-                n_split=bufs[0].n_split, scan_ms=scan_ms, topk_ms=topk_ms, attn_ms=attn_ms, merge_ms=merge_ms,
+                n_split=bufs[0].n_split, scan_ms=scan_ms, attn_ms=attn_ms, merge_ms=merge_ms,
                 scan_launch_bytes=scan_launch_bytes, scan_gbs=scan_gbs, layers=layers, bufs=bufs)
 
 
@@ -270,7 +269,7 @@ def main():
 
     t_all = time.time()
     dec = run_decode(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
-    log(f"decode: {dec['ms']:.4f} ms/step, scan {dec['scan_ms'] * 1e3:.1f} us/launch")
+    log(f"decode: {dec['ms']:.4f} ms/step, scan+select {dec['scan_ms'] * 1e3:.1f} us/launch")
     del dec["layers"], dec["bufs"]
     torch.cuda.empty_cache()
     pre, pflops = run_prefill(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
@@ -300,7 +299,7 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "step_bytes": dec["step_bytes"],
-        "breakdown_us_per_layer": {"scan": round(dec["scan_ms"] * 1e3, 2), "topk": round(dec["topk_ms"] * 1e3, 2),
+        "breakdown_us_per_layer": {"scan_select": round(dec["scan_ms"] * 1e3, 2),
                                    "attend": round(dec["attn_ms"] * 1e3, 2),
                                    "merge": round(dec["merge_ms"] * 1e3, 2)},
         "pool_ms_all_layers": round(dec["pool_ms"], 3),
@@ -308,7 +307,7 @@ def main():
                     "tflops": round(t8["tflops"], 2), "mfma_frac": round(t8["tflops"] / BF16_PEAK_TFLOPS, 5),
                     "useful_gflop": round(pflops["total"] / 1e9, 2),
                     "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)}},
-        "roofline": {"kernel": "scores_gemv_a (pooled-key scan)", "bound": "hbm",
+        "roofline": {"kernel": "index_topk_a (pooled-key scan + exact top-512, one launch)", "bound": "hbm",
                      "achieved": round(dec["scan_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["scan_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
                      "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["scan_ms"] * 1e3, 3)},

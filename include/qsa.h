@@ -165,6 +165,32 @@ qsa_status qsa_topk_blocks(const qsa_sel_cfg* cfg, int32_t nq,
 
 size_t qsa_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx);
 
+/* ----------------------------------------------------------- A2 + A3 ----
+ * qsa_index_topk: qsa_index_scores followed by qsa_topk_blocks, in one
+ * launch (decode: each query scores the pooled keys of its own sequence).
+ * Writes exactly what the two calls write: scores[i][b] for b < n_i and the
+ * selection sel / n_sel, bit-identical to them. Each work-group scores one
+ * chunk of blocks and keeps the chunk's best candidates; the last
+ * work-group of a query to finish selects the exact top-k from them.
+ * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの" and "なぜ".)
+ * Variant A only (block 4, idx_dim 128, idx_heads 1); other configurations
+ * return QSA_ERR_UNSUPPORTED.
+ *   q_seq, q_ctx, q_idx, keys, scores, ld_scores: as qsa_index_scores.
+ *   sel, n_sel: as qsa_topk_blocks.
+ *   ws (device) workspace of at least qsa_index_topk_workspace_bytes(cfg,
+ *      nq, max_ctx) bytes. Its first bytes are per-query arrival counters:
+ *      the whole workspace must be zero before the first call, and every
+ *      completed call leaves the counters zero again (so one zero-fill at
+ *      allocation suffices). Calls that share a workspace must not run
+ *      concurrently. */
+qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq,
+                          const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
+                          const qsa_bf16* keys, int64_t keys_seq_stride,
+                          float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel,
+                          void* ws, size_t ws_bytes, qsa_stream_t stream);
+
+size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx);
+
 /* ---------------------------------------------------------------- A4 ----
  * qsa_sparse_decode: softmax attention of each query over its selected
  * tokens, split into n_split partial results.

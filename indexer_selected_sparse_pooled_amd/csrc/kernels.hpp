@@ -73,6 +73,34 @@ struct AttendArgs {
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
+// Decode scan + exact top-k in one launch (variant A: 128-d pooled keys).
+struct IndexTopkArgs {
+  const int* q_seq;  // nullable
+  const int* q_ctx;
+  int max_ctx;
+  int nq;
+  const uint16_t* q_idx;
+  const uint16_t* keys;
+  int64_t keys_ss;
+  float* scores;
+  int64_t ld;
+  int topk;
+  int* sel;
+  int* n_sel;
+  // workspace views (filled by launch_index_topk)
+  uint32_t* counter;
+  uint64_t* list;        // [nq][n_chunks][16] (key << 32 | block), 0 = empty
+  uint64_t* list_bound;  // [nq][n_chunks]
+  int n_chunks;
+};
+struct IndexTopkPlan {
+  int tpw;        // 64-key tiles per wave (chunk = 256 * tpw keys)
+  int n_chunks;   // chunks per query at max_ctx
+  size_t off_list, off_bound, ws_bytes;
+};
+IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk);
+hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, hipStream_t s);
+
 hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, int64_t o_ps,
                         const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,
                         float* lse_out, hipStream_t s);

@@ -1,0 +1,383 @@
+// Exact top-k selection building blocks (wave64, gfx950).
+//
+// Ranking ("125B MoE を 3090 3 枚で運用する vLLM 最適化編", section 3.3: the
+// top-k there ranks an order-preserving integer image of each value and
+// gives equal values to the smaller id): every fp32 score becomes an
+// order-preserving 32-bit key (order_key, never 0 for a finite score, so 0
+// marks an empty slot) and elements rank by (key descending, index
+// ascending). The k best elements are therefore unique, and so is the
+// selection. As a single 64-bit value, rank64(key, index) orders elements
+// the same way (larger ranks better).
+//
+// Three kinds of selectors:
+//  * wave_*:   one wave, keys in registers, no barrier (bit-by-bit
+//              threshold search with ballot counts);
+//  * regsel_*: one work-group, keys in registers, threshold found by 8-bit
+//              radix passes over LDS histograms that start below the common
+//              prefix of the largest and smallest key (one barrier a pass);
+//  * stream_*: one work-group, keys read through a functor (global memory),
+//              any count; slow path.
+#pragma once
+
+#include "common.hpp"
+
+namespace qsa {
+
+__device__ __forceinline__ uint64_t rank64(uint32_t key, int idx) {
+  return (uint64_t(key) << 32) | uint32_t(~uint32_t(idx));
+}
+
+__device__ __forceinline__ uint64_t lanes_below() {
+  const int lane = threadIdx.x & 63;
+  return lane == 0 ? 0ull : (~0ull >> (64 - lane));
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t o = uint32_t(__shfl_xor(int(v), m));
+    v = o > v ? o : v;
+  }
+  return v;
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) {
+    const uint32_t o = uint32_t(__shfl_xor(int(v), m));
+    v = o < v ? o : v;
+  }
+  return v;
+}
+
+// ------------------------------------------------------------------ wave ----
+// Keys key[r] of lane l are element r*64 + l of the wave's range; empty slots
+// hold 0 and never count (every candidate threshold is >= 1).
+
+// k-th largest key among the wave's nonzero keys; need = k - #{key > kstar}.
+// Requires 1 <= k <= number of nonzero keys. Wave-uniform results.
+template <int R>
+__device__ __forceinline__ void wave_select(const uint32_t (&key)[R], int k, uint32_t& kstar, int& need) {
+  uint32_t t = 0;
+#pragma unroll 1
+  for (int bit = 31; bit >= 0; bit--) {
+    const uint32_t cand = t | (1u << bit);
+    int c = 0;
+#pragma unroll
+    for (int r = 0; r < R; r++) c += __popcll(__ballot(key[r] >= cand));
+    if (c >= k) t = cand;
+  }
+  int gt = 0;
+  if (t != 0xFFFFFFFFu) {
+#pragma unroll
+    for (int r = 0; r < R; r++) gt += __popcll(__ballot(key[r] > t));
+  }
+  kstar = t;
+  need = k - gt;
+}
+
+// Emit, in element order, every key > kstar and the first `need` keys equal
+// to kstar: emit(position, element, key). Returns the element that is the
+// need-th one equal to kstar (wave-uniform), or -1 if there is none.
+template <int R, class Emit>
+__device__ __forceinline__ int wave_compact(const uint32_t (&key)[R], uint32_t kstar, int need, Emit emit) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = lanes_below();
+  int base_g = 0, base_e = 0, tau = -1;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const bool fg = key[r] > kstar;
+    const bool fe = key[r] == kstar && key[r] != 0u;
+    const uint64_t bg = __ballot(fg), be = __ballot(fe);
+    const int gb = base_g + __popcll(bg & lt);
+    const int eb = base_e + __popcll(be & lt);
+    if (fg || (fe && eb < need)) emit(gb + (eb < need ? eb : need), r * 64 + lane, key[r]);
+    const uint64_t tm = __ballot(fe && eb == need - 1);
+    if (tm) tau = r * 64 + int(__ffsll(static_cast<unsigned long long>(tm)) - 1);
+    base_g += __popcll(bg);
+    base_e += __popcll(be);
+  }
+  return tau;
+}
+
+// --------------------------------------------------------- work-group, regs --
+// Element j = tid * R + r lives in key[r] of thread tid (so element order is
+// thread order, then register order). Empty slots hold 0.
+
+template <int NT>
+struct RegSelLds {
+  uint32_t hist[3][256];
+  uint32_t wmax[NT / 64], wmin[NT / 64];
+  int wg[NT / 64], we[NT / 64];
+  int tau_slot;
+  int tau_val;
+};
+
+// The k-th largest nonzero key (kstar) and need = k - #{key > kstar} >= 1.
+// Requires 1 <= k <= number of nonzero keys.
+template <int NT, int R>
+__device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>& sh, uint32_t& kstar, int& need) {
+  constexpr int NW = NT / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    if (key[r] != 0u) {
+      mx = key[r] > mx ? key[r] : mx;
+      mn = key[r] < mn ? key[r] : mn;
+    }
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane == 0) {
+    sh.wmax[wave] = mx;
+    sh.wmin[wave] = mn;
+  }
+  for (int b = threadIdx.x; b < 256; b += NT) sh.hist[0][b] = 0u;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    mx = sh.wmax[w] > mx ? sh.wmax[w] : mx;
+    mn = sh.wmin[w] < mn ? sh.wmin[w] : mn;
+  }
+  const uint32_t diff = mx ^ mn;
+  if (diff == 0u) {  // every nonzero key is equal
+    kstar = mx;
+    need = k;
+    return;
+  }
+  int lo = 32 - __clz(diff);  // bits [lo, 32) are common to every nonzero key
+  uint32_t mask = lo >= 32 ? 0u : ~((1u << lo) - 1u);
+  uint32_t prefix = mx & mask;
+  int remaining = k;
+  int pass = 0;
+  while (lo > 0) {
+    const int width = lo < 8 ? lo : 8;
+    const int shift = lo - width;
+    const uint32_t dmask = (1u << width) - 1u;
+    uint32_t* h = sh.hist[pass % 3];
+    uint32_t* hz = sh.hist[(pass + 1) % 3];
+    for (int b = threadIdx.x; b < 256; b += NT) hz[b] = 0u;
+#pragma unroll
+    for (int r = 0; r < R; r++)
+      if (key[r] != 0u && (key[r] & mask) == prefix) atomicAdd(&h[(key[r] >> shift) & dmask], 1u);
+    __syncthreads();
+    // every wave finds the digit (same result everywhere): lane holds the
+    // bins 255 - 4*lane - e, e = 0..3, i.e. digits in descending order
+    int cnt[4];
+    int lsum = 0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      cnt[e] = int(h[255 - (4 * lane + e)]);
+      lsum += cnt[e];
+    }
+    int incl = lsum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int o = __shfl_up(incl, d);
+      if (lane >= d) incl += o;
+    }
+    int above = incl - lsum;
+    int my_digit = -1, my_above = 0;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      if (my_digit < 0 && above < remaining && remaining <= above + cnt[e]) {
+        my_digit = 255 - (4 * lane + e);
+        my_above = above;
+      }
+      above += cnt[e];
+    }
+    const uint64_t hit = __ballot(my_digit >= 0);
+    const int src = int(__ffsll(static_cast<unsigned long long>(hit)) - 1);
+    const uint32_t digit = uint32_t(__shfl(my_digit, src));
+    remaining -= __shfl(my_above, src);
+    prefix |= digit << shift;
+    mask |= dmask << shift;
+    lo = shift;
+    pass++;
+  }
+  kstar = prefix;
+  need = remaining;
+}
+
+// Output position of every element (-1 if not selected): keys > kstar and
+// the first `need` keys equal to kstar in element order. Also records the
+// element that is the need-th equal one (the k-th best): its slot in
+// sh.tau_slot and its val[] entry in sh.tau_val. Ends with a barrier.
+template <int NT, int R>
+__device__ void regsel_positions(const uint32_t (&key)[R], const int (&val)[R], uint32_t kstar, int need,
+                                 RegSelLds<NT>& sh, int (&pos)[R]) {
+  constexpr int NW = NT / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  int g = 0, e = 0;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    g += key[r] > kstar ? 1 : 0;
+    e += (key[r] == kstar && key[r] != 0u) ? 1 : 0;
+  }
+  int ig = g, ie = e;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int og = __shfl_up(ig, d), oe = __shfl_up(ie, d);
+    if (lane >= d) {
+      ig += og;
+      ie += oe;
+    }
+  }
+  if (lane == 63) {
+    sh.wg[wave] = ig;
+    sh.we[wave] = ie;
+  }
+  __syncthreads();
+  int gb = ig - g, eb = ie - e;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    if (w < wave) {
+      gb += sh.wg[w];
+      eb += sh.we[w];
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    pos[r] = -1;
+    if (key[r] > kstar) {
+      pos[r] = gb + (eb < need ? eb : need);
+      gb++;
+    } else if (key[r] == kstar && key[r] != 0u) {
+      if (eb < need) pos[r] = gb + eb;
+      if (eb == need - 1) {
+        sh.tau_slot = threadIdx.x * R + r;
+        sh.tau_val = val[r];
+      }
+      eb++;
+    }
+  }
+  __syncthreads();
+}
+
+// ---------------------------------------------------- work-group, streamed --
+
+struct StreamLds {
+  uint32_t hist[256];
+  int wsum[2][16];
+  int digit;
+  int above;
+};
+
+// Block-wide sums of two per-wave counters (up to 16 waves): this wave's
+// exclusive offsets and the totals.
+template <int NT>
+__device__ __forceinline__ void wave_offsets(int a, int b, StreamLds& sh, int& off_a, int& off_b, int& tot_a,
+                                             int& tot_b) {
+  constexpr int NW = NT / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  if (lane == 0) {
+    sh.wsum[0][wave] = a;
+    sh.wsum[1][wave] = b;
+  }
+  __syncthreads();
+  off_a = 0, off_b = 0, tot_a = 0, tot_b = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    const int x = sh.wsum[0][w], y = sh.wsum[1][w];
+    if (w < wave) {
+      off_a += x;
+      off_b += y;
+    }
+    tot_a += x;
+    tot_b += y;
+  }
+  __syncthreads();
+}
+
+// The k-th largest key among key_at(0..n) and need = k - #{key > kstar}.
+// Four 8-bit radix passes, each reading every key once. Requires 1 <= k <= n.
+template <int NT, class KeyAt>
+__device__ void stream_select(KeyAt key_at, int n, int k, StreamLds& sh, uint32_t& kstar, int& need) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  uint32_t prefix = 0, mask = 0;
+  int remaining = k;
+  for (int pass = 0; pass < 4; pass++) {
+    const int shift = 24 - 8 * pass;
+    for (int b = threadIdx.x; b < 256; b += NT) sh.hist[b] = 0;
+    __syncthreads();
+    for (int j = threadIdx.x; j < n; j += NT) {
+      const uint32_t key = key_at(j);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int cnt[4];
+      int lsum = 0;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        cnt[e] = int(sh.hist[255 - (4 * lane + e)]);
+        lsum += cnt[e];
+      }
+      int incl = lsum;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int o = __shfl_up(incl, d);
+        if (lane >= d) incl += o;
+      }
+      int above = incl - lsum;
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        if (above < remaining && remaining <= above + cnt[e]) {
+          sh.digit = 255 - (4 * lane + e);
+          sh.above = above;
+        }
+        above += cnt[e];
+      }
+    }
+    __syncthreads();
+    remaining -= sh.above;
+    prefix |= uint32_t(sh.digit) << shift;
+    mask |= 0xFFu << shift;
+    __syncthreads();
+  }
+  kstar = prefix;
+  need = remaining;
+}
+
+// Emit, in ascending index order, every j with key > kstar plus the first
+// `need` j with key == kstar: emit(position, j).
+template <int NT, class KeyAt, class Emit>
+__device__ void stream_compact(KeyAt key_at, int n, uint32_t kstar, int need, StreamLds& sh, Emit emit) {
+  const uint64_t lt = lanes_below();
+  int base_g = 0, base_e = 0;
+  for (int r0 = 0; r0 < n; r0 += NT) {
+    const int j = r0 + threadIdx.x;
+    const uint32_t key = j < n ? key_at(j) : 0u;
+    const bool fg = j < n && key > kstar;
+    const bool fe = j < n && key == kstar;
+    const uint64_t bg = __ballot(fg), be = __ballot(fe);
+    int og, oe, tg, te;
+    wave_offsets<NT>(__popcll(bg), __popcll(be), sh, og, oe, tg, te);
+    const int gb = base_g + og + __popcll(bg & lt);
+    const int eb = base_e + oe + __popcll(be & lt);
+    if (fg || (fe && eb < need)) emit(gb + (eb < need ? eb : need), j);
+    base_g += tg;
+    base_e += te;
+  }
+}
+
+// Index of the need-th (1-based) element equal to kstar, in index order.
+template <int NT, class KeyAt>
+__device__ int stream_nth_equal(KeyAt key_at, int n, uint32_t kstar, int need, StreamLds& sh, int* out) {
+  const uint64_t lt = lanes_below();
+  int base_e = 0;
+  for (int r0 = 0; r0 < n; r0 += NT) {
+    const int j = r0 + threadIdx.x;
+    const bool fe = j < n && key_at(j) == kstar;
+    const uint64_t be = __ballot(fe);
+    int og, oe, tg, te;
+    wave_offsets<NT>(0, __popcll(be), sh, og, oe, tg, te);
+    if (fe && base_e + oe + __popcll(be & lt) == need - 1) *out = j;
+    base_e += te;
+    if (base_e >= need) break;
+  }
+  __syncthreads();
+  return *out;
+}
+
+}  // namespace qsa

@@ -22,6 +22,7 @@
 //    from global memory. Both give the same, exact answer.
 #include "common.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace qsa {
 namespace {
@@ -31,135 +32,10 @@ constexpr int kListLen = 64;    // candidates per chunk
 constexpr int kUnionCap = 16384;
 
 struct Scratch {
-  uint32_t hist[256];
-  int wsum[2][16];
-  int digit;
-  int above;
+  StreamLds st;
   int flag;
   int tau_idx;
 };
-
-// Block-wide sum over up to 16 waves of two counters, exclusive per wave.
-template <int NT>
-__device__ __forceinline__ void wave_offsets(int a, int b, Scratch& sh, int& off_a, int& off_b,
-                                             int& tot_a, int& tot_b) {
-  constexpr int NW = NT / 64;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  if (lane == 0) {
-    sh.wsum[0][wave] = a;
-    sh.wsum[1][wave] = b;
-  }
-  __syncthreads();
-  off_a = 0, off_b = 0, tot_a = 0, tot_b = 0;
-#pragma unroll
-  for (int w = 0; w < NW; w++) {
-    const int x = sh.wsum[0][w], y = sh.wsum[1][w];
-    if (w < wave) {
-      off_a += x;
-      off_b += y;
-    }
-    tot_a += x;
-    tot_b += y;
-  }
-  __syncthreads();
-}
-
-// The k-th largest key among key_at(0..n), and how many elements equal to it
-// belong to the top k (need >= 1). Requires 1 <= k <= n.
-template <int NT, class KeyAt>
-__device__ void radix_select(KeyAt key_at, int n, int k, Scratch& sh, uint32_t& kstar, int& need) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t prefix = 0, mask = 0;
-  int remaining = k;
-  for (int pass = 0; pass < 4; pass++) {
-    const int shift = 24 - 8 * pass;
-    for (int b = threadIdx.x; b < 256; b += NT) sh.hist[b] = 0;
-    __syncthreads();
-    for (int j = threadIdx.x; j < n; j += NT) {
-      const uint32_t key = key_at(j);
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
-    }
-    __syncthreads();
-    if (wave == 0) {
-      // lane holds digits 255-4*lane-e, e = 0..3 (descending)
-      int cnt[4];
-      int lsum = 0;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        cnt[e] = int(sh.hist[255 - (4 * lane + e)]);
-        lsum += cnt[e];
-      }
-      int incl = lsum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
-      int above = incl - lsum;
-#pragma unroll
-      for (int e = 0; e < 4; e++) {
-        if (above < remaining && remaining <= above + cnt[e]) {
-          sh.digit = 255 - (4 * lane + e);
-          sh.above = above;
-        }
-        above += cnt[e];
-      }
-    }
-    __syncthreads();
-    const uint32_t digit = uint32_t(sh.digit);
-    remaining -= sh.above;
-    prefix |= digit << shift;
-    mask |= 0xFFu << shift;
-    __syncthreads();
-  }
-  kstar = prefix;
-  need = remaining;
-}
-
-// Emit, in ascending index order, every j with key > kstar plus the first
-// `need` j with key == kstar: emit(position, j).
-template <int NT, class KeyAt, class Emit>
-__device__ void ordered_compact(KeyAt key_at, int n, uint32_t kstar, int need, Scratch& sh, Emit emit) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int base_g = 0, base_e = 0;
-  for (int r0 = 0; r0 < n; r0 += NT) {
-    const int j = r0 + threadIdx.x;
-    uint32_t key = 0;
-    if (j < n) key = key_at(j);
-    const bool fg = j < n && key > kstar;
-    const bool fe = j < n && key == kstar;
-    const uint64_t bg = __ballot(fg), be = __ballot(fe);
-    const int pg = __popcll(bg & lt_mask), pe = __popcll(be & lt_mask);
-    int og, oe, tg, te;
-    wave_offsets<NT>(__popcll(bg), __popcll(be), sh, og, oe, tg, te);
-    const int gb = base_g + og + pg;  // keys > kstar before j
-    const int eb = base_e + oe + pe;  // keys == kstar before j
-    if (fg || (fe && eb < need)) emit(gb + min(eb, need), j);
-    base_g += tg;
-    base_e += te;
-  }
-}
-
-// Index of the `need`-th (1-based) element equal to kstar, in index order.
-template <int NT, class KeyAt>
-__device__ int nth_equal(KeyAt key_at, int n, uint32_t kstar, int need, Scratch& sh) {
-  const int lane = threadIdx.x & 63;
-  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  int base_e = 0;
-  for (int r0 = 0; r0 < n; r0 += NT) {
-    const int j = r0 + threadIdx.x;
-    const bool fe = j < n && key_at(j) == kstar;
-    const uint64_t be = __ballot(fe);
-    int og, oe, tg, te;
-    wave_offsets<NT>(0, __popcll(be), sh, og, oe, tg, te);
-    if (fe && base_e + oe + __popcll(be & lt_mask) == need - 1) sh.tau_idx = j;
-    base_e += te;
-    if (base_e >= need) break;
-  }
-  __syncthreads();
-  return sh.tau_idx;
-}
 
 __device__ __forceinline__ int query_n(const TopkArgs& a, int i) {
   return clamp_ctx(a.q_ctx[i], a.max_ctx) / a.block;
@@ -201,8 +77,8 @@ __global__ __launch_bounds__(256) void topk_local(TopkArgs a, TopkPlan p) {
   }
   uint32_t kstar;
   int need;
-  radix_select<256>(key_at, m, p.list_len, sh, kstar, need);
-  ordered_compact<256>(key_at, m, kstar, need, sh, [&](int pos, int j) {
+  stream_select<256>(key_at, m, p.list_len, sh.st, kstar, need);
+  stream_compact<256>(key_at, m, kstar, need, sh.st, [&](int pos, int j) {
     ws.list_idx[base + pos] = lo + j;
     ws.list_key[base + pos] = lkeys[j];
   });
@@ -229,8 +105,8 @@ __global__ __launch_bounds__(1024) void topk_final(TopkArgs a, TopkPlan p) {
     auto key_at = [&](int j) { return dyn[j]; };
     uint32_t kstar;
     int need;
-    radix_select<1024>(key_at, n, topk, sh, kstar, need);
-    ordered_compact<1024>(key_at, n, kstar, need, sh, [&](int pos, int j) { sel[pos] = j; });
+    stream_select<1024>(key_at, n, topk, sh.st, kstar, need);
+    stream_compact<1024>(key_at, n, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = j; });
     return;
   }
   // union of the chunk lists, ascending index order
@@ -252,13 +128,13 @@ __global__ __launch_bounds__(1024) void topk_final(TopkArgs a, TopkPlan p) {
   auto gkey_at = [&](int j) { return order_key(sc[j]); };
   if (u < topk) {
     // too few listed candidates to bound the threshold: select over everything
-    radix_select<1024>(gkey_at, n, topk, sh, kstar, need);
-    ordered_compact<1024>(gkey_at, n, kstar, need, sh, [&](int pos, int j) { sel[pos] = j; });
+    stream_select<1024>(gkey_at, n, topk, sh.st, kstar, need);
+    stream_compact<1024>(gkey_at, n, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = j; });
     return;
   }
   auto ukey_at = [&](int j) { return ukey[j]; };
-  radix_select<1024>(ukey_at, u, topk, sh, kstar, need);
-  const int tau_idx = nth_equal<1024>(ukey_at, u, kstar, need, sh);
+  stream_select<1024>(ukey_at, u, topk, sh.st, kstar, need);
+  const int tau_idx = stream_nth_equal<1024>(ukey_at, u, kstar, need, sh.st, &sh.tau_idx);
   // a full list whose smallest element (lowest key, then highest index)
   // ranks at or above tau may have left out elements that also do
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -279,12 +155,12 @@ __global__ __launch_bounds__(1024) void topk_final(TopkArgs a, TopkPlan p) {
   }
   __syncthreads();
   if (!sh.flag) {
-    ordered_compact<1024>(ukey_at, u, kstar, need, sh, [&](int pos, int j) { sel[pos] = uidx[j]; });
+    stream_compact<1024>(ukey_at, u, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = uidx[j]; });
     return;
   }
   // fallback: exact select over every score, read from global memory
-  radix_select<1024>(gkey_at, n, topk, sh, kstar, need);
-  ordered_compact<1024>(gkey_at, n, kstar, need, sh, [&](int pos, int j) { sel[pos] = j; });
+  stream_select<1024>(gkey_at, n, topk, sh.st, kstar, need);
+  stream_compact<1024>(gkey_at, n, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = j; });
 }
 
 }  // namespace

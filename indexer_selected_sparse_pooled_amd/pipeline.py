@@ -21,6 +21,7 @@ class DecodeBuffers:
     sel: torch.Tensor       # [nq, topk] int32
     n_sel: torch.Tensor     # [nq] int32
     ws: torch.Tensor        # top-k workspace (or None)
+    itk_ws: torch.Tensor    # zero-filled workspace of the one-launch scan + top-k (or None)
     o_part: torch.Tensor    # [n_split, nq, hq, dv] fp32
     lse_part: torch.Tensor  # [n_split, nq, hq] fp32
     o: torch.Tensor         # [nq, hq, dv] fp32
@@ -37,6 +38,12 @@ def default_n_split(nq: int, hkv: int, budget_tokens: int) -> int:
     return int(min(want, most, 256))
 
 
+def fused_select(sel_cfg) -> bool:
+    """Whether qsa_index_topk covers this indexer (pooled 4-token blocks,
+    one 128-d indexer head)."""
+    return sel_cfg.block == 4 and sel_cfg.idx_dim == 128 and sel_cfg.idx_heads == 1
+
+
 def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") -> DecodeBuffers:
     nmax = max(1, max_ctx // sel_cfg.block)
     if n_split is None:
@@ -47,6 +54,7 @@ def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") 
         sel=torch.empty(nq, sel_cfg.topk, dtype=torch.int32, device=device),
         n_sel=torch.empty(nq, dtype=torch.int32, device=device),
         ws=qsa.topk_workspace(sel_cfg, nq, max_ctx, device),
+        itk_ws=qsa.index_topk_workspace(sel_cfg, nq, max_ctx, device) if fused_select(sel_cfg) else None,
         o_part=torch.empty(n_split, nq, attn_cfg.hq, attn_cfg.dv, **f32),
         lse_part=torch.empty(n_split, nq, attn_cfg.hq, **f32),
         o=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, **f32),
@@ -59,9 +67,13 @@ def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") 
 def decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: DecodeBuffers,
                  q_seq=None, w_idx=None, stream=None) -> None:
     """One decode layer for nq queries (one per sequence): results in bufs.o / o_bf16 / lse."""
-    qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=q_seq, w_idx=w_idx,
-                         stream=stream)
-    qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
+    if bufs.itk_ws is not None and w_idx is None:
+        qsa.qsa_index_topk(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, bufs.sel, bufs.n_sel, bufs.itk_ws,
+                           q_seq=q_seq, stream=stream)
+    else:
+        qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=q_seq, w_idx=w_idx,
+                             stream=stream)
+        qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
     qsa.qsa_sparse_decode(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, bufs.n_split,
                           bufs.o_part, bufs.lse_part, q_seq=q_seq, stream=stream)
     qsa.qsa_lse_merge(bufs.o_part, bufs.lse_part, o_out=bufs.o, o_out_bf16=bufs.o_bf16, lse_out=bufs.lse,

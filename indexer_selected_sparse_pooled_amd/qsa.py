@@ -58,6 +58,8 @@ _SIGS = {
     "qsa_index_scores": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_topk_blocks": [_vp, _i32, _vp, _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
     "qsa_topk_workspace_bytes": [_vp, _i32, _i32],
+    "qsa_index_topk": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
+    "qsa_index_topk_workspace_bytes": [_vp, _i32, _i32],
     "qsa_sparse_decode": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp],
     "qsa_sparse_prefill": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
     "qsa_lse_merge": [_i32, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
@@ -65,7 +67,7 @@ _SIGS = {
     "qsa_last_error": [],
     "qsa_version": [],
 }
-_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
+_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
         "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
 EXPORTS = tuple(_SIGS)
 
@@ -174,6 +176,35 @@ def qsa_topk_blocks(cfg, q_ctx, max_ctx, scores, sel, n_sel, ws=None, stream=Non
         ctypes.byref(cfg), nq, _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(scores, _F32, "scores"),
         scores.stride(0), _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), ws_ptr, ws_n,
         _stream(stream)))
+
+
+def qsa_index_topk_workspace_bytes(cfg, nq, max_ctx) -> int:
+    return int(lib().qsa_index_topk_workspace_bytes(ctypes.byref(cfg), nq, max_ctx))
+
+
+def index_topk_workspace(cfg, nq, max_ctx, device="cuda"):
+    """A zero-filled workspace tensor for qsa_index_topk (its counters must
+    start at zero; every call leaves them zero)."""
+    n = qsa_index_topk_workspace_bytes(cfg, nq, max_ctx)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def qsa_index_topk(cfg, q_ctx, max_ctx, q_idx, keys, scores, sel, n_sel, ws, q_seq=None, stream=None):
+    """qsa_index_scores + qsa_topk_blocks in one launch. Shapes as those two;
+    ws: index_topk_workspace(...)."""
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(q_idx, "q_idx", 3)
+    _rowmajor_tail(keys, "keys", 2)
+    _rowmajor_tail(scores, "scores", 1)
+    if max_ctx // cfg.block > keys.shape[1]:
+        raise ValueError("qsa_index_topk: keys hold fewer than max_ctx / block rows")
+    if sel.shape != (nq, cfg.topk) or not sel.is_contiguous():
+        raise ValueError("qsa_index_topk: sel must be a contiguous [nq, topk] tensor")
+    _check("qsa_index_topk", lib().qsa_index_topk(
+        ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
+        _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0),
+        _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"),
+        ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def make_kv(k, v=None):

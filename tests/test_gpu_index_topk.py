@@ -1,0 +1,163 @@
+"""GPU parity of qsa_index_topk (pooled-key scan + exact top-k in one launch).
+
+The fused call must write exactly what qsa_index_scores followed by
+qsa_topk_blocks writes (bit for bit), its scores must be within the fp32
+accumulation bound of the oracle's fp64 scores, and its selection must be
+the oracle's selection (full sort by score descending, block ascending)
+applied to the GPU's own fp32 scores, bit-exact. Cases cover every path of
+the kernel: all blocks (n <= topk), the register select over raw scores
+(n <= 4096), the union of chunk lists (large n), the exact streamed select
+(few chunks), and inputs built so that chunk lists overflow (planted runs
+of top blocks, all-equal keys), which must fall back to the exact select.
+"""
+import numpy as np
+import pytest
+import torch
+
+import qsa_inputs as qi
+from oracle import qsa_oracle as orc
+from tests import qsa_cases as qc
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pkg():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import indexer_selected_sparse_pooled_amd as p
+    p.qsa.lib()
+    return p
+
+
+def _print_case(name, **kw):
+    print(f"[case] {name} {kw}", flush=True)
+
+
+def _keys(n_seq, n_blk, seed):
+    from qsa_inputs.gpu import fill_normal_bf16
+    keys = torch.empty(n_seq, n_blk, 128, dtype=torch.bfloat16, device="cuda")
+    for s in range(n_seq):
+        fill_normal_bf16(keys[s], seed, qi.stream_id(0, s, "misc"))
+    return keys
+
+
+def _run_fused(pkg, ctxs, q_seq, keys, q_idx, ws=None):
+    nq = len(ctxs)
+    max_ctx = max(max(ctxs), 4)
+    ld = max_ctx // 4 + 5
+    scores = torch.full((nq, ld), float("nan"), device="cuda")
+    sel = torch.full((nq, 512), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((nq,), -7, dtype=torch.int32, device="cuda")
+    if ws is None:
+        ws = pkg.index_topk_workspace(pkg.SEL_A, nq, max_ctx)
+    pkg.qsa_index_topk(pkg.SEL_A, qc.i32(ctxs), max_ctx, q_idx, keys, scores, sel, n_sel, ws,
+                       q_seq=qc.i32(q_seq))
+    torch.cuda.synchronize()
+    return scores, sel, n_sel
+
+
+def _run_unfused(pkg, ctxs, q_seq, keys, q_idx):
+    nq = len(ctxs)
+    max_ctx = max(max(ctxs), 4)
+    ld = max_ctx // 4 + 5
+    scores = torch.full((nq, ld), float("nan"), device="cuda")
+    sel = torch.full((nq, 512), -7, dtype=torch.int32, device="cuda")
+    n_sel = torch.full((nq,), -7, dtype=torch.int32, device="cuda")
+    pkg.qsa_index_scores(pkg.SEL_A, qc.i32(ctxs), max_ctx, q_idx, keys, scores, q_seq=qc.i32(q_seq))
+    ws = pkg.topk_workspace(pkg.SEL_A, nq, max_ctx)
+    pkg.qsa_topk_blocks(pkg.SEL_A, qc.i32(ctxs), max_ctx, scores, sel, n_sel, ws)
+    torch.cuda.synchronize()
+    return scores, sel, n_sel
+
+
+def _check(pkg, ctxs, q_seq, keys, q_idx, fused, check_scores=True):
+    scores, sel, n_sel = (t.cpu().numpy() for t in fused)
+    keys_np = qc.from_dev_bits(keys) if check_scores else None
+    q_np = qc.from_dev_bits(q_idx)
+    for i, ctx in enumerate(ctxs):
+        n = ctx // 4
+        assert np.all(np.isnan(scores[i, n:])), f"query {i}: wrote past the candidates"
+        got_s = scores[i, :n].astype(np.float64)
+        if check_scores and n:
+            ref = orc.index_scores(q_np[i, 0], keys_np[q_seq[i]], n)
+            tol = qc.score_tolerance(q_np[i, 0], keys_np[q_seq[i]], n)
+            assert np.all(np.abs(got_s - ref) <= tol), f"query {i}: scores"
+        want = orc.select_blocks(got_s, ctx, 4, 512)
+        assert n_sel[i] == want.size, (i, n_sel[i], want.size)
+        assert np.array_equal(sel[i, :n_sel[i]], want), f"query {i} (ctx {ctx}): selection"
+        assert np.all(sel[i, n_sel[i]:] == -1)
+
+
+@pytest.mark.parametrize("max_ctx", [1048320, 131072])
+def test_index_topk_paths(pkg, max_ctx):
+    """Queries of one launch take different paths: all blocks, raw register
+    select, union of chunk lists, streamed select."""
+    ctxs = [max_ctx, max_ctx - 4001, 0, 3, 2051, 2052, 9001, 16404, 20000, max_ctx - 17]
+    q_seq = [0, 1, 0, 1, 0, 1, 0, 1, 0, 1]
+    _print_case("index_topk_paths", max_ctx=max_ctx)
+    keys = _keys(2, max_ctx // 4, 41)
+    q_idx = qc.to_dev(qc.bits(41, 5, (len(ctxs), 1, 128)))
+    fused = _run_fused(pkg, ctxs, q_seq, keys, q_idx)
+    _check(pkg, ctxs, q_seq, keys, q_idx, fused)
+    unf = _run_unfused(pkg, ctxs, q_seq, keys, q_idx)
+    for a, b, name in zip(fused, unf, ("scores", "sel", "n_sel")):
+        assert torch.equal(a.nan_to_num(7.0), b.nan_to_num(7.0)), f"fused != unfused ({name})"
+
+
+def test_index_topk_repeated_calls_share_workspace(pkg):
+    """The arrival counters reset themselves: consecutive calls on one
+    workspace, with different contexts, stay exact."""
+    max_ctx = 1048320
+    keys = _keys(2, max_ctx // 4, 43)
+    ws = pkg.index_topk_workspace(pkg.SEL_A, 3, max_ctx)
+    for rep, ctxs in enumerate([[max_ctx, max_ctx, 400000], [300001, max_ctx - 8, 2052], [max_ctx] * 3]):
+        _print_case("index_topk_repeat", rep=rep)
+        q_idx = qc.to_dev(qc.bits(43, 10 + rep, (3, 1, 128)))
+        q_seq = [0, 1, 1]
+        fused = _run_fused(pkg, ctxs, q_seq, keys, q_idx, ws=ws)
+        _check(pkg, ctxs, q_seq, keys, q_idx, fused, check_scores=False)
+    assert torch.count_nonzero(ws[:16]).item() == 0, "counters not reset"
+
+
+def _planted(n_blk, runs, seed):
+    """Keys whose dimension 0 carries the score (q_idx = e0): i.i.d. N(0,1)
+    everywhere, plus runs of consecutive blocks planted with high values."""
+    keys = qc.bits(seed, 3, (n_blk, 128))
+    for (b0, length, val, step) in runs:
+        v = val + step * np.arange(length)
+        keys[b0:b0 + length, 0] = orc.f64_to_bf16(v)
+    return keys
+
+
+@pytest.mark.parametrize("kind", ["tied_run", "graded_run", "two_runs"])
+def test_index_topk_overflowing_chunks(pkg, kind):
+    """Top blocks packed into a few chunks: chunk lists cannot hold them,
+    the bound check must catch it and the exact path must be used."""
+    n_blk = 262080
+    runs = {"tied_run": [(100003, 700, 8.0, 0.0)],
+            "graded_run": [(5000, 600, 6.0, 2.0**-6)],
+            "two_runs": [(0, 300, 7.0, 0.0), (262080 - 400, 400, 7.0, 0.0)]}[kind]
+    _print_case("index_topk_overflow", kind=kind)
+    keys_np = _planted(n_blk, runs, 47)
+    keys = qc.to_dev(keys_np).unsqueeze(0)  # unit dim with a real stride
+    q = np.zeros((1, 1, 128), dtype=np.uint16)
+    q[0, 0, 0] = 0x3F80  # 1.0: score = key dimension 0, exactly
+    q_idx = qc.to_dev(q)
+    ctxs = [4 * n_blk]
+    fused = _run_fused(pkg, ctxs, [0], keys, q_idx)
+    _check(pkg, ctxs, [0], keys, q_idx, fused)
+    s = fused[0][0, :n_blk].cpu().numpy()
+    assert np.array_equal(s, orc.bf16_to_f64(keys_np[:, 0]).astype(np.float32))
+
+
+def test_index_topk_all_equal_keys(pkg):
+    """Every score equal: the selection is blocks 0..511 (ties to the
+    smaller index), which no chunk list alone can show."""
+    n_blk = 262080
+    keys = torch.full((1, n_blk, 128), 0.5, dtype=torch.bfloat16, device="cuda")
+    q_idx = qc.to_dev(qc.bits(48, 1, (1, 1, 128)))
+    fused = _run_fused(pkg, [4 * n_blk], [0], keys, q_idx)
+    sel = fused[1].cpu().numpy()[0]
+    assert np.array_equal(sel, np.arange(512))
+    _check(pkg, [4 * n_blk], [0], keys, q_idx, fused, check_scores=False)
