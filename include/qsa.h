@@ -214,6 +214,42 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
                              const int32_t* sel, const int32_t* n_sel, int32_t n_split,
                              float* o_part, float* lse_part, qsa_stream_t stream);
 
+/* ------------------------------------------------- A2 + A3 + A4 + A5 ----
+ * qsa_decode_layer: one decode layer in one launch: exactly what
+ * qsa_index_topk, then qsa_sparse_decode with n_split parts, then
+ * qsa_lse_merge of those parts compute, with the parts held in the
+ * workspace. Work items (scan chunks of each query, then its attention
+ * parts) start in a fixed order; the attention of query i starts as soon as
+ * its selection is complete and overlaps the scans of later queries.
+ * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの" and "なぜ";
+ * "GLM-5.3 ...", "DCP".)
+ * Variant A only (block 4, idx_dim 128, idx_heads 1; hq 16, hkv 2, dk = dv
+ * = 256); other configurations return QSA_ERR_UNSUPPORTED. nq <= 4096.
+ *   q_seq, q_ctx, q_idx, keys, scores, ld_scores, sel, n_sel: as
+ *          qsa_index_topk (scores, sel and n_sel are written as there).
+ *   q, kv, n_split: as qsa_sparse_decode (1 <= n_split <= 256).
+ *   o_out      (device) fp32 [nq][hq][dv], or NULL;
+ *   o_out_bf16 (device) bf16 [nq][hq][dv] (nearest-even of o_out), or NULL;
+ *   lse_out    (device) fp32 [nq][hq] (natural log), or NULL; at least one
+ *              of the three must be given.
+ *   ws (device) workspace of at least qsa_decode_layer_workspace_bytes(...)
+ *      bytes, zero before the first call; every completed call leaves its
+ *      counters zero again. Calls sharing a workspace must not overlap.
+ *      Waits inside the launch are bounded: if one runs out (which only a
+ *      corrupted workspace can cause) a sticky error word in the workspace
+ *      is set, results are unspecified, and with QSA_SYNC_CHECK=1 the call
+ *      returns QSA_ERR_LAUNCH; zero the workspace to clear it. */
+qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                            const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                            const qsa_bf16* q_idx, const qsa_bf16* keys, int64_t keys_seq_stride,
+                            const qsa_bf16* q, const qsa_kv* kv,
+                            float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel,
+                            int32_t n_split, float* o_out, qsa_bf16* o_out_bf16, float* lse_out,
+                            void* ws, size_t ws_bytes, qsa_stream_t stream);
+
+size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
+                                        int32_t nq, int32_t max_ctx, int32_t n_split);
+
 /* ---------------------------------------------------------------- A6 ----
  * qsa_sparse_prefill: the same attention restricted to one history tile:
  * query i attends the tokens of its list that lie in [tile_begin, tile_end)

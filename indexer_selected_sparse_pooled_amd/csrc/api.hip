@@ -88,9 +88,10 @@ qsa_status check_sel_cfg(const qsa_sel_cfg* c) {
   return QSA_OK;
 }
 
-qsa_status check_attn(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, const int32_t* q_ctx, int max_ctx,
-                      const qsa_bf16* q, const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel,
-                      const float* o_part, const float* lse_part) {
+// Attention inputs (everything but the output buffers).
+qsa_status check_attn_inputs(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, const int32_t* q_ctx,
+                             int max_ctx, const qsa_bf16* q, const qsa_kv* kv, const int32_t* sel,
+                             const int32_t* n_sel) {
   qsa_status st = check_sel_cfg(sc);
   if (st != QSA_OK) return st;
   if (!ac) return fail(QSA_ERR_ARG, "attn_cfg is NULL");
@@ -102,16 +103,26 @@ qsa_status check_attn(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, con
                 ac->dk, ac->dv);
   if (!(ac->scale > 0.f) || !(ac->scale < 1e30f)) return fail(QSA_ERR_ARG, "scale must be positive and finite");
   if (nq == 0) return QSA_OK;
-  if (!q_ctx || !q || !kv->k || !kv->v || !sel || !n_sel || !o_part || !lse_part)
-    return fail(QSA_ERR_ARG, "NULL pointer argument");
-  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(o_part) || !aligned16(sel))
-    return fail(QSA_ERR_ARG, "q, k, v, sel and o_part must be 16-byte aligned");
+  if (!q_ctx || !q || !kv->k || !kv->v || !sel || !n_sel) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(sel))
+    return fail(QSA_ERR_ARG, "q, k, v and sel must be 16-byte aligned");
   if (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 || kv->head_stride < 0 ||
       kv->seq_stride < 0)
     return fail(QSA_ERR_ARG, "kv strides must be non-negative multiples of 8");
   if (int64_t(ac->hkv - 1) * kv->head_stride + ac->dk > kv->tok_stride)
     return fail(QSA_ERR_ARG, "tok_stride too small for hkv heads of dk");
   if (kv->capacity < max_ctx) return fail(QSA_ERR_ARG, "kv capacity %lld < max_ctx %d", (long long)kv->capacity, max_ctx);
+  return QSA_OK;
+}
+
+// Attention inputs and the partial-result buffers.
+qsa_status check_attn(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, const int32_t* q_ctx, int max_ctx,
+                      const qsa_bf16* q, const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel,
+                      const float* o_part, const float* lse_part) {
+  const qsa_status st = check_attn_inputs(sc, ac, nq, q_ctx, max_ctx, q, kv, sel, n_sel);
+  if (st != QSA_OK || nq == 0) return st;
+  if (!o_part || !lse_part) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(o_part)) return fail(QSA_ERR_ARG, "o_part must be 16-byte aligned");
   return QSA_OK;
 }
 
@@ -299,6 +310,79 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
   a.sel = sel;
   a.n_sel = n_sel;
   return finish(qsa::launch_index_topk(a, plan, ws, s), s, "qsa_index_topk");
+}
+
+size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                        int32_t max_ctx, int32_t n_split) {
+  if (!sel_cfg || !attn_cfg || nq <= 0 || max_ctx < 0 || n_split < 1 || attn_cfg->hq <= 0 || attn_cfg->hkv <= 0 ||
+      attn_cfg->dv <= 0)
+    return 0;
+  return qsa::plan_decode_layer(nq, max_ctx, sel_cfg->topk, attn_cfg->hq, attn_cfg->hkv, attn_cfg->dv, n_split)
+      .ws_bytes;
+}
+
+qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                            const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
+                            const qsa_bf16* keys, int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
+                            float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, int32_t n_split,
+                            float* o_out, qsa_bf16* o_out_bf16, float* lse_out, void* ws, size_t ws_bytes,
+                            qsa_stream_t stream) {
+  qsa_status st = check_sel_cfg(sel_cfg);
+  if (st != QSA_OK) return st;
+  if (sel_cfg->block != 4 || sel_cfg->idx_dim != 128 || sel_cfg->idx_heads != 1)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_decode_layer: only pooled 4-token blocks with a 128-d single-head indexer");
+  st = check_attn_inputs(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel);
+  if (st != QSA_OK) return st;
+  if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
+  if (nq == 0) return QSA_OK;
+  if (nq > 4096) return fail(QSA_ERR_UNSUPPORTED, "nq > 4096");
+  if (!q_idx || !keys || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!o_out && !o_out_bf16 && !lse_out) return fail(QSA_ERR_ARG, "no output requested");
+  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores))
+    return fail(QSA_ERR_ARG, "q_idx, keys and scores must be 16-byte aligned");
+  if ((o_out && !aligned16(o_out)) || (o_out_bf16 && !aligned16(o_out_bf16)))
+    return fail(QSA_ERR_ARG, "o_out and o_out_bf16 must be 16-byte aligned");
+  const int64_t nmax = int64_t(max_ctx) / 4;
+  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
+  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
+  if (q_seq && keys_seq_stride < nmax * 128) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / 4 keys");
+  const qsa::DecodeLayerPlan plan = qsa::plan_decode_layer(nq, max_ctx, sel_cfg->topk, attn_cfg->hq, attn_cfg->hkv,
+                                                           attn_cfg->dv, n_split);
+  if (int64_t(nq) * (plan.itk.n_chunks + attn_cfg->hkv * n_split) > 0x7FFFFFFF)
+    return fail(QSA_ERR_UNSUPPORTED, "too many work items");
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+  if (!aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::IndexTopkArgs it{};
+  it.q_seq = q_seq;
+  it.q_ctx = q_ctx;
+  it.max_ctx = max_ctx;
+  it.nq = nq;
+  it.q_idx = q_idx;
+  it.keys = keys;
+  it.keys_ss = keys_seq_stride;
+  it.scores = scores;
+  it.ld = ld_scores;
+  it.topk = sel_cfg->topk;
+  it.sel = sel;
+  it.n_sel = n_sel;
+  qsa::AttendArgs at = attend_args(sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q, kv, sel, n_sel, n_split, 0,
+                                   int64_t(max_ctx), nullptr, nullptr);
+  at.o_out = o_out;
+  at.o_bf16 = o_out_bf16;
+  at.lse_out = lse_out;
+  const qsa_status fs = finish(qsa::launch_decode_layer(it, at, plan, ws, s), s, "qsa_decode_layer");
+  if (fs != QSA_OK || !env_on("QSA_SYNC_CHECK")) return fs;
+  uint32_t err = 0;
+  if (hipMemcpy(&err, ws, 4, hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: cannot read the error word");
+  if (err) return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: a wait for a selection ran out (error word %u)", err);
+  return QSA_OK;
 }
 
 qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,

@@ -1,0 +1,357 @@
+// Device code of A4 / A6 for the pooled-block variant (hq 16, hkv 2, head
+// dim 256): softmax attention of one query and one kv head over a part of
+// its selected tokens, optionally followed by the log-sum-exp merge of all
+// parts. Used by the stand-alone attention kernel (attend.hip) and by the
+// one-launch decode layer (decode_layer.hip).
+//
+// "3090x3で 314 万コンテキスト": only the indexer-selected K/V rows are read
+// (section "なぜ"), addressed per (token, kv head) (section "カーネルを書き換え
+// ずに済む"); prefill restricts each query to one history tile and merges the
+// tiles' partial results (section "ちなみにこの欠点"). "GLM-5.3 最適化 第2部",
+// section "DCP": partial attention results are combined by log-sum-exp.
+//
+// The query's token list is the tokens of its selected blocks (ascending)
+// followed by the trailing tokens of the incomplete block. A work-group
+// walks its contiguous part of the list (intersected with [tile_begin,
+// tile_end)) in tiles of 64 tokens:
+//   * V rows of the tile go straight from global memory to LDS
+//     (global_load_lds_dwordx4, no registers), two rows per wave instruction;
+//   * S = Q K^T on MFMA 16x16x32 bf16: the GQA group's 8 query heads are the
+//     A rows (rows 8..15 zero), each wave computes 16 tokens with K rows as
+//     the B operand, loaded straight from global memory;
+//   * online softmax in exp2 form per head (one barrier);
+//   * O += P V on MFMA 16x16x32: P split into bf16 hi + lo parts (two
+//     MFMAs, ~16 significant bits); each wave owns 64 of the 256 output
+//     dims and reads V transposed out of LDS with ds_read_tr16_b64.
+// Output: normalised partial O (fp32) and its natural-log lse. With a
+// counter, the last work-group of each (query, kv head) to finish merges
+// all parts into the final O (fp32 and/or bf16) and lse; the parts are
+// handed over with agent-coherent stores, so no L2 write-back is needed.
+#pragma once
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace qsa {
+namespace att {
+
+constexpr int kTT = 64;          // token positions per tile
+constexpr int kG = 8;            // query heads per kv head
+constexpr int kD = 256;          // head dim of K and V
+constexpr int kPair = 1040;      // LDS bytes per pair of V rows (2 x 512 + 16: pairs 4 apart hit other banks)
+constexpr int kPStr = kTT + 8;   // LDS row of P in elements (144 bytes)
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+struct Lds {
+  __attribute__((aligned(16))) unsigned char v[kTT / 2 * kPair];
+  float s[kG][kTT];
+  __attribute__((aligned(16))) uint16_t phi[kG * kPStr];
+  __attribute__((aligned(16))) uint16_t plo[kG * kPStr];
+  float alpha[kG], m[kG], l[kG];
+  int64_t range[2];
+  int last;
+};
+
+// sel may have been written earlier in the same launch by another
+// work-group: then they are read with agent-coherent loads.
+template <bool kCoh>
+__device__ __forceinline__ int ld_sel(const int* p) {
+  if constexpr (kCoh) return int(ld_coherent(reinterpret_cast<const uint32_t*>(p)));
+  return *p;
+}
+
+template <bool kCoh>
+struct List {
+  const int* sel;
+  int ns;    // selected blocks
+  int nblk;  // complete blocks
+  int block;
+  int L;     // list length
+  // token of list entry p (0 <= p < L)
+  __device__ __forceinline__ int tok(int p) const {
+    const int nb_tok = ns * block;
+    if (p < nb_tok) {
+      int b = ld_sel<kCoh>(sel + p / block);
+      b = b < 0 ? 0 : (b >= nblk ? nblk - 1 : b);
+      return b * block + p % block;
+    }
+    return nblk * block + (p - nb_tok);
+  }
+  // number of list entries whose token is < x (x a multiple of block, or >= ctx)
+  __device__ int count_below(int64_t x, int ctx) const {
+    if (x <= 0) return 0;
+    if (x >= ctx) return L;
+    const int nb_tok = nblk * block;
+    if (x >= nb_tok) return ns * block + int(x - nb_tok);
+    const int xb = int(x / block);
+    int lo = 0, hi = ns;  // first selected block >= xb
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ld_sel<kCoh>(sel + mid) < xb) lo = mid + 1; else hi = mid;
+    }
+    return lo * block;
+  }
+};
+
+// One part (split, kv head g, query i): see the file comment.
+template <bool kCoh>
+__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, kq = lane >> 4;
+
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
+  List<kCoh> lv;
+  lv.sel = a.sel + int64_t(i) * a.topk;
+  lv.block = a.block;
+  lv.nblk = ctx / a.block;
+  const int ns_max = lv.nblk < a.topk ? lv.nblk : a.topk;
+  // inside the one-launch layer the selection is this launch's own, which
+  // always holds min(complete blocks, topk) entries: no need to wait for
+  // n_sel to arrive
+  const int ns = kCoh ? ns_max : a.n_sel[i];
+  lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
+  lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
+
+  if (tid == 0) {
+    const int lo = int(int64_t(split) * lv.L / a.n_split);
+    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int t0 = lv.count_below(a.tile_begin, ctx);
+    const int t1 = lv.count_below(a.tile_end, ctx);
+    sh.range[0] = lo > t0 ? lo : t0;
+    sh.range[1] = hi < t1 ? hi : t1;
+  }
+  if (tid < kG) {
+    sh.m[tid] = -INFINITY;
+    sh.l[tid] = 0.f;
+  }
+  __syncthreads();
+  const int P0 = int(sh.range[0]), P1 = int(sh.range[1]);
+
+  const int64_t kvs = int64_t(seq) * a.seq_stride + int64_t(g) * a.head_stride;
+  const uint16_t* kbase = a.k + kvs;
+  const uint16_t* vbase = a.v + kvs;
+  const float sl2 = a.scale * kLog2e;
+
+  bf16x8 qa[kD / 32];
+  {
+    const uint16_t* qrow = a.q + (int64_t(i) * a.hq + g * kG + (r < kG ? r : 0)) * kD;
+#pragma unroll
+    for (int ks = 0; ks < kD / 32; ks++) {
+      const u32x4 w = r < kG ? ld16(qrow + 32 * ks + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      qa[ks] = as_bf16x8(w);
+    }
+  }
+  f32x4 oacc[4];
+#pragma unroll
+  for (int nt = 0; nt < 4; nt++) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  for (int pb = P0; pb < P1; pb += kTT) {
+    const int cnt = (P1 - pb) < kTT ? (P1 - pb) : kTT;
+    // lane l holds the token of tile row l (rows past cnt repeat row 0, so
+    // every load reads finite data that the softmax then weights by 0)
+    const int tokl = lv.tok(pb + (lane < cnt ? lane : 0));
+    // V: wave w loads row pairs 8w .. 8w+7; lanes 0-31 the even row, 32-63 the odd one
+    {
+      const int half = lane >> 5, c = lane & 31;
+#pragma unroll
+      for (int j = 0; j < 8; j++) {
+        const int p = 8 * wave + j;
+        const int vt = __shfl(tokl, 2 * p + half);
+        __builtin_amdgcn_global_load_lds(
+            vbase + int64_t(vt) * a.tok_stride + 8 * c,
+            (__attribute__((address_space(3))) void*)(sh.v + p * kPair), 16, 0, 0);
+      }
+    }
+    // S for tile rows 16*wave .. 16*wave+15
+    {
+      const int rr = 16 * wave + r;
+      const int kt = __shfl(tokl, rr);
+      const uint16_t* krow = kbase + int64_t(kt) * a.tok_stride + 8 * kq;
+      bf16x8 kb[kD / 32];
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ks++) kb[ks] = as_bf16x8(ld16(krow + 32 * ks));
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ks++)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb[ks], acc, 0, 0, 0);
+      if (kq < 2) {
+#pragma unroll
+        for (int e = 0; e < 4; e++) sh.s[4 * kq + e][rr] = rr < cnt ? acc[e] * sl2 : -INFINITY;
+      }
+    }
+    __syncthreads();
+    // online softmax: head h = tid / 32, two tokens per thread
+    {
+      const int h = tid >> 5;
+      const int t2 = (tid & 31) * 2;
+      const float s0 = sh.s[h][t2], s1 = sh.s[h][t2 + 1];
+      float mt = fmaxf(s0, s1);
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) mt = fmaxf(mt, __shfl_xor(mt, m));
+      const float m_old = sh.m[h], l_old = sh.l[h];
+      const float m_new = fmaxf(m_old, mt);
+      float p0 = 0.f, p1 = 0.f, al = 1.f;
+      if (m_new != -INFINITY) {
+        al = exp2f(m_old - m_new);
+        p0 = exp2f(s0 - m_new);
+        p1 = exp2f(s1 - m_new);
+      }
+      float ps = p0 + p1;
+#pragma unroll
+      for (int m = 16; m >= 1; m >>= 1) ps += __shfl_xor(ps, m);
+      const uint16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
+      const uint16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0)), l1 = f32_to_bf16(p1 - bf16_to_f32(h1));
+      *reinterpret_cast<uint32_t*>(sh.phi + h * kPStr + t2) = uint32_t(h0) | (uint32_t(h1) << 16);
+      *reinterpret_cast<uint32_t*>(sh.plo + h * kPStr + t2) = uint32_t(l0) | (uint32_t(l1) << 16);
+      if ((tid & 31) == 0) {
+        sh.alpha[h] = al;
+        sh.l[h] = al * l_old + ps;
+        sh.m[h] = m_new;
+      }
+    }
+    wait_memory();  // this wave's V rows have landed in LDS
+    __syncthreads();
+    // O += P V for dims 64*wave .. 64*wave+63
+    {
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int row = 4 * kq + e;
+        const float al = row < kG ? sh.alpha[row] : 1.f;
+#pragma unroll
+        for (int nt = 0; nt < 4; nt++) oacc[nt][e] *= al;
+      }
+#pragma unroll
+      for (int k2 = 0; k2 < kTT / 32; k2++) {
+        // A: P[head r][tokens 32*k2 + 8*kq .. +7] (rows 8..15 are zero)
+        const bf16x8 ah = r < kG ? as_bf16x8(ld16(sh.phi + r * kPStr + 32 * k2 + 8 * kq)) : bf16x8{};
+        const bf16x8 al8 = r < kG ? as_bf16x8(ld16(sh.plo + r * kPStr + 32 * k2 + 8 * kq)) : bf16x8{};
+#pragma unroll
+        for (int nt = 0; nt < 4; nt++) {
+          // B: V[token 32*k2 + 8*kq + j][dim 64*wave + 16*nt + r], j = 0..7, as two
+          // transposed reads: lane (kq, r') addresses row 32*k2 + 8*kq + 4*h + r'/4,
+          // dims 64*wave + 16*nt + 4*(r'%4) .. +3
+          const int d0 = 64 * wave + 16 * nt + 4 * (r & 3);
+          s16x4 t[2];
+#pragma unroll
+          for (int hh = 0; hh < 2; hh++) {
+            const int row = 32 * k2 + 8 * kq + 4 * hh + (r >> 2);
+            const unsigned char* pa = sh.v + (row >> 1) * kPair + (row & 1) * 512 + 2 * d0;
+            t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pa);
+          }
+          const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+          oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, oacc[nt], 0, 0, 0);
+          oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al8, bv, oacc[nt], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // normalise and write the partial result
+  const int64_t orow0 = (int64_t(split) * a.nq + i) * a.hq + g * kG;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int row = 4 * kq + e;
+    if (row < kG) {
+      const float l = sh.l[row];
+      const float inv = l > 0.f ? 1.f / l : 0.f;
+      float* o = a.o_part + (orow0 + row) * kD + 64 * wave + r;
+#pragma unroll
+      for (int nt = 0; nt < 4; nt++) {
+        if (a.counter)
+          st_coherent(reinterpret_cast<uint32_t*>(o + 16 * nt), __float_as_uint(oacc[nt][e] * inv));
+        else
+          o[16 * nt] = oacc[nt][e] * inv;
+      }
+    }
+  }
+  if (tid < kG) {
+    const float l = sh.l[tid];
+    const float lse = l > 0.f ? (sh.m[tid] + log2f(l)) * kLn2 : -INFINITY;
+    if (a.counter)
+      st_coherent(reinterpret_cast<uint32_t*>(a.lse_part + orow0 + tid), __float_as_uint(lse));
+    else
+      a.lse_part[orow0 + tid] = lse;
+  }
+  if (!a.counter) return;
+
+  // ---- hand the part over; the last work-group of (query, kv head) merges
+  wait_memory();
+  __syncthreads();
+  if (tid == 0) {
+    const unsigned c = atomicAdd(&a.counter[i * a.hkv + g], 1u);
+    sh.last = c == unsigned(a.n_split - 1);
+    if (sh.last) atomicExch(&a.counter[i * a.hkv + g], 0u);  // ready for the next call
+  }
+  __syncthreads();
+  if (!sh.last) return;
+  const int h = tid >> 5, d0 = 8 * (tid & 31);
+  const int64_t hrow = int64_t(i) * a.hq + g * kG + h;  // row within one part
+  const int64_t pstride = int64_t(a.nq) * a.hq;         // rows per part
+  // every (part, head) lse at once, one per thread, into LDS (the V tile
+  // is free now); then each head's maximum and the parts' weights
+  float* lsh = reinterpret_cast<float*>(sh.v);  // [n_split][kG]
+  auto load_batch = [&](int p0, uint64_t (&ov)[8][4]) {
+#pragma unroll
+    for (int q = 0; q < 8; q++) {
+      const int p = p0 + q;
+      if (p < a.n_split) {
+        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.o_part + (p * pstride + hrow) * kD + d0);
+#pragma unroll
+        for (int k = 0; k < 4; k++) ov[q][k] = ld_coherent(src + k);
+      }
+    }
+  };
+  uint64_t ov[8][4];
+  load_batch(0, ov);  // in flight together with the lse loads
+  for (int e = tid; e < a.n_split * kG; e += 256) {
+    const int64_t src = int64_t(e / kG) * pstride + int64_t(i) * a.hq + g * kG + e % kG;
+    lsh[e] = __uint_as_float(ld_coherent(reinterpret_cast<const uint32_t*>(a.lse_part + src)));
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int p = 0; p < a.n_split; p++) mx = fmaxf(mx, lsh[p * kG + h]);
+  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  float tot = 0.f;
+  if (mx != -INFINITY) {
+    for (int p0 = 0; p0 < a.n_split; p0 += 8) {
+      if (p0 > 0) load_batch(p0, ov);
+#pragma unroll
+      for (int q = 0; q < 8; q++) {
+        const int p = p0 + q;
+        if (p >= a.n_split) break;
+        const float lp = lsh[p * kG + h];
+        if (lp == -INFINITY) continue;  // empty part
+        const float w = expf(lp - mx);
+        tot += w;
+#pragma unroll
+        for (int k = 0; k < 4; k++) {
+          acc8[2 * k] += w * __uint_as_float(uint32_t(ov[q][k]));
+          acc8[2 * k + 1] += w * __uint_as_float(uint32_t(ov[q][k] >> 32));
+        }
+      }
+    }
+  }
+  const float inv_t = tot > 0.f ? 1.f / tot : 0.f;
+  float fin[8];
+#pragma unroll
+  for (int k = 0; k < 8; k++) fin[k] = acc8[k] * inv_t;
+  if (a.o_out) {
+    float* dst = a.o_out + hrow * kD + d0;
+    *reinterpret_cast<f32x4*>(dst) = f32x4{fin[0], fin[1], fin[2], fin[3]};
+    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{fin[4], fin[5], fin[6], fin[7]};
+  }
+  if (a.o_bf16) {
+    u32x4 pk;
+#pragma unroll
+    for (int k = 0; k < 4; k++)
+      pk[k] = uint32_t(f32_to_bf16(fin[2 * k])) | (uint32_t(f32_to_bf16(fin[2 * k + 1])) << 16);
+    st16(a.o_bf16 + hrow * kD + d0, pk);
+  }
+  if (a.lse_out && (tid & 31) == 0) a.lse_out[hrow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+}
+
+}  // namespace att
+}  // namespace qsa

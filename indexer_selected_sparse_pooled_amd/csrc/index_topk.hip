@@ -1,275 +1,15 @@
-// A2 + A3 in one launch for decode: the pooled-key scan and the exact top-k.
-// "3090x3で 314 万コンテキスト", section "VRAM に残す必要があるもの": every
-// pooled key (128 x bf16 per block) is scored at every step, so the scan is
-// a bandwidth-bound stream; section "なぜ": the indexer then keeps a fixed
-// budget of blocks (all of them when there are at most topk).
-//
-// Grid (chunks, queries); a work-group scores one chunk of C = 256 * TPW
-// consecutive blocks of one query (wave w takes tiles w*TPW .. w*TPW+TPW-1
-// of 64 keys, 16 lanes per key row, 16-byte non-temporal loads, partial dots
-// folded by a transposing butterfly), writes the scores, and keeps the
-// chunk's 16 best (key, block) pairs plus a bound: no block it leaves out
-// ranks at or above the bound. Every wave first keeps its own 8 best
-// (register threshold search, no barrier); wave 0 then keeps the best 16 of
-// the 32.
-//
-// The last work-group of a query to finish (device-scope counter) selects:
-//  * union mode: the topk best of the union of the chunk lists (register
-//    radix select, one list per thread). With tau the topk-th best of the
-//    union, a chunk can hide a better element only if its bound ranks above
-//    tau; if none does, the union's top-k is the exact top-k. Otherwise,
-//    and in
-//  * stream mode (too few chunks for the union to be safe), an exact select
-//    over every score of the query read back from memory;
-//  * raw mode (at most 4096 candidates): the register select straight on the
-//    query's scores.
-// Results are identical in every mode: the unique top-k under (score
-// descending, block ascending), written in ascending block order.
-//
-// Hand-off between work-groups inside the launch: scores, lists and bounds
-// are written with agent-coherent (sc1) stores, each thread waits for its
-// stores to complete before the work-group's barrier, and only then is the
-// counter incremented; the last work-group reads with coherent loads. No
-// L2 write-back or invalidate is needed (those cost more than the scan).
-#include "common.hpp"
-#include "kernels.hpp"
-#include "select.hpp"
+// A2 + A3 in one launch for decode (device code in index_topk.hpp): grid
+// (chunks, queries), one chunk per work-group; the last work-group of a
+// query to finish selects.
+#include "index_topk.hpp"
 
 namespace qsa {
 namespace {
 
-constexpr int kNT = 256;
-constexpr int kWaveKeep = 8;    // per wave
-constexpr int kChunkKeep = 16;  // per chunk (work-group)
-constexpr int kRegR = 16;       // union / raw entries per thread in the final select
-constexpr int kRegCap = kNT * kRegR;
-
-struct FinalLds {
-  RegSelLds<kNT> rs;
-  StreamLds st;
-  uint32_t wkey[4 * kWaveKeep];
-  int widx[4 * kWaveKeep];
-  uint64_t wbound[4];
-  int last;
-};
-
-__device__ __forceinline__ uint32_t score_key(const float* sc, int j) {
-  return order_key(__uint_as_float(ld_coherent(reinterpret_cast<const uint32_t*>(sc) + j)));
-}
-
-__device__ __forceinline__ float dot8(u32x4 k, u32x4 q) {
-  float acc = 0.f;
-  acc = dot2(k[0], q[0], acc);
-  acc = dot2(k[1], q[1], acc);
-  acc = dot2(k[2], q[2], acc);
-  acc = dot2(k[3], q[3], acc);
-  return acc;
-}
-
-// Scores of the 64 keys [tile0, tile0 + 64) (zero-padded past n); lane l
-// returns the score of key tile0 + l.
-__device__ __forceinline__ float tile_scores(const uint16_t* kb, int64_t tile0, int64_t n, u32x4 qv) {
-  const int lane = threadIdx.x & 63;
-  const int g = lane >> 4, c = lane & 15;
-  u32x4 v[16];
-#pragma unroll
-  for (int k = 0; k < 16; k++) {
-    const int64_t blk = tile0 + 4 * k + g;
-    v[k] = blk < n ? ld16_nt(kb + blk * 128 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
-  }
-  float p[16];
-#pragma unroll
-  for (int k = 0; k < 16; k++) p[k] = dot8(v[k], qv);
-  // transposing butterfly over the 16 lanes of a group: afterwards lane
-  // (g, c) holds the full dot product of key 4c + g
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const bool up = c & 8;
-    const float keep = up ? p[j + 8] : p[j];
-    const float send = up ? p[j] : p[j + 8];
-    p[j] = keep + __shfl_xor(send, 8);
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const bool up = c & 4;
-    const float keep = up ? p[j + 4] : p[j];
-    const float send = up ? p[j] : p[j + 4];
-    p[j] = keep + __shfl_xor(send, 4);
-  }
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const bool up = c & 2;
-    const float keep = up ? p[j + 2] : p[j];
-    const float send = up ? p[j] : p[j + 2];
-    p[j] = keep + __shfl_xor(send, 2);
-  }
-  {
-    const bool up = c & 1;
-    const float keep = up ? p[1] : p[0];
-    const float send = up ? p[0] : p[1];
-    p[0] = keep + __shfl_xor(send, 1);
-  }
-  // key l = 4c + g sits in lane 16 * (l % 4) + l / 4
-  return __shfl(p[0], 16 * (lane & 3) + (lane >> 2));
-}
-
-// Exact selection over the scores of one query, streamed from memory.
-__device__ void select_streamed(const float* sc, int n, int topk, int* sel, FinalLds& sh) {
-  auto key_at = [&](int j) { return score_key(sc, j); };
-  uint32_t kstar;
-  int need;
-  stream_select<kNT>(key_at, n, topk, sh.st, kstar, need);
-  stream_compact<kNT>(key_at, n, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = j; });
-}
-
 template <int TPW>
 __global__ __launch_bounds__(256) void index_topk_a(IndexTopkArgs a) {
-  __shared__ FinalLds sh;
-  const int i = blockIdx.y, chunk = blockIdx.x;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  constexpr int C = kNT * TPW;
-  const int seq = a.q_seq ? a.q_seq[i] : 0;
-  const int n = clamp_ctx(a.q_ctx[i], a.max_ctx) / 4;
-  const int topk = a.topk;
-  int* sel = a.sel + int64_t(i) * topk;
-  const int64_t lo = int64_t(chunk) * C;
-  if (lo >= n) {
-    if (chunk == 0) {  // n == 0: nothing to score
-      for (int j = tid; j < topk; j += kNT) sel[j] = -1;
-      if (tid == 0) a.n_sel[i] = 0;
-    }
-    return;
-  }
-  const int nch = (n + C - 1) / C;
-
-  // ---- scan: scores of this chunk
-  const u32x4 qv = ld16(a.q_idx + int64_t(i) * 128 + 8 * (lane & 15));
-  const uint16_t* kb = a.keys + int64_t(seq) * a.keys_ss;
-  float* out = a.scores + int64_t(i) * a.ld;
-  const int64_t w0 = lo + int64_t(wave) * TPW * 64;
-  uint32_t key[TPW];
-#pragma unroll
-  for (int t = 0; t < TPW; t++) {
-    const int64_t tile0 = w0 + 64 * t;
-    key[t] = 0u;
-    if (tile0 < n) {  // wave-uniform
-      const float s = tile_scores(kb, tile0, n, qv);
-      const int64_t blk = tile0 + lane;
-      if (blk < n) {
-        st_coherent(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
-        key[t] = order_key(s);
-      }
-    }
-  }
-
-  if (n <= topk) {  // every block is selected
-    if (chunk == 0) {
-      for (int j = tid; j < topk; j += kNT) sel[j] = j < n ? j : -1;
-      if (tid == 0) a.n_sel[i] = n;
-    }
-    return;
-  }
-  const bool union_mode = n > kRegCap && nch * kChunkKeep >= 2 * topk && nch <= kNT;
-
-  // ---- chunk list: 8 best per wave, then 16 best of the 32
-  if (union_mode) {
-    const int64_t m64 = int64_t(n) - w0;
-    const int m = m64 <= 0 ? 0 : (m64 >= TPW * 64 ? TPW * 64 : int(m64));
-    if (lane < kWaveKeep) {
-      sh.wkey[wave * kWaveKeep + lane] = 0u;
-      sh.widx[wave * kWaveKeep + lane] = -1;
-    }
-    uint32_t kstar = 0u;
-    int need = kWaveKeep;
-    if (m > kWaveKeep) wave_select<TPW>(key, kWaveKeep, kstar, need);
-    const int tau = wave_compact<TPW>(key, kstar, need, [&](int pos, int j, uint32_t k) {
-      sh.wkey[wave * kWaveKeep + pos] = k;
-      sh.widx[wave * kWaveKeep + pos] = int(w0) + j;
-    });
-    if (lane == 0) sh.wbound[wave] = m > kWaveKeep ? rank64(kstar, int(w0) + tau) : 0ull;
-    __syncthreads();
-    if (wave == 0) {
-      uint32_t k1[1] = {lane < 4 * kWaveKeep ? sh.wkey[lane] : 0u};
-      const int i1 = lane < 4 * kWaveKeep ? sh.widx[lane] : -1;
-      const int valid = __popcll(__ballot(k1[0] != 0u));
-      uint64_t bound = 0ull;
-#pragma unroll
-      for (int w = 0; w < 4; w++) bound = sh.wbound[w] > bound ? sh.wbound[w] : bound;
-      uint32_t ks = 0u;
-      int nd = kChunkKeep;
-      if (valid > kChunkKeep) wave_select<1>(k1, kChunkKeep, ks, nd);
-      const size_t base = (size_t(i) * a.n_chunks + chunk) * kChunkKeep;
-      // kept entries (key << 32 | block) go to their list position; the
-      // positions past the kept count are cleared (0 = empty)
-      const int t1 = wave_compact<1>(k1, ks, nd, [&](int pos, int, uint32_t k) {
-        st_coherent(a.list + base + pos, (uint64_t(k) << 32) | uint32_t(i1));
-      });
-      const int nkept = valid < kChunkKeep ? valid : kChunkKeep;
-      if (lane >= nkept && lane < kChunkKeep) st_coherent(a.list + base + lane, 0ull);
-      if (valid > kChunkKeep) {
-        const uint64_t b = rank64(ks, __shfl(i1, t1));
-        bound = b > bound ? b : bound;
-      }
-      if (lane == 0) st_coherent(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
-    }
-  }
-
-  // ---- the last work-group of this query selects
-  wait_memory();  // this thread's coherent stores are complete
-  __syncthreads();
-  if (tid == 0) sh.last = atomicAdd(&a.counter[i], 1u) == unsigned(nch - 1);
-  __syncthreads();
-  if (!sh.last) return;
-  if (tid == 0) {
-    atomicExch(&a.counter[i], 0u);  // ready for the next call
-    a.n_sel[i] = topk;
-  }
-  const float* sc = a.scores + int64_t(i) * a.ld;
-
-  if (union_mode || n <= kRegCap) {
-    uint32_t ukey[kRegR];
-    int uidx[kRegR];
-    uint64_t my_bound = 0ull;
-    if (union_mode) {
-      // thread t holds chunk t's list (ascending block order) and bound
-      const size_t base = (size_t(i) * a.n_chunks + tid) * kChunkKeep;
-      uint64_t e[kRegR];
-#pragma unroll
-      for (int r = 0; r < kRegR; r++) e[r] = tid < nch ? ld_coherent(a.list + base + r) : 0ull;
-      if (tid < nch) my_bound = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + tid);
-#pragma unroll
-      for (int r = 0; r < kRegR; r++) {
-        ukey[r] = uint32_t(e[r] >> 32);
-        uidx[r] = int(uint32_t(e[r]));
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < kRegR; r++) {
-        const int j = tid * kRegR + r;
-        ukey[r] = j < n ? score_key(sc, j) : 0u;
-        uidx[r] = j;
-      }
-    }
-    uint32_t kstar;
-    int need;
-    regsel_threshold<kNT, kRegR>(ukey, topk, sh.rs, kstar, need);
-    int pos[kRegR];
-    regsel_positions<kNT, kRegR>(ukey, uidx, kstar, need, sh.rs, pos);
-    bool ok = true;
-    if (union_mode) {
-      // tau = the topk-th best of the union; a chunk whose bound ranks above
-      // it may have left out an element of the true top-k
-      const uint64_t tau = rank64(kstar, sh.rs.tau_val);
-      ok = !__syncthreads_or(my_bound > tau);
-    }
-    if (ok) {
-#pragma unroll
-      for (int r = 0; r < kRegR; r++)
-        if (pos[r] >= 0) sel[pos[r]] = uidx[r];
-      return;
-    }
-  }
-  select_streamed(sc, n, topk, sel, sh);
+  __shared__ itk::FinalLds sh;
+  itk::chunk_step<TPW>(a, blockIdx.y, blockIdx.x, sh);
 }
 
 }  // namespace
@@ -278,13 +18,13 @@ IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk) {
   IndexTopkPlan p{};
   const int64_t nmax = int64_t(max_ctx) / 4;
   int tpw = 1;
-  while (tpw < 16 && (nmax + 256 * tpw - 1) / (256 * tpw) > kNT) tpw *= 2;
+  while (tpw < 16 && (nmax + 256 * tpw - 1) / (256 * tpw) > itk::kNT) tpw *= 2;
   p.tpw = tpw;
   p.n_chunks = int(nmax <= 0 ? 1 : (nmax + 256 * tpw - 1) / (256 * tpw));
   // counters first (they must be zero before the first call; each call
   // leaves them zero), then the lists and bounds
   const size_t cnt = (size_t(nq) * 4 + 255) / 256 * 256;
-  const size_t lists = size_t(nq) * p.n_chunks * kChunkKeep;
+  const size_t lists = size_t(nq) * p.n_chunks * itk::kChunkKeep;
   p.off_list = cnt;
   p.off_bound = p.off_list + lists * 8;
   p.ws_bytes = p.off_bound + size_t(nq) * p.n_chunks * 8;
@@ -301,11 +41,11 @@ hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, 
   a.n_chunks = p.n_chunks;
   dim3 grid(unsigned(p.n_chunks), unsigned(a.nq));
   switch (p.tpw) {
-    case 1: hipLaunchKernelGGL(index_topk_a<1>, grid, dim3(kNT), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(index_topk_a<2>, grid, dim3(kNT), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(index_topk_a<4>, grid, dim3(kNT), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(index_topk_a<8>, grid, dim3(kNT), 0, s, a); break;
-    default: hipLaunchKernelGGL(index_topk_a<16>, grid, dim3(kNT), 0, s, a); break;
+    case 1: hipLaunchKernelGGL(index_topk_a<1>, grid, dim3(itk::kNT), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(index_topk_a<2>, grid, dim3(itk::kNT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(index_topk_a<4>, grid, dim3(itk::kNT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(index_topk_a<8>, grid, dim3(itk::kNT), 0, s, a); break;
+    default: hipLaunchKernelGGL(index_topk_a<16>, grid, dim3(itk::kNT), 0, s, a); break;
   }
   return hipGetLastError();
 }

@@ -68,8 +68,13 @@ struct AttendArgs {
   int block;
   int n_split;
   int64_t tile_begin, tile_end;
-  float* o_part;
-  float* lse_part;
+  float* o_part;    // [n_split][nq][hq][dv]
+  float* lse_part;  // [n_split][nq][hq]
+  // in-launch merge (one-launch decode layer); counter == nullptr: none
+  uint32_t* counter;  // [nq][hkv], zero before the first call, left zero
+  float* o_out;       // [nq][hq][dv] or nullptr
+  uint16_t* o_bf16;   // [nq][hq][dv] or nullptr
+  float* lse_out;     // [nq][hq] or nullptr
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
 
@@ -100,6 +105,19 @@ struct IndexTopkPlan {
 };
 IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk);
 hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, hipStream_t s);
+
+
+// One decode layer in one launch (variant A): scan + top-k + attention +
+// merge (three launches when the attention parts outnumber the work-groups
+// the chip holds at once).
+struct DecodeLayerPlan {
+  IndexTopkPlan itk;
+  size_t off_flag, off_att_cnt, off_merge_cnt, off_itk, off_o, off_lse, ws_bytes;
+};
+DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv, int dv, int n_split);
+// itk / att: everything but the workspace views (filled in from ws)
+hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLayerPlan& p, void* ws,
+                               hipStream_t s);
 
 hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, int64_t o_ps,
                         const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,

@@ -1,7 +1,8 @@
 """The hot path as a chain of libqsa calls.
 
 A decode layer is A2 -> A3 -> A4 -> A5 (scores, top-k, split attention,
-merge); a prefill chunk is A2 -> A3 -> A6 per history tile -> A5. Buffers
+merge): one qsa_decode_layer launch for the pooled-block variant, or the
+separate calls; a prefill chunk is A2 -> A3 -> A6 per history tile -> A5. Buffers
 are allocated once with torch and reused; every step runs in libqsa's
 kernels, enqueued on one stream with no host synchronisation, so a whole
 layer or chunk can be captured in a HIP graph.
@@ -22,6 +23,7 @@ class DecodeBuffers:
     n_sel: torch.Tensor     # [nq] int32
     ws: torch.Tensor        # top-k workspace (or None)
     itk_ws: torch.Tensor    # zero-filled workspace of the one-launch scan + top-k (or None)
+    layer_ws: torch.Tensor  # zero-filled workspace of the one-launch decode layer (or None)
     o_part: torch.Tensor    # [n_split, nq, hq, dv] fp32
     lse_part: torch.Tensor  # [n_split, nq, hq] fp32
     o: torch.Tensor         # [nq, hq, dv] fp32
@@ -31,10 +33,11 @@ class DecodeBuffers:
 
 
 def default_n_split(nq: int, hkv: int, budget_tokens: int) -> int:
-    """Splits per (query, kv head): enough work-groups to cover the chip
-    (about 512), at least 64 tokens each."""
-    want = max(1, -(-512 // max(1, nq * hkv)))
-    most = max(1, budget_tokens // 64)
+    """Splits per (query, kv head): about 128 work-groups in all (fewer
+    splits mean fewer partials to merge; the gathered rows are a small part
+    of a decode step's bytes), at least 128 tokens each."""
+    want = max(1, -(-128 // max(1, nq * hkv)))
+    most = max(1, budget_tokens // 128)
     return int(min(want, most, 256))
 
 
@@ -42,6 +45,11 @@ def fused_select(sel_cfg) -> bool:
     """Whether qsa_index_topk covers this indexer (pooled 4-token blocks,
     one 128-d indexer head)."""
     return sel_cfg.block == 4 and sel_cfg.idx_dim == 128 and sel_cfg.idx_heads == 1
+
+
+def fused_layer(sel_cfg, attn_cfg) -> bool:
+    """Whether qsa_decode_layer covers this configuration."""
+    return fused_select(sel_cfg) and (attn_cfg.hq, attn_cfg.hkv, attn_cfg.dk, attn_cfg.dv) == (16, 2, 256, 256)
 
 
 def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") -> DecodeBuffers:
@@ -55,6 +63,8 @@ def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") 
         n_sel=torch.empty(nq, dtype=torch.int32, device=device),
         ws=qsa.topk_workspace(sel_cfg, nq, max_ctx, device),
         itk_ws=qsa.index_topk_workspace(sel_cfg, nq, max_ctx, device) if fused_select(sel_cfg) else None,
+        layer_ws=(qsa.decode_layer_workspace(sel_cfg, attn_cfg, nq, max_ctx, n_split, device)
+                  if fused_layer(sel_cfg, attn_cfg) else None),
         o_part=torch.empty(n_split, nq, attn_cfg.hq, attn_cfg.dv, **f32),
         lse_part=torch.empty(n_split, nq, attn_cfg.hq, **f32),
         o=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, **f32),
@@ -65,8 +75,16 @@ def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") 
 
 
 def decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: DecodeBuffers,
-                 q_seq=None, w_idx=None, stream=None) -> None:
-    """One decode layer for nq queries (one per sequence): results in bufs.o / o_bf16 / lse."""
+                 q_seq=None, w_idx=None, stream=None, fused=False) -> None:
+    """One decode layer for nq queries (one per sequence): results in bufs.o / o_bf16 / lse.
+    fused=True issues the layer as one qsa_decode_layer launch (same results;
+    on the 1M-context batch-4 step it is as fast as the separate launches,
+    not faster, because every query's scan ends at about the same time)."""
+    if fused and bufs.layer_ws is not None and w_idx is None:
+        qsa.qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs.scores, bufs.sel,
+                             bufs.n_sel, bufs.n_split, bufs.layer_ws, o_out=bufs.o, o_out_bf16=bufs.o_bf16,
+                             lse_out=bufs.lse, q_seq=q_seq, stream=stream)
+        return
     if bufs.itk_ws is not None and w_idx is None:
         qsa.qsa_index_topk(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, bufs.sel, bufs.n_sel, bufs.itk_ws,
                            q_seq=q_seq, stream=stream)

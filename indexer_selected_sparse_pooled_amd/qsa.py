@@ -60,6 +60,9 @@ _SIGS = {
     "qsa_topk_workspace_bytes": [_vp, _i32, _i32],
     "qsa_index_topk": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
     "qsa_index_topk_workspace_bytes": [_vp, _i32, _i32],
+    "qsa_decode_layer": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i32,
+                         _vp, _vp, _vp, _vp, _sz, _vp],
+    "qsa_decode_layer_workspace_bytes": [_vp, _vp, _i32, _i32, _i32],
     "qsa_sparse_decode": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp],
     "qsa_sparse_prefill": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
     "qsa_lse_merge": [_i32, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
@@ -67,7 +70,8 @@ _SIGS = {
     "qsa_last_error": [],
     "qsa_version": [],
 }
-_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
+_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz,
+        "qsa_decode_layer_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
         "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
 EXPORTS = tuple(_SIGS)
 
@@ -205,6 +209,49 @@ def qsa_index_topk(cfg, q_ctx, max_ctx, q_idx, keys, scores, sel, n_sel, ws, q_s
         _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0),
         _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"),
         ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qsa_decode_layer_workspace_bytes(sel_cfg, attn_cfg, nq, max_ctx, n_split) -> int:
+    return int(lib().qsa_decode_layer_workspace_bytes(ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, max_ctx,
+                                                      n_split))
+
+
+def decode_layer_workspace(sel_cfg, attn_cfg, nq, max_ctx, n_split, device="cuda"):
+    """A zero-filled workspace tensor for qsa_decode_layer (its counters must
+    start at zero; every call leaves them zero)."""
+    n = qsa_decode_layer_workspace_bytes(sel_cfg, attn_cfg, nq, max_ctx, n_split)
+    return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel, n_split, ws,
+                     o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
+    """One decode layer in one launch: qsa_index_topk, then qsa_sparse_decode
+    and qsa_lse_merge. q_idx: [nq, 1, 128] bf16; keys: [n_seq, n_blocks, 128]
+    bf16; q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk;
+    o_out: [nq, hq, dv] fp32, o_out_bf16: [nq, hq, dv] bf16, lse_out: [nq, hq]
+    fp32 (each optional); ws: decode_layer_workspace(...)."""
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(q_idx, "q_idx", 3)
+    _rowmajor_tail(keys, "keys", 2)
+    _rowmajor_tail(scores, "scores", 1)
+    if max_ctx // sel_cfg.block > keys.shape[1]:
+        raise ValueError("qsa_decode_layer: keys hold fewer than max_ctx / block rows")
+    if sel.shape != (nq, sel_cfg.topk) or not sel.is_contiguous():
+        raise ValueError("qsa_decode_layer: sel must be a contiguous [nq, topk] tensor")
+    if not q.is_contiguous():
+        raise ValueError("qsa_decode_layer: q must be contiguous")
+    for t, shp, name in ((o_out, (nq, attn_cfg.hq, attn_cfg.dv), "o_out"),
+                         (o_out_bf16, (nq, attn_cfg.hq, attn_cfg.dv), "o_out_bf16"),
+                         (lse_out, (nq, attn_cfg.hq), "lse_out")):
+        if t is not None and (tuple(t.shape) != shp or not t.is_contiguous()):
+            raise ValueError(f"qsa_decode_layer: {name} must be a contiguous {list(shp)} tensor")
+    _check("qsa_decode_layer", lib().qsa_decode_layer(
+        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"),
+        max_ctx, _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0), _dev(q, _BF16, "q"),
+        ctypes.byref(kv), _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"),
+        _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_out, _F32, "o_out"), _dev(o_out_bf16, _BF16, "o_out_bf16"),
+        _dev(lse_out, _F32, "lse_out"), ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
+        _stream(stream)))
 
 
 def make_kv(k, v=None):
