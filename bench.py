@@ -37,6 +37,9 @@ BF16_PEAK_TFLOPS = 2500.0
 
 DECODE = dict(name="decode L=1048320 B=4 12 layers, 16 q heads / 2 kv heads, head_dim 256, top-512 of 4-token blocks",
               config_id=3, ctx=1048320, batch=4, layers=12)
+MLA = dict(name="shared-latent variant: 64 q heads over one 576-wide bf16 latent row per token (V = first 512), "
+                "token indexer 4 heads x 64-d ReLU-weighted, top-2048 tokens, context 131072",
+           config_id=5, ctx=131072, batch=8, chunk=2048, tiles=(131072, 32768))
 PREFILL = dict(name="prefill 4096 queries after a 60000-token history, 8192-token tiles", config_id=4,
                history=60000, chunk=4096, tiles=(8192, 1024))
 
@@ -198,9 +201,124 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
 
         ms, wall, g = time_graph(torch, chunk, max(3, steps // 5), max(1, warmup))
         out[tile] = dict(ms=ms, tok_s=C / (ms * 1e-3), tflops=flops["total"] / (ms * 1e-3) / 1e12)
+        if tile == PREFILL["tiles"][0]:
+            r = max(3, steps // 10)
+            t_sc = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_A, q_ctx, ctx_max, q_idx, pooled,
+                                                                     bufs.scores), r)
+            t_tk = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, ctx_max, bufs.scores, bufs.sel,
+                                                                    bufs.n_sel, bufs.ws), r)
+
+            def tiles_only():
+                for t, (a0, a1) in enumerate(bufs.tiles):
+                    pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, bufs.sel, bufs.n_sel, a0, a1,
+                                           bufs.o_tiles[t], bufs.lse_tiles[t])
+
+            t_at = time_launches(torch, tiles_only, r)
+            t_mg = time_launches(torch, lambda: pkg.qsa_lse_merge(bufs.o_tiles, bufs.lse_tiles, o_out=bufs.o,
+                                                                  o_out_bf16=bufs.o_bf16, lse_out=bufs.lse), r)
+            out["breakdown_us"] = {"scores": round(t_sc * 1e3, 1), "topk": round(t_tk * 1e3, 1),
+                                   "attend_all_tiles": round(t_at * 1e3, 1), "merge": round(t_mg * 1e3, 1)}
+            out["attend_tflops"] = round(flops["attention"] / (t_at * 1e-3) / 1e12, 1)
         del g, bufs
         log(f"prefill tile {tile}: {ms:.3f} ms/chunk")
     return out, flops
+
+
+def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
+    """Config 5: batch-8 decode at context 131,072 (indexer scores over every
+    earlier token, top-2048, attention, merge) and a prefill chunk of 2048
+    queries at positions 129,024..131,071 of one sequence."""
+    import numpy as np
+    L, B, C = MLA["ctx"], MLA["batch"], MLA["chunk"]
+    seed = qi.config_seed(MLA["config_id"])
+    dev = "cuda"
+    bf16 = dict(dtype=torch.bfloat16, device=dev)
+    out = {}
+    lat = torch.empty(B, L, 1, 576, **bf16)
+    keys = torch.empty(B, L, 64, **bf16)
+    q = torch.empty(B, 64, 576, **bf16)
+    q_idx = torch.empty(B, 4, 64, **bf16)
+    for s in range(B):
+        for t, kind in ((lat, "latent"), (keys, "raw_key"), (q, "q"), (q_idx, "q_idx")):
+            fill(t[s], seed, qi.stream_id(0, s, kind))
+    w = torch.tensor(np.stack([qi.uniform_f32(seed, qi.stream_id(0, s, "w_idx"), 4) for s in range(B)]), device=dev)
+    kv = pkg.make_kv(lat, lat)
+    q_ctx = torch.full((B,), L, dtype=torch.int32, device=dev)
+    q_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, B, L)
+
+    def dstep():
+        pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, w_idx=w)
+
+    ms, _, g = time_graph(torch, dstep, max(10, steps // 2), warmup)
+    del g
+    reps = max(10, steps // 5)
+    t_sc = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, bufs.scores,
+                                                             q_seq=q_seq, w_idx=w), reps)
+    t_tk = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, bufs.scores, bufs.sel, bufs.n_sel,
+                                                            bufs.ws), reps)
+    t_at = time_launches(torch, lambda: pkg.qsa_sparse_decode(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv, bufs.sel,
+                                                              bufs.n_sel, bufs.n_split, bufs.o_part, bufs.lse_part,
+                                                              q_seq=q_seq), reps)
+    step_bytes = B * bm.mla_decode_unit_bytes(L)
+    out["decode"] = dict(workload=f"decode batch {B}, context {L}, one layer", steps_s=round(1e3 / ms, 1),
+                         ms_per_step=round(ms, 5), hbm_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+                         step_bytes=step_bytes, n_split=bufs.n_split,
+                         breakdown_us={"scores": round(t_sc * 1e3, 2), "topk": round(t_tk * 1e3, 2),
+                                       "attend": round(t_at * 1e3, 2)})
+    log(f"mla decode: {ms:.4f} ms/step")
+    del lat, keys, q, q_idx, kv, bufs
+    torch.cuda.empty_cache()
+    # prefill chunk: queries at positions L - C .. L - 1 of one sequence
+    lat = torch.empty(1, L, 1, 576, **bf16)
+    keys = torch.empty(1, L, 64, **bf16)
+    q = torch.empty(C, 64, 576, **bf16)
+    q_idx = torch.empty(C, 4, 64, **bf16)
+    for t, kind in ((lat, "latent"), (keys, "raw_key"), (q, "q"), (q_idx, "q_idx")):
+        fill(t, seed, qi.stream_id(1, 0, kind))
+    w = torch.tensor(qi.uniform_f32(seed, qi.stream_id(1, 0, "w_idx"), C * 4).reshape(C, 4), device=dev)
+    kv = pkg.make_kv(lat, lat)
+    ctxs = list(range(L - C + 1, L + 1))
+    q_ctx = torch.tensor(ctxs, dtype=torch.int32, device=dev)
+    flops = bm.mla_prefill_flops(ctxs)
+    pre = {}
+    for tile in MLA["tiles"]:
+        pb = pipeline.prefill_buffers(pkg.SEL_B, pkg.ATTN_B, C, L, tile)
+
+        def chunk():
+            pipeline.prefill_chunk(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, pb, w_idx=w)
+
+        ms_p, _, g = time_graph(torch, chunk, max(3, steps // 10), max(1, warmup // 2))
+        del g
+        pre[tile] = dict(ms=ms_p, tok_s=C / (ms_p * 1e-3), tflops=flops["total"] / (ms_p * 1e-3) / 1e12)
+        if tile == MLA["tiles"][0]:
+            r = max(3, steps // 20)
+            t_sc = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, pb.scores,
+                                                                     w_idx=w), r)
+            t_tk = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, pb.scores, pb.sel, pb.n_sel,
+                                                                    pb.ws), r)
+            a0, a1 = pb.tiles[0]
+            t_at = time_launches(torch, lambda: pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv, pb.sel,
+                                                                       pb.n_sel, a0, a1, pb.o_tiles[0],
+                                                                       pb.lse_tiles[0]), r)
+            att_tflops = flops["attention"] / (t_at * 1e-3) / 1e12
+            pre["breakdown_us"] = {"scores": round(t_sc * 1e3, 1), "topk": round(t_tk * 1e3, 1),
+                                   "attend": round(t_at * 1e3, 1)}
+            pre["attend_tflops"] = round(att_tflops, 1)
+        del pb
+        torch.cuda.empty_cache()
+        log(f"mla prefill tile {tile}: {ms_p:.3f} ms/chunk")
+    t0 = MLA["tiles"][0]
+    out["prefill"] = dict(workload=f"prefill {C} queries at context {L - C + 1}..{L}, one sequence",
+                          tok_s=round(pre[t0]["tok_s"], 1), ms_per_chunk=round(pre[t0]["ms"], 4),
+                          tflops=round(pre[t0]["tflops"], 2), mfma_frac=round(pre[t0]["tflops"] / BF16_PEAK_TFLOPS, 4),
+                          useful_gflop=round(flops["total"] / 1e9, 1), history_tile=t0,
+                          attend_tflops=pre["attend_tflops"],
+                          attend_mfma_frac=round(pre["attend_tflops"] / BF16_PEAK_TFLOPS, 4),
+                          breakdown_us=pre["breakdown_us"],
+                          **{f"tile_{t}": {"tok_s": round(pre[t]["tok_s"], 1), "ms_per_chunk": round(pre[t]["ms"], 4)}
+                             for t in MLA["tiles"][1:]})
+    return out
 
 
 def cpu_baseline(qi, orc, bm):
@@ -283,6 +401,9 @@ def main():
     del dec["layers"], dec["bufs"]
     torch.cuda.empty_cache()
     pre, pflops = run_prefill(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
+    torch.cuda.empty_cache()
+    mla = run_mla(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
+    torch.cuda.empty_cache()
 
     from oracle import qsa_oracle as orc
     cpu = cpu_baseline(qi, orc, bm)
@@ -317,7 +438,9 @@ def main():
         "prefill": {"workload": PREFILL["name"], "tok_s": round(t8["tok_s"], 1), "ms_per_chunk": round(t8["ms"], 4),
                     "tflops": round(t8["tflops"], 2), "mfma_frac": round(t8["tflops"] / BF16_PEAK_TFLOPS, 5),
                     "useful_gflop": round(pflops["total"] / 1e9, 2),
+                    "breakdown_us": pre["breakdown_us"], "attend_tflops": pre["attend_tflops"],
                     "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)}},
+        "mla": mla,
         "roofline": {"kernel": "index_topk_a (pooled-key scan + exact top-512, one launch)", "bound": "hbm",
                      "achieved": round(dec["scan_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["scan_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,

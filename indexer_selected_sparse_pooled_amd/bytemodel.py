@@ -54,3 +54,25 @@ def per_token_bytes(layers: int = 12, idx_dim: int = 128, block: int = 4, hkv: i
     pooled = layers * idx_dim * BF16 / block
     rows = layers * (2 * hkv * d * BF16 + idx_dim * BF16)
     return {"pooled": pooled, "kv_and_raw_keys": rows}
+
+
+# Shared-latent variant ("GLM-5.3 最適化 第2部", section "PCP" and footnote 1):
+# token-level indexer of idx_heads x idx_dim, top-2048 tokens, 64 query heads
+# over one 576-wide latent row per token (V = its first 512 columns).
+
+def mla_decode_unit_bytes(ctx: int, topk: int = 2048, idx_dim: int = 64, idx_heads: int = 4, hq: int = 64,
+                          dk: int = 576, dv: int = 512) -> int:
+    """One query in one layer: every earlier token's indexer key, the indexer
+    query and head weights, the selected latent rows, the query and the bf16
+    output."""
+    s = attended_tokens(ctx, 1, topk)
+    return (ctx * idx_dim * BF16 + idx_heads * idx_dim * BF16 + idx_heads * 4 + s * dk * BF16
+            + hq * dk * BF16 + hq * dv * BF16)
+
+
+def mla_prefill_flops(ctxs, topk: int = 2048, idx_dim: int = 64, idx_heads: int = 4, hq: int = 64,
+                      dk: int = 576, dv: int = 512) -> dict:
+    """Useful FLOPs of a prefill chunk of the shared-latent variant."""
+    att = sum(2 * hq * attended_tokens(c, 1, topk) * (dk + dv) for c in ctxs)
+    idx = sum(2 * idx_heads * idx_dim * c for c in ctxs)
+    return {"attention": att, "indexer": idx, "total": att + idx}

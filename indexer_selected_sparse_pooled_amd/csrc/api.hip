@@ -98,7 +98,8 @@ qsa_status check_attn_inputs(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int 
   if (!kv) return fail(QSA_ERR_ARG, "kv is NULL");
   if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
   if (ac->hq <= 0 || ac->hkv <= 0 || ac->hq % ac->hkv != 0) return fail(QSA_ERR_ARG, "hq %% hkv != 0");
-  if (!(ac->hq == 16 && ac->hkv == 2 && ac->dk == 256 && ac->dv == 256))
+  if (!(ac->hq == 16 && ac->hkv == 2 && ac->dk == 256 && ac->dv == 256) &&
+      !(ac->hq == 64 && ac->hkv == 1 && ac->dk == 576 && ac->dv == 512))
     return fail(QSA_ERR_UNSUPPORTED, "attention shape (hq %d, hkv %d, dk %d, dv %d) not compiled", ac->hq, ac->hkv,
                 ac->dk, ac->dv);
   if (!(ac->scale > 0.f) || !(ac->scale < 1e30f)) return fail(QSA_ERR_ARG, "scale must be positive and finite");
@@ -240,7 +241,7 @@ qsa_status qsa_topk_blocks(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_
   if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores < max_ctx / block");
   if (nmax > 8388608) return fail(QSA_ERR_UNSUPPORTED, "more than 8388608 candidates per query");
   const qsa::TopkPlan plan = qsa::plan_topk(nq, max_ctx, cfg->block, cfg->topk);
-  if (plan.chunked && nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535 with more than 32768 candidates");
+  if (plan.chunked && nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535 with more than 8192 candidates");
   if (ws_bytes < plan.ws_bytes || (plan.ws_bytes && !ws))
     return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
   if (ws && !aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");

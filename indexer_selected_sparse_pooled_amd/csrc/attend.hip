@@ -1,9 +1,11 @@
-// A4 / A6: the stand-alone attention launch (device code in attend.hpp).
+// A4 / A6: the stand-alone attention launches (device code in attend.hpp
+// for the pooled-block variant, attend_mla.hpp for the shared latent).
 // One work-group per (query, split) and kv head; each writes one partial
 // (O, lse). Decode combines the splits with qsa_lse_merge; prefill calls it
 // once per history tile ("3090x3で 314 万コンテキスト", section "ちなみにこの
 // 欠点") and merges the tiles the same way.
 #include "attend.hpp"
+#include "attend_mla.hpp"
 
 namespace qsa {
 namespace {
@@ -14,6 +16,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
   att::attend_part<false>(a, split, blockIdx.y, i, sh);
 }
 
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_b(AttendArgs a) {
+  __shared__ mla::Lds sh;
+  const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
+  mla::attend_part<false>(a, split, i, sh);
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
@@ -21,6 +29,10 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.hq == 16 && a.hkv == 2 && a.dk == 256 && a.dv == 256) {
     dim3 grid(unsigned(int64_t(a.nq) * a.n_split), unsigned(a.hkv));
     hipLaunchKernelGGL(attend_a, grid, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
+  if (a.hq == mla::kH && a.hkv == 1 && a.dk == mla::kDK && a.dv == mla::kDV) {
+    hipLaunchKernelGGL(attend_b, dim3(unsigned(int64_t(a.nq) * a.n_split)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

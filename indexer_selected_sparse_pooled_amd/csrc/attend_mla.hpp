@@ -1,0 +1,196 @@
+// Device code of A4 / A6 for the shared-latent variant: 64 query heads attend
+// one 576-wide bf16 latent row per selected token; the first 512 columns of
+// the same row serve as V.
+// "GLM-5.3 最適化 第2部：16基のH200上でのPCP、DCP、およびHybrid HiSparse",
+// section "PCP" (the indexer picks 2,048 tokens per query for sparse MLA;
+// the latent is shared by all 64 heads) and footnote 1 (576-d QK, 512-d PV
+// per latent row); section "DCP" (partials combined by log-sum-exp).
+//
+// Every gathered row serves all 64 heads, so here the contractions are
+// dense enough for MFMA to matter (about 120 FLOP per gathered byte). One
+// work-group per (query, split); wave w owns heads 16w .. 16w+15 and keeps
+// their 576-d queries in registers as MFMA A operands. The part's token list
+// is walked in tiles of 32 tokens:
+//   * the 32 latent rows go straight from global memory to LDS
+//     (global_load_lds_dwordx4) with a row stride of 73 x 16 bytes, so rows
+//     that are read together fall on different banks;
+//   * S = Q K^T on MFMA 16x16x32 bf16, B operands read from LDS (18 k-steps
+//     of 32 per 16-token half);
+//   * online softmax per head on the MFMA result layout (each wave its own
+//     heads, no barrier);
+//   * O += P V on MFMA 16x16x32: P as bf16 hi + lo parts (two MFMAs, ~16
+//     significant bits) through a per-wave LDS tile, V read transposed from
+//     the same LDS rows with ds_read_tr16_b64; each wave accumulates 16
+//     heads x 512 dims.
+// Output: normalised partial O (fp32) and natural-log lse per head.
+#pragma once
+
+#include "attend.hpp"
+
+namespace qsa {
+namespace mla {
+
+constexpr int kH = 64;      // query heads
+constexpr int kDK = 576;    // latent row (QK)
+constexpr int kDV = 512;    // V columns (first kDV of the row)
+constexpr int kTT = 32;     // tokens per tile
+constexpr int kRowC = kDK / 8;          // 16-byte chunks per latent row (72)
+constexpr int kRowL = kRowC + 1;        // LDS chunks per row incl. one pad chunk (73)
+constexpr int kTileC = kTT * kRowL;     // LDS chunks per tile (2336)
+constexpr int kPStr = kTT + 8;          // LDS row of P in elements (80 bytes)
+
+struct Lds {
+  __attribute__((aligned(16))) unsigned char kv[kTileC * 16];
+  __attribute__((aligned(16))) uint16_t p[4][2][16 * kPStr];  // per wave: P hi, lo [head][token]
+  int64_t range[2];
+};
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+template <bool kCoh>
+__device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, kq = lane >> 4;
+
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
+  att::List<kCoh> lv;
+  lv.sel = a.sel + int64_t(i) * a.topk;
+  lv.block = a.block;
+  lv.nblk = ctx / a.block;
+  const int ns_max = lv.nblk < a.topk ? lv.nblk : a.topk;
+  const int ns = kCoh ? ns_max : a.n_sel[i];
+  lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
+  lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
+  if (tid == 0) {
+    const int lo = int(int64_t(split) * lv.L / a.n_split);
+    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int t0 = lv.count_below(a.tile_begin, ctx);
+    const int t1 = lv.count_below(a.tile_end, ctx);
+    sh.range[0] = lo > t0 ? lo : t0;
+    sh.range[1] = hi < t1 ? hi : t1;
+  }
+  __syncthreads();
+  const int P0 = int(sh.range[0]), P1 = int(sh.range[1]);
+
+  const uint16_t* kvbase = a.k + int64_t(seq) * a.seq_stride;
+  const float sl2 = a.scale * kLog2e;
+
+  // A operands: Q[head 16*wave + r][32*ks + 8*kq .. +7]
+  bf16x8 qa[kDK / 32];
+  {
+    const uint16_t* qrow = a.q + (int64_t(i) * kH + 16 * wave + r) * kDK + 8 * kq;
+#pragma unroll
+    for (int ks = 0; ks < kDK / 32; ks++) qa[ks] = as_bf16x8(ld16(qrow + 32 * ks));
+  }
+  float m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    m[e] = -INFINITY;
+    l[e] = 0.f;
+  }
+  f32x4 o[kDV / 16];
+#pragma unroll
+  for (int nt = 0; nt < kDV / 16; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* phi = sh.p[wave][0];
+  uint16_t* plo = sh.p[wave][1];
+
+  for (int pb = P0; pb < P1; pb += kTT) {
+    const int cnt = (P1 - pb) < kTT ? (P1 - pb) : kTT;
+    // lane l < 32 holds the token of tile row l (rows past cnt repeat row 0)
+    const int tokl = lv.tok(pb + ((lane & 31) < cnt ? (lane & 31) : 0));
+    // latent rows -> LDS: wave instruction slot s covers LDS chunks 64s .. 64s+63
+    for (int s = wave; s * 64 < kTileC; s += 4) {
+      const int c = 64 * s + lane;
+      const int row = c / kRowL, col = c % kRowL;
+      const int rt = __shfl(tokl, row < kTT ? row : 0);
+      if (c < kTileC) {
+        const int cc = col < kRowC ? col : 0;  // the pad chunk takes a copy of chunk 0
+        __builtin_amdgcn_global_load_lds(kvbase + int64_t(rt) * a.tok_stride + 8 * cc,
+                                         (__attribute__((address_space(3))) void*)(sh.kv + 1024 * s), 16, 0, 0);
+      }
+    }
+    wait_memory();
+    __syncthreads();
+    // S = Q K^T for the two 16-token halves: lane (kq, r) holds S[head 4kq+e][token 16h + r]
+    f32x4 acc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      acc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const unsigned char* krow = sh.kv + ((16 * hf + r) * kRowL + kq) * 16;
+#pragma unroll
+      for (int ks = 0; ks < kDK / 32; ks++) {
+        const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 64 * ks));
+        acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc[hf], 0, 0, 0);
+      }
+    }
+    // online softmax per head over the tile's 32 tokens (16 lanes x 2 halves)
+    float alpha[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float s0 = r < cnt ? acc[0][e] * sl2 : -INFINITY;
+      const float s1 = 16 + r < cnt ? acc[1][e] * sl2 : -INFINITY;
+      float tm = fmaxf(s0, s1);
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) tm = fmaxf(tm, __shfl_xor(tm, d));
+      const float mn = fmaxf(m[e], tm);
+      float p0 = 0.f, p1 = 0.f;
+      alpha[e] = 1.f;
+      if (mn != -INFINITY) {
+        p0 = exp2f(s0 - mn);
+        p1 = exp2f(s1 - mn);
+        alpha[e] = exp2f(m[e] - mn);
+      }
+      float ps = p0 + p1;
+#pragma unroll
+      for (int d = 1; d < 16; d <<= 1) ps += __shfl_xor(ps, d);
+      l[e] = l[e] * alpha[e] + ps;
+      m[e] = mn;
+      const int row = 4 * kq + e;
+      const uint16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
+      phi[row * kPStr + r] = h0;
+      phi[row * kPStr + 16 + r] = h1;
+      plo[row * kPStr + r] = f32_to_bf16(p0 - bf16_to_f32(h0));
+      plo[row * kPStr + 16 + r] = f32_to_bf16(p1 - bf16_to_f32(h1));
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[nt][e] *= alpha[e];
+    // O += P V: A = P[head r][tokens 8kq .. 8kq+7]; B = V[token 8kq + j][dim 16nt + r]
+    const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(phi + r * kPStr + 8 * kq));
+    const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(plo + r * kPStr + 8 * kq));
+    const unsigned char* vb0 = sh.kv + (8 * kq + (r >> 2)) * kRowL * 16 + 8 * (r & 3);
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++) {
+      s16x4 t[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; hh++)
+        t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) s16x4*)(vb0 + 4 * hh * kRowL * 16 + 32 * nt));
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, o[nt], 0, 0, 0);
+      o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, o[nt], 0, 0, 0);
+      // keep the transposed reads in groups of 8 n-tiles (registers)
+      if (nt % 8 == 7) __builtin_amdgcn_sched_barrier(0);
+    }
+    __syncthreads();  // the tile's rows are read; the next tile may overwrite them
+  }
+
+  // normalise and write the partial result: heads 16*wave + 4kq + e
+  const int64_t orow0 = (int64_t(split) * a.nq + i) * kH + 16 * wave;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int hrow = 4 * kq + e;
+    const float inv = l[e] > 0.f ? 1.f / l[e] : 0.f;
+    float* op = a.o_part + (orow0 + hrow) * kDV + r;
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++) op[16 * nt] = o[nt][e] * inv;
+    if (r == 0) a.lse_part[orow0 + hrow] = l[e] > 0.f ? (m[e] + log2f(l[e])) * kLn2 : -INFINITY;
+  }
+}
+
+}  // namespace mla
+}  // namespace qsa

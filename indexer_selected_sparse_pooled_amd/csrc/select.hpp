@@ -290,19 +290,54 @@ __device__ __forceinline__ void wave_offsets(int a, int b, StreamLds& sh, int& o
 }
 
 // The k-th largest key among key_at(0..n) and need = k - #{key > kstar}.
-// Four 8-bit radix passes, each reading every key once. Requires 1 <= k <= n.
+// Radix passes of up to 8 bits, each reading every key once, that start
+// below the common prefix of the largest and smallest key (one extra read
+// finds them): scores cluster in their top bits, and a pass over bits every
+// key shares would send them all to one histogram bin. Requires
+// 1 <= k <= n.
 template <int NT, class KeyAt>
 __device__ void stream_select(KeyAt key_at, int n, int k, StreamLds& sh, uint32_t& kstar, int& need) {
+  constexpr int NW = NT / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  uint32_t prefix = 0, mask = 0;
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+  for (int j = threadIdx.x; j < n; j += NT) {
+    const uint32_t key = key_at(j);
+    mx = key > mx ? key : mx;
+    mn = key < mn ? key : mn;
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane == 0) {
+    sh.wsum[0][wave] = int(mx);
+    sh.wsum[1][wave] = int(mn);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    const uint32_t x = uint32_t(sh.wsum[0][w]), y = uint32_t(sh.wsum[1][w]);
+    mx = x > mx ? x : mx;
+    mn = y < mn ? y : mn;
+  }
+  __syncthreads();
+  const uint32_t diff = mx ^ mn;
+  if (diff == 0u) {  // every key is equal
+    kstar = mx;
+    need = k;
+    return;
+  }
+  int lo = 32 - __clz(diff);  // bits [lo, 32) are common to every key
+  uint32_t mask = lo >= 32 ? 0u : ~((1u << lo) - 1u);
+  uint32_t prefix = mx & mask;
   int remaining = k;
-  for (int pass = 0; pass < 4; pass++) {
-    const int shift = 24 - 8 * pass;
+  while (lo > 0) {
+    const int width = lo < 8 ? lo : 8;
+    const int shift = lo - width;
+    const uint32_t dmask = (1u << width) - 1u;
     for (int b = threadIdx.x; b < 256; b += NT) sh.hist[b] = 0;
     __syncthreads();
     for (int j = threadIdx.x; j < n; j += NT) {
       const uint32_t key = key_at(j);
-      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      if ((key & mask) == prefix) atomicAdd(&sh.hist[(key >> shift) & dmask], 1u);
     }
     __syncthreads();
     if (wave == 0) {
@@ -332,7 +367,8 @@ __device__ void stream_select(KeyAt key_at, int n, int k, StreamLds& sh, uint32_
     __syncthreads();
     remaining -= sh.above;
     prefix |= uint32_t(sh.digit) << shift;
-    mask |= 0xFFu << shift;
+    mask |= dmask << shift;
+    lo = shift;
     __syncthreads();
   }
   kstar = prefix;
@@ -340,22 +376,49 @@ __device__ void stream_select(KeyAt key_at, int n, int k, StreamLds& sh, uint32_
 }
 
 // Emit, in ascending index order, every j with key > kstar plus the first
-// `need` j with key == kstar: emit(position, j).
+// `need` j with key == kstar: emit(position, j). Each round a thread takes
+// kB consecutive keys, so a block-wide prefix (two barriers) covers NT * kB
+// keys at once.
 template <int NT, class KeyAt, class Emit>
 __device__ void stream_compact(KeyAt key_at, int n, uint32_t kstar, int need, StreamLds& sh, Emit emit) {
-  const uint64_t lt = lanes_below();
+  constexpr int kB = 16;
+  const int lane = threadIdx.x & 63;
   int base_g = 0, base_e = 0;
-  for (int r0 = 0; r0 < n; r0 += NT) {
-    const int j = r0 + threadIdx.x;
-    const uint32_t key = j < n ? key_at(j) : 0u;
-    const bool fg = j < n && key > kstar;
-    const bool fe = j < n && key == kstar;
-    const uint64_t bg = __ballot(fg), be = __ballot(fe);
-    int og, oe, tg, te;
-    wave_offsets<NT>(__popcll(bg), __popcll(be), sh, og, oe, tg, te);
-    const int gb = base_g + og + __popcll(bg & lt);
-    const int eb = base_e + oe + __popcll(be & lt);
-    if (fg || (fe && eb < need)) emit(gb + (eb < need ? eb : need), j);
+  for (int r0 = 0; r0 < n; r0 += NT * kB) {
+    const int j0 = r0 + kB * int(threadIdx.x);
+    uint32_t fg = 0u, fe = 0u;  // bit r: key j0 + r is greater / equal
+#pragma unroll
+    for (int r = 0; r < kB; r++) {
+      const int j = j0 + r;
+      const uint32_t key = j < n ? key_at(j) : 0u;
+      fg |= uint32_t(j < n && key > kstar) << r;
+      fe |= uint32_t(j < n && key == kstar) << r;
+    }
+    const int cg = __popc(fg), ce = __popc(fe);
+    // inclusive scan of (cg, ce) over the wave
+    int ig = cg, ie = ce;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int og = __shfl_up(ig, d), oe = __shfl_up(ie, d);
+      if (lane >= d) {
+        ig += og;
+        ie += oe;
+      }
+    }
+    int wg_off, we_off, tg, te;
+    wave_offsets<NT>(__shfl(ig, 63), __shfl(ie, 63), sh, wg_off, we_off, tg, te);
+    int gb = base_g + wg_off + ig - cg;
+    int eb = base_e + we_off + ie - ce;
+#pragma unroll
+    for (int r = 0; r < kB; r++) {
+      if ((fg >> r) & 1u) {
+        emit(gb + (eb < need ? eb : need), j0 + r);
+        gb++;
+      } else if ((fe >> r) & 1u) {
+        if (eb < need) emit(gb + eb, j0 + r);
+        eb++;
+      }
+    }
     base_g += tg;
     base_e += te;
   }

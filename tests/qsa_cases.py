@@ -110,3 +110,18 @@ def check_attention(o_gpu, lse_gpu, o_ref, lse_ref, o_bf16=None):
         ob = orc.bf16_to_f64(o_bf16)
         live = ~np.isneginf(lse_ref)
         assert np.max(np.abs(ob[live] - o_ref[live]), initial=0.0) <= BF16_TOL_ABS
+
+
+def check_row(gpu_sel, gpu_n, o, lse, ob, ref, ctx, block, topk, q_bits, k_bits, v_bits, scale, dv=None):
+    """One query's selection and attention against the oracle result ref
+    (decode_query). Where the boundary rule tolerated a swap, the attention
+    is checked against the oracle run on the GPU's own selection. Returns
+    True if the selection was bit-identical."""
+    same = check_selection(gpu_sel, gpu_n, ref["scores"], ctx, block, topk)
+    if same:
+        o_ref, lse_ref = ref["o"], ref["lse"]
+    else:
+        toks = orc.selected_tokens(np.asarray(gpu_sel[:gpu_n]), ctx, block)
+        o_ref, lse_ref = orc.attend(q_bits, k_bits, v_bits, toks, scale, dv)
+    check_attention(o, lse, o_ref, lse_ref, ob)
+    return same
