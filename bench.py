@@ -321,6 +321,27 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
     return out
 
 
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_decode_1M_b4_prefill_tile.txt")
+
+
+def counter_traffic(kernel: str, groups: str):
+    """HBM bytes per launch (read + written) of `kernel` with `groups`
+    work-groups from the committed rocprofv3 counter summary, or None if the
+    kernel sources changed since those counters were taken (or none exist)."""
+    from indexer_selected_sparse_pooled_amd.profile_kernels import source_digest
+    if not os.path.exists(COUNTERS):
+        return None
+    lines = open(COUNTERS).read().splitlines()
+    digest = [l.split(":", 1)[1].strip() for l in lines if l.startswith("source digest:")]
+    if not digest or digest[0] != source_digest():
+        return None
+    for l in lines:
+        f = l.split()
+        if len(f) == 7 and f[0] == kernel and f[1] == groups:
+            return int(f[5]) + int(f[6])
+    return None
+
+
 def cpu_baseline(qi, orc, bm):
     """The oracle on one (layer, sequence) unit of the decode workload: scan of
     262,080 pooled keys, top-512 selection, attention over the 2,048 selected
@@ -443,7 +464,8 @@ def main():
         "mla": mla,
         "roofline": {"kernel": "index_topk_a (pooled-key scan + exact top-512, one launch)", "bound": "hbm",
                      "achieved": round(dec["scan_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec["scan_gbs"] / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(dec["scan_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("index_topk_a<4>", "1024"),
                      "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["scan_ms"] * 1e3, 3)},
         "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "wall_s": round(time.time() - t_all, 1),

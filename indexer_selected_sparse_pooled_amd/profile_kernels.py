@@ -1,0 +1,185 @@
+"""Small, fixed workload for hardware-counter runs (rocprofv3 --pmc).
+
+Runs, each `--reps` times, on seeded synthetic inputs already in HBM:
+  * a plain device copy of 256 MiB (torch copy_): the reference that scales
+    the memory counters (it reads and writes exactly 268,435,456 bytes);
+  * one layer of the 1,048,320-token batch-4 decode step: qsa_index_topk
+    (pooled-key scan + exact top-512), qsa_sparse_decode, qsa_lse_merge,
+    and the same layer as one qsa_decode_layer launch;
+  * one history tile of the 4096-query prefill chunk (qsa_sparse_prefill).
+
+Usage (one counter group per run):
+  rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- \
+      python <repo>/indexer_selected_sparse_pooled_amd/profile_kernels.py
+
+Summaries of rocprofv3 CSV output (host only, no GPU):
+  python profile_kernels.py --trace OUT/run_kernel_trace.csv
+  python profile_kernels.py --pmc FETCH/run_counter_collection.csv WRITE/run_counter_collection.csv
+The counter summary scales each memory counter by what it reads for the
+256 MiB copy, so its figures are bytes moved to and from memory.
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import os
+import re
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+COPY_BYTES = 256 << 20
+COPY_KERNEL = "__amd_rocclr_copyBuffer"
+
+
+def kernel_name(raw: str) -> str:
+    n = raw.replace("(anonymous namespace)::", "").replace("qsa::", "")
+    n = re.sub(r"\(.*", "", n).replace("void ", "")
+    return n.strip()[:40]
+
+
+def summarize_trace(path: str) -> str:
+    """Per (kernel, grid): launches and average / min / max duration (us)."""
+    g = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        wg = int(r["Workgroup_Size_X"])
+        key = (kernel_name(r["Kernel_Name"]), f'{int(r["Grid_Size_X"]) // wg}x{r["Grid_Size_Y"]}', wg,
+               r["VGPR_Count"], r["Accum_VGPR_Count"], r["LDS_Block_Size"])
+        g.setdefault(key, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    out = [f"{'kernel':40s} {'grid(wg)':>10s} {'wg':>5s} {'vgpr':>4s} {'agpr':>4s} {'lds':>6s} {'calls':>6s} "
+           f"{'avg_us':>9s} {'min_us':>9s} {'max_us':>9s}"]
+    for (n, grid, wg, v, a, lds), ds in sorted(g.items(), key=lambda kv: -sum(kv[1])):
+        out.append(f"{n:40s} {grid:>10s} {wg:5d} {v:>4s} {a:>4s} {lds:>6s} {len(ds):6d} {sum(ds) / len(ds):9.2f} "
+                   f"{min(ds):9.2f} {max(ds):9.2f}")
+    return "\n".join(out)
+
+
+def _counter(path: str, name: str):
+    g = collections.OrderedDict()
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != name:
+            continue
+        wg = int(r["Workgroup_Size"])
+        key = (kernel_name(r["Kernel_Name"]), f'{int(r["Grid_Size"]) // wg}', wg)
+        g.setdefault(key, []).append(float(r["Counter_Value"]))
+    return g
+
+
+def source_digest() -> str:
+    """sha256 over the library's kernel sources (csrc/*.hip, *.hpp), so a
+    counter summary can tell whether the kernels changed since."""
+    import hashlib
+    d = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".hip", ".hpp")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
+    """Per (kernel, grid): FETCH_SIZE and WRITE_SIZE per dispatch (KiB as
+    read), and bytes after scaling by the copy reference."""
+    f, w = _counter(fetch_csv, "FETCH_SIZE"), _counter(write_csv, "WRITE_SIZE")
+    copy_f = [v for k, v in f.items() if k[0] == COPY_KERNEL]
+    copy_w = [v for k, v in w.items() if k[0] == COPY_KERNEL]
+    if not copy_f or not copy_w:
+        raise SystemExit("no copy reference in the counter files")
+    sf = COPY_BYTES / (1024.0 * sum(copy_f[0]) / len(copy_f[0]))
+    sw = COPY_BYTES / (1024.0 * sum(copy_w[0]) / len(copy_w[0]))
+    out = [f"source digest: {source_digest()}",
+           f"scale: FETCH_SIZE x {sf:.4f}, WRITE_SIZE x {sw:.4f} (the {COPY_BYTES}-byte copy reads and writes "
+           f"{COPY_BYTES} bytes)",
+           f"{'kernel':40s} {'wgs':>8s} {'n':>3s} {'FETCH_KiB':>12s} {'WRITE_KiB':>12s} {'read_B':>14s} "
+           f"{'written_B':>14s}"]
+    for k, fv in f.items():
+        wv = w.get(k, [0.0])
+        fa, wa = sum(fv) / len(fv), sum(wv) / len(wv)
+        out.append(f"{k[0]:40s} {k[1]:>8s} {len(fv):3d} {fa:12.1f} {wa:12.1f} {fa * 1024 * sf:14.0f} "
+                   f"{wa * 1024 * sw:14.0f}")
+    return "\n".join(out)
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--trace", help="summarize a rocprofv3 kernel_trace.csv and exit")
+    ap.add_argument("--pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="summarize two rocprofv3 counter_collection.csv files and exit")
+    args = ap.parse_args()
+    if args.trace:
+        print(summarize_trace(args.trace))
+        return 0
+    if args.pmc:
+        print(summarize_pmc(*args.pmc))
+        return 0
+    import torch
+
+    import indexer_selected_sparse_pooled_amd as pkg
+    import qsa_inputs as qi
+    from indexer_selected_sparse_pooled_amd import pipeline
+    from qsa_inputs.gpu import fill_normal_bf16
+
+    pkg.qsa.lib()
+    dev = "cuda"
+    # reference copy
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    fill_normal_bf16(src, 1, 1)
+    for _ in range(args.reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+    # one decode layer, 1,048,320-token context, batch 4
+    L, B = 1048320, 4
+    seed = qi.config_seed(3)
+    keys = torch.empty(B, L // 4, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(B, L, 2, 256, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(B, L, 2, 256, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(B, 16, 256, dtype=torch.bfloat16, device=dev)
+    q_idx = torch.empty(B, 1, 128, dtype=torch.bfloat16, device=dev)
+    for s in range(B):
+        for t, kind in ((keys, "misc"), (k, "k"), (v, "v"), (q, "q"), (q_idx, "q_idx")):
+            fill_normal_bf16(t[s], seed, qi.stream_id(0, s, kind))
+    kv = pkg.make_kv(k, v)
+    q_ctx = torch.full((B,), L, dtype=torch.int32, device=dev)
+    q_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    bufs = pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, B, L)
+    for _ in range(args.reps):
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq)
+    for _ in range(args.reps):
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, fused=True)
+    torch.cuda.synchronize()
+    del keys, k, v, kv, bufs
+    torch.cuda.empty_cache()
+    # one history tile of the prefill chunk: 4096 queries after 60,000 tokens
+    H, C = 60000, 4096
+    ctx_max = H + C
+    seed = qi.config_seed(4)
+    pooled = torch.empty(1, ctx_max // 4, 128, dtype=torch.bfloat16, device=dev)
+    k = torch.empty(1, ctx_max, 2, 256, dtype=torch.bfloat16, device=dev)
+    v = torch.empty(1, ctx_max, 2, 256, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(C, 16, 256, dtype=torch.bfloat16, device=dev)
+    q_idx = torch.empty(C, 1, 128, dtype=torch.bfloat16, device=dev)
+    for t, kind in ((pooled, "misc"), (k, "k"), (v, "v"), (q, "q"), (q_idx, "q_idx")):
+        fill_normal_bf16(t, seed, qi.stream_id(0, 0, kind))
+    kv = pkg.make_kv(k, v)
+    q_ctx = torch.arange(H + 1, H + C + 1, dtype=torch.int32, device=dev)
+    pb = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, C, ctx_max, 8192)
+    pkg.qsa_index_scores(pkg.SEL_A, q_ctx, ctx_max, q_idx, pooled, pb.scores)
+    pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, ctx_max, pb.scores, pb.sel, pb.n_sel, pb.ws)
+    a0, a1 = pb.tiles[3]
+    for _ in range(args.reps):
+        pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, pb.sel, pb.n_sel, a0, a1,
+                               pb.o_tiles[3], pb.lse_tiles[3])
+    torch.cuda.synchronize()
+    print("profile_kernels: done", flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
