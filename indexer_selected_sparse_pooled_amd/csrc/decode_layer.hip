@@ -155,6 +155,8 @@ hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLa
   itk.list = reinterpret_cast<uint64_t*>(wi + p.itk.off_list);
   itk.list_bound = reinterpret_cast<uint64_t*>(wi + p.itk.off_bound);
   itk.n_chunks = p.itk.n_chunks;
+  itk.keep = p.itk.keep;
+  itk.wkeep = p.itk.wkeep;
   att.counter = reinterpret_cast<uint32_t*>(w + p.off_merge_cnt);
   att.o_part = reinterpret_cast<float*>(w + p.off_o);
   att.lse_part = reinterpret_cast<float*>(w + p.off_lse);

@@ -17,14 +17,21 @@ __global__ __launch_bounds__(256) void index_topk_a(IndexTopkArgs a) {
 IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk) {
   IndexTopkPlan p{};
   const int64_t nmax = int64_t(max_ctx) / 4;
+  // at most 256 chunks per query (a 1M-token context: 1024 blocks per chunk,
+  // 1024 work-groups for 4 queries, all resident at once); more, smaller
+  // chunks (tried: 512 of 512 blocks) were not faster
   int tpw = 1;
   while (tpw < 16 && (nmax + 256 * tpw - 1) / (256 * tpw) > itk::kNT) tpw *= 2;
   p.tpw = tpw;
   p.n_chunks = int(nmax <= 0 ? 1 : (nmax + 256 * tpw - 1) / (256 * tpw));
+  // candidates kept: 8 per wave, 16 per chunk up to 256 chunks, else 8, so
+  // the union never exceeds 4096 entries
+  p.keep = p.n_chunks <= itk::kNT ? itk::kChunkKeep : itk::kChunkKeep / 2;
+  p.wkeep = itk::kWaveKeep;
   // counters first (they must be zero before the first call; each call
   // leaves them zero), then the lists and bounds
   const size_t cnt = (size_t(nq) * 4 + 255) / 256 * 256;
-  const size_t lists = size_t(nq) * p.n_chunks * itk::kChunkKeep;
+  const size_t lists = size_t(nq) * p.n_chunks * p.keep;
   p.off_list = cnt;
   p.off_bound = p.off_list + lists * 8;
   p.ws_bytes = p.off_bound + size_t(nq) * p.n_chunks * 8;
@@ -39,6 +46,8 @@ hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, 
   a.list = reinterpret_cast<uint64_t*>(w + p.off_list);
   a.list_bound = reinterpret_cast<uint64_t*>(w + p.off_bound);
   a.n_chunks = p.n_chunks;
+  a.keep = p.keep;
+  a.wkeep = p.wkeep;
   dim3 grid(unsigned(p.n_chunks), unsigned(a.nq));
   switch (p.tpw) {
     case 1: hipLaunchKernelGGL(index_topk_a<1>, grid, dim3(itk::kNT), 0, s, a); break;

@@ -10,10 +10,10 @@
 // consecutive blocks of one query (wave w takes tiles w*TPW .. w*TPW+TPW-1
 // of 64 keys, 16 lanes per key row, 16-byte non-temporal loads, partial dots
 // folded by a transposing butterfly), writes the scores, and keeps the
-// chunk's 16 best (key, block) pairs plus a bound: no block it leaves out
-// ranks at or above the bound. Every wave first keeps its own 8 best
-// (register threshold search, no barrier); wave 0 then keeps the best 16 of
-// the 32.
+// chunk's best (key, block) pairs (16, or 8 when a query has more than 256
+// chunks) plus a bound: the best block it leaves out. Every wave first keeps
+// its own 8 best (register threshold search, no barrier); wave 0 then keeps
+// the chunk's best of the 32.
 //
 // The last work-group of a query to finish (device-scope counter) selects:
 //  * union mode: the topk best of the union of the chunk lists (register
@@ -54,8 +54,8 @@ __device__ __forceinline__ void publish() {
 
 
 constexpr int kNT = 256;
-constexpr int kWaveKeep = 8;    // per wave
-constexpr int kChunkKeep = 16;  // per chunk (work-group)
+constexpr int kWaveKeep = 8;    // at most, per wave (a.wkeep)
+constexpr int kChunkKeep = 16;  // at most, per chunk (a.keep)
 constexpr int kRegR = 16;       // union / raw entries per thread in the final select
 constexpr int kRegCap = kNT * kRegR;
 
@@ -189,7 +189,8 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     }
     return false;
   }
-  const bool union_mode = n > kRegCap && nch * kChunkKeep >= 2 * topk && nch <= kNT;
+  const int keep = a.keep, wkeep = a.wkeep;
+  const bool union_mode = n > kRegCap && nch * keep >= 2 * topk && nch * keep <= kRegCap;
 
   // ---- chunk list: 8 best per wave, then 16 best of the 32
   if (union_mode) {
@@ -200,13 +201,14 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
       sh.widx[wave * kWaveKeep + lane] = -1;
     }
     uint32_t kstar = 0u;
-    int need = kWaveKeep;
-    if (m > kWaveKeep) wave_select<TPW>(key, kWaveKeep, kstar, need);
-    const int tau = wave_compact<TPW>(key, kstar, need, [&](int pos, int j, uint32_t k) {
+    int need = wkeep;
+    if (m > wkeep) wave_select<TPW>(key, wkeep, kstar, need);
+    wave_compact<TPW>(key, kstar, need, [&](int pos, int j, uint32_t k) {
       sh.wkey[wave * kWaveKeep + pos] = k;
       sh.widx[wave * kWaveKeep + pos] = int(w0) + j;
     });
-    if (lane == 0) sh.wbound[wave] = m > kWaveKeep ? rank64(kstar, int(w0) + tau) : 0ull;
+    const uint64_t wb = wave_best_excluded<TPW>(key, kstar, need, [&](int j) { return int(w0) + j; });
+    if (lane == 0) sh.wbound[wave] = wb;
     __syncthreads();
     if (wave == 0) {
       uint32_t k1[1] = {lane < 4 * kWaveKeep ? sh.wkey[lane] : 0u};
@@ -216,20 +218,18 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
 #pragma unroll
       for (int w = 0; w < 4; w++) bound = sh.wbound[w] > bound ? sh.wbound[w] : bound;
       uint32_t ks = 0u;
-      int nd = kChunkKeep;
-      if (valid > kChunkKeep) wave_select<1>(k1, kChunkKeep, ks, nd);
-      const size_t base = (size_t(i) * a.n_chunks + chunk) * kChunkKeep;
+      int nd = keep;
+      if (valid > keep) wave_select<1>(k1, keep, ks, nd);
+      const size_t base = (size_t(i) * a.n_chunks + chunk) * keep;
       // kept entries (key << 32 | block) go to their list position; the
       // positions past the kept count are cleared (0 = empty)
-      const int t1 = wave_compact<1>(k1, ks, nd, [&](int pos, int, uint32_t k) {
+      wave_compact<1>(k1, ks, nd, [&](int pos, int, uint32_t k) {
         st_coherent(a.list + base + pos, (uint64_t(k) << 32) | uint32_t(i1));
       });
-      const int nkept = valid < kChunkKeep ? valid : kChunkKeep;
-      if (lane >= nkept && lane < kChunkKeep) st_coherent(a.list + base + lane, 0ull);
-      if (valid > kChunkKeep) {
-        const uint64_t b = rank64(ks, __shfl(i1, t1));
-        bound = b > bound ? b : bound;
-      }
+      const int nkept = valid < keep ? valid : keep;
+      if (lane >= nkept && lane < keep) st_coherent(a.list + base + lane, 0ull);
+      const uint64_t b = wave_best_excluded<1>(k1, ks, nd, [&](int) { return i1; });
+      bound = b > bound ? b : bound;
       if (lane == 0) st_coherent(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
     }
   }
@@ -251,12 +251,18 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     int uidx[kRegR];
     uint64_t my_bound = 0ull;
     if (union_mode) {
-      // thread t holds chunk t's list (ascending block order) and bound
-      const size_t base = (size_t(i) * a.n_chunks + tid) * kChunkKeep;
+      // thread t holds union entries 16t .. 16t+15 (chunk-major, each list in
+      // ascending block order), i.e. the lists of chunks 16t/keep .. (16t+15)/keep,
+      // and checks their bounds
+      const size_t base = size_t(i) * a.n_chunks * keep + size_t(tid) * kRegR;
+      const int u = nch * keep;
       uint64_t e[kRegR];
 #pragma unroll
-      for (int r = 0; r < kRegR; r++) e[r] = tid < nch ? ld_coherent(a.list + base + r) : 0ull;
-      if (tid < nch) my_bound = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + tid);
+      for (int r = 0; r < kRegR; r++) e[r] = tid * kRegR + r < u ? ld_coherent(a.list + base + r) : 0ull;
+      for (int c = tid * kRegR / keep; c < (tid + 1) * kRegR / keep && c < nch; c++) {
+        const uint64_t b = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + c);
+        my_bound = b > my_bound ? b : my_bound;
+      }
 #pragma unroll
       for (int r = 0; r < kRegR; r++) {
         ukey[r] = uint32_t(e[r] >> 32);

@@ -94,15 +94,18 @@ struct IndexTopkArgs {
   int topk;
   int* sel;
   int* n_sel;
-  // workspace views (filled by launch_index_topk)
+  // workspace views and list sizes (filled by launch_index_topk)
   uint32_t* counter;
-  uint64_t* list;        // [nq][n_chunks][16] (key << 32 | block), 0 = empty
+  uint64_t* list;        // [nq][n_chunks][keep] (key << 32 | block), 0 = empty
   uint64_t* list_bound;  // [nq][n_chunks]
   int n_chunks;
+  int keep;              // candidates kept per chunk
+  int wkeep;             // candidates kept per wave
 };
 struct IndexTopkPlan {
   int tpw;        // 64-key tiles per wave (chunk = 256 * tpw keys)
   int n_chunks;   // chunks per query at max_ctx
+  int keep, wkeep;
   size_t off_list, off_bound, ws_bytes;
 };
 IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk);

@@ -11,6 +11,10 @@
 namespace qsa {
 namespace {
 
+// ND = ceil(dv / 256) passes of 256 dims; PB partials are loaded per batch,
+// all before any is used (the loads do not depend on the weights), so a
+// merge of up to PB partials costs one memory round trip.
+template <int ND, int PB>
 __global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, int dv,
                                                     const float* __restrict__ o, int64_t ops,
                                                     const float* __restrict__ l, int64_t lps,
@@ -19,44 +23,65 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, in
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t row = int64_t(blockIdx.x) * 4 + wave;
   if (row >= rows) return;
+  bool in[ND];
+#pragma unroll
+  for (int c = 0; c < ND; c++) in[c] = 256 * c + 4 * lane < dv;
+  const float* src0 = o + row * dv + 4 * lane;
+  // first batch of partials, in flight together with the lse loads
+  f32x4 v[PB][ND];
+#pragma unroll
+  for (int q = 0; q < PB; q++)
+#pragma unroll
+    for (int c = 0; c < ND; c++)
+      v[q][c] = (q < n_part && in[c]) ? *reinterpret_cast<const f32x4*>(src0 + q * ops + 256 * c)
+                                     : f32x4{0.f, 0.f, 0.f, 0.f};
+  // lse of partial p0 + lane in this lane
   float mx = -INFINITY;
-  for (int p = lane; p < n_part; p += 64) mx = fmaxf(mx, l[p * lps + row]);
+  for (int p0 = 0; p0 < n_part; p0 += 64) {
+    const int p = p0 + lane;
+    if (p < n_part) mx = fmaxf(mx, l[p * lps + row]);
+  }
   mx = wave_max(mx);
   float tot = 0.f;
   if (mx != -INFINITY)
-    for (int p = lane; p < n_part; p += 64) tot += expf(l[p * lps + row] - mx);
+    for (int p0 = 0; p0 < n_part; p0 += 64) {
+      const int p = p0 + lane;
+      if (p < n_part) tot += expf(l[p * lps + row] - mx);
+    }
   tot = wave_sum(tot);
   const float lse = mx == -INFINITY ? -INFINITY : mx + logf(tot);
-  const int nd = (dv + 255) / 256;  // 256 dims per pass of the wave (4 per lane)
-  f32x4 acc[4];
+  f32x4 acc[ND];
 #pragma unroll
-  for (int c = 0; c < 4; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < ND; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
   if (mx != -INFINITY) {
-    for (int p0 = 0; p0 < n_part; p0 += 64) {
-      // weight of partial p0 + lane, then broadcast one partial at a time
-      const int p = p0 + lane;
-      const float w_lane = p < n_part ? expf(l[p * lps + row] - lse) : 0.f;
-      const int cnt = min(64, n_part - p0);
-#pragma unroll 8
-      for (int pp = 0; pp < cnt; pp++) {
-        const float w = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), pp));
-        const float* src = o + (p0 + pp) * ops + row * dv + 4 * lane;
+    for (int p0 = 0; p0 < n_part; p0 += PB) {
+      if (p0 > 0) {
 #pragma unroll
-        for (int c = 0; c < 4; c++) {
-          if (c < nd && 256 * c + 4 * lane < dv) {
-            // loads are unconditional so that several partials are in flight;
-            // an empty partial (lse = -inf, weight 0) adds nothing
-            const f32x4 v = *reinterpret_cast<const f32x4*>(src + 256 * c);
-            if (w != 0.f) acc[c] += w * v;
-          }
+        for (int q = 0; q < PB; q++)
+#pragma unroll
+          for (int c = 0; c < ND; c++)
+            v[q][c] = (p0 + q < n_part && in[c]) ? *reinterpret_cast<const f32x4*>(src0 + (p0 + q) * ops + 256 * c)
+                                                 : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+      // weight of partial (p0 & ~63) + lane, broadcast per partial
+      const int pl = (p0 & ~63) + lane;
+      const float w_lane = pl < n_part ? expf(l[pl * lps + row] - lse) : 0.f;
+#pragma unroll
+      for (int q = 0; q < PB; q++) {
+        if (p0 + q >= n_part) break;
+        const float w =
+            __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w_lane), (p0 + q) & 63));
+        if (w != 0.f) {  // an empty partial (lse = -inf) adds nothing
+#pragma unroll
+          for (int c = 0; c < ND; c++) acc[c] += w * v[q][c];
         }
       }
     }
   }
 #pragma unroll
-  for (int c = 0; c < 4; c++) {
+  for (int c = 0; c < ND; c++) {
     const int d0 = 256 * c + 4 * lane;
-    if (c >= nd || d0 >= dv) continue;
+    if (!in[c]) continue;
     if (oo) *reinterpret_cast<f32x4*>(oo + row * dv + d0) = acc[c];
     if (ob) {
       u32x2 pk;
@@ -74,9 +99,17 @@ hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, 
                         const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,
                         float* lse_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const int64_t grid = (rows + 3) / 4;
-  hipLaunchKernelGGL(merge_kernel, dim3(unsigned(grid)), dim3(256), 0, s, n_part, rows, dv, o_parts,
-                     o_ps, lse_parts, l_ps, o_out, o_bf16, lse_out);
+  const dim3 grid(unsigned((rows + 3) / 4));
+  const int nd = (dv + 255) / 256;
+  if (nd == 1)
+    hipLaunchKernelGGL((merge_kernel<1, 16>), grid, dim3(256), 0, s, n_part, rows, dv, o_parts, o_ps, lse_parts,
+                       l_ps, o_out, o_bf16, lse_out);
+  else if (nd == 2)
+    hipLaunchKernelGGL((merge_kernel<2, 8>), grid, dim3(256), 0, s, n_part, rows, dv, o_parts, o_ps, lse_parts,
+                       l_ps, o_out, o_bf16, lse_out);
+  else
+    hipLaunchKernelGGL((merge_kernel<4, 4>), grid, dim3(256), 0, s, n_part, rows, dv, o_parts, o_ps, lse_parts,
+                       l_ps, o_out, o_bf16, lse_out);
   return hipGetLastError();
 }
 

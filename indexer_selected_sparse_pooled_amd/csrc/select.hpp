@@ -99,6 +99,36 @@ __device__ __forceinline__ int wave_compact(const uint32_t (&key)[R], uint32_t k
   return tau;
 }
 
+// rank64 of the best element that wave_compact(key, kstar, need) leaves out
+// (0 if it keeps every nonzero key); idx_of(j) is element j's index.
+// Wave-uniform.
+template <int R, class IdxOf>
+__device__ __forceinline__ uint64_t wave_best_excluded(const uint32_t (&key)[R], uint32_t kstar, int need,
+                                                       IdxOf idx_of) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t lt = lanes_below();
+  int base_e = 0;
+  uint64_t best = 0ull;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const bool fe = key[r] == kstar && key[r] != 0u;
+    const uint64_t be = __ballot(fe);
+    const int eb = base_e + __popcll(be & lt);
+    const bool out = key[r] != 0u && (key[r] < kstar || (fe && eb >= need));
+    if (out) {
+      const uint64_t k64 = rank64(key[r], idx_of(r * 64 + lane));
+      best = k64 > best ? k64 : best;
+    }
+    base_e += __popcll(be);
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) {
+    const uint64_t o = __shfl_xor(best, d);
+    best = o > best ? o : best;
+  }
+  return best;
+}
+
 // --------------------------------------------------------- work-group, regs --
 // Element j = tid * R + r lives in key[r] of thread tid (so element order is
 // thread order, then register order). Empty slots hold 0.
