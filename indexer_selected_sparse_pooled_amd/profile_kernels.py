@@ -6,7 +6,10 @@ Runs, each `--reps` times, on seeded synthetic inputs already in HBM:
   * one layer of the 1,048,320-token batch-4 decode step: qsa_index_topk
     (pooled-key scan + exact top-512), qsa_sparse_decode, qsa_lse_merge,
     and the same layer as one qsa_decode_layer launch;
-  * one history tile of the 4096-query prefill chunk (qsa_sparse_prefill).
+  * one history tile of the 4096-query prefill chunk (qsa_sparse_prefill);
+  * the shared-latent prefill attention of 2048 queries at context 131,072
+    (one qsa_sparse_prefill over the whole history).
+`--parts` picks a subset (copy, decode, prefill, mla).
 
 Usage (one counter group per run):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- \
@@ -107,6 +110,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=5)
+    ap.add_argument("--parts", default="copy,decode,prefill,mla")
     ap.add_argument("--trace", help="summarize a rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 counter_collection.csv files and exit")
@@ -126,15 +130,33 @@ def main() -> int:
 
     pkg.qsa.lib()
     dev = "cuda"
-    # reference copy
+    parts = set(args.parts.split(","))
+    if "copy" in parts:
+        copy_reference(torch, fill_normal_bf16, args.reps)
+    if "decode" in parts:
+        decode_layer(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
+    if "prefill" in parts:
+        prefill_tile(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
+    if "mla" in parts:
+        mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
+    torch.cuda.synchronize()
+    print("profile_kernels: done", flush=True)
+    return 0
+
+
+def copy_reference(torch, fill_normal_bf16, reps):
+    dev = "cuda"
     src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device=dev)
     dst = torch.empty_like(src)
     fill_normal_bf16(src, 1, 1)
-    for _ in range(args.reps):
+    for _ in range(reps):
         dst.copy_(src)
     torch.cuda.synchronize()
-    del src, dst
-    # one decode layer, 1,048,320-token context, batch 4
+
+
+def decode_layer(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
+    """One decode layer, 1,048,320-token context, batch 4."""
+    dev = "cuda"
     L, B = 1048320, 4
     seed = qi.config_seed(3)
     keys = torch.empty(B, L // 4, 128, dtype=torch.bfloat16, device=dev)
@@ -149,14 +171,18 @@ def main() -> int:
     q_ctx = torch.full((B,), L, dtype=torch.int32, device=dev)
     q_seq = torch.arange(B, dtype=torch.int32, device=dev)
     bufs = pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, B, L)
-    for _ in range(args.reps):
+    for _ in range(reps):
         pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq)
-    for _ in range(args.reps):
+    for _ in range(reps):
         pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, fused=True)
     torch.cuda.synchronize()
     del keys, k, v, kv, bufs
     torch.cuda.empty_cache()
-    # one history tile of the prefill chunk: 4096 queries after 60,000 tokens
+
+
+def prefill_tile(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
+    """One history tile of the prefill chunk: 4096 queries after 60,000 tokens."""
+    dev = "cuda"
     H, C = 60000, 4096
     ctx_max = H + C
     seed = qi.config_seed(4)
@@ -173,12 +199,37 @@ def main() -> int:
     pkg.qsa_index_scores(pkg.SEL_A, q_ctx, ctx_max, q_idx, pooled, pb.scores)
     pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, ctx_max, pb.scores, pb.sel, pb.n_sel, pb.ws)
     a0, a1 = pb.tiles[3]
-    for _ in range(args.reps):
+    for _ in range(reps):
         pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, pb.sel, pb.n_sel, a0, a1,
                                pb.o_tiles[3], pb.lse_tiles[3])
     torch.cuda.synchronize()
-    print("profile_kernels: done", flush=True)
-    return 0
+    del pb, k, v, kv
+    torch.cuda.empty_cache()
+
+
+def mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
+    """Shared-latent prefill attention: 2048 queries at positions
+    129,024..131,071, each over its top-2048 tokens, one history tile."""
+    import numpy as np
+    dev = "cuda"
+    L, C = 131072, 2048
+    seed = qi.config_seed(5)
+    lat = torch.empty(1, L, 1, 576, dtype=torch.bfloat16, device=dev)
+    keys = torch.empty(1, L, 64, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(C, 64, 576, dtype=torch.bfloat16, device=dev)
+    q_idx = torch.empty(C, 4, 64, dtype=torch.bfloat16, device=dev)
+    for t, kind in ((lat, "latent"), (keys, "raw_key"), (q, "q"), (q_idx, "q_idx")):
+        fill_normal_bf16(t, seed, qi.stream_id(1, 0, kind))
+    w = torch.tensor(qi.uniform_f32(seed, qi.stream_id(1, 0, "w_idx"), C * 4).reshape(C, 4), device=dev)
+    kv = pkg.make_kv(lat, lat)
+    q_ctx = torch.tensor(np.arange(L - C + 1, L + 1, dtype=np.int32), device=dev)
+    pb = pipeline.prefill_buffers(pkg.SEL_B, pkg.ATTN_B, C, L, L)
+    pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, pb.scores, w_idx=w)
+    pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, pb.scores, pb.sel, pb.n_sel, pb.ws)
+    for _ in range(reps):
+        pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv, pb.sel, pb.n_sel, 0, L, pb.o_tiles[0],
+                               pb.lse_tiles[0])
+    torch.cuda.synchronize()
 
 
 if __name__ == "__main__":
