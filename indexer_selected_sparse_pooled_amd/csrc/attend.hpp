@@ -281,9 +281,10 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& s
   wait_memory();
   __syncthreads();
   if (tid == 0) {
-    const unsigned c = atomicAdd(&a.counter[i * a.hkv + g], 1u);
+    uint32_t* cnt = a.counter + size_t(i * a.hkv + g) * kCounterStride;
+    const unsigned c = atomicAdd(cnt, 1u);
     sh.last = c == unsigned(a.n_split - 1);
-    if (sh.last) atomicExch(&a.counter[i * a.hkv + g], 0u);  // ready for the next call
+    if (sh.last) atomicExch(cnt, 0u);  // ready for the next call
   }
   __syncthreads();
   if (!sh.last) return;

@@ -63,6 +63,11 @@ __device__ __forceinline__ uint64_t ld_coherent(const uint64_t* p) {
 // (s_waitcnt vmcnt(0)); coherent stores are then visible chip-wide.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
+// Device-scope counters (work-group hand-off) sit kCounterStride words
+// apart, one per 256-byte line, so that counters of different queries or
+// heads never share a line.
+constexpr int kCounterStride = 64;
+
 __device__ __forceinline__ bf16x2 as_bf16x2(uint32_t w) { return __builtin_bit_cast(bf16x2, w); }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 w) { return __builtin_bit_cast(bf16x8, w); }
 

@@ -24,7 +24,8 @@
 //
 // Counters and flags live in the caller's workspace; each call leaves them
 // zero. No counter is shared by all work-groups (a single device-scope
-// atomic per work-group on one address serialises at the memory side).
+// atomic per work-group on one address serialises at the memory side), and
+// each has a line of its own.
 #include "attend.hpp"
 #include "index_topk.hpp"
 
@@ -44,7 +45,7 @@ struct LayerArgs {
   AttendArgs att;
   uint32_t* error;     // [1] sticky: 1 = a wait ran out
   char* flag;          // copy c of query q's flag at flag + (q * kFlagCopies + c) * kFlagStride
-  uint32_t* att_cnt;   // [nq] attention items of query q finished
+  uint32_t* att_cnt;   // [nq] lines: attention items of query q finished
   int nq, n_chunks, n_att;
 };
 
@@ -88,8 +89,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) voi
     if (tid == 0) {
       // the last attention item of the query clears its flag: every other
       // item of the query has passed its wait
-      if (atomicAdd(L.att_cnt + q, 1u) == unsigned(L.n_att - 1)) {
-        atomicExch(L.att_cnt + q, 0u);
+      uint32_t* cnt = L.att_cnt + size_t(q) * kCounterStride;
+      if (atomicAdd(cnt, 1u) == unsigned(L.n_att - 1)) {
+        atomicExch(cnt, 0u);
         for (int c = 0; c < kFlagCopies; c++) st_coherent(flag_at(L, q, c), 0u);
       }
     }
@@ -130,9 +132,9 @@ DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv
   // (page aligned), the scan's own workspace, the parts
   size_t off = 64;
   p.off_att_cnt = off;
-  off += size_t(nq) * 4;
+  off += size_t(nq) * kCounterStride * 4;
   p.off_merge_cnt = off;
-  off += size_t(nq) * hkv * 4;
+  off += size_t(nq) * hkv * kCounterStride * 4;
   off = (off + kFlagStride - 1) / kFlagStride * kFlagStride;
   p.off_flag = off;
   off += size_t(nq) * kFlagCopies * kFlagStride;

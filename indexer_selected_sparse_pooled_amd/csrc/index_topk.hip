@@ -28,9 +28,9 @@ IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk) {
   // the union never exceeds 4096 entries
   p.keep = p.n_chunks <= itk::kNT ? itk::kChunkKeep : itk::kChunkKeep / 2;
   p.wkeep = itk::kWaveKeep;
-  // counters first (they must be zero before the first call; each call
-  // leaves them zero), then the lists and bounds
-  const size_t cnt = (size_t(nq) * 4 + 255) / 256 * 256;
+  // counters first, one line per query (they must be zero before the first
+  // call; each call leaves them zero), then the lists and bounds
+  const size_t cnt = size_t(nq) * kCounterStride * 4;
   const size_t lists = size_t(nq) * p.n_chunks * p.keep;
   p.off_list = cnt;
   p.off_bound = p.off_list + lists * 8;

@@ -81,20 +81,30 @@ __device__ __forceinline__ float dot8(u32x4 k, u32x4 q) {
   return acc;
 }
 
-// Scores of the 64 keys [tile0, tile0 + 64) (zero-padded past n); lane l
-// returns the score of key tile0 + l.
-__device__ __forceinline__ float tile_scores(const uint16_t* kb, int64_t tile0, int64_t n, u32x4 qv) {
+// A tile is 64 consecutive keys; lane (g, c) = (lane / 16, lane % 16) reads
+// bytes 16c .. 16c+15 of keys tile0 + 4k + g, k = 0..15. Rows past n are
+// clamped to row n - 1 (read, then ignored), so the loads carry no branch.
+__device__ __forceinline__ void load_tile(const uint16_t* kb, int64_t tile0, int64_t n, u32x4 (&v)[16]) {
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, c = lane & 15;
-  u32x4 v[16];
 #pragma unroll
   for (int k = 0; k < 16; k++) {
     const int64_t blk = tile0 + 4 * k + g;
-    v[k] = blk < n ? ld16_nt(kb + blk * 128 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    v[k] = ld16_nt(kb + (blk < n ? blk : n - 1) * 128 + 8 * c);
   }
+  // keep the tile's loads together, in issue order: scoring a tile then
+  // waits for its own loads only, not for the next tile's
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// Scores of the tile loaded by load_tile (keys past n score 0); lane l
+// returns the score of key tile0 + l.
+__device__ __forceinline__ float tile_scores(const u32x4 (&v)[16], int64_t tile0, int64_t n, u32x4 qv) {
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, c = lane & 15;
   float p[16];
 #pragma unroll
-  for (int k = 0; k < 16; k++) p[k] = dot8(v[k], qv);
+  for (int k = 0; k < 16; k++) p[k] = tile0 + 4 * k + g < n ? dot8(v[k], qv) : 0.f;
   // transposing butterfly over the 16 lanes of a group: afterwards lane
   // (g, c) holds the full dot product of key 4c + g
 #pragma unroll
@@ -166,12 +176,19 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   float* out = a.scores + int64_t(i) * a.ld;
   const int64_t w0 = lo + int64_t(wave) * TPW * 64;
   uint32_t key[TPW];
+  // two tiles in flight per wave: the next tile's loads are issued before
+  // the current one is scored. The loads are unconditional (tiles past n
+  // re-read row n - 1): on a branch, scoring would have to wait for every
+  // load in flight, the next tile's included.
+  u32x4 v[2][16];
+  load_tile(kb, w0, n, v[0]);
 #pragma unroll
   for (int t = 0; t < TPW; t++) {
     const int64_t tile0 = w0 + 64 * t;
+    if (t + 1 < TPW) load_tile(kb, tile0 + 64, n, v[(t + 1) & 1]);
     key[t] = 0u;
     if (tile0 < n) {  // wave-uniform
-      const float s = tile_scores(kb, tile0, n, qv);
+      const float s = tile_scores(v[t & 1], tile0, n, qv);
       const int64_t blk = tile0 + lane;
       if (blk < n) {
         st_coherent(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
@@ -237,11 +254,12 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   // ---- the last work-group of this query selects
   wait_memory();  // this thread's coherent stores are complete
   __syncthreads();
-  if (tid == 0) sh.last = atomicAdd(&a.counter[i], 1u) == unsigned(nch - 1);
+  uint32_t* cnt = a.counter + size_t(i) * kCounterStride;
+  if (tid == 0) sh.last = atomicAdd(cnt, 1u) == unsigned(nch - 1);
   __syncthreads();
   if (!sh.last) return false;
   if (tid == 0) {
-    atomicExch(&a.counter[i], 0u);  // ready for the next call
+    atomicExch(cnt, 0u);  // ready for the next call
     st_sel(a.n_sel + i, topk);
   }
   const float* sc = a.scores + int64_t(i) * a.ld;

@@ -73,7 +73,7 @@ struct AttendArgs {
   float* o_part;    // [n_split][nq][hq][dv]
   float* lse_part;  // [n_split][nq][hq]
   // in-launch merge (one-launch decode layer); counter == nullptr: none
-  uint32_t* counter;  // [nq][hkv], zero before the first call, left zero
+  uint32_t* counter;  // [nq][hkv] lines of kCounterStride words, zero before the first call, left zero
   float* o_out;       // [nq][hq][dv] or nullptr
   uint16_t* o_bf16;   // [nq][hq][dv] or nullptr
   float* lse_out;     // [nq][hq] or nullptr
@@ -95,7 +95,7 @@ struct IndexTopkArgs {
   int* sel;
   int* n_sel;
   // workspace views and list sizes (filled by launch_index_topk)
-  uint32_t* counter;
+  uint32_t* counter;     // [nq] lines of kCounterStride words: chunks finished
   uint64_t* list;        // [nq][n_chunks][keep] (key << 32 | block), 0 = empty
   uint64_t* list_bound;  // [nq][n_chunks]
   int n_chunks;
