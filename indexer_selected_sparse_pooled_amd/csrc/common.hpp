@@ -80,6 +80,63 @@ __device__ __forceinline__ int clamp_ctx(int c, int max_ctx) {
   return c < 0 ? 0 : (c > max_ctx ? max_ctx : c);
 }
 
+// Cross-lane moves through DPP, without an LDS round trip (gfx9 controls:
+// row_shr:n = 0x110 + n, row_bcast:15 = 0x142, row_bcast:31 = 0x143).
+// Lanes outside kRowMask, and lanes whose source is out of range when
+// kZero is false, return `old`; with kZero they read 0 instead.
+template <int kCtrl, int kRowMask = 0xf, bool kZero = false>
+__device__ __forceinline__ uint32_t dpp(uint32_t old, uint32_t v) {
+  return uint32_t(__builtin_amdgcn_update_dpp(int(old), int(v), kCtrl, kRowMask, 0xf, kZero));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave: a scan within each row
+// of 16 lanes, then the totals of rows 0 and 2 are added to rows 1 and 3,
+// and the total of rows 0-1 to rows 2-3.
+__device__ __forceinline__ int wave_incl_sum(int x) {
+  x += int(dpp<0x111, 0xf, true>(0u, uint32_t(x)));
+  x += int(dpp<0x112, 0xf, true>(0u, uint32_t(x)));
+  x += int(dpp<0x114, 0xf, true>(0u, uint32_t(x)));
+  x += int(dpp<0x118, 0xf, true>(0u, uint32_t(x)));
+  x += int(dpp<0x142, 0xa>(0u, uint32_t(x)));
+  x += int(dpp<0x143, 0xc>(0u, uint32_t(x)));
+  return x;
+}
+
+// Wave-wide maximum / minimum of unsigned values, the same steps with max or
+// min in place of the sum (a lane with no source keeps its own value); lane
+// 63 ends with the result, which is returned to every lane.
+template <class Op>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v, Op op) {
+  v = op(v, dpp<0x111>(v, v));
+  v = op(v, dpp<0x112>(v, v));
+  v = op(v, dpp<0x114>(v, v));
+  v = op(v, dpp<0x118>(v, v));
+  v = op(v, dpp<0x142, 0xa>(v, v));
+  v = op(v, dpp<0x143, 0xc>(v, v));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  return wave_reduce_u32(v, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
+}
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  auto step = [](uint64_t x, uint32_t hi, uint32_t lo) {
+    const uint64_t o = (uint64_t(hi) << 32) | lo;
+    return o > x ? o : x;
+  };
+  v = step(v, dpp<0x111>(uint32_t(v >> 32), uint32_t(v >> 32)), dpp<0x111>(uint32_t(v), uint32_t(v)));
+  v = step(v, dpp<0x112>(uint32_t(v >> 32), uint32_t(v >> 32)), dpp<0x112>(uint32_t(v), uint32_t(v)));
+  v = step(v, dpp<0x114>(uint32_t(v >> 32), uint32_t(v >> 32)), dpp<0x114>(uint32_t(v), uint32_t(v)));
+  v = step(v, dpp<0x118>(uint32_t(v >> 32), uint32_t(v >> 32)), dpp<0x118>(uint32_t(v), uint32_t(v)));
+  v = step(v, dpp<0x142, 0xa>(uint32_t(v >> 32), uint32_t(v >> 32)), dpp<0x142, 0xa>(uint32_t(v), uint32_t(v)));
+  v = step(v, dpp<0x143, 0xc>(uint32_t(v >> 32), uint32_t(v >> 32)), dpp<0x143, 0xc>(uint32_t(v), uint32_t(v)));
+  const uint32_t hi = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v >> 32)), 63));
+  const uint32_t lo = uint32_t(__builtin_amdgcn_readlane(int(uint32_t(v)), 63));
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

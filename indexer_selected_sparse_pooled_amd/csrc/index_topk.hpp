@@ -12,8 +12,11 @@
 // folded by a transposing butterfly), writes the scores, and keeps the
 // chunk's best (key, block) pairs (16, or 8 when a query has more than 256
 // chunks) plus a bound: the best block it leaves out. Every wave first keeps
-// its own 8 best (register threshold search, no barrier); wave 0 then keeps
-// the chunk's best of the 32.
+// 8 (register threshold search, no barrier), wave 0 then 16 of the 32. The
+// lists are chosen on the top 16 bits of the keys (every key above the
+// 16-bit threshold, then the first at it), which halves the search; the
+// bound is still the best block left out at full precision, which is all
+// the selection below relies on.
 //
 // The last work-group of a query to finish (device-scope counter) selects:
 //  * union mode: the topk best of the union of the chunk lists (register
@@ -217,18 +220,22 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
       sh.wkey[wave * kWaveKeep + lane] = 0u;
       sh.widx[wave * kWaveKeep + lane] = -1;
     }
+    uint32_t kh[TPW];  // top 16 bits (nonzero for every nonzero key)
+#pragma unroll
+    for (int t = 0; t < TPW; t++) kh[t] = key[t] >> 16;
     uint32_t kstar = 0u;
     int need = wkeep;
-    if (m > wkeep) wave_select<TPW>(key, wkeep, kstar, need);
-    wave_compact<TPW>(key, kstar, need, [&](int pos, int j, uint32_t k) {
-      sh.wkey[wave * kWaveKeep + pos] = k;
-      sh.widx[wave * kWaveKeep + pos] = int(w0) + j;
+    if (m > wkeep) wave_select<TPW, 16>(kh, wkeep, kstar, need);
+    wave_compact<TPW>(kh, kstar, need, [&](int pos, int r) {
+      sh.wkey[wave * kWaveKeep + pos] = key[r];
+      sh.widx[wave * kWaveKeep + pos] = int(w0) + 64 * r + lane;
     });
-    const uint64_t wb = wave_best_excluded<TPW>(key, kstar, need, [&](int j) { return int(w0) + j; });
+    const uint64_t wb = wave_best_excluded<TPW>(kh, key, kstar, need, [&](int j) { return int(w0) + j; });
     if (lane == 0) sh.wbound[wave] = wb;
     __syncthreads();
     if (wave == 0) {
-      uint32_t k1[1] = {lane < 4 * kWaveKeep ? sh.wkey[lane] : 0u};
+      const uint32_t k1[1] = {lane < 4 * kWaveKeep ? sh.wkey[lane] : 0u};
+      const uint32_t h1[1] = {k1[0] >> 16};
       const int i1 = lane < 4 * kWaveKeep ? sh.widx[lane] : -1;
       const int valid = __popcll(__ballot(k1[0] != 0u));
       uint64_t bound = 0ull;
@@ -236,16 +243,16 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
       for (int w = 0; w < 4; w++) bound = sh.wbound[w] > bound ? sh.wbound[w] : bound;
       uint32_t ks = 0u;
       int nd = keep;
-      if (valid > keep) wave_select<1>(k1, keep, ks, nd);
+      if (valid > keep) wave_select<1, 16>(h1, keep, ks, nd);
       const size_t base = (size_t(i) * a.n_chunks + chunk) * keep;
       // kept entries (key << 32 | block) go to their list position; the
       // positions past the kept count are cleared (0 = empty)
-      wave_compact<1>(k1, ks, nd, [&](int pos, int, uint32_t k) {
-        st_coherent(a.list + base + pos, (uint64_t(k) << 32) | uint32_t(i1));
+      wave_compact<1>(h1, ks, nd, [&](int pos, int) {
+        st_coherent(a.list + base + pos, (uint64_t(k1[0]) << 32) | uint32_t(i1));
       });
       const int nkept = valid < keep ? valid : keep;
       if (lane >= nkept && lane < keep) st_coherent(a.list + base + lane, 0ull);
-      const uint64_t b = wave_best_excluded<1>(k1, ks, nd, [&](int) { return i1; });
+      const uint64_t b = wave_best_excluded<1>(h1, k1, ks, nd, [&](int) { return i1; });
       bound = b > bound ? b : bound;
       if (lane == 0) st_coherent(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
     }
@@ -265,31 +272,31 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   const float* sc = a.scores + int64_t(i) * a.ld;
 
   if (union_mode || n <= kRegCap) {
+    // register-major: element j = r * kNT + tid (coalesced loads); element
+    // order is block order, so the selection comes out ascending
     uint32_t ukey[kRegR];
     int uidx[kRegR];
     uint64_t my_bound = 0ull;
     if (union_mode) {
-      // thread t holds union entries 16t .. 16t+15 (chunk-major, each list in
-      // ascending block order), i.e. the lists of chunks 16t/keep .. (16t+15)/keep,
-      // and checks their bounds
-      const size_t base = size_t(i) * a.n_chunks * keep + size_t(tid) * kRegR;
+      // union entry e = chunk * keep + slot (each list in ascending block
+      // order); thread t checks the bounds of chunks t, t + kNT, ...
+      const uint64_t* ul = a.list + size_t(i) * a.n_chunks * keep;
       const int u = nch * keep;
-      uint64_t e[kRegR];
-#pragma unroll
-      for (int r = 0; r < kRegR; r++) e[r] = tid * kRegR + r < u ? ld_coherent(a.list + base + r) : 0ull;
-      for (int c = tid * kRegR / keep; c < (tid + 1) * kRegR / keep && c < nch; c++) {
-        const uint64_t b = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + c);
-        my_bound = b > my_bound ? b : my_bound;
-      }
 #pragma unroll
       for (int r = 0; r < kRegR; r++) {
-        ukey[r] = uint32_t(e[r] >> 32);
-        uidx[r] = int(uint32_t(e[r]));
+        const int e = r * kNT + tid;
+        const uint64_t v = e < u ? ld_coherent(ul + e) : 0ull;
+        ukey[r] = uint32_t(v >> 32);
+        uidx[r] = int(uint32_t(v));
+      }
+      for (int c = tid; c < nch; c += kNT) {
+        const uint64_t b = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + c);
+        my_bound = b > my_bound ? b : my_bound;
       }
     } else {
 #pragma unroll
       for (int r = 0; r < kRegR; r++) {
-        const int j = tid * kRegR + r;
+        const int j = r * kNT + tid;
         ukey[r] = j < n ? score_key(sc, j) : 0u;
         uidx[r] = j;
       }
@@ -298,7 +305,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     int need;
     regsel_threshold<kNT, kRegR>(ukey, topk, sh.rs, kstar, need);
     int pos[kRegR];
-    regsel_positions<kNT, kRegR>(ukey, uidx, kstar, need, sh.rs, pos);
+    regsel_positions_rm<kNT, kRegR>(ukey, uidx, kstar, need, sh.rs, pos);
     bool ok = true;
     if (union_mode) {
       // tau = the topk-th best of the union; a chunk whose bound ranks above

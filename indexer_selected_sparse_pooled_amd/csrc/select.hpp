@@ -32,34 +32,19 @@ __device__ __forceinline__ uint64_t lanes_below() {
   return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t o = uint32_t(__shfl_xor(int(v), m));
-    v = o > v ? o : v;
-  }
-  return v;
-}
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    const uint32_t o = uint32_t(__shfl_xor(int(v), m));
-    v = o < v ? o : v;
-  }
-  return v;
-}
 
 // ------------------------------------------------------------------ wave ----
 // Keys key[r] of lane l are element r*64 + l of the wave's range; empty slots
 // hold 0 and never count (every candidate threshold is >= 1).
 
 // k-th largest key among the wave's nonzero keys; need = k - #{key > kstar}.
+// Keys hold kBits bits (the bits above are zero): one ballot step per bit.
 // Requires 1 <= k <= number of nonzero keys. Wave-uniform results.
-template <int R>
+template <int R, int kBits = 32>
 __device__ __forceinline__ void wave_select(const uint32_t (&key)[R], int k, uint32_t& kstar, int& need) {
   uint32_t t = 0;
 #pragma unroll 1
-  for (int bit = 31; bit >= 0; bit--) {
+  for (int bit = kBits - 1; bit >= 0; bit--) {
     const uint32_t cand = t | (1u << bit);
     int c = 0;
 #pragma unroll
@@ -76,8 +61,9 @@ __device__ __forceinline__ void wave_select(const uint32_t (&key)[R], int k, uin
 }
 
 // Emit, in element order, every key > kstar and the first `need` keys equal
-// to kstar: emit(position, element, key). Returns the element that is the
-// need-th one equal to kstar (wave-uniform), or -1 if there is none.
+// to kstar: emit(position, r) for key[r] of the calling lane. Returns the
+// element that is the need-th one equal to kstar (wave-uniform), or -1 if
+// there is none.
 template <int R, class Emit>
 __device__ __forceinline__ int wave_compact(const uint32_t (&key)[R], uint32_t kstar, int need, Emit emit) {
   const int lane = threadIdx.x & 63;
@@ -90,7 +76,7 @@ __device__ __forceinline__ int wave_compact(const uint32_t (&key)[R], uint32_t k
     const uint64_t bg = __ballot(fg), be = __ballot(fe);
     const int gb = base_g + __popcll(bg & lt);
     const int eb = base_e + __popcll(be & lt);
-    if (fg || (fe && eb < need)) emit(gb + (eb < need ? eb : need), r * 64 + lane, key[r]);
+    if (fg || (fe && eb < need)) emit(gb + (eb < need ? eb : need), r);
     const uint64_t tm = __ballot(fe && eb == need - 1);
     if (tm) tau = r * 64 + int(__ffsll(static_cast<unsigned long long>(tm)) - 1);
     base_g += __popcll(bg);
@@ -100,11 +86,12 @@ __device__ __forceinline__ int wave_compact(const uint32_t (&key)[R], uint32_t k
 }
 
 // rank64 of the best element that wave_compact(key, kstar, need) leaves out
-// (0 if it keeps every nonzero key); idx_of(j) is element j's index.
-// Wave-uniform.
+// (0 if it keeps every nonzero key), ranked by its full key fkey[r] (key may
+// be a coarser image of it, e.g. its top bits); idx_of(j) is element j's
+// index. Wave-uniform.
 template <int R, class IdxOf>
-__device__ __forceinline__ uint64_t wave_best_excluded(const uint32_t (&key)[R], uint32_t kstar, int need,
-                                                       IdxOf idx_of) {
+__device__ __forceinline__ uint64_t wave_best_excluded(const uint32_t (&key)[R], const uint32_t (&fkey)[R],
+                                                       uint32_t kstar, int need, IdxOf idx_of) {
   const int lane = threadIdx.x & 63;
   const uint64_t lt = lanes_below();
   int base_e = 0;
@@ -116,17 +103,12 @@ __device__ __forceinline__ uint64_t wave_best_excluded(const uint32_t (&key)[R],
     const int eb = base_e + __popcll(be & lt);
     const bool out = key[r] != 0u && (key[r] < kstar || (fe && eb >= need));
     if (out) {
-      const uint64_t k64 = rank64(key[r], idx_of(r * 64 + lane));
+      const uint64_t k64 = rank64(fkey[r], idx_of(r * 64 + lane));
       best = k64 > best ? k64 : best;
     }
     base_e += __popcll(be);
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint64_t o = __shfl_xor(best, d);
-    best = o > best ? o : best;
-  }
-  return best;
+  return wave_max_u64(best);
 }
 
 // --------------------------------------------------------- work-group, regs --
@@ -138,6 +120,7 @@ struct RegSelLds {
   uint32_t hist[3][256];
   uint32_t wmax[NT / 64], wmin[NT / 64];
   int wg[NT / 64], we[NT / 64];
+  int pg[64], pe[64];  // register-major positions: counts per (register, wave)
   int tau_slot;
   int tau_val;
 };
@@ -200,13 +183,7 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
       cnt[e] = int(h[255 - (4 * lane + e)]);
       lsum += cnt[e];
     }
-    int incl = lsum;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int o = __shfl_up(incl, d);
-      if (lane >= d) incl += o;
-    }
-    int above = incl - lsum;
+    int above = wave_incl_sum(lsum) - lsum;
     int my_digit = -1, my_above = 0;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -218,8 +195,8 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
     }
     const uint64_t hit = __ballot(my_digit >= 0);
     const int src = int(__ffsll(static_cast<unsigned long long>(hit)) - 1);
-    const uint32_t digit = uint32_t(__shfl(my_digit, src));
-    remaining -= __shfl(my_above, src);
+    const uint32_t digit = uint32_t(__builtin_amdgcn_readlane(my_digit, src));
+    remaining -= __builtin_amdgcn_readlane(my_above, src);
     prefix |= digit << shift;
     mask |= dmask << shift;
     lo = shift;
@@ -244,15 +221,7 @@ __device__ void regsel_positions(const uint32_t (&key)[R], const int (&val)[R], 
     g += key[r] > kstar ? 1 : 0;
     e += (key[r] == kstar && key[r] != 0u) ? 1 : 0;
   }
-  int ig = g, ie = e;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int og = __shfl_up(ig, d), oe = __shfl_up(ie, d);
-    if (lane >= d) {
-      ig += og;
-      ie += oe;
-    }
-  }
+  const int ig = wave_incl_sum(g), ie = wave_incl_sum(e);
   if (lane == 63) {
     sh.wg[wave] = ig;
     sh.we[wave] = ie;
@@ -279,6 +248,57 @@ __device__ void regsel_positions(const uint32_t (&key)[R], const int (&val)[R], 
         sh.tau_val = val[r];
       }
       eb++;
+    }
+  }
+  __syncthreads();
+}
+
+// regsel_positions for the register-major layout: element j = r * NT + tid
+// lives in key[r] of thread tid (consecutive threads hold consecutive
+// elements, so loading them is coalesced). Same results and the same
+// sh.tau_slot / sh.tau_val; ends with a barrier. Each wave counts its
+// greater / equal keys per register with ballots; one exchange of those
+// counts gives every (register, wave) pair its offset.
+template <int NT, int R>
+__device__ void regsel_positions_rm(const uint32_t (&key)[R], const int (&val)[R], uint32_t kstar, int need,
+                                    RegSelLds<NT>& sh, int (&pos)[R]) {
+  constexpr int NW = NT / 64;
+  static_assert(R * NW <= 64, "one lane per (register, wave) pair");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const uint64_t lt = lanes_below();
+  uint64_t bg[R], be[R];
+  int cg = 0, ce = 0;  // lane r: this wave's counts for register r
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    bg[r] = __ballot(key[r] > kstar);
+    be[r] = __ballot(key[r] == kstar && key[r] != 0u);
+    if (lane == r) {
+      cg = __popcll(bg[r]);
+      ce = __popcll(be[r]);
+    }
+  }
+  if (lane < R) {
+    sh.pg[lane * NW + wave] = cg;
+    sh.pe[lane * NW + wave] = ce;
+  }
+  __syncthreads();
+  // lane l holds pair l = r * NW + w (element order); exclusive prefix sums
+  const int xg = lane < R * NW ? sh.pg[lane] : 0, xe = lane < R * NW ? sh.pe[lane] : 0;
+  const int og = wave_incl_sum(xg) - xg, oe = wave_incl_sum(xe) - xe;
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const int gb = __builtin_amdgcn_readlane(og, r * NW + wave) + __popcll(bg[r] & lt);
+    const int eb = __builtin_amdgcn_readlane(oe, r * NW + wave) + __popcll(be[r] & lt);
+    pos[r] = -1;
+    if (key[r] > kstar) {
+      pos[r] = gb + (eb < need ? eb : need);
+    } else if (key[r] == kstar && key[r] != 0u) {
+      if (eb < need) pos[r] = gb + eb;
+      if (eb == need - 1) {
+        sh.tau_slot = r * NT + int(threadIdx.x);
+        sh.tau_val = val[r];
+      }
     }
   }
   __syncthreads();
@@ -378,13 +398,7 @@ __device__ void stream_select(KeyAt key_at, int n, int k, StreamLds& sh, uint32_
         cnt[e] = int(sh.hist[255 - (4 * lane + e)]);
         lsum += cnt[e];
       }
-      int incl = lsum;
-#pragma unroll
-      for (int d = 1; d < 64; d <<= 1) {
-        const int o = __shfl_up(incl, d);
-        if (lane >= d) incl += o;
-      }
-      int above = incl - lsum;
+      int above = wave_incl_sum(lsum) - lsum;
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         if (above < remaining && remaining <= above + cnt[e]) {
@@ -426,17 +440,9 @@ __device__ void stream_compact(KeyAt key_at, int n, uint32_t kstar, int need, St
     }
     const int cg = __popc(fg), ce = __popc(fe);
     // inclusive scan of (cg, ce) over the wave
-    int ig = cg, ie = ce;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int og = __shfl_up(ig, d), oe = __shfl_up(ie, d);
-      if (lane >= d) {
-        ig += og;
-        ie += oe;
-      }
-    }
+    const int ig = wave_incl_sum(cg), ie = wave_incl_sum(ce);
     int wg_off, we_off, tg, te;
-    wave_offsets<NT>(__shfl(ig, 63), __shfl(ie, 63), sh, wg_off, we_off, tg, te);
+    wave_offsets<NT>(__builtin_amdgcn_readlane(ig, 63), __builtin_amdgcn_readlane(ie, 63), sh, wg_off, we_off, tg, te);
     int gb = base_g + wg_off + ig - cg;
     int eb = base_e + we_off + ie - ce;
 #pragma unroll

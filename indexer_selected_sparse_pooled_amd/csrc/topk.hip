@@ -104,11 +104,7 @@ __global__ __launch_bounds__(256) void topk_chunks(TopkArgs a, TopkPlan p) {
       b = k64 > b ? k64 : b;
     }
   }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) {
-    const uint64_t o = __shfl_xor(b, d);
-    b = o > b ? o : b;
-  }
+  b = wave_max_u64(b);
   if ((tid & 63) == 0) sh.wb[tid >> 6] = b;
   __syncthreads();
   if (tid == 0) {
