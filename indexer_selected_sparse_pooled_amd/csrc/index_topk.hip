@@ -17,11 +17,13 @@ __global__ __launch_bounds__(256) void index_topk_a(IndexTopkArgs a) {
 IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk) {
   IndexTopkPlan p{};
   const int64_t nmax = int64_t(max_ctx) / 4;
-  // at most 256 chunks per query (a 1M-token context: 1024 blocks per chunk,
-  // 1024 work-groups for 4 queries, all resident at once); more, smaller
-  // chunks (tried: 512 of 512 blocks) were not faster
+  // at most 512 chunks per query (a 1M-token context: 512 blocks per chunk,
+  // 2048 work-groups for 4 queries). Small chunks balance best: the chip
+  // holds about 768 of these work-groups and hands out the rest as they
+  // finish, so no CU is left with a long chunk at the end (2048 / 1024 /
+  // 512 work-groups: 57 / 60 / 65 us for the scan and top-512)
   int tpw = 1;
-  while (tpw < 16 && (nmax + 256 * tpw - 1) / (256 * tpw) > itk::kNT) tpw *= 2;
+  while (tpw < 16 && (nmax + 256 * tpw - 1) / (256 * tpw) > 2 * itk::kNT) tpw *= 2;
   p.tpw = tpw;
   p.n_chunks = int(nmax <= 0 ? 1 : (nmax + 256 * tpw - 1) / (256 * tpw));
   // candidates kept: 8 per wave, 16 per chunk up to 256 chunks, else 8, so
