@@ -59,7 +59,7 @@ __device__ __forceinline__ uint32_t* flag_at(const LayerArgs& L, int q, int c) {
 }
 
 template <int TPW>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void decode_layer_a(LayerArgs L) {
+__global__ __launch_bounds__(256) void decode_layer_a(LayerArgs L) {
   __shared__ LayerLds sh;
   const int tid = threadIdx.x;
   const int n_scan = L.nq * L.n_chunks;
