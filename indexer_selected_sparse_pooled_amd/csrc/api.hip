@@ -382,7 +382,7 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
   uint32_t err = 0;
   if (hipMemcpy(&err, ws, 4, hipMemcpyDeviceToHost) != hipSuccess)
     return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: cannot read the error word");
-  if (err) return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: a wait for a selection ran out (error word %u)", err);
+  if (err) return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: a merge wait ran out (error word %u)", err);
   return QSA_OK;
 }
 

@@ -40,6 +40,7 @@ constexpr int kG = 8;            // query heads per kv head
 constexpr int kD = 256;          // head dim of K and V
 constexpr int kPair = 1040;      // LDS bytes per pair of V rows (2 x 512 + 16: pairs 4 apart hit other banks)
 constexpr int kPStr = kTT + 8;   // LDS row of P in elements (144 bytes)
+constexpr unsigned kMergeSpinLimit = 1u << 24;  // polls while the parts of a merge arrive
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
@@ -68,11 +69,13 @@ struct List {
   int nblk;  // complete blocks
   int block;
   int L;     // list length
+  const int* cache = nullptr;  // LDS copy of sel[0 .. ns), or nullptr
+  __device__ __forceinline__ int sel_at(int j) const { return cache ? cache[j] : ld_sel<kCoh>(sel + j); }
   // token of list entry p (0 <= p < L)
   __device__ __forceinline__ int tok(int p) const {
     const int nb_tok = ns * block;
     if (p < nb_tok) {
-      int b = ld_sel<kCoh>(sel + p / block);
+      int b = sel_at(p / block);
       b = b < 0 ? 0 : (b >= nblk ? nblk - 1 : b);
       return b * block + p % block;
     }
@@ -88,15 +91,18 @@ struct List {
     int lo = 0, hi = ns;  // first selected block >= xb
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
-      if (ld_sel<kCoh>(sel + mid) < xb) lo = mid + 1; else hi = mid;
+      if (sel_at(mid) < xb) lo = mid + 1; else hi = mid;
     }
     return lo * block;
   }
 };
 
-// One part (split, kv head g, query i): see the file comment.
+// One part (split, kv head g, query i): see the file comment. sel_lds, when
+// given, holds the query's ns_lds selected blocks in LDS (ascending) and
+// replaces sel / n_sel.
 template <bool kCoh>
-__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& sh) {
+__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& sh, const int* sel_lds = nullptr,
+                            int ns_lds = 0) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, kq = lane >> 4;
 
@@ -110,8 +116,9 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& s
   // inside the one-launch layer the selection is this launch's own, which
   // always holds min(complete blocks, topk) entries: no need to wait for
   // n_sel to arrive
-  const int ns = kCoh ? ns_max : a.n_sel[i];
+  const int ns = sel_lds ? ns_lds : (kCoh ? ns_max : a.n_sel[i]);
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
+  lv.cache = sel_lds;
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
 
   if (tid == 0) {
@@ -277,81 +284,72 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& s
   }
   if (!a.counter) return;
 
-  // ---- hand the part over; the last work-group of (query, kv head) merges
+  // ---- merge: once every part of (query, kv head) has stored its result,
+  // part `split` merges dims [256 split / n_split, 256 (split + 1) / n_split)
+  // of the 8 heads, each element over all parts, every load of a batch issued
+  // before any is used. The parts of a (query, kv head) are resident
+  // together (the host checks this), so the wait ends.
   wait_memory();
   __syncthreads();
+  uint32_t* arrive = a.counter + size_t(i * a.hkv + g) * 2 * kCounterStride;
+  uint32_t* depart = arrive + kCounterStride;
   if (tid == 0) {
-    uint32_t* cnt = a.counter + size_t(i * a.hkv + g) * kCounterStride;
-    const unsigned c = atomicAdd(cnt, 1u);
-    sh.last = c == unsigned(a.n_split - 1);
-    if (sh.last) atomicExch(cnt, 0u);  // ready for the next call
-  }
-  __syncthreads();
-  if (!sh.last) return;
-  const int h = tid >> 5, d0 = 8 * (tid & 31);
-  const int64_t hrow = int64_t(i) * a.hq + g * kG + h;  // row within one part
-  const int64_t pstride = int64_t(a.nq) * a.hq;         // rows per part
-  // every (part, head) lse at once, one per thread, into LDS (the V tile
-  // is free now); then each head's maximum and the parts' weights
-  float* lsh = reinterpret_cast<float*>(sh.v);  // [n_split][kG]
-  auto load_batch = [&](int p0, uint64_t (&ov)[8][4]) {
-#pragma unroll
-    for (int q = 0; q < 8; q++) {
-      const int p = p0 + q;
-      if (p < a.n_split) {
-        const uint64_t* src = reinterpret_cast<const uint64_t*>(a.o_part + (p * pstride + hrow) * kD + d0);
-#pragma unroll
-        for (int k = 0; k < 4; k++) ov[q][k] = ld_coherent(src + k);
+    atomicAdd(arrive, 1u);
+    unsigned polls = 0;
+    while (ld_coherent(arrive) < unsigned(a.n_split)) {
+      if (++polls > kMergeSpinLimit) {
+        if (a.error) atomicOr(a.error, 2u);
+        break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
-  };
-  uint64_t ov[8][4];
-  load_batch(0, ov);  // in flight together with the lse loads
-  for (int e = tid; e < a.n_split * kG; e += 256) {
-    const int64_t src = int64_t(e / kG) * pstride + int64_t(i) * a.hq + g * kG + e % kG;
-    lsh[e] = __uint_as_float(ld_coherent(reinterpret_cast<const uint32_t*>(a.lse_part + src)));
   }
   __syncthreads();
-  float mx = -INFINITY;
-  for (int p = 0; p < a.n_split; p++) mx = fmaxf(mx, lsh[p * kG + h]);
-  float acc8[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  float tot = 0.f;
-  if (mx != -INFINITY) {
-    for (int p0 = 0; p0 < a.n_split; p0 += 8) {
-      if (p0 > 0) load_batch(p0, ov);
+  const int d0 = kD * split / a.n_split, w = kD * (split + 1) / a.n_split - d0;
+  const int64_t pstride = int64_t(a.nq) * a.hq;  // rows per part
+  const int64_t row0 = int64_t(i) * a.hq + g * kG;
+  constexpr int kMB = 16;  // parts per batch
+  for (int e = tid; e < kG * w; e += 256) {
+    const int h = e / w, d = d0 + e % w;
+    float mx = -INFINITY, tot = 0.f, acc = 0.f;
+    for (int p0 = 0; p0 < a.n_split; p0 += kMB) {
+      float lp[kMB], op[kMB];
 #pragma unroll
-      for (int q = 0; q < 8; q++) {
+      for (int q = 0; q < kMB; q++) {
         const int p = p0 + q;
-        if (p >= a.n_split) break;
-        const float lp = lsh[p * kG + h];
-        if (lp == -INFINITY) continue;  // empty part
-        const float w = expf(lp - mx);
-        tot += w;
+        const bool ok = p < a.n_split;
+        const int64_t r = p * pstride + row0 + h;
+        lp[q] = ok ? __uint_as_float(ld_coherent(reinterpret_cast<const uint32_t*>(a.lse_part + r))) : -INFINITY;
+        op[q] = ok ? __uint_as_float(ld_coherent(reinterpret_cast<const uint32_t*>(a.o_part + r * kD + d))) : 0.f;
+      }
+      float bm = mx;
 #pragma unroll
-        for (int k = 0; k < 4; k++) {
-          acc8[2 * k] += w * __uint_as_float(uint32_t(ov[q][k]));
-          acc8[2 * k + 1] += w * __uint_as_float(uint32_t(ov[q][k] >> 32));
-        }
+      for (int q = 0; q < kMB; q++) bm = fmaxf(bm, lp[q]);
+      if (bm == -INFINITY) continue;
+      const float sc = expf(mx - bm);
+      tot *= sc;
+      acc *= sc;
+      mx = bm;
+#pragma unroll
+      for (int q = 0; q < kMB; q++) {
+        if (lp[q] == -INFINITY) continue;  // empty part
+        const float wq = expf(lp[q] - mx);
+        tot += wq;
+        acc += wq * op[q];
       }
     }
+    const float o = tot > 0.f ? acc / tot : 0.f;
+    const int64_t hrow = row0 + h;
+    if (a.o_out) a.o_out[hrow * kD + d] = o;
+    if (a.o_bf16) a.o_bf16[hrow * kD + d] = f32_to_bf16(o);
+    if (a.lse_out && split == 0 && e % w == 0) a.lse_out[hrow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
   }
-  const float inv_t = tot > 0.f ? 1.f / tot : 0.f;
-  float fin[8];
-#pragma unroll
-  for (int k = 0; k < 8; k++) fin[k] = acc8[k] * inv_t;
-  if (a.o_out) {
-    float* dst = a.o_out + hrow * kD + d0;
-    *reinterpret_cast<f32x4*>(dst) = f32x4{fin[0], fin[1], fin[2], fin[3]};
-    *reinterpret_cast<f32x4*>(dst + 4) = f32x4{fin[4], fin[5], fin[6], fin[7]};
+  // the last part to leave resets both counters for the next call: every
+  // part has passed its wait by then
+  if (tid == 0 && atomicAdd(depart, 1u) == unsigned(a.n_split - 1)) {
+    atomicExch(arrive, 0u);
+    atomicExch(depart, 0u);
   }
-  if (a.o_bf16) {
-    u32x4 pk;
-#pragma unroll
-    for (int k = 0; k < 4; k++)
-      pk[k] = uint32_t(f32_to_bf16(fin[2 * k])) | (uint32_t(f32_to_bf16(fin[2 * k + 1])) << 16);
-    st16(a.o_bf16 + hrow * kD + d0, pk);
-  }
-  if (a.lse_out && (tid & 31) == 0) a.lse_out[hrow] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
 }  // namespace att

@@ -1,126 +1,112 @@
-// One decode layer in one launch (pooled-block variant): A2 + A3 + A4 + A5.
+// One decode layer (pooled-block variant) in two launches: A2 + A3 + A4 + A5.
 // "3090x3で 314 万コンテキスト": every pooled key is scored at every step
 // (section "VRAM に残す必要があるもの"), a fixed budget of blocks is kept and
 // only their K/V rows are read (section "なぜ"); "GLM-5.3 最適化 第2部",
 // section "DCP": the partial attention results are merged by log-sum-exp.
 //
-// One work item per work-group, in block order: first the scan chunks of
-// every query (index_topk.hpp: score a chunk, keep its best candidates; the
-// last chunk of a query to finish selects its top-k), then the attention
-// parts (attend.hpp: one (kv head, split) part each; the last part of a kv
-// head merges). An attention item waits until the selection of its query
-// is published, so a query's attention overlaps the scans still running for
-// later queries, and the whole layer costs one launch.
+// Launch 1 (index_lists_a): each work-group scores one chunk of one query's
+// pooled keys and writes the chunk's best candidates and a bound
+// (index_topk.hpp, without the selection).
 //
-// Why this cannot deadlock: a scan item never waits, and the attention
-// items are fewer than the work-groups the chip holds at once (the host
-// checks this before it launches, and otherwise issues the scan, the
-// attention and the merge as three launches). So however the hardware
-// orders the dispatch, waiting attention items can never take every slot:
-// the scans always progress and publish every selection. Every wait is
-// also bounded: past the bound the kernel raises a sticky error word and
-// carries on (selections are clamped into range, so every access stays
-// inside the buffers).
+// Launch 2 (attend_select_a): one work-group per (query, kv head, split).
+// Every work-group selects its query's exact top-k itself, from the chunk
+// lists, into LDS (final_select, the same code the last chunk of
+// qsa_index_topk runs): the parts of a query repeat the same register
+// select side by side instead of waiting for one of them to publish it.
+// Part (kv head 0, split 0) also writes sel and n_sel. Each part then
+// attends its split of the token list (attend.hpp) and stores its partial
+// result; the parts of a (query, kv head) wait for each other and merge,
+// each part one slice of the output dims. That wait needs every part
+// resident at once: the host checks it with the occupancy API, and
+// otherwise the parts only write their partials and a third launch merges.
 //
-// Counters and flags live in the caller's workspace; each call leaves them
-// zero. No counter is shared by all work-groups (a single device-scope
-// atomic per work-group on one address serialises at the memory side), and
-// each has a line of its own.
+// Counters live in the caller's workspace; each call leaves them zero.
+// Every wait is bounded: past the bound the kernel sets a sticky error word
+// and carries on (every access stays inside the buffers).
 #include "attend.hpp"
 #include "index_topk.hpp"
 
 namespace qsa {
 namespace {
 
-constexpr unsigned kSpinLimit = 1u << 22;  // polls of a selection flag (seconds)
-// Each selection flag has kFlagCopies copies kFlagStride bytes apart, and
-// the attention parts of a query poll different copies with a growing
-// pause: hundreds of pollers on one line would tie up the memory channel
-// that serves it, and with it the scans still running.
-constexpr int kFlagCopies = 8;
-constexpr int kFlagStride = 4096;
+constexpr int kMaxTopk = 2048;
 
-struct LayerArgs {
-  IndexTopkArgs itk;
-  AttendArgs att;
-  uint32_t* error;     // [1] sticky: 1 = a wait ran out
-  char* flag;          // copy c of query q's flag at flag + (q * kFlagCopies + c) * kFlagStride
-  uint32_t* att_cnt;   // [nq] lines: attention items of query q finished
-  int nq, n_chunks, n_att;
+struct SelAttnLds {
+  int sel[kMaxTopk];  // the query's selected blocks, ascending
+  union {
+    itk::FinalLds f;
+    att::Lds a;
+  } u;
 };
-
-union LayerLds {
-  itk::FinalLds scan;
-  att::Lds attn;
-};
-
-__device__ __forceinline__ uint32_t* flag_at(const LayerArgs& L, int q, int c) {
-  return reinterpret_cast<uint32_t*>(L.flag + (size_t(q) * kFlagCopies + c) * kFlagStride);
-}
 
 template <int TPW>
-__global__ __launch_bounds__(256) void decode_layer_a(LayerArgs L) {
-  __shared__ LayerLds sh;
+__global__ __launch_bounds__(256) void index_lists_a(IndexTopkArgs a) {
+  __shared__ itk::FinalLds sh;
+  itk::chunk_step<TPW, false>(a, blockIdx.y, blockIdx.x, sh);
+}
+
+__global__ __launch_bounds__(256) void attend_select_a(IndexTopkArgs it, AttendArgs at) {
+  __shared__ SelAttnLds sh;
   const int tid = threadIdx.x;
-  const int n_scan = L.nq * L.n_chunks;
-  const int t = int(blockIdx.x);
-  const bool scan = t < n_scan;
-  const int q = scan ? t / L.n_chunks : (t - n_scan) / L.n_att;
-  const int idx = scan ? t % L.n_chunks : (t - n_scan) % L.n_att;
-  if (scan) {
-    if (itk::chunk_step<TPW>(L.itk, q, idx, sh.scan) && tid < kFlagCopies)
-      st_coherent(flag_at(L, q, tid), 1u);
+  const int n_att = at.hkv * at.n_split;
+  const int i = int(blockIdx.x) / n_att, r = int(blockIdx.x) % n_att;
+  const int g = r / at.n_split, split = r % at.n_split;
+  // the lists and bounds are loaded at the plan's full size before the
+  // query's context arrives (one round trip instead of two); entries past
+  // the query's own lists are dropped below
+  uint64_t ent[itk::kRegR];
+  itk::load_union(it, i, it.n_chunks * it.keep, ent);
+  const uint64_t* bq = it.list_bound + size_t(i) * it.n_chunks;
+  const uint64_t b0 = tid < it.n_chunks ? ld_coherent(bq + tid) : 0ull;
+  const uint64_t b1 = tid + itk::kNT < it.n_chunks ? ld_coherent(bq + tid + itk::kNT) : 0ull;
+  const int n = clamp_ctx(it.q_ctx[i], it.max_ctx) / 4;
+  const int topk = it.topk;
+  const int ns = n < topk ? n : topk;
+  const bool writer = g == 0 && split == 0;
+  int* gsel = it.sel + int64_t(i) * topk;
+  auto emit = [&](int pos, int blk) {
+    sh.sel[pos] = blk;
+    if (writer) gsel[pos] = blk;
+  };
+  if (n <= topk) {  // every complete block
+    for (int j = tid; j < ns; j += 256) sh.sel[j] = j;
+    if (writer)
+      for (int j = tid; j < topk; j += 256) gsel[j] = j < n ? j : -1;
+  } else if (itk::use_union(it, n) && it.n_chunks <= 2 * itk::kNT) {
+    const int nch = (n + it.chunk_blocks - 1) / it.chunk_blocks;
+    const int u = nch * it.keep;
+    uint32_t ukey[itk::kRegR];
+    int uidx[itk::kRegR];
+#pragma unroll
+    for (int rr = 0; rr < itk::kRegR; rr++) {
+      const bool in = rr * itk::kNT + tid < u;
+      ukey[rr] = in ? uint32_t(ent[rr] >> 32) : 0u;
+      uidx[rr] = int(uint32_t(ent[rr]));
+    }
+    uint64_t my_bound = tid < nch ? b0 : 0ull;
+    if (tid + itk::kNT < nch) my_bound = b1 > my_bound ? b1 : my_bound;
+    if (!itk::select_registers(it, true, ukey, uidx, my_bound, sh.u.f, emit))
+      itk::select_streamed(it.scores + int64_t(i) * it.ld, n, topk, sh.u.f, emit);
   } else {
-    if (tid == 0) {
-      const uint32_t* f = flag_at(L, q, idx % kFlagCopies);
-      unsigned polls = 0, pause = 1;
-      while (ld_coherent(f) == 0u) {
-        if (++polls > kSpinLimit) {
-          atomicOr(L.error, 1u);
-          break;
-        }
-        for (unsigned k = 0; k < pause; k++) __builtin_amdgcn_s_sleep(8);  // 512 cycles each
-        pause = pause < 4 ? 2 * pause : 4;
-      }
-    }
-    __syncthreads();
-    const int n_split = L.att.n_split;
-    att::attend_part<true>(L.att, idx % n_split, idx / n_split, q, sh.attn);
-    if (tid == 0) {
-      // the last attention item of the query clears its flag: every other
-      // item of the query has passed its wait
-      uint32_t* cnt = L.att_cnt + size_t(q) * kCounterStride;
-      if (atomicAdd(cnt, 1u) == unsigned(L.n_att - 1)) {
-        atomicExch(cnt, 0u);
-        for (int c = 0; c < kFlagCopies; c++) st_coherent(flag_at(L, q, c), 0u);
-      }
-    }
+    itk::final_select(it, i, n, sh.u.f, emit);
   }
+  if (writer && tid == 0) it.n_sel[i] = ns;
+  __syncthreads();
+  att::attend_part<false>(at, split, g, i, sh.u.a, sh.sel, ns);
 }
 
-// Work-groups of decode_layer_a<TPW> the current device holds at once.
-template <int TPW>
+// Work-groups of attend_select_a the current device holds at once.
 int resident_groups() {
   static int cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (cache[dev] == 0) {
     int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_layer_a<TPW>, 256, 0) != hipSuccess) per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_select_a, 256, 0) != hipSuccess) per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
     cache[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
   }
   return cache[dev];
-}
-
-template <int TPW>
-hipError_t launch_t(const LayerArgs& L, hipStream_t s, bool& launched) {
-  const int n_att_all = L.nq * L.n_att;
-  launched = n_att_all < resident_groups<TPW>();
-  if (!launched) return hipSuccess;
-  const unsigned grid = unsigned(L.nq * (L.n_chunks + L.n_att));
-  hipLaunchKernelGGL(decode_layer_a<TPW>, dim3(grid), dim3(256), 0, s, L);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -128,16 +114,12 @@ hipError_t launch_t(const LayerArgs& L, hipStream_t s, bool& launched) {
 DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv, int dv, int n_split) {
   DecodeLayerPlan p{};
   p.itk = plan_index_topk(nq, max_ctx, topk);
-  // the error word, the per-query counters, the merge counters, the flags
-  // (page aligned), the scan's own workspace, the parts
-  size_t off = 64;
-  p.off_att_cnt = off;
-  off += size_t(nq) * kCounterStride * 4;
+  // the error word, the merge counters (two lines per (query, kv head)),
+  // the scan's workspace, the parts
+  size_t off = 256;
   p.off_merge_cnt = off;
-  off += size_t(nq) * hkv * kCounterStride * 4;
-  off = (off + kFlagStride - 1) / kFlagStride * kFlagStride;
-  p.off_flag = off;
-  off += size_t(nq) * kFlagCopies * kFlagStride;
+  off += size_t(nq) * hkv * 2 * kCounterStride * 4;
+  off = (off + 255) / 256 * 256;
   p.off_itk = off;
   off += (p.itk.ws_bytes + 255) / 256 * 256;
   p.off_o = off;
@@ -157,37 +139,30 @@ hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLa
   itk.list = reinterpret_cast<uint64_t*>(wi + p.itk.off_list);
   itk.list_bound = reinterpret_cast<uint64_t*>(wi + p.itk.off_bound);
   itk.n_chunks = p.itk.n_chunks;
+  itk.chunk_blocks = 256 * p.itk.tpw;
   itk.keep = p.itk.keep;
   itk.wkeep = p.itk.wkeep;
-  att.counter = reinterpret_cast<uint32_t*>(w + p.off_merge_cnt);
   att.o_part = reinterpret_cast<float*>(w + p.off_o);
   att.lse_part = reinterpret_cast<float*>(w + p.off_lse);
-  LayerArgs L{};
-  L.itk = itk;
-  L.att = att;
-  L.error = reinterpret_cast<uint32_t*>(w);
-  L.flag = w + p.off_flag;
-  L.att_cnt = reinterpret_cast<uint32_t*>(w + p.off_att_cnt);
-  L.nq = itk.nq;
-  L.n_chunks = p.itk.n_chunks;
-  L.n_att = att.hkv * att.n_split;
-  bool launched = false;
-  hipError_t e;
+  att.error = reinterpret_cast<uint32_t*>(w);
+  const int n_att_all = itk.nq * att.hkv * att.n_split;
+  const bool merge_in = n_att_all <= resident_groups();
+  att.counter = merge_in ? reinterpret_cast<uint32_t*>(w + p.off_merge_cnt) : nullptr;
+
+  dim3 grid(unsigned(p.itk.n_chunks), unsigned(itk.nq));
   switch (p.itk.tpw) {
-    case 1: e = launch_t<1>(L, s, launched); break;
-    case 2: e = launch_t<2>(L, s, launched); break;
-    case 4: e = launch_t<4>(L, s, launched); break;
-    case 8: e = launch_t<8>(L, s, launched); break;
-    default: e = launch_t<16>(L, s, launched); break;
+    case 1: hipLaunchKernelGGL(index_lists_a<1>, grid, dim3(256), 0, s, itk); break;
+    case 2: hipLaunchKernelGGL(index_lists_a<2>, grid, dim3(256), 0, s, itk); break;
+    case 4: hipLaunchKernelGGL(index_lists_a<4>, grid, dim3(256), 0, s, itk); break;
+    case 8: hipLaunchKernelGGL(index_lists_a<8>, grid, dim3(256), 0, s, itk); break;
+    default: hipLaunchKernelGGL(index_lists_a<16>, grid, dim3(256), 0, s, itk); break;
   }
-  if (e != hipSuccess || launched) return e;
-  // too many attention parts to wait inside one launch: three launches
-  e = launch_index_topk(itk, p.itk, wi, s);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  AttendArgs a2 = att;
-  a2.counter = nullptr;
-  e = launch_attend(a2, s);
-  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attend_select_a, dim3(unsigned(n_att_all)), dim3(256), 0, s, itk, att);
+  e = hipGetLastError();
+  if (e != hipSuccess || merge_in) return e;
+  // too many parts to be resident together: merge in a third launch
   const int64_t rows = int64_t(att.nq) * att.hq;
   return launch_merge(att.n_split, rows, att.dv, att.o_part, rows * att.dv, att.lse_part, rows, att.o_out, att.o_bf16,
                       att.lse_out, s);

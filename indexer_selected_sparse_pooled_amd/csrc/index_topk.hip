@@ -48,6 +48,7 @@ hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, 
   a.list = reinterpret_cast<uint64_t*>(w + p.off_list);
   a.list_bound = reinterpret_cast<uint64_t*>(w + p.off_bound);
   a.n_chunks = p.n_chunks;
+  a.chunk_blocks = 256 * p.tpw;
   a.keep = p.keep;
   a.wkeep = p.wkeep;
   dim3 grid(unsigned(p.n_chunks), unsigned(a.nq));

@@ -142,18 +142,110 @@ __device__ __forceinline__ float tile_scores(const u32x4 (&v)[16], int64_t tile0
 }
 
 // Exact selection over the scores of one query, streamed from memory.
-__device__ void select_streamed(const float* sc, int n, int topk, int* sel, FinalLds& sh) {
+template <class Emit>
+__device__ void select_streamed(const float* sc, int n, int topk, FinalLds& sh, Emit emit) {
   auto key_at = [&](int j) { return score_key(sc, j); };
   uint32_t kstar;
   int need;
   stream_select<kNT>(key_at, n, topk, sh.st, kstar, need);
-  stream_compact<kNT>(key_at, n, kstar, need, sh.st, [&](int pos, int j) { st_sel(sel + pos, j); });
+  stream_compact<kNT>(key_at, n, kstar, need, sh.st, emit);
+}
+
+// Whether query i's exact top-k comes from the union of its chunk lists:
+// enough lists for the union to hold the top-k twice over, few enough for
+// the registers. Otherwise the scores themselves are selected from.
+__device__ __forceinline__ bool use_union(const IndexTopkArgs& a, int n) {
+  const int nch = (n + a.chunk_blocks - 1) / a.chunk_blocks;
+  return n > kRegCap && nch * a.keep >= 2 * a.topk && nch * a.keep <= kRegCap;
+}
+
+// Union entry e = chunk * keep + slot of query i (each list in ascending
+// block order, so entry order is block order), as (key << 32 | block), 0 =
+// empty; thread t holds entries r * kNT + t. Entries at or past u are 0.
+__device__ __forceinline__ void load_union(const IndexTopkArgs& a, int i, int u, uint64_t (&ent)[kRegR]) {
+  const uint64_t* ul = a.list + size_t(i) * a.n_chunks * a.keep;
+#pragma unroll
+  for (int r = 0; r < kRegR; r++) {
+    const int e = r * kNT + int(threadIdx.x);
+    ent[r] = e < u ? ld_coherent(ul + e) : 0ull;
+  }
+}
+
+// The topk best of the keys in registers (element j = r * kNT + tid, in
+// block order): emit(position, block) for each, positions ascending, and
+// true; or false, emitting nothing, when in union mode a chunk's bound (the
+// best block it left out; my_bound is the largest this thread checked)
+// ranks above the union's topk-th, so the union may miss a better block.
+template <class Emit>
+__device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, uint32_t (&ukey)[kRegR],
+                                 int (&uidx)[kRegR], uint64_t my_bound, FinalLds& sh, Emit emit) {
+  uint32_t kstar;
+  int need;
+  regsel_threshold<kNT, kRegR>(ukey, a.topk, sh.rs, kstar, need);
+  int pos[kRegR];
+  regsel_positions_rm<kNT, kRegR>(ukey, uidx, kstar, need, sh.rs, pos);
+  if (union_mode) {
+    const uint64_t tau = rank64(kstar, sh.rs.tau_val);
+    if (__syncthreads_or(my_bound > tau)) return false;
+  }
+#pragma unroll
+  for (int r = 0; r < kRegR; r++)
+    if (pos[r] >= 0) emit(pos[r], uidx[r]);
+  return true;
+}
+
+// The exact top-k of query i (n > topk candidates), once every chunk of the
+// query has written its scores and list: emit(position, block) for each of
+// the topk selected blocks, positions in ascending block order. Lists,
+// bounds and scores are read with agent-coherent loads (they may have been
+// written earlier in the same launch). Modes:
+//  * union: register select over the chunk lists; exact unless a chunk's
+//    bound (the best block it left out) ranks above the union's topk-th;
+//  * raw (n <= 4096): register select straight over the scores;
+//  * streamed: exact select over every score (too many or too few lists,
+//    or a failed bound check).
+template <class Emit>
+__device__ void final_select(const IndexTopkArgs& a, int i, int n, FinalLds& sh, Emit emit) {
+  const int tid = threadIdx.x;
+  const float* sc = a.scores + int64_t(i) * a.ld;
+  const bool union_mode = use_union(a, n);
+  if (union_mode || n <= kRegCap) {
+    uint32_t ukey[kRegR];
+    int uidx[kRegR];
+    uint64_t my_bound = 0ull;
+    if (union_mode) {
+      const int nch = (n + a.chunk_blocks - 1) / a.chunk_blocks;
+      uint64_t ent[kRegR];
+      load_union(a, i, nch * a.keep, ent);
+#pragma unroll
+      for (int r = 0; r < kRegR; r++) {
+        ukey[r] = uint32_t(ent[r] >> 32);
+        uidx[r] = int(uint32_t(ent[r]));
+      }
+      for (int c = tid; c < nch; c += kNT) {
+        const uint64_t b = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + c);
+        my_bound = b > my_bound ? b : my_bound;
+      }
+    } else {
+      // register-major raw scores: element j = r * kNT + tid
+#pragma unroll
+      for (int r = 0; r < kRegR; r++) {
+        const int j = r * kNT + tid;
+        ukey[r] = j < n ? score_key(sc, j) : 0u;
+        uidx[r] = j;
+      }
+    }
+    if (select_registers(a, union_mode, ukey, uidx, my_bound, sh, emit)) return;
+  }
+  select_streamed(sc, n, a.topk, sh, emit);
 }
 
 // One chunk of query i. Returns true in the one work-group that completed
 // the query's selection (sel and n_sel written, the stores complete); the
 // caller may then hand the selection on.
-template <int TPW>
+// kSelect == false: scores and lists only (the selection is made by the
+// caller's next kernel), and the function returns false.
+template <int TPW, bool kSelect = true>
 __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int C = kNT * TPW;
@@ -163,7 +255,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   int* sel = a.sel + int64_t(i) * topk;
   const int64_t lo = int64_t(chunk) * C;
   if (lo >= n) {
-    if (chunk == 0) {  // n == 0: nothing to score
+    if (kSelect && chunk == 0) {  // n == 0: nothing to score
       for (int j = tid; j < topk; j += kNT) st_sel(sel + j, -1);
       if (tid == 0) st_sel(a.n_sel + i, 0);
       publish();
@@ -201,7 +293,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   }
 
   if (n <= topk) {  // every block is selected
-    if (chunk == 0) {
+    if (kSelect && chunk == 0) {
       for (int j = tid; j < topk; j += kNT) st_sel(sel + j, j < n ? j : -1);
       if (tid == 0) st_sel(a.n_sel + i, n);
       publish();
@@ -210,7 +302,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     return false;
   }
   const int keep = a.keep, wkeep = a.wkeep;
-  const bool union_mode = n > kRegCap && nch * keep >= 2 * topk && nch * keep <= kRegCap;
+  const bool union_mode = use_union(a, n);
 
   // ---- chunk list: 8 best per wave, then 16 best of the 32
   if (union_mode) {
@@ -258,6 +350,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     }
   }
 
+  if (!kSelect) return false;
   // ---- the last work-group of this query selects
   wait_memory();  // this thread's coherent stores are complete
   __syncthreads();
@@ -269,59 +362,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     atomicExch(cnt, 0u);  // ready for the next call
     st_sel(a.n_sel + i, topk);
   }
-  const float* sc = a.scores + int64_t(i) * a.ld;
-
-  if (union_mode || n <= kRegCap) {
-    // register-major: element j = r * kNT + tid (coalesced loads); element
-    // order is block order, so the selection comes out ascending
-    uint32_t ukey[kRegR];
-    int uidx[kRegR];
-    uint64_t my_bound = 0ull;
-    if (union_mode) {
-      // union entry e = chunk * keep + slot (each list in ascending block
-      // order); thread t checks the bounds of chunks t, t + kNT, ...
-      const uint64_t* ul = a.list + size_t(i) * a.n_chunks * keep;
-      const int u = nch * keep;
-#pragma unroll
-      for (int r = 0; r < kRegR; r++) {
-        const int e = r * kNT + tid;
-        const uint64_t v = e < u ? ld_coherent(ul + e) : 0ull;
-        ukey[r] = uint32_t(v >> 32);
-        uidx[r] = int(uint32_t(v));
-      }
-      for (int c = tid; c < nch; c += kNT) {
-        const uint64_t b = ld_coherent(a.list_bound + size_t(i) * a.n_chunks + c);
-        my_bound = b > my_bound ? b : my_bound;
-      }
-    } else {
-#pragma unroll
-      for (int r = 0; r < kRegR; r++) {
-        const int j = r * kNT + tid;
-        ukey[r] = j < n ? score_key(sc, j) : 0u;
-        uidx[r] = j;
-      }
-    }
-    uint32_t kstar;
-    int need;
-    regsel_threshold<kNT, kRegR>(ukey, topk, sh.rs, kstar, need);
-    int pos[kRegR];
-    regsel_positions_rm<kNT, kRegR>(ukey, uidx, kstar, need, sh.rs, pos);
-    bool ok = true;
-    if (union_mode) {
-      // tau = the topk-th best of the union; a chunk whose bound ranks above
-      // it may have left out an element of the true top-k
-      const uint64_t tau = rank64(kstar, sh.rs.tau_val);
-      ok = !__syncthreads_or(my_bound > tau);
-    }
-    if (ok) {
-#pragma unroll
-      for (int r = 0; r < kRegR; r++)
-        if (pos[r] >= 0) st_sel(sel + pos[r], uidx[r]);
-      publish();
-      return true;
-    }
-  }
-  select_streamed(sc, n, topk, sel, sh);
+  final_select(a, i, n, sh, [&](int pos, int blk) { st_sel(sel + pos, blk); });
   publish();
   return true;
 }

@@ -72,8 +72,9 @@ struct AttendArgs {
   int64_t tile_begin, tile_end;
   float* o_part;    // [n_split][nq][hq][dv]
   float* lse_part;  // [n_split][nq][hq]
-  // in-launch merge (one-launch decode layer); counter == nullptr: none
-  uint32_t* counter;  // [nq][hkv] lines of kCounterStride words, zero before the first call, left zero
+  // merge inside the launch (decode layer); counter == nullptr: none
+  uint32_t* counter;  // [nq][hkv] pairs of lines (kCounterStride words each), zero before the first call, left zero
+  uint32_t* error;    // sticky error word (bit 1: a merge wait ran out), or nullptr
   float* o_out;       // [nq][hq][dv] or nullptr
   uint16_t* o_bf16;   // [nq][hq][dv] or nullptr
   float* lse_out;     // [nq][hq] or nullptr
@@ -99,6 +100,7 @@ struct IndexTopkArgs {
   uint64_t* list;        // [nq][n_chunks][keep] (key << 32 | block), 0 = empty
   uint64_t* list_bound;  // [nq][n_chunks]
   int n_chunks;
+  int chunk_blocks;      // blocks per chunk
   int keep;              // candidates kept per chunk
   int wkeep;             // candidates kept per wave
 };
@@ -112,12 +114,12 @@ IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk);
 hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, hipStream_t s);
 
 
-// One decode layer in one launch (variant A): scan + top-k + attention +
-// merge (three launches when the attention parts outnumber the work-groups
-// the chip holds at once).
+// One decode layer (variant A): scan with chunk lists, then attention whose
+// work-groups select their query's blocks themselves and merge in-launch
+// (a third launch merges when the parts cannot be resident together).
 struct DecodeLayerPlan {
   IndexTopkPlan itk;
-  size_t off_flag, off_att_cnt, off_merge_cnt, off_itk, off_o, off_lse, ws_bytes;
+  size_t off_merge_cnt, off_itk, off_o, off_lse, ws_bytes;
 };
 DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv, int dv, int n_split);
 // itk / att: everything but the workspace views (filled in from ws)
