@@ -11,9 +11,9 @@ namespace qsa {
 namespace {
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4, 8))) void attend_a(AttendArgs a) {
-  __shared__ att::Lds sh;
+  __shared__ att::Lds<1> sh;
   const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
-  att::attend_part<false>(a, split, blockIdx.y, i, sh);
+  att::attend_part<false, 1>(a, split, blockIdx.y, i, sh);
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_b(AttendArgs a) {

@@ -13,12 +13,13 @@
 // The query's token list is the tokens of its selected blocks (ascending)
 // followed by the trailing tokens of the incomplete block. A work-group
 // walks its contiguous part of the list (intersected with [tile_begin,
-// tile_end)) in tiles of 64 tokens:
-//   * V rows of the tile go straight from global memory to LDS
-//     (global_load_lds_dwordx4, no registers), two rows per wave instruction;
-//   * S = Q K^T on MFMA 16x16x32 bf16: the GQA group's 8 query heads are the
-//     A rows (rows 8..15 zero), each wave computes 16 tokens with K rows as
-//     the B operand, loaded straight from global memory;
+// tile_end)) in groups of GT tiles of 64 tokens, every load of a group
+// issued before any is used:
+//   * K rows go straight from global memory to registers as the B operand
+//     of S = Q K^T on MFMA 16x16x32 bf16: the GQA group's 8 query heads are
+//     the A rows (rows 8..15 zero), each wave computes 16 * GT tokens;
+//   * V rows go straight from global memory to LDS (global_load_lds_dwordx4,
+//     no registers), two rows per wave instruction;
 //   * online softmax in exp2 form per head (one barrier);
 //   * O += P V on MFMA 16x16x32: P split into bf16 hi + lo parts (two
 //     MFMAs, ~16 significant bits); each wave owns 64 of the 256 output
@@ -39,19 +40,21 @@ constexpr int kTT = 64;          // token positions per tile
 constexpr int kG = 8;            // query heads per kv head
 constexpr int kD = 256;          // head dim of K and V
 constexpr int kPair = 1040;      // LDS bytes per pair of V rows (2 x 512 + 16: pairs 4 apart hit other banks)
-constexpr int kPStr = kTT + 8;   // LDS row of P in elements (144 bytes)
 constexpr unsigned kMergeSpinLimit = 1u << 24;  // polls while the parts of a merge arrive
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 
+// LDS of one work-group; a group of GT tiles (64 * GT tokens) is loaded at once.
+template <int GT>
 struct Lds {
-  __attribute__((aligned(16))) unsigned char v[kTT / 2 * kPair];
-  float s[kG][kTT];
+  static constexpr int kTok = kTT * GT;
+  static constexpr int kPStr = kTok + 8;  // LDS row of P in elements
+  __attribute__((aligned(16))) unsigned char v[kTok / 2 * kPair];
+  float s[kG][kTok];
   __attribute__((aligned(16))) uint16_t phi[kG * kPStr];
   __attribute__((aligned(16))) uint16_t plo[kG * kPStr];
   float alpha[kG], m[kG], l[kG];
   int64_t range[2];
-  int last;
 };
 
 // sel may have been written earlier in the same launch by another
@@ -100,9 +103,11 @@ struct List {
 // One part (split, kv head g, query i): see the file comment. sel_lds, when
 // given, holds the query's ns_lds selected blocks in LDS (ascending) and
 // replaces sel / n_sel.
-template <bool kCoh>
-__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& sh, const int* sel_lds = nullptr,
+template <bool kCoh, int GT>
+__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT>& sh, const int* sel_lds = nullptr,
                             int ns_lds = 0) {
+  constexpr int kTok = Lds<GT>::kTok, kPStr = Lds<GT>::kPStr;
+  constexpr int kRW = 16 * GT;  // token rows per wave
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, kq = lane >> 4;
 
@@ -154,64 +159,89 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& s
 #pragma unroll
   for (int nt = 0; nt < 4; nt++) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  for (int pb = P0; pb < P1; pb += kTT) {
-    const int cnt = (P1 - pb) < kTT ? (P1 - pb) : kTT;
-    // lane l holds the token of tile row l (rows past cnt repeat row 0, so
-    // every load reads finite data that the softmax then weights by 0)
-    const int tokl = lv.tok(pb + (lane < cnt ? lane : 0));
-    // V: wave w loads row pairs 8w .. 8w+7; lanes 0-31 the even row, 32-63 the odd one
-    {
+  for (int pb = P0; pb < P1; pb += kTok) {
+    const int cnt = (P1 - pb) < kTok ? (P1 - pb) : kTok;
+    // wave w owns group rows kRW*w .. kRW*w + kRW-1 (its S rows and its V
+    // rows); lane l holds the token of row kRW*w + l % kRW. Rows past cnt
+    // repeat row 0, so every load reads finite data that the softmax then
+    // weights by 0.
+    const int row_l = kRW * wave + lane % kRW;
+    const int tokl = lv.tok(pb + (row_l < cnt ? row_l : 0));
+    // V rows go straight to LDS (no registers) and K rows to registers as
+    // the B operands of S. With one tile per group (many work-groups per CU)
+    // the V rows are issued first; with several tiles (few, latency-bound
+    // work-groups) the K rows are, so that S waits for them alone.
+    auto load_v = [&]() {
       const int half = lane >> 5, c = lane & 31;
 #pragma unroll
-      for (int j = 0; j < 8; j++) {
-        const int p = 8 * wave + j;
-        const int vt = __shfl(tokl, 2 * p + half);
+      for (int j = 0; j < 8 * GT; j++) {
+        const int p = 8 * GT * wave + j;
+        const int vt = __shfl(tokl, 2 * j + half);
         __builtin_amdgcn_global_load_lds(
             vbase + int64_t(vt) * a.tok_stride + 8 * c,
             (__attribute__((address_space(3))) void*)(sh.v + p * kPair), 16, 0, 0);
       }
-    }
-    // S for tile rows 16*wave .. 16*wave+15
-    {
-      const int rr = 16 * wave + r;
-      const int kt = __shfl(tokl, rr);
-      const uint16_t* krow = kbase + int64_t(kt) * a.tok_stride + 8 * kq;
-      bf16x8 kb[kD / 32];
+    };
+    if constexpr (GT == 1) load_v();
+    bf16x8 kb[GT][kD / 32];
 #pragma unroll
-      for (int ks = 0; ks < kD / 32; ks++) kb[ks] = as_bf16x8(ld16(krow + 32 * ks));
+    for (int b = 0; b < GT; b++) {
+      const int kt = __shfl(tokl, 16 * b + r);
+      const uint16_t* krow = kbase + int64_t(kt) * a.tok_stride + 8 * kq;
+#pragma unroll
+      for (int ks = 0; ks < kD / 32; ks++) kb[b][ks] = as_bf16x8(ld16(krow + 32 * ks));
+    }
+    if constexpr (GT > 1) load_v();
+    // S for the wave's rows, 16 at a time: lane (kq, r) holds S[head 4kq+e][row r]
+#pragma unroll
+    for (int b = 0; b < GT; b++) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < kD / 32; ks++)
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb[b][ks], acc, 0, 0, 0);
+      const int rr = kRW * wave + 16 * b + r;
       if (kq < 2) {
 #pragma unroll
         for (int e = 0; e < 4; e++) sh.s[4 * kq + e][rr] = rr < cnt ? acc[e] * sl2 : -INFINITY;
       }
     }
     __syncthreads();
-    // online softmax: head h = tid / 32, two tokens per thread
+    // online softmax: head h = tid / 32, 2 * GT consecutive tokens per thread
     {
+      constexpr int kE = 2 * GT;
       const int h = tid >> 5;
-      const int t2 = (tid & 31) * 2;
-      const float s0 = sh.s[h][t2], s1 = sh.s[h][t2 + 1];
-      float mt = fmaxf(s0, s1);
+      const int t0 = (tid & 31) * kE;
+      float sv[kE];
+#pragma unroll
+      for (int e = 0; e < kE; e++) sv[e] = sh.s[h][t0 + e];
+      float mt = sv[0];
+#pragma unroll
+      for (int e = 1; e < kE; e++) mt = fmaxf(mt, sv[e]);
 #pragma unroll
       for (int m = 16; m >= 1; m >>= 1) mt = fmaxf(mt, __shfl_xor(mt, m));
       const float m_old = sh.m[h], l_old = sh.l[h];
       const float m_new = fmaxf(m_old, mt);
-      float p0 = 0.f, p1 = 0.f, al = 1.f;
+      float pv[kE];
+      float al = 1.f, ps = 0.f;
+#pragma unroll
+      for (int e = 0; e < kE; e++) pv[e] = 0.f;
       if (m_new != -INFINITY) {
         al = exp2f(m_old - m_new);
-        p0 = exp2f(s0 - m_new);
-        p1 = exp2f(s1 - m_new);
+#pragma unroll
+        for (int e = 0; e < kE; e++) {
+          pv[e] = exp2f(sv[e] - m_new);
+          ps += pv[e];
+        }
       }
-      float ps = p0 + p1;
 #pragma unroll
       for (int m = 16; m >= 1; m >>= 1) ps += __shfl_xor(ps, m);
-      const uint16_t h0 = f32_to_bf16(p0), h1 = f32_to_bf16(p1);
-      const uint16_t l0 = f32_to_bf16(p0 - bf16_to_f32(h0)), l1 = f32_to_bf16(p1 - bf16_to_f32(h1));
-      *reinterpret_cast<uint32_t*>(sh.phi + h * kPStr + t2) = uint32_t(h0) | (uint32_t(h1) << 16);
-      *reinterpret_cast<uint32_t*>(sh.plo + h * kPStr + t2) = uint32_t(l0) | (uint32_t(l1) << 16);
+#pragma unroll
+      for (int e = 0; e < kE; e += 2) {
+        const uint16_t h0 = f32_to_bf16(pv[e]), h1 = f32_to_bf16(pv[e + 1]);
+        const uint16_t l0 = f32_to_bf16(pv[e] - bf16_to_f32(h0)), l1 = f32_to_bf16(pv[e + 1] - bf16_to_f32(h1));
+        *reinterpret_cast<uint32_t*>(sh.phi + h * kPStr + t0 + e) = uint32_t(h0) | (uint32_t(h1) << 16);
+        *reinterpret_cast<uint32_t*>(sh.plo + h * kPStr + t0 + e) = uint32_t(l0) | (uint32_t(l1) << 16);
+      }
       if ((tid & 31) == 0) {
         sh.alpha[h] = al;
         sh.l[h] = al * l_old + ps;
@@ -230,7 +260,7 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds& s
         for (int nt = 0; nt < 4; nt++) oacc[nt][e] *= al;
       }
 #pragma unroll
-      for (int k2 = 0; k2 < kTT / 32; k2++) {
+      for (int k2 = 0; k2 < kTok / 32; k2++) {
         // A: P[head r][tokens 32*k2 + 8*kq .. +7] (rows 8..15 are zero)
         const bf16x8 ah = r < kG ? as_bf16x8(ld16(sh.phi + r * kPStr + 32 * k2 + 8 * kq)) : bf16x8{};
         const bf16x8 al8 = r < kG ? as_bf16x8(ld16(sh.plo + r * kPStr + 32 * k2 + 8 * kq)) : bf16x8{};

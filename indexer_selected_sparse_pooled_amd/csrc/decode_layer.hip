@@ -30,12 +30,15 @@ namespace qsa {
 namespace {
 
 constexpr int kMaxTopk = 2048;
+// tiles of 64 tokens an attention part loads at once (a decode part of the
+// 1M-context batch-4 layer holds two)
+constexpr int kLayerGT = 2;
 
 struct SelAttnLds {
   int sel[kMaxTopk];  // the query's selected blocks, ascending
   union {
     itk::FinalLds f;
-    att::Lds a;
+    att::Lds<kLayerGT> a;
   } u;
 };
 
@@ -45,7 +48,8 @@ __global__ __launch_bounds__(256) void index_lists_a(IndexTopkArgs a) {
   itk::chunk_step<TPW, false>(a, blockIdx.y, blockIdx.x, sh);
 }
 
-__global__ __launch_bounds__(256) void attend_select_a(IndexTopkArgs it, AttendArgs at) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_select_a(IndexTopkArgs it,
+                                                                                       AttendArgs at) {
   __shared__ SelAttnLds sh;
   const int tid = threadIdx.x;
   const int n_att = at.hkv * at.n_split;
@@ -64,8 +68,9 @@ __global__ __launch_bounds__(256) void attend_select_a(IndexTopkArgs it, AttendA
   const int ns = n < topk ? n : topk;
   const bool writer = g == 0 && split == 0;
   int* gsel = it.sel + int64_t(i) * topk;
-  auto emit = [&](int pos, int blk) {
-    sh.sel[pos] = blk;
+  int* const lsel = sh.sel;
+  auto emit = [lsel, writer, gsel](int pos, int blk) {
+    lsel[pos] = blk;
     if (writer) gsel[pos] = blk;
   };
   if (n <= topk) {  // every complete block
@@ -92,7 +97,7 @@ __global__ __launch_bounds__(256) void attend_select_a(IndexTopkArgs it, AttendA
   }
   if (writer && tid == 0) it.n_sel[i] = ns;
   __syncthreads();
-  att::attend_part<false>(at, split, g, i, sh.u.a, sh.sel, ns);
+  att::attend_part<false, kLayerGT>(at, split, g, i, sh.u.a, sh.sel, ns);
 }
 
 // Work-groups of attend_select_a the current device holds at once.
