@@ -2,20 +2,21 @@
 """Benchmark of the indexer-selected sparse-attention hot path on one MI355X.
 
 Headline (``value``): decode steps/s at 1,048,320-token context, batch 4,
-12 sparse-attention layers run in sequence (each layer: pooled-key scan
-and exact top-512 block selection in one launch, sparse attention over the
-2,048 selected tokens in splits, log-sum-exp merge). One step = all 12
-layers for the 4 sequences, captured once in a HIP graph and replayed. The
-one-launch layer (qsa_decode_layer) is timed the same way and reported
-beside it. Inputs (K, V, raw and pooled
+12 sparse-attention layers run in sequence, one qsa_decode_layer call per
+layer (pooled-key scan with per-chunk candidate lists; then per (query,
+kv head, split) the exact top-512 blocks, sparse attention over the 2,048
+selected tokens and the log-sum-exp merge). One step = all 12 layers for
+the 4 sequences, captured once in a HIP graph and replayed. The same step
+as separate calls (qsa_index_topk, qsa_sparse_decode, qsa_lse_merge) is
+timed the same way and reported beside it. Inputs (K, V, raw and pooled
 indexer keys, queries) are seeded, synthetic and resident in HBM before the
 timed region.
 
 Also reported: HBM GB/s of the step (algorithmic bytes), the prefill chunk
 (4096 queries after a 60,000-token history, 8192-token history tiles, and
 1024-token tiles) in query tokens/s, the roofline of the dominant kernel
-(the pooled-key scan with the top-k) with its launch duration timed by HIP events on the
-launch stream, and the CPU oracle timed on the host on a bounded sample.
+(the pooled-key scan with its candidate lists, qsa_index_lists) with its launch duration
+timed by HIP events on the launch stream, and the CPU oracle timed on the host on a bounded sample.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -132,43 +133,38 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
     L, B = DECODE["ctx"], DECODE["batch"]
     bufs = [pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, B, L) for _ in layers]
 
-    def step():
+    def step(fused):
         for lay, bf in zip(layers, bufs):
             pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay["q_idx"], lay["pooled"], lay["q"], lay["kv"],
-                                  bf, q_seq=q_seq)
+                                  bf, q_seq=q_seq, fused=fused)
 
-    ms, wall, graph = time_graph(torch, step, steps, warmup)
+    # headline: one qsa_decode_layer call per layer
+    ms, wall, graph = time_graph(torch, lambda: step(True), steps, warmup)
     del graph
-
-    def step_fused():
-        for lay, bf in zip(layers, bufs):
-            pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay["q_idx"], lay["pooled"], lay["q"], lay["kv"],
-                                  bf, q_seq=q_seq, fused=True)
-
-    ms_fused, _, graph = time_graph(torch, step_fused, max(10, steps // 2), warmup)
+    # the same step as separate calls (index_topk, sparse_decode, lse_merge)
+    ms_sep, _, graph = time_graph(torch, lambda: step(False), max(10, steps // 2), warmup)
+    del graph
     unit_bytes = bm.decode_unit_bytes(L)
     step_bytes = unit_bytes * B * len(layers)
     # per-kernel durations, each timed alone over every layer (HIP events, launch stream)
     b0, lay0 = bufs[0], layers[0]
     reps = max(10, steps)
 
+    def lists_only():
+        for lay, bf in zip(layers, bufs):
+            pkg.qsa_index_lists(pkg.SEL_A, q_ctx, L, lay["q_idx"], lay["pooled"], bf.scores, bf.itk_ws, q_seq=q_seq)
+
     def scan_select_only():
         for lay, bf in zip(layers, bufs):
             pkg.qsa_index_topk(pkg.SEL_A, q_ctx, L, lay["q_idx"], lay["pooled"], bf.scores, bf.sel, bf.n_sel,
                                bf.itk_ws, q_seq=q_seq)
 
+    lists_ms = time_launches(torch, lists_only, reps) / len(layers)
     scan_ms = time_launches(torch, scan_select_only, reps) / len(layers)
-    attn_ms = time_launches(torch, lambda: pkg.qsa_sparse_decode(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"],
-                                                                 lay0["kv"], b0.sel, b0.n_sel, b0.n_split, b0.o_part,
-                                                                 b0.lse_part, q_seq=q_seq), reps)
-    merge_ms = time_launches(torch, lambda: pkg.qsa_lse_merge(b0.o_part, b0.lse_part, o_out=b0.o,
-                                                              o_out_bf16=b0.o_bf16, lse_out=b0.lse), reps)
     scan_launch_bytes = B * (bm.scan_bytes(L) + 128 * 2)
-    scan_gbs = scan_launch_bytes / (scan_ms * 1e-3) / 1e9
-    del graph
-    return dict(ms=ms, ms_fused=ms_fused, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
-                n_split=bufs[0].n_split, scan_ms=scan_ms, attn_ms=attn_ms, merge_ms=merge_ms,
-                scan_launch_bytes=scan_launch_bytes, scan_gbs=scan_gbs, layers=layers, bufs=bufs)
+    return dict(ms=ms, ms_sep=ms_sep, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
+                n_split=bufs[0].n_split, lists_ms=lists_ms, scan_ms=scan_ms, scan_launch_bytes=scan_launch_bytes,
+                lists_gbs=scan_launch_bytes / (lists_ms * 1e-3) / 1e9, layers=layers, bufs=bufs)
 
 
 def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
@@ -321,7 +317,7 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
     return out
 
 
-COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_decode_1M_b4_prefill_tile.txt")
+COUNTERS = os.path.join(ROOT, "profiles", "hbm_counters_decode_1M_b4_prefill_tile_mla.txt")
 
 
 def counter_traffic(kernel: str, groups: str):
@@ -418,7 +414,8 @@ def main():
 
     t_all = time.time()
     dec = run_decode(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
-    log(f"decode: {dec['ms']:.4f} ms/step, scan+select {dec['scan_ms'] * 1e3:.1f} us/launch")
+    log(f"decode: {dec['ms']:.4f} ms/step (separate calls {dec['ms_sep']:.4f}), "
+        f"scan {dec['lists_ms'] * 1e3:.1f} us/launch")
     del dec["layers"], dec["bufs"]
     torch.cuda.empty_cache()
     pre, pflops = run_prefill(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
@@ -451,10 +448,11 @@ def main():
         "hbm_gbs": round(hbm_gbs, 1),
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "step_bytes": dec["step_bytes"],
-        "one_launch_layer_ms_per_step": round(dec["ms_fused"], 5),
-        "breakdown_us_per_layer": {"scan_select": round(dec["scan_ms"] * 1e3, 2),
-                                   "attend": round(dec["attn_ms"] * 1e3, 2),
-                                   "merge": round(dec["merge_ms"] * 1e3, 2)},
+        "separate_calls_ms_per_step": round(dec["ms_sep"], 5),
+        "breakdown_us_per_layer": {"scan_lists": round(dec["lists_ms"] * 1e3, 2),
+                                   "select_attend_merge": round(dec["ms"] * 1e3 / DECODE["layers"]
+                                                                - dec["lists_ms"] * 1e3, 2),
+                                   "separate_scan_select": round(dec["scan_ms"] * 1e3, 2)},
         "pool_ms_all_layers": round(dec["pool_ms"], 3),
         "prefill": {"workload": PREFILL["name"], "tok_s": round(t8["tok_s"], 1), "ms_per_chunk": round(t8["ms"], 4),
                     "tflops": round(t8["tflops"], 2), "mfma_frac": round(t8["tflops"] / BF16_PEAK_TFLOPS, 5),
@@ -462,11 +460,12 @@ def main():
                     "breakdown_us": pre["breakdown_us"], "attend_tflops": pre["attend_tflops"],
                     "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)}},
         "mla": mla,
-        "roofline": {"kernel": "index_topk_a (pooled-key scan + exact top-512, one launch)", "bound": "hbm",
-                     "achieved": round(dec["scan_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(dec["scan_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic("index_topk_a<4>", "1024"),
-                     "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["scan_ms"] * 1e3, 3)},
+        "roofline": {"kernel": "index_lists_a (pooled-key scan + per-chunk candidate lists, first launch of "
+                               "qsa_decode_layer)", "bound": "hbm",
+                     "achieved": round(dec["lists_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dec["lists_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": counter_traffic("index_lists_a<2>", "2048"),
+                     "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["lists_ms"] * 1e3, 3)},
         "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "wall_s": round(time.time() - t_all, 1),
     }

@@ -191,6 +191,26 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
 
 size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx);
 
+/* --------------------------------------------- A2 + chunk lists of A3 ----
+ * qsa_index_lists: the pooled-key scan that qsa_decode_layer issues first,
+ * on its own: writes scores[i][b] for b < n_i (as qsa_index_scores) and, in
+ * the workspace, each chunk's best candidate blocks with a bound (the best
+ * block it left out); it selects nothing (sel / n_sel are not written).
+ * qsa_decode_layer continues from such lists inside its own workspace;
+ * calling this entry point separately lets a caller time or schedule the
+ * scan on its own. ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの":
+ * every pooled key is scored at every step.)
+ * Variant A only (block 4, idx_dim 128, idx_heads 1).
+ *   q_seq, q_ctx, q_idx, keys, scores, ld_scores: as qsa_index_scores.
+ *   ws (device) workspace of at least qsa_index_topk_workspace_bytes(cfg,
+ *      nq, max_ctx) bytes; contents ignored on entry, list layout internal.
+ *      Calls that share a workspace must not run concurrently. */
+qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq,
+                           const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
+                           const qsa_bf16* keys, int64_t keys_seq_stride,
+                           float* scores, int64_t ld_scores,
+                           void* ws, size_t ws_bytes, qsa_stream_t stream);
+
 /* ---------------------------------------------------------------- A4 ----
  * qsa_sparse_decode: softmax attention of each query over its selected
  * tokens, split into n_split partial results.
@@ -215,12 +235,13 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
                              float* o_part, float* lse_part, qsa_stream_t stream);
 
 /* ------------------------------------------------- A2 + A3 + A4 + A5 ----
- * qsa_decode_layer: one decode layer in one launch: exactly what
- * qsa_index_topk, then qsa_sparse_decode with n_split parts, then
- * qsa_lse_merge of those parts compute, with the parts held in the
- * workspace. Work items (scan chunks of each query, then its attention
- * parts) start in a fixed order; the attention of query i starts as soon as
- * its selection is complete and overlaps the scans of later queries.
+ * qsa_decode_layer: one decode layer: exactly what qsa_index_topk, then
+ * qsa_sparse_decode with n_split parts, then qsa_lse_merge of those parts
+ * compute, with the parts held in the workspace. Two launches: the scan
+ * (qsa_index_lists), then one work-group per (query, kv head, split) that
+ * selects the query's blocks from the chunk lists itself, attends its part
+ * and merges with the other parts in the same launch (a third launch merges
+ * when the parts cannot all be resident at once).
  * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの" and "なぜ";
  * "GLM-5.3 ...", "DCP".)
  * Variant A only (block 4, idx_dim 128, idx_heads 1; hq 16, hkv 2, dk = dv
@@ -235,10 +256,12 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
  *   ws (device) workspace of at least qsa_decode_layer_workspace_bytes(...)
  *      bytes, zero before the first call; every completed call leaves its
  *      counters zero again. Calls sharing a workspace must not overlap.
- *      Waits inside the launch are bounded: if one runs out (which only a
- *      corrupted workspace can cause) a sticky error word in the workspace
- *      is set, results are unspecified, and with QSA_SYNC_CHECK=1 the call
- *      returns QSA_ERR_LAUNCH; zero the workspace to clear it. */
+ *      The parts of a (query, kv head) wait for each other before they
+ *      merge; the wait is bounded: if it runs out (which only a corrupted
+ *      workspace or a device shared with other work can cause) a sticky
+ *      error word in the workspace is set, results are unspecified, and
+ *      with QSA_SYNC_CHECK=1 the call returns QSA_ERR_LAUNCH; zero the
+ *      workspace to clear it. */
 qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
                             const qsa_bf16* q_idx, const qsa_bf16* keys, int64_t keys_seq_stride,

@@ -313,6 +313,47 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
   return finish(qsa::launch_index_topk(a, plan, ws, s), s, "qsa_index_topk");
 }
 
+qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
+                           int32_t max_ctx, const qsa_bf16* q_idx, const qsa_bf16* keys, int64_t keys_seq_stride,
+                           float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, qsa_stream_t stream) {
+  qsa_status st = check_sel_cfg(cfg);
+  if (st != QSA_OK) return st;
+  if (cfg->block != 4 || cfg->idx_dim != 128 || cfg->idx_heads != 1)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_index_lists: only pooled 4-token blocks with a 128-d single-head indexer");
+  if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
+  if (nq == 0) return QSA_OK;
+  if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
+  if (!q_ctx || !q_idx || !keys || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores))
+    return fail(QSA_ERR_ARG, "q_idx, keys and scores must be 16-byte aligned");
+  const int64_t nmax = int64_t(max_ctx) / 4;
+  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
+  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
+  if (q_seq && keys_seq_stride < nmax * 128) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / 4 keys");
+  const qsa::IndexTopkPlan plan = qsa::plan_index_topk(nq, max_ctx, cfg->topk);
+  if (plan.n_chunks > 65535) return fail(QSA_ERR_UNSUPPORTED, "context too long");
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+  if (!aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::IndexTopkArgs a{};
+  a.q_seq = q_seq;
+  a.q_ctx = q_ctx;
+  a.max_ctx = max_ctx;
+  a.nq = nq;
+  a.q_idx = q_idx;
+  a.keys = keys;
+  a.keys_ss = keys_seq_stride;
+  a.scores = scores;
+  a.ld = ld_scores;
+  a.topk = cfg->topk;
+  return finish(qsa::launch_index_lists(a, plan, ws, s), s, "qsa_index_lists");
+}
+
 size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                                         int32_t max_ctx, int32_t n_split) {
   if (!sel_cfg || !attn_cfg || nq <= 0 || max_ctx < 0 || n_split < 1 || attn_cfg->hq <= 0 || attn_cfg->hkv <= 0 ||

@@ -4,9 +4,10 @@
 // only their K/V rows are read (section "なぜ"); "GLM-5.3 最適化 第2部",
 // section "DCP": the partial attention results are merged by log-sum-exp.
 //
-// Launch 1 (index_lists_a): each work-group scores one chunk of one query's
-// pooled keys and writes the chunk's best candidates and a bound
-// (index_topk.hpp, without the selection).
+// Launch 1 (index_lists_a, also qsa_index_lists on its own): each
+// work-group scores one chunk of one query's pooled keys and writes the
+// chunk's best candidates and a bound (index_topk.hpp, without the
+// selection).
 //
 // Launch 2 (attend_select_a): one work-group per (query, kv head, split).
 // Every work-group selects its query's exact top-k itself, from the chunk
@@ -116,6 +117,27 @@ int resident_groups() {
 
 }  // namespace
 
+hipError_t launch_index_lists(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  char* w = static_cast<char*>(ws);
+  a.counter = reinterpret_cast<uint32_t*>(w);
+  a.list = reinterpret_cast<uint64_t*>(w + p.off_list);
+  a.list_bound = reinterpret_cast<uint64_t*>(w + p.off_bound);
+  a.n_chunks = p.n_chunks;
+  a.chunk_blocks = 256 * p.tpw;
+  a.keep = p.keep;
+  a.wkeep = p.wkeep;
+  dim3 grid(unsigned(p.n_chunks), unsigned(a.nq));
+  switch (p.tpw) {
+    case 1: hipLaunchKernelGGL(index_lists_a<1>, grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL(index_lists_a<2>, grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL(index_lists_a<4>, grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL(index_lists_a<8>, grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL(index_lists_a<16>, grid, dim3(256), 0, s, a); break;
+  }
+  return hipGetLastError();
+}
+
 DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv, int dv, int n_split) {
   DecodeLayerPlan p{};
   p.itk = plan_index_topk(nq, max_ctx, topk);
@@ -140,13 +162,6 @@ hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLa
   if (itk.nq <= 0) return hipSuccess;
   char* w = static_cast<char*>(ws);
   char* wi = w + p.off_itk;
-  itk.counter = reinterpret_cast<uint32_t*>(wi);
-  itk.list = reinterpret_cast<uint64_t*>(wi + p.itk.off_list);
-  itk.list_bound = reinterpret_cast<uint64_t*>(wi + p.itk.off_bound);
-  itk.n_chunks = p.itk.n_chunks;
-  itk.chunk_blocks = 256 * p.itk.tpw;
-  itk.keep = p.itk.keep;
-  itk.wkeep = p.itk.wkeep;
   att.o_part = reinterpret_cast<float*>(w + p.off_o);
   att.lse_part = reinterpret_cast<float*>(w + p.off_lse);
   att.error = reinterpret_cast<uint32_t*>(w);
@@ -154,16 +169,15 @@ hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLa
   const bool merge_in = n_att_all <= resident_groups();
   att.counter = merge_in ? reinterpret_cast<uint32_t*>(w + p.off_merge_cnt) : nullptr;
 
-  dim3 grid(unsigned(p.itk.n_chunks), unsigned(itk.nq));
-  switch (p.itk.tpw) {
-    case 1: hipLaunchKernelGGL(index_lists_a<1>, grid, dim3(256), 0, s, itk); break;
-    case 2: hipLaunchKernelGGL(index_lists_a<2>, grid, dim3(256), 0, s, itk); break;
-    case 4: hipLaunchKernelGGL(index_lists_a<4>, grid, dim3(256), 0, s, itk); break;
-    case 8: hipLaunchKernelGGL(index_lists_a<8>, grid, dim3(256), 0, s, itk); break;
-    default: hipLaunchKernelGGL(index_lists_a<16>, grid, dim3(256), 0, s, itk); break;
-  }
-  hipError_t e = hipGetLastError();
+  hipError_t e = launch_index_lists(itk, p.itk, wi, s);
   if (e != hipSuccess) return e;
+  itk.counter = reinterpret_cast<uint32_t*>(wi);
+  itk.list = reinterpret_cast<uint64_t*>(wi + p.itk.off_list);
+  itk.list_bound = reinterpret_cast<uint64_t*>(wi + p.itk.off_bound);
+  itk.n_chunks = p.itk.n_chunks;
+  itk.chunk_blocks = 256 * p.itk.tpw;
+  itk.keep = p.itk.keep;
+  itk.wkeep = p.itk.wkeep;
   hipLaunchKernelGGL(attend_select_a, dim3(unsigned(n_att_all)), dim3(256), 0, s, itk, att);
   e = hipGetLastError();
   if (e != hipSuccess || merge_in) return e;

@@ -112,6 +112,8 @@ struct IndexTopkPlan {
 };
 IndexTopkPlan plan_index_topk(int nq, int max_ctx, int topk);
 hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, hipStream_t s);
+// The scan and chunk lists alone (no selection), into an index_topk workspace.
+hipError_t launch_index_lists(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, hipStream_t s);
 
 
 // One decode layer (variant A): scan with chunk lists, then attention whose

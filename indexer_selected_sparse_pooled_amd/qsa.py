@@ -60,6 +60,7 @@ _SIGS = {
     "qsa_topk_workspace_bytes": [_vp, _i32, _i32],
     "qsa_index_topk": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
     "qsa_index_topk_workspace_bytes": [_vp, _i32, _i32],
+    "qsa_index_lists": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
     "qsa_decode_layer": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i32,
                          _vp, _vp, _vp, _vp, _sz, _vp],
     "qsa_decode_layer_workspace_bytes": [_vp, _vp, _i32, _i32, _i32],
@@ -209,6 +210,22 @@ def qsa_index_topk(cfg, q_ctx, max_ctx, q_idx, keys, scores, sel, n_sel, ws, q_s
         _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0),
         _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"),
         ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qsa_index_lists(cfg, q_ctx, max_ctx, q_idx, keys, scores, ws, q_seq=None, stream=None):
+    """The scan qsa_decode_layer issues first, on its own: scores and the
+    chunk candidate lists (in ws: index_topk_workspace(...)); no selection."""
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(q_idx, "q_idx", 3)
+    _rowmajor_tail(keys, "keys", 2)
+    _rowmajor_tail(scores, "scores", 1)
+    if max_ctx // cfg.block > keys.shape[1]:
+        raise ValueError("qsa_index_lists: keys hold fewer than max_ctx / block rows")
+    _check("qsa_index_lists", lib().qsa_index_lists(
+        ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
+        _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0),
+        _dev(scores, _F32, "scores"), scores.stride(0), ctypes.c_void_p(ws.data_ptr()),
+        ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def qsa_decode_layer_workspace_bytes(sel_cfg, attn_cfg, nq, max_ctx, n_split) -> int:

@@ -161,3 +161,35 @@ def test_index_topk_all_equal_keys(pkg):
     sel = fused[1].cpu().numpy()[0]
     assert np.array_equal(sel, np.arange(512))
     _check(pkg, [4 * n_blk], [0], keys, q_idx, fused, check_scores=False)
+
+
+def test_index_lists_scores_match_index_scores(pkg):
+    """qsa_index_lists writes the same scores as qsa_index_scores (bit for
+    bit), nothing past each query's candidates, and leaves sel alone; a
+    qsa_index_topk call on the same workspace afterwards still selects
+    exactly (the lists are rewritten each call)."""
+    ctxs = [1048320, 600004, 70001, 4096, 3]
+    q_seq = [0, 1, 1, 0, 1]
+    _print_case("index_lists", ctxs=ctxs)
+    n_blk = max(ctxs) // 4
+    keys = _keys(2, n_blk, qi.config_seed(3))
+    q_idx = torch.empty(len(ctxs), 1, 128, dtype=torch.bfloat16, device="cuda")
+    from qsa_inputs.gpu import fill_normal_bf16
+    fill_normal_bf16(q_idx, qi.config_seed(3), qi.stream_id(0, 9, "q_idx"))
+    nq, max_ctx = len(ctxs), max(ctxs)
+    ld = max_ctx // 4 + 5
+    ws = pkg.index_topk_workspace(pkg.SEL_A, nq, max_ctx)
+    scores = torch.full((nq, ld), float("nan"), device="cuda")
+    pkg.qsa_index_lists(pkg.SEL_A, qc.i32(ctxs), max_ctx, q_idx, keys, scores, ws, q_seq=qc.i32(q_seq))
+    ref = torch.full((nq, ld), float("nan"), device="cuda")
+    pkg.qsa_index_scores(pkg.SEL_A, qc.i32(ctxs), max_ctx, q_idx, keys, ref, q_seq=qc.i32(q_seq))
+    torch.cuda.synchronize()
+    a, b = scores.cpu().numpy(), ref.cpu().numpy()
+    for i, ctx in enumerate(ctxs):
+        n = ctx // 4
+        assert np.array_equal(a[i, :n].view(np.uint32), b[i, :n].view(np.uint32)), f"query {i}: scores differ"
+        assert np.all(np.isnan(a[i, n:])), f"query {i}: wrote past the candidates"
+    fused = _run_fused(pkg, ctxs, q_seq, keys, q_idx, ws=ws)
+    unfused = _run_unfused(pkg, ctxs, q_seq, keys, q_idx)
+    for x, y in zip(fused[1:], unfused[1:]):
+        assert torch.equal(x, y)
