@@ -2,7 +2,7 @@
 // dim 256): softmax attention of one query and one kv head over a part of
 // its selected tokens, optionally followed by the log-sum-exp merge of all
 // parts. Used by the stand-alone attention kernel (attend.hip) and by the
-// one-launch decode layer (decode_layer.hip).
+// decode layer (decode_layer.hip).
 //
 // "3090x3で 314 万コンテキスト": only the indexer-selected K/V rows are read
 // (section "なぜ"), addressed per (token, kv head) (section "カーネルを書き換え
@@ -118,9 +118,8 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
   lv.block = a.block;
   lv.nblk = ctx / a.block;
   const int ns_max = lv.nblk < a.topk ? lv.nblk : a.topk;
-  // inside the one-launch layer the selection is this launch's own, which
-  // always holds min(complete blocks, topk) entries: no need to wait for
-  // n_sel to arrive
+  // a selection made in this launch (sel_lds, or kCoh) always holds
+  // min(complete blocks, topk) entries: no need to read n_sel
   const int ns = sel_lds ? ns_lds : (kCoh ? ns_max : a.n_sel[i]);
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.cache = sel_lds;

@@ -1,6 +1,6 @@
 // Device code of A2 + A3 for decode: the pooled-key scan and the exact top-k
 // of one chunk of one query (index_topk.hip launches it on its own,
-// decode_layer.hip inside the one-launch decode layer).
+// decode_layer.hip as the decode layer's first launch, without the selection).
 // "3090x3で 314 万コンテキスト", section "VRAM に残す必要があるもの": every
 // pooled key (128 x bf16 per block) is scored at every step, so the scan is
 // a bandwidth-bound stream; section "なぜ": the indexer then keeps a fixed
@@ -45,8 +45,8 @@
 namespace qsa {
 namespace itk {
 
-// Selections are written with agent-coherent stores: in the one-launch
-// decode layer other work-groups read them in the same launch.
+// Selections are written with agent-coherent stores, as every hand-off
+// between work-groups of one launch is.
 __device__ __forceinline__ void st_sel(int* p, int v) { st_coherent(reinterpret_cast<uint32_t*>(p), uint32_t(v)); }
 
 // Every thread's stores are complete before the work-group goes on.

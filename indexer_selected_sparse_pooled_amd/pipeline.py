@@ -1,7 +1,7 @@
 """The hot path as a chain of libqsa calls.
 
 A decode layer is A2 -> A3 -> A4 -> A5 (scores, top-k, split attention,
-merge): one qsa_decode_layer launch for the pooled-block variant, or the
+merge): one qsa_decode_layer call for the pooled-block variant, or the
 separate calls; a prefill chunk is A2 -> A3 -> A6 per history tile -> A5. Buffers
 are allocated once with torch and reused; every step runs in libqsa's
 kernels, enqueued on one stream with no host synchronisation, so a whole
@@ -22,8 +22,8 @@ class DecodeBuffers:
     sel: torch.Tensor       # [nq, topk] int32
     n_sel: torch.Tensor     # [nq] int32
     ws: torch.Tensor        # top-k workspace (or None)
-    itk_ws: torch.Tensor    # zero-filled workspace of the one-launch scan + top-k (or None)
-    layer_ws: torch.Tensor  # zero-filled workspace of the one-launch decode layer (or None)
+    itk_ws: torch.Tensor    # zero-filled workspace of qsa_index_topk / qsa_index_lists (or None)
+    layer_ws: torch.Tensor  # zero-filled workspace of qsa_decode_layer (or None)
     o_part: torch.Tensor    # [n_split, nq, hq, dv] fp32
     lse_part: torch.Tensor  # [n_split, nq, hq] fp32
     o: torch.Tensor         # [nq, hq, dv] fp32
@@ -77,9 +77,10 @@ def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") 
 def decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: DecodeBuffers,
                  q_seq=None, w_idx=None, stream=None, fused=False) -> None:
     """One decode layer for nq queries (one per sequence): results in bufs.o / o_bf16 / lse.
-    fused=True issues the layer as one qsa_decode_layer launch (same results;
-    on the 1M-context batch-4 step it is as fast as the separate launches,
-    not faster, because every query's scan ends at about the same time)."""
+    fused=True issues the layer as one qsa_decode_layer call (same results;
+    two launches instead of three, and the attention work-groups select
+    their query's blocks themselves, so no selection is written and re-read
+    in between)."""
     if fused and bufs.layer_ws is not None and w_idx is None:
         qsa.qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs.scores, bufs.sel,
                              bufs.n_sel, bufs.n_split, bufs.layer_ws, o_out=bufs.o, o_out_bf16=bufs.o_bf16,

@@ -5,7 +5,7 @@ Runs, each `--reps` times, on seeded synthetic inputs already in HBM:
     the memory counters (it reads and writes exactly 268,435,456 bytes);
   * one layer of the 1,048,320-token batch-4 decode step: qsa_index_topk
     (pooled-key scan + exact top-512), qsa_sparse_decode, qsa_lse_merge,
-    and the same layer as one qsa_decode_layer launch;
+    and the same layer as one qsa_decode_layer call (two launches);
   * one history tile of the 4096-query prefill chunk (qsa_sparse_prefill);
   * the shared-latent prefill attention of 2048 queries at context 131,072
     (one qsa_sparse_prefill over the whole history).

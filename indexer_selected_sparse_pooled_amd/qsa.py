@@ -242,7 +242,7 @@ def decode_layer_workspace(sel_cfg, attn_cfg, nq, max_ctx, n_split, device="cuda
 
 def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel, n_split, ws,
                      o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
-    """One decode layer in one launch: qsa_index_topk, then qsa_sparse_decode
+    """One decode layer (two launches): qsa_index_topk, then qsa_sparse_decode
     and qsa_lse_merge. q_idx: [nq, 1, 128] bf16; keys: [n_seq, n_blocks, 128]
     bf16; q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk;
     o_out: [nq, hq, dv] fp32, o_out_bf16: [nq, hq, dv] bf16, lse_out: [nq, hq]

@@ -80,7 +80,7 @@ def _check_against_oracle(bufs, refs, ctxs, q_bits, k_rows, v_rows):
 @pytest.mark.parametrize("n_split", [1, 3, 32, 64])
 def test_decode_layer_mixed_contexts(Q, n_split):
     """Full attention (ctx <= 2051), trailing tokens, an empty context and
-    long contexts in one launch."""
+    long contexts in one call."""
     pkg, pipeline = Q
     ctxs = [8195, 2051, 2052, 3, 0, 40000, 8192, 131071]
     _print_case("decode_layer_mixed", n_split=n_split)
