@@ -161,8 +161,29 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
 
     lists_ms = time_launches(torch, lists_only, reps) / len(layers)
     scan_ms = time_launches(torch, scan_select_only, reps) / len(layers)
+    # the step with the cache write in front of each layer: the token at
+    # position L - 1 (its K/V rows, raw key, and the pooled key of the block
+    # it completes), as a decode step does before the layer reads the cache
+    seed = qi.config_seed(DECODE["config_id"])
+    k_new = torch.empty(B, 2, 256, dtype=torch.bfloat16, device="cuda")
+    v_new = torch.empty_like(k_new)
+    raw_new = torch.empty(B, 128, dtype=torch.bfloat16, device="cuda")
+    fill(k_new, seed, qi.stream_id(99, 0, "k"))
+    fill(v_new, seed, qi.stream_id(99, 0, "v"))
+    fill(raw_new, seed, qi.stream_id(99, 0, "raw_key"))
+    q_pos = q_ctx - 1
+
+    def step_append():
+        for lay, bf in zip(layers, bufs):
+            pkg.qsa_kv_append(pkg.SEL_A, pkg.ATTN_A, q_pos, k_new, lay["kv"], v_new=v_new, raw_new=raw_new,
+                              raw_keys=lay["raw"], pooled=lay["pooled"], q_seq=q_seq)
+            pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay["q_idx"], lay["pooled"], lay["q"], lay["kv"],
+                                  bf, q_seq=q_seq, fused=True)
+
+    ms_app, _, graph = time_graph(torch, step_append, max(10, steps // 2), warmup)
+    del graph
     scan_launch_bytes = B * (bm.scan_bytes(L) + 128 * 2)
-    return dict(ms=ms, ms_sep=ms_sep, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
+    return dict(ms=ms, ms_sep=ms_sep, ms_app=ms_app, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
                 n_split=bufs[0].n_split, lists_ms=lists_ms, scan_ms=scan_ms, scan_launch_bytes=scan_launch_bytes,
                 lists_gbs=scan_launch_bytes / (lists_ms * 1e-3) / 1e9, layers=layers, bufs=bufs)
 
@@ -449,6 +470,7 @@ def main():
         "hbm_frac": round(hbm_gbs / HBM_PEAK_GBS, 4),
         "step_bytes": dec["step_bytes"],
         "separate_calls_ms_per_step": round(dec["ms_sep"], 5),
+        "with_kv_append_ms_per_step": round(dec["ms_app"], 5),
         "breakdown_us_per_layer": {"scan_lists": round(dec["lists_ms"] * 1e3, 2),
                                    "select_attend_merge": round(dec["ms"] * 1e3 / DECODE["layers"]
                                                                 - dec["lists_ms"] * 1e3, 2),

@@ -122,6 +122,36 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride,
                          int32_t n_seq, int64_t tok_begin, int64_t tok_end,
                          int32_t dim, int32_t block, qsa_stream_t stream);
 
+/* ------------------------------------------------- A1 at decode time ----
+ * qsa_kv_append: the decode step's write of one new token per query into
+ * the cache, before the layer reads it. Query i writes, at position
+ * q_pos[i] of sequence q_seq[i] (sequence i if q_seq is NULL):
+ *   - its K row for every kv head (k_new[i], hkv x dk) and, unless the
+ *     cache's v is its k (a shared latent row), its V row (v_new[i],
+ *     hkv x dv), addressed as in qsa_kv;
+ *   - its raw indexer key (raw_new[i], idx_dim values) at raw_keys +
+ *     seq * raw_seq_stride + pos * idx_dim, when raw_new is given;
+ *   - when pos + 1 is a multiple of block and pooled is given, the pooled
+ *     key of the block it completes, bit-identical to qsa_pool_keys over the
+ *     same raw keys (the block's earlier tokens are read from raw_keys).
+ * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの": pooled keys stay
+ * device-resident and the raw keys are kept so that blocks can be pooled;
+ * "カーネルを書き換えずに済む": per (token, kv head) addressing.)
+ *   q_seq (device) int32 [nq] or NULL; q_pos (device) int32 [nq], positions
+ *          in [0, kv->capacity): a query with another position writes
+ *          nothing. At most one query per sequence per call (a block's
+ *          pooling reads the sequence's earlier tokens).
+ *   k_new, v_new, raw_new (device) bf16 rows as above; v_new must be NULL
+ *          exactly when kv->v == kv->k. raw_new, raw_keys: both or neither;
+ *          pooled needs them, and block 4 (NULL for block 1, where the raw
+ *          key is the indexer key).
+ * Graph-capturable: positions are read on the device at replay. */
+qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                         const int32_t* q_seq, const int32_t* q_pos, const qsa_bf16* k_new,
+                         const qsa_bf16* v_new, const qsa_bf16* raw_new, const qsa_kv* kv,
+                         qsa_bf16* raw_keys, int64_t raw_seq_stride, qsa_bf16* pooled,
+                         int64_t pooled_seq_stride, qsa_stream_t stream);
+
 /* ---------------------------------------------------------------- A2 ----
  * qsa_index_scores: indexer scores of every candidate block for nq queries.
  * Query i reads the keys of sequence q_seq[i] and has n_i = q_ctx[i] / block

@@ -9,6 +9,6 @@ from .qsa import (  # noqa: F401
     ATTN_A, ATTN_B, SEL_A, SEL_B, AttnCfg, QsaError, SelCfg, decode_layer_workspace, make_kv,
     qsa_decode_layer, qsa_decode_layer_workspace_bytes, qsa_index_scores,
     qsa_index_topk, qsa_index_topk_workspace_bytes, index_topk_workspace, qsa_index_lists,
-    qsa_lse_merge, qsa_pool_keys, qsa_sparse_decode, qsa_sparse_prefill, qsa_topk_blocks,
+    qsa_kv_append, qsa_lse_merge, qsa_pool_keys, qsa_sparse_decode, qsa_sparse_prefill, qsa_topk_blocks,
     qsa_topk_workspace_bytes, qsa_version, topk_workspace,
 )

@@ -185,6 +185,73 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride, qsa_bf16* 
                 "qsa_pool_keys");
 }
 
+qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                         const int32_t* q_seq, const int32_t* q_pos, const qsa_bf16* k_new,
+                         const qsa_bf16* v_new, const qsa_bf16* raw_new, const qsa_kv* kv,
+                         qsa_bf16* raw_keys, int64_t raw_seq_stride, qsa_bf16* pooled,
+                         int64_t pooled_seq_stride, qsa_stream_t stream) {
+  qsa_status st = check_sel_cfg(sel_cfg);
+  if (st != QSA_OK) return st;
+  if (!attn_cfg || !kv) return fail(QSA_ERR_ARG, "attn_cfg or kv is NULL");
+  if (nq < 0) return fail(QSA_ERR_ARG, "negative nq");
+  if (nq == 0) return QSA_OK;
+  if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
+  const int hkv = attn_cfg->hkv, dk = attn_cfg->dk, dv = attn_cfg->dv;
+  if (hkv <= 0 || dk <= 0 || dv <= 0 || dk % 8 || dv % 8 || dv > dk)
+    return fail(QSA_ERR_ARG, "hkv, dk, dv must be positive multiples of 8 with dv <= dk");
+  if (!q_pos || !k_new || !kv->k) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  const bool shared = kv->v == kv->k;  // a latent row serves as K and (its first dv columns) V
+  if (!shared && (!v_new || !kv->v)) return fail(QSA_ERR_ARG, "v_new and kv->v are required when v != k");
+  if (shared && v_new) return fail(QSA_ERR_ARG, "v_new must be NULL when kv->v == kv->k");
+  if (!aligned16(k_new) || (v_new && !aligned16(v_new)) || !aligned16(kv->k) || !aligned16(kv->v))
+    return fail(QSA_ERR_ARG, "k_new, v_new, k and v must be 16-byte aligned");
+  if (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 || kv->head_stride < 0 ||
+      kv->seq_stride < 0)
+    return fail(QSA_ERR_ARG, "kv strides must be non-negative multiples of 8");
+  if (int64_t(hkv - 1) * kv->head_stride + dk > kv->tok_stride) return fail(QSA_ERR_ARG, "tok_stride too small");
+  if (kv->capacity <= 0 || kv->capacity > 0x7FFFFFFF) return fail(QSA_ERR_ARG, "bad kv capacity");
+  const int dim = sel_cfg->idx_dim;
+  if (raw_new || raw_keys) {
+    if (!raw_new || !raw_keys) return fail(QSA_ERR_ARG, "raw_new and raw_keys go together");
+    if (!aligned16(raw_new) || !aligned16(raw_keys)) return fail(QSA_ERR_ARG, "raw_new and raw_keys must be 16-byte aligned");
+    if (raw_seq_stride % 8 || raw_seq_stride < 0) return fail(QSA_ERR_ARG, "raw_seq_stride must be a multiple of 8");
+    if (pooled) {
+      if (sel_cfg->block == 1) return fail(QSA_ERR_ARG, "pooled must be NULL when block == 1");
+      if (!aligned16(pooled)) return fail(QSA_ERR_ARG, "pooled must be 16-byte aligned");
+      if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return fail(QSA_ERR_ARG, "pooled_seq_stride must be a multiple of 8");
+    }
+  } else if (pooled) {
+    return fail(QSA_ERR_ARG, "pooling needs raw_new and raw_keys");
+  }
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  qsa::AppendArgs a{};
+  a.nq = nq;
+  a.q_seq = q_seq;
+  a.q_pos = q_pos;
+  a.capacity = int(kv->capacity);
+  a.k_new = k_new;
+  a.v_new = shared ? nullptr : v_new;
+  a.raw_new = raw_new;
+  a.k = const_cast<qsa_bf16*>(kv->k);
+  a.v = const_cast<qsa_bf16*>(kv->v);
+  a.seq_stride = kv->seq_stride;
+  a.tok_stride = kv->tok_stride;
+  a.head_stride = kv->head_stride;
+  a.k_row = hkv * dk;
+  a.v_row = hkv * dv;
+  a.head_dim = dk;
+  a.v_dim = dv;
+  a.raw = raw_keys;
+  a.raw_ss = raw_seq_stride;
+  a.pooled = pooled;
+  a.pooled_ss = pooled_seq_stride;
+  a.dim = dim;
+  a.block = sel_cfg->block;
+  return finish(qsa::launch_append(a, s), s, "qsa_kv_append");
+}
+
 qsa_status qsa_index_scores(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
                             int32_t max_ctx, const qsa_bf16* q_idx, const float* w_idx, const qsa_bf16* keys,
                             int64_t keys_seq_stride, float* scores, int64_t ld_scores, qsa_stream_t stream) {

@@ -11,6 +11,28 @@ namespace qsa {
 hipError_t launch_pool(const uint16_t* raw, int64_t raw_ss, uint16_t* pooled, int64_t pooled_ss,
                        int n_seq, int64_t b0, int64_t nb, int dim, int block, hipStream_t s);
 
+// Decode-step append (one new token per query).
+struct AppendArgs {
+  int nq;
+  const int* q_seq;  // nullable: query i appends to sequence i
+  const int* q_pos;  // [nq] position of the new token
+  int capacity;      // token rows per sequence
+  const uint16_t* k_new;    // [nq][k_row]
+  const uint16_t* v_new;    // [nq][v_row] or nullptr
+  const uint16_t* raw_new;  // [nq][dim] or nullptr
+  uint16_t* k;
+  uint16_t* v;
+  int64_t seq_stride, tok_stride, head_stride;
+  int k_row, v_row;         // elements per token row: hkv * head_dim, hkv * v_dim
+  int head_dim, v_dim;
+  uint16_t* raw;            // raw indexer keys, or nullptr
+  int64_t raw_ss;
+  uint16_t* pooled;         // pooled keys, or nullptr (no pooling)
+  int64_t pooled_ss;
+  int dim, block;
+};
+hipError_t launch_append(const AppendArgs& a, hipStream_t s);
+
 struct ScoreArgs {
   const int* q_seq;   // nullable
   const int* q_ctx;

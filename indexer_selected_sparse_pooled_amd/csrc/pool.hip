@@ -1,7 +1,12 @@
-// A1: pooled indexer keys, one per complete block of tokens.
+// A1: pooled indexer keys, one per complete block of tokens, and the decode
+// step's append of a new token (its K/V rows, its raw indexer key, and the
+// pooled key of the block it completes).
 // "3090x3で 314 万コンテキスト", section "VRAM に残す必要があるもの": each
-// block's keys are summarised into one 128 x bf16 pooled key; here the
-// summary is the exact mean rounded once to bf16 (nearest, ties to even).
+// block's keys are summarised into one 128 x bf16 pooled key, kept in VRAM
+// and completed as tokens arrive (the raw keys are kept so a block can be
+// pooled); here the summary is the exact mean rounded once to bf16
+// (nearest, ties to even). Section "カーネルを書き換えずに済む": the cache is
+// addressed per (token, kv head).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -54,7 +59,71 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   st16(pooled + s * pooled_ss + b * dim + 8 * c, out);
 }
 
+// One work-group per appended token (query i): copies the token's K and V
+// rows (every kv head) and its raw indexer key into the cache at position
+// q_pos[i] of sequence q_seq[i]; when the token completes a block, also
+// writes the block's pooled key with pool_kernel's arithmetic (exact fp64
+// sum of the block's raw keys, mean rounded once to bf16). The block's
+// earlier tokens are read from the cache and the new one from its input
+// row, so the pooled key never depends on a store of this launch.
+__global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int seq = a.q_seq ? a.q_seq[i] : i;
+  const int pos = a.q_pos[i];
+  if (pos < 0 || pos >= a.capacity) return;  // a caller error: nothing is written
+  const int kc = a.k_row / 8, vc = a.v_row / 8, rc = a.dim / 8;
+  const uint16_t* kn = a.k_new + int64_t(i) * a.k_row;
+  const uint16_t* vn = a.v_new ? a.v_new + int64_t(i) * a.v_row : nullptr;
+  const uint16_t* rn = a.raw_new ? a.raw_new + int64_t(i) * a.dim : nullptr;
+  // rows of one token: kv head g at k + tok * tok_stride + g * head_stride
+  for (int c = tid; c < kc; c += 256) {
+    const int g = (8 * c) / a.head_dim, d = (8 * c) % a.head_dim;
+    st16(a.k + int64_t(seq) * a.seq_stride + int64_t(pos) * a.tok_stride + int64_t(g) * a.head_stride + d,
+         ld16(kn + 8 * c));
+  }
+  if (vn) {
+    for (int c = tid; c < vc; c += 256) {
+      const int g = (8 * c) / a.v_dim, d = (8 * c) % a.v_dim;
+      st16(a.v + int64_t(seq) * a.seq_stride + int64_t(pos) * a.tok_stride + int64_t(g) * a.head_stride + d,
+           ld16(vn + 8 * c));
+    }
+  }
+  if (!rn) return;
+  for (int c = tid; c < rc; c += 256)
+    st16(a.raw + int64_t(seq) * a.raw_ss + int64_t(pos) * a.dim + 8 * c, ld16(rn + 8 * c));
+  if (!a.pooled || (pos + 1) % a.block != 0) return;
+  const int64_t b = pos / a.block;
+  for (int c = tid; c < rc; c += 256) {
+    double acc[8];
+    u32x4 w = ld16(rn + 8 * c);
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      acc[2 * e] = double(bf16_lo(w[e]));
+      acc[2 * e + 1] = double(bf16_hi(w[e]));
+    }
+    for (int j = 0; j < a.block - 1; j++) {
+      w = ld16(a.raw + int64_t(seq) * a.raw_ss + (b * a.block + j) * a.dim + 8 * c);
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        acc[2 * e] += double(bf16_lo(w[e]));
+        acc[2 * e + 1] += double(bf16_hi(w[e]));
+      }
+    }
+    u32x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      out[e] = uint32_t(f64_to_bf16(acc[2 * e] / a.block)) | (uint32_t(f64_to_bf16(acc[2 * e + 1] / a.block)) << 16);
+    st16(a.pooled + int64_t(seq) * a.pooled_ss + b * a.dim + 8 * c, out);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(append_kernel, dim3(unsigned(a.nq)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_pool(const uint16_t* raw, int64_t raw_ss, uint16_t* pooled, int64_t pooled_ss,
                        int n_seq, int64_t b0, int64_t nb, int dim, int block, hipStream_t s) {

@@ -55,6 +55,7 @@ _lib = None
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "qsa_pool_keys": [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _i32, _vp],
+    "qsa_kv_append": [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_index_scores": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_topk_blocks": [_vp, _i32, _vp, _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
     "qsa_topk_workspace_bytes": [_vp, _i32, _i32],
@@ -269,6 +270,27 @@ def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scor
         _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_out, _F32, "o_out"), _dev(o_out_bf16, _BF16, "o_out_bf16"),
         _dev(lse_out, _F32, "lse_out"), ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
         _stream(stream)))
+
+
+def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None, raw_keys=None, pooled=None,
+                  q_seq=None, stream=None):
+    """Write one new token per query into the cache at q_pos (device int32
+    [nq]): k_new [nq, hkv, dk] (and v_new [nq, hkv, dv] unless the cache's v
+    is its k), raw_new [nq, idx_dim] into raw_keys [n_seq, capacity, idx_dim],
+    and the pooled key [n_seq, n_blocks, idx_dim] of each block a token
+    completes. kv: make_kv(...) of the cache."""
+    nq = q_pos.shape[0]
+    for t, name in ((k_new, "k_new"), (v_new, "v_new"), (raw_new, "raw_new")):
+        if t is not None and (t.shape[0] != nq or not t.is_contiguous()):
+            raise ValueError(f"qsa_kv_append: {name} must be contiguous with {nq} rows")
+    for t, name in ((raw_keys, "raw_keys"), (pooled, "pooled")):
+        if t is not None:
+            _rowmajor_tail(t, name, 2)
+    _check("qsa_kv_append", lib().qsa_kv_append(
+        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_pos, _I32, "q_pos"),
+        _dev(k_new, _BF16, "k_new"), _dev(v_new, _BF16, "v_new"), _dev(raw_new, _BF16, "raw_new"), ctypes.byref(kv),
+        _dev(raw_keys, _BF16, "raw_keys"), 0 if raw_keys is None else raw_keys.stride(0),
+        _dev(pooled, _BF16, "pooled"), 0 if pooled is None else pooled.stride(0), _stream(stream)))
 
 
 def make_kv(k, v=None):
