@@ -65,9 +65,10 @@ struct TopkArgs {
 // Workspace layout of the chunked (large-context) path.
 struct TopkPlan {
   bool chunked;      // false: every query is selected directly (or all taken)
+  bool filter;       // chunk lists keep every score above a sampled threshold (else the best list_len)
   int chunk;         // scores per chunk
   int n_chunks;      // chunks per query at max_ctx
-  int list_len;      // candidates kept per chunk
+  int list_len;      // candidates kept per chunk (capacity in filter mode)
   int final_threads; // work-group size of the per-query selection (256 or 1024)
   int direct_max;    // queries with at most this many candidates skip the chunk lists
   size_t ws_bytes;

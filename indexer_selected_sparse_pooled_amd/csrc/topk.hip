@@ -12,18 +12,32 @@
 //  * n <= 8192 (2048 when the lists of the larger queries are short): one
 //    work-group holds all keys in registers (8 per thread) and selects directly (radix threshold over LDS histograms that
 //    start below the keys' common prefix, then ordered positions).
-//  * larger n: (1) one work-group per chunk of 4096 scores (256 threads x 16
-//    registers) keeps the chunk's best L as a list in ascending index order,
-//    with a bound: the best element it left out; L is about twice a chunk's
-//    expected share of the top-k plus a margin. (2) One work-group per query
-//    selects the top-k of the union of the lists (at most 8192 entries, in
-//    registers; 256 threads when it holds at most 2048). With tau the topk-th best of the union, a chunk can hide a
-//    better element only if its bound ranks above tau; if none does, the
-//    union's top-k is the exact top-k. If the chunks only left out keys equal
-//    to the union's topk-th key (ties, e.g. many scores of exactly zero), one
-//    ordered pass over all n scores picks the smallest indices among them.
-//    Otherwise (rare: a chunk holding far more than its share) the query
-//    falls back to an exact radix select over all n scores read from memory.
+//  * larger n, threshold lists (when a chunk's list can hold twice its
+//    expected share): (0) one work-group per query reads 4096 of its scores
+//    (256 evenly spread runs of 16) and takes as threshold theta the sample
+//    key that about 1.75 x topk of all scores exceed; (1) one work-group per
+//    chunk of 4096 scores lists every score above theta, in index order (one
+//    prefix sum, no select), and counts the scores above and equal to theta;
+//    (2) one work-group per query selects the top-k of the union. Every score
+//    left out is at most theta, below every listed one, so when no list
+//    overflowed and the union holds at least topk scores its top-k is the
+//    exact top-k. If fewer scores exceed theta but enough equal it (ties,
+//    e.g. exact zeros after a ReLU), one ordered pass over all n scores takes
+//    the smallest indices among those equal to theta.
+//  * larger n otherwise: (1) one work-group per chunk of 4096 scores
+//    (256 threads x 16 registers) keeps the chunk's best L as a list in
+//    ascending index order, with a bound: the best element it left out; L is
+//    about twice a chunk's expected share of the top-k plus a margin. (2) One
+//    work-group per query selects the top-k of the union of the lists (at
+//    most 8192 entries, in registers; 256 threads when it holds at most
+//    2048). With tau the topk-th best of the union, a chunk can hide a better
+//    element only if its bound ranks above tau; if none does, the union's
+//    top-k is the exact top-k. If the chunks only left out keys equal to the
+//    union's topk-th key (ties), one ordered pass over all n scores picks the
+//    smallest indices among them.
+//  * Otherwise (rare: a chunk holding far more than its share, or a
+//    threshold above too many scores) the query falls back to an exact
+//    radix select over all n scores read from memory.
 // Every path writes the same, exact answer in ascending index order.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -47,6 +61,19 @@ struct FinalLds {
   StreamLds st;
 };
 
+// Sum of x over the work-group (every thread gets it); uses rs.wg.
+template <int NT>
+__device__ __forceinline__ int block_sum(int x, RegSelLds<NT>& rs) {
+  const int w = wave_incl_sum(x);
+  __syncthreads();
+  if ((threadIdx.x & 63) == 63) rs.wg[threadIdx.x >> 6] = w;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; k++) t += rs.wg[k];
+  return t;
+}
+
 __device__ __forceinline__ int query_n(const TopkArgs& a, int i) {
   return clamp_ctx(a.q_ctx[i], a.max_ctx) / a.block;
 }
@@ -55,8 +82,37 @@ __device__ __forceinline__ int query_n(const TopkArgs& a, int i) {
 __device__ __forceinline__ uint64_t* list_of(const TopkArgs& a, const TopkPlan& p, int i, int c) {
   return reinterpret_cast<uint64_t*>(a.ws) + (size_t(i) * p.n_chunks + c) * p.list_len;
 }
+// per-chunk word: the bound (best element left out), or in filter mode the
+// counts of scores above (low 32 bits) and equal to (high 32 bits) theta
 __device__ __forceinline__ uint64_t* bound_of(const TopkArgs& a, const TopkPlan& p, int i) {
   return reinterpret_cast<uint64_t*>(a.ws) + size_t(a.nq) * p.n_chunks * p.list_len + size_t(i) * p.n_chunks;
+}
+// filter mode: the threshold key of query i
+__device__ __forceinline__ uint32_t* theta_of(const TopkArgs& a, const TopkPlan& p, int i) {
+  return reinterpret_cast<uint32_t*>(reinterpret_cast<uint64_t*>(a.ws) + size_t(a.nq) * p.n_chunks * (p.list_len + 1)) +
+         i;
+}
+
+// Filter mode, step 0: the threshold of each chunked query. grid = nq, 256
+// threads; thread t reads the 16 consecutive scores of run t, runs spread
+// evenly over [0, n).
+__global__ __launch_bounds__(256) void topk_sample(TopkArgs a, TopkPlan p) {
+  __shared__ RegSelLds<kNTc> sh;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int n = query_n(a, i);
+  if (n <= a.topk || n <= p.direct_max) return;
+  const float* sc = a.scores + int64_t(i) * a.ld;
+  const int64_t start = int64_t(tid) * (n - kRc) / (kNTc - 1);
+  uint32_t key[kRc];
+#pragma unroll
+  for (int r = 0; r < kRc; r++) key[r] = order_key(sc[start + r]);
+  // rank of the sample that about 1.75 x topk of the n scores exceed
+  int rank = int((7.0 * double(a.topk) * double(kChunk) + 4.0 * double(n) - 1.0) / (4.0 * double(n)));
+  rank = rank < 1 ? 1 : (rank > kChunk ? kChunk : rank);
+  uint32_t kstar;
+  int need;
+  regsel_threshold<kNTc, kRc>(key, rank, sh, kstar, need);
+  if (tid == 0) *theta_of(a, p, i) = kstar;
 }
 
 // Chunk lists. grid = (n_chunks, nq), 256 threads.
@@ -115,6 +171,89 @@ __global__ __launch_bounds__(256) void topk_chunks(TopkArgs a, TopkPlan p) {
   }
 }
 
+// Filter mode, step 1: the threshold lists. grid = (ceil(n_chunks / kCpw),
+// nq), 256 threads; each work-group takes kCpw consecutive chunks of one
+// query, all their scores loaded before any is used (thread t holds
+// elements 16t .. 16t+15 of each chunk). A chunk's list holds every score
+// above theta in index order (one prefix sum); its word counts the scores
+// above (low half) and equal to (high half) theta.
+constexpr int kCpw = 4;
+
+__device__ __forceinline__ void load16(const float* p, bool vec, float (&v)[kRc]) {
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < kRc / 4; q++) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * q);
+#pragma unroll
+      for (int e = 0; e < 4; e++) v[4 * q + e] = x[e];
+    }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRc; r++) v[r] = p[r];
+  }
+}
+
+__global__ __launch_bounds__(256) void topk_chunks_threshold(TopkArgs a, TopkPlan p) {
+  __shared__ int wsum[kCpw][kNTc / 64];
+  const int i = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = query_n(a, i);
+  if (n <= a.topk || n <= p.direct_max) return;
+  const int c0 = blockIdx.x * kCpw;
+  if (int64_t(c0) * kChunk >= n) return;
+  const float* row = a.scores + int64_t(i) * a.ld;
+  // 16-byte loads when every thread's 16 scores are 16-byte aligned
+  const bool vec = (reinterpret_cast<uintptr_t>(row) & 15) == 0;
+  float v[kCpw][kRc];
+#pragma unroll
+  for (int k = 0; k < kCpw; k++) {
+    const int lo = (c0 + k) * kChunk + kRc * tid;
+    if (lo + kRc <= n) {
+      load16(row + lo, vec, v[k]);
+    } else {
+#pragma unroll
+      for (int r = 0; r < kRc; r++) v[k][r] = lo + r < n ? row[lo + r] : 0.f;
+    }
+  }
+  const uint32_t th = *theta_of(a, p, i);
+  const int L = p.list_len;
+#pragma unroll
+  for (int k = 0; k < kCpw; k++) {
+    const int c = c0 + k;
+    const int lo = c * kChunk;
+    if (lo >= n) break;  // uniform
+    const int j0 = lo + kRc * tid;
+    uint32_t key[kRc];
+    int cg = 0, ce = 0;
+#pragma unroll
+    for (int r = 0; r < kRc; r++) {
+      key[r] = j0 + r < n ? order_key(v[k][r]) : 0u;
+      cg += key[r] > th ? 1 : 0;
+      ce += key[r] == th ? 1 : 0;
+    }
+    const int pk = cg + (ce << 16);  // at most 4096 each
+    const int ic = wave_incl_sum(pk);
+    if (lane == 63) wsum[k][wave] = ic;
+    __syncthreads();
+    int off = ic - pk, tot = 0;
+#pragma unroll
+    for (int w = 0; w < kNTc / 64; w++) {
+      const int x = wsum[k][w];
+      if (w < wave) off += x;
+      tot += x;
+    }
+    uint64_t* lst = list_of(a, p, i, c);
+    int slot = off & 0xFFFF;
+#pragma unroll
+    for (int r = 0; r < kRc; r++) {
+      if (key[r] > th) {
+        if (slot < L) lst[slot] = (uint64_t(key[r]) << 32) | uint32_t(j0 + r);
+        slot++;
+      }
+    }
+    if (tid == 0) bound_of(a, p, i)[c] = uint64_t(uint32_t(tot & 0xFFFF)) | (uint64_t(uint32_t(tot >> 16)) << 32);
+  }
+}
+
 // Selection per query. grid = nq, NT threads; NT * kRf covers the union (or
 // every candidate of a directly selected query).
 template <int NT>
@@ -131,9 +270,10 @@ __global__ __launch_bounds__(NT) void topk_final(TopkArgs a, TopkPlan p) {
     if (tid == 0) a.n_sel[i] = n;
     return;
   }
+  const bool direct = n <= kCap;
+  if (p.filter && !direct) return;  // topk_final_threshold selects these
   if (tid == 0) a.n_sel[i] = topk;
   const float* sc = a.scores + int64_t(i) * a.ld;
-  const bool direct = n <= kCap;
   bool usable = true;
   uint32_t key[kRf];
   int idx[kRf];
@@ -197,6 +337,70 @@ __global__ __launch_bounds__(NT) void topk_final(TopkArgs a, TopkPlan p) {
   stream_compact<kNTf>(gkey_at, n, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = j; });
 }
 
+// Filter mode, step 2: selection per chunked query from the threshold lists
+// (see the file comment). grid = nq, NT threads; NT * kRf covers the union.
+template <int NT>
+__global__ __launch_bounds__(NT) void topk_final_threshold(TopkArgs a, TopkPlan p) {
+  constexpr int kNTf = NT;
+  constexpr int kCap = NT * kRf;
+  __shared__ FinalLds<NT> sh;
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int n = query_n(a, i);
+  const int topk = a.topk;
+  if (n <= topk || n <= kCap) return;  // topk_final selects these
+  int* sel = a.sel + int64_t(i) * topk;
+  if (tid == 0) a.n_sel[i] = topk;
+  const float* sc = a.scores + int64_t(i) * a.ld;
+  const int L = p.list_len;
+  const int nch = (n + kChunk - 1) / kChunk;
+  const uint32_t th = *theta_of(a, p, i);
+  const uint64_t* lists = list_of(a, p, i, 0);
+  const uint64_t* cnts = bound_of(a, p, i);
+  // counts above / equal to theta: thread t < nch holds chunk t's
+  const uint64_t cw = tid < nch ? cnts[tid] : 0ull;
+  const int gt = int(uint32_t(cw)), eq = int(uint32_t(cw >> 32));
+  const bool overflow = __syncthreads_or(gt > L);
+  const int n_gt = block_sum<kNTf>(gt, sh.rs);
+  if (!overflow && nch <= p.n_chunks && int64_t(nch) * L <= kCap && n_gt >= topk) {
+    // union entry e = chunk e / L, slot e % L (ascending index order); slots
+    // past a chunk's count are empty
+    uint32_t key[kRf];
+    int idx[kRf];
+#pragma unroll
+    for (int r = 0; r < kRf; r++) {
+      const int e = kRf * tid + r;
+      const int ch = e / L, slot = e % L;
+      const bool in = ch < nch && slot < int(uint32_t(cnts[ch]));
+      const uint64_t v = in ? lists[e] : 0ull;
+      key[r] = uint32_t(v >> 32);
+      idx[r] = int(uint32_t(v));
+    }
+    uint32_t kstar;
+    int need;
+    regsel_threshold<kNTf, kRf>(key, topk, sh.rs, kstar, need);
+    int pos[kRf];
+    regsel_positions<kNTf, kRf>(key, idx, kstar, need, sh.rs, pos);
+#pragma unroll
+    for (int r = 0; r < kRf; r++)
+      if (pos[r] >= 0) sel[pos[r]] = idx[r];
+    return;
+  }
+  auto gkey_at = [sc](int j) { return order_key(sc[j]); };
+  int* const out = sel;
+  auto emit = [out](int pos, int j) { out[pos] = j; };
+  const int n_eq = block_sum<kNTf>(eq, sh.rs);
+  if (!overflow && n_gt < topk && topk <= n_gt + n_eq) {
+    // every score above theta, then the smallest indices among those equal to it
+    stream_compact<kNTf>(gkey_at, n, th, topk - n_gt, sh.st, emit);
+    return;
+  }
+  // exact select over every score, read from memory
+  uint32_t kstar;
+  int need;
+  stream_select<kNTf>(gkey_at, n, topk, sh.st, kstar, need);
+  stream_compact<kNTf>(gkey_at, n, kstar, need, sh.st, emit);
+}
+
 }  // namespace
 
 TopkPlan plan_topk(int nq, int max_ctx, int block, int topk) {
@@ -212,9 +416,30 @@ TopkPlan plan_topk(int nq, int max_ctx, int block, int topk) {
     }
     return p;
   }
+  const int64_t nch = (nmax + kChunk - 1) / kChunk;
+  // threshold lists: a chunk's list holds twice its expected count above
+  // the sampled threshold (1.75 x its share of the top-k) plus a margin,
+  // within the chunk and the final union
+  {
+    const double expect = 1.75 * double(kChunk) * double(topk) / double(nmax);
+    const int64_t cap = (int64_t(2.0 * expect) + 32 + 15) / 16 * 16;
+    if (cap <= kChunk && nch * cap <= kUnionMax) {
+      p.chunked = true;
+      p.filter = true;
+      p.chunk = kChunk;
+      p.n_chunks = int(nch);
+      p.list_len = int(cap);
+      if (nch * cap <= kSmallMax) {
+        p.final_threads = 256;
+        p.direct_max = kSmallMax;
+      }
+      // lists, one word per chunk, one threshold per query
+      p.ws_bytes = size_t(nq) * size_t(nch) * (size_t(cap) + 1) * 8 + (size_t(nq) * 4 + 7) / 8 * 8;
+      return p;
+    }
+  }
   // list length: twice a chunk's expected share of the top-k plus a margin,
   // rounded up to 16, within the chunk and within the final union
-  const int64_t nch = (nmax + kChunk - 1) / kChunk;
   const double mu = double(kChunk) * double(topk) / double(nmax);
   int64_t L = (int64_t(2.0 * mu) + 48 + 15) / 16 * 16;
   if (L > kChunk) L = kChunk;
@@ -233,11 +458,30 @@ TopkPlan plan_topk(int nq, int max_ctx, int block, int topk) {
 
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
-  if (p.chunked) {
+  if (p.filter) {
+    hipLaunchKernelGGL(topk_sample, dim3(unsigned(a.nq)), dim3(kNTc), 0, s, a, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (p.filter) {
+    hipLaunchKernelGGL(topk_chunks_threshold, dim3(unsigned((p.n_chunks + kCpw - 1) / kCpw), unsigned(a.nq)),
+                       dim3(kNTc), 0, s, a, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else if (p.chunked) {
     hipLaunchKernelGGL(topk_chunks, dim3(unsigned(p.n_chunks), unsigned(a.nq)), dim3(kNTc), 0, s, a, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  if (p.filter) {
+    if (p.final_threads == 256)
+      hipLaunchKernelGGL(topk_final_threshold<256>, dim3(unsigned(a.nq)), dim3(256), 0, s, a, p);
+    else
+      hipLaunchKernelGGL(topk_final_threshold<1024>, dim3(unsigned(a.nq)), dim3(1024), 0, s, a, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  // direct queries (and, outside filter mode, every query)
   if (p.final_threads == 256)
     hipLaunchKernelGGL(topk_final<256>, dim3(unsigned(a.nq)), dim3(256), 0, s, a, p);
   else

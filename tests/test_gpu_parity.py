@@ -156,10 +156,13 @@ def _run_topk(pkg, cfg, scores_np, ctxs):
 @pytest.mark.parametrize("n,kind", [(2048, "uniform"), (2049, "uniform"), (513, "ties"), (16024, "uniform"),
                                     (16024, "ties"), (32768, "ties"), (32769, "uniform"), (262080, "uniform"),
                                     (262080, "ties"), (100003, "sorted_desc"), (100003, "sorted_asc"),
-                                    (70000, "all_equal")])
+                                    (70000, "all_equal"), (262080, "sampled_high")])
 def test_topk_bit_exact(Q, n, kind):
     """Selection from fixed fp32 scores: the GPU must reproduce the oracle's
-    ranking (score desc, index asc) exactly, on every path."""
+    ranking (score desc, index asc) exactly, on every path. "sampled_high"
+    raises exactly the scores the threshold sample reads (256 runs of 16
+    spread over the candidates), so the sampled threshold lies above all but
+    a few scores and the exact fallback must run."""
     pkg, _ = Q
     _print_case("topk", n=n, kind=kind)
     nq = 3
@@ -173,6 +176,11 @@ def test_topk_bit_exact(Q, n, kind):
             s = np.sort(qi.uniform_f32(21, i, n))[::-1].copy()
         elif kind == "sorted_asc":
             s = np.sort(qi.uniform_f32(21, i, n))
+        elif kind == "sampled_high":
+            s = qi.uniform_f32(21, 1000 * n + i, n)
+            for t in range(256):
+                st = t * (n - 16) // 255
+                s[st:st + 16] += np.float32(10.0)
         else:
             s = np.full(n, 0.5, dtype=np.float32)
         rows.append(s)
