@@ -182,8 +182,30 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
 
     ms_app, _, graph = time_graph(torch, step_append, max(10, steps // 2), warmup)
     del graph
+    # layer 0 with its K/V rows in pinned host memory, read zero-copy over the
+    # host link (pooled keys, queries and outputs stay in device memory)
+    lay0, b0 = layers[0], bufs[0]
+    k_host = torch.empty(lay0["k"].shape, dtype=torch.bfloat16, pin_memory=True)
+    v_host = torch.empty(lay0["v"].shape, dtype=torch.bfloat16, pin_memory=True)
+    k_host.copy_(lay0["k"])
+    v_host.copy_(lay0["v"])
+    torch.cuda.synchronize()
+    kv_host = pkg.make_kv(k_host, v_host)
+
+    def layer_host():
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q_idx"], lay0["pooled"], lay0["q"], kv_host,
+                              b0, q_seq=q_seq, fused=True)
+
+    def layer_dev():
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q_idx"], lay0["pooled"], lay0["q"], lay0["kv"],
+                              b0, q_seq=q_seq, fused=True)
+
+    ms_host, _, graph = time_graph(torch, layer_host, max(10, steps // 2), warmup)
+    del graph
+    ms_dev1, _, graph = time_graph(torch, layer_dev, max(10, steps // 2), warmup)
+    del graph, kv_host, k_host, v_host
     scan_launch_bytes = B * (bm.scan_bytes(L) + 128 * 2)
-    return dict(ms=ms, ms_sep=ms_sep, ms_app=ms_app, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
+    return dict(ms=ms, ms_sep=ms_sep, ms_app=ms_app, ms_host=ms_host, ms_dev1=ms_dev1, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
                 n_split=bufs[0].n_split, lists_ms=lists_ms, scan_ms=scan_ms, scan_launch_bytes=scan_launch_bytes,
                 lists_gbs=scan_launch_bytes / (lists_ms * 1e-3) / 1e9, layers=layers, bufs=bufs)
 
@@ -471,6 +493,12 @@ def main():
         "step_bytes": dec["step_bytes"],
         "separate_calls_ms_per_step": round(dec["ms_sep"], 5),
         "with_kv_append_ms_per_step": round(dec["ms_app"], 5),
+        "host_resident_kv": {"workload": "one layer of the step (batch 4, 1,048,320 tokens) with K/V rows in pinned "
+                                         "host memory read zero-copy; pooled keys in device memory",
+                             "ms_per_layer": round(dec["ms_host"], 4),
+                             "ms_per_layer_device_kv": round(dec["ms_dev1"], 4),
+                             "kv_bytes_per_layer": 4 * 2048 * 2 * 2 * 256 * 2,
+                             "kv_gbs": round(4 * 2048 * 2 * 2 * 256 * 2 / (dec["ms_host"] * 1e-3) / 1e9, 1)},
         "breakdown_us_per_layer": {"scan_lists": round(dec["lists_ms"] * 1e3, 2),
                                    "select_attend_merge": round(dec["ms"] * 1e3 / DECODE["layers"]
                                                                 - dec["lists_ms"] * 1e3, 2),

@@ -293,8 +293,33 @@ def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None,
         _dev(pooled, _BF16, "pooled"), 0 if pooled is None else pooled.stride(0), _stream(stream)))
 
 
+_hip = None
+
+
+def _kv_address(t, name):
+    """Device address of a K/V tensor: device memory as is; pinned host memory
+    (torch.empty(..., pin_memory=True)) through the address HIP maps it to,
+    so kernels read it over the host link. Anything else is refused."""
+    global _hip
+    if t.dtype not in _BF16:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected bf16")
+    if t.is_cuda:
+        return t.data_ptr()
+    if not t.is_pinned():
+        raise ValueError(f"{name} must be a CUDA tensor or pinned host memory")
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipHostGetDevicePointer.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_void_p, ctypes.c_uint]
+    dptr = ctypes.c_void_p()
+    err = _hip.hipHostGetDevicePointer(ctypes.byref(dptr), ctypes.c_void_p(t.data_ptr()), 0)
+    if err != 0 or not dptr.value:
+        raise ValueError(f"{name}: pinned host memory is not mapped for the device (hip error {err})")
+    return dptr.value
+
+
 def make_kv(k, v=None):
-    """KV descriptor of k, v: [n_seq, capacity, hkv, d] bf16 (v defaults to k)."""
+    """KV descriptor of k, v: [n_seq, capacity, hkv, d] bf16 (v defaults to k),
+    in device memory or in pinned host memory (read zero-copy)."""
     if v is None:
         v = k
     for t, name in ((k, "k"), (v, "v")):
@@ -302,7 +327,7 @@ def make_kv(k, v=None):
             raise ValueError(f"{name} must be [n_seq, capacity, hkv, d] with unit last stride")
     if k.stride()[:3] != v.stride()[:3] or k.shape[:2] != v.shape[:2]:
         raise ValueError("k and v must share their sequence, token and head strides")
-    kv = KV(ctypes.c_void_p(k.data_ptr()), ctypes.c_void_p(v.data_ptr()), k.stride(0), k.stride(1),
+    kv = KV(ctypes.c_void_p(_kv_address(k, "k")), ctypes.c_void_p(_kv_address(v, "v")), k.stride(0), k.stride(1),
             k.stride(2), k.shape[1])
     kv._keep = (k, v)
     return kv

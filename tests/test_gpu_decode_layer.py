@@ -194,3 +194,41 @@ def test_decode_layer_repeated_calls_and_graph(Q):
         _same_as_separate(bufs, sep, ctxs)
         assert torch.count_nonzero(bufs.layer_ws[:64]).item() == 0
     del g
+
+
+def test_decode_layer_with_host_resident_kv(Q):
+    """K/V rows in pinned host memory, read zero-copy over the host link
+    (pooled keys stay in device memory): the same results, bit for bit, as
+    with the K/V rows in device memory, for the one-call layer and for the
+    separate calls."""
+    pkg, pipeline = Q
+    ctxs = [20000, 13333]
+    _print_case("decode_layer_host_kv", ctxs=ctxs)
+    case = qc.DecodeCase(31, ctxs)
+    nq, max_ctx = len(ctxs), max(ctxs)
+    pooled = torch.zeros(nq, case.cap // 4, 128, dtype=torch.bfloat16, device="cuda")
+    pkg.qsa_pool_keys(qc.to_dev(case.raw), pooled, block=4)
+    k_dev, v_dev = qc.to_dev(case.k), qc.to_dev(case.v)
+    k_host = torch.empty(k_dev.shape, dtype=torch.bfloat16, pin_memory=True)
+    v_host = torch.empty(v_dev.shape, dtype=torch.bfloat16, pin_memory=True)
+    k_host.copy_(k_dev)
+    v_host.copy_(v_dev)
+    torch.cuda.synchronize()
+    q_idx, q = qc.to_dev(case.q_idx[:, None, :]), qc.to_dev(case.q)
+    for fused in (True, False):
+        outs = []
+        for kv in (pkg.make_kv(k_dev, v_dev), pkg.make_kv(k_host, v_host)):
+            bufs = pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, nq, max_ctx)
+            pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, qc.i32(ctxs), max_ctx, q_idx, pooled, q, kv, bufs,
+                                  q_seq=qc.i32(range(nq)), fused=fused)
+            torch.cuda.synchronize()
+            outs.append((bufs.sel.clone(), bufs.o.clone(), bufs.lse.clone()))
+        for a, b in zip(*outs):
+            assert torch.equal(a, b)
+
+
+def test_host_kv_must_be_pinned(Q):
+    pkg, _ = Q
+    k = torch.zeros(1, 8, 2, 256, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        pkg.make_kv(k, k)
