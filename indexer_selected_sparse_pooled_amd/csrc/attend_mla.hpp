@@ -83,6 +83,7 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
 #pragma unroll
     for (int ks = 0; ks < kDK / 32; ks++) qa[ks] = as_bf16x8(ld16(qrow + 32 * ks));
   }
+
   float m[4], l[4];
 #pragma unroll
   for (int e = 0; e < 4; e++) {
@@ -130,9 +131,7 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
     for (int e = 0; e < 4; e++) {
       const float s0 = r < cnt ? acc[0][e] * sl2 : -INFINITY;
       const float s1 = 16 + r < cnt ? acc[1][e] * sl2 : -INFINITY;
-      float tm = fmaxf(s0, s1);
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) tm = fmaxf(tm, __shfl_xor(tm, d));
+      const float tm = row16_max(fmaxf(s0, s1));
       const float mn = fmaxf(m[e], tm);
       float p0 = 0.f, p1 = 0.f;
       alpha[e] = 1.f;
@@ -141,9 +140,7 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
         p1 = exp2f(s1 - mn);
         alpha[e] = exp2f(m[e] - mn);
       }
-      float ps = p0 + p1;
-#pragma unroll
-      for (int d = 1; d < 16; d <<= 1) ps += __shfl_xor(ps, d);
+      const float ps = row16_sum(p0 + p1);
       l[e] = l[e] * alpha[e] + ps;
       m[e] = mn;
       const int row = 4 * kq + e;

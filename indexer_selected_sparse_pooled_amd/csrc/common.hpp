@@ -137,6 +137,32 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
   return (uint64_t(hi) << 32) | lo;
 }
 
+// Reductions over each row of 16 lanes, every lane getting its row's
+// result, through DPP (no LDS round trip): lanes xor 1 and xor 2 by quad
+// permutes, then the other quads of the row by rotations of 4 and 8.
+// (gfx9 controls: quad_perm [1,0,3,2] = 0xB1, [2,3,0,1] = 0x4E,
+// row_ror:4 = 0x124, row_ror:8 = 0x128.)
+__device__ __forceinline__ float dppf(float v, int ctrl) {
+  switch (ctrl) {
+    case 0xB1: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xf, 0xf, false));
+    case 0x4E: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xf, 0xf, false));
+    case 0x124: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x124, 0xf, 0xf, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x128, 0xf, 0xf, false));
+  }
+}
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dppf(v, 0xB1));
+  v = fmaxf(v, dppf(v, 0x4E));
+  v = fmaxf(v, dppf(v, 0x124));
+  return fmaxf(v, dppf(v, 0x128));
+}
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dppf(v, 0xB1);
+  v += dppf(v, 0x4E);
+  v += dppf(v, 0x124);
+  return v + dppf(v, 0x128);
+}
+
 // Wave-wide reductions (64 lanes).
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
