@@ -59,11 +59,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   // the lists and bounds are loaded at the plan's full size before the
   // query's context arrives (one round trip instead of two); entries past
   // the query's own lists are dropped below
+  // (written by the first launch: plain loads)
   uint64_t ent[itk::kRegR];
-  itk::load_union(it, i, it.n_chunks * it.keep, ent);
+  itk::load_union<false>(it, i, it.n_chunks * it.keep, ent);
   const uint64_t* bq = it.list_bound + size_t(i) * it.n_chunks;
-  const uint64_t b0 = tid < it.n_chunks ? ld_coherent(bq + tid) : 0ull;
-  const uint64_t b1 = tid + itk::kNT < it.n_chunks ? ld_coherent(bq + tid + itk::kNT) : 0ull;
+  const uint64_t b0 = tid < it.n_chunks ? bq[tid] : 0ull;
+  const uint64_t b1 = tid + itk::kNT < it.n_chunks ? bq[tid + itk::kNT] : 0ull;
   const int n = clamp_ctx(it.q_ctx[i], it.max_ctx) / 4;
   const int topk = it.topk;
   const int ns = n < topk ? n : topk;

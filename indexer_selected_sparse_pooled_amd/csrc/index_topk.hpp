@@ -49,6 +49,18 @@ namespace itk {
 // between work-groups of one launch is.
 __device__ __forceinline__ void st_sel(int* p, int v) { st_coherent(reinterpret_cast<uint32_t*>(p), uint32_t(v)); }
 
+// Stores of the scan's outputs: agent-coherent when a work-group of the
+// same launch reads them (the last arrival's selection), plain when only a
+// later launch does (kernel boundaries order those).
+template <bool kCoh>
+__device__ __forceinline__ void put(uint32_t* p, uint32_t v) {
+  if constexpr (kCoh) st_coherent(p, v); else *p = v;
+}
+template <bool kCoh>
+__device__ __forceinline__ void put(uint64_t* p, uint64_t v) {
+  if constexpr (kCoh) st_coherent(p, v); else *p = v;
+}
+
 // Every thread's stores are complete before the work-group goes on.
 __device__ __forceinline__ void publish() {
   wait_memory();
@@ -162,12 +174,16 @@ __device__ __forceinline__ bool use_union(const IndexTopkArgs& a, int n) {
 // Union entry e = chunk * keep + slot of query i (each list in ascending
 // block order, so entry order is block order), as (key << 32 | block), 0 =
 // empty; thread t holds entries r * kNT + t. Entries at or past u are 0.
+// kCoh: written by other work-groups of the same launch (else by an
+// earlier launch, and plain loads see it).
+template <bool kCoh = true>
 __device__ __forceinline__ void load_union(const IndexTopkArgs& a, int i, int u, uint64_t (&ent)[kRegR]) {
   const uint64_t* ul = a.list + size_t(i) * a.n_chunks * a.keep;
 #pragma unroll
   for (int r = 0; r < kRegR; r++) {
     const int e = r * kNT + int(threadIdx.x);
-    ent[r] = e < u ? ld_coherent(ul + e) : 0ull;
+    if constexpr (kCoh) ent[r] = e < u ? ld_coherent(ul + e) : 0ull;
+    else ent[r] = e < u ? ul[e] : 0ull;
   }
 }
 
@@ -286,7 +302,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
       const float s = tile_scores(v[t & 1], tile0, n, qv);
       const int64_t blk = tile0 + lane;
       if (blk < n) {
-        st_coherent(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
+        put<kSelect>(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
         key[t] = order_key(s);
       }
     }
@@ -340,13 +356,13 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
       // kept entries (key << 32 | block) go to their list position; the
       // positions past the kept count are cleared (0 = empty)
       wave_compact<1>(h1, ks, nd, [&](int pos, int) {
-        st_coherent(a.list + base + pos, (uint64_t(k1[0]) << 32) | uint32_t(i1));
+        put<kSelect>(a.list + base + pos, (uint64_t(k1[0]) << 32) | uint32_t(i1));
       });
       const int nkept = valid < keep ? valid : keep;
-      if (lane >= nkept && lane < keep) st_coherent(a.list + base + lane, 0ull);
+      if (lane >= nkept && lane < keep) put<kSelect>(a.list + base + lane, 0ull);
       const uint64_t b = wave_best_excluded<1>(h1, k1, ks, nd, [&](int) { return i1; });
       bound = b > bound ? b : bound;
-      if (lane == 0) st_coherent(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
+      if (lane == 0) put<kSelect>(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
     }
   }
 
