@@ -28,6 +28,14 @@ or a worked example):
   the top-k would otherwise take the dense path: sparse equals dense there).
 * [FLASH] "125B MoE を 3090 3 枚で運用する vLLM 最適化編", section 3.3
   (MoE block): top-k on packed keys where equal values go to the smaller id.
+* [GLM] footnotes 1 and 3: the FP8 cache formats: an indexer key is 128
+  FP8 values plus a 4-byte scale (132 bytes per token); a sparse-MLA row is
+  656 bytes in the FP8 MLA format (the 512 latent values as FP8 with their
+  scales, the 64 rotary values kept in 16-bit).
+* OCP 8-bit floating point specification (E4M3): 1 sign bit, 4 exponent bits
+  with bias 7, 3 mantissa bits; exponent field 0 holds subnormals; the
+  pattern S.1111.111 is NaN; there are no infinities; the largest finite
+  magnitude is 448.
 
 Readings taken where the pages are silent (each also listed in the design doc):
 
@@ -50,6 +58,15 @@ R9  GQA: query head h reads kv head h // (hq // hkv).
 R10 softmax scale is a parameter (1/16 for head_dim 256); lse is natural-log.
 R11 an empty partial (no selected token in a tile) is (O = 0, lse = -inf).
 R12 tiles are [k*T, (k+1)*T) in absolute token positions.
+R17 FP8 values are OCP E4M3. A group of values (a whole indexer key, or 128
+    consecutive latent values) shares one fp32 scale s = amax / 448 (fp32
+    division of the group's largest magnitude); each value x is stored as
+    the E4M3 code nearest to the fp32 quotient x / s (ties to even,
+    magnitudes past 448 saturating to 448) and read back as code * s. An
+    all-zero group has s = 0 and zero codes.
+R18 the FP8 indexer key of a pooled block quantizes its bf16 pooled key
+    (R1), one scale per key; the FP8 sparse-MLA row quantizes the first 512
+    latent values in 4 groups of 128 and keeps the 64 rotary values as bf16.
 """
 from __future__ import annotations
 
@@ -131,6 +148,108 @@ def pool_keys(raw_bits: np.ndarray, block: int) -> np.ndarray:
     return f64_to_bf16(s / block)
 
 
+# ----------------------------------------------------------- FP8 E4M3 ----
+
+E4M3_MAX = 448.0
+
+
+def e4m3_to_f64(codes) -> np.ndarray:
+    """Exact value of OCP E4M3 codes (uint8) as float64.
+
+    Exponent field e (bits 6..3), mantissa m (bits 2..0): e >= 1 is the
+    normal number 2**(e-7) * (1 + m/8); e = 0 is the subnormal
+    2**-6 * (m/8); S.1111.111 is NaN; bit 7 is the sign.
+    """
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    e = (c >> 3) & 0xF
+    m = c & 7
+    mag = np.where(e == 0, np.ldexp(m.astype(np.float64), -9),
+                   np.ldexp((8 + m).astype(np.float64), e - 10))
+    mag = np.where((e == 15) & (m == 7), np.nan, mag)
+    return np.where((c & 0x80) != 0, -mag, mag)
+
+
+def f64_to_e4m3(x) -> np.ndarray:
+    """Round finite values to E4M3 codes: nearest, ties to even, magnitudes
+    above 448 saturate to 448. The sign of the input is kept (also for
+    results that round to zero).
+
+    Around a normal |x| = f * 2**e (0.5 <= f < 1) the format keeps 4
+    significant bits, so its spacing is 2**(e-4); below 2**-6 the spacing
+    is the subnormal step 2**-9.
+    """
+    x = np.atleast_1d(np.asarray(x, dtype=np.float64))
+    if not np.all(np.isfinite(x)):
+        raise ValueError("E4M3 rounding takes finite values")
+    a = np.abs(x)
+    _, e = np.frexp(a)
+    q = np.maximum(e - 4, -9)
+    y = np.minimum(np.ldexp(np.rint(np.ldexp(a, -q)), q), E4M3_MAX)  # rint: ties to even
+    # encode the (now representable) magnitude y
+    _, ey = np.frexp(y)
+    normal = y >= 2.0 ** -6
+    ef = np.where(normal, ey - 1 + 7, 0)
+    mf = np.where(normal, np.ldexp(y, -(ey - 1)) * 8 - 8, np.ldexp(y, 9))
+    code = (ef.astype(np.int64) << 3) | mf.astype(np.int64)
+    code = code | np.where(np.signbit(x), 0x80, 0)
+    return code.astype(np.uint8)
+
+
+def quantize_e4m3(x, group: int):
+    """R17: groups of `group` consecutive values along the last axis, each
+    with one fp32 scale s = amax / 448 and codes = E4M3(x / s), both
+    quotients in fp32. x must be exactly representable in fp32 (bf16 values
+    are). Returns (codes uint8 [..., n], scales float32 [..., n / group])."""
+    x = np.asarray(x, dtype=np.float64)
+    n = x.shape[-1]
+    if n % group:
+        raise ValueError("the last axis must be a whole number of groups")
+    xf = x.astype(np.float32)
+    if not np.array_equal(xf.astype(np.float64), x):
+        raise ValueError("values must be exact in fp32")
+    g = xf.reshape(x.shape[:-1] + (n // group, group))
+    amax = np.abs(g).max(axis=-1)
+    scale = (amax / np.float32(E4M3_MAX)).astype(np.float32)  # fp32 / fp32, correctly rounded
+    safe = np.where(scale > 0, scale, np.float32(1.0)).astype(np.float32)
+    quot = (g / safe[..., None]).astype(np.float32)  # fp32 division per value
+    codes = f64_to_e4m3(quot.astype(np.float64)).reshape(g.shape)
+    codes = np.where(scale[..., None] > 0, codes, np.uint8(0)).astype(np.uint8)
+    return codes.reshape(x.shape), scale
+
+
+def dequantize_e4m3(codes, scales, group: int) -> np.ndarray:
+    """code value * its group's scale, exact in float64 (4 + 24 significant bits)."""
+    v = e4m3_to_f64(codes)
+    sc = np.repeat(np.asarray(scales, dtype=np.float64), group, axis=-1)
+    return v * sc
+
+
+def fp8_keys(keys_bits):
+    """R18: FP8 indexer keys, one scale per key (idx_dim codes + 4 bytes).
+    [GLM] footnote 3: 128 FP8 values and a 4-byte scale per key.
+    keys_bits: uint16 [n][dim] (bf16). Returns (codes [n][dim], scales [n])."""
+    k = np.asarray(keys_bits, dtype=np.uint16)
+    codes, scales = quantize_e4m3(bf16_to_f64(k), k.shape[-1])
+    return codes, scales[..., 0]
+
+
+def fp8_latent(latent_bits, n_quant: int = 512, group: int = 128):
+    """R18: the FP8 sparse-MLA row: the first n_quant latent values in groups
+    of `group` with one fp32 scale each, the rest (the rotary part) kept as
+    bf16. [GLM] footnote 1: a 656-byte FP8 row (512 + 4*4 + 64*2 bytes).
+    latent_bits: uint16 [n][576]. Returns (codes [n][512], scales [n][4],
+    rope_bits [n][64])."""
+    lat = np.asarray(latent_bits, dtype=np.uint16)
+    codes, scales = quantize_e4m3(bf16_to_f64(lat[:, :n_quant]), group)
+    return codes, scales, lat[:, n_quant:].copy()
+
+
+def fp8_latent_values(codes, scales, rope_bits, group: int = 128) -> np.ndarray:
+    """The float64 row an FP8 sparse-MLA row stands for: dequantized latent
+    values, then the bf16 rotary values."""
+    return np.concatenate([dequantize_e4m3(codes, scales, group), bf16_to_f64(rope_bits)], axis=-1)
+
+
 # ---------------------------------------------------------- A2 scores ----
 
 def index_scores(q_idx_bits: np.ndarray, keys_bits: np.ndarray, n: int) -> np.ndarray:
@@ -155,6 +274,22 @@ def index_scores_relu(q_idx_bits: np.ndarray, w: np.ndarray, keys_bits: np.ndarr
     k = bf16_to_f64(keys_bits[:n])
     per_head = k @ q.T  # [n][heads]
     return np.maximum(per_head, 0.0) @ np.asarray(w, dtype=np.float64)
+
+
+def index_scores_fp8(q_idx_bits: np.ndarray, codes: np.ndarray, scales: np.ndarray, n: int) -> np.ndarray:
+    """A2, variant A with FP8 keys (R17, R18): s[b] = q_idx . (codes[b] * scales[b])."""
+    q = bf16_to_f64(q_idx_bits)
+    k = dequantize_e4m3(codes[:n], np.asarray(scales)[:n, None], codes.shape[-1])
+    return k @ q
+
+
+def index_scores_relu_fp8(q_idx_bits: np.ndarray, w: np.ndarray, codes: np.ndarray, scales: np.ndarray,
+                          n: int) -> np.ndarray:
+    """A2, variant B with FP8 token keys: the ReLU-weighted sum over the
+    dequantized keys."""
+    q = bf16_to_f64(q_idx_bits)
+    k = dequantize_e4m3(codes[:n], np.asarray(scales)[:n, None], codes.shape[-1])
+    return np.maximum(k @ q.T, 0.0) @ np.asarray(w, dtype=np.float64)
 
 
 # ------------------------------------------------------------- A3 top-k ----
@@ -223,10 +358,18 @@ def attend(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, tokens: n
     read, addressed per (token, kv head).
     Returns (O float64 [hq][dv], lse float64 [hq]).
     """
+    return attend_values(q_bits, k_bits, v_bits, tokens, scale, dv, to_f64=bf16_to_f64)
+
+
+def attend_values(q_bits, k_rows, v_rows, tokens, scale, dv=None, to_f64=None):
+    """A4 over K/V rows given as float64 values (to_f64 None), or as any
+    encoding that to_f64 turns into them (bf16 bits in attend). The FP8
+    sparse-MLA rows enter here through fp8_latent_values."""
+    conv = (lambda a: np.asarray(a, dtype=np.float64)) if to_f64 is None else to_f64
     hq, dk = q_bits.shape
-    hkv = k_bits.shape[1]
+    hkv = k_rows.shape[1]
     if dv is None:
-        dv = v_bits.shape[2]
+        dv = v_rows.shape[2]
     group = hq // hkv
     q = bf16_to_f64(q_bits)
     out = np.zeros((hq, dv))
@@ -235,8 +378,8 @@ def attend(q_bits: np.ndarray, k_bits: np.ndarray, v_bits: np.ndarray, tokens: n
     if tokens.size == 0:
         return out, lse
     for g in range(hkv):
-        kg = bf16_to_f64(k_bits[tokens, g, :])
-        vg = bf16_to_f64(v_bits[tokens, g, :dv])
+        kg = conv(k_rows[tokens, g, :])
+        vg = conv(v_rows[tokens, g, :dv])
         for h in range(g * group, (g + 1) * group):
             z = scale * (kg @ q[h])
             m = z.max()
