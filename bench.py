@@ -204,10 +204,65 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
     del graph
     ms_dev1, _, graph = time_graph(torch, layer_dev, max(10, steps // 2), warmup)
     del graph, kv_host, k_host, v_host
+    # the same step with FP8 pooled keys (128 E4M3 codes + an fp32 scale per
+    # block, quantized from each layer's bf16 pooled keys; K/V rows stay bf16)
+    for lay in layers:
+        lay["pooled_fp8"] = pkg.fp8_keys_empty(B, L // 4, 128)
+        pkg.qsa_quantize_keys(lay["pooled"], lay["pooled_fp8"])
+    torch.cuda.synchronize()
+
+    def step_fp8():
+        for lay, bf in zip(layers, bufs):
+            pipeline.decode_layer(pkg.SEL_A_FP8, pkg.ATTN_A, q_ctx, L, lay["q_idx"], lay["pooled_fp8"], lay["q"],
+                                  lay["kv"], bf, q_seq=q_seq, fused=True)
+
+    def lists_fp8():
+        for lay, bf in zip(layers, bufs):
+            pkg.qsa_index_lists(pkg.SEL_A_FP8, q_ctx, L, lay["q_idx"], lay["pooled_fp8"], bf.scores, bf.itk_ws,
+                                q_seq=q_seq)
+
+    ms_fp8, _, graph = time_graph(torch, step_fp8, steps, warmup)
+    del graph
+    lists_fp8_ms = time_launches(torch, lists_fp8, reps) / len(layers)
+    for lay in layers:
+        del lay["pooled_fp8"]
+    # two micro-batches (sequences 0-1 and 2-3), each its 12 layers in order
+    # on a stream of its own: the step ends when both have finished
+    halves = []
+    for a, b in ((0, B // 2), (B // 2, B)):
+        halves.append((a, b, torch.arange(a, b, dtype=torch.int32, device="cuda"), q_ctx[a:b].contiguous(),
+                       [pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, b - a, L) for _ in layers]))
+    side = torch.cuda.Stream()
+
+    def chain(h):
+        a, b, qs, qc, bfs = h
+        for lay, bf in zip(layers, bfs):
+            pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, qc, L, lay["q_idx"][a:b], lay["pooled"], lay["q"][a:b],
+                                  lay["kv"], bf, q_seq=qs, fused=True)
+
+    def step_two_streams():
+        cur = torch.cuda.current_stream()
+        side.wait_stream(cur)
+        chain(halves[0])
+        with torch.cuda.stream(side):
+            chain(halves[1])
+        cur.wait_stream(side)
+
+    ms_two, _, graph = time_graph(torch, step_two_streams, steps, warmup)
+    del graph
+    for l, bf in enumerate(bufs):  # the same outputs as the batch-4 step, bit for bit
+        step_out = torch.cat([halves[0][4][l].o, halves[1][4][l].o])
+        if not torch.equal(step_out, bf.o):
+            raise RuntimeError("two-stream step: outputs differ from the batch-4 step")
+    del halves
     scan_launch_bytes = B * (bm.scan_bytes(L) + 128 * 2)
-    return dict(ms=ms, ms_sep=ms_sep, ms_app=ms_app, ms_host=ms_host, ms_dev1=ms_dev1, wall=wall, step_bytes=step_bytes, unit_bytes=unit_bytes, pool_ms=pool_ms,
-                n_split=bufs[0].n_split, lists_ms=lists_ms, scan_ms=scan_ms, scan_launch_bytes=scan_launch_bytes,
-                lists_gbs=scan_launch_bytes / (lists_ms * 1e-3) / 1e9, layers=layers, bufs=bufs)
+    scan_fp8_bytes = B * (bm.scan_bytes_fp8(L) + 128 * 2)
+    return dict(ms=ms, ms_sep=ms_sep, ms_app=ms_app, ms_host=ms_host, ms_dev1=ms_dev1, wall=wall, step_bytes=step_bytes,
+                unit_bytes=unit_bytes, pool_ms=pool_ms, n_split=bufs[0].n_split, lists_ms=lists_ms, scan_ms=scan_ms,
+                scan_launch_bytes=scan_launch_bytes, lists_gbs=scan_launch_bytes / (lists_ms * 1e-3) / 1e9,
+                ms_fp8=ms_fp8, step_bytes_fp8=bm.decode_unit_bytes_fp8(L) * B * len(layers),
+                lists_fp8_ms=lists_fp8_ms, lists_fp8_gbs=scan_fp8_bytes / (lists_fp8_ms * 1e-3) / 1e9,
+                ms_two=ms_two, layers=layers, bufs=bufs)
 
 
 def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
@@ -493,6 +548,17 @@ def main():
         "step_bytes": dec["step_bytes"],
         "separate_calls_ms_per_step": round(dec["ms_sep"], 5),
         "with_kv_append_ms_per_step": round(dec["ms_app"], 5),
+        "two_streams": {"workload": "the same step as two micro-batches (sequences 0-1, 2-3), each going through its "
+                                    "12 layers in order on its own stream; outputs identical to the batch-4 step",
+                        "ms_per_step": round(dec["ms_two"], 5), "steps_s": round(1e3 / dec["ms_two"], 1),
+                        "hbm_gbs": round(dec["step_bytes"] / (dec["ms_two"] * 1e-3) / 1e9, 1)},
+        "fp8_keys": {"workload": "the same step with FP8 pooled keys (128 E4M3 codes + an fp32 scale = 132 B per "
+                                 "block); K/V rows bf16",
+                     "ms_per_step": round(dec["ms_fp8"], 5), "steps_s": round(1e3 / dec["ms_fp8"], 1),
+                     "step_bytes": dec["step_bytes_fp8"],
+                     "hbm_gbs": round(dec["step_bytes_fp8"] / (dec["ms_fp8"] * 1e-3) / 1e9, 1),
+                     "scan_us_per_launch": round(dec["lists_fp8_ms"] * 1e3, 2),
+                     "scan_gbs": round(dec["lists_fp8_gbs"], 1)},
         "host_resident_kv": {"workload": "one layer of the step (batch 4, 1,048,320 tokens) with K/V rows in pinned "
                                          "host memory read zero-copy; pooled keys in device memory",
                              "ms_per_layer": round(dec["ms_host"], 4),

@@ -61,16 +61,34 @@ typedef enum {
   QSA_ERR_DEVICE = 5        /* no usable gfx950 device */
 } qsa_status;
 
+/* Storage of indexer keys.
+ *   QSA_KEYS_BF16: key b of a sequence is idx_dim bf16 values at
+ *     keys + seq * keys_seq_stride + b * idx_dim (strides in elements).
+ *   QSA_KEYS_FP8: each key is idx_dim OCP E4M3 codes plus one fp32 scale
+ *     and stands for code * scale ("GLM-5.3 ...", footnote 3: 128 FP8
+ *     values and a 4-byte scale, 132 bytes per key). Keys are stored in
+ *     pages of 64: page p holds the codes of keys 64p .. 64p+63 (idx_dim
+ *     bytes each, key-major) followed by their 64 scales, so key b's codes
+ *     start at byte (b/64) * 64*(idx_dim+4) + (b%64) * idx_dim and its scale
+ *     at (b/64) * 64*(idx_dim+4) + 64*idx_dim + 4*(b%64) of its sequence;
+ *     sequence strides are in bytes (multiples of 16).
+ *     qsa_fp8_keys_bytes gives the bytes n keys need; qsa_quantize_keys and
+ *     qsa_kv_append write this layout. Supported for the single-head 128-d
+ *     indexer (variant A). */
+typedef enum { QSA_KEYS_BF16 = 0, QSA_KEYS_FP8 = 1 } qsa_key_format;
+
 /* Indexer / selection parameters.
  *   variant A (pooled block keys):   block 4, topk 512,  idx_dim 128, idx_heads 1
  *   variant B (token keys, MLA-like): block 1, topk 2048, idx_dim 64,  idx_heads 4
  * Supported: block in {1, 4}; 1 <= topk <= 2048; (idx_dim, idx_heads) in
- * {(128, 1), (64, 4)}. */
+ * {(128, 1), (64, 4)}; key_format a qsa_key_format (QSA_KEYS_FP8 with
+ * (128, 1) only). */
 typedef struct {
   int32_t block;
   int32_t topk;
   int32_t idx_dim;
   int32_t idx_heads;
+  int32_t key_format;
 } qsa_sel_cfg;
 
 /* Attention shape. Query head h reads kv head h / (hq / hkv).
@@ -122,6 +140,26 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride,
                          int32_t n_seq, int64_t tok_begin, int64_t tok_end,
                          int32_t dim, int32_t block, qsa_stream_t stream);
 
+/* -------------------------------------------------------- A1, FP8 ----
+ * qsa_quantize_keys: FP8 indexer keys (QSA_KEYS_FP8 layout) from bf16 keys
+ * [key_begin, key_end) of n_seq sequences, for instance pooled keys written
+ * by qsa_pool_keys. Per key: scale = amax / 448 (amax the largest |value|;
+ * fp32 division, correctly rounded) and code[d] = the E4M3 value nearest to
+ * the fp32 quotient key[d] / scale (ties to even, magnitudes past 448 set
+ * to 448); an all-zero key gets scale 0 and zero codes. ("GLM-5.3 ...",
+ * footnote 3: FP8 values with one 4-byte scale per key.)
+ *   keys (device) bf16: key b of sequence s at keys + s*keys_seq_stride + b*dim.
+ *   out  (device) FP8 pages of sequence s at out + s*out_seq_stride (bytes,
+ *        a multiple of 16); only the codes and scales of the keys in range
+ *        are written.
+ *   dim in {64, 128}. */
+qsa_status qsa_quantize_keys(const qsa_bf16* keys, int64_t keys_seq_stride, void* out,
+                             int64_t out_seq_stride, int32_t n_seq, int64_t key_begin,
+                             int64_t key_end, int32_t dim, qsa_stream_t stream);
+
+/* Bytes that hold FP8 keys 0 .. n_keys-1 of one sequence (whole pages). */
+int64_t qsa_fp8_keys_bytes(int64_t n_keys, int32_t dim);
+
 /* ------------------------------------------------- A1 at decode time ----
  * qsa_kv_append: the decode step's write of one new token per query into
  * the cache, before the layer reads it. Query i writes, at position
@@ -133,7 +171,9 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride,
  *     seq * raw_seq_stride + pos * idx_dim, when raw_new is given;
  *   - when pos + 1 is a multiple of block and pooled is given, the pooled
  *     key of the block it completes, bit-identical to qsa_pool_keys over the
- *     same raw keys (the block's earlier tokens are read from raw_keys).
+ *     same raw keys (the block's earlier tokens are read from raw_keys);
+ *     with sel_cfg->key_format QSA_KEYS_FP8, that key quantized as
+ *     qsa_quantize_keys does, into FP8 pages (pooled_seq_stride in bytes).
  * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの": pooled keys stay
  * device-resident and the raw keys are kept so that blocks can be pooled;
  * "カーネルを書き換えずに済む": per (token, kv head) addressing.)
@@ -149,7 +189,7 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride,
 qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                          const int32_t* q_seq, const int32_t* q_pos, const qsa_bf16* k_new,
                          const qsa_bf16* v_new, const qsa_bf16* raw_new, const qsa_kv* kv,
-                         qsa_bf16* raw_keys, int64_t raw_seq_stride, qsa_bf16* pooled,
+                         qsa_bf16* raw_keys, int64_t raw_seq_stride, void* pooled,
                          int64_t pooled_seq_stride, qsa_stream_t stream);
 
 /* ---------------------------------------------------------------- A2 ----
@@ -166,13 +206,15 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
  *   q_ctx  (device) int32 [nq] visible tokens per query (its own included).
  *   q_idx  (device) bf16 [nq][idx_heads][idx_dim].
  *   w_idx  (device) fp32 [nq][idx_heads]; NULL when idx_heads == 1.
- *   keys   (device) bf16: key b of sequence s at keys + s*keys_seq_stride + b*idx_dim
- *          (pooled block keys for block 4, per-token keys for block 1).
+ *   keys   (device) in cfg->key_format: bf16 key b of sequence s at
+ *          keys + s*keys_seq_stride + b*idx_dim, or FP8 pages (then the
+ *          score uses code * scale for each key value); pooled block keys
+ *          for block 4, per-token keys for block 1.
  *   scores (device) fp32 [nq][ld_scores], ld_scores >= max_ctx / block. */
 qsa_status qsa_index_scores(const qsa_sel_cfg* cfg, int32_t nq,
                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
                             const qsa_bf16* q_idx, const float* w_idx,
-                            const qsa_bf16* keys, int64_t keys_seq_stride,
+                            const void* keys, int64_t keys_seq_stride,
                             float* scores, int64_t ld_scores, qsa_stream_t stream);
 
 /* ---------------------------------------------------------------- A3 ----
@@ -203,8 +245,8 @@ size_t qsa_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_
  * chunk of blocks and keeps the chunk's best candidates; the last
  * work-group of a query to finish selects the exact top-k from them.
  * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの" and "なぜ".)
- * Variant A only (block 4, idx_dim 128, idx_heads 1); other configurations
- * return QSA_ERR_UNSUPPORTED.
+ * Variant A only (block 4, idx_dim 128, idx_heads 1; bf16 or FP8 keys);
+ * other configurations return QSA_ERR_UNSUPPORTED.
  *   q_seq, q_ctx, q_idx, keys, scores, ld_scores: as qsa_index_scores.
  *   sel, n_sel: as qsa_topk_blocks.
  *   ws (device) workspace of at least qsa_index_topk_workspace_bytes(cfg,
@@ -215,7 +257,7 @@ size_t qsa_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_
  *      concurrently. */
 qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq,
                           const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
-                          const qsa_bf16* keys, int64_t keys_seq_stride,
+                          const void* keys, int64_t keys_seq_stride,
                           float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel,
                           void* ws, size_t ws_bytes, qsa_stream_t stream);
 
@@ -230,14 +272,14 @@ size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_
  * calling this entry point separately lets a caller time or schedule the
  * scan on its own. ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの":
  * every pooled key is scored at every step.)
- * Variant A only (block 4, idx_dim 128, idx_heads 1).
+ * Variant A only (block 4, idx_dim 128, idx_heads 1; bf16 or FP8 keys).
  *   q_seq, q_ctx, q_idx, keys, scores, ld_scores: as qsa_index_scores.
  *   ws (device) workspace of at least qsa_index_topk_workspace_bytes(cfg,
  *      nq, max_ctx) bytes; contents ignored on entry, list layout internal.
  *      Calls that share a workspace must not run concurrently. */
 qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq,
                            const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
-                           const qsa_bf16* keys, int64_t keys_seq_stride,
+                           const void* keys, int64_t keys_seq_stride,
                            float* scores, int64_t ld_scores,
                            void* ws, size_t ws_bytes, qsa_stream_t stream);
 
@@ -274,8 +316,9 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
  * when the parts cannot all be resident at once).
  * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの" and "なぜ";
  * "GLM-5.3 ...", "DCP".)
- * Variant A only (block 4, idx_dim 128, idx_heads 1; hq 16, hkv 2, dk = dv
- * = 256); other configurations return QSA_ERR_UNSUPPORTED. nq <= 4096.
+ * Variant A only (block 4, idx_dim 128, idx_heads 1, bf16 or FP8 keys; hq
+ * 16, hkv 2, dk = dv = 256); other configurations return
+ * QSA_ERR_UNSUPPORTED. nq <= 4096.
  *   q_seq, q_ctx, q_idx, keys, scores, ld_scores, sel, n_sel: as
  *          qsa_index_topk (scores, sel and n_sel are written as there).
  *   q, kv, n_split: as qsa_sparse_decode (1 <= n_split <= 256).
@@ -294,7 +337,7 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
  *      workspace to clear it. */
 qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
-                            const qsa_bf16* q_idx, const qsa_bf16* keys, int64_t keys_seq_stride,
+                            const qsa_bf16* q_idx, const void* keys, int64_t keys_seq_stride,
                             const qsa_bf16* q, const qsa_kv* kv,
                             float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel,
                             int32_t n_split, float* o_out, qsa_bf16* o_out_bf16, float* lse_out,

@@ -22,6 +22,12 @@ def scan_bytes(ctx: int, block: int = 4, idx_dim: int = 128) -> int:
     return (ctx // block) * idx_dim * BF16
 
 
+def scan_bytes_fp8(ctx: int, block: int = 4, idx_dim: int = 128) -> int:
+    """FP8 keys: idx_dim one-byte codes plus a 4-byte scale per key
+    ("GLM-5.3 ...", footnote 3: 132 bytes for a 128-value key)."""
+    return (ctx // block) * (idx_dim + 4)
+
+
 def kv_bytes(n_tokens: int, hkv: int = 2, d: int = 256) -> int:
     return n_tokens * hkv * d * BF16 * 2
 
@@ -31,6 +37,13 @@ def decode_unit_bytes(ctx: int, block: int = 4, topk: int = 512, idx_dim: int = 
     s = attended_tokens(ctx, block, topk)
     return (scan_bytes(ctx, block, idx_dim) + idx_dim * BF16 + kv_bytes(s, hkv, d)
             + hq * d * BF16 + hq * d * BF16)
+
+
+def decode_unit_bytes_fp8(ctx: int, block: int = 4, topk: int = 512, idx_dim: int = 128, hq: int = 16,
+                          hkv: int = 2, d: int = 256) -> int:
+    """decode_unit_bytes with FP8 pooled keys (the K/V rows stay bf16)."""
+    return decode_unit_bytes(ctx, block, topk, idx_dim, hq, hkv, d) - scan_bytes(ctx, block, idx_dim) \
+        + scan_bytes_fp8(ctx, block, idx_dim)
 
 
 def decode_unit_flops(ctx: int, block: int = 4, topk: int = 512, idx_dim: int = 128, hq: int = 16,

@@ -9,6 +9,7 @@
 #include <vector>
 
 #include "../../include/qsa.h"
+#include "fp8.hpp"
 #include "kernels.hpp"
 
 namespace {
@@ -85,6 +86,25 @@ qsa_status check_sel_cfg(const qsa_sel_cfg* c) {
   const bool a = c->idx_dim == 128 && c->idx_heads == 1;
   const bool b = c->idx_dim == 64 && c->idx_heads == 4;
   if (!a && !b) return fail(QSA_ERR_UNSUPPORTED, "(idx_dim, idx_heads) = (%d, %d) not supported", c->idx_dim, c->idx_heads);
+  if (c->key_format != QSA_KEYS_BF16 && c->key_format != QSA_KEYS_FP8)
+    return fail(QSA_ERR_UNSUPPORTED, "key_format %d not supported", c->key_format);
+  return QSA_OK;
+}
+
+// Indexer keys: bf16 rows (stride in elements, a multiple of 8) or FP8 pages
+// (stride in bytes, a multiple of 16; the single-head 128-d indexer only).
+// per_seq: queries read their own sequences, so the stride must hold nmax keys.
+qsa_status check_keys(const qsa_sel_cfg* c, const void* keys, int64_t ss, int64_t nmax, bool per_seq) {
+  if (!keys || !aligned16(keys)) return fail(QSA_ERR_ARG, "keys must be a non-NULL 16-byte aligned pointer");
+  if (c->key_format == QSA_KEYS_FP8) {
+    if (c->idx_heads != 1) return fail(QSA_ERR_UNSUPPORTED, "FP8 keys: only the single-head 128-d indexer");
+    if (ss % 16 || ss < 0) return fail(QSA_ERR_ARG, "FP8 keys_seq_stride must be a non-negative multiple of 16 bytes");
+    if (per_seq && ss < qsa::fp8_keys_bytes(nmax, c->idx_dim))
+      return fail(QSA_ERR_ARG, "keys_seq_stride smaller than the pages of max_ctx / block keys");
+  } else {
+    if (ss % 8 || ss < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
+    if (per_seq && ss < nmax * c->idx_dim) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / block keys");
+  }
   return QSA_OK;
 }
 
@@ -185,10 +205,36 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride, qsa_bf16* 
                 "qsa_pool_keys");
 }
 
+int64_t qsa_fp8_keys_bytes(int64_t n_keys, int32_t dim) {
+  if (n_keys < 0 || dim <= 0) return 0;
+  return qsa::fp8_keys_bytes(n_keys, dim);
+}
+
+qsa_status qsa_quantize_keys(const qsa_bf16* keys, int64_t keys_seq_stride, void* out, int64_t out_seq_stride,
+                             int32_t n_seq, int64_t key_begin, int64_t key_end, int32_t dim, qsa_stream_t stream) {
+  if (dim != 64 && dim != 128) return fail(QSA_ERR_UNSUPPORTED, "dim %d not in {64, 128}", dim);
+  if (n_seq < 0 || key_begin < 0 || key_end < key_begin) return fail(QSA_ERR_ARG, "bad n_seq or key range");
+  if (n_seq == 0 || key_end == key_begin) return QSA_OK;
+  if (!keys || !out) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(keys) || !aligned16(out)) return fail(QSA_ERR_ARG, "keys and out must be 16-byte aligned");
+  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a multiple of 8");
+  if (out_seq_stride % 16 || out_seq_stride < 0) return fail(QSA_ERR_ARG, "out_seq_stride must be a multiple of 16");
+  if (n_seq > 1 && (keys_seq_stride < key_end * dim || out_seq_stride < qsa::fp8_keys_bytes(key_end, dim)))
+    return fail(QSA_ERR_ARG, "sequence strides too small");
+  if (n_seq > 65535) return fail(QSA_ERR_UNSUPPORTED, "n_seq > 65535");
+  if ((key_end - key_begin + 3) / 4 > 0x7FFFFFFF) return fail(QSA_ERR_UNSUPPORTED, "too many keys");
+  qsa_status st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(qsa::launch_quantize(keys, keys_seq_stride, static_cast<uint8_t*>(out), out_seq_stride, n_seq,
+                                     key_begin, key_end - key_begin, dim, s),
+                s, "qsa_quantize_keys");
+}
+
 qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                          const int32_t* q_seq, const int32_t* q_pos, const qsa_bf16* k_new,
                          const qsa_bf16* v_new, const qsa_bf16* raw_new, const qsa_kv* kv,
-                         qsa_bf16* raw_keys, int64_t raw_seq_stride, qsa_bf16* pooled,
+                         qsa_bf16* raw_keys, int64_t raw_seq_stride, void* pooled,
                          int64_t pooled_seq_stride, qsa_stream_t stream) {
   qsa_status st = check_sel_cfg(sel_cfg);
   if (st != QSA_OK) return st;
@@ -218,7 +264,13 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
     if (pooled) {
       if (sel_cfg->block == 1) return fail(QSA_ERR_ARG, "pooled must be NULL when block == 1");
       if (!aligned16(pooled)) return fail(QSA_ERR_ARG, "pooled must be 16-byte aligned");
-      if (pooled_seq_stride % 8 || pooled_seq_stride < 0) return fail(QSA_ERR_ARG, "pooled_seq_stride must be a multiple of 8");
+      if (sel_cfg->key_format == QSA_KEYS_FP8) {
+        if (sel_cfg->idx_heads != 1) return fail(QSA_ERR_UNSUPPORTED, "FP8 keys: only the single-head 128-d indexer");
+        if (pooled_seq_stride % 16 || pooled_seq_stride < 0)
+          return fail(QSA_ERR_ARG, "FP8 pooled_seq_stride must be a non-negative multiple of 16 bytes");
+      } else if (pooled_seq_stride % 8 || pooled_seq_stride < 0) {
+        return fail(QSA_ERR_ARG, "pooled_seq_stride must be a multiple of 8");
+      }
     }
   } else if (pooled) {
     return fail(QSA_ERR_ARG, "pooling needs raw_new and raw_keys");
@@ -247,26 +299,27 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
   a.raw_ss = raw_seq_stride;
   a.pooled = pooled;
   a.pooled_ss = pooled_seq_stride;
+  a.pooled_fp8 = sel_cfg->key_format == QSA_KEYS_FP8;
   a.dim = dim;
   a.block = sel_cfg->block;
   return finish(qsa::launch_append(a, s), s, "qsa_kv_append");
 }
 
 qsa_status qsa_index_scores(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
-                            int32_t max_ctx, const qsa_bf16* q_idx, const float* w_idx, const qsa_bf16* keys,
+                            int32_t max_ctx, const qsa_bf16* q_idx, const float* w_idx, const void* keys,
                             int64_t keys_seq_stride, float* scores, int64_t ld_scores, qsa_stream_t stream) {
   qsa_status st = check_sel_cfg(cfg);
   if (st != QSA_OK) return st;
   if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
   if (nq == 0) return QSA_OK;
   if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
-  if (!q_ctx || !q_idx || !keys || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!q_ctx || !q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
   if (cfg->idx_heads > 1 && !w_idx) return fail(QSA_ERR_ARG, "w_idx required when idx_heads > 1");
-  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx, keys and scores must be 16-byte aligned");
+  if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
   const int64_t nmax = int64_t(max_ctx) / cfg->block;
   if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / block = %lld", (long long)ld_scores, (long long)nmax);
-  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
-  if (q_seq && keys_seq_stride < nmax * cfg->idx_dim) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / block keys");
+  st = check_keys(cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
+  if (st != QSA_OK) return st;
   st = check_device();
   if (st != QSA_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -284,6 +337,7 @@ qsa_status qsa_index_scores(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q
   a.w_idx = w_idx;
   a.keys = keys;
   a.keys_ss = keys_seq_stride;
+  a.key_fp8 = cfg->key_format == QSA_KEYS_FP8;
   a.scores = scores;
   a.ld = ld_scores;
   return finish(qsa::launch_scores(a, s), s, "qsa_index_scores");
@@ -337,7 +391,7 @@ size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_
 }
 
 qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
-                          int32_t max_ctx, const qsa_bf16* q_idx, const qsa_bf16* keys, int64_t keys_seq_stride,
+                          int32_t max_ctx, const qsa_bf16* q_idx, const void* keys, int64_t keys_seq_stride,
                           float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, void* ws,
                           size_t ws_bytes, qsa_stream_t stream) {
   qsa_status st = check_sel_cfg(cfg);
@@ -347,13 +401,13 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
   if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
   if (nq == 0) return QSA_OK;
   if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
-  if (!q_ctx || !q_idx || !keys || !scores || !sel || !n_sel) return fail(QSA_ERR_ARG, "NULL pointer argument");
-  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores) || !aligned16(sel))
-    return fail(QSA_ERR_ARG, "q_idx, keys, scores and sel must be 16-byte aligned");
+  if (!q_ctx || !q_idx || !scores || !sel || !n_sel) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q_idx) || !aligned16(scores) || !aligned16(sel))
+    return fail(QSA_ERR_ARG, "q_idx, scores and sel must be 16-byte aligned");
   const int64_t nmax = int64_t(max_ctx) / 4;
   if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
-  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
-  if (q_seq && keys_seq_stride < nmax * 128) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / 4 keys");
+  st = check_keys(cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
+  if (st != QSA_OK) return st;
   const qsa::IndexTopkPlan plan = qsa::plan_index_topk(nq, max_ctx, cfg->topk);
   if (plan.n_chunks > 65535) return fail(QSA_ERR_UNSUPPORTED, "context too long");
   if (!ws || ws_bytes < plan.ws_bytes)
@@ -372,6 +426,7 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
   a.q_idx = q_idx;
   a.keys = keys;
   a.keys_ss = keys_seq_stride;
+  a.key_fp8 = cfg->key_format == QSA_KEYS_FP8;
   a.scores = scores;
   a.ld = ld_scores;
   a.topk = cfg->topk;
@@ -381,7 +436,7 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
 }
 
 qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
-                           int32_t max_ctx, const qsa_bf16* q_idx, const qsa_bf16* keys, int64_t keys_seq_stride,
+                           int32_t max_ctx, const qsa_bf16* q_idx, const void* keys, int64_t keys_seq_stride,
                            float* scores, int64_t ld_scores, void* ws, size_t ws_bytes, qsa_stream_t stream) {
   qsa_status st = check_sel_cfg(cfg);
   if (st != QSA_OK) return st;
@@ -390,13 +445,12 @@ qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_
   if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
   if (nq == 0) return QSA_OK;
   if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
-  if (!q_ctx || !q_idx || !keys || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
-  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores))
-    return fail(QSA_ERR_ARG, "q_idx, keys and scores must be 16-byte aligned");
+  if (!q_ctx || !q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
   const int64_t nmax = int64_t(max_ctx) / 4;
   if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
-  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
-  if (q_seq && keys_seq_stride < nmax * 128) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / 4 keys");
+  st = check_keys(cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
+  if (st != QSA_OK) return st;
   const qsa::IndexTopkPlan plan = qsa::plan_index_topk(nq, max_ctx, cfg->topk);
   if (plan.n_chunks > 65535) return fail(QSA_ERR_UNSUPPORTED, "context too long");
   if (!ws || ws_bytes < plan.ws_bytes)
@@ -415,6 +469,7 @@ qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_
   a.q_idx = q_idx;
   a.keys = keys;
   a.keys_ss = keys_seq_stride;
+  a.key_fp8 = cfg->key_format == QSA_KEYS_FP8;
   a.scores = scores;
   a.ld = ld_scores;
   a.topk = cfg->topk;
@@ -432,7 +487,7 @@ size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_at
 
 qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
-                            const qsa_bf16* keys, int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
+                            const void* keys, int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
                             float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, int32_t n_split,
                             float* o_out, qsa_bf16* o_out_bf16, float* lse_out, void* ws, size_t ws_bytes,
                             qsa_stream_t stream) {
@@ -445,16 +500,15 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
   if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
   if (nq == 0) return QSA_OK;
   if (nq > 4096) return fail(QSA_ERR_UNSUPPORTED, "nq > 4096");
-  if (!q_idx || !keys || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
   if (!o_out && !o_out_bf16 && !lse_out) return fail(QSA_ERR_ARG, "no output requested");
-  if (!aligned16(q_idx) || !aligned16(keys) || !aligned16(scores))
-    return fail(QSA_ERR_ARG, "q_idx, keys and scores must be 16-byte aligned");
+  if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
   if ((o_out && !aligned16(o_out)) || (o_out_bf16 && !aligned16(o_out_bf16)))
     return fail(QSA_ERR_ARG, "o_out and o_out_bf16 must be 16-byte aligned");
   const int64_t nmax = int64_t(max_ctx) / 4;
   if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
-  if (keys_seq_stride % 8 || keys_seq_stride < 0) return fail(QSA_ERR_ARG, "keys_seq_stride must be a non-negative multiple of 8");
-  if (q_seq && keys_seq_stride < nmax * 128) return fail(QSA_ERR_ARG, "keys_seq_stride smaller than max_ctx / 4 keys");
+  st = check_keys(sel_cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
+  if (st != QSA_OK) return st;
   const qsa::DecodeLayerPlan plan = qsa::plan_decode_layer(nq, max_ctx, sel_cfg->topk, attn_cfg->hq, attn_cfg->hkv,
                                                            attn_cfg->dv, n_split);
   if (int64_t(nq) * (plan.itk.n_chunks + attn_cfg->hkv * n_split) > 0x7FFFFFFF)
@@ -475,6 +529,7 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
   it.q_idx = q_idx;
   it.keys = keys;
   it.keys_ss = keys_seq_stride;
+  it.key_fp8 = sel_cfg->key_format == QSA_KEYS_FP8;
   it.scores = scores;
   it.ld = ld_scores;
   it.topk = sel_cfg->topk;

@@ -43,10 +43,21 @@ struct SelAttnLds {
   } u;
 };
 
-template <int TPW>
+template <int TPW, bool kFp8>
 __global__ __launch_bounds__(256) void index_lists_a(IndexTopkArgs a) {
   __shared__ itk::FinalLds sh;
-  itk::chunk_step<TPW, false>(a, blockIdx.y, blockIdx.x, sh);
+  itk::chunk_step<TPW, false, kFp8>(a, blockIdx.y, blockIdx.x, sh);
+}
+
+template <bool kFp8>
+void launch_lists_tpw(const IndexTopkArgs& a, int tpw, dim3 grid, hipStream_t s) {
+  switch (tpw) {
+    case 1: hipLaunchKernelGGL((index_lists_a<1, kFp8>), grid, dim3(256), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((index_lists_a<2, kFp8>), grid, dim3(256), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((index_lists_a<4, kFp8>), grid, dim3(256), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((index_lists_a<8, kFp8>), grid, dim3(256), 0, s, a); break;
+    default: hipLaunchKernelGGL((index_lists_a<16, kFp8>), grid, dim3(256), 0, s, a); break;
+  }
 }
 
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_select_a(IndexTopkArgs it,
@@ -129,13 +140,10 @@ hipError_t launch_index_lists(IndexTopkArgs a, const IndexTopkPlan& p, void* ws,
   a.keep = p.keep;
   a.wkeep = p.wkeep;
   dim3 grid(unsigned(p.n_chunks), unsigned(a.nq));
-  switch (p.tpw) {
-    case 1: hipLaunchKernelGGL(index_lists_a<1>, grid, dim3(256), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(index_lists_a<2>, grid, dim3(256), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(index_lists_a<4>, grid, dim3(256), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(index_lists_a<8>, grid, dim3(256), 0, s, a); break;
-    default: hipLaunchKernelGGL(index_lists_a<16>, grid, dim3(256), 0, s, a); break;
-  }
+  if (a.key_fp8)
+    launch_lists_tpw<true>(a, p.tpw, grid, s);
+  else
+    launch_lists_tpw<false>(a, p.tpw, grid, s);
   return hipGetLastError();
 }
 

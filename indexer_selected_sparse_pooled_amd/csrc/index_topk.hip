@@ -6,10 +6,21 @@
 namespace qsa {
 namespace {
 
-template <int TPW>
+template <int TPW, bool kFp8>
 __global__ __launch_bounds__(256) void index_topk_a(IndexTopkArgs a) {
   __shared__ itk::FinalLds sh;
-  itk::chunk_step<TPW>(a, blockIdx.y, blockIdx.x, sh);
+  itk::chunk_step<TPW, true, kFp8>(a, blockIdx.y, blockIdx.x, sh);
+}
+
+template <bool kFp8>
+void launch_tpw(const IndexTopkArgs& a, int tpw, dim3 grid, hipStream_t s) {
+  switch (tpw) {
+    case 1: hipLaunchKernelGGL((index_topk_a<1, kFp8>), grid, dim3(itk::kNT), 0, s, a); break;
+    case 2: hipLaunchKernelGGL((index_topk_a<2, kFp8>), grid, dim3(itk::kNT), 0, s, a); break;
+    case 4: hipLaunchKernelGGL((index_topk_a<4, kFp8>), grid, dim3(itk::kNT), 0, s, a); break;
+    case 8: hipLaunchKernelGGL((index_topk_a<8, kFp8>), grid, dim3(itk::kNT), 0, s, a); break;
+    default: hipLaunchKernelGGL((index_topk_a<16, kFp8>), grid, dim3(itk::kNT), 0, s, a); break;
+  }
 }
 
 }  // namespace
@@ -52,13 +63,10 @@ hipError_t launch_index_topk(IndexTopkArgs a, const IndexTopkPlan& p, void* ws, 
   a.keep = p.keep;
   a.wkeep = p.wkeep;
   dim3 grid(unsigned(p.n_chunks), unsigned(a.nq));
-  switch (p.tpw) {
-    case 1: hipLaunchKernelGGL(index_topk_a<1>, grid, dim3(itk::kNT), 0, s, a); break;
-    case 2: hipLaunchKernelGGL(index_topk_a<2>, grid, dim3(itk::kNT), 0, s, a); break;
-    case 4: hipLaunchKernelGGL(index_topk_a<4>, grid, dim3(itk::kNT), 0, s, a); break;
-    case 8: hipLaunchKernelGGL(index_topk_a<8>, grid, dim3(itk::kNT), 0, s, a); break;
-    default: hipLaunchKernelGGL(index_topk_a<16>, grid, dim3(itk::kNT), 0, s, a); break;
-  }
+  if (a.key_fp8)
+    launch_tpw<true>(a, p.tpw, grid, s);
+  else
+    launch_tpw<false>(a, p.tpw, grid, s);
   return hipGetLastError();
 }
 

@@ -39,6 +39,7 @@
 #pragma once
 
 #include "common.hpp"
+#include "fp8.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
 
@@ -261,7 +262,8 @@ __device__ void final_select(const IndexTopkArgs& a, int i, int n, FinalLds& sh,
 // caller may then hand the selection on.
 // kSelect == false: scores and lists only (the selection is made by the
 // caller's next kernel), and the function returns false.
-template <int TPW, bool kSelect = true>
+// kFp8: the keys are FP8 pages (fp8.hpp) instead of bf16 rows.
+template <int TPW, bool kSelect = true, bool kFp8 = false>
 __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& sh) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   constexpr int C = kNT * TPW;
@@ -282,8 +284,6 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   const int nch = (n + C - 1) / C;
 
   // ---- scan: scores of this chunk
-  const u32x4 qv = ld16(a.q_idx + int64_t(i) * 128 + 8 * (lane & 15));
-  const uint16_t* kb = a.keys + int64_t(seq) * a.keys_ss;
   float* out = a.scores + int64_t(i) * a.ld;
   const int64_t w0 = lo + int64_t(wave) * TPW * 64;
   uint32_t key[TPW];
@@ -291,20 +291,38 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   // the current one is scored. The loads are unconditional (tiles past n
   // re-read row n - 1): on a branch, scoring would have to wait for every
   // load in flight, the next tile's included.
-  u32x4 v[2][16];
-  load_tile(kb, w0, n, v[0]);
+  auto keep_score = [&](int t, int64_t tile0, float s) {
+    const int64_t blk = tile0 + lane;
+    if (blk < n) {
+      put<kSelect>(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
+      key[t] = order_key(s);
+    }
+  };
+  if constexpr (kFp8) {
+    float qf[16];
+    fp8::load_query(a.q_idx + int64_t(i) * 128, qf);
+    const uint8_t* kb = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
+    u32x4 v[2][8];
+    float sc[2];
+    fp8::load_tile(kb, w0, n, v[0], sc[0]);
 #pragma unroll
-  for (int t = 0; t < TPW; t++) {
-    const int64_t tile0 = w0 + 64 * t;
-    if (t + 1 < TPW) load_tile(kb, tile0 + 64, n, v[(t + 1) & 1]);
-    key[t] = 0u;
-    if (tile0 < n) {  // wave-uniform
-      const float s = tile_scores(v[t & 1], tile0, n, qv);
-      const int64_t blk = tile0 + lane;
-      if (blk < n) {
-        put<kSelect>(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
-        key[t] = order_key(s);
-      }
+    for (int t = 0; t < TPW; t++) {
+      const int64_t tile0 = w0 + 64 * t;
+      if (t + 1 < TPW) fp8::load_tile(kb, tile0 + 64, n, v[(t + 1) & 1], sc[(t + 1) & 1]);
+      key[t] = 0u;
+      if (tile0 < n) keep_score(t, tile0, fp8::tile_scores(v[t & 1], sc[t & 1], tile0, n, qf));  // wave-uniform
+    }
+  } else {
+    const u32x4 qv = ld16(a.q_idx + int64_t(i) * 128 + 8 * (lane & 15));
+    const uint16_t* kb = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss;
+    u32x4 v[2][16];
+    load_tile(kb, w0, n, v[0]);
+#pragma unroll
+    for (int t = 0; t < TPW; t++) {
+      const int64_t tile0 = w0 + 64 * t;
+      if (t + 1 < TPW) load_tile(kb, tile0 + 64, n, v[(t + 1) & 1]);
+      key[t] = 0u;
+      if (tile0 < n) keep_score(t, tile0, tile_scores(v[t & 1], tile0, n, qv));  // wave-uniform
     }
   }
 

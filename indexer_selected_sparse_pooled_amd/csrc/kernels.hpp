@@ -10,6 +10,10 @@ namespace qsa {
 
 hipError_t launch_pool(const uint16_t* raw, int64_t raw_ss, uint16_t* pooled, int64_t pooled_ss,
                        int n_seq, int64_t b0, int64_t nb, int dim, int block, hipStream_t s);
+// FP8 indexer keys (pages of 64: codes, then fp32 scales) of keys [k0, k0 + nk)
+// of n_seq sequences; out_ss in bytes.
+hipError_t launch_quantize(const uint16_t* keys, int64_t keys_ss, uint8_t* out, int64_t out_ss, int n_seq,
+                           int64_t k0, int64_t nk, int dim, hipStream_t s);
 
 // Decode-step append (one new token per query).
 struct AppendArgs {
@@ -27,8 +31,9 @@ struct AppendArgs {
   int head_dim, v_dim;
   uint16_t* raw;            // raw indexer keys, or nullptr
   int64_t raw_ss;
-  uint16_t* pooled;         // pooled keys, or nullptr (no pooling)
-  int64_t pooled_ss;
+  void* pooled;             // pooled keys (bf16 rows, or FP8 pages), or nullptr (no pooling)
+  int64_t pooled_ss;        // elements for bf16 rows, bytes for FP8 pages
+  int pooled_fp8;
   int dim, block;
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
@@ -43,8 +48,9 @@ struct ScoreArgs {
   int idx_heads;
   const uint16_t* q_idx;
   const float* w_idx;  // nullable when idx_heads == 1
-  const uint16_t* keys;
+  const void* keys;    // bf16 rows, or FP8 pages (key_fp8; keys_ss then in bytes)
   int64_t keys_ss;
+  int key_fp8;
   float* scores;
   int64_t ld;
 };
@@ -111,8 +117,9 @@ struct IndexTopkArgs {
   int max_ctx;
   int nq;
   const uint16_t* q_idx;
-  const uint16_t* keys;
+  const void* keys;  // bf16 rows, or FP8 pages (key_fp8; keys_ss then in bytes)
   int64_t keys_ss;
+  int key_fp8;
   float* scores;
   int64_t ld;
   int topk;

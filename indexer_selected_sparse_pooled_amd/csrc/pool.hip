@@ -8,6 +8,7 @@
 // (nearest, ties to even). Section "カーネルを書き換えずに済む": the cache is
 // addressed per (token, kv head).
 #include "common.hpp"
+#include "fp8.hpp"
 #include "kernels.hpp"
 
 namespace qsa {
@@ -59,6 +60,34 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t* __restrict__ 
   st16(pooled + s * pooled_ss + b * dim + 8 * c, out);
 }
 
+// FP8 indexer keys ("GLM-5.3 最適化 第2部", footnote 3: FP8 values plus a
+// 4-byte scale per key): one wave per key, dim <= 128. scale = amax / 448
+// and code = E4M3(x / scale), both quotients correctly rounded fp32
+// divisions; an all-zero key gets scale 0 and zero codes.
+__device__ __forceinline__ void quantize_key_wave(float x0, float x1, int dim, uint8_t* row, float* scale_at) {
+  const int lane = threadIdx.x & 63;
+  const float m = wave_max(fmaxf(fabsf(x0), fabsf(x1)));
+  const float sc = m / kE4m3Max;
+  if (lane < dim) row[lane] = uint8_t(sc > 0.f ? e4m3_code(x0 / sc) : 0u);
+  if (lane + 64 < dim) row[lane + 64] = uint8_t(sc > 0.f ? e4m3_code(x1 / sc) : 0u);
+  if (lane == 0) *scale_at = sc;
+}
+
+__global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restrict__ keys, int64_t keys_ss,
+                                                       uint8_t* __restrict__ out, int64_t out_ss, int64_t k0,
+                                                       int64_t nk, int dim) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t kk = int64_t(blockIdx.x) * 4 + wave;
+  if (kk >= nk) return;  // wave-uniform
+  const int64_t b = k0 + kk;
+  const int s = blockIdx.y;
+  const uint16_t* src = keys + s * keys_ss + b * dim;
+  const float x0 = lane < dim ? bf16_to_f32(src[lane]) : 0.f;
+  const float x1 = lane + 64 < dim ? bf16_to_f32(src[lane + 64]) : 0.f;
+  uint8_t* base = out + s * out_ss;
+  quantize_key_wave(x0, x1, dim, base + fp8_code_off(b, dim), reinterpret_cast<float*>(base + fp8_scale_off(b, dim)));
+}
+
 // One work-group per appended token (query i): copies the token's K and V
 // rows (every kv head) and its raw indexer key into the cache at position
 // q_pos[i] of sequence q_seq[i]; when the token completes a block, also
@@ -93,6 +122,26 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     st16(a.raw + int64_t(seq) * a.raw_ss + int64_t(pos) * a.dim + 8 * c, ld16(rn + 8 * c));
   if (!a.pooled || (pos + 1) % a.block != 0) return;
   const int64_t b = pos / a.block;
+  if (a.pooled_fp8) {
+    // the bf16 pooled key as below, then quantized (wave 0; dim <= 128)
+    if (tid >= 64) return;
+    const int lane = tid;
+    float x[2] = {0.f, 0.f};
+#pragma unroll
+    for (int h = 0; h < 2; h++) {
+      const int d = lane + 64 * h;
+      if (d < a.dim) {
+        double acc = double(bf16_to_f32(rn[d]));
+        for (int j = 0; j < a.block - 1; j++)
+          acc += double(bf16_to_f32(a.raw[int64_t(seq) * a.raw_ss + (b * a.block + j) * a.dim + d]));
+        x[h] = bf16_to_f32(f64_to_bf16(acc / a.block));
+      }
+    }
+    uint8_t* base = static_cast<uint8_t*>(a.pooled) + int64_t(seq) * a.pooled_ss;
+    quantize_key_wave(x[0], x[1], a.dim, base + fp8_code_off(b, a.dim),
+                      reinterpret_cast<float*>(base + fp8_scale_off(b, a.dim)));
+    return;
+  }
   for (int c = tid; c < rc; c += 256) {
     double acc[8];
     u32x4 w = ld16(rn + 8 * c);
@@ -113,7 +162,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; e++)
       out[e] = uint32_t(f64_to_bf16(acc[2 * e] / a.block)) | (uint32_t(f64_to_bf16(acc[2 * e + 1] / a.block)) << 16);
-    st16(a.pooled + int64_t(seq) * a.pooled_ss + b * a.dim + 8 * c, out);
+    st16(static_cast<uint16_t*>(a.pooled) + int64_t(seq) * a.pooled_ss + b * a.dim + 8 * c, out);
   }
 }
 
@@ -122,6 +171,14 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
 hipError_t launch_append(const AppendArgs& a, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
   hipLaunchKernelGGL(append_kernel, dim3(unsigned(a.nq)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize(const uint16_t* keys, int64_t keys_ss, uint8_t* out, int64_t out_ss, int n_seq,
+                           int64_t k0, int64_t nk, int dim, hipStream_t s) {
+  if (nk <= 0 || n_seq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_kernel, dim3(unsigned((nk + 3) / 4), unsigned(n_seq)), dim3(256), 0, s, keys, keys_ss,
+                     out, out_ss, k0, nk, dim);
   return hipGetLastError();
 }
 

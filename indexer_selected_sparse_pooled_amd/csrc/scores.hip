@@ -12,6 +12,7 @@
 // A prefill chunk (all queries in one sequence) uses MFMA 16x16x32 bf16
 // tiles: 16 queries x 16 keys x 32 dims per instruction.
 #include "common.hpp"
+#include "fp8.hpp"
 #include "kernels.hpp"
 
 namespace qsa {
@@ -39,7 +40,7 @@ __global__ __launch_bounds__(256) void scores_gemv_a(ScoreArgs a) {
   const int64_t wg0 = int64_t(blockIdx.x) * (4 * TPW * 64);
   if (wg0 >= n) return;
   const u32x4 qv = ld16(a.q_idx + int64_t(i) * 128 + 8 * c);
-  const uint16_t* kb = a.keys + int64_t(seq) * a.keys_ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss;
   float* out = a.scores + int64_t(i) * a.ld;
   for (int t = 0; t < TPW; t++) {
     const int64_t tile0 = wg0 + int64_t(wave * TPW + t) * 64;
@@ -86,6 +87,31 @@ __global__ __launch_bounds__(256) void scores_gemv_a(ScoreArgs a) {
   }
 }
 
+// Variant A decode with FP8 keys (fp8.hpp): 64 keys per tile, 8 lanes per
+// 128-byte code row, the key's scale applied to the dot product.
+template <int TPW>
+__global__ __launch_bounds__(256) void scores_gemv_a_fp8(ScoreArgs a) {
+  const int i = blockIdx.y;
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int64_t n = clamp_ctx(a.q_ctx[i], a.max_ctx) / a.block;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t wg0 = int64_t(blockIdx.x) * (4 * TPW * 64);
+  if (wg0 >= n) return;
+  float qf[16];
+  fp8::load_query(a.q_idx + int64_t(i) * 128, qf);
+  const uint8_t* kb = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
+  float* out = a.scores + int64_t(i) * a.ld;
+  for (int t = 0; t < TPW; t++) {
+    const int64_t tile0 = wg0 + int64_t(wave * TPW + t) * 64;
+    if (tile0 >= n) break;
+    u32x4 v[8];
+    float sc;
+    fp8::load_tile(kb, tile0, n, v, sc);
+    const float sv = fp8::tile_scores(v, sc, tile0, n, qf);
+    if (tile0 + lane < n) out[tile0 + lane] = sv;
+  }
+}
+
 // Variant B decode: 64-d token keys, 4 indexer heads, ReLU-weighted sum.
 // A wave owns 128 consecutive keys (16 KiB); lane (g = lane/8, c = lane%8)
 // loads dims [8c, 8c+8) of keys 8k+g; after the butterfly over the 8 lanes
@@ -105,7 +131,7 @@ __global__ __launch_bounds__(256) void scores_gemv_b(ScoreArgs a) {
     qv[h] = ld16(a.q_idx + (int64_t(i) * 4 + h) * 64 + 8 * c);
     w[h] = a.w_idx[int64_t(i) * 4 + h];
   }
-  const uint16_t* kb = a.keys + int64_t(seq) * a.keys_ss;
+  const uint16_t* kb = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss;
   float p[16][4];
 #pragma unroll
   for (int k = 0; k < 16; k++) {
@@ -199,13 +225,60 @@ __global__ __launch_bounds__(256) void scores_gemm_a(ScoreArgs a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < 4; ks++) {
-      u32x4 w = blk < nmax ? ld16(a.keys + blk * 128 + 32 * ks + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w = blk < nmax ? ld16(static_cast<const uint16_t*>(a.keys) + blk * 128 + 32 * ks + 8 * kq)
+                           : u32x4{0u, 0u, 0u, 0u};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], as_bf16x8(w), acc, 0, 0, 0);
     }
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       const int q = q0 + 16 * wave + 4 * kq + e;
       if (blk < nrow[e]) a.scores[int64_t(q) * a.ld + blk] = acc[e];
+    }
+  }
+}
+
+// Prefill chunk, variant A with FP8 keys: the same tiles, the B operand
+// converted from E4M3 to bf16 (exact) and each key column scaled after the
+// MFMA: score = scale_b * (q . codes_b).
+__global__ __launch_bounds__(256) void scores_gemm_a_fp8(ScoreArgs a) {
+  __shared__ int red[1];
+  const int q0 = blockIdx.y * 64;
+  const int64_t b0 = int64_t(blockIdx.x) * 128;
+  const int64_t nmax = wg_max_n(a, q0, red);
+  if (b0 >= nmax) return;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int r = lane & 15, kq = lane >> 4;
+  const int qa_row = q0 + 16 * wave + r;
+  const uint8_t* kb = static_cast<const uint8_t*>(a.keys);
+  bf16x8 qa[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ks++) {
+    u32x4 w = qa_row < a.nq ? ld16(a.q_idx + int64_t(qa_row) * 128 + 32 * ks + 8 * kq)
+                            : u32x4{0u, 0u, 0u, 0u};
+    qa[ks] = as_bf16x8(w);
+  }
+  int64_t nrow[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int q = q0 + 16 * wave + 4 * kq + e;
+    nrow[e] = q < a.nq ? clamp_ctx(a.q_ctx[q], a.max_ctx) / a.block : 0;
+  }
+  for (int nt = 0; nt < 8; nt++) {
+    const int64_t blk = b0 + 16 * nt + r;
+    if (b0 + 16 * nt >= nmax) break;
+    const int64_t bc = blk < nmax ? blk : nmax - 1;
+    const uint8_t* row = kb + fp8_code_off(bc, 128);
+    const float sc = *reinterpret_cast<const float*>(kb + fp8_scale_off(bc, 128));
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < 4; ks++) {
+      const u32x2 w = *reinterpret_cast<const u32x2*>(row + 32 * ks + 8 * kq);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], e4m3x8_bf16(w), acc, 0, 0, 0);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int q = q0 + 16 * wave + 4 * kq + e;
+      if (blk < nrow[e]) a.scores[int64_t(q) * a.ld + blk] = acc[e] * sc;
     }
   }
 }
@@ -244,7 +317,8 @@ __global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
     bf16x8 kb[2];
 #pragma unroll
     for (int ks = 0; ks < 2; ks++) {
-      u32x4 w = tok < nmax ? ld16(a.keys + tok * 64 + 32 * ks + 8 * kq) : u32x4{0u, 0u, 0u, 0u};
+      u32x4 w = tok < nmax ? ld16(static_cast<const uint16_t*>(a.keys) + tok * 64 + 32 * ks + 8 * kq)
+                           : u32x4{0u, 0u, 0u, 0u};
       kb[ks] = as_bf16x8(w);
     }
     float s[4] = {0.f, 0.f, 0.f, 0.f};
@@ -271,7 +345,21 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
   const int64_t nmax = int64_t(a.max_ctx) / a.block;
   if (nmax <= 0) return hipSuccess;
   const bool chunk = a.q_seq == nullptr && a.nq >= 16;
-  if (a.idx_heads == 1) {
+  if (a.idx_heads == 1 && a.key_fp8) {
+    if (chunk) {
+      dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
+      hipLaunchKernelGGL(scores_gemm_a_fp8, grid, dim3(256), 0, s, a);
+    } else {
+      const int64_t wgs1 = ((nmax + 255) / 256) * a.nq;
+      if (wgs1 >= 8192) {
+        dim3 grid(unsigned((nmax + 511) / 512), unsigned(a.nq));
+        hipLaunchKernelGGL(scores_gemv_a_fp8<2>, grid, dim3(256), 0, s, a);
+      } else {
+        dim3 grid(unsigned((nmax + 255) / 256), unsigned(a.nq));
+        hipLaunchKernelGGL(scores_gemv_a_fp8<1>, grid, dim3(256), 0, s, a);
+      }
+    }
+  } else if (a.idx_heads == 1) {
     if (chunk) {
       dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
       hipLaunchKernelGGL(scores_gemm_a, grid, dim3(256), 0, s, a);

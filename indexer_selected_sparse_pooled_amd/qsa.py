@@ -27,9 +27,13 @@ class QsaError(RuntimeError):
         self.status = status
 
 
+KEYS_BF16, KEYS_FP8 = 0, 1  # qsa_key_format
+
+
 class SelCfg(ctypes.Structure):
     _fields_ = [("block", ctypes.c_int32), ("topk", ctypes.c_int32),
-                ("idx_dim", ctypes.c_int32), ("idx_heads", ctypes.c_int32)]
+                ("idx_dim", ctypes.c_int32), ("idx_heads", ctypes.c_int32),
+                ("key_format", ctypes.c_int32)]
 
 
 class AttnCfg(ctypes.Structure):
@@ -45,9 +49,11 @@ class KV(ctypes.Structure):
 
 # The two parameter sets of the pages (variant A: pooled 4-token blocks,
 # variant B: token-level indexer with an MLA-like shared latent).
-SEL_A = SelCfg(4, 512, 128, 1)
+SEL_A = SelCfg(4, 512, 128, 1, KEYS_BF16)
+# variant A with FP8 pooled keys (128 E4M3 codes + an fp32 scale per block)
+SEL_A_FP8 = SelCfg(4, 512, 128, 1, KEYS_FP8)
 ATTN_A = AttnCfg(16, 2, 256, 256, 1.0 / 16.0)
-SEL_B = SelCfg(1, 2048, 64, 4)
+SEL_B = SelCfg(1, 2048, 64, 4, KEYS_BF16)
 ATTN_B = AttnCfg(64, 1, 576, 512, 1.0 / 24.0)
 
 _lib = None
@@ -55,6 +61,8 @@ _lib = None
 _vp, _i32, _i64, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
 _SIGS = {
     "qsa_pool_keys": [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _i32, _vp],
+    "qsa_quantize_keys": [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _vp],
+    "qsa_fp8_keys_bytes": [_i64, _i32],
     "qsa_kv_append": [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_index_scores": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_topk_blocks": [_vp, _i32, _vp, _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
@@ -72,7 +80,7 @@ _SIGS = {
     "qsa_last_error": [],
     "qsa_version": [],
 }
-_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz,
+_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_fp8_keys_bytes": _i64,
         "qsa_decode_layer_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
         "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
 EXPORTS = tuple(_SIGS)
@@ -114,6 +122,7 @@ def _dev(t, dtypes, name):
 
 
 _BF16 = (torch.bfloat16, torch.int16, torch.uint16)
+_U8 = (torch.uint8,)
 _F32 = (torch.float32,)
 _I32 = (torch.int32,)
 
@@ -145,19 +154,57 @@ def qsa_pool_keys(raw, pooled, tok_begin=0, tok_end=None, block=4, stream=None):
         n_seq, tok_begin, tok_end, dim, block, _stream(stream)))
 
 
+def qsa_fp8_keys_bytes(n_keys, dim) -> int:
+    return int(lib().qsa_fp8_keys_bytes(n_keys, dim))
+
+
+def fp8_keys_empty(n_seq, n_keys, dim, device="cuda"):
+    """A zero-filled uint8 [n_seq, bytes] tensor that holds n_keys FP8 keys
+    per sequence in the library's page layout."""
+    return torch.zeros(n_seq, qsa_fp8_keys_bytes(n_keys, dim), dtype=torch.uint8, device=device)
+
+
+def qsa_quantize_keys(keys, out, key_begin=0, key_end=None, stream=None):
+    """keys: [n_seq, n_keys, dim] bf16; out: fp8_keys_empty(n_seq, >= key_end, dim)."""
+    n_seq, n_keys, dim = keys.shape
+    _rowmajor_tail(keys, "keys", 2)
+    if key_end is None:
+        key_end = n_keys
+    if key_end > n_keys or out.dim() != 2 or out.shape[0] != n_seq or out.stride(1) != 1 or \
+            out.shape[1] < qsa_fp8_keys_bytes(key_end, dim):
+        raise ValueError("qsa_quantize_keys: shapes do not cover the key range")
+    _check("qsa_quantize_keys", lib().qsa_quantize_keys(
+        _dev(keys, _BF16, "keys"), keys.stride(0), _dev(out, _U8, "out"), out.stride(0), n_seq, key_begin, key_end,
+        dim, _stream(stream)))
+
+
+def _keys_arg(cfg, keys, max_ctx, fn):
+    """(pointer, sequence stride) of indexer keys: bf16 [n_seq, n_keys, dim]
+    (stride in elements) or, for FP8 configurations, the uint8 [n_seq, bytes]
+    page buffer (stride in bytes)."""
+    n = max_ctx // cfg.block
+    if cfg.key_format == KEYS_FP8:
+        if keys.dim() != 2 or keys.stride(1) != 1 or keys.shape[1] < qsa_fp8_keys_bytes(n, cfg.idx_dim):
+            raise ValueError(f"{fn}: FP8 keys must be a uint8 [n_seq, bytes] buffer holding max_ctx / block keys")
+        return _dev(keys, _U8, "keys"), keys.stride(0)
+    _rowmajor_tail(keys, "keys", 2)
+    if n > keys.shape[1]:
+        raise ValueError(f"{fn}: keys hold fewer than max_ctx / block rows")
+    return _dev(keys, _BF16, "keys"), keys.stride(0)
+
+
 def qsa_index_scores(cfg, q_ctx, max_ctx, q_idx, keys, scores, q_seq=None, w_idx=None, stream=None):
-    """q_ctx: [nq] int32; q_idx: [nq, heads, dim] bf16; keys: [n_seq, n_keys, dim] bf16;
+    """q_ctx: [nq] int32; q_idx: [nq, heads, dim] bf16; keys: [n_seq, n_keys, dim] bf16, or
+    for cfg.key_format KEYS_FP8 a uint8 [n_seq, bytes] page buffer (fp8_keys_empty);
     scores: [nq, ld] fp32; q_seq: [nq] int32 or None; w_idx: [nq, heads] fp32 or None."""
     nq = q_ctx.shape[0]
     _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(keys, "keys", 2)
     _rowmajor_tail(scores, "scores", 1)
-    if max_ctx // cfg.block > keys.shape[1]:
-        raise ValueError("qsa_index_scores: keys hold fewer than max_ctx / block rows")
+    kp, kss = _keys_arg(cfg, keys, max_ctx, "qsa_index_scores")
     _check("qsa_index_scores", lib().qsa_index_scores(
         ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
-        _dev(q_idx, _BF16, "q_idx"), _dev(w_idx, _F32, "w_idx"), _dev(keys, _BF16, "keys"),
-        keys.stride(0), _dev(scores, _F32, "scores"), scores.stride(0), _stream(stream)))
+        _dev(q_idx, _BF16, "q_idx"), _dev(w_idx, _F32, "w_idx"), kp, kss, _dev(scores, _F32, "scores"),
+        scores.stride(0), _stream(stream)))
 
 
 def qsa_topk_workspace_bytes(cfg, nq, max_ctx) -> int:
@@ -200,15 +247,13 @@ def qsa_index_topk(cfg, q_ctx, max_ctx, q_idx, keys, scores, sel, n_sel, ws, q_s
     ws: index_topk_workspace(...)."""
     nq = q_ctx.shape[0]
     _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(keys, "keys", 2)
     _rowmajor_tail(scores, "scores", 1)
-    if max_ctx // cfg.block > keys.shape[1]:
-        raise ValueError("qsa_index_topk: keys hold fewer than max_ctx / block rows")
+    kp, kss = _keys_arg(cfg, keys, max_ctx, "qsa_index_topk")
     if sel.shape != (nq, cfg.topk) or not sel.is_contiguous():
         raise ValueError("qsa_index_topk: sel must be a contiguous [nq, topk] tensor")
     _check("qsa_index_topk", lib().qsa_index_topk(
         ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
-        _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0),
+        _dev(q_idx, _BF16, "q_idx"), kp, kss,
         _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"),
         ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -218,13 +263,11 @@ def qsa_index_lists(cfg, q_ctx, max_ctx, q_idx, keys, scores, ws, q_seq=None, st
     chunk candidate lists (in ws: index_topk_workspace(...)); no selection."""
     nq = q_ctx.shape[0]
     _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(keys, "keys", 2)
     _rowmajor_tail(scores, "scores", 1)
-    if max_ctx // cfg.block > keys.shape[1]:
-        raise ValueError("qsa_index_lists: keys hold fewer than max_ctx / block rows")
+    kp, kss = _keys_arg(cfg, keys, max_ctx, "qsa_index_lists")
     _check("qsa_index_lists", lib().qsa_index_lists(
         ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
-        _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0),
+        _dev(q_idx, _BF16, "q_idx"), kp, kss,
         _dev(scores, _F32, "scores"), scores.stride(0), ctypes.c_void_p(ws.data_ptr()),
         ws.numel() * ws.element_size(), _stream(stream)))
 
@@ -245,15 +288,13 @@ def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scor
                      o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
     """One decode layer (two launches): qsa_index_topk, then qsa_sparse_decode
     and qsa_lse_merge. q_idx: [nq, 1, 128] bf16; keys: [n_seq, n_blocks, 128]
-    bf16; q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk;
+    bf16 (or FP8 pages, see qsa_index_scores); q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk;
     o_out: [nq, hq, dv] fp32, o_out_bf16: [nq, hq, dv] bf16, lse_out: [nq, hq]
     fp32 (each optional); ws: decode_layer_workspace(...)."""
     nq = q_ctx.shape[0]
     _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(keys, "keys", 2)
     _rowmajor_tail(scores, "scores", 1)
-    if max_ctx // sel_cfg.block > keys.shape[1]:
-        raise ValueError("qsa_decode_layer: keys hold fewer than max_ctx / block rows")
+    kp, kss = _keys_arg(sel_cfg, keys, max_ctx, "qsa_decode_layer")
     if sel.shape != (nq, sel_cfg.topk) or not sel.is_contiguous():
         raise ValueError("qsa_decode_layer: sel must be a contiguous [nq, topk] tensor")
     if not q.is_contiguous():
@@ -265,7 +306,7 @@ def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scor
             raise ValueError(f"qsa_decode_layer: {name} must be a contiguous {list(shp)} tensor")
     _check("qsa_decode_layer", lib().qsa_decode_layer(
         ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"),
-        max_ctx, _dev(q_idx, _BF16, "q_idx"), _dev(keys, _BF16, "keys"), keys.stride(0), _dev(q, _BF16, "q"),
+        max_ctx, _dev(q_idx, _BF16, "q_idx"), kp, kss, _dev(q, _BF16, "q"),
         ctypes.byref(kv), _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"),
         _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_out, _F32, "o_out"), _dev(o_out_bf16, _BF16, "o_out_bf16"),
         _dev(lse_out, _F32, "lse_out"), ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
@@ -278,19 +319,25 @@ def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None,
     [nq]): k_new [nq, hkv, dk] (and v_new [nq, hkv, dv] unless the cache's v
     is its k), raw_new [nq, idx_dim] into raw_keys [n_seq, capacity, idx_dim],
     and the pooled key [n_seq, n_blocks, idx_dim] of each block a token
-    completes. kv: make_kv(...) of the cache."""
+    completes (for an FP8 sel_cfg: quantized into the uint8 [n_seq, bytes]
+    page buffer). kv: make_kv(...) of the cache."""
     nq = q_pos.shape[0]
     for t, name in ((k_new, "k_new"), (v_new, "v_new"), (raw_new, "raw_new")):
         if t is not None and (t.shape[0] != nq or not t.is_contiguous()):
             raise ValueError(f"qsa_kv_append: {name} must be contiguous with {nq} rows")
-    for t, name in ((raw_keys, "raw_keys"), (pooled, "pooled")):
-        if t is not None:
-            _rowmajor_tail(t, name, 2)
+    fp8 = sel_cfg.key_format == KEYS_FP8
+    if raw_keys is not None:
+        _rowmajor_tail(raw_keys, "raw_keys", 2)
+    if pooled is not None:
+        if fp8 and (pooled.dim() != 2 or pooled.stride(1) != 1):
+            raise ValueError("qsa_kv_append: FP8 pooled keys must be a uint8 [n_seq, bytes] page buffer")
+        if not fp8:
+            _rowmajor_tail(pooled, "pooled", 2)
     _check("qsa_kv_append", lib().qsa_kv_append(
         ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_pos, _I32, "q_pos"),
         _dev(k_new, _BF16, "k_new"), _dev(v_new, _BF16, "v_new"), _dev(raw_new, _BF16, "raw_new"), ctypes.byref(kv),
         _dev(raw_keys, _BF16, "raw_keys"), 0 if raw_keys is None else raw_keys.stride(0),
-        _dev(pooled, _BF16, "pooled"), 0 if pooled is None else pooled.stride(0), _stream(stream)))
+        _dev(pooled, _U8 if fp8 else _BF16, "pooled"), 0 if pooled is None else pooled.stride(0), _stream(stream)))
 
 
 _hip = None

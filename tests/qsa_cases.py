@@ -125,3 +125,29 @@ def check_row(gpu_sel, gpu_n, o, lse, ob, ref, ctx, block, topk, q_bits, k_bits,
         o_ref, lse_ref = orc.attend(q_bits, k_bits, v_bits, toks, scale, dv)
     check_attention(o, lse, o_ref, lse_ref, ob)
     return same
+
+
+# ---- FP8 key pages (layout only: 64 keys per page, codes then fp32 scales)
+
+def unpack_fp8_pages(buf, n, dim):
+    """(codes uint8 [n][dim], scales float32 [n]) of keys 0..n-1 in one
+    sequence's page buffer (uint8 array)."""
+    buf = np.asarray(buf, dtype=np.uint8)
+    page = 64 * (dim + 4)
+    npg = -(-n // 64)
+    p = buf[:npg * page].reshape(npg, page)
+    codes = p[:, :64 * dim].reshape(npg * 64, dim)[:n]
+    scales = np.ascontiguousarray(p[:, 64 * dim:]).view(np.float32).reshape(-1)[:n]
+    return codes, scales
+
+
+def pack_fp8_pages(codes, scales):
+    """The page buffer of keys given as codes [n][dim] and scales [n]."""
+    n, dim = codes.shape
+    npg = -(-n // 64)
+    c = np.zeros((npg * 64, dim), dtype=np.uint8)
+    c[:n] = codes
+    s = np.zeros(npg * 64, dtype=np.float32)
+    s[:n] = scales
+    pages = np.concatenate([c.reshape(npg, 64 * dim), s.view(np.uint8).reshape(npg, 256)], axis=1)
+    return pages.reshape(-1)

@@ -74,3 +74,36 @@ def test_topk_workspace_query(lib):
     assert qsa.qsa_topk_workspace_bytes(qsa.SEL_A, 4, 8192) == 0
     big = qsa.qsa_topk_workspace_bytes(qsa.SEL_A, 4, 1048320)
     assert big > 0 and big % 16 == 0
+
+
+def test_fp8_key_layout_sizes(lib):
+    """Pages of 64 keys, each key idx_dim codes + a 4-byte scale (132 bytes
+    for the 128-d pooled key)."""
+    assert lib.qsa_fp8_keys_bytes(64, 128) == 64 * 132
+    assert lib.qsa_fp8_keys_bytes(65, 128) == 2 * 64 * 132
+    assert lib.qsa_fp8_keys_bytes(0, 128) == 0
+    assert lib.qsa_fp8_keys_bytes(262080, 128) == 262080 * 132  # 4095 whole pages
+    assert lib.qsa_fp8_keys_bytes(1, 64) == 64 * 68
+
+
+def test_fp8_validation_on_the_host(lib):
+    from indexer_selected_sparse_pooled_amd import qsa
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    # unknown key format
+    cfg = qsa.SelCfg(4, 512, 128, 1, 7)
+    st = lib.qsa_index_scores(ctypes.byref(cfg), 1, None, fake, 4096, fake, None, fake, 0, fake, 1024, None)
+    assert st == 2 and b"key_format" in lib.qsa_last_error()
+    # FP8 keys with the 4-head token indexer: not supported
+    cfg = qsa.SelCfg(1, 2048, 64, 4, qsa.KEYS_FP8)
+    st = lib.qsa_index_scores(ctypes.byref(cfg), 1, None, fake, 4096, fake, fake, fake, 0, fake, 4096, None)
+    assert st == 2 and b"FP8" in lib.qsa_last_error()
+    # FP8 sequence stride must be a multiple of 16 bytes and hold the pages
+    st = lib.qsa_index_scores(ctypes.byref(qsa.SEL_A_FP8), 1, fake, fake, 4096, fake, None, fake, 8, fake, 1024,
+                              None)
+    assert st == 1
+    st = lib.qsa_index_scores(ctypes.byref(qsa.SEL_A_FP8), 1, fake, fake, 4096, fake, None, fake, 16 * 100,
+                              fake, 1024, None)
+    assert st == 1 and b"pages" in lib.qsa_last_error()
+    # quantize: only 64- and 128-d keys
+    st = lib.qsa_quantize_keys(fake, 0, fake, 0, 1, 0, 10, 96, None)
+    assert st == 2

@@ -35,3 +35,10 @@ def test_decode_unit_at_1m():
     assert b == 262080 * 256 + 256 + 4194304 + 8192 + 8192
     assert bm.attended_tokens(2051) == 2051 and bm.attended_tokens(2052) == 2048
     assert bm.attended_tokens(1048323) == 2051
+
+
+def test_fp8_scan_bytes():
+    """FP8 keys: 128 codes + a 4-byte scale = 132 bytes per pooled block
+    ("GLM-5.3 ...", footnote 3), against 256 for bf16."""
+    assert bm.scan_bytes_fp8(1048320) == 262080 * 132
+    assert bm.decode_unit_bytes(1048320) - bm.decode_unit_bytes_fp8(1048320) == 262080 * (256 - 132)
