@@ -111,6 +111,16 @@ typedef struct {
  * q_ctx <= capacity). The pages' gather kernel uses
  * [token][kv_head][head_dim] ("カーネルを書き換えずに済む"): tok_stride =
  * hkv * dk, head_stride = dk. */
+typedef enum { QSA_KV_BF16 = 0, QSA_KV_FP8_MLA = 1 } qsa_kv_format;
+
+/* format QSA_KV_FP8_MLA (the shared-latent shape only, v == k): each token
+ * holds one 656-byte FP8 sparse-MLA row ("GLM-5.3 ...", footnote 1): bytes
+ * [0, 512) the first 512 latent values as OCP E4M3 codes, [512, 528) four
+ * fp32 scales (one per 128 codes; value = code * scale), [528, 656) the 64
+ * rotary values as bf16. k points at the rows; the row of (sequence s,
+ * token t) starts at byte s * seq_stride + t * tok_stride (strides in
+ * bytes, multiples of 16, tok_stride >= 656; head_stride unused).
+ * qsa_quantize_latent and qsa_kv_append write these rows. */
 typedef struct {
   const qsa_bf16* k;
   const qsa_bf16* v;
@@ -118,6 +128,7 @@ typedef struct {
   int64_t tok_stride;
   int64_t head_stride;
   int64_t capacity;
+  int32_t format;   /* qsa_kv_format */
 } qsa_kv;
 
 /* ---------------------------------------------------------------- A1 ----
@@ -160,13 +171,27 @@ qsa_status qsa_quantize_keys(const qsa_bf16* keys, int64_t keys_seq_stride, void
 /* Bytes that hold FP8 keys 0 .. n_keys-1 of one sequence (whole pages). */
 int64_t qsa_fp8_keys_bytes(int64_t n_keys, int32_t dim);
 
+/* qsa_quantize_latent: FP8 sparse-MLA rows (QSA_KV_FP8_MLA) of tokens
+ * [tok_begin, tok_end) of n_seq sequences from 576-wide bf16 latent rows:
+ * values 128g .. 128g+127 (g < 4) quantized as qsa_quantize_keys does with
+ * one scale per group, the 64 rotary values copied. ("GLM-5.3 ...",
+ * footnote 1: the 656-byte FP8 row.)
+ *   latent (device) bf16: row (s, t) at latent + s*seq_stride + t*tok_stride
+ *          (elements, multiples of 8, tok_stride >= 576).
+ *   out    (device): row (s, t) at byte s*out_seq_stride + t*out_tok_stride
+ *          (multiples of 16, out_tok_stride >= 656). */
+qsa_status qsa_quantize_latent(const qsa_bf16* latent, int64_t seq_stride, int64_t tok_stride, void* out,
+                               int64_t out_seq_stride, int64_t out_tok_stride, int32_t n_seq,
+                               int64_t tok_begin, int64_t tok_end, qsa_stream_t stream);
+
 /* ------------------------------------------------- A1 at decode time ----
  * qsa_kv_append: the decode step's write of one new token per query into
  * the cache, before the layer reads it. Query i writes, at position
  * q_pos[i] of sequence q_seq[i] (sequence i if q_seq is NULL):
  *   - its K row for every kv head (k_new[i], hkv x dk) and, unless the
  *     cache's v is its k (a shared latent row), its V row (v_new[i],
- *     hkv x dv), addressed as in qsa_kv;
+ *     hkv x dv), addressed as in qsa_kv; a QSA_KV_FP8_MLA cache gets the
+ *     row quantized as qsa_quantize_latent does;
  *   - its raw indexer key (raw_new[i], idx_dim values) at raw_keys +
  *     seq * raw_seq_stride + pos * idx_dim, when raw_new is given;
  *   - when pos + 1 is a multiple of block and pooled is given, the pooled
@@ -297,6 +322,8 @@ qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_
  * rows are read; "カーネルを書き換えずに済む": rows addressed per token and
  * kv head.)
  *   q        (device) bf16 [nq][hq][dk].
+ *   kv       bf16 rows, or (shared-latent shape) FP8 sparse-MLA rows, each
+ *            standing for its dequantized values in both K and V.
  *   o_part   (device) fp32 [n_split][nq][hq][dv];
  *   lse_part (device) fp32 [n_split][nq][hq] (natural log).
  *   1 <= n_split <= 256. Combine the splits with qsa_lse_merge. */
@@ -317,7 +344,7 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
  * ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの" and "なぜ";
  * "GLM-5.3 ...", "DCP".)
  * Variant A only (block 4, idx_dim 128, idx_heads 1, bf16 or FP8 keys; hq
- * 16, hkv 2, dk = dv = 256); other configurations return
+ * 16, hkv 2, dk = dv = 256; bf16 K/V rows); other configurations return
  * QSA_ERR_UNSUPPORTED. nq <= 4096.
  *   q_seq, q_ctx, q_idx, keys, scores, ld_scores, sel, n_sel: as
  *          qsa_index_topk (scores, sel and n_sel are written as there).

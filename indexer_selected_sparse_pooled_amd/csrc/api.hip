@@ -108,6 +108,19 @@ qsa_status check_keys(const qsa_sel_cfg* c, const void* keys, int64_t ss, int64_
   return QSA_OK;
 }
 
+// The cache format: bf16 rows, or FP8 sparse-MLA rows (656 bytes, strides in
+// bytes, multiples of 16; the shared-latent shape with v == k only).
+qsa_status check_kv_format(const qsa_attn_cfg* ac, const qsa_kv* kv) {
+  if (kv->format == QSA_KV_BF16) return QSA_OK;
+  if (kv->format != QSA_KV_FP8_MLA) return fail(QSA_ERR_UNSUPPORTED, "kv format %d not supported", kv->format);
+  if (!(ac->hq == 64 && ac->hkv == 1 && ac->dk == 576 && ac->dv == 512))
+    return fail(QSA_ERR_UNSUPPORTED, "FP8 rows: only the 576-wide shared latent (hq 64, hkv 1, dk 576, dv 512)");
+  if (kv->v != kv->k) return fail(QSA_ERR_ARG, "FP8 rows: v must equal k (one latent row per token)");
+  if (kv->tok_stride < 656 || kv->tok_stride % 16 || kv->seq_stride % 16 || kv->seq_stride < 0)
+    return fail(QSA_ERR_ARG, "FP8 rows: tok_stride >= 656 and strides multiples of 16 bytes");
+  return QSA_OK;
+}
+
 // Attention inputs (everything but the output buffers).
 qsa_status check_attn_inputs(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int nq, const int32_t* q_ctx,
                              int max_ctx, const qsa_bf16* q, const qsa_kv* kv, const int32_t* sel,
@@ -127,11 +140,15 @@ qsa_status check_attn_inputs(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int 
   if (!q_ctx || !q || !kv->k || !kv->v || !sel || !n_sel) return fail(QSA_ERR_ARG, "NULL pointer argument");
   if (!aligned16(q) || !aligned16(kv->k) || !aligned16(kv->v) || !aligned16(sel))
     return fail(QSA_ERR_ARG, "q, k, v and sel must be 16-byte aligned");
-  if (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 || kv->head_stride < 0 ||
-      kv->seq_stride < 0)
-    return fail(QSA_ERR_ARG, "kv strides must be non-negative multiples of 8");
-  if (int64_t(ac->hkv - 1) * kv->head_stride + ac->dk > kv->tok_stride)
-    return fail(QSA_ERR_ARG, "tok_stride too small for hkv heads of dk");
+  st = check_kv_format(ac, kv);
+  if (st != QSA_OK) return st;
+  if (kv->format == QSA_KV_BF16) {
+    if (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 ||
+        kv->head_stride < 0 || kv->seq_stride < 0)
+      return fail(QSA_ERR_ARG, "kv strides must be non-negative multiples of 8");
+    if (int64_t(ac->hkv - 1) * kv->head_stride + ac->dk > kv->tok_stride)
+      return fail(QSA_ERR_ARG, "tok_stride too small for hkv heads of dk");
+  }
   if (kv->capacity < max_ctx) return fail(QSA_ERR_ARG, "kv capacity %lld < max_ctx %d", (long long)kv->capacity, max_ctx);
   return QSA_OK;
 }
@@ -167,6 +184,7 @@ qsa::AttendArgs attend_args(const qsa_sel_cfg* sc, const qsa_attn_cfg* ac, int n
   a.seq_stride = kv->seq_stride;
   a.tok_stride = kv->tok_stride;
   a.head_stride = kv->head_stride;
+  a.kv_fp8 = kv->format == QSA_KV_FP8_MLA;
   a.sel = sel;
   a.n_sel = n_sel;
   a.topk = sc->topk;
@@ -203,6 +221,26 @@ qsa_status qsa_pool_keys(const qsa_bf16* raw, int64_t raw_seq_stride, qsa_bf16* 
   hipStream_t s = static_cast<hipStream_t>(stream);
   return finish(qsa::launch_pool(raw, raw_seq_stride, pooled, pooled_seq_stride, n_seq, b0, b1 - b0, dim, block, s), s,
                 "qsa_pool_keys");
+}
+
+qsa_status qsa_quantize_latent(const qsa_bf16* latent, int64_t seq_stride, int64_t tok_stride, void* out,
+                               int64_t out_seq_stride, int64_t out_tok_stride, int32_t n_seq, int64_t tok_begin,
+                               int64_t tok_end, qsa_stream_t stream) {
+  if (n_seq < 0 || tok_begin < 0 || tok_end < tok_begin) return fail(QSA_ERR_ARG, "bad n_seq or token range");
+  if (n_seq == 0 || tok_end == tok_begin) return QSA_OK;
+  if (!latent || !out) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(latent) || !aligned16(out)) return fail(QSA_ERR_ARG, "latent and out must be 16-byte aligned");
+  if (seq_stride % 8 || tok_stride % 8 || seq_stride < 0 || tok_stride < 576)
+    return fail(QSA_ERR_ARG, "latent strides: multiples of 8 elements, tok_stride >= 576");
+  if (out_seq_stride % 16 || out_tok_stride % 16 || out_seq_stride < 0 || out_tok_stride < 656)
+    return fail(QSA_ERR_ARG, "out strides: multiples of 16 bytes, out_tok_stride >= 656");
+  if (n_seq > 65535 || tok_end - tok_begin > 0x7FFFFFFF) return fail(QSA_ERR_UNSUPPORTED, "too many rows");
+  qsa_status st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return finish(qsa::launch_quantize_latent(latent, seq_stride, tok_stride, static_cast<uint8_t*>(out), out_seq_stride,
+                                            out_tok_stride, n_seq, tok_begin, tok_end - tok_begin, s),
+                s, "qsa_quantize_latent");
 }
 
 int64_t qsa_fp8_keys_bytes(int64_t n_keys, int32_t dim) {
@@ -246,15 +284,19 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
   if (hkv <= 0 || dk <= 0 || dv <= 0 || dk % 8 || dv % 8 || dv > dk)
     return fail(QSA_ERR_ARG, "hkv, dk, dv must be positive multiples of 8 with dv <= dk");
   if (!q_pos || !k_new || !kv->k) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  st = check_kv_format(attn_cfg, kv);
+  if (st != QSA_OK) return st;
+  const bool fp8_rows = kv->format == QSA_KV_FP8_MLA;
   const bool shared = kv->v == kv->k;  // a latent row serves as K and (its first dv columns) V
   if (!shared && (!v_new || !kv->v)) return fail(QSA_ERR_ARG, "v_new and kv->v are required when v != k");
   if (shared && v_new) return fail(QSA_ERR_ARG, "v_new must be NULL when kv->v == kv->k");
   if (!aligned16(k_new) || (v_new && !aligned16(v_new)) || !aligned16(kv->k) || !aligned16(kv->v))
     return fail(QSA_ERR_ARG, "k_new, v_new, k and v must be 16-byte aligned");
-  if (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 || kv->head_stride < 0 ||
-      kv->seq_stride < 0)
+  if (!fp8_rows && (kv->tok_stride % 8 || kv->head_stride % 8 || kv->seq_stride % 8 || kv->tok_stride <= 0 ||
+                    kv->head_stride < 0 || kv->seq_stride < 0))
     return fail(QSA_ERR_ARG, "kv strides must be non-negative multiples of 8");
-  if (int64_t(hkv - 1) * kv->head_stride + dk > kv->tok_stride) return fail(QSA_ERR_ARG, "tok_stride too small");
+  if (!fp8_rows && int64_t(hkv - 1) * kv->head_stride + dk > kv->tok_stride)
+    return fail(QSA_ERR_ARG, "tok_stride too small");
   if (kv->capacity <= 0 || kv->capacity > 0x7FFFFFFF) return fail(QSA_ERR_ARG, "bad kv capacity");
   const int dim = sel_cfg->idx_dim;
   if (raw_new || raw_keys) {
@@ -291,6 +333,7 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
   a.seq_stride = kv->seq_stride;
   a.tok_stride = kv->tok_stride;
   a.head_stride = kv->head_stride;
+  a.kv_fp8 = fp8_rows;
   a.k_row = hkv * dk;
   a.v_row = hkv * dv;
   a.head_dim = dk;
@@ -500,6 +543,7 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
   if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
   if (nq == 0) return QSA_OK;
   if (nq > 4096) return fail(QSA_ERR_UNSUPPORTED, "nq > 4096");
+  if (kv->format != QSA_KV_BF16) return fail(QSA_ERR_UNSUPPORTED, "qsa_decode_layer: bf16 K/V rows only");
   if (!q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
   if (!o_out && !o_out_bf16 && !lse_out) return fail(QSA_ERR_ARG, "no output requested");
   if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");

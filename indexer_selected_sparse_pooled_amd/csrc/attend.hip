@@ -22,6 +22,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   mla::attend_part<false>(a, split, i, sh);
 }
 
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_b_fp8(AttendArgs a) {
+  __shared__ mla::LdsF8 sh;
+  const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
+  mla::attend_part_fp8<false>(a, split, i, sh);
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
@@ -32,7 +38,10 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.hq == mla::kH && a.hkv == 1 && a.dk == mla::kDK && a.dv == mla::kDV) {
-    hipLaunchKernelGGL(attend_b, dim3(unsigned(int64_t(a.nq) * a.n_split)), dim3(256), 0, s, a);
+    if (a.kv_fp8)
+      hipLaunchKernelGGL(attend_b_fp8, dim3(unsigned(int64_t(a.nq) * a.n_split)), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(attend_b, dim3(unsigned(int64_t(a.nq) * a.n_split)), dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

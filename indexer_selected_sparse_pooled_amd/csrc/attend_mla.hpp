@@ -26,6 +26,7 @@
 #pragma once
 
 #include "attend.hpp"
+#include "fp8.hpp"
 
 namespace qsa {
 namespace mla {
@@ -177,6 +178,222 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
   }
 
   // normalise and write the partial result: heads 16*wave + 4kq + e
+  const int64_t orow0 = (int64_t(split) * a.nq + i) * kH + 16 * wave;
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    const int hrow = 4 * kq + e;
+    const float inv = l[e] > 0.f ? 1.f / l[e] : 0.f;
+    float* op = a.o_part + (orow0 + hrow) * kDV + r;
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++) op[16 * nt] = o[nt][e] * inv;
+    if (r == 0) a.lse_part[orow0 + hrow] = l[e] > 0.f ? (m[e] + log2f(l[e])) * kLn2 : -INFINITY;
+  }
+}
+
+// ---- FP8 latent rows
+// "GLM-5.3 最適化 第2部", footnote 1: the FP8 sparse-MLA row is 656 bytes:
+// the 512 latent values as E4M3 codes in 4 groups of 128 with one fp32
+// scale each (value = code * scale), then the 64 rotary values in bf16:
+//   bytes [0, 512) codes, [512, 528) scales, [528, 656) rotary values.
+// Same work-group layout and MFMA tiles as above; per tile:
+//   * the 32 rows arrive by LDS DMA in a staging area (656-byte stride);
+//   * all threads convert the codes to bf16 (exact, unscaled) into the bf16
+//     tile above, copy the rotary values and keep the 4 scales per token;
+//     the staging area is then free and the next tile's rows are requested
+//     at once, so their gather overlaps this tile's MFMA work;
+//   * S: each 128-column group's MFMA partial is scaled by the token's
+//     group scale (the rotary columns are not scaled);
+//   * O += P' V per group, with P' = P * (the token's group scale) split
+//     into bf16 hi + lo parts, so the codes serve as V unscaled.
+constexpr int kF8Row = 656;                 // bytes per FP8 row
+constexpr int kF8RowC = kF8Row / 16;        // 16-byte chunks per FP8 row (41)
+constexpr int kF8TileC = kTT * kF8RowC;     // chunks per staged tile (1312)
+
+struct LdsF8 {
+  __attribute__((aligned(16))) unsigned char kv[kTileC * 16];      // bf16 tile (as Lds::kv)
+  __attribute__((aligned(16))) unsigned char stage[kF8TileC * 16];  // FP8 rows of the tile in flight
+  __attribute__((aligned(16))) uint16_t p[4][2][16 * kPStr];
+  float sc[kTT][4];
+  int64_t range[2];
+};
+
+template <bool kCoh>
+__device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int r = lane & 15, kq = lane >> 4;
+
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
+  att::List<kCoh> lv;
+  lv.sel = a.sel + int64_t(i) * a.topk;
+  lv.block = a.block;
+  lv.nblk = ctx / a.block;
+  const int ns_max = lv.nblk < a.topk ? lv.nblk : a.topk;
+  const int ns = kCoh ? ns_max : a.n_sel[i];
+  lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
+  lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
+  if (tid == 0) {
+    const int lo = int(int64_t(split) * lv.L / a.n_split);
+    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int t0 = lv.count_below(a.tile_begin, ctx);
+    const int t1 = lv.count_below(a.tile_end, ctx);
+    sh.range[0] = lo > t0 ? lo : t0;
+    sh.range[1] = hi < t1 ? hi : t1;
+  }
+  __syncthreads();
+  const int P0 = int(sh.range[0]), P1 = int(sh.range[1]);
+
+  // strides in bytes
+  const unsigned char* kvbase = reinterpret_cast<const unsigned char*>(a.k) + int64_t(seq) * a.seq_stride;
+  const float sl2 = a.scale * kLog2e;
+
+  // the rows of the tile starting at list position pb -> staging area
+  auto request = [&](int pb) {
+    const int cnt = (P1 - pb) < kTT ? (P1 - pb) : kTT;
+    const int tokl = lv.tok(pb + ((lane & 31) < cnt ? (lane & 31) : 0));
+    for (int s = wave; s * 64 < kF8TileC; s += 4) {
+      const int c = 64 * s + lane;
+      const int row = c / kF8RowC, col = c % kF8RowC;
+      const int rt = __shfl(tokl, row < kTT ? row : 0);
+      if (c < kF8TileC)
+        __builtin_amdgcn_global_load_lds(kvbase + int64_t(rt) * a.tok_stride + 16 * col,
+                                         (__attribute__((address_space(3))) void*)(sh.stage + 1024 * s), 16, 0, 0);
+    }
+  };
+
+  bf16x8 qa[kDK / 32];
+  {
+    const uint16_t* qrow = a.q + (int64_t(i) * kH + 16 * wave + r) * kDK + 8 * kq;
+#pragma unroll
+    for (int ks = 0; ks < kDK / 32; ks++) qa[ks] = as_bf16x8(ld16(qrow + 32 * ks));
+  }
+  float m[4], l[4];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    m[e] = -INFINITY;
+    l[e] = 0.f;
+  }
+  f32x4 o[kDV / 16];
+#pragma unroll
+  for (int nt = 0; nt < kDV / 16; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* phi = sh.p[wave][0];
+  uint16_t* plo = sh.p[wave][1];
+
+  if (P0 < P1) request(P0);
+  for (int pb = P0; pb < P1; pb += kTT) {
+    const int cnt = (P1 - pb) < kTT ? (P1 - pb) : kTT;
+    wait_memory();
+    __syncthreads();  // the staged rows have landed; every wave is done with the previous bf16 tile
+    // codes -> bf16 tile (row t, chunks 2cc, 2cc+1 hold columns 16cc .. 16cc+15)
+#pragma unroll
+    for (int k = 0; k < 4; k++) {
+      const int u = tid + 256 * k;
+      const int row = u >> 5, cc = u & 31;
+      const u32x4 w = *reinterpret_cast<const u32x4*>(sh.stage + row * kF8Row + 16 * cc);
+      u32x4 lo, hi;
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const bf16x8 b = e4m3x8_bf16(u32x2{w[2 * j], w[2 * j + 1]});
+        if (j == 0) lo = __builtin_bit_cast(u32x4, b);
+        else hi = __builtin_bit_cast(u32x4, b);
+      }
+      unsigned char* dst = sh.kv + (row * kRowL + 2 * cc) * 16;
+      *reinterpret_cast<u32x4*>(dst) = lo;
+      *reinterpret_cast<u32x4*>(dst + 16) = hi;
+    }
+    {  // rotary values: row tid / 8, chunk tid % 8 -> bf16 tile chunk 64 + tid % 8
+      const int row = tid >> 3, rc = tid & 7;
+      *reinterpret_cast<u32x4*>(sh.kv + (row * kRowL + 64 + rc) * 16) =
+          *reinterpret_cast<const u32x4*>(sh.stage + row * kF8Row + 528 + 16 * rc);
+    }
+    if (tid < kTT * 4)
+      sh.sc[tid >> 2][tid & 3] = *reinterpret_cast<const float*>(sh.stage + (tid >> 2) * kF8Row + 512 + 4 * (tid & 3));
+    __syncthreads();  // bf16 tile and scales ready; the staging area is free
+    if (pb + kTT < P1) request(pb + kTT);
+
+    // S = Q K^T: lane (kq, r) holds S[head 4kq+e][token 16h + r]
+    f32x4 acc[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; hf++) {
+      acc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const unsigned char* krow = sh.kv + ((16 * hf + r) * kRowL + kq) * 16;
+#pragma unroll
+      for (int ks = kDV / 32; ks < kDK / 32; ks++) {  // rotary columns, unscaled
+        const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 64 * ks));
+        acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc[hf], 0, 0, 0);
+      }
+#pragma unroll
+      for (int g = 0; g < 4; g++) {
+        f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 4 * g; ks < 4 * g + 4; ks++) {
+          const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 64 * ks));
+          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, part, 0, 0, 0);
+        }
+        const float scg = sh.sc[16 * hf + r][g];
+#pragma unroll
+        for (int e = 0; e < 4; e++) acc[hf][e] = fmaf(part[e], scg, acc[hf][e]);
+      }
+    }
+    float alpha[4], p0[4], p1[4];
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const float s0 = r < cnt ? acc[0][e] * sl2 : -INFINITY;
+      const float s1 = 16 + r < cnt ? acc[1][e] * sl2 : -INFINITY;
+      const float tm = row16_max(fmaxf(s0, s1));
+      const float mn = fmaxf(m[e], tm);
+      p0[e] = 0.f;
+      p1[e] = 0.f;
+      alpha[e] = 1.f;
+      if (mn != -INFINITY) {
+        p0[e] = exp2f(s0 - mn);
+        p1[e] = exp2f(s1 - mn);
+        alpha[e] = exp2f(m[e] - mn);
+      }
+      const float ps = row16_sum(p0[e] + p1[e]);
+      l[e] = l[e] * alpha[e] + ps;
+      m[e] = mn;
+    }
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[nt][e] *= alpha[e];
+    // O += P' V, one 128-column group at a time
+    const unsigned char* vb0 = sh.kv + (8 * kq + (r >> 2)) * kRowL * 16 + 8 * (r & 3);
+#pragma unroll
+    for (int g = 0; g < 4; g++) {
+      const float sa = sh.sc[r][g], sb = sh.sc[16 + r][g];
+#pragma unroll
+      for (int e = 0; e < 4; e++) {
+        const int row = 4 * kq + e;
+        const float x0 = p0[e] * sa, x1 = p1[e] * sb;
+        const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
+        phi[row * kPStr + r] = h0;
+        phi[row * kPStr + 16 + r] = h1;
+        plo[row * kPStr + r] = f32_to_bf16(x0 - bf16_to_f32(h0));
+        plo[row * kPStr + 16 + r] = f32_to_bf16(x1 - bf16_to_f32(h1));
+      }
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      const bf16x8 ah = as_bf16x8(*reinterpret_cast<const u32x4*>(phi + r * kPStr + 8 * kq));
+      const bf16x8 al = as_bf16x8(*reinterpret_cast<const u32x4*>(plo + r * kPStr + 8 * kq));
+#pragma unroll
+      for (int nt = 8 * g; nt < 8 * g + 8; nt++) {
+        s16x4 t[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; hh++)
+          t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (__attribute__((address_space(3))) s16x4*)(vb0 + 4 * hh * kRowL * 16 + 32 * nt));
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t[0], t[1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bv, o[nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();  // this group's P' is read before the next one overwrites it
+    }
+  }
+
   const int64_t orow0 = (int64_t(split) * a.nq + i) * kH + 16 * wave;
 #pragma unroll
   for (int e = 0; e < 4; e++) {

@@ -14,6 +14,10 @@ hipError_t launch_pool(const uint16_t* raw, int64_t raw_ss, uint16_t* pooled, in
 // of n_seq sequences; out_ss in bytes.
 hipError_t launch_quantize(const uint16_t* keys, int64_t keys_ss, uint8_t* out, int64_t out_ss, int n_seq,
                            int64_t k0, int64_t nk, int dim, hipStream_t s);
+// FP8 sparse-MLA rows (656 bytes) of tokens [t0, t0 + nt) of n_seq sequences
+// from 576-wide bf16 latent rows; ss, ts in elements, oss, ots in bytes.
+hipError_t launch_quantize_latent(const uint16_t* lat, int64_t ss, int64_t ts, uint8_t* out, int64_t oss, int64_t ots,
+                                  int n_seq, int64_t t0, int64_t nt, hipStream_t s);
 
 // Decode-step append (one new token per query).
 struct AppendArgs {
@@ -26,7 +30,8 @@ struct AppendArgs {
   const uint16_t* raw_new;  // [nq][dim] or nullptr
   uint16_t* k;
   uint16_t* v;
-  int64_t seq_stride, tok_stride, head_stride;
+  int64_t seq_stride, tok_stride, head_stride;  // elements; bytes for FP8 rows
+  int kv_fp8;               // the cache holds FP8 sparse-MLA rows (k_new is then quantized)
   int k_row, v_row;         // elements per token row: hkv * head_dim, hkv * v_dim
   int head_dim, v_dim;
   uint16_t* raw;            // raw indexer keys, or nullptr
@@ -92,7 +97,8 @@ struct AttendArgs {
   const uint16_t* q;
   const uint16_t* k;
   const uint16_t* v;
-  int64_t seq_stride, tok_stride, head_stride;
+  int64_t seq_stride, tok_stride, head_stride;  // elements; bytes for FP8 rows
+  int kv_fp8;                                    // FP8 sparse-MLA rows (656 bytes) instead of bf16
   const int* sel;
   const int* n_sel;
   int topk;

@@ -88,6 +88,27 @@ __global__ __launch_bounds__(256) void quantize_kernel(const uint16_t* __restric
   quantize_key_wave(x0, x1, dim, base + fp8_code_off(b, dim), reinterpret_cast<float*>(base + fp8_scale_off(b, dim)));
 }
 
+// One FP8 sparse-MLA row ("GLM-5.3 最適化 第2部", footnote 1: 656 bytes)
+// from a 576-wide bf16 latent row, by a 256-thread work-group: wave g
+// quantizes columns 128g .. 128g+127 with one scale (codes at bytes 128g..,
+// scale at byte 512 + 4g); wave 0 also copies the 64 rotary values (bytes
+// 528 .. 655) unchanged.
+__device__ __forceinline__ void quantize_latent_row(const uint16_t* src, uint8_t* dst) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float x0 = bf16_to_f32(src[128 * wave + lane]);
+  const float x1 = bf16_to_f32(src[128 * wave + 64 + lane]);
+  quantize_key_wave(x0, x1, 128, dst + 128 * wave, reinterpret_cast<float*>(dst + 512 + 4 * wave));
+  if (wave == 0 && lane < 8) st16(dst + 528 + 16 * lane, ld16(src + 512 + 8 * lane));
+}
+
+__global__ __launch_bounds__(256) void quantize_latent_kernel(const uint16_t* __restrict__ lat, int64_t ss, int64_t ts,
+                                                              uint8_t* __restrict__ out, int64_t oss, int64_t ots,
+                                                              int64_t t0) {
+  const int64_t t = t0 + blockIdx.x;
+  const int s = blockIdx.y;
+  quantize_latent_row(lat + s * ss + t * ts, out + s * oss + t * ots);
+}
+
 // One work-group per appended token (query i): copies the token's K and V
 // rows (every kv head) and its raw indexer key into the cache at position
 // q_pos[i] of sequence q_seq[i]; when the token completes a block, also
@@ -100,10 +121,15 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   const int seq = a.q_seq ? a.q_seq[i] : i;
   const int pos = a.q_pos[i];
   if (pos < 0 || pos >= a.capacity) return;  // a caller error: nothing is written
-  const int kc = a.k_row / 8, vc = a.v_row / 8, rc = a.dim / 8;
+  int kc = a.k_row / 8;
+  const int vc = a.v_row / 8, rc = a.dim / 8;
   const uint16_t* kn = a.k_new + int64_t(i) * a.k_row;
   const uint16_t* vn = a.v_new ? a.v_new + int64_t(i) * a.v_row : nullptr;
   const uint16_t* rn = a.raw_new ? a.raw_new + int64_t(i) * a.dim : nullptr;
+  if (a.kv_fp8) {  // one FP8 sparse-MLA row (strides in bytes)
+    quantize_latent_row(kn, reinterpret_cast<uint8_t*>(a.k) + int64_t(seq) * a.seq_stride + int64_t(pos) * a.tok_stride);
+    kc = 0;  // written
+  }
   // rows of one token: kv head g at k + tok * tok_stride + g * head_stride
   for (int c = tid; c < kc; c += 256) {
     const int g = (8 * c) / a.head_dim, d = (8 * c) % a.head_dim;
@@ -179,6 +205,14 @@ hipError_t launch_quantize(const uint16_t* keys, int64_t keys_ss, uint8_t* out, 
   if (nk <= 0 || n_seq <= 0) return hipSuccess;
   hipLaunchKernelGGL(quantize_kernel, dim3(unsigned((nk + 3) / 4), unsigned(n_seq)), dim3(256), 0, s, keys, keys_ss,
                      out, out_ss, k0, nk, dim);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_latent(const uint16_t* lat, int64_t ss, int64_t ts, uint8_t* out, int64_t oss, int64_t ots,
+                                  int n_seq, int64_t t0, int64_t nt, hipStream_t s) {
+  if (nt <= 0 || n_seq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(quantize_latent_kernel, dim3(unsigned(nt), unsigned(n_seq)), dim3(256), 0, s, lat, ss, ts, out,
+                     oss, ots, t0);
   return hipGetLastError();
 }
 

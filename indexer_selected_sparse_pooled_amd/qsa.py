@@ -41,10 +41,14 @@ class AttnCfg(ctypes.Structure):
                 ("dv", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
+KV_BF16, KV_FP8_MLA = 0, 1  # qsa_kv_format
+FP8_MLA_ROW = 656          # bytes of an FP8 sparse-MLA row
+
+
 class KV(ctypes.Structure):
     _fields_ = [("k", ctypes.c_void_p), ("v", ctypes.c_void_p), ("seq_stride", ctypes.c_int64),
                 ("tok_stride", ctypes.c_int64), ("head_stride", ctypes.c_int64),
-                ("capacity", ctypes.c_int64)]
+                ("capacity", ctypes.c_int64), ("format", ctypes.c_int32)]
 
 
 # The two parameter sets of the pages (variant A: pooled 4-token blocks,
@@ -63,6 +67,7 @@ _SIGS = {
     "qsa_pool_keys": [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _i32, _vp],
     "qsa_quantize_keys": [_vp, _i64, _vp, _i64, _i32, _i64, _i64, _i32, _vp],
     "qsa_fp8_keys_bytes": [_i64, _i32],
+    "qsa_quantize_latent": [_vp, _i64, _i64, _vp, _i64, _i64, _i32, _i64, _i64, _vp],
     "qsa_kv_append": [_vp, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_index_scores": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _i64, _vp],
     "qsa_topk_blocks": [_vp, _i32, _vp, _i32, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
@@ -152,6 +157,22 @@ def qsa_pool_keys(raw, pooled, tok_begin=0, tok_end=None, block=4, stream=None):
     _check("qsa_pool_keys", lib().qsa_pool_keys(
         _dev(raw, _BF16, "raw"), raw.stride(0), _dev(pooled, _BF16, "pooled"), pooled.stride(0),
         n_seq, tok_begin, tok_end, dim, block, _stream(stream)))
+
+
+def qsa_quantize_latent(latent, out, tok_begin=0, tok_end=None, stream=None):
+    """latent: [n_seq, capacity, 1, 576] (or [n_seq, capacity, 576]) bf16;
+    out: uint8 [n_seq, capacity, 656] FP8 sparse-MLA rows."""
+    n_seq, cap = latent.shape[:2]
+    if latent.shape[-1] != 576 or latent.stride(-1) != 1:
+        raise ValueError("qsa_quantize_latent: latent rows must be 576 contiguous bf16 values")
+    if out.dtype != torch.uint8 or out.dim() != 3 or out.shape[2] != FP8_MLA_ROW or out.shape[:2] != (n_seq, cap) \
+            or out.stride(2) != 1:
+        raise ValueError("qsa_quantize_latent: out must be uint8 [n_seq, capacity, 656]")
+    if tok_end is None:
+        tok_end = cap
+    _check("qsa_quantize_latent", lib().qsa_quantize_latent(
+        _dev(latent, _BF16, "latent"), latent.stride(0), latent.stride(1), _dev(out, _U8, "out"), out.stride(0),
+        out.stride(1), n_seq, tok_begin, tok_end, _stream(stream)))
 
 
 def qsa_fp8_keys_bytes(n_keys, dim) -> int:
@@ -348,8 +369,8 @@ def _kv_address(t, name):
     (torch.empty(..., pin_memory=True)) through the address HIP maps it to,
     so kernels read it over the host link. Anything else is refused."""
     global _hip
-    if t.dtype not in _BF16:
-        raise TypeError(f"{name} has dtype {t.dtype}, expected bf16")
+    if t.dtype not in _BF16 + _U8:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected bf16 (or uint8 FP8 rows)")
     if t.is_cuda:
         return t.data_ptr()
     if not t.is_pinned():
@@ -366,7 +387,15 @@ def _kv_address(t, name):
 
 def make_kv(k, v=None):
     """KV descriptor of k, v: [n_seq, capacity, hkv, d] bf16 (v defaults to k),
-    in device memory or in pinned host memory (read zero-copy)."""
+    in device memory or in pinned host memory (read zero-copy); or of FP8
+    sparse-MLA rows: k a uint8 [n_seq, capacity, 656] tensor (v None)."""
+    if k.dtype == torch.uint8:
+        if v is not None or k.dim() != 3 or k.shape[2] != FP8_MLA_ROW or k.stride(2) != 1:
+            raise ValueError("FP8 rows: k must be a uint8 [n_seq, capacity, 656] tensor, v None")
+        addr = ctypes.c_void_p(_kv_address(k, "k"))
+        kv = KV(addr, addr, k.stride(0), k.stride(1), 0, k.shape[1], KV_FP8_MLA)
+        kv._keep = (k,)
+        return kv
     if v is None:
         v = k
     for t, name in ((k, "k"), (v, "v")):
@@ -375,7 +404,7 @@ def make_kv(k, v=None):
     if k.stride()[:3] != v.stride()[:3] or k.shape[:2] != v.shape[:2]:
         raise ValueError("k and v must share their sequence, token and head strides")
     kv = KV(ctypes.c_void_p(_kv_address(k, "k")), ctypes.c_void_p(_kv_address(v, "v")), k.stride(0), k.stride(1),
-            k.stride(2), k.shape[1])
+            k.stride(2), k.shape[1], KV_BF16)
     kv._keep = (k, v)
     return kv
 
