@@ -363,7 +363,24 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
                          breakdown_us={"scores": round(t_sc * 1e3, 2), "topk": round(t_tk * 1e3, 2),
                                        "attend": round(t_at * 1e3, 2)})
     log(f"mla decode: {ms:.4f} ms/step")
-    del lat, keys, q, q_idx, kv, bufs
+    # the same step over FP8 sparse-MLA rows (656 bytes per token)
+    rows8 = torch.empty(B, L, 656, dtype=torch.uint8, device=dev)
+    pkg.qsa_quantize_latent(lat, rows8)
+    kv8 = pkg.make_kv(rows8)
+
+    def dstep8():
+        pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv8, bufs, q_seq=q_seq, w_idx=w)
+
+    ms8, _, g = time_graph(torch, dstep8, max(10, steps // 2), warmup)
+    del g
+    t_at8 = time_launches(torch, lambda: pkg.qsa_sparse_decode(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv8, bufs.sel,
+                                                               bufs.n_sel, bufs.n_split, bufs.o_part, bufs.lse_part,
+                                                               q_seq=q_seq), reps)
+    step_bytes8 = B * bm.mla_decode_unit_bytes_fp8_rows(L)
+    out["decode"]["fp8_rows"] = dict(ms_per_step=round(ms8, 5), steps_s=round(1e3 / ms8, 1), step_bytes=step_bytes8,
+                                     hbm_gbs=round(step_bytes8 / (ms8 * 1e-3) / 1e9, 1),
+                                     attend_us=round(t_at8 * 1e3, 2))
+    del lat, keys, q, q_idx, kv, bufs, rows8, kv8
     torch.cuda.empty_cache()
     # prefill chunk: queries at positions L - C .. L - 1 of one sequence
     lat = torch.empty(1, L, 1, 576, **bf16)
@@ -401,6 +418,25 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
             pre["breakdown_us"] = {"scores": round(t_sc * 1e3, 1), "topk": round(t_tk * 1e3, 1),
                                    "attend": round(t_at * 1e3, 1)}
             pre["attend_tflops"] = round(att_tflops, 1)
+        if tile == MLA["tiles"][0]:  # the same chunk over FP8 sparse-MLA rows
+            rows8 = torch.empty(1, L, 656, dtype=torch.uint8, device=dev)
+            pkg.qsa_quantize_latent(lat, rows8)
+            kv8 = pkg.make_kv(rows8)
+
+            def chunk8():
+                pipeline.prefill_chunk(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv8, pb, w_idx=w)
+
+            ms8, _, g = time_graph(torch, chunk8, max(3, steps // 10), max(1, warmup // 2))
+            del g
+            a0, a1 = pb.tiles[0]
+            t_at8 = time_launches(torch, lambda: pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv8, pb.sel,
+                                                                        pb.n_sel, a0, a1, pb.o_tiles[0],
+                                                                        pb.lse_tiles[0]), r)
+            pre["fp8_rows"] = dict(ms_per_chunk=round(ms8, 4), tok_s=round(C / (ms8 * 1e-3), 1),
+                                   tflops=round(flops["total"] / (ms8 * 1e-3) / 1e12, 2),
+                                   attend_us=round(t_at8 * 1e3, 1),
+                                   attend_tflops=round(flops["attention"] / (t_at8 * 1e-3) / 1e12, 1))
+            del rows8, kv8
         del pb
         torch.cuda.empty_cache()
         log(f"mla prefill tile {tile}: {ms_p:.3f} ms/chunk")
@@ -411,7 +447,7 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
                           useful_gflop=round(flops["total"] / 1e9, 1), history_tile=t0,
                           attend_tflops=pre["attend_tflops"],
                           attend_mfma_frac=round(pre["attend_tflops"] / BF16_PEAK_TFLOPS, 4),
-                          breakdown_us=pre["breakdown_us"],
+                          breakdown_us=pre["breakdown_us"], fp8_rows=pre["fp8_rows"],
                           **{f"tile_{t}": {"tok_s": round(pre[t]["tok_s"], 1), "ms_per_chunk": round(pre[t]["ms"], 4)}
                              for t in MLA["tiles"][1:]})
     return out

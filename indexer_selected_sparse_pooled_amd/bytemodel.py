@@ -83,6 +83,17 @@ def mla_decode_unit_bytes(ctx: int, topk: int = 2048, idx_dim: int = 64, idx_hea
             + hq * dk * BF16 + hq * dv * BF16)
 
 
+FP8_MLA_ROW = 656  # "GLM-5.3 ...", footnote 1: 512 FP8 values + 4 scales + 64 bf16 rotary values
+
+
+def mla_decode_unit_bytes_fp8_rows(ctx: int, topk: int = 2048, idx_dim: int = 64, idx_heads: int = 4,
+                                   hq: int = 64, dk: int = 576, dv: int = 512) -> int:
+    """mla_decode_unit_bytes with the selected latent rows in the 656-byte
+    FP8 format (indexer keys bf16)."""
+    s = attended_tokens(ctx, 1, topk)
+    return mla_decode_unit_bytes(ctx, topk, idx_dim, idx_heads, hq, dk, dv) - s * dk * BF16 + s * FP8_MLA_ROW
+
+
 def mla_prefill_flops(ctxs, topk: int = 2048, idx_dim: int = 64, idx_heads: int = 4, hq: int = 64,
                       dk: int = 576, dv: int = 512) -> dict:
     """Useful FLOPs of a prefill chunk of the shared-latent variant."""

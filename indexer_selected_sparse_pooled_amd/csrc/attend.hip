@@ -22,7 +22,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   mla::attend_part<false>(a, split, i, sh);
 }
 
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_b_fp8(AttendArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_b_fp8(AttendArgs a) {
   __shared__ mla::LdsF8 sh;
   const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
   mla::attend_part_fp8<false>(a, split, i, sh);

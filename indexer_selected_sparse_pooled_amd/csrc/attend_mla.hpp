@@ -201,8 +201,10 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
 //     tile above, copy the rotary values and keep the 4 scales per token;
 //     the staging area is then free and the next tile's rows are requested
 //     at once, so their gather overlaps this tile's MFMA work;
-//   * S: each 128-column group's MFMA partial is scaled by the token's
-//     group scale (the rotary columns are not scaled);
+//   * S: one MFMA chain over the 18 k-steps; the accumulator is kept in
+//     units of the current group's scale (rescaled by s_prev / s_g on
+//     entering group g, back to real units before the rotary columns), so
+//     no second accumulator is live;
 //   * O += P' V per group, with P' = P * (the token's group scale) split
 //     into bf16 hi + lo parts, so the codes serve as V unscaled.
 constexpr int kF8Row = 656;                 // bytes per FP8 row
@@ -213,6 +215,7 @@ struct LdsF8 {
   __attribute__((aligned(16))) unsigned char kv[kTileC * 16];      // bf16 tile (as Lds::kv)
   __attribute__((aligned(16))) unsigned char stage[kF8TileC * 16];  // FP8 rows of the tile in flight
   __attribute__((aligned(16))) uint16_t p[4][2][16 * kPStr];
+  __attribute__((aligned(16))) float pf[4][64][8];  // per wave and lane: the tile's P before scaling
   float sc[kTT][4];
   int64_t range[2];
 };
@@ -285,7 +288,7 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
     wait_memory();
     __syncthreads();  // the staged rows have landed; every wave is done with the previous bf16 tile
     // codes -> bf16 tile (row t, chunks 2cc, 2cc+1 hold columns 16cc .. 16cc+15)
-#pragma unroll
+#pragma unroll 1
     for (int k = 0; k < 4; k++) {
       const int u = tid + 256 * k;
       const int row = u >> 5, cc = u & 31;
@@ -318,41 +321,45 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
       acc[hf] = f32x4{0.f, 0.f, 0.f, 0.f};
       const unsigned char* krow = sh.kv + ((16 * hf + r) * kRowL + kq) * 16;
 #pragma unroll
-      for (int ks = kDV / 32; ks < kDK / 32; ks++) {  // rotary columns, unscaled
+      for (int ks = 0; ks < kDK / 32; ks++) {
         const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 64 * ks));
+        // entering group g = ks / 4: rescale to its units (a zero scale, an
+        // all-zero group, keeps the units: its codes add nothing)
+        if (ks % 4 == 0 && ks < kDV / 32) {
+          const float sg = sh.sc[16 * hf + r][ks / 4];
+          const float inv = sg > 0.f ? 1.f / sg : 1.f;
+          const float prev = ks == 0 ? 1.f : sh.sc[16 * hf + r][ks / 4 - 1];
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[hf][e] = acc[hf][e] * (prev > 0.f ? prev : 1.f) * inv;
+        }
+        if (ks == kDV / 32) {
+          const float prev = sh.sc[16 * hf + r][3];
+#pragma unroll
+          for (int e = 0; e < 4; e++) acc[hf][e] *= prev > 0.f ? prev : 1.f;
+        }
         acc[hf] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, acc[hf], 0, 0, 0);
       }
-#pragma unroll
-      for (int g = 0; g < 4; g++) {
-        f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ks = 4 * g; ks < 4 * g + 4; ks++) {
-          const bf16x8 kb = as_bf16x8(*reinterpret_cast<const u32x4*>(krow + 64 * ks));
-          part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], kb, part, 0, 0, 0);
-        }
-        const float scg = sh.sc[16 * hf + r][g];
-#pragma unroll
-        for (int e = 0; e < 4; e++) acc[hf][e] = fmaf(part[e], scg, acc[hf][e]);
-      }
     }
-    float alpha[4], p0[4], p1[4];
+    float alpha[4];
+    float* pl = sh.pf[wave][lane];
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       const float s0 = r < cnt ? acc[0][e] * sl2 : -INFINITY;
       const float s1 = 16 + r < cnt ? acc[1][e] * sl2 : -INFINITY;
       const float tm = row16_max(fmaxf(s0, s1));
       const float mn = fmaxf(m[e], tm);
-      p0[e] = 0.f;
-      p1[e] = 0.f;
+      float p0 = 0.f, p1 = 0.f;
       alpha[e] = 1.f;
       if (mn != -INFINITY) {
-        p0[e] = exp2f(s0 - mn);
-        p1[e] = exp2f(s1 - mn);
+        p0 = exp2f(s0 - mn);
+        p1 = exp2f(s1 - mn);
         alpha[e] = exp2f(m[e] - mn);
       }
-      const float ps = row16_sum(p0[e] + p1[e]);
+      const float ps = row16_sum(p0 + p1);
       l[e] = l[e] * alpha[e] + ps;
       m[e] = mn;
+      pl[2 * e] = p0;  // kept in LDS (the lane's own slot) for the four groups below
+      pl[2 * e + 1] = p1;
     }
 #pragma unroll
     for (int nt = 0; nt < kDV / 16; nt++)
@@ -366,7 +373,7 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
 #pragma unroll
       for (int e = 0; e < 4; e++) {
         const int row = 4 * kq + e;
-        const float x0 = p0[e] * sa, x1 = p1[e] * sb;
+        const float x0 = pl[2 * e] * sa, x1 = pl[2 * e + 1] * sb;
         const uint16_t h0 = f32_to_bf16(x0), h1 = f32_to_bf16(x1);
         phi[row * kPStr + r] = h0;
         phi[row * kPStr + 16 + r] = h1;
