@@ -317,7 +317,48 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
             out["attend_tflops"] = round(flops["attention"] / (t_at * 1e-3) / 1e12, 1)
         del g, bufs
         log(f"prefill tile {tile}: {ms:.3f} ms/chunk")
+    # the same chunk with correlated indexer queries: AR(1) over positions,
+    # neighbouring top-512 selections overlapping about 0.72 as the pages
+    # measured (the correlation comes from tests/golden/correlated_overlap.txt)
+    import numpy as np
+    rho = correlated_rho()
+    qc_np = qi.ar1_normal_bf16(seed, qi.stream_id(0, 0, "q_idx", salt=1), C, 128, rho)
+    q_idx_c = torch.from_numpy(qc_np.view(np.int16)).view(torch.bfloat16).reshape(C, 1, 128).to(dev)
+    tile = PREFILL["tiles"][0]
+    bufs = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, C, ctx_max, tile)
+
+    def chunk_c():
+        pipeline.prefill_chunk(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q_idx_c, pooled, q, kv, bufs)
+
+    ms_c, _, g = time_graph(torch, chunk_c, max(3, steps // 5), max(1, warmup))
+    del g
+
+    def tiles_c():
+        for t, (a0, a1) in enumerate(bufs.tiles):
+            pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, bufs.sel, bufs.n_sel, a0, a1,
+                                   bufs.o_tiles[t], bufs.lse_tiles[t])
+
+    t_at_c = time_launches(torch, tiles_c, max(3, steps // 10))
+    sel = bufs.sel.cpu().numpy()
+    ov = [np.intersect1d(sel[i], sel[i - 1]).size / 512 for i in range(1, C)]
+    out["correlated"] = dict(workload=f"the same chunk with AR(1) indexer queries over positions (rho {rho})",
+                             ms_per_chunk=round(ms_c, 4), tok_s=round(C / (ms_c * 1e-3), 1),
+                             tflops=round(flops["total"] / (ms_c * 1e-3) / 1e12, 2),
+                             attend_all_tiles_us=round(t_at_c * 1e3, 1),
+                             attend_tflops=round(flops["attention"] / (t_at_c * 1e-3) / 1e12, 1),
+                             mean_selection_overlap=round(float(np.mean(ov)), 4))
+    log(f"prefill correlated: {ms_c:.3f} ms/chunk, overlap {np.mean(ov):.3f}")
+    del bufs
     return out, flops
+
+
+def correlated_rho() -> float:
+    """The AR(1) correlation of the correlated-selection workload."""
+    path = os.path.join(ROOT, "tests", "golden", "correlated_overlap.txt")
+    for line in open(path):
+        if line.startswith("rho "):
+            return float(line.split()[1])
+    raise RuntimeError(f"no rho in {path}")
 
 
 def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
@@ -612,7 +653,8 @@ def main():
                     "tflops": round(t8["tflops"], 2), "mfma_frac": round(t8["tflops"] / BF16_PEAK_TFLOPS, 5),
                     "useful_gflop": round(pflops["total"] / 1e9, 2),
                     "breakdown_us": pre["breakdown_us"], "attend_tflops": pre["attend_tflops"],
-                    "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)}},
+                    "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)},
+                    "correlated": pre["correlated"]},
         "mla": mla,
         "roofline": {"kernel": "index_lists_a (pooled-key scan + per-chunk candidate lists, first launch of "
                                "qsa_decode_layer)", "bound": "hbm",

@@ -22,6 +22,6 @@ regenerate exactly the rows it needs of a tensor the GPU filled whole.
 """
 from .gen import (  # noqa: F401
     G, H, mix64, stream_key, words, codes, normal_table, normal_bf16,
-    uniform_f32, tie_heavy_f32, stream_id, config_seed, KIND,
+    uniform_f32, tie_heavy_f32, ar1_normal_bf16, stream_id, config_seed, KIND,
     bf16_bits_to_f32,
 )

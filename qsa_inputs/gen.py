@@ -131,6 +131,22 @@ def normal_bf16(seed: int, stream: int, start: int, count: int = None, index=Non
     return normal_table()[codes(seed, stream, index)]
 
 
+def ar1_normal_bf16(seed: int, stream: int, n_rows: int, dim: int, rho: float) -> np.ndarray:
+    """bf16 bit patterns [n_rows][dim] of a first-order autoregressive
+    sequence of standard-normal vectors: x_0 = z_0 and
+    x_r = rho * x_{r-1} + sqrt(1 - rho**2) * z_r, computed in float64 from
+    z = normal_bf16 elements of (seed, stream) (row-major), then rounded to
+    fp32 and to bf16 (nearest, ties to even). Neighbouring rows have
+    correlation rho; each row is N(0, 1) per element."""
+    z = bf16_bits_to_f32(normal_bf16(seed, stream, 0, n_rows * dim)).astype(np.float64).reshape(n_rows, dim)
+    x = np.empty_like(z)
+    c = float(np.sqrt(1.0 - rho * rho))
+    x[0] = z[0]
+    for r in range(1, n_rows):
+        x[r] = rho * x[r - 1] + c * z[r]
+    return _f32_to_bf16_bits(x.astype(np.float32))
+
+
 def uniform_f32(seed: int, stream: int, count: int, lo: float = -1.0, hi: float = 1.0) -> np.ndarray:
     """fp32 values on a 2**-24 grid of [lo, hi) (exactly representable)."""
     u = words(seed, stream, np.arange(count, dtype=np.uint64))
