@@ -660,7 +660,7 @@ def main():
                                "qsa_decode_layer)", "bound": "hbm",
                      "achieved": round(dec["lists_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["lists_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": counter_traffic("index_lists_a<2>", "2048"),
+                     "traffic": counter_traffic("index_lists_a<2, false>", "2048"),
                      "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["lists_ms"] * 1e3, 3)},
         "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
         "wall_s": round(time.time() - t_all, 1),

@@ -175,8 +175,13 @@ def decode_layer(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
         pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq)
     for _ in range(reps):
         pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, fused=True)
+    # the same layer over FP8 pooled keys (132 B per block)
+    keys8 = pkg.fp8_keys_empty(B, L // 4, 128)
+    pkg.qsa_quantize_keys(keys, keys8)
+    for _ in range(reps):
+        pipeline.decode_layer(pkg.SEL_A_FP8, pkg.ATTN_A, q_ctx, L, q_idx, keys8, q, kv, bufs, q_seq=q_seq, fused=True)
     torch.cuda.synchronize()
-    del keys, k, v, kv, bufs
+    del keys, keys8, k, v, kv, bufs
     torch.cuda.empty_cache()
 
 
@@ -228,6 +233,13 @@ def mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
     pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, pb.scores, pb.sel, pb.n_sel, pb.ws)
     for _ in range(reps):
         pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv, pb.sel, pb.n_sel, 0, L, pb.o_tiles[0],
+                               pb.lse_tiles[0])
+    # the same attention over FP8 sparse-MLA rows (656 B per token)
+    rows = torch.empty(1, L, 656, dtype=torch.uint8, device=dev)
+    pkg.qsa_quantize_latent(lat, rows)
+    kv8 = pkg.make_kv(rows)
+    for _ in range(reps):
+        pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv8, pb.sel, pb.n_sel, 0, L, pb.o_tiles[0],
                                pb.lse_tiles[0])
     torch.cuda.synchronize()
 
