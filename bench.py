@@ -508,10 +508,10 @@ def counter_traffic(kernel: str, groups: str):
     digest = [l.split(":", 1)[1].strip() for l in lines if l.startswith("source digest:")]
     if not digest or digest[0] != source_digest():
         return None
-    for l in lines:
-        f = l.split()
-        if len(f) == 7 and f[0] == kernel and f[1] == groups:
-            return int(f[5]) + int(f[6])
+    for l in lines:  # the kernel name fills the first 40 columns (it may contain spaces)
+        f = l[40:].split()
+        if len(f) == 6 and l[:40].strip() == kernel and f[0] == groups:
+            return int(f[4]) + int(f[5])
     return None
 
 
