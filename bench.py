@@ -421,7 +421,24 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
     out["decode"]["fp8_rows"] = dict(ms_per_step=round(ms8, 5), steps_s=round(1e3 / ms8, 1), step_bytes=step_bytes8,
                                      hbm_gbs=round(step_bytes8 / (ms8 * 1e-3) / 1e9, 1),
                                      attend_us=round(t_at8 * 1e3, 2))
-    del lat, keys, q, q_idx, kv, bufs, rows8, kv8
+    # and with FP8 token keys too (68 + 656 bytes of cache per token)
+    keys8 = pkg.fp8_keys_empty(B, L, 64)
+    pkg.qsa_quantize_keys(keys, keys8)
+    bufs8 = pipeline.decode_buffers(pkg.SEL_B_FP8, pkg.ATTN_B, B, L)
+
+    def dstep88():
+        pipeline.decode_layer(pkg.SEL_B_FP8, pkg.ATTN_B, q_ctx, L, q_idx, keys8, q, kv8, bufs8, q_seq=q_seq, w_idx=w)
+
+    ms88, _, g = time_graph(torch, dstep88, max(10, steps // 2), warmup)
+    del g
+    t_sc8 = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_B_FP8, q_ctx, L, q_idx, keys8, bufs8.scores,
+                                                              q_seq=q_seq, w_idx=w), reps)
+    step_bytes88 = B * bm.mla_decode_unit_bytes_fp8(L)
+    out["decode"]["fp8_keys_and_rows"] = dict(ms_per_step=round(ms88, 5), steps_s=round(1e3 / ms88, 1),
+                                              step_bytes=step_bytes88,
+                                              hbm_gbs=round(step_bytes88 / (ms88 * 1e-3) / 1e9, 1),
+                                              scores_us=round(t_sc8 * 1e3, 2))
+    del lat, keys, q, q_idx, kv, bufs, rows8, kv8, keys8, bufs8
     torch.cuda.empty_cache()
     # prefill chunk: queries at positions L - C .. L - 1 of one sequence
     lat = torch.empty(1, L, 1, 576, **bf16)

@@ -73,16 +73,15 @@ typedef enum {
  *     at (b/64) * 64*(idx_dim+4) + 64*idx_dim + 4*(b%64) of its sequence;
  *     sequence strides are in bytes (multiples of 16).
  *     qsa_fp8_keys_bytes gives the bytes n keys need; qsa_quantize_keys and
- *     qsa_kv_append write this layout. Supported for the single-head 128-d
- *     indexer (variant A). */
+ *     qsa_kv_append write this layout. Supported for both indexers (132
+ *     bytes per pooled 128-d key, 68 bytes per 64-d token key). */
 typedef enum { QSA_KEYS_BF16 = 0, QSA_KEYS_FP8 = 1 } qsa_key_format;
 
 /* Indexer / selection parameters.
  *   variant A (pooled block keys):   block 4, topk 512,  idx_dim 128, idx_heads 1
  *   variant B (token keys, MLA-like): block 1, topk 2048, idx_dim 64,  idx_heads 4
  * Supported: block in {1, 4}; 1 <= topk <= 2048; (idx_dim, idx_heads) in
- * {(128, 1), (64, 4)}; key_format a qsa_key_format (QSA_KEYS_FP8 with
- * (128, 1) only). */
+ * {(128, 1), (64, 4)}; key_format a qsa_key_format. */
 typedef struct {
   int32_t block;
   int32_t topk;
@@ -193,7 +192,9 @@ qsa_status qsa_quantize_latent(const qsa_bf16* latent, int64_t seq_stride, int64
  *     hkv x dv), addressed as in qsa_kv; a QSA_KV_FP8_MLA cache gets the
  *     row quantized as qsa_quantize_latent does;
  *   - its raw indexer key (raw_new[i], idx_dim values) at raw_keys +
- *     seq * raw_seq_stride + pos * idx_dim, when raw_new is given;
+ *     seq * raw_seq_stride + pos * idx_dim, when raw_new is given; with
+ *     block 1 (the raw key is the indexer key) and QSA_KEYS_FP8, quantized
+ *     as qsa_quantize_keys does into raw_keys as FP8 pages (stride in bytes);
  *   - when pos + 1 is a multiple of block and pooled is given, the pooled
  *     key of the block it completes, bit-identical to qsa_pool_keys over the
  *     same raw keys (the block's earlier tokens are read from raw_keys);

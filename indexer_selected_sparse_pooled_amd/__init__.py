@@ -6,7 +6,7 @@ calls into a decode layer and a tiled prefill chunk.
 """
 from . import qsa  # noqa: F401
 from .qsa import (  # noqa: F401
-    ATTN_A, ATTN_B, KEYS_BF16, KEYS_FP8, SEL_A, SEL_A_FP8, SEL_B, AttnCfg, QsaError, SelCfg, decode_layer_workspace,
+    ATTN_A, ATTN_B, KEYS_BF16, KEYS_FP8, SEL_A, SEL_A_FP8, SEL_B, SEL_B_FP8, AttnCfg, QsaError, SelCfg, decode_layer_workspace,
     FP8_MLA_ROW, KV_BF16, KV_FP8_MLA, fp8_keys_empty, make_kv, qsa_fp8_keys_bytes, qsa_quantize_keys,
     qsa_quantize_latent,
     qsa_decode_layer, qsa_decode_layer_workspace_bytes, qsa_index_scores,

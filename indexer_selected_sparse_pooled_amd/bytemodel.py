@@ -94,6 +94,13 @@ def mla_decode_unit_bytes_fp8_rows(ctx: int, topk: int = 2048, idx_dim: int = 64
     return mla_decode_unit_bytes(ctx, topk, idx_dim, idx_heads, hq, dk, dv) - s * dk * BF16 + s * FP8_MLA_ROW
 
 
+def mla_decode_unit_bytes_fp8(ctx: int, topk: int = 2048, idx_dim: int = 64, idx_heads: int = 4, hq: int = 64,
+                              dk: int = 576, dv: int = 512) -> int:
+    """FP8 token keys (idx_dim codes + a 4-byte scale) and FP8 sparse-MLA rows."""
+    return mla_decode_unit_bytes_fp8_rows(ctx, topk, idx_dim, idx_heads, hq, dk, dv) - ctx * idx_dim * BF16 \
+        + ctx * (idx_dim + 4)
+
+
 def mla_prefill_flops(ctxs, topk: int = 2048, idx_dim: int = 64, idx_heads: int = 4, hq: int = 64,
                       dk: int = 576, dv: int = 512) -> dict:
     """Useful FLOPs of a prefill chunk of the shared-latent variant."""

@@ -92,12 +92,11 @@ qsa_status check_sel_cfg(const qsa_sel_cfg* c) {
 }
 
 // Indexer keys: bf16 rows (stride in elements, a multiple of 8) or FP8 pages
-// (stride in bytes, a multiple of 16; the single-head 128-d indexer only).
+// (stride in bytes, a multiple of 16).
 // per_seq: queries read their own sequences, so the stride must hold nmax keys.
 qsa_status check_keys(const qsa_sel_cfg* c, const void* keys, int64_t ss, int64_t nmax, bool per_seq) {
   if (!keys || !aligned16(keys)) return fail(QSA_ERR_ARG, "keys must be a non-NULL 16-byte aligned pointer");
   if (c->key_format == QSA_KEYS_FP8) {
-    if (c->idx_heads != 1) return fail(QSA_ERR_UNSUPPORTED, "FP8 keys: only the single-head 128-d indexer");
     if (ss % 16 || ss < 0) return fail(QSA_ERR_ARG, "FP8 keys_seq_stride must be a non-negative multiple of 16 bytes");
     if (per_seq && ss < qsa::fp8_keys_bytes(nmax, c->idx_dim))
       return fail(QSA_ERR_ARG, "keys_seq_stride smaller than the pages of max_ctx / block keys");
@@ -299,15 +298,20 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
     return fail(QSA_ERR_ARG, "tok_stride too small");
   if (kv->capacity <= 0 || kv->capacity > 0x7FFFFFFF) return fail(QSA_ERR_ARG, "bad kv capacity");
   const int dim = sel_cfg->idx_dim;
+  // with one-token blocks the raw key is the indexer key: FP8 keys are then
+  // written to raw_keys as FP8 pages
+  const bool raw_fp8 = sel_cfg->block == 1 && sel_cfg->key_format == QSA_KEYS_FP8;
   if (raw_new || raw_keys) {
     if (!raw_new || !raw_keys) return fail(QSA_ERR_ARG, "raw_new and raw_keys go together");
     if (!aligned16(raw_new) || !aligned16(raw_keys)) return fail(QSA_ERR_ARG, "raw_new and raw_keys must be 16-byte aligned");
-    if (raw_seq_stride % 8 || raw_seq_stride < 0) return fail(QSA_ERR_ARG, "raw_seq_stride must be a multiple of 8");
+    if (raw_fp8 && (raw_seq_stride % 16 || raw_seq_stride < 0))
+      return fail(QSA_ERR_ARG, "FP8 raw_seq_stride must be a non-negative multiple of 16 bytes");
+    if (!raw_fp8 && (raw_seq_stride % 8 || raw_seq_stride < 0))
+      return fail(QSA_ERR_ARG, "raw_seq_stride must be a multiple of 8");
     if (pooled) {
       if (sel_cfg->block == 1) return fail(QSA_ERR_ARG, "pooled must be NULL when block == 1");
       if (!aligned16(pooled)) return fail(QSA_ERR_ARG, "pooled must be 16-byte aligned");
       if (sel_cfg->key_format == QSA_KEYS_FP8) {
-        if (sel_cfg->idx_heads != 1) return fail(QSA_ERR_UNSUPPORTED, "FP8 keys: only the single-head 128-d indexer");
         if (pooled_seq_stride % 16 || pooled_seq_stride < 0)
           return fail(QSA_ERR_ARG, "FP8 pooled_seq_stride must be a non-negative multiple of 16 bytes");
       } else if (pooled_seq_stride % 8 || pooled_seq_stride < 0) {
@@ -340,6 +344,7 @@ qsa_status qsa_kv_append(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cf
   a.v_dim = dv;
   a.raw = raw_keys;
   a.raw_ss = raw_seq_stride;
+  a.raw_fp8 = raw_fp8;
   a.pooled = pooled;
   a.pooled_ss = pooled_seq_stride;
   a.pooled_fp8 = sel_cfg->key_format == QSA_KEYS_FP8;

@@ -35,7 +35,8 @@ struct AppendArgs {
   int k_row, v_row;         // elements per token row: hkv * head_dim, hkv * v_dim
   int head_dim, v_dim;
   uint16_t* raw;            // raw indexer keys, or nullptr
-  int64_t raw_ss;
+  int64_t raw_ss;           // elements; bytes for FP8 pages
+  int raw_fp8;              // one-token blocks with FP8 keys: raw points to FP8 pages (the key is quantized)
   void* pooled;             // pooled keys (bf16 rows, or FP8 pages), or nullptr (no pooling)
   int64_t pooled_ss;        // elements for bf16 rows, bytes for FP8 pages
   int pooled_fp8;

@@ -144,6 +144,16 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
     }
   }
   if (!rn) return;
+  if (a.raw_fp8) {  // the token's indexer key, quantized into FP8 pages (wave 0; dim <= 128)
+    if (tid < 64) {
+      const float x0 = tid < a.dim ? bf16_to_f32(rn[tid]) : 0.f;
+      const float x1 = tid + 64 < a.dim ? bf16_to_f32(rn[tid + 64]) : 0.f;
+      uint8_t* base = reinterpret_cast<uint8_t*>(a.raw) + int64_t(seq) * a.raw_ss;
+      quantize_key_wave(x0, x1, a.dim, base + fp8_code_off(pos, a.dim),
+                        reinterpret_cast<float*>(base + fp8_scale_off(pos, a.dim)));
+    }
+    return;
+  }
   for (int c = tid; c < rc; c += 256)
     st16(a.raw + int64_t(seq) * a.raw_ss + int64_t(pos) * a.dim + 8 * c, ld16(rn + 8 * c));
   if (!a.pooled || (pos + 1) % a.block != 0) return;

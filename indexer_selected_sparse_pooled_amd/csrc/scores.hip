@@ -116,6 +116,10 @@ __global__ __launch_bounds__(256) void scores_gemv_a_fp8(ScoreArgs a) {
 // A wave owns 128 consecutive keys (16 KiB); lane (g = lane/8, c = lane%8)
 // loads dims [8c, 8c+8) of keys 8k+g; after the butterfly over the 8 lanes
 // of a group it holds the 4 head dots of keys 8(2c+j)+g, j = 0, 1.
+// kFp8: FP8 token keys (pages of 64 keys of 64 codes + scales): each lane
+// reads its 8 codes, converts them to bf16 exactly, and the key's scale
+// multiplies the final score (ReLU commutes with a non-negative scale).
+template <bool kFp8>
 __global__ __launch_bounds__(256) void scores_gemv_b(ScoreArgs a) {
   const int i = blockIdx.y;
   const int seq = a.q_seq ? a.q_seq[i] : 0;
@@ -132,11 +136,18 @@ __global__ __launch_bounds__(256) void scores_gemv_b(ScoreArgs a) {
     w[h] = a.w_idx[int64_t(i) * 4 + h];
   }
   const uint16_t* kb = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss;
+  const uint8_t* kb8 = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
   float p[16][4];
 #pragma unroll
   for (int k = 0; k < 16; k++) {
     const int64_t tok = tile0 + 8 * k + g;
-    const u32x4 v = tok < n ? ld16_nt(kb + tok * 64 + 8 * c) : u32x4{0u, 0u, 0u, 0u};
+    u32x4 v = u32x4{0u, 0u, 0u, 0u};
+    if constexpr (kFp8) {
+      if (tok < n)
+        v = __builtin_bit_cast(u32x4, e4m3x8_bf16(*reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(tok, 64) + 8 * c)));
+    } else {
+      if (tok < n) v = ld16_nt(kb + tok * 64 + 8 * c);
+    }
 #pragma unroll
     for (int h = 0; h < 4; h++) p[k][h] = dot8(v, qv[h]);
   }
@@ -177,6 +188,9 @@ __global__ __launch_bounds__(256) void scores_gemv_b(ScoreArgs a) {
     float s = 0.f;
 #pragma unroll
     for (int h = 0; h < 4; h++) s += w[h] * fmaxf(p[j][h], 0.f);
+    if constexpr (kFp8) {
+      if (tok < n) s *= *reinterpret_cast<const float*>(kb8 + fp8_scale_off(tok, 64));
+    }
     if (tok < n) out[tok] = s;
   }
 }
@@ -284,6 +298,8 @@ __global__ __launch_bounds__(256) void scores_gemm_a_fp8(ScoreArgs a) {
 }
 
 // Prefill chunk, variant B: 4 heads x 64 dims, score = sum_h w_h relu(dot_h).
+// kFp8: B operands converted from E4M3 codes, the key scale applied last.
+template <bool kFp8>
 __global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
   __shared__ int red[1];
   const int q0 = blockIdx.y * 64;
@@ -315,11 +331,21 @@ __global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
     const int64_t tok = b0 + 16 * nt + r;
     if (b0 + 16 * nt >= nmax) break;
     bf16x8 kb[2];
+    float ksc = 1.f;
+    if constexpr (kFp8) {
+      const int64_t tc = tok < nmax ? tok : nmax - 1;
+      const uint8_t* kb8 = static_cast<const uint8_t*>(a.keys);
+      ksc = *reinterpret_cast<const float*>(kb8 + fp8_scale_off(tc, 64));
 #pragma unroll
-    for (int ks = 0; ks < 2; ks++) {
-      u32x4 w = tok < nmax ? ld16(static_cast<const uint16_t*>(a.keys) + tok * 64 + 32 * ks + 8 * kq)
-                           : u32x4{0u, 0u, 0u, 0u};
-      kb[ks] = as_bf16x8(w);
+      for (int ks = 0; ks < 2; ks++)
+        kb[ks] = e4m3x8_bf16(*reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(tc, 64) + 32 * ks + 8 * kq));
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) {
+        u32x4 w = tok < nmax ? ld16(static_cast<const uint16_t*>(a.keys) + tok * 64 + 32 * ks + 8 * kq)
+                             : u32x4{0u, 0u, 0u, 0u};
+        kb[ks] = as_bf16x8(w);
+      }
     }
     float s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -333,7 +359,7 @@ __global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       const int q = q0 + 16 * wave + 4 * kq + e;
-      if (tok < nrow[e]) a.scores[int64_t(q) * a.ld + tok] = s[e];
+      if (tok < nrow[e]) a.scores[int64_t(q) * a.ld + tok] = s[e] * ksc;
     }
   }
 }
@@ -377,10 +403,16 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
   } else {
     if (chunk) {
       dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
-      hipLaunchKernelGGL(scores_gemm_b, grid, dim3(256), 0, s, a);
+      if (a.key_fp8)
+        hipLaunchKernelGGL(scores_gemm_b<true>, grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(scores_gemm_b<false>, grid, dim3(256), 0, s, a);
     } else {
       dim3 grid(unsigned((nmax + 511) / 512), unsigned(a.nq));
-      hipLaunchKernelGGL(scores_gemv_b, grid, dim3(256), 0, s, a);
+      if (a.key_fp8)
+        hipLaunchKernelGGL(scores_gemv_b<true>, grid, dim3(256), 0, s, a);
+      else
+        hipLaunchKernelGGL(scores_gemv_b<false>, grid, dim3(256), 0, s, a);
     }
   }
   return hipGetLastError();

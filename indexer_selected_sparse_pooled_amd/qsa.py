@@ -58,6 +58,8 @@ SEL_A = SelCfg(4, 512, 128, 1, KEYS_BF16)
 SEL_A_FP8 = SelCfg(4, 512, 128, 1, KEYS_FP8)
 ATTN_A = AttnCfg(16, 2, 256, 256, 1.0 / 16.0)
 SEL_B = SelCfg(1, 2048, 64, 4, KEYS_BF16)
+# variant B with FP8 token keys (64 E4M3 codes + an fp32 scale per token)
+SEL_B_FP8 = SelCfg(1, 2048, 64, 4, KEYS_FP8)
 ATTN_B = AttnCfg(64, 1, 576, 512, 1.0 / 24.0)
 
 _lib = None
@@ -347,8 +349,12 @@ def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None,
         if t is not None and (t.shape[0] != nq or not t.is_contiguous()):
             raise ValueError(f"qsa_kv_append: {name} must be contiguous with {nq} rows")
     fp8 = sel_cfg.key_format == KEYS_FP8
+    raw_fp8 = fp8 and sel_cfg.block == 1  # the token key is the indexer key: FP8 pages
     if raw_keys is not None:
-        _rowmajor_tail(raw_keys, "raw_keys", 2)
+        if raw_fp8 and (raw_keys.dim() != 2 or raw_keys.stride(1) != 1):
+            raise ValueError("qsa_kv_append: FP8 token keys must be a uint8 [n_seq, bytes] page buffer")
+        if not raw_fp8:
+            _rowmajor_tail(raw_keys, "raw_keys", 2)
     if pooled is not None:
         if fp8 and (pooled.dim() != 2 or pooled.stride(1) != 1):
             raise ValueError("qsa_kv_append: FP8 pooled keys must be a uint8 [n_seq, bytes] page buffer")
@@ -357,7 +363,7 @@ def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None,
     _check("qsa_kv_append", lib().qsa_kv_append(
         ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_pos, _I32, "q_pos"),
         _dev(k_new, _BF16, "k_new"), _dev(v_new, _BF16, "v_new"), _dev(raw_new, _BF16, "raw_new"), ctypes.byref(kv),
-        _dev(raw_keys, _BF16, "raw_keys"), 0 if raw_keys is None else raw_keys.stride(0),
+        _dev(raw_keys, _U8 if raw_fp8 else _BF16, "raw_keys"), 0 if raw_keys is None else raw_keys.stride(0),
         _dev(pooled, _U8 if fp8 else _BF16, "pooled"), 0 if pooled is None else pooled.stride(0), _stream(stream)))
 
 

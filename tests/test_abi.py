@@ -93,10 +93,11 @@ def test_fp8_validation_on_the_host(lib):
     cfg = qsa.SelCfg(4, 512, 128, 1, 7)
     st = lib.qsa_index_scores(ctypes.byref(cfg), 1, None, fake, 4096, fake, None, fake, 0, fake, 1024, None)
     assert st == 2 and b"key_format" in lib.qsa_last_error()
-    # FP8 keys with the 4-head token indexer: not supported
-    cfg = qsa.SelCfg(1, 2048, 64, 4, qsa.KEYS_FP8)
-    st = lib.qsa_index_scores(ctypes.byref(cfg), 1, None, fake, 4096, fake, fake, fake, 0, fake, 4096, None)
-    assert st == 2 and b"FP8" in lib.qsa_last_error()
+    # FP8 rows only for the shared-latent attention shape
+    kv = qsa.KV(fake, fake, 0, 656, 0, 4096, qsa.KV_FP8_MLA)
+    st = lib.qsa_sparse_decode(ctypes.byref(qsa.SEL_A), ctypes.byref(qsa.ATTN_A), 1, None, fake, 4096, fake,
+                               ctypes.byref(kv), fake, fake, 1, fake, fake, None)
+    assert st == 2 and b"FP8 rows" in lib.qsa_last_error()
     # FP8 sequence stride must be a multiple of 16 bytes and hold the pages
     st = lib.qsa_index_scores(ctypes.byref(qsa.SEL_A_FP8), 1, fake, fake, 4096, fake, None, fake, 8, fake, 1024,
                               None)

@@ -180,3 +180,102 @@ def test_fp8_mla_prefill_chunk_tiled(Q, tile):
         toks = orc.selected_tokens(sel[i, :n_sel[i]], ctxs[i], 1)
         o_ref, lse_ref = orc.attend_values(q[i], v, v, toks, SCALE, dv=512)
         qc.check_attention(o[i], lse[i], o_ref, lse_ref, ob[i])
+
+
+def _relu_tolerance(q_bits, w, codes, scales, n):
+    q = orc.bf16_to_f64(q_bits)
+    k = orc.dequantize_e4m3(codes[:n], scales[:n, None], 64)
+    return 70 * 2.0 ** -24 * (np.abs(k) @ np.abs(q).T) @ np.abs(np.asarray(w, dtype=np.float64)) + 1e-30
+
+
+def test_fp8_token_key_scores(Q):
+    """The 4-head ReLU-weighted indexer over FP8 token keys (64 codes + a
+    scale per token): decode stream and prefill MFMA paths against the
+    oracle on the dequantized keys."""
+    pkg, _ = Q
+    n = 20000
+    keys_np = np.stack([qc.bits(81, s, (n, 64)) for s in range(2)])
+    keys8 = pkg.fp8_keys_empty(2, n, 64)
+    pkg.qsa_quantize_keys(qc.to_dev(keys_np), keys8)
+    ref = [orc.fp8_keys(keys_np[s]) for s in range(2)]
+    for chunk in (False, True):
+        rng = np.random.default_rng(82)
+        nq = 40 if chunk else 6
+        ctxs = [int(x) for x in rng.integers(0, n + 1, nq)]
+        ctxs[0], ctxs[-1] = n, 1
+        q_seq = None if chunk else [i % 2 for i in range(nq)]
+        _print_case("fp8_token_key_scores", chunk=chunk)
+        q_np = qc.bits(83, int(chunk), (nq, 4, 64))
+        w_np = np.stack([qi.uniform_f32(84, i, 4) for i in range(nq)])
+        sc = torch.full((nq, n + 5), float("nan"), device="cuda")
+        pkg.qsa_index_scores(pkg.SEL_B_FP8, qc.i32(ctxs), n, qc.to_dev(q_np), keys8[0:1] if chunk else keys8, sc,
+                             q_seq=None if chunk else qc.i32(q_seq), w_idx=torch.tensor(w_np, device="cuda"))
+        torch.cuda.synchronize()
+        got = sc.cpu().numpy()
+        for i, ctx in enumerate(ctxs):
+            c, s = ref[0 if chunk else q_seq[i]]
+            want = orc.index_scores_relu_fp8(q_np[i], w_np[i], c, s, ctx)
+            assert np.all(np.abs(got[i, :ctx] - want) <= _relu_tolerance(q_np[i], w_np[i], c, s, ctx)), f"query {i}"
+            assert np.all(np.isnan(got[i, ctx:]))
+
+
+def test_fp8_mla_decode_keys_and_rows(Q):
+    """Decode over FP8 token keys and FP8 rows (the GLM cache: 68 + 656
+    bytes per token): scores within the accumulation bound, the selection
+    the oracle's on the GPU's own scores, attention against the oracle on
+    the dequantized rows."""
+    pkg, pipeline = Q
+    ctxs = [20000, 2048, 2049, 7, 12345]
+    nq, cap = len(ctxs), 20000
+    _print_case("fp8_mla_decode_keys_rows", ctxs=ctxs)
+    lat = _latent(85, nq, cap)
+    keys_np = np.stack([qc.bits(86, s, (cap, 64)) for s in range(nq)])
+    q = np.stack([qc.bits(87, s, (64, 576)) for s in range(nq)])
+    q_idx = np.stack([qc.bits(88, s, (4, 64)) for s in range(nq)])
+    w = np.stack([qi.uniform_f32(89, s, 4) for s in range(nq)])
+    rows = _fp8_rows(pkg, qc.to_dev(lat))
+    keys8 = pkg.fp8_keys_empty(nq, cap, 64)
+    pkg.qsa_quantize_keys(qc.to_dev(keys_np), keys8)
+    kv = pkg.make_kv(rows)
+    bufs = pipeline.decode_buffers(pkg.SEL_B_FP8, pkg.ATTN_B, nq, cap)
+    bufs.scores.fill_(float("nan"))
+    pipeline.decode_layer(pkg.SEL_B_FP8, pkg.ATTN_B, qc.i32(ctxs), cap, qc.to_dev(q_idx), keys8, qc.to_dev(q), kv,
+                          bufs, q_seq=qc.i32(range(nq)), w_idx=torch.tensor(w, device="cuda"))
+    torch.cuda.synchronize()
+    sc, sel, n_sel = bufs.scores.cpu().numpy(), bufs.sel.cpu().numpy(), bufs.n_sel.cpu().numpy()
+    o, lse, ob = bufs.o.cpu().numpy(), bufs.lse.cpu().numpy(), qc.from_dev_bits(bufs.o_bf16)
+    vals = _values(rows.cpu().numpy())
+    for i, ctx in enumerate(ctxs):
+        c, s = orc.fp8_keys(keys_np[i])
+        want = orc.index_scores_relu_fp8(q_idx[i], w[i], c, s, ctx)
+        assert np.all(np.abs(sc[i, :ctx] - want) <= _relu_tolerance(q_idx[i], w[i], c, s, ctx)), f"query {i}: scores"
+        exp = orc.select_blocks(sc[i, :ctx].astype(np.float64), ctx, 1, 2048)
+        assert n_sel[i] == exp.size and np.array_equal(sel[i, :n_sel[i]], exp), f"query {i}: selection"
+        v = vals[i][:, None, :]
+        o_ref, lse_ref = orc.attend_values(q[i], v, v, orc.selected_tokens(exp, ctx, 1), SCALE, dv=512)
+        qc.check_attention(o[i], lse[i], o_ref, lse_ref, ob[i])
+
+
+def test_append_fp8_token_keys(Q):
+    pkg, _ = Q
+    cap, n_seq = 130, 2
+    rows = torch.zeros(n_seq, cap, 656, dtype=torch.uint8, device="cuda")
+    kv = pkg.make_kv(rows)
+    keys8 = pkg.fp8_keys_empty(n_seq, cap, 64)
+    for step, pos in enumerate(([0, 129], [64, 63], [65, 1])):
+        _print_case("append_fp8_token_keys", pos=pos)
+        new = qc.bits(90, step, (n_seq, 1, 576))
+        knew = qc.bits(91, step, (n_seq, 64))
+        knew[1, :5] = 0x8000
+        before = keys8.cpu().numpy()
+        pkg.qsa_kv_append(pkg.SEL_B_FP8, pkg.ATTN_B, qc.i32(pos), qc.to_dev(new), kv, raw_new=qc.to_dev(knew),
+                          raw_keys=keys8)
+        torch.cuda.synchronize()
+        after = keys8.cpu().numpy()
+        for s, p in enumerate(pos):
+            codes, scales = qc.unpack_fp8_pages(after[s], cap, 64)
+            wc, ws = orc.fp8_keys(knew[s:s + 1])
+            assert np.array_equal(codes[p], wc[0]) and scales[p].view(np.uint32) == ws[0].view(np.uint32)
+            oc, os_ = qc.unpack_fp8_pages(before[s], cap, 64)
+            others = np.arange(cap) != p
+            assert np.array_equal(codes[others], oc[others]) and np.array_equal(scales[others], os_[others])
