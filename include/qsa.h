@@ -374,6 +374,45 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
 size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
                                         int32_t nq, int32_t max_ctx, int32_t n_split);
 
+/* ------------------------------------------- A4 with an HBM row cache ----
+ * For K/V rows kept in host memory (pinned, read zero-copy): a direct-mapped
+ * cache of rows in device memory that later decode steps read instead of
+ * crossing the host link again ("3090x3で 314 万コンテキスト", section 5:
+ * consecutive selections overlap by 0.72 on average; one slot holds a
+ * token's K and V for every kv head, keyed by the row's position; the slots
+ * of stored rows are invalidated; per step an epoch, hit marks and claimed
+ * fill rights keep reads and fills consistent inside one launch).
+ * The pooled-block attention shape only (hq 16, hkv 2, dk = dv = 256).
+ *
+ * qsa_row_cache_bytes: bytes of a cache of n_slots rows (0 if unsupported).
+ *   The caller allocates it in device memory, zero-filled once, one per layer
+ *   (it may be shared by the sequences of one kv: keys are seq * capacity +
+ *   token).
+ * qsa_row_cache_step: once per step and layer, before that layer's
+ *   qsa_sparse_decode_cached: advances the cache's epoch and drops the rows
+ *   at (row_seq[j], row_pos[j]), j < n_rows: every row of kv stored since
+ *   the cache last saw it (e.g. by qsa_kv_append) must be listed, else a
+ *   later hit returns its old bytes; row_seq NULL: sequence j. Positions
+ *   outside [0, capacity) are ignored. To drop every row (e.g. after a
+ *   prefill rewrote many), zero-fill the cache again instead.
+ * qsa_sparse_decode_cached: exactly what qsa_sparse_decode computes, bit for
+ *   bit, reading each selected row from the cache when it holds it and from
+ *   kv otherwise, and leaving rows read from kv in the cache (a slot keeps
+ *   one row; of several rows that want one slot in a step, one is kept).
+ *   plan_ws: device workspace of qsa_decode_cached_plan_bytes(sel_cfg, nq)
+ *   bytes (contents ignored). Calls sharing a cache must not overlap. */
+size_t qsa_row_cache_bytes(const qsa_attn_cfg* attn_cfg, int64_t n_slots);
+size_t qsa_decode_cached_plan_bytes(const qsa_sel_cfg* sel_cfg, int32_t nq);
+qsa_status qsa_row_cache_step(const qsa_attn_cfg* attn_cfg, void* cache, size_t cache_bytes, int64_t n_slots,
+                              int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos,
+                              const qsa_kv* kv, qsa_stream_t stream);
+qsa_status qsa_sparse_decode_cached(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                    const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                                    const qsa_bf16* q, const qsa_kv* kv, const int32_t* sel,
+                                    const int32_t* n_sel, int32_t n_split, float* o_part, float* lse_part,
+                                    void* cache, size_t cache_bytes, int64_t n_slots, void* plan_ws,
+                                    size_t plan_ws_bytes, qsa_stream_t stream);
+
 /* ---------------------------------------------------------------- A6 ----
  * qsa_sparse_prefill: the same attention restricted to one history tile:
  * query i attends the tokens of its list that lie in [tile_begin, tile_end)

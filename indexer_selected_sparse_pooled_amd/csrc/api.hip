@@ -617,6 +617,88 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
   return finish(qsa::launch_attend(a, s), s, "qsa_sparse_decode");
 }
 
+size_t qsa_row_cache_bytes(const qsa_attn_cfg* attn_cfg, int64_t n_slots) {
+  if (!attn_cfg || n_slots <= 0) return 0;
+  if (!(attn_cfg->hq == 16 && attn_cfg->hkv == 2 && attn_cfg->dk == 256 && attn_cfg->dv == 256)) return 0;
+  return qsa::row_cache_layout(n_slots, int64_t(attn_cfg->hkv) * (attn_cfg->dk + attn_cfg->dv) * 2).bytes;
+}
+
+size_t qsa_decode_cached_plan_bytes(const qsa_sel_cfg* sel_cfg, int32_t nq) {
+  if (!sel_cfg || nq <= 0 || sel_cfg->block <= 0 || sel_cfg->topk <= 0) return 0;
+  return size_t(nq) * size_t(sel_cfg->topk * sel_cfg->block + sel_cfg->block - 1) * 4;
+}
+
+namespace {
+qsa_status check_row_cache(const qsa_attn_cfg* ac, const void* cache, size_t cache_bytes, int64_t n_slots) {
+  if (!ac || !cache) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!(ac->hq == 16 && ac->hkv == 2 && ac->dk == 256 && ac->dv == 256))
+    return fail(QSA_ERR_UNSUPPORTED, "row cache: the pooled-block attention shape only (hq 16, hkv 2, dk = dv = 256)");
+  if (n_slots < 1 || n_slots > 0x7FFFFFFF) return fail(QSA_ERR_ARG, "n_slots %lld not in [1, 2^31)", (long long)n_slots);
+  if (!aligned16(cache)) return fail(QSA_ERR_ARG, "cache must be 16-byte aligned");
+  const size_t need = qsa_row_cache_bytes(ac, n_slots);
+  if (cache_bytes < need) return fail(QSA_ERR_WORKSPACE, "row cache %zu bytes < %zu required", cache_bytes, need);
+  return QSA_OK;
+}
+}  // namespace
+
+qsa_status qsa_row_cache_step(const qsa_attn_cfg* attn_cfg, void* cache, size_t cache_bytes, int64_t n_slots,
+                              int32_t n_rows, const int32_t* row_seq, const int32_t* row_pos, const qsa_kv* kv,
+                              qsa_stream_t stream) {
+  qsa_status st = check_row_cache(attn_cfg, cache, cache_bytes, n_slots);
+  if (st != QSA_OK) return st;
+  if (!kv || kv->capacity <= 0) return fail(QSA_ERR_ARG, "kv with a positive capacity is required");
+  if (n_rows < 0) return fail(QSA_ERR_ARG, "negative n_rows");
+  if (n_rows > 0 && !row_pos) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const qsa::RowCacheLayout L = qsa::row_cache_layout(n_slots, int64_t(attn_cfg->hkv) * (attn_cfg->dk + attn_cfg->dv) * 2);
+  return finish(qsa::launch_row_cache_step(static_cast<unsigned char*>(cache), L, n_rows, row_seq, row_pos, kv->capacity, s), s,
+                "qsa_row_cache_step");
+}
+
+qsa_status qsa_sparse_decode_cached(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                    const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q,
+                                    const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel, int32_t n_split,
+                                    float* o_part, float* lse_part, void* cache, size_t cache_bytes, int64_t n_slots,
+                                    void* plan_ws, size_t plan_ws_bytes, qsa_stream_t stream) {
+  qsa_status st = check_attn(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel, o_part, lse_part);
+  if (st != QSA_OK) return st;
+  if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
+  st = check_row_cache(attn_cfg, cache, cache_bytes, n_slots);
+  if (st != QSA_OK) return st;
+  if (kv->format != QSA_KV_BF16) return fail(QSA_ERR_UNSUPPORTED, "row cache: bf16 K/V rows only");
+  if (nq == 0) return QSA_OK;
+  if (int64_t(nq) * n_split > 0x7FFFFFFF || nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "too many work-groups");
+  const size_t need = qsa_decode_cached_plan_bytes(sel_cfg, nq);
+  if (!plan_ws || plan_ws_bytes < need) return fail(QSA_ERR_WORKSPACE, "plan workspace %zu bytes < %zu", plan_ws_bytes, need);
+  if (!aligned16(plan_ws)) return fail(QSA_ERR_ARG, "plan workspace must be 16-byte aligned");
+  if (need / 4 >= 0xFFFFFFFFull) return fail(QSA_ERR_UNSUPPORTED, "too many list positions");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::AttendArgs a = attend_args(sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q, kv, sel, n_sel, n_split, 0,
+                                  int64_t(max_ctx), o_part, lse_part);
+  const qsa::RowCacheLayout L = qsa::row_cache_layout(n_slots, int64_t(attn_cfg->hkv) * (attn_cfg->dk + attn_cfg->dv) * 2);
+  unsigned char* c = static_cast<unsigned char*>(cache);
+  const int src_ld = sel_cfg->topk * sel_cfg->block + sel_cfg->block - 1;
+  a.src_ld = src_ld;
+  a.c_rows = c + L.off_rows;
+  a.c_tag = reinterpret_cast<uint64_t*>(c + L.off_tag);
+  a.c_hit = reinterpret_cast<const uint32_t*>(c + L.off_hit);
+  a.c_claim = reinterpret_cast<const uint64_t*>(c + L.off_claim);
+  a.c_epoch = reinterpret_cast<const uint32_t*>(c);
+  a.n_slots = n_slots;
+  a.row_bytes = L.row_bytes;
+  a.key_stride = kv->capacity;
+  hipError_t e = qsa::launch_row_cache_plan(a, c, L, static_cast<int*>(plan_ws), src_ld, s);
+  if (e != hipSuccess) return finish(e, s, "qsa_sparse_decode_cached");
+  a.src = static_cast<const int*>(plan_ws);
+  return finish(qsa::launch_attend(a, s), s, "qsa_sparse_decode_cached");
+}
+
 qsa_status qsa_sparse_prefill(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                               const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q,
                               const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel, int64_t tile_begin,

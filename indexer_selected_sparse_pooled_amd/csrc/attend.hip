@@ -28,13 +28,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   mla::attend_part_fp8<false>(a, split, i, sh);
 }
 
+// The pooled-block variant over K/V in host memory with the HBM row cache.
+__global__ __launch_bounds__(256) void attend_a_cached(AttendArgs a) {
+  __shared__ att::Lds<1> sh;
+  const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
+  att::attend_part<false, 1, true>(a, split, blockIdx.y, i, sh);
+}
+
 }  // namespace
 
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
   if (a.hq == 16 && a.hkv == 2 && a.dk == 256 && a.dv == 256) {
     dim3 grid(unsigned(int64_t(a.nq) * a.n_split), unsigned(a.hkv));
-    hipLaunchKernelGGL(attend_a, grid, dim3(256), 0, s, a);
+    if (a.src)
+      hipLaunchKernelGGL(attend_a_cached, grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(attend_a, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   if (a.hq == mla::kH && a.hkv == 1 && a.dk == mla::kDK && a.dv == mla::kDV) {

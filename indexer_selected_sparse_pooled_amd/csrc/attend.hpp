@@ -100,10 +100,18 @@ struct List {
   }
 };
 
+__device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
+  const uint32_t lo = __shfl(uint32_t(v), src), hi = __shfl(uint32_t(v >> 32), src);
+  return (uint64_t(hi) << 32) | lo;
+}
+
 // One part (split, kv head g, query i): see the file comment. sel_lds, when
 // given, holds the query's ns_lds selected blocks in LDS (ascending) and
-// replaces sel / n_sel.
-template <bool kCoh, int GT>
+// replaces sel / n_sel. kCached: rows come from the HBM row cache on a hit
+// (the plan in a.src) and from their home (host) memory otherwise, and the
+// rows this part may fill are written to the cache after the tile
+// (row_cache.hip).
+template <bool kCoh, int GT, bool kCached = false>
 __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT>& sh, const int* sel_lds = nullptr,
                             int ns_lds = 0) {
   constexpr int kTok = Lds<GT>::kTok, kPStr = Lds<GT>::kPStr;
@@ -144,6 +152,9 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
   const uint16_t* kbase = a.k + kvs;
   const uint16_t* vbase = a.v + kvs;
   const float sl2 = a.scale * kLog2e;
+  [[maybe_unused]] uint32_t epoch = 0;
+  if constexpr (kCached) epoch = *a.c_epoch;
+  [[maybe_unused]] const int64_t slot_off = int64_t(g) * (a.dk + a.dv) * 2;  // kv head g's K, V in a slot
 
   bf16x8 qa[kD / 32];
   {
@@ -165,7 +176,28 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
     // repeat row 0, so every load reads finite data that the softmax then
     // weights by 0.
     const int row_l = kRW * wave + lane % kRW;
-    const int tokl = lv.tok(pb + (row_l < cnt ? row_l : 0));
+    const int pos_l = pb + (row_l < cnt ? row_l : 0);
+    int tokl = 0;
+    [[maybe_unused]] uint64_t krow_l = 0, vrow_l = 0, key_l = 0;  // cached: the row's K, V addresses and key
+    [[maybe_unused]] int64_t slot_l = 0;
+    [[maybe_unused]] bool fill_l = false;
+    if constexpr (kCached) {
+      const int e = a.src[int64_t(i) * a.src_ld + pos_l];
+      if (e < 0) {  // in the cache
+        slot_l = -int64_t(e) - 1;
+        krow_l = uint64_t(a.c_rows + slot_l * a.row_bytes + slot_off);
+        vrow_l = krow_l + 2 * a.dk;
+      } else {  // from its home memory; may fill its slot
+        krow_l = uint64_t(kbase + int64_t(e) * a.tok_stride);
+        vrow_l = uint64_t(vbase + int64_t(e) * a.tok_stride);
+        key_l = uint64_t(int64_t(seq) * a.key_stride + e) + 1u;
+        slot_l = int64_t((key_l - 1u) % uint64_t(a.n_slots));
+        const uint32_t id = uint32_t(int64_t(i) * a.src_ld + pos_l) + 1u;
+        fill_l = row_l < cnt && a.c_claim[slot_l] == ((uint64_t(epoch) << 32) | id) && a.c_hit[slot_l] != epoch;
+      }
+    } else {
+      tokl = lv.tok(pos_l);
+    }
     // V rows go straight to LDS (no registers) and K rows to registers as
     // the B operands of S. With one tile per group (many work-groups per CU)
     // the V rows are issued first; with several tiles (few, latency-bound
@@ -175,18 +207,28 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
 #pragma unroll
       for (int j = 0; j < 8 * GT; j++) {
         const int p = 8 * GT * wave + j;
-        const int vt = __shfl(tokl, 2 * j + half);
-        __builtin_amdgcn_global_load_lds(
-            vbase + int64_t(vt) * a.tok_stride + 8 * c,
-            (__attribute__((address_space(3))) void*)(sh.v + p * kPair), 16, 0, 0);
+        const uint16_t* vsrc;
+        if constexpr (kCached) {
+          vsrc = reinterpret_cast<const uint16_t*>(shfl64(vrow_l, 2 * j + half)) + 8 * c;
+        } else {
+          const int vt = __shfl(tokl, 2 * j + half);
+          vsrc = vbase + int64_t(vt) * a.tok_stride + 8 * c;
+        }
+        __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(sh.v + p * kPair), 16, 0,
+                                         0);
       }
     };
     if constexpr (GT == 1) load_v();
     bf16x8 kb[GT][kD / 32];
 #pragma unroll
     for (int b = 0; b < GT; b++) {
-      const int kt = __shfl(tokl, 16 * b + r);
-      const uint16_t* krow = kbase + int64_t(kt) * a.tok_stride + 8 * kq;
+      const uint16_t* krow;
+      if constexpr (kCached) {
+        krow = reinterpret_cast<const uint16_t*>(shfl64(krow_l, 16 * b + r)) + 8 * kq;
+      } else {
+        const int kt = __shfl(tokl, 16 * b + r);
+        krow = kbase + int64_t(kt) * a.tok_stride + 8 * kq;
+      }
 #pragma unroll
       for (int ks = 0; ks < kD / 32; ks++) kb[b][ks] = as_bf16x8(ld16(krow + 32 * ks));
     }
@@ -280,6 +322,34 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
           oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bv, oacc[nt], 0, 0, 0);
           oacc[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al8, bv, oacc[nt], 0, 0, 0);
         }
+      }
+    }
+    if constexpr (kCached) {
+      // rows this part may fill: K from the registers (lane (kq, r) holds
+      // dims 32ks + 8kq .. +7 of wave row 16b + r), V from LDS (as loaded)
+#pragma unroll
+      for (int b = 0; b < GT; b++) {
+        const int sl = 16 * b + r;
+        const bool f = __shfl(int(fill_l), sl) != 0;
+        const int64_t c = int64_t(shfl64(uint64_t(slot_l), sl));
+        const uint64_t key = shfl64(key_l, sl);
+        if (f) {
+          unsigned char* dst = a.c_rows + c * a.row_bytes + slot_off;
+#pragma unroll
+          for (int ks = 0; ks < kD / 32; ks++) st16(dst + 2 * (32 * ks + 8 * kq), __builtin_bit_cast(u32x4, kb[b][ks]));
+          if (kq == 0 && g == 0) a.c_tag[c] = key;
+        }
+      }
+      const int half = lane >> 5, c32 = lane & 31;
+#pragma unroll
+      for (int j = 0; j < 8 * GT; j++) {
+        const int p = 8 * GT * wave + j;
+        const int sl = 2 * j + half;
+        const bool f = __shfl(int(fill_l), sl) != 0;
+        const int64_t c = int64_t(shfl64(uint64_t(slot_l), sl));
+        if (f)
+          st16(a.c_rows + c * a.row_bytes + slot_off + 2 * a.dk + 16 * c32,
+               *reinterpret_cast<const u32x4*>(sh.v + p * kPair + 512 * half + 16 * c32));
       }
     }
     __syncthreads();

@@ -114,8 +114,29 @@ struct AttendArgs {
   float* o_out;       // [nq][hq][dv] or nullptr
   uint16_t* o_bf16;   // [nq][hq][dv] or nullptr
   float* lse_out;     // [nq][hq] or nullptr
+  // HBM row cache (qsa_sparse_decode_cached); src == nullptr: none
+  const int* src;           // [nq][src_ld] per list position: -(slot + 1) for a hit, else the token
+  int src_ld;
+  unsigned char* c_rows;    // [n_slots][row_bytes]: per slot, kv head g's K then V (bf16)
+  uint64_t* c_tag;          // [n_slots] key + 1 of the held row (0: empty)
+  const uint32_t* c_hit;    // [n_slots] epoch of the last step with a hit on the slot
+  const uint64_t* c_claim;  // [n_slots] epoch << 32 | claimer id, the step's fill right
+  const uint32_t* c_epoch;
+  int64_t n_slots, row_bytes, key_stride;  // key of (seq, tok) = seq * key_stride + tok
 };
 hipError_t launch_attend(const AttendArgs& a, hipStream_t s);
+
+// Row cache: layout of the caller's buffer, the per-step invalidation and
+// epoch advance, and the plan of one decode launch.
+struct RowCacheLayout {
+  int64_t n_slots, row_bytes;
+  size_t off_tag, off_hit, off_claim, off_rows, bytes;
+};
+RowCacheLayout row_cache_layout(int64_t n_slots, int64_t row_bytes);
+hipError_t launch_row_cache_step(unsigned char* cache, const RowCacheLayout& L, int n_rows, const int* row_seq,
+                                 const int* row_pos, int64_t key_stride, hipStream_t s);
+hipError_t launch_row_cache_plan(const AttendArgs& a, unsigned char* cache, const RowCacheLayout& L, int* src,
+                                 int src_ld, hipStream_t s);
 
 // Decode scan + exact top-k in one launch (variant A: 128-d pooled keys).
 struct IndexTopkArgs {

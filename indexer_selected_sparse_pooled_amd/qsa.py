@@ -81,6 +81,11 @@ _SIGS = {
                          _vp, _vp, _vp, _vp, _sz, _vp],
     "qsa_decode_layer_workspace_bytes": [_vp, _vp, _i32, _i32, _i32],
     "qsa_sparse_decode": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp],
+    "qsa_row_cache_bytes": [_vp, _i64],
+    "qsa_decode_cached_plan_bytes": [_vp, _i32],
+    "qsa_row_cache_step": [_vp, _vp, _sz, _i64, _i32, _vp, _vp, _vp, _vp],
+    "qsa_sparse_decode_cached": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
+                                 _i64, _vp, _sz, _vp],
     "qsa_sparse_prefill": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
     "qsa_lse_merge": [_i32, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "qsa_status_string": [_i32],
@@ -88,7 +93,8 @@ _SIGS = {
     "qsa_version": [],
 }
 _RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_fp8_keys_bytes": _i64,
-        "qsa_decode_layer_workspace_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
+        "qsa_decode_layer_workspace_bytes": _sz,
+        "qsa_row_cache_bytes": _sz, "qsa_decode_cached_plan_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
         "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
 EXPORTS = tuple(_SIGS)
 
@@ -431,6 +437,54 @@ def qsa_sparse_decode(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, n_sp
         _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q, _BF16, "q"), ctypes.byref(kv),
         _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_part, _F32, "o_part"),
         _dev(lse_part, _F32, "lse_part"), _stream(stream)))
+
+
+def qsa_row_cache_bytes(attn_cfg, n_slots):
+    """Bytes of an HBM row cache of n_slots rows (0: shape not supported)."""
+    return lib().qsa_row_cache_bytes(ctypes.byref(attn_cfg), n_slots)
+
+
+def qsa_decode_cached_plan_bytes(sel_cfg, nq):
+    return lib().qsa_decode_cached_plan_bytes(ctypes.byref(sel_cfg), nq)
+
+
+def row_cache_empty(attn_cfg, n_slots, device="cuda"):
+    """A zero-filled row cache (uint8 device tensor) of n_slots rows."""
+    n = qsa_row_cache_bytes(attn_cfg, n_slots)
+    if n == 0:
+        raise ValueError("row cache: unsupported attention shape or slot count")
+    return torch.zeros(n, dtype=torch.uint8, device=device)
+
+
+def qsa_row_cache_step(attn_cfg, cache, n_slots, row_pos, kv, row_seq=None, stream=None):
+    """Advance the cache's epoch and drop the rows at (row_seq[j], row_pos[j])
+    (int32 device tensors; row_seq None: sequence j)."""
+    n_rows = 0 if row_pos is None else row_pos.shape[0]
+    _check("qsa_row_cache_step", lib().qsa_row_cache_step(
+        ctypes.byref(attn_cfg), _dev(cache, _U8, "cache"), cache.numel(), n_slots, n_rows,
+        _dev(row_seq, _I32, "row_seq"), _dev(row_pos, _I32, "row_pos"), ctypes.byref(kv), _stream(stream)))
+
+
+def qsa_sparse_decode_cached(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, n_split, o_part, lse_part,
+                             cache, n_slots, plan_ws, q_seq=None, stream=None):
+    """qsa_sparse_decode reading rows through the HBM row cache `cache`
+    (row_cache_empty); plan_ws: device tensor of at least
+    qsa_decode_cached_plan_bytes(sel_cfg, nq) bytes."""
+    nq = q_ctx.shape[0]
+    if not q.is_contiguous() or not o_part.is_contiguous() or not lse_part.is_contiguous():
+        raise ValueError("q, o_part and lse_part must be contiguous")
+    if tuple(o_part.shape) != (n_split, nq, attn_cfg.hq, attn_cfg.dv):
+        raise ValueError("o_part must be [n_split, nq, hq, dv]")
+    if tuple(lse_part.shape) != (n_split, nq, attn_cfg.hq):
+        raise ValueError("lse_part must be [n_split, nq, hq]")
+    if not plan_ws.is_contiguous():
+        raise ValueError("plan_ws must be contiguous")
+    _check("qsa_sparse_decode_cached", lib().qsa_sparse_decode_cached(
+        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"),
+        _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q, _BF16, "q"), ctypes.byref(kv),
+        _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_part, _F32, "o_part"),
+        _dev(lse_part, _F32, "lse_part"), _dev(cache, _U8, "cache"), cache.numel(), n_slots,
+        _dev(plan_ws, _U8 + _I32, "plan_ws"), plan_ws.numel() * plan_ws.element_size(), _stream(stream)))
 
 
 def qsa_sparse_prefill(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, tile_begin, tile_end,

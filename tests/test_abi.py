@@ -108,3 +108,34 @@ def test_fp8_validation_on_the_host(lib):
     # quantize: only 64- and 128-d keys
     st = lib.qsa_quantize_keys(fake, 0, fake, 0, 1, 0, 10, 96, None)
     assert st == 2
+
+
+def test_row_cache_sizes_and_host_validation(lib):
+    """Row cache buffer: a 256-byte header (the epoch), then per slot a tag
+    (8 B), a hit mark (4 B), a claim (8 B) and the row (K and V of both kv
+    heads, 2 KiB), each array 256-byte aligned. Misuse fails on the host."""
+    from indexer_selected_sparse_pooled_amd import qsa
+    up = lambda x: (x + 255) // 256 * 256
+    n = 1000
+    want = up(up(up(256 + 8 * n) + 4 * n) + 8 * n) + n * 2048
+    assert qsa.qsa_row_cache_bytes(qsa.ATTN_A, n) == want
+    assert qsa.qsa_row_cache_bytes(qsa.ATTN_B, n) == 0
+    assert qsa.qsa_row_cache_bytes(qsa.ATTN_A, 0) == 0
+    assert qsa.qsa_decode_cached_plan_bytes(qsa.SEL_A, 4) == 4 * 2051 * 4
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    kv = qsa.KV(fake, fake, 4096 * 1024, 1024, 256, 4096, qsa.KV_BF16)
+
+    def decode(attn, kvd, cache_bytes, n_slots, plan_bytes):
+        return lib.qsa_sparse_decode_cached(ctypes.byref(qsa.SEL_A), ctypes.byref(attn), 1, None, fake, 4096, fake,
+                                            ctypes.byref(kvd), fake, fake, 1, fake, fake, fake, cache_bytes, n_slots,
+                                            fake, plan_bytes, None)
+    assert decode(qsa.ATTN_A, kv, want - 1, n, 2051 * 4) == 3
+    assert decode(qsa.ATTN_A, kv, want, n, 2051 * 4 - 1) == 3
+    assert decode(qsa.ATTN_A, kv, want, 0, 2051 * 4) == 1
+    kv8 = qsa.KV(fake, fake, 0, 656, 0, 4096, qsa.KV_FP8_MLA)
+    st = decode(qsa.ATTN_A, kv8, want, n, 2051 * 4)
+    assert st == 2
+    st = lib.qsa_row_cache_step(ctypes.byref(qsa.ATTN_B), fake, want, n, 0, None, None, ctypes.byref(kv), None)
+    assert st == 2 and b"row cache" in lib.qsa_last_error()
+    st = lib.qsa_row_cache_step(ctypes.byref(qsa.ATTN_A), fake, want, n, -1, None, None, ctypes.byref(kv), None)
+    assert st == 1
