@@ -203,7 +203,9 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
     ms_host, _, graph = time_graph(torch, layer_host, max(10, steps // 2), warmup)
     del graph
     ms_dev1, _, graph = time_graph(torch, layer_dev, max(10, steps // 2), warmup)
-    del graph, kv_host, k_host, v_host
+    del graph
+    rcache = run_row_cache(pkg, pipeline, qi, torch, lay0, kv_host, q_ctx, q_seq, L, B, b0.n_split)
+    del kv_host, k_host, v_host
     # the same step with FP8 pooled keys (128 E4M3 codes + an fp32 scale per
     # block, quantized from each layer's bf16 pooled keys; K/V rows stay bf16)
     for lay in layers:
@@ -264,7 +266,196 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
                 scan_launch_bytes=scan_launch_bytes, lists_gbs=scan_launch_bytes / (lists_ms * 1e-3) / 1e9,
                 ms_fp8=ms_fp8, step_bytes_fp8=bm.decode_unit_bytes_fp8(L) * B * len(layers),
                 lists_fp8_ms=lists_fp8_ms, lists_fp8_gbs=scan_fp8_bytes / (lists_fp8_ms * 1e-3) / 1e9,
-                ms_two=ms_two, layers=layers, bufs=bufs)
+                ms_two=ms_two, rcache=rcache, layers=layers, bufs=bufs)
+
+
+ROW_CACHE_SLOTS = 65536  # 128 MiB per layer: about 8 steps of batch-4 rows
+PAGES_CACHE_SLOTS = 12144  # the per-layer slot count the pages' cache used
+LARGE_CACHE_SLOTS = 262144  # 512 MiB per layer (6 GiB for 12 layers)
+
+
+def run_row_cache(pkg, pipeline, qi, torch, lay0, kv_host, q_ctx, q_seq, L, B, n_split, warm=16, timed=32, reps=3):
+    """The attention of one layer over K/V rows in pinned host memory, without
+    and with the HBM row cache, over consecutive decode steps whose
+    selections come from AR(1)-correlated indexer queries (plus the
+    repeated-selection and random-selection extremes). Per step: the cache
+    step (the row each sequence just stored is dropped), the plan and the
+    cached attention; the partial-result merge is the same for both paths and
+    left out of both. Then the whole layer over the same steps (scan and
+    selection from each step's indexer query, attention, merge): the one-call
+    layer over host-resident rows against the separate calls with the cache."""
+    import numpy as np
+    T = warm + timed
+    seed = qi.config_seed(DECODE["config_id"])
+    rho = correlated_rho("correlated_overlap_decode.txt")
+    qb = np.stack([qi.ar1_normal_bf16(seed, qi.stream_id(0, s, "q_idx", salt=2), T, 128, rho) for s in range(B)])
+    q_all = torch.from_numpy(qb.view(np.int16)).to("cuda").view(torch.bfloat16)
+    scores = torch.empty(B, L // 4, dtype=torch.float32, device="cuda")
+    ws = pkg.index_topk_workspace(pkg.SEL_A, B, L)
+    sel_corr = torch.empty(T, B, 512, dtype=torch.int32, device="cuda")
+    n_sel = torch.empty(T, B, dtype=torch.int32, device="cuda")
+    for t in range(T):
+        pkg.qsa_index_topk(pkg.SEL_A, q_ctx, L, q_all[:, t:t + 1].contiguous(), lay0["pooled"], scores, sel_corr[t],
+                           n_sel[t], ws, q_seq=q_seq)
+    torch.cuda.synchronize()
+    sc = sel_corr.cpu().numpy()
+    overlap = float(np.mean([np.intersect1d(sc[t, b], sc[t - 1, b]).size / 512
+                             for t in range(1, T) for b in range(B)]))
+    rng = np.random.default_rng(seed)
+    rnd = np.stack([np.stack([np.sort(rng.choice(L // 4, 512, replace=False)) for _ in range(B)])
+                    for _ in range(T)]).astype(np.int32)
+    sel_rnd = torch.from_numpy(rnd).cuda()
+    sel_same = sel_corr[:1].expand(T, B, 512).contiguous()
+    o = torch.empty(n_split, B, 16, 256, device="cuda")
+    lse = torch.empty(n_split, B, 16, device="cuda")
+    plan = torch.empty(B, pkg.qsa_decode_cached_plan_bytes(pkg.SEL_A, B) // (4 * B), dtype=torch.int32, device="cuda")
+    stored = (q_ctx - 1).contiguous()
+
+    def one(sel_t, ns_t, cache, n_slots, kv=kv_host):
+        if cache is None:
+            pkg.qsa_sparse_decode(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"], kv, sel_t, ns_t, n_split, o, lse,
+                                  q_seq=q_seq)
+        else:
+            pkg.qsa_row_cache_step(pkg.ATTN_A, cache, n_slots, stored, kv_host, row_seq=q_seq)
+            pkg.qsa_sparse_decode_cached(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"], kv_host, sel_t, ns_t, n_split,
+                                         o, lse, cache, n_slots, plan, q_seq=q_seq)
+
+    def regime(sel, n_slots=None, kv=kv_host):
+        cache = pkg.row_cache_empty(pkg.ATTN_A, n_slots) if n_slots else None
+
+        def warm_part():
+            if cache is not None:
+                cache.zero_()
+            for t in range(warm):
+                one(sel[t], n_sel[t], cache, n_slots, kv)
+
+        def timed_part():
+            for t in range(warm, T):
+                one(sel[t], n_sel[t], cache, n_slots, kv)
+
+        warm_part()
+        timed_part()
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ga):
+            warm_part()
+        with torch.cuda.graph(gb):
+            timed_part()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for _ in range(reps):
+            ga.replay()
+            e0.record()
+            gb.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        out = dict(ms=round(tot / reps / timed, 4))
+        if cache is not None:  # the same steps again, eagerly, counting the hits of the timed ones
+            hits = 0
+            cache.zero_()
+            for t in range(T):
+                one(sel[t], n_sel[t], cache, n_slots)
+                if t >= warm:
+                    hits += int((plan[:, :2048] < 0).sum().item())
+            out["hit_rate"] = round(hits / (timed * B * 2048), 4)
+            out["host_link_mb_per_step"] = round((1 - out["hit_rate"]) * B * 2048 * 2048 / 1e6, 2)
+        del ga, gb
+        return out
+
+    res = {
+        "all_rows_from_host": regime(sel_corr),
+        "cached_correlated": regime(sel_corr, ROW_CACHE_SLOTS),
+        "cached_correlated_pages_size": regime(sel_corr, PAGES_CACHE_SLOTS),
+        "cached_correlated_large": regime(sel_corr, LARGE_CACHE_SLOTS),
+        "cached_same_selection": regime(sel_same, ROW_CACHE_SLOTS),
+        "cached_random_selection": regime(sel_rnd, ROW_CACHE_SLOTS),
+        "all_rows_from_host_random": regime(sel_rnd),
+        "all_rows_in_hbm": regime(sel_corr, kv=lay0["kv"]),
+    }
+    # the whole layer per step, from the step's indexer query
+    q_steps = [q_all[:, t:t + 1].contiguous() for t in range(T)]
+    lbuf = pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, B, L, n_split=n_split)
+    ws = pkg.index_topk_workspace(pkg.SEL_A, B, L)
+    sel_l = torch.empty(B, 512, dtype=torch.int32, device="cuda")
+    nsel_l = torch.empty(B, dtype=torch.int32, device="cuda")
+    o_fin = torch.empty(B, 16, 256, device="cuda")
+    ob_fin = torch.empty(B, 16, 256, dtype=torch.bfloat16, device="cuda")
+    lse_fin = torch.empty(B, 16, device="cuda")
+
+    def layer_steps(cache, n_slots, ts):
+        for t in ts:
+            if cache is None:
+                pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, q_steps[t], lay0["pooled"], lay0["q"],
+                                      kv_host, lbuf, q_seq=q_seq, fused=True)
+                continue
+            pkg.qsa_index_topk(pkg.SEL_A, q_ctx, L, q_steps[t], lay0["pooled"], scores, sel_l, nsel_l, ws,
+                               q_seq=q_seq)
+            pkg.qsa_row_cache_step(pkg.ATTN_A, cache, n_slots, stored, kv_host, row_seq=q_seq)
+            pkg.qsa_sparse_decode_cached(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"], kv_host, sel_l, nsel_l,
+                                         n_split, o, lse, cache, n_slots, plan, q_seq=q_seq)
+            pkg.qsa_lse_merge(o, lse, o_out=o_fin, o_out_bf16=ob_fin, lse_out=lse_fin)
+
+    def layer_regime(n_slots):
+        cache = pkg.row_cache_empty(pkg.ATTN_A, n_slots) if n_slots else None
+
+        def warm_part():
+            if cache is not None:
+                cache.zero_()
+            layer_steps(cache, n_slots, range(warm))
+
+        warm_part()
+        layer_steps(cache, n_slots, range(warm, T))
+        torch.cuda.synchronize()
+        ga, gb = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+        with torch.cuda.graph(ga):
+            warm_part()
+        with torch.cuda.graph(gb):
+            layer_steps(cache, n_slots, range(warm, T))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        tot = 0.0
+        for _ in range(reps):
+            ga.replay()
+            e0.record()
+            gb.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            tot += e0.elapsed_time(e1)
+        del ga, gb
+        return round(tot / reps / timed, 4)
+
+    layer = {"one_call_layer_all_rows_from_host": layer_regime(None),
+             "separate_calls_with_cache": layer_regime(ROW_CACHE_SLOTS),
+             "separate_calls_with_large_cache": layer_regime(LARGE_CACHE_SLOTS)}
+    # the cached layer's output equals that of the same calls without the
+    # cache, bit for bit (last step)
+    pkg.qsa_index_topk(pkg.SEL_A, q_ctx, L, q_steps[T - 1], lay0["pooled"], scores, sel_l, nsel_l, ws, q_seq=q_seq)
+    pkg.qsa_sparse_decode(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay0["q"], kv_host, sel_l, nsel_l, n_split, o, lse,
+                          q_seq=q_seq)
+    pkg.qsa_lse_merge(o, lse, o_out=o_fin, o_out_bf16=ob_fin, lse_out=lse_fin)
+    torch.cuda.synchronize()
+    ref_o = o_fin.clone()
+    cache = pkg.row_cache_empty(pkg.ATTN_A, ROW_CACHE_SLOTS)
+    layer_steps(cache, ROW_CACHE_SLOTS, range(T))
+    torch.cuda.synchronize()
+    if not torch.equal(o_fin, ref_o):
+        raise RuntimeError("row cache: cached layer output differs from the one-call layer's")
+    del cache
+    # the cached attention's outputs are those of the uncached one, bit for bit
+    cache = pkg.row_cache_empty(pkg.ATTN_A, PAGES_CACHE_SLOTS)
+    for t in range(3):
+        one(sel_corr[t], n_sel[t], None, None)
+        ref = (o.clone(), lse.clone())
+        one(sel_corr[t], n_sel[t], cache, PAGES_CACHE_SLOTS)
+        torch.cuda.synchronize()
+        if not (torch.equal(o, ref[0]) and torch.equal(lse, ref[1])):
+            raise RuntimeError("row cache: cached attention differs from the uncached one")
+    del cache
+    log("row cache: " + ", ".join(f"{k} {v['ms']:.4f} ms" + (f" (hits {v['hit_rate']:.3f})" if "hit_rate" in v else "")
+                                  for k, v in res.items()) + f"; selection overlap {overlap:.3f}; layer {layer}")
+    return dict(overlap_prev_step=round(overlap, 4), n_slots=ROW_CACHE_SLOTS, layer_ms=layer,
+                cache_mib_per_layer=round(pkg.qsa_row_cache_bytes(pkg.ATTN_A, ROW_CACHE_SLOTS) / 2**20, 1),
+                pages_n_slots=PAGES_CACHE_SLOTS, n_split=n_split, regimes=res)
 
 
 def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
@@ -352,12 +543,14 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
     return out, flops
 
 
-def correlated_rho() -> float:
-    """The AR(1) correlation of the correlated-selection workload."""
-    path = os.path.join(ROOT, "tests", "golden", "correlated_overlap.txt")
-    for line in open(path):
-        if line.startswith("rho "):
-            return float(line.split()[1])
+def correlated_rho(name: str = "correlated_overlap.txt") -> float:
+    """The AR(1) correlation of a correlated-selection workload (prefill:
+    correlated_overlap.txt; the 1M-token decode: correlated_overlap_decode.txt)."""
+    path = os.path.join(ROOT, "tests", "golden", name)
+    with open(path) as f:
+        for line in f:
+            if line.startswith("rho "):
+                return float(line.split()[1])
     raise RuntimeError(f"no rho in {path}")
 
 
@@ -660,7 +853,13 @@ def main():
                              "ms_per_layer": round(dec["ms_host"], 4),
                              "ms_per_layer_device_kv": round(dec["ms_dev1"], 4),
                              "kv_bytes_per_layer": 4 * 2048 * 2 * 2 * 256 * 2,
-                             "kv_gbs": round(4 * 2048 * 2 * 2 * 256 * 2 / (dec["ms_host"] * 1e-3) / 1e9, 1)},
+                             "kv_gbs": round(4 * 2048 * 2 * 2 * 256 * 2 / (dec["ms_host"] * 1e-3) / 1e9, 1),
+                             "row_cache": dict(workload="the layer's attention over those host-resident K/V rows "
+                                                        "over 32 consecutive decode steps (after 16 warm-up steps) "
+                                                        "whose selections come from AR(1)-correlated indexer queries"
+                                                        " (rho from tests/golden/correlated_overlap_decode.txt), "
+                                                        "without and with the HBM row cache; ms per step",
+                                               **dec["rcache"])},
         "breakdown_us_per_layer": {"scan_lists": round(dec["lists_ms"] * 1e3, 2),
                                    "select_attend_merge": round(dec["ms"] * 1e3 / DECODE["layers"]
                                                                 - dec["lists_ms"] * 1e3, 2),

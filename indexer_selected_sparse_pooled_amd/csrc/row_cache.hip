@@ -39,10 +39,12 @@ __global__ __launch_bounds__(256) void row_cache_step_kernel(unsigned char* cach
   }
 }
 
-// One work-group per query: every position of its token list.
+// Work-group (i, y): list positions 256y .. 256y + 255 of query i, one per
+// thread (a single round of dependent loads per position).
 __global__ __launch_bounds__(256) void row_cache_plan_kernel(AttendArgs a, unsigned char* cache, RowCacheLayout L,
                                                              int* src, int src_ld) {
   const int i = blockIdx.x;
+  const int p = int(blockIdx.y) * 256 + int(threadIdx.x);
   const int seq = a.q_seq ? a.q_seq[i] : 0;
   const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
   att::List<false> lv;
@@ -54,22 +56,21 @@ __global__ __launch_bounds__(256) void row_cache_plan_kernel(AttendArgs a, unsig
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
   const int Lq = lv.L < src_ld ? lv.L : src_ld;
+  if (p >= Lq) return;
   const uint32_t epoch = *reinterpret_cast<const uint32_t*>(cache);
   const uint64_t* tag = reinterpret_cast<const uint64_t*>(cache + L.off_tag);
   uint32_t* hit = reinterpret_cast<uint32_t*>(cache + L.off_hit);
   unsigned long long* claim = reinterpret_cast<unsigned long long*>(cache + L.off_claim);
-  for (int p = threadIdx.x; p < Lq; p += 256) {
-    const int tok = lv.tok(p);
-    const uint64_t key = uint64_t(int64_t(seq) * a.key_stride + tok) + 1u;
-    const int64_t c = int64_t((key - 1u) % uint64_t(L.n_slots));
-    if (tag[c] == key) {
-      hit[c] = epoch;
-      src[int64_t(i) * src_ld + p] = -int(c) - 1;
-    } else {
-      const uint32_t id = uint32_t(int64_t(i) * src_ld + p) + 1u;
-      atomicMax(claim + c, (static_cast<unsigned long long>(epoch) << 32) | id);
-      src[int64_t(i) * src_ld + p] = tok;
-    }
+  const int tok = lv.tok(p);
+  const uint64_t key = uint64_t(int64_t(seq) * a.key_stride + tok) + 1u;
+  const int64_t c = int64_t((key - 1u) % uint64_t(L.n_slots));
+  if (tag[c] == key) {
+    hit[c] = epoch;
+    src[int64_t(i) * src_ld + p] = -int(c) - 1;
+  } else {
+    const uint32_t id = uint32_t(int64_t(i) * src_ld + p) + 1u;
+    atomicMax(claim + c, (static_cast<unsigned long long>(epoch) << 32) | id);
+    src[int64_t(i) * src_ld + p] = tok;
   }
 }
 
@@ -101,7 +102,8 @@ hipError_t launch_row_cache_step(unsigned char* cache, const RowCacheLayout& L, 
 hipError_t launch_row_cache_plan(const AttendArgs& a, unsigned char* cache, const RowCacheLayout& L, int* src,
                                  int src_ld, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
-  hipLaunchKernelGGL(row_cache_plan_kernel, dim3(unsigned(a.nq)), dim3(256), 0, s, a, cache, L, src, src_ld);
+  const unsigned gy = unsigned((src_ld + 255) / 256);
+  hipLaunchKernelGGL(row_cache_plan_kernel, dim3(unsigned(a.nq), gy), dim3(256), 0, s, a, cache, L, src, src_ld);
   return hipGetLastError();
 }
 

@@ -45,3 +45,30 @@ def test_ar1_generator_statistics():
     assert abs(c - 0.94859) < 0.01
     x0 = qi.bf16_bits_to_f32(qi.ar1_normal_bf16(9, 3, 4000, 128, 0.0)).astype(np.float64)
     assert abs(np.mean(np.sum(x0[1:] * x0[:-1], axis=1) / 128)) < 0.01
+
+
+def _golden_decode():
+    vals = {}
+    for line in open(os.path.join(os.path.dirname(__file__), "golden", "correlated_overlap_decode.txt")):
+        if not line.startswith("#"):
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def test_decode_workload_overlap_is_the_pages_figure():
+    """The 1M-token decode workload (262,080 candidate blocks): the recorded
+    rho gives the pages' average overlap with the previous step, within the
+    stated 60-85% range, and the union of the last four steps covers more."""
+    g = _golden_decode()
+    assert abs(g["mean_overlap_previous"] - 0.72) <= 0.015
+    assert 0.60 <= g["min_overlap_previous"] and g["max_overlap_previous"] <= 0.85
+    assert g["mean_overlap_union4"] > g["mean_overlap_previous"]
+
+
+def test_decode_workload_overlap_on_a_sample():
+    """Recomputed with the oracle for 10 consecutive steps of sequence 2."""
+    from tests.golden import correlated_overlap_decode as cod
+    g = _golden_decode()
+    prev, _ = cod.overlaps(cod.selections(cod.pooled_keys(2), cod.queries(2, g["rho"], 10)))
+    assert abs(np.mean(prev) - 0.72) <= 0.05, np.mean(prev)
