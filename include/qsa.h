@@ -289,6 +289,30 @@ qsa_status qsa_index_topk(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_s
 
 size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx);
 
+/* --------------------------------------- A2 + A3 for a prefill chunk ----
+ * qsa_index_topk_prefill: the selections of qsa_index_scores followed by
+ * qsa_topk_blocks for a prefill chunk of the token-level indexer ("GLM-5.3
+ * 最適化 第2部", section "PCP": 4 heads x 64 dims, every earlier token scored,
+ * the top-2048 attended), bit for bit, without writing every score: a score
+ * pass over every s-th key sets a per-query threshold, the full pass keeps
+ * only the scores ranked at or above it, and the top-k is taken from those.
+ * A query for which that leaves fewer than topk candidates (or more than
+ * the workspace holds) gets its full scores in `scores` and the regular
+ * top-k; for every other query `scores` is not written.
+ * One sequence (keys as in qsa_index_scores with q_seq NULL), cfg with
+ * block 1, idx_heads 4, idx_dim 64 (bf16 or FP8 keys), 16 <= nq <= 65535,
+ * max_ctx <= 262144. Other arguments as in qsa_index_scores and
+ * qsa_topk_blocks.
+ *   ws (device) workspace of at least qsa_index_topk_prefill_workspace_bytes
+ *      (cfg, nq, max_ctx) bytes (0: not supported), contents ignored on
+ *      entry. Calls that share a workspace must not run concurrently. */
+qsa_status qsa_index_topk_prefill(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_ctx,
+                                  int32_t max_ctx, const qsa_bf16* q_idx, const float* w_idx,
+                                  const void* keys, float* scores, int64_t ld_scores,
+                                  int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                  qsa_stream_t stream);
+size_t qsa_index_topk_prefill_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx);
+
 /* --------------------------------------------- A2 + chunk lists of A3 ----
  * qsa_index_lists: the pooled-key scan that qsa_decode_layer issues first,
  * on its own: writes scores[i][b] for b < n_i (as qsa_index_scores) and, in

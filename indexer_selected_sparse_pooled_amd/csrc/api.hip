@@ -433,6 +433,66 @@ qsa_status qsa_topk_blocks(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_
   return finish(qsa::launch_topk(a, plan, s), s, "qsa_topk_blocks");
 }
 
+size_t qsa_index_topk_prefill_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx) {
+  if (!cfg || cfg->block <= 0 || cfg->topk <= 0 || nq <= 0 || max_ctx < 0) return 0;
+  const qsa::PrefillSelectPlan p = qsa::plan_prefill_select(nq, max_ctx, cfg->block, cfg->topk);
+  return p.supported ? p.ws_bytes : 0;
+}
+
+qsa_status qsa_index_topk_prefill(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_ctx, int32_t max_ctx,
+                                  const qsa_bf16* q_idx, const float* w_idx, const void* keys, float* scores,
+                                  int64_t ld_scores, int32_t* sel, int32_t* n_sel, void* ws, size_t ws_bytes,
+                                  qsa_stream_t stream) {
+  qsa_status st = check_sel_cfg(cfg);
+  if (st != QSA_OK) return st;
+  if (cfg->block != 1 || cfg->idx_dim != 64 || cfg->idx_heads != 4)
+    return fail(QSA_ERR_UNSUPPORTED, "qsa_index_topk_prefill: only the 4-head, 64-d token-level indexer");
+  if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
+  if (nq == 0) return QSA_OK;
+  if (nq < 16 || nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "qsa_index_topk_prefill: nq %d not in [16, 65535]", nq);
+  if (!q_ctx || !q_idx || !w_idx || !scores || !sel || !n_sel) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q_idx) || !aligned16(scores) || !aligned16(sel))
+    return fail(QSA_ERR_ARG, "q_idx, scores and sel must be 16-byte aligned");
+  const int64_t nmax = int64_t(max_ctx) / cfg->block;
+  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx = %lld", (long long)ld_scores, (long long)nmax);
+  st = check_keys(cfg, keys, 0, nmax, false);
+  if (st != QSA_OK) return st;
+  const qsa::PrefillSelectPlan plan = qsa::plan_prefill_select(nq, max_ctx, cfg->block, cfg->topk);
+  if (!plan.supported) return fail(QSA_ERR_UNSUPPORTED, "qsa_index_topk_prefill: more than 262144 keys per query");
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+  if (!aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, nullptr, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::ScoreArgs a{};
+  a.q_ctx = q_ctx;
+  a.max_ctx = max_ctx;
+  a.nq = nq;
+  a.block = cfg->block;
+  a.idx_dim = cfg->idx_dim;
+  a.idx_heads = cfg->idx_heads;
+  a.q_idx = q_idx;
+  a.w_idx = w_idx;
+  a.keys = keys;
+  a.key_fp8 = cfg->key_format == QSA_KEYS_FP8;
+  a.scores = scores;
+  a.ld = ld_scores;
+  qsa::TopkArgs t{};
+  t.q_ctx = q_ctx;
+  t.max_ctx = max_ctx;
+  t.nq = nq;
+  t.block = cfg->block;
+  t.topk = cfg->topk;
+  t.scores = scores;
+  t.ld = ld_scores;
+  t.sel = sel;
+  t.n_sel = n_sel;
+  return finish(qsa::launch_prefill_select(a, t, plan, ws, s), s, "qsa_index_topk_prefill");
+}
+
 size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_t max_ctx) {
   if (!cfg || nq <= 0 || max_ctx < 0) return 0;
   return qsa::plan_index_topk(nq, max_ctx, cfg->topk).ws_bytes;

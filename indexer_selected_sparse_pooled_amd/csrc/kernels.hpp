@@ -44,6 +44,9 @@ struct AppendArgs {
 };
 hipError_t launch_append(const AppendArgs& a, hipStream_t s);
 
+// list-mode counters, one per 128-byte line: every work-group of a query
+// row adds to its queries' counters
+constexpr int kCountStride = 32;
 struct ScoreArgs {
   const int* q_seq;   // nullable
   const int* q_ctx;
@@ -59,8 +62,17 @@ struct ScoreArgs {
   int key_fp8;
   float* scores;
   int64_t ld;
+  // prefill chunk of variant B only (scores_gemm_b):
+  int64_t tok_step;        // column t scores key t * tok_step (0 or 1: every key)
+  const uint32_t* only;    // nullable: score only the queries flagged here
+  const uint64_t* theta;   // list mode: per query, the rank64-style threshold (key << 32 | index)
+  uint64_t* lists;         // list mode: [nq][list_cap] entries (score bits << 32) | index, unordered
+  uint32_t* counts;        // list mode: entries reserved for query q at counts[q * kCountStride] (may exceed list_cap)
+  int list_cap;
 };
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t s);
+// the variant B chunk GEMM over n_cols columns (keys t * tok_step): scores, or lists
+hipError_t launch_scores_gemm_b(const ScoreArgs& a, int64_t n_cols, bool lists, hipStream_t s);
 
 struct TopkArgs {
   const int* q_ctx;
@@ -73,6 +85,7 @@ struct TopkArgs {
   int* sel;
   int* n_sel;
   void* ws;
+  const uint32_t* only;  // nullable: select only for the queries flagged here
 };
 // Workspace layout of the chunked (large-context) path.
 struct TopkPlan {
@@ -87,6 +100,20 @@ struct TopkPlan {
 };
 TopkPlan plan_topk(int nq, int max_ctx, int block, int topk);
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t s);
+
+// A2 + A3 of a variant B prefill chunk without materialised scores
+// (prefill_select.hip); the scores buffer is used only by flagged queries.
+struct PrefillSelectPlan {
+  bool supported;  // keys per query within the list select's bitmap, topk within half the list
+  int64_t step;    // sample stride
+  int n_samp;      // sample columns per query
+  int cap;         // list capacity per query
+  TopkPlan tp;     // the regular top-k for flagged queries
+  size_t off_samp, off_theta, off_counts, off_fail, off_lists, off_topk, ws_bytes;
+};
+PrefillSelectPlan plan_prefill_select(int nq, int max_ctx, int block, int topk);
+hipError_t launch_prefill_select(const ScoreArgs& sa, const TopkArgs& ta, const PrefillSelectPlan& p, void* ws,
+                                 hipStream_t s);
 
 struct AttendArgs {
   const int* q_seq;  // nullable

@@ -14,6 +14,7 @@
 #include "common.hpp"
 #include "fp8.hpp"
 #include "kernels.hpp"
+#include "select.hpp"
 
 namespace qsa {
 namespace {
@@ -299,13 +300,26 @@ __global__ __launch_bounds__(256) void scores_gemm_a_fp8(ScoreArgs a) {
 
 // Prefill chunk, variant B: 4 heads x 64 dims, score = sum_h w_h relu(dot_h).
 // kFp8: B operands converted from E4M3 codes, the key scale applied last.
-template <bool kFp8>
-__global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
-  __shared__ int red[1];
+constexpr int kListBatches = 8;  // list mode: 8 x 128 columns per work-group
+constexpr int kStage = 64;       // list mode: LDS entries staged per query row
+
+template <bool kFp8, bool kList>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void scores_gemm_b(ScoreArgs a) {
+  __shared__ int red[2];
   const int q0 = blockIdx.y * 64;
-  const int64_t b0 = int64_t(blockIdx.x) * 128;
-  const int64_t nmax = wg_max_n(a, q0, red);
-  if (b0 >= nmax) return;
+  if (a.only) {  // only the tiles that hold a flagged query
+    if (threadIdx.x == 0) red[1] = 0;
+    __syncthreads();
+    if (threadIdx.x < 64 && q0 + int(threadIdx.x) < a.nq && a.only[q0 + threadIdx.x]) red[1] = 1;
+    __syncthreads();
+    if (red[1] == 0) return;
+  }
+  const int64_t step = a.tok_step > 0 ? a.tok_step : 1;
+  // a work-group covers 128 columns, or kListBatches x 128 in list mode
+  const int64_t b00 = int64_t(blockIdx.x) * 128 * (kList ? kListBatches : 1);
+  const int64_t nmax = (wg_max_n(a, q0, red) + step - 1) / step;  // in units of tok_step
+  if (b00 >= nmax) return;
+  [[maybe_unused]] __shared__ uint64_t stage[kList ? 64 : 1][kList ? kStage : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, kq = lane >> 4;
   const int qa_row = q0 + 16 * wave + r;
@@ -320,51 +334,173 @@ __global__ __launch_bounds__(256) void scores_gemm_b(ScoreArgs a) {
     }
   int64_t nrow[4];
   float wr[4][4];
+  [[maybe_unused]] uint64_t th[4];
 #pragma unroll
   for (int e = 0; e < 4; e++) {
     const int q = q0 + 16 * wave + 4 * kq + e;
-    nrow[e] = q < a.nq ? clamp_ctx(a.q_ctx[q], a.max_ctx) / a.block : 0;
+    const int64_t n = q < a.nq ? clamp_ctx(a.q_ctx[q], a.max_ctx) / a.block : 0;
+    nrow[e] = (n + step - 1) / step;
+    if (a.only && q < a.nq && !a.only[q]) nrow[e] = 0;
 #pragma unroll
     for (int h = 0; h < 4; h++) wr[e][h] = q < a.nq ? a.w_idx[int64_t(q) * 4 + h] : 0.f;
+    if constexpr (kList) th[e] = q < a.nq ? a.theta[q] : ~0ull;
   }
-  for (int nt = 0; nt < 8; nt++) {
-    const int64_t tok = b0 + 16 * nt + r;
-    if (b0 + 16 * nt >= nmax) break;
-    bf16x8 kb[2];
-    float ksc = 1.f;
+  // Column tiles t = 0 .. T-1 of the span (tokens b00 + 16 t + r); the key
+  // rows of tile t + 2 are fetched before tile t is computed, so loads stay
+  // two tiles ahead of the MFMAs. Columns past nmax read a valid row (the
+  // last) and are ignored.
+  struct KRaw {
+    u32x4 w[2];
+    float sc;
+  };
+  auto fetch = [&](int t) {
+    KRaw k;
+    const int64_t tok = b00 + 16 * t + r;
+    const int64_t kt = (tok < nmax ? tok : nmax - 1) * step;  // the key row of column tok
+    k.sc = 1.f;
     if constexpr (kFp8) {
-      const int64_t tc = tok < nmax ? tok : nmax - 1;
       const uint8_t* kb8 = static_cast<const uint8_t*>(a.keys);
-      ksc = *reinterpret_cast<const float*>(kb8 + fp8_scale_off(tc, 64));
-#pragma unroll
-      for (int ks = 0; ks < 2; ks++)
-        kb[ks] = e4m3x8_bf16(*reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(tc, 64) + 32 * ks + 8 * kq));
-    } else {
+      k.sc = *reinterpret_cast<const float*>(kb8 + fp8_scale_off(kt, 64));
 #pragma unroll
       for (int ks = 0; ks < 2; ks++) {
-        u32x4 w = tok < nmax ? ld16(static_cast<const uint16_t*>(a.keys) + tok * 64 + 32 * ks + 8 * kq)
-                             : u32x4{0u, 0u, 0u, 0u};
-        kb[ks] = as_bf16x8(w);
+        const u32x2 c = *reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(kt, 64) + 32 * ks + 8 * kq);
+        k.w[ks] = u32x4{c[0], c[1], 0u, 0u};
       }
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < 2; ks++) k.w[ks] = ld16(static_cast<const uint16_t*>(a.keys) + kt * 64 + 32 * ks + 8 * kq);
     }
-    float s[4] = {0.f, 0.f, 0.f, 0.f};
+    return k;
+  };
+  auto compute = [&](const KRaw& k, float (&sc)[4]) {
+    bf16x8 kb[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ks++) {
+      if constexpr (kFp8)
+        kb[ks] = e4m3x8_bf16(u32x2{k.w[ks][0], k.w[ks][1]});
+      else
+        kb[ks] = as_bf16x8(k.w[ks]);
+    }
+    float acc_s[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int h = 0; h < 4; h++) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], kb[0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], kb[1], acc, 0, 0, 0);
 #pragma unroll
-      for (int e = 0; e < 4; e++) s[e] += wr[e][h] * fmaxf(acc[e], 0.f);
+      for (int e = 0; e < 4; e++) acc_s[e] += wr[e][h] * fmaxf(acc[e], 0.f);
     }
 #pragma unroll
+    for (int e = 0; e < 4; e++) sc[e] = acc_s[e] * k.sc;
+  };
+  constexpr int kTiles = 8 * (kList ? kListBatches : 1);
+  const int T = int((nmax - b00 + 15) / 16 < kTiles ? (nmax - b00 + 15) / 16 : kTiles);  // >= 1
+  [[maybe_unused]] int staged[4] = {0, 0, 0, 0};  // list mode: uniform in the lane group
+  // list mode: the threshold as a float and an index, 32-bit counts, and the
+  // lane group's ballot masks
+  [[maybe_unused]] float thf[4];
+  [[maybe_unused]] int thi[4], nrow32[4];
+  [[maybe_unused]] const uint64_t gmask = 0xFFFFull << (16 * kq);
+  [[maybe_unused]] const uint64_t gbelow = kq == 0 ? 0ull : (~0ull >> (64 - 16 * kq));
+  if constexpr (kList) {
+#pragma unroll
     for (int e = 0; e < 4; e++) {
-      const int q = q0 + 16 * wave + 4 * kq + e;
-      if (tok < nrow[e]) a.scores[int64_t(q) * a.ld + tok] = s[e] * ksc;
+      const uint32_t tk = uint32_t(th[e] >> 32);
+      // the float whose order key is tk (tk >= 0x80000000: non-negative)
+      thf[e] = __uint_as_float(tk & 0x80000000u ? tk & 0x7FFFFFFFu : ~tk);
+      const uint64_t ti = th[e] & 0xFFFFFFFFull;
+      thi[e] = ti > 0x7FFFFFFFull ? 0x7FFFFFFF : int(ti);
+      nrow32[e] = int(nrow[e]);
+      if (tk == 0xFFFFFFFFu) nrow32[e] = 0;  // keep none
+      if (tk == 0u) { thf[e] = -INFINITY; thi[e] = 0x7FFFFFFF; }  // keep every score
     }
+  }
+  // list mode: query row 16 wave + 4 kq + e belongs to the 16 lanes of group
+  // kq of one wave; they stage its kept entries in LDS (ballot prefix, no
+  // atomics) and, when the stage is full and after the span, reserve list
+  // slots with one atomic and copy
+  [[maybe_unused]] auto flush = [&](int e) {
+    const int q = q0 + 16 * wave + 4 * kq + e;
+    const int row = 16 * wave + 4 * kq + e;
+    uint32_t base = 0u;
+    if (r == 0) base = atomicAdd(a.counts + int64_t(q) * kCountStride, uint32_t(staged[e]));
+    base = uint32_t(__shfl(int(base), 16 * kq));
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int jj = 0; jj < kStage / 16; jj++) {  // straight-line: at most kStage entries
+      const int j = r + 16 * jj;
+      if (j < staged[e] && base + uint32_t(j) < uint32_t(a.list_cap))
+        a.lists[int64_t(q) * a.list_cap + base + j] = stage[row][j];
+    }
+    __builtin_amdgcn_wave_barrier();
+    staged[e] = 0;
+  };
+  // per-tile work on tile t's scores: list staging or score stores
+  auto work = [&](int t, const float (&sc)[4]) {
+    const int64_t tok = b00 + 16 * t + r;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      if constexpr (kList) {
+        // keep the scores ranked at least as high as the query's threshold
+        // (score descending, index ascending; float order equals key order)
+        const int tk32 = int(tok);
+        const bool keep = tk32 < nrow32[e] && (sc[e] > thf[e] || (sc[e] == thf[e] && tk32 <= thi[e]));
+        const uint64_t bal = __ballot(keep);
+        const int c = __popcll(bal & gmask);                          // kept in the lane's group
+        const int before = __popcll(bal & lanes_below()) - __popcll(bal & gbelow);  // ... ahead of the lane
+        if (staged[e] + c > kStage) flush(e);  // rare; uniform in the group
+        if (keep)
+          stage[16 * wave + 4 * kq + e][staged[e] + before] =
+              (uint64_t(__float_as_uint(sc[e])) << 32) | uint64_t(uint32_t(tk32));
+        staged[e] += c;
+      } else {
+        const int q = q0 + 16 * wave + 4 * kq + e;
+        if (tok < nrow[e]) a.scores[int64_t(q) * a.ld + tok] = sc[e];
+      }
+    }
+  };
+  // two fetch buffers with fixed roles (unrolled by two, no copies of
+  // registers still being loaded); with T odd the last step computes the
+  // tile past the span's keys, whose columns are all past nmax and ignored
+  KRaw ka = fetch(0);
+  KRaw kb = fetch(T > 1 ? 1 : 0);
+  for (int t = 0; t < T; t += 2) {
+    float sc[4];
+    compute(ka, sc);
+    ka = fetch(t + 2 < T ? t + 2 : T - 1);
+    __builtin_amdgcn_sched_barrier(0);  // keep the fetches in program order
+    work(t, sc);
+    compute(kb, sc);
+    kb = fetch(t + 3 < T ? t + 3 : T - 1);
+    __builtin_amdgcn_sched_barrier(0);
+    work(t + 1, sc);
+  }
+  if constexpr (kList) {
+#pragma unroll
+    for (int e = 0; e < 4; e++)
+      if (staged[e] > 0) flush(e);
   }
 }
 
 }  // namespace
+
+hipError_t launch_scores_gemm_b(const ScoreArgs& a, int64_t n_cols, bool lists, hipStream_t s) {
+  if (a.nq <= 0 || n_cols <= 0) return hipSuccess;
+  const int64_t span = 128 * (lists ? kListBatches : 1);
+  dim3 grid(unsigned((n_cols + span - 1) / span), unsigned((a.nq + 63) / 64));
+  if (lists) {
+    if (a.key_fp8)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<true, true>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (a.key_fp8)
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<true, false>), grid, dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<false, false>), grid, dim3(256), 0, s, a);
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
@@ -404,9 +540,9 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
     if (chunk) {
       dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
       if (a.key_fp8)
-        hipLaunchKernelGGL(scores_gemm_b<true>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<true, false>), grid, dim3(256), 0, s, a);
       else
-        hipLaunchKernelGGL(scores_gemm_b<false>, grid, dim3(256), 0, s, a);
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<false, false>), grid, dim3(256), 0, s, a);
     } else {
       dim3 grid(unsigned((nmax + 511) / 512), unsigned(a.nq));
       if (a.key_fp8)

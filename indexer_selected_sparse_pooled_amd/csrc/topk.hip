@@ -99,6 +99,7 @@ __device__ __forceinline__ uint32_t* theta_of(const TopkArgs& a, const TopkPlan&
 __global__ __launch_bounds__(256) void topk_sample(TopkArgs a, TopkPlan p) {
   __shared__ RegSelLds<kNTc> sh;
   const int i = blockIdx.x, tid = threadIdx.x;
+  if (a.only && !a.only[i]) return;  // another path selected this query
   const int n = query_n(a, i);
   if (n <= a.topk || n <= p.direct_max) return;
   const float* sc = a.scores + int64_t(i) * a.ld;
@@ -119,6 +120,7 @@ __global__ __launch_bounds__(256) void topk_sample(TopkArgs a, TopkPlan p) {
 __global__ __launch_bounds__(256) void topk_chunks(TopkArgs a, TopkPlan p) {
   __shared__ ChunkLds sh;
   const int i = blockIdx.y, c = blockIdx.x, tid = threadIdx.x;
+  if (a.only && !a.only[i]) return;  // another path selected this query
   const int n = query_n(a, i);
   if (n <= a.topk || n <= p.direct_max) return;  // the final kernel handles these alone
   const int lo = c * kChunk;
@@ -196,6 +198,7 @@ __device__ __forceinline__ void load16(const float* p, bool vec, float (&v)[kRc]
 __global__ __launch_bounds__(256) void topk_chunks_threshold(TopkArgs a, TopkPlan p) {
   __shared__ int wsum[kCpw][kNTc / 64];
   const int i = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.only && !a.only[i]) return;  // another path selected this query
   const int n = query_n(a, i);
   if (n <= a.topk || n <= p.direct_max) return;
   const int c0 = blockIdx.x * kCpw;
@@ -262,6 +265,7 @@ __global__ __launch_bounds__(NT) void topk_final(TopkArgs a, TopkPlan p) {
   constexpr int kCap = NT * kRf;
   __shared__ FinalLds<NT> sh;
   const int i = blockIdx.x, tid = threadIdx.x;
+  if (a.only && !a.only[i]) return;  // another path selected this query
   const int n = query_n(a, i);
   const int topk = a.topk;
   int* sel = a.sel + int64_t(i) * topk;
@@ -345,6 +349,7 @@ __global__ __launch_bounds__(NT) void topk_final_threshold(TopkArgs a, TopkPlan 
   constexpr int kCap = NT * kRf;
   __shared__ FinalLds<NT> sh;
   const int i = blockIdx.x, tid = threadIdx.x;
+  if (a.only && !a.only[i]) return;  // another path selected this query
   const int n = query_n(a, i);
   const int topk = a.topk;
   if (n <= topk || n <= kCap) return;  // topk_final selects these

@@ -111,6 +111,7 @@ class PrefillBuffers:
     o_bf16: torch.Tensor
     lse: torch.Tensor
     tiles: list
+    sel_ws: torch.Tensor = None  # qsa_index_topk_prefill's workspace where that call applies
 
 
 def history_tiles(ctx_max: int, tile: int):
@@ -133,16 +134,24 @@ def prefill_buffers(sel_cfg, attn_cfg, nq, max_ctx, tile, device="cuda") -> Pref
         o_bf16=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, dtype=torch.bfloat16, device=device),
         lse=torch.empty(nq, attn_cfg.hq, **f32),
         tiles=tiles,
+        sel_ws=(qsa.index_topk_prefill_workspace(sel_cfg, nq, max_ctx, device)
+                if sel_cfg.block == 1 and sel_cfg.idx_heads == 4 and nq >= 16 else None),
     )
 
 
 def prefill_chunk(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: PrefillBuffers,
-                  w_idx=None, stream=None) -> None:
+                  w_idx=None, stream=None, fused_select=True) -> None:
     """A chunk of queries of one sequence: selection, then the history tiles
-    in the outer loop (one attention call per tile), then the merge."""
-    qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=None, w_idx=w_idx,
-                         stream=stream)
-    qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
+    in the outer loop (one attention call per tile), then the merge. The
+    token-level indexer selects in one call (qsa_index_topk_prefill) unless
+    fused_select is False."""
+    if fused_select and bufs.sel_ws is not None:
+        qsa.qsa_index_topk_prefill(sel_cfg, q_ctx, max_ctx, q_idx, w_idx, keys, bufs.scores, bufs.sel, bufs.n_sel,
+                                   bufs.sel_ws, stream=stream)
+    else:
+        qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=None, w_idx=w_idx,
+                             stream=stream)
+        qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
     for t, (a, b) in enumerate(bufs.tiles):
         qsa.qsa_sparse_prefill(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, a, b,
                                bufs.o_tiles[t], bufs.lse_tiles[t], stream=stream)

@@ -76,6 +76,8 @@ _SIGS = {
     "qsa_topk_workspace_bytes": [_vp, _i32, _i32],
     "qsa_index_topk": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
     "qsa_index_topk_workspace_bytes": [_vp, _i32, _i32],
+    "qsa_index_topk_prefill": [_vp, _i32, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _sz, _vp],
+    "qsa_index_topk_prefill_workspace_bytes": [_vp, _i32, _i32],
     "qsa_index_lists": [_vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _i64, _vp, _sz, _vp],
     "qsa_decode_layer": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i32,
                          _vp, _vp, _vp, _vp, _sz, _vp],
@@ -92,7 +94,7 @@ _SIGS = {
     "qsa_last_error": [],
     "qsa_version": [],
 }
-_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_fp8_keys_bytes": _i64,
+_RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_index_topk_prefill_workspace_bytes": _sz, "qsa_fp8_keys_bytes": _i64,
         "qsa_decode_layer_workspace_bytes": _sz,
         "qsa_row_cache_bytes": _sz, "qsa_decode_cached_plan_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
         "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
@@ -234,6 +236,32 @@ def qsa_index_scores(cfg, q_ctx, max_ctx, q_idx, keys, scores, q_seq=None, w_idx
         ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
         _dev(q_idx, _BF16, "q_idx"), _dev(w_idx, _F32, "w_idx"), kp, kss, _dev(scores, _F32, "scores"),
         scores.stride(0), _stream(stream)))
+
+
+def qsa_index_topk_prefill_workspace_bytes(cfg, nq, max_ctx) -> int:
+    return int(lib().qsa_index_topk_prefill_workspace_bytes(ctypes.byref(cfg), nq, max_ctx))
+
+
+def index_topk_prefill_workspace(cfg, nq, max_ctx, device="cuda"):
+    """A workspace tensor for qsa_index_topk_prefill, or None where that call
+    does not apply."""
+    n = qsa_index_topk_prefill_workspace_bytes(cfg, nq, max_ctx)
+    return torch.empty(n, dtype=torch.uint8, device=device) if n else None
+
+
+def qsa_index_topk_prefill(cfg, q_ctx, max_ctx, q_idx, w_idx, keys, scores, sel, n_sel, ws, stream=None):
+    """The selections of qsa_index_scores + qsa_topk_blocks for a prefill
+    chunk of one sequence (token-level 4-head indexer), without writing every
+    score. keys: [1, n_keys, 64] bf16 or an FP8 page buffer; ws:
+    index_topk_prefill_workspace(...)."""
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(q_idx, "q_idx", 3)
+    _rowmajor_tail(scores, "scores", 1)
+    kp, _ = _keys_arg(cfg, keys, max_ctx, "qsa_index_topk_prefill")
+    _check("qsa_index_topk_prefill", lib().qsa_index_topk_prefill(
+        ctypes.byref(cfg), nq, _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q_idx, _BF16, "q_idx"),
+        _dev(w_idx, _F32, "w_idx"), kp, _dev(scores, _F32, "scores"), scores.stride(0),
+        _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), _dev(ws, _U8, "ws"), ws.numel(), _stream(stream)))
 
 
 def qsa_topk_workspace_bytes(cfg, nq, max_ctx) -> int:
