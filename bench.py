@@ -661,13 +661,15 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
                                                                      w_idx=w), r)
             t_tk = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, pb.scores, pb.sel, pb.n_sel,
                                                                     pb.ws), r)
+            t_sel = time_launches(torch, lambda: pkg.qsa_index_topk_prefill(pkg.SEL_B, q_ctx, L, q_idx, w, keys,
+                                                                            pb.scores, pb.sel, pb.n_sel, pb.sel_ws), r)
             a0, a1 = pb.tiles[0]
             t_at = time_launches(torch, lambda: pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv, pb.sel,
                                                                        pb.n_sel, a0, a1, pb.o_tiles[0],
                                                                        pb.lse_tiles[0]), r)
             att_tflops = flops["attention"] / (t_at * 1e-3) / 1e12
-            pre["breakdown_us"] = {"scores": round(t_sc * 1e3, 1), "topk": round(t_tk * 1e3, 1),
-                                   "attend": round(t_at * 1e3, 1)}
+            pre["breakdown_us"] = {"select": round(t_sel * 1e3, 1), "attend": round(t_at * 1e3, 1),
+                                   "separate_calls": {"scores": round(t_sc * 1e3, 1), "topk": round(t_tk * 1e3, 1)}}
             pre["attend_tflops"] = round(att_tflops, 1)
         if tile == MLA["tiles"][0]:  # the same chunk over FP8 sparse-MLA rows
             rows8 = torch.empty(1, L, 656, dtype=torch.uint8, device=dev)
