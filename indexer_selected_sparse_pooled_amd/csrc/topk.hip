@@ -92,6 +92,11 @@ __device__ __forceinline__ uint32_t* theta_of(const TopkArgs& a, const TopkPlan&
   return reinterpret_cast<uint32_t*>(reinterpret_cast<uint64_t*>(a.ws) + size_t(a.nq) * p.n_chunks * (p.list_len + 1)) +
          i;
 }
+// filter mode: how many scores equal to theta query i takes (0: none, its
+// selection is complete without them)
+__device__ __forceinline__ int* ties_of(const TopkArgs& a, const TopkPlan& p, int i) {
+  return reinterpret_cast<int*>(theta_of(a, p, 0) + a.nq) + i;
+}
 
 // Filter mode, step 0: the threshold of each chunked query. grid = nq, 256
 // threads; thread t reads the 16 consecutive scores of run t, runs spread
@@ -257,6 +262,80 @@ __global__ __launch_bounds__(256) void topk_chunks_threshold(TopkArgs a, TopkPla
   }
 }
 
+// Filter mode, ties (after topk_final_threshold): for a query whose top-k
+// holds every score above theta and the `need` smallest-index scores equal
+// to it, chunk c writes its share in index order at its offset: the chunks
+// before it contribute all their scores above theta and, in chunk order, the
+// equal ones until `need` are taken. grid = (n_chunks, nq), 256 threads.
+__global__ __launch_bounds__(kNTc) void topk_ties(TopkArgs a, TopkPlan p) {
+  __shared__ int wsum[kNTc / 64];
+  __shared__ int hdr[2];
+  const int i = blockIdx.y, c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (a.only && !a.only[i]) return;  // another path selected this query
+  const int n = query_n(a, i);
+  if (n <= a.topk || n <= p.final_threads * kRf) return;  // not a filter-path query
+  const int need = *ties_of(a, p, i);
+  if (need <= 0) return;
+  const int lo = c * kChunk;
+  if (lo >= n) return;
+  const uint64_t* cnts = bound_of(a, p, i);
+  if (tid == 0) {
+    int off = 0, eq_before = 0;
+    for (int j = 0; j < c; j++) {
+      const int g = int(uint32_t(cnts[j]) & 0xFFFFu), e = int(uint32_t(cnts[j] >> 32));
+      const int take = need - eq_before < e ? (need - eq_before > 0 ? need - eq_before : 0) : e;
+      off += g + take;
+      eq_before += e;
+    }
+    const int e_c = int(uint32_t(cnts[c] >> 32));
+    const int quota = need - eq_before < e_c ? (need - eq_before > 0 ? need - eq_before : 0) : e_c;
+    hdr[0] = off;
+    hdr[1] = quota;
+  }
+  __syncthreads();
+  const int off = hdr[0], quota = hdr[1];
+  const uint32_t th = *theta_of(a, p, i);
+  const float* row = a.scores + int64_t(i) * a.ld;
+  const int j0 = lo + kRc * tid;
+  uint32_t key[kRc];
+  int ne = 0;
+#pragma unroll
+  for (int r = 0; r < kRc; r++) {
+    key[r] = j0 + r < n ? order_key(row[j0 + r]) : 0u;
+    ne += key[r] == th ? 1 : 0;
+  }
+  // rank of the lane's first equal score among the chunk's equal scores
+  const int ie = wave_incl_sum(ne);
+  if (lane == 63) wsum[wave] = ie;
+  __syncthreads();
+  int e_rank = ie - ne;
+#pragma unroll
+  for (int w = 0; w < kNTc / 64; w++) e_rank += w < wave ? wsum[w] : 0;
+  __syncthreads();
+  bool take[kRc];
+  int ns = 0;
+#pragma unroll
+  for (int r = 0; r < kRc; r++) {
+    const bool eqk = key[r] == th;
+    take[r] = key[r] > th || (eqk && e_rank < quota);
+    e_rank += eqk ? 1 : 0;
+    ns += take[r] ? 1 : 0;
+  }
+  const int is = wave_incl_sum(ns);
+  if (lane == 63) wsum[wave] = is;
+  __syncthreads();
+  int pos = off + is - ns;
+#pragma unroll
+  for (int w = 0; w < kNTc / 64; w++) pos += w < wave ? wsum[w] : 0;
+  int* sel = a.sel + int64_t(i) * a.topk;
+#pragma unroll
+  for (int r = 0; r < kRc; r++)
+    if (take[r]) {
+      if (pos < a.topk) sel[pos] = j0 + r;
+      pos++;
+    }
+}
+
 // Selection per query. grid = nq, NT threads; NT * kRf covers the union (or
 // every candidate of a directly selected query).
 template <int NT>
@@ -361,6 +440,7 @@ __global__ __launch_bounds__(NT) void topk_final_threshold(TopkArgs a, TopkPlan 
   const uint32_t th = *theta_of(a, p, i);
   const uint64_t* lists = list_of(a, p, i, 0);
   const uint64_t* cnts = bound_of(a, p, i);
+  if (tid == 0) *ties_of(a, p, i) = 0;
   // counts above / equal to theta: thread t < nch holds chunk t's
   const uint64_t cw = tid < nch ? cnts[tid] : 0ull;
   const int gt = int(uint32_t(cw)), eq = int(uint32_t(cw >> 32));
@@ -394,9 +474,11 @@ __global__ __launch_bounds__(NT) void topk_final_threshold(TopkArgs a, TopkPlan 
   int* const out = sel;
   auto emit = [out](int pos, int j) { out[pos] = j; };
   const int n_eq = block_sum<kNTf>(eq, sh.rs);
-  if (!overflow && n_gt < topk && topk <= n_gt + n_eq) {
-    // every score above theta, then the smallest indices among those equal to it
-    stream_compact<kNTf>(gkey_at, n, th, topk - n_gt, sh.st, emit);
+  if (n_gt < topk && topk <= n_gt + n_eq) {
+    // every score above theta, then the smallest indices among those equal
+    // to it: written chunk by chunk by topk_ties (the counts fix each
+    // chunk's share and offset)
+    if (tid == 0) *ties_of(a, p, i) = topk - n_gt;
     return;
   }
   // exact select over every score, read from memory
@@ -439,7 +521,7 @@ TopkPlan plan_topk(int nq, int max_ctx, int block, int topk) {
         p.direct_max = kSmallMax;
       }
       // lists, one word per chunk, one threshold per query
-      p.ws_bytes = size_t(nq) * size_t(nch) * (size_t(cap) + 1) * 8 + (size_t(nq) * 4 + 7) / 8 * 8;
+      p.ws_bytes = size_t(nq) * size_t(nch) * (size_t(cap) + 1) * 8 + size_t(nq) * 8;  // + theta, ties
       return p;
     }
   }
@@ -483,7 +565,10 @@ hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t s) {
       hipLaunchKernelGGL(topk_final_threshold<256>, dim3(unsigned(a.nq)), dim3(256), 0, s, a, p);
     else
       hipLaunchKernelGGL(topk_final_threshold<1024>, dim3(unsigned(a.nq)), dim3(1024), 0, s, a, p);
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_ties, dim3(unsigned(p.n_chunks), unsigned(a.nq)), dim3(kNTc), 0, s, a, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   // direct queries (and, outside filter mode, every query)
