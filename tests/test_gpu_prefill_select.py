@@ -7,7 +7,9 @@ other GPU tests; here a few rows are also checked against the oracle
 directly). Cases: mixed contexts (empty, at most topk, at most the list
 capacity, long), queries whose head weights are all negative (their best
 scores are exact zeros, so the top-2048 is decided by index among ties),
-FP8 keys, repeated calls on one workspace, HIP-graph replays, and inputs
+FP8 keys, a chunk whose queries all fit the list and the largest context
+the path takes (262,144 keys), repeated calls on one workspace, HIP-graph
+replays, and inputs
 planted so that the sampled threshold fails both ways: sampled keys that
 score far above the rest (too few candidates) and unsampled keys that do
 (too many). Those queries must take the regular path, and only their score
@@ -193,3 +195,21 @@ def test_argument_errors(Q):
         pkg.qsa_index_topk_prefill(pkg.SEL_B, qc.i32([1000] * 8), 1000, q_idx, w, keys, scores, sel, n_sel, ws)
     assert pkg.qsa_index_topk_prefill_workspace_bytes(pkg.SEL_B, 16, 300000) == 0
     assert pkg.qsa_index_topk_prefill_workspace_bytes(pkg.SEL_B, 16, 131072) > 0
+
+
+@pytest.mark.parametrize("max_ctx,ctxs", [
+    (3000, [3000 - 37 * i for i in range(16)]),             # every query's keys fit the list (stride 1)
+    (262144, [262144 - 1000 * i for i in range(15)] + [9000]),  # the path's largest context (full bitmap)
+])
+def test_context_extremes(Q, max_ctx, ctxs):
+    pkg = Q
+    nq = len(ctxs)
+    _print_case("prefill_select_extremes", max_ctx=max_ctx, nq=nq)
+    keys, q_idx, w = _inputs(75, nq, max_ctx, (1,))
+    fused, ref = _both(pkg, pkg.SEL_B, ctxs, max_ctx, qc.to_dev(q_idx), torch.tensor(w, device="cuda"),
+                       qc.to_dev(keys[None]))
+    _assert_same(fused, ref)
+    assert np.all(np.isnan(fused[2])), "a query took the regular path"
+    i = nq - 1
+    sc = orc.index_scores_relu(q_idx[i], w[i], keys, ctxs[i])
+    qc.check_selection(fused[0][i], fused[1][i], sc, ctxs[i], 1, TOPK)
