@@ -767,8 +767,34 @@ def cpu_baseline(qi, orc, bm):
         o, lse = orc.attend(q, k_rows, v_rows, rows, 1.0 / 16)
     dt = time.perf_counter() - t0
     unit_s = dt / reps
+
+    def unit():
+        s = orc.index_scores(q_idx, pooled, L // 4)
+        toks = orc.selected_tokens(orc.select_blocks(s, L, 4, 512), L, 4)
+        orc.attend(q, k_rows, v_rows, np.array([row_of[int(t)] for t in toks]), 1.0 / 16)
+
+    # the same unit on one thread
+    unit_1t = None
+    try:
+        from threadpoolctl import threadpool_limits
+        with threadpool_limits(limits=1):
+            t1 = time.perf_counter()
+            for _ in range(4):
+                unit()
+            unit_1t = (time.perf_counter() - t1) / 4
+    except Exception:  # pragma: no cover
+        pass
+    cpu_model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
     return dict(value=1.0 / (unit_s * DECODE["batch"] * DECODE["layers"]), unit="steps/s", cores=int(cores),
-                kind="oracle",
+                kind="oracle", cpu_model=cpu_model,
+                value_1thread=(round(1.0 / (unit_1t * DECODE["batch"] * DECODE["layers"]), 4) if unit_1t else None),
                 sample=(f"one (layer, sequence) unit of the 1M-context decode step (scan of 262,080 pooled keys, "
                         f"top-512, attention over 2,048 tokens; K/V rows it reads are generated by index beforehand), "
                         f"run {reps} times (a step has 48 such units); {unit_s * 1e3:.1f} ms per unit; "
