@@ -906,7 +906,7 @@ def main():
                      "frac": round(dec["lists_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic("index_lists_a<2, false>", "2048"),
                      "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["lists_ms"] * 1e3, 3)},
-        "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample")},
+        "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample", "value_1thread", "cpu_model")},
         "wall_s": round(time.time() - t_all, 1),
     }
     print(json.dumps(line), flush=True)
