@@ -11,7 +11,9 @@
 //      (keys / s) in (key descending, index ascending) order, as a 64-bit
 //      (order key, index) pair;
 //   3. lists: the full score GEMM keeps, per query, every score ranked at
-//      least as high as the threshold (unordered; one atomic per 16 lanes);
+//      least as high as the threshold (unordered: a query row's lane group
+//      stages its entries in LDS and reserves list slots with one atomic per
+//      1024-key span);
 //   4. select: per query the top-k of its list, written in ascending index
 //      order through an LDS bitmap of the candidates.
 // Every score left out ranks below the threshold and every listed one at or

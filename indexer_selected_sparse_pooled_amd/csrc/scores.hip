@@ -300,6 +300,12 @@ __global__ __launch_bounds__(256) void scores_gemm_a_fp8(ScoreArgs a) {
 
 // Prefill chunk, variant B: 4 heads x 64 dims, score = sum_h w_h relu(dot_h).
 // kFp8: B operands converted from E4M3 codes, the key scale applied last.
+// Work-group = 64 queries (16 per wave) x 128 columns; column t scores key
+// t * tok_step (the sample pass of the one-call selection strides). kList
+// (the one-call selection, prefill_select.hip): 8 x 128 columns per
+// work-group, and instead of storing scores each query row keeps the
+// entries ranked at or above its threshold in a per-query list.
+// The key rows of tile t + 2 are fetched before tile t is computed.
 constexpr int kListBatches = 8;  // list mode: 8 x 128 columns per work-group
 constexpr int kStage = 64;       // list mode: LDS entries staged per query row
 
