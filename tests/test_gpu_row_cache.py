@@ -13,7 +13,9 @@ whose row was read in an earlier step and not dropped since: that set is
 computed on the host and compared. Every plan entry is checked for validity
 (a miss names its token, a hit names the row's slot), one step is compared
 with the oracle, and a row rewritten without being dropped is shown to come
-from the cache (the pages' consistency rule made visible).
+from the cache (the pages' consistency rule made visible). The cache step and
+the cached decode are also replayed from a HIP graph, each replay equal to the
+uncached decode while the cache fills.
 """
 import numpy as np
 import pytest
@@ -281,3 +283,46 @@ def test_cached_decode_argument_errors(pkg):
     with pytest.raises(pkg.QsaError):
         pkg.qsa_row_cache_step(pkg.ATTN_A, cache, 0, qc.i32([1]), kv)
     torch.cuda.synchronize()
+
+
+def test_cached_decode_graph_replays(pkg):
+    """The cache step and the cached decode captured in one HIP graph and
+    replayed (with eager work between replays): every replay equals the
+    uncached decode, while the cache fills and then serves hits."""
+    ctxs = [9000, 5003]
+    _print_case("row_cache_graph", ctxs=ctxs)
+    cap = (max(ctxs) + 8 + 7) // 8 * 8
+    st = Stepper(pkg, 46, ctxs, range(2), 2 * cap, 4, 1)
+    ou, lu, oc, lc, _, _ = st.step([])  # selections fixed from here on
+    sel = torch.full((2, TOPK), -1, dtype=torch.int32, device="cuda")
+    n_sel = torch.zeros(2, dtype=torch.int32, device="cuda")
+    for i, s in enumerate(st.sels):
+        sel[i, :len(s)] = torch.tensor(s.astype(np.int32))
+        n_sel[i] = len(s)
+    q_ctx, q_seq = qc.i32(ctxs), qc.i32([0, 1])
+    stored = qc.i32([c - 1 for c in ctxs])
+    o = torch.empty(4, 2, 16, D, device="cuda")
+    lse = torch.empty(4, 2, 16, device="cuda")
+    st.cache.zero_()
+    torch.cuda.synchronize()
+
+    def call():
+        pkg.qsa_row_cache_step(pkg.ATTN_A, st.cache, st.n_slots, stored, st.kv, row_seq=q_seq)
+        pkg.qsa_sparse_decode_cached(pkg.SEL_A, pkg.ATTN_A, q_ctx, st.cap, st.q_dev, st.kv, sel, n_sel, 4, o, lse,
+                                     st.cache, st.n_slots, st.plan, q_seq=q_seq)
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        call()
+    hits = []
+    for _ in range(4):
+        o.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, ou) and torch.equal(lse, lu), "replay differs from the uncached decode"
+        hits.append(int((st.plan[:, :TOPK * BLOCK] < 0).sum().item()))
+    assert hits[0] == 0 and hits[1] > 0, hits
+    del g
