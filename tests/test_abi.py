@@ -139,3 +139,29 @@ def test_row_cache_sizes_and_host_validation(lib):
     assert st == 2 and b"row cache" in lib.qsa_last_error()
     st = lib.qsa_row_cache_step(ctypes.byref(qsa.ATTN_A), fake, want, n, -1, None, None, ctypes.byref(kv), None)
     assert st == 1
+
+
+def test_prefill_select_workspace_and_host_validation(lib):
+    """qsa_index_topk_prefill: workspace = sample scores (nq x ceil(keys / s),
+    s = ceil(keys / 4096)), thresholds, one 128-byte counter line and a flag
+    per query, lists of 8192 entries per query, then the regular top-k's
+    workspace, each 256-byte aligned; unsupported shapes and short workspaces
+    fail on the host."""
+    from indexer_selected_sparse_pooled_amd import qsa
+    up = lambda x: (x + 255) // 256 * 256
+    nq, ctx = 2048, 131072
+    n_samp = 4096
+    want = up(up(up(up(up(nq * n_samp * 4) + nq * 8) + nq * 128) + nq * 4) + nq * 8192 * 8)
+    want += qsa.qsa_topk_workspace_bytes(qsa.SEL_B, nq, ctx)
+    assert qsa.qsa_index_topk_prefill_workspace_bytes(qsa.SEL_B, nq, ctx) == want
+    assert qsa.qsa_index_topk_prefill_workspace_bytes(qsa.SEL_B, 16, 262145) == 0  # past the bitmap
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+
+    def call(cfg, n, ws_bytes):
+        return lib.qsa_index_topk_prefill(ctypes.byref(cfg), n, fake, ctx, fake, fake, fake, fake, ctx, fake, fake,
+                                          fake, ws_bytes, None)
+    assert call(qsa.SEL_A, 64, want) == 2  # the pooled-block indexer
+    assert call(qsa.SEL_B, 8, want) == 2   # fewer than 16 queries
+    ws64 = qsa.qsa_index_topk_prefill_workspace_bytes(qsa.SEL_B, 64, ctx)
+    assert call(qsa.SEL_B, 64, ws64 - 1) == 3
+    assert call(qsa.SEL_B, 0, 0) == 0      # no work
