@@ -35,9 +35,12 @@ class DecodeBuffers:
 def default_n_split(nq: int, hkv: int, budget_tokens: int) -> int:
     """Splits per (query, kv head): about 128 work-groups in all (fewer
     splits mean fewer partials to merge; the gathered rows are a small part
-    of a decode step's bytes), at least 128 tokens each."""
-    want = max(1, -(-128 // max(1, nq * hkv)))
-    most = max(1, budget_tokens // 128)
+    of a decode step's bytes), or about 256 for the shared latent (one kv
+    head, 64 heads per work-group: measured best at batch 8), at least 128
+    tokens each (64 for the shared latent)."""
+    target, least = (256, 64) if hkv == 1 else (128, 128)
+    want = max(1, -(-target // max(1, nq * hkv)))
+    most = max(1, budget_tokens // least)
     return int(min(want, most, 256))
 
 

@@ -54,7 +54,7 @@ class MlaCase:
                                 self.ctxs[i], block=1, topk=2048, scale=SCALE, w_idx=self.w[i], dv=512)
 
 
-@pytest.mark.parametrize("n_split", [1, 5, 16])
+@pytest.mark.parametrize("n_split", [1, 5, 16, 32])
 def test_mla_attention_on_given_selection(Q, n_split):
     pkg, _ = Q
     ctxs = [5000, 2048, 2049, 1, 0, 3001]
