@@ -823,7 +823,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {args.gpus}). "
               "The decode step would shard by sequence and layer, one GPU per shard; run with --gpus 1.",
               file=sys.stderr)
         return 2

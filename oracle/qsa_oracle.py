@@ -37,7 +37,7 @@ or a worked example):
   pattern S.1111.111 is NaN; there are no infinities; the largest finite
   magnitude is 448.
 
-Readings taken where the pages are silent (each also listed in the design doc):
+Readings taken where the pages are silent:
 
 R1  pooled key = exact mean of the block's raw keys, rounded once to bf16
     (round to nearest, ties to even).
