@@ -297,8 +297,8 @@ size_t qsa_index_topk_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq, int32_
  * pass over every s-th key sets a per-query threshold, the full pass keeps
  * only the scores ranked at or above it, and the top-k is taken from those.
  * A query for which that leaves fewer than topk candidates (or more than
- * the workspace holds) gets its full scores in `scores` and the regular
- * top-k; for every other query `scores` is not written.
+ * the workspace holds) gets its full scores in `scores` and an exact
+ * select over them; for every other query `scores` is not written.
  * One sequence (keys as in qsa_index_scores with q_seq NULL), cfg with
  * block 1, idx_heads 4, idx_dim 64 (bf16 or FP8 keys), 16 <= nq <= 65535,
  * max_ctx <= 262144. Other arguments as in qsa_index_scores and

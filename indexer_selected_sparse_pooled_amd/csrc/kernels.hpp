@@ -96,6 +96,8 @@ struct TopkPlan {
   int list_len;      // candidates kept per chunk (capacity in filter mode)
   int final_threads; // work-group size of the per-query selection (256 or 1024)
   int direct_max;    // queries with at most this many candidates skip the chunk lists
+  bool stream_only;  // one launch: an exact select over all scores for each flagged query (needs a.only,
+                     // queries with more than 8192 candidates; no workspace)
   size_t ws_bytes;
 };
 TopkPlan plan_topk(int nq, int max_ctx, int block, int topk);
@@ -109,7 +111,7 @@ struct PrefillSelectPlan {
   int n_samp;      // sample columns per query
   int cap;         // list capacity per query
   TopkPlan tp;     // the regular top-k for flagged queries
-  size_t off_samp, off_theta, off_counts, off_fail, off_lists, off_topk, ws_bytes;
+  size_t off_samp, off_theta, off_counts, off_fail, off_lists, ws_bytes;
 };
 PrefillSelectPlan plan_prefill_select(int nq, int max_ctx, int block, int topk);
 hipError_t launch_prefill_select(const ScoreArgs& sa, const TopkArgs& ta, const PrefillSelectPlan& p, void* ws,

@@ -20,8 +20,8 @@
 // above it, so when a list holds at least topk entries and did not overflow,
 // its top-k is the exact top-k (ties included: the threshold carries an
 // index). A query whose list came up short or overflowed is flagged; the
-// regular path (full scores for the flagged queries only, then the chunked
-// top-k) then selects it, so every query gets the exact answer.
+// regular path (full scores for the flagged queries only, then an exact
+// select over them) then selects it, so every query gets the exact answer.
 #include "common.hpp"
 #include "kernels.hpp"
 #include "select.hpp"
@@ -196,8 +196,7 @@ PrefillSelectPlan plan_prefill_select(int nq, int max_ctx, int block, int topk) 
   off = up(off + size_t(nq) * 4);
   p.off_lists = off;
   off = up(off + size_t(nq) * size_t(kCap) * 8);
-  p.off_topk = off;
-  p.ws_bytes = off + p.tp.ws_bytes;
+  p.ws_bytes = off;
   return p;
 }
 
@@ -242,7 +241,7 @@ hipError_t launch_prefill_select(const ScoreArgs& sa, const TopkArgs& ta, const 
   hipLaunchKernelGGL(select_lists, dim3(unsigned(sa.nq)), dim3(kFinalNT), 0, s, a3, ta.topk, ta.sel, ta.n_sel, fail);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // 5. flagged queries: their full scores, then the regular top-k
+  // 5. flagged queries: their full scores, then an exact select over them (one launch)
   ScoreArgs a5 = sa;
   a5.tok_step = 1;
   a5.only = fail;
@@ -251,8 +250,10 @@ hipError_t launch_prefill_select(const ScoreArgs& sa, const TopkArgs& ta, const 
   if (e != hipSuccess) return e;
   TopkArgs t5 = ta;
   t5.only = fail;
-  t5.ws = w + p.off_topk;
-  return launch_topk(t5, p.tp, s);
+  t5.ws = nullptr;
+  TopkPlan tp5 = p.tp;
+  tp5.stream_only = true;  // flagged queries all have more than kCap keys
+  return launch_topk(t5, tp5, s);
 }
 
 }  // namespace qsa

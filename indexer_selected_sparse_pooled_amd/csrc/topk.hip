@@ -435,6 +435,14 @@ __global__ __launch_bounds__(NT) void topk_final_threshold(TopkArgs a, TopkPlan 
   int* sel = a.sel + int64_t(i) * topk;
   if (tid == 0) a.n_sel[i] = topk;
   const float* sc = a.scores + int64_t(i) * a.ld;
+  if (p.stream_only) {  // exact select over every score, read from memory
+    auto gk = [sc](int j) { return order_key(sc[j]); };
+    uint32_t kstar;
+    int need;
+    stream_select<kNTf>(gk, n, topk, sh.st, kstar, need);
+    stream_compact<kNTf>(gk, n, kstar, need, sh.st, [&](int pos, int j) { sel[pos] = j; });
+    return;
+  }
   const int L = p.list_len;
   const int nch = (n + kChunk - 1) / kChunk;
   const uint32_t th = *theta_of(a, p, i);
@@ -545,6 +553,11 @@ TopkPlan plan_topk(int nq, int max_ctx, int block, int topk) {
 
 hipError_t launch_topk(const TopkArgs& a, const TopkPlan& p, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
+  if (p.stream_only) {
+    if (!a.only) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(topk_final_threshold<1024>, dim3(unsigned(a.nq)), dim3(1024), 0, s, a, p);
+    return hipGetLastError();
+  }
   if (p.filter) {
     hipLaunchKernelGGL(topk_sample, dim3(unsigned(a.nq)), dim3(kNTc), 0, s, a, p);
     const hipError_t e = hipGetLastError();

@@ -144,15 +144,14 @@ def test_row_cache_sizes_and_host_validation(lib):
 def test_prefill_select_workspace_and_host_validation(lib):
     """qsa_index_topk_prefill: workspace = sample scores (nq x ceil(keys / s),
     s = ceil(keys / 4096)), thresholds, one 128-byte counter line and a flag
-    per query, lists of 8192 entries per query, then the regular top-k's
-    workspace, each 256-byte aligned; unsupported shapes and short workspaces
+    per query and lists of 8192 entries per query, each 256-byte aligned;
+    unsupported shapes and short workspaces
     fail on the host."""
     from indexer_selected_sparse_pooled_amd import qsa
     up = lambda x: (x + 255) // 256 * 256
     nq, ctx = 2048, 131072
     n_samp = 4096
-    want = up(up(up(up(up(nq * n_samp * 4) + nq * 8) + nq * 128) + nq * 4) + nq * 8192 * 8)
-    want += qsa.qsa_topk_workspace_bytes(qsa.SEL_B, nq, ctx)
+    want = up(up(up(up(nq * n_samp * 4) + nq * 8) + nq * 128) + nq * 4) + nq * 8192 * 8
     assert qsa.qsa_index_topk_prefill_workspace_bytes(qsa.SEL_B, nq, ctx) == want
     assert qsa.qsa_index_topk_prefill_workspace_bytes(qsa.SEL_B, 16, 262145) == 0  # past the bitmap
     fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
