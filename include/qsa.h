@@ -15,7 +15,8 @@
  * ずに済む", "VRAM に残す必要があるもの", "ちなみにこの欠点"); "GLM-5.3 最適化
  * 第2部：16基のH200上でのPCP、DCP、およびHybrid HiSparse" (sections "PCP",
  * "DCP", footnote 1); "125B MoE を 3090 3 枚で運用する vLLM 最適化編"
- * (section 3.3, ties in top-k go to the smaller id).
+ * (section 3.3, ties in top-k go to the smaller id; section 5, the K/V row
+ * cache in device memory).
  *
  * Conventions for every entry point:
  *   - Pointers marked (device) are device memory owned by the caller; the
@@ -401,7 +402,7 @@ size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_at
 /* ------------------------------------------- A4 with an HBM row cache ----
  * For K/V rows kept in host memory (pinned, read zero-copy): a direct-mapped
  * cache of rows in device memory that later decode steps read instead of
- * crossing the host link again ("3090x3で 314 万コンテキスト", section 5:
+ * crossing the host link again ("125B MoE を 3090 3 枚で運用する vLLM 最適化編", section 5:
  * consecutive selections overlap by 0.72 on average; one slot holds a
  * token's K and V for every kv head, keyed by the row's position; the slots
  * of stored rows are invalidated; per step an epoch, hit marks and claimed

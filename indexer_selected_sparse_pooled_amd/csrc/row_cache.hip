@@ -1,5 +1,5 @@
 // HBM row cache for K/V rows kept in host memory.
-// "3090x3で 314 万コンテキスト", section 5 (decode, third part): selections
+// "125B MoE を 3090 3 枚で運用する vLLM 最適化編", section 5 (decode, third part): selections
 // at consecutive steps overlap (0.72 on average), so rows read over the host
 // link are kept in a direct-mapped cache in device memory, one slot per token
 // (its K and V for every kv head), keyed by the row's physical position. Per

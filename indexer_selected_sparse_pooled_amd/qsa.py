@@ -341,6 +341,22 @@ def decode_layer_workspace(sel_cfg, attn_cfg, nq, max_ctx, n_split, device="cuda
     return torch.zeros(max(n, 16), dtype=torch.uint8, device=device)
 
 
+def decode_layer_error(ws) -> int:
+    """The sticky error word of a qsa_decode_layer workspace (its first 4
+    bytes, uint32): 0 when every bounded wait of the calls made on it since
+    it was zero-filled ended in time. Reading it synchronises with the
+    device."""
+    return int(ws[:4].view(torch.int32).item()) & 0xFFFFFFFF
+
+
+def check_decode_layer_error(ws) -> None:
+    """Raise QsaError if the workspace's error word is set (the outputs of
+    the calls that set it are unspecified)."""
+    e = decode_layer_error(ws)
+    if e:
+        raise QsaError("qsa_decode_layer", 4, f"error word {e:#x}: a bounded wait in the layer ran out")
+
+
 def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel, n_split, ws,
                      o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
     """One decode layer (two launches): qsa_index_topk, then qsa_sparse_decode

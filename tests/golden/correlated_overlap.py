@@ -1,7 +1,7 @@
 """Tunes the correlated-selection workload and records it in
 correlated_overlap.txt.
 
-"3090x3で 314 万コンテキスト", section 5 (decode, third part): the indexer's
+"125B MoE を 3090 3 枚で運用する vLLM 最適化編", section 5 (decode, third part): the indexer's
 selections at consecutive steps overlap by 60-85%, 0.72 on average with the
 previous step and 0.86 with the union of the previous four. The synthetic
 stand-in keeps every input of the 60,000-token-history prefill chunk i.i.d.

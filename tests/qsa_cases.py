@@ -127,6 +127,21 @@ def check_row(gpu_sel, gpu_n, o, lse, ob, ref, ctx, block, topk, q_bits, k_bits,
     return same
 
 
+def check_row_with(gpu_sel, gpu_n, o, lse, ob, oracle_scores, ctx, block, topk, attend_ref):
+    """check_row with the oracle's attention given as a function:
+    attend_ref(tokens) -> (o_ref, lse_ref) over the listed token positions
+    (e.g. rows the oracle dequantized itself, or rows regenerated by index).
+    The selection is checked against the oracle's scores first; the
+    attention is then compared with the oracle on the GPU's selection, which
+    is the oracle's own unless a boundary swap was tolerated. Returns True if
+    the selection was bit-identical."""
+    same = check_selection(gpu_sel, gpu_n, oracle_scores, ctx, block, topk)
+    toks = orc.selected_tokens(np.asarray(gpu_sel[:gpu_n]), ctx, block)
+    o_ref, lse_ref = attend_ref(toks)
+    check_attention(o, lse, o_ref, lse_ref, ob)
+    return same
+
+
 # ---- FP8 key pages (layout only: 64 keys per page, codes then fp32 scales)
 
 def unpack_fp8_pages(buf, n, dim):

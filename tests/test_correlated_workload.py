@@ -1,6 +1,6 @@
 """The correlated-selection workload against the pages' figure.
 
-"3090x3で 314 万コンテキスト", section 5: selections at consecutive steps
+"125B MoE を 3090 3 枚で運用する vLLM 最適化編", section 5: selections at consecutive steps
 overlap by 60-85%, 0.72 on average with the previous step. The committed
 AR(1) correlation (tests/golden/correlated_overlap.txt, written by
 correlated_overlap.py from the oracle's selections over all 4096 queries of

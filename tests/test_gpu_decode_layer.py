@@ -43,6 +43,8 @@ def _run(pkg, pipeline, ctxs, q_idx, pooled, q, kv, fused, n_split=None, bufs=No
     pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, qc.i32(ctxs), max_ctx, q_idx, pooled, q, kv, bufs,
                           q_seq=qc.i32(range(nq)), fused=fused)
     torch.cuda.synchronize()
+    if fused:
+        pkg.check_decode_layer_error(bufs.layer_ws)  # every bounded wait ended in time
     return bufs
 
 

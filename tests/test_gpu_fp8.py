@@ -11,10 +11,10 @@ per key, stored in pages of 64) through the C ABI.
   oracle's scores over the dequantized keys within the fp32 accumulation
   bound.
 * qsa_index_topk, qsa_index_lists and qsa_decode_layer with FP8 keys: the
-  same scores bit for bit as qsa_index_scores, the selection equal to the
-  oracle's selection applied to those scores, and the decode layer's
-  attention within tolerance of the oracle on the selected tokens, on the
-  1,048,320-token batch-4 shape.
+  same scores bit for bit as qsa_index_scores; on the 1,048,320-token
+  batch-4 shape, end to end against the oracle, which quantizes the
+  regenerated bf16 keys itself: its selection on its own scores (boundary
+  rule) and its attention over the selected tokens.
 """
 import numpy as np
 import pytest
@@ -174,16 +174,20 @@ def test_fp8_scores_decode_and_prefill(pkg):
 def test_fp8_select_and_decode_layer_full_size(pkg):
     """The 1,048,320-token batch-4 decode shape with FP8 pooled keys: the
     fused scan + top-k, the lists-only scan and the decode layer agree with
-    qsa_index_scores + qsa_topk_blocks bit for bit, the selection is the
-    oracle's on those scores, the scores are within the accumulation bound
-    of the oracle's, and the attention output matches the oracle on the
-    selected tokens. Mixed contexts in a second call take the other
-    selection paths."""
+    qsa_index_scores + qsa_topk_blocks bit for bit; against the oracle, end
+    to end: the oracle regenerates the bf16 keys on the host and quantizes
+    them itself (the GPU's pages must equal its codes and scales), scores
+    them, and the GPU selection must be the oracle's selection on the
+    oracle's scores (boundary rule), the GPU scores within the accumulation
+    bound, and the attention output the oracle's on the selected tokens
+    (K/V rows regenerated by index). Mixed contexts in a second call take
+    the other selection paths."""
     from indexer_selected_sparse_pooled_amd import pipeline
     from qsa_inputs.gpu import fill_normal_bf16
     L, B = 1048320, 4
     nb = L // 4
     seed = qi.config_seed(3) + 17
+    S = lambda s, kind: qi.stream_id(0, s, kind)
     _print_case("fp8_decode_full", ctx=L, batch=B)
     keys = torch.empty(B, nb, 128, dtype=torch.bfloat16, device="cuda")
     k = torch.empty(B, L, 2, 256, dtype=torch.bfloat16, device="cuda")
@@ -192,11 +196,21 @@ def test_fp8_select_and_decode_layer_full_size(pkg):
     q_idx = torch.empty(B, 1, 128, dtype=torch.bfloat16, device="cuda")
     for s in range(B):
         for t, kind in ((keys, "misc"), (k, "k"), (v, "v"), (q, "q"), (q_idx, "q_idx")):
-            fill_normal_bf16(t[s], seed, qi.stream_id(0, s, kind))
+            fill_normal_bf16(t[s], seed, S(s, kind))
     f8 = _fp8_keys_dev(pkg, keys)
     del keys
     kv = pkg.make_kv(k, v)
     cfg, acfg = pkg.SEL_A_FP8, pkg.ATTN_A
+    # the oracle's own inputs: regenerated on the host, quantized by the oracle
+    ref_keys = [orc.fp8_keys(qc.bits(seed, S(s, "misc"), (nb, 128))) for s in range(B)]
+    q_idx_np = [qc.bits(seed, S(s, "q_idx"), (128,)) for s in range(B)]
+    q_np = [qc.bits(seed, S(s, "q"), (16, 256)) for s in range(B)]
+    f8h = f8.cpu().numpy()
+    for s in range(B):
+        c, scl = qc.unpack_fp8_pages(f8h[s], nb, 128)
+        assert np.array_equal(c, ref_keys[s][0]), f"seq {s}: FP8 codes differ from the oracle's"
+        assert np.array_equal(scl.view(np.uint32), ref_keys[s][1].view(np.uint32)), f"seq {s}: scales"
+    del f8h
     for ctxs in ([L] * B, [L - 4001, 2052, 600004, 9001]):
         _print_case("fp8_decode_full_ctxs", ctxs=ctxs)
         q_ctx, q_seq = qc.i32(ctxs), qc.i32(range(B))
@@ -216,25 +230,29 @@ def test_fp8_select_and_decode_layer_full_size(pkg):
         sc3 = torch.full_like(sc, float("nan"))
         pkg.qsa_index_lists(cfg, q_ctx, L, q_idx, f8, sc3, pkg.index_topk_workspace(cfg, B, L), q_seq=q_seq)
         torch.cuda.synchronize()
+        pkg.check_decode_layer_error(bufs.layer_ws)
         for name, t in (("decode_layer", bufs.scores), ("index_topk", sc2), ("index_lists", sc3)):
             assert torch.equal(t.nan_to_num(7.0), sc.nan_to_num(7.0)), f"{name}: scores differ"
         for name, (a, b) in (("decode_layer", (bufs.sel, bufs.n_sel)), ("index_topk", (sel2, n_sel2))):
             assert torch.equal(a, sel) and torch.equal(b, n_sel), f"{name}: selection differs"
-        # against the oracle
-        f8h = f8.cpu().numpy()
         got_sc, got_sel, got_n = sc.cpu().numpy(), sel.cpu().numpy(), n_sel.cpu().numpy()
         o, lse, ob = bufs.o.cpu().numpy(), bufs.lse.cpu().numpy(), qc.from_dev_bits(bufs.o_bf16)
         for s, ctx in enumerate(ctxs):
             n = ctx // 4
-            c, scl = qc.unpack_fp8_pages(f8h[s], nb, 128)
-            qib = qc.from_dev_bits(q_idx[s, 0])
-            ref = orc.index_scores_fp8(qib, c, scl, n)
-            assert np.all(np.abs(got_sc[s, :n] - ref) <= _fp8_tolerance(qib, c, scl, n)), f"seq {s}: scores"
-            want = orc.select_blocks(got_sc[s, :n].astype(np.float64), ctx, 4, 512)
-            assert got_n[s] == want.size and np.array_equal(got_sel[s, :got_n[s]], want), f"seq {s}: selection"
-            toks = orc.selected_tokens(want, ctx, 4)
-            kr = qc.from_dev_bits(k[s, torch.from_numpy(toks).cuda()])
-            vr = qc.from_dev_bits(v[s, torch.from_numpy(toks).cuda()])
-            o_ref, lse_ref = orc.attend(qc.from_dev_bits(q[s]), kr, vr, np.arange(toks.size), 1.0 / 16)
-            qc.check_attention(o[s], lse[s], o_ref, lse_ref, ob[s])
+            c, scl = ref_keys[s]
+            ref = orc.index_scores_fp8(q_idx_np[s], c, scl, n)
+            assert np.all(np.abs(got_sc[s, :n] - ref) <= _fp8_tolerance(q_idx_np[s], c, scl, n)), f"seq {s}: scores"
+
+            def attend_ref(toks, s=s):
+                kr = _rows(seed, S(s, "k"), toks, 512).reshape(-1, 2, 256)
+                vr = _rows(seed, S(s, "v"), toks, 512).reshape(-1, 2, 256)
+                return orc.attend(q_np[s], kr, vr, np.arange(toks.size), 1.0 / 16)
+
+            qc.check_row_with(got_sel[s], got_n[s], o[s], lse[s], ob[s], ref, ctx, 4, 512, attend_ref)
         assert torch.count_nonzero(bufs.layer_ws[:64]).item() == 0, "control words not reset"
+
+
+def _rows(seed, stream, toks, width):
+    """Rows `toks` of a [tokens][width] bf16 tensor filled by the generator."""
+    idx = (np.asarray(toks, dtype=np.int64)[:, None] * width + np.arange(width)[None, :]).reshape(-1)
+    return qi.normal_bf16(seed, stream, 0, index=idx.astype(np.uint64)).reshape(len(toks), width)

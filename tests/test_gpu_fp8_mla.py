@@ -106,9 +106,11 @@ def test_append_fp8_latent_rows(Q):
         assert np.array_equal(after[mask], before[mask]), "rows outside the appended positions changed"
 
 
-def _values(rows_np):
-    codes, scales, rope = _unpack_rows(rows_np)
-    return orc.fp8_latent_values(codes, scales, rope)  # [.., 576] float64
+def _oracle_values(lat_bits):
+    """The float64 values the oracle's own FP8 rows of bf16 latent rows
+    [n][576] stand for (the GPU rows are pinned to these codes bit for bit
+    in test_quantize_latent_bit_exact)."""
+    return orc.fp8_latent_values(*orc.fp8_latent(lat_bits))  # [n, 576] float64
 
 
 @pytest.mark.parametrize("n_split", [1, 5, 16])
@@ -119,7 +121,7 @@ def test_fp8_mla_attention_on_given_selection(Q, n_split):
     _print_case("fp8_mla_attend", n_split=n_split)
     lat = _latent(74, nq, cap)
     rows = _fp8_rows(pkg, qc.to_dev(lat))
-    vals = _values(rows.cpu().numpy())
+    vals = [_oracle_values(lat[s, :, 0, :]) for s in range(nq)]
     q = np.stack([qc.bits(75, s, (64, 576)) for s in range(nq)])
     rng = np.random.default_rng(76)
     sel = torch.full((nq, 2048), -1, dtype=torch.int32, device="cuda")
@@ -165,7 +167,7 @@ def test_fp8_mla_prefill_chunk_tiled(Q, tile):
     w = np.stack([qi.uniform_f32(seed, 100 + i, 4) for i in range(nq)])
     ctxs = [hist + i + 1 for i in range(nq)]
     rows = _fp8_rows(pkg, qc.to_dev(lat))
-    vals = _values(rows.cpu().numpy()[0])
+    vals = _oracle_values(lat[0, :, 0, :])
     kv = pkg.make_kv(rows)
     bufs = pipeline.prefill_buffers(pkg.SEL_B, pkg.ATTN_B, nq, ctx_max, tile)
     pipeline.prefill_chunk(pkg.SEL_B, pkg.ATTN_B, qc.i32(ctxs), ctx_max, qc.to_dev(q_idx), qc.to_dev(keys[None]),
@@ -176,10 +178,8 @@ def test_fp8_mla_prefill_chunk_tiled(Q, tile):
     v = vals[:, None, :]
     for i in range(nq):
         sc = orc.index_scores_relu(q_idx[i], w[i], keys, ctxs[i])
-        qc.check_selection(sel[i], n_sel[i], sc, ctxs[i], 1, 2048)
-        toks = orc.selected_tokens(sel[i, :n_sel[i]], ctxs[i], 1)
-        o_ref, lse_ref = orc.attend_values(q[i], v, v, toks, SCALE, dv=512)
-        qc.check_attention(o[i], lse[i], o_ref, lse_ref, ob[i])
+        qc.check_row_with(sel[i], n_sel[i], o[i], lse[i], ob[i], sc, ctxs[i], 1, 2048,
+                          lambda toks, i=i: orc.attend_values(q[i], v, v, toks, SCALE, dv=512))
 
 
 def _relu_tolerance(q_bits, w, codes, scales, n):
@@ -221,9 +221,10 @@ def test_fp8_token_key_scores(Q):
 
 def test_fp8_mla_decode_keys_and_rows(Q):
     """Decode over FP8 token keys and FP8 rows (the GLM cache: 68 + 656
-    bytes per token): scores within the accumulation bound, the selection
-    the oracle's on the GPU's own scores, attention against the oracle on
-    the dequantized rows."""
+    bytes per token), end to end against the oracle, which quantizes the
+    bf16 keys and rows itself: scores within the accumulation bound, the
+    selection the oracle's on its own scores (boundary rule), attention the
+    oracle's over its dequantized rows."""
     pkg, pipeline = Q
     ctxs = [20000, 2048, 2049, 7, 12345]
     nq, cap = len(ctxs), 20000
@@ -244,16 +245,14 @@ def test_fp8_mla_decode_keys_and_rows(Q):
     torch.cuda.synchronize()
     sc, sel, n_sel = bufs.scores.cpu().numpy(), bufs.sel.cpu().numpy(), bufs.n_sel.cpu().numpy()
     o, lse, ob = bufs.o.cpu().numpy(), bufs.lse.cpu().numpy(), qc.from_dev_bits(bufs.o_bf16)
-    vals = _values(rows.cpu().numpy())
     for i, ctx in enumerate(ctxs):
+        # the oracle quantizes the bf16 keys and rows itself
         c, s = orc.fp8_keys(keys_np[i])
         want = orc.index_scores_relu_fp8(q_idx[i], w[i], c, s, ctx)
         assert np.all(np.abs(sc[i, :ctx] - want) <= _relu_tolerance(q_idx[i], w[i], c, s, ctx)), f"query {i}: scores"
-        exp = orc.select_blocks(sc[i, :ctx].astype(np.float64), ctx, 1, 2048)
-        assert n_sel[i] == exp.size and np.array_equal(sel[i, :n_sel[i]], exp), f"query {i}: selection"
-        v = vals[i][:, None, :]
-        o_ref, lse_ref = orc.attend_values(q[i], v, v, orc.selected_tokens(exp, ctx, 1), SCALE, dv=512)
-        qc.check_attention(o[i], lse[i], o_ref, lse_ref, ob[i])
+        v = _oracle_values(lat[i, :, 0, :])[:, None, :]
+        qc.check_row_with(sel[i], n_sel[i], o[i], lse[i], ob[i], want, ctx, 1, 2048,
+                          lambda toks, i=i, v=v: orc.attend_values(q[i], v, v, toks, SCALE, dv=512))
 
 
 def test_append_fp8_token_keys(Q):

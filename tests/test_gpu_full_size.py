@@ -7,8 +7,11 @@ benchmark times, on sampled queries the oracle computes one by one.
   overlapping about 0.72 as the pages measured), whose mean overlap over
   all 4096 GPU selections must match the one recorded by
   tests/golden/correlated_overlap.py.
+* The pooled-key prefill chunk at 1024-token history tiles (63 tiles).
 * The shared-latent prefill chunk: 2048 queries at positions
   129,024..131,071, one history tile of 131,072 tokens.
+* The shared-latent decode step: batch 8 at context 131,072, every query
+  (one with all-negative indexer head weights).
 
 Inputs come from the seeded generator on the GPU exactly as bench.py makes
 them; the oracle regenerates the keys in full and the K/V (latent) rows of
@@ -54,14 +57,14 @@ def _rows(seed, stream, toks, width):
     return qi.normal_bf16(seed, stream, 0, index=idx.astype(np.uint64)).reshape(len(toks), width)
 
 
-@pytest.mark.parametrize("correlated", [False, True])
-def test_prefill_full_size_sampled(Q, correlated):
+@pytest.mark.parametrize("correlated,tile", [(False, 8192), (False, 1024), (True, 8192)])
+def test_prefill_full_size_sampled(Q, correlated, tile):
     pkg, pipeline = Q
     from qsa_inputs.gpu import fill_normal_bf16
     H, C = 60000, 4096
     ctx_max = H + C
     seed = qi.config_seed(4)
-    _print_case("prefill_full", correlated=correlated)
+    _print_case("prefill_full", correlated=correlated, tile=tile)
     S = lambda kind, salt=0: qi.stream_id(0, 0, kind, salt)
     raw = torch.empty(1, ctx_max, 128, dtype=torch.bfloat16, device="cuda")
     k = torch.empty(1, ctx_max, 2, 256, dtype=torch.bfloat16, device="cuda")
@@ -80,7 +83,7 @@ def test_prefill_full_size_sampled(Q, correlated):
     pkg.qsa_pool_keys(raw, pooled, block=4)
     kv = pkg.make_kv(k, v)
     ctxs = list(range(H + 1, H + C + 1))
-    bufs = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, C, ctx_max, 8192)
+    bufs = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, C, ctx_max, tile)
     pipeline.prefill_chunk(pkg.SEL_A, pkg.ATTN_A, qc.i32(ctxs), ctx_max, q_idx, pooled, q, kv, bufs)
     torch.cuda.synchronize()
     sel, n_sel = bufs.sel.cpu().numpy(), bufs.n_sel.cpu().numpy()
@@ -90,13 +93,14 @@ def test_prefill_full_size_sampled(Q, correlated):
     for i in (0, 1, 777, 2048, 3001, 4094, 4095):
         ctx = ctxs[i]
         sc = orc.index_scores(q_idx_np[i], pooled_np, ctx // 4)
-        qc.check_selection(sel[i], n_sel[i], sc, ctx, 4, 512)
-        toks = orc.selected_tokens(sel[i, :n_sel[i]], ctx, 4)
-        kr = _rows(seed, S("k"), toks, 512).reshape(-1, 2, 256)
-        vr = _rows(seed, S("v"), toks, 512).reshape(-1, 2, 256)
         qb = qi.normal_bf16(seed, S("q"), i * 4096, 4096).reshape(16, 256)
-        o_ref, lse_ref = orc.attend(qb, kr, vr, np.arange(toks.size), 1.0 / 16)
-        qc.check_attention(o[i], lse[i], o_ref, lse_ref, ob[i])
+
+        def attend_ref(toks, qb=qb):
+            kr = _rows(seed, S("k"), toks, 512).reshape(-1, 2, 256)
+            vr = _rows(seed, S("v"), toks, 512).reshape(-1, 2, 256)
+            return orc.attend(qb, kr, vr, np.arange(toks.size), 1.0 / 16)
+
+        qc.check_row_with(sel[i], n_sel[i], o[i], lse[i], ob[i], sc, ctx, 4, 512, attend_ref)
     if correlated:
         ov = np.mean([np.intersect1d(sel[i], sel[i - 1]).size / 512 for i in range(1, C)])
         assert abs(ov - _golden("mean_overlap_previous")) <= 0.005, ov
@@ -129,9 +133,65 @@ def test_mla_prefill_full_size_sampled(Q):
         ctx = ctxs[i]
         qi_np = qi.normal_bf16(seed, S("q_idx"), i * 256, 256).reshape(4, 64)
         sc = orc.index_scores_relu(qi_np, w_np[i], keys_np, ctx)
-        qc.check_selection(sel[i], n_sel[i], sc, ctx, 1, 2048)
-        toks = orc.selected_tokens(sel[i, :n_sel[i]], ctx, 1)
-        lr = _rows(seed, S("latent"), toks, 576)[:, None, :]
         qb = qi.normal_bf16(seed, S("q"), i * 64 * 576, 64 * 576).reshape(64, 576)
-        o_ref, lse_ref = orc.attend(qb, lr, lr, np.arange(toks.size), 1.0 / 24, dv=512)
-        qc.check_attention(o[i], lse[i], o_ref, lse_ref, ob[i])
+
+        def attend_ref(toks, qb=qb):
+            lr = _rows(seed, S("latent"), toks, 576)[:, None, :]
+            return orc.attend(qb, lr, lr, np.arange(toks.size), 1.0 / 24, dv=512)
+
+        qc.check_row_with(sel[i], n_sel[i], o[i], lse[i], ob[i], sc, ctx, 1, 2048, attend_ref)
+
+
+def test_mla_decode_full_size(Q):
+    """The shared-latent decode step as the benchmark times it: batch 8 at
+    context 131,072, layer 0 of the workload's inputs, one call chain per
+    step in its launch configuration (32 splits). Every query is checked
+    against the oracle: the whole score row (131,072 tokens) and the top-2048
+    from the oracle's own scores, then the attention over the selected latent
+    rows regenerated by index. Query 5's indexer head weights are all
+    negative (the workload's draw): its best scores are exact zeros and its
+    selection is the 2,048 smallest-index zero-score tokens."""
+    pkg, pipeline = Q
+    from qsa_inputs.gpu import fill_normal_bf16
+    L, B = 131072, 8
+    seed = qi.config_seed(5)
+    _print_case("mla_decode_full", ctx=L, batch=B)
+    S = lambda s, kind: qi.stream_id(0, s, kind)
+    lat = torch.empty(B, L, 1, 576, dtype=torch.bfloat16, device="cuda")
+    keys = torch.empty(B, L, 64, dtype=torch.bfloat16, device="cuda")
+    q = torch.empty(B, 64, 576, dtype=torch.bfloat16, device="cuda")
+    q_idx = torch.empty(B, 4, 64, dtype=torch.bfloat16, device="cuda")
+    for s in range(B):
+        for t, kind in ((lat, "latent"), (keys, "raw_key"), (q, "q"), (q_idx, "q_idx")):
+            fill_normal_bf16(t[s], seed, S(s, kind))
+    w_np = np.stack([qi.uniform_f32(seed, S(s, "w_idx"), 4) for s in range(B)])
+    assert np.all(w_np[5] < 0), "the workload's query 5 has all-negative head weights"
+    kv = pkg.make_kv(lat, lat)
+    q_ctx, q_seq = qc.i32([L] * B), qc.i32(range(B))
+    bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, B, L)
+    assert bufs.n_split == 32
+    pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq,
+                          w_idx=torch.tensor(w_np, device="cuda"))
+    torch.cuda.synchronize()
+    if bufs.layer_ws is not None:
+        pkg.check_decode_layer_error(bufs.layer_ws)
+    sel, n_sel = bufs.sel.cpu().numpy(), bufs.n_sel.cpu().numpy()
+    o, lse, ob = bufs.o.cpu().numpy(), bufs.lse.cpu().numpy(), qc.from_dev_bits(bufs.o_bf16)
+    got_sc = bufs.scores.cpu().numpy()
+    for i in range(B):
+        keys_np = qi.normal_bf16(seed, S(i, "raw_key"), 0, L * 64).reshape(L, 64)
+        qi_np = qi.normal_bf16(seed, S(i, "q_idx"), 0, 256).reshape(4, 64)
+        sc = orc.index_scores_relu(qi_np, w_np[i], keys_np, L)
+        # fp32 accumulation of 64 exact products per head, then 4 weighted terms
+        bound = 70 * 2.0 ** -24 * ((np.abs(orc.bf16_to_f64(keys_np)) @ np.abs(orc.bf16_to_f64(qi_np)).T)
+                                   @ np.abs(w_np[i].astype(np.float64))) + 1e-30
+        assert np.all(np.abs(got_sc[i, :L] - sc) <= bound), f"query {i}: scores"
+        qb = qi.normal_bf16(seed, S(i, "q"), 0, 64 * 576).reshape(64, 576)
+
+        def attend_ref(toks, qb=qb, i=i):
+            lr = _rows(seed, S(i, "latent"), toks, 576)[:, None, :]
+            return orc.attend(qb, lr, lr, np.arange(toks.size), 1.0 / 24, dv=512)
+
+        qc.check_row_with(sel[i], n_sel[i], o[i], lse[i], ob[i], sc, L, 1, 2048, attend_ref)
+        if i == 5:  # ties at zero, decided by index
+            assert np.all(sc[sel[i, :n_sel[i]]] == 0.0)

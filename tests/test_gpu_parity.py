@@ -311,9 +311,10 @@ def test_decode_layer_end_to_end(Q, ctxs):
     for i, r in enumerate(refs):
         nb = ctxs[i] // 4
         assert np.array_equal(pooled_np[i, :nb], r["pooled"])
-        same = qc.check_selection(sel[i], n_sel[i], r["scores"], ctxs[i], 4, 512)
-        if same:
-            qc.check_attention(o[i], lse[i], r["o"], r["lse"], ob[i])
+        # every row's attention is checked: against the oracle's result, or
+        # after a tolerated boundary swap against the oracle on the GPU's selection
+        qc.check_row(sel[i], n_sel[i], o[i], lse[i], ob[i], r, ctxs[i], 4, 512, case.q[i], case.k[i], case.v[i],
+                     1.0 / 16)
 
 
 def test_decode_is_deterministic(Q):

@@ -108,6 +108,12 @@ def test_fp8_keys(Q):
     pkg.qsa_quantize_keys(kd, k8)
     fused, ref = _both(pkg, pkg.SEL_B_FP8, ctxs, max_ctx, qc.to_dev(q_idx), torch.tensor(w, device="cuda"), k8)
     _assert_same(fused, ref)
+    # end to end: the oracle quantizes the bf16 keys itself, scores them and
+    # selects; every query's selection must be the oracle's (boundary rule)
+    codes, scales = orc.fp8_keys(keys)
+    for i, ctx in enumerate(ctxs):
+        sc = orc.index_scores_relu_fp8(q_idx[i], w[i], codes, scales, ctx)
+        qc.check_selection(fused[0][i], fused[1][i], sc, ctx, 1, TOPK)
 
 
 def _planted(seed, nq, max_ctx, sampled_high):

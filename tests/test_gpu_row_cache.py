@@ -1,5 +1,5 @@
 """GPU checks of the HBM row cache over K/V rows in pinned host memory
-(qsa_row_cache_step + qsa_sparse_decode_cached; "3090x3で 314 万コンテキスト",
+(qsa_row_cache_step + qsa_sparse_decode_cached; "125B MoE を 3090 3 枚で運用する vLLM 最適化編",
 section 5).
 
 A hit reads the same bytes the host holds and the arithmetic is unchanged,
