@@ -399,6 +399,33 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
 size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
                                         int32_t nq, int32_t max_ctx, int32_t n_split);
 
+/* ------------------------------------- A2-A5, no caller workspace ----
+ * qsa_decode_layer_noalloc: for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). Computes exactly what qsa_decode_layer computes, bit for bit,
+ * with the same kernels, but its workspace is a static array in the
+ * library's device code (16 MiB = 16,777,216 bytes, one per device, held
+ * until the process ends) instead of a caller buffer; it allocates and frees
+ * nothing. Arguments as qsa_decode_layer, without ws / ws_bytes.
+ *   - A call needs qsa_decode_layer_workspace_bytes(sel_cfg, attn_cfg, nq,
+ *     max_ctx, n_split) bytes of it (e.g. 1.15 MiB for 4 queries at
+ *     1,048,320 tokens with 16 splits); a larger call returns
+ *     QSA_ERR_UNSUPPORTED and launches nothing.
+ *   - Each call clears the control words it relies on (the error word and
+ *     the merge counters) in its first launch, so the contents left by an
+ *     earlier call do not matter.
+ *   - Every call on one device shares that device's array: calls that
+ *     overlap on one device (different streams or threads without ordering)
+ *     race and their results are unspecified. Serialize them.
+ *   - A timed-out merge wait is reported with QSA_SYNC_CHECK=1 as for
+ *     qsa_decode_layer; the error word is not otherwise readable. */
+qsa_status qsa_decode_layer_noalloc(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                    const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                                    const qsa_bf16* q_idx, const void* keys, int64_t keys_seq_stride,
+                                    const qsa_bf16* q, const qsa_kv* kv, float* scores, int64_t ld_scores,
+                                    int32_t* sel, int32_t* n_sel, int32_t n_split, float* o_out,
+                                    qsa_bf16* o_out_bf16, float* lse_out, qsa_stream_t stream);
+
 /* ------------------------------------------- A4 with an HBM row cache ----
  * For K/V rows kept in host memory (pinned, read zero-copy): a direct-mapped
  * cache of rows in device memory that later decode steps read instead of

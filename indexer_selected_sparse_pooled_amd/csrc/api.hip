@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/qsa.h"
@@ -593,22 +594,55 @@ size_t qsa_decode_layer_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_at
       .ws_bytes;
 }
 
-qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
-                            const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
-                            const void* keys, int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
-                            float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, int32_t n_split,
-                            float* o_out, qsa_bf16* o_out_bf16, float* lse_out, void* ws, size_t ws_bytes,
-                            qsa_stream_t stream) {
+namespace {
+
+// Scratch of qsa_decode_layer_noalloc: one array per device, kept until the
+// process ends. In host code `scratch` names a host-side stand-in, not the
+// device array: its device address comes from hipGetSymbolAddress, looked up
+// once per device (scratch_on_device) and used everywhere host code needs it.
+constexpr size_t kNoallocScratchBytes = size_t(16) << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64];
+
+// The current device's address of `scratch` (looked up on the first call on
+// that device, with that device current).
+qsa_status scratch_on_device(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(QSA_ERR_DEVICE, "no HIP device");
+  if (dev < 0 || dev >= 64) return fail(QSA_ERR_DEVICE, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(QSA_ERR_DEVICE, "cannot find the device address of the static scratch: %s", hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return QSA_OK;
+}
+
+// qsa_decode_layer with the workspace given (noalloc false) or the static
+// scratch (noalloc true: ws / ws_bytes are ignored, the call's control words
+// are cleared by its first launch).
+qsa_status decode_layer_call(const char* fn, const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
+                             const void* keys, int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
+                             float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, int32_t n_split,
+                             float* o_out, qsa_bf16* o_out_bf16, float* lse_out, void* ws, size_t ws_bytes,
+                             bool noalloc, qsa_stream_t stream) {
   qsa_status st = check_sel_cfg(sel_cfg);
   if (st != QSA_OK) return st;
   if (sel_cfg->block != 4 || sel_cfg->idx_dim != 128 || sel_cfg->idx_heads != 1)
-    return fail(QSA_ERR_UNSUPPORTED, "qsa_decode_layer: only pooled 4-token blocks with a 128-d single-head indexer");
+    return fail(QSA_ERR_UNSUPPORTED, "%s: only pooled 4-token blocks with a 128-d single-head indexer", fn);
   st = check_attn_inputs(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel);
   if (st != QSA_OK) return st;
   if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
   if (nq == 0) return QSA_OK;
   if (nq > 4096) return fail(QSA_ERR_UNSUPPORTED, "nq > 4096");
-  if (kv->format != QSA_KV_BF16) return fail(QSA_ERR_UNSUPPORTED, "qsa_decode_layer: bf16 K/V rows only");
+  if (kv->format != QSA_KV_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s: bf16 K/V rows only", fn);
   if (!q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
   if (!o_out && !o_out_bf16 && !lse_out) return fail(QSA_ERR_ARG, "no output requested");
   if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
@@ -622,11 +656,23 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
                                                            attn_cfg->dv, n_split);
   if (int64_t(nq) * (plan.itk.n_chunks + attn_cfg->hkv * n_split) > 0x7FFFFFFF)
     return fail(QSA_ERR_UNSUPPORTED, "too many work items");
-  if (!ws || ws_bytes < plan.ws_bytes)
-    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
-  if (!aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  if (noalloc) {
+    if (plan.ws_bytes > kNoallocScratchBytes)
+      return fail(QSA_ERR_UNSUPPORTED,
+                  "%s: this call needs %zu bytes of scratch; the static scratch holds %zu (use qsa_decode_layer "
+                  "with a workspace of qsa_decode_layer_workspace_bytes)",
+                  fn, plan.ws_bytes, kNoallocScratchBytes);
+  } else {
+    if (!ws || ws_bytes < plan.ws_bytes)
+      return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+    if (!aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  }
   st = check_device();
   if (st != QSA_OK) return st;
+  if (noalloc) {
+    st = scratch_on_device(&ws);
+    if (st != QSA_OK) return st;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
   if (st != QSA_OK) return st;
@@ -649,13 +695,37 @@ qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn
   at.o_out = o_out;
   at.o_bf16 = o_out_bf16;
   at.lse_out = lse_out;
-  const qsa_status fs = finish(qsa::launch_decode_layer(it, at, plan, ws, s), s, "qsa_decode_layer");
+  const qsa_status fs = finish(qsa::launch_decode_layer(it, at, plan, ws, s, noalloc), s, fn);
   if (fs != QSA_OK || !env_on("QSA_SYNC_CHECK")) return fs;
   uint32_t err = 0;
   if (hipMemcpy(&err, ws, 4, hipMemcpyDeviceToHost) != hipSuccess)
-    return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: cannot read the error word");
-  if (err) return fail(QSA_ERR_LAUNCH, "qsa_decode_layer: a merge wait ran out (error word %u)", err);
+    return fail(QSA_ERR_LAUNCH, "%s: cannot read the error word", fn);
+  if (err) return fail(QSA_ERR_LAUNCH, "%s: a merge wait ran out (error word %u)", fn, err);
   return QSA_OK;
+}
+
+}  // namespace
+
+qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                            const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q_idx,
+                            const void* keys, int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
+                            float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel, int32_t n_split,
+                            float* o_out, qsa_bf16* o_out_bf16, float* lse_out, void* ws, size_t ws_bytes,
+                            qsa_stream_t stream) {
+  return decode_layer_call("qsa_decode_layer", sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q_idx, keys,
+                           keys_seq_stride, q, kv, scores, ld_scores, sel, n_sel, n_split, o_out, o_out_bf16, lse_out,
+                           ws, ws_bytes, false, stream);
+}
+
+qsa_status qsa_decode_layer_noalloc(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                    const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                                    const qsa_bf16* q_idx, const void* keys, int64_t keys_seq_stride,
+                                    const qsa_bf16* q, const qsa_kv* kv, float* scores, int64_t ld_scores,
+                                    int32_t* sel, int32_t* n_sel, int32_t n_split, float* o_out,
+                                    qsa_bf16* o_out_bf16, float* lse_out, qsa_stream_t stream) {
+  return decode_layer_call("qsa_decode_layer_noalloc", sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q_idx, keys,
+                           keys_seq_stride, q, kv, scores, ld_scores, sel, n_sel, n_split, o_out, o_out_bf16, lse_out,
+                           nullptr, 0, true, stream);
 }
 
 qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,

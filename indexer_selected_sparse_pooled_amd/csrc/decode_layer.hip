@@ -46,6 +46,8 @@ struct SelAttnLds {
 template <int TPW, bool kFp8>
 __global__ __launch_bounds__(256) void index_lists_a(IndexTopkArgs a) {
   __shared__ itk::FinalLds sh;
+  if (a.clear && blockIdx.x == 0 && blockIdx.y == 0)
+    for (int j = threadIdx.x; j < a.n_clear; j += 256) a.clear[j] = 0u;
   itk::chunk_step<TPW, false, kFp8>(a, blockIdx.y, blockIdx.x, sh);
 }
 
@@ -167,9 +169,11 @@ DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv
 }
 
 hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLayerPlan& p, void* ws,
-                               hipStream_t s) {
+                               hipStream_t s, bool clear_control) {
   if (itk.nq <= 0) return hipSuccess;
   char* w = static_cast<char*>(ws);
+  itk.clear = clear_control ? reinterpret_cast<uint32_t*>(w) : nullptr;
+  itk.n_clear = clear_control ? int(p.off_itk / 4) : 0;
   char* wi = w + p.off_itk;
   att.o_part = reinterpret_cast<float*>(w + p.off_o);
   att.lse_part = reinterpret_cast<float*>(w + p.off_lse);
@@ -180,6 +184,8 @@ hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLa
 
   hipError_t e = launch_index_lists(itk, p.itk, wi, s);
   if (e != hipSuccess) return e;
+  itk.clear = nullptr;
+  itk.n_clear = 0;
   itk.counter = reinterpret_cast<uint32_t*>(wi);
   itk.list = reinterpret_cast<uint64_t*>(wi + p.itk.off_list);
   itk.list_bound = reinterpret_cast<uint64_t*>(wi + p.itk.off_bound);

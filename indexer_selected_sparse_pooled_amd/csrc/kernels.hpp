@@ -190,6 +190,10 @@ struct IndexTopkArgs {
   int chunk_blocks;      // blocks per chunk
   int keep;              // candidates kept per chunk
   int wkeep;             // candidates kept per wave
+  // words the first work-group of index_lists_a zeroes before it scans
+  // (control words a later launch of the same call relies on), or NULL
+  uint32_t* clear;
+  int n_clear;
 };
 struct IndexTopkPlan {
   int tpw;        // 64-key tiles per wave (chunk = 256 * tpw keys)
@@ -211,9 +215,12 @@ struct DecodeLayerPlan {
   size_t off_merge_cnt, off_itk, off_o, off_lse, ws_bytes;
 };
 DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv, int dv, int n_split);
-// itk / att: everything but the workspace views (filled in from ws)
+// itk / att: everything but the workspace views (filled in from ws).
+// clear_control: the scan launch zeroes the workspace's control words (the
+// error word and the merge counters, bytes [0, p.off_itk)) first, so their
+// contents on entry do not matter.
 hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLayerPlan& p, void* ws,
-                               hipStream_t s);
+                               hipStream_t s, bool clear_control = false);
 
 hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, int64_t o_ps,
                         const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,

@@ -82,6 +82,8 @@ _SIGS = {
     "qsa_decode_layer": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i32,
                          _vp, _vp, _vp, _vp, _sz, _vp],
     "qsa_decode_layer_workspace_bytes": [_vp, _vp, _i32, _i32, _i32],
+    "qsa_decode_layer_noalloc": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
+                                 _i32, _vp, _vp, _vp, _vp],
     "qsa_sparse_decode": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp],
     "qsa_row_cache_bytes": [_vp, _i64],
     "qsa_decode_cached_plan_bytes": [_vp, _i32],
@@ -357,6 +359,28 @@ def check_decode_layer_error(ws) -> None:
         raise QsaError("qsa_decode_layer", 4, f"error word {e:#x}: a bounded wait in the layer ran out")
 
 
+def _decode_layer_args(fn, sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel, n_split,
+                       o_out, o_out_bf16, lse_out, q_seq):
+    nq = q_ctx.shape[0]
+    _rowmajor_tail(q_idx, "q_idx", 3)
+    _rowmajor_tail(scores, "scores", 1)
+    kp, kss = _keys_arg(sel_cfg, keys, max_ctx, fn)
+    if sel.shape != (nq, sel_cfg.topk) or not sel.is_contiguous():
+        raise ValueError(f"{fn}: sel must be a contiguous [nq, topk] tensor")
+    if not q.is_contiguous():
+        raise ValueError(f"{fn}: q must be contiguous")
+    for t, shp, name in ((o_out, (nq, attn_cfg.hq, attn_cfg.dv), "o_out"),
+                         (o_out_bf16, (nq, attn_cfg.hq, attn_cfg.dv), "o_out_bf16"),
+                         (lse_out, (nq, attn_cfg.hq), "lse_out")):
+        if t is not None and (tuple(t.shape) != shp or not t.is_contiguous()):
+            raise ValueError(f"{fn}: {name} must be a contiguous {list(shp)} tensor")
+    return [ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"),
+            max_ctx, _dev(q_idx, _BF16, "q_idx"), kp, kss, _dev(q, _BF16, "q"),
+            ctypes.byref(kv), _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"),
+            _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_out, _F32, "o_out"), _dev(o_out_bf16, _BF16, "o_out_bf16"),
+            _dev(lse_out, _F32, "lse_out")]
+
+
 def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel, n_split, ws,
                      o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
     """One decode layer (two launches): qsa_index_topk, then qsa_sparse_decode
@@ -364,26 +388,20 @@ def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scor
     bf16 (or FP8 pages, see qsa_index_scores); q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk;
     o_out: [nq, hq, dv] fp32, o_out_bf16: [nq, hq, dv] bf16, lse_out: [nq, hq]
     fp32 (each optional); ws: decode_layer_workspace(...)."""
-    nq = q_ctx.shape[0]
-    _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(scores, "scores", 1)
-    kp, kss = _keys_arg(sel_cfg, keys, max_ctx, "qsa_decode_layer")
-    if sel.shape != (nq, sel_cfg.topk) or not sel.is_contiguous():
-        raise ValueError("qsa_decode_layer: sel must be a contiguous [nq, topk] tensor")
-    if not q.is_contiguous():
-        raise ValueError("qsa_decode_layer: q must be contiguous")
-    for t, shp, name in ((o_out, (nq, attn_cfg.hq, attn_cfg.dv), "o_out"),
-                         (o_out_bf16, (nq, attn_cfg.hq, attn_cfg.dv), "o_out_bf16"),
-                         (lse_out, (nq, attn_cfg.hq), "lse_out")):
-        if t is not None and (tuple(t.shape) != shp or not t.is_contiguous()):
-            raise ValueError(f"qsa_decode_layer: {name} must be a contiguous {list(shp)} tensor")
+    args = _decode_layer_args("qsa_decode_layer", sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel,
+                              n_sel, n_split, o_out, o_out_bf16, lse_out, q_seq)
     _check("qsa_decode_layer", lib().qsa_decode_layer(
-        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"),
-        max_ctx, _dev(q_idx, _BF16, "q_idx"), kp, kss, _dev(q, _BF16, "q"),
-        ctypes.byref(kv), _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"),
-        _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_out, _F32, "o_out"), _dev(o_out_bf16, _BF16, "o_out_bf16"),
-        _dev(lse_out, _F32, "lse_out"), ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(),
-        _stream(stream)))
+        *args, ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
+
+
+def qsa_decode_layer_noalloc(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel, n_split,
+                             o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
+    """qsa_decode_layer without a workspace argument: the library's static
+    device scratch (16 MiB per device) serves as the workspace. Calls on one
+    device must not overlap."""
+    args = _decode_layer_args("qsa_decode_layer_noalloc", sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv,
+                              scores, sel, n_sel, n_split, o_out, o_out_bf16, lse_out, q_seq)
+    _check("qsa_decode_layer_noalloc", lib().qsa_decode_layer_noalloc(*args, _stream(stream)))
 
 
 def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None, raw_keys=None, pooled=None,

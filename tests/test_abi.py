@@ -164,3 +164,22 @@ def test_prefill_select_workspace_and_host_validation(lib):
     ws64 = qsa.qsa_index_topk_prefill_workspace_bytes(qsa.SEL_B, 64, ctx)
     assert call(qsa.SEL_B, 64, ws64 - 1) == 3
     assert call(qsa.SEL_B, 0, 0) == 0      # no work
+
+
+def test_noalloc_decode_layer_refuses_beyond_its_scratch_on_the_host(lib):
+    """qsa_decode_layer_noalloc needs no workspace argument, and a call whose
+    workspace need exceeds the library's 16 MiB static scratch is refused on
+    the host (nothing launched, no device needed); so is a malformed one."""
+    from indexer_selected_sparse_pooled_amd import qsa
+    fake = ctypes.c_void_p(1 << 20)  # never dereferenced: every call below fails validation
+    kv = qsa.KV(fake, fake, 1 << 30, 512, 256, 1 << 20, 0)
+
+    def call(nq, max_ctx, n_split, cfg=qsa.SEL_A):
+        return lib.qsa_decode_layer_noalloc(ctypes.byref(cfg), ctypes.byref(qsa.ATTN_A), nq, fake, fake, max_ctx,
+                                            fake, fake, 1 << 24, fake, ctypes.byref(kv), fake, max_ctx // 4, fake,
+                                            fake, n_split, fake, None, None, None)
+    assert qsa.qsa_decode_layer_workspace_bytes(qsa.SEL_A, qsa.ATTN_A, 8, 4096, 256) > 16 << 20
+    assert call(8, 4096, 256) == 2 and b"static scratch" in lib.qsa_last_error()
+    assert call(1, 4096, 300) == 1                  # n_split out of range
+    assert call(1, 4096, 16, qsa.SEL_B) == 2        # the token-level indexer
+    assert call(0, 4096, 16) == 0                   # no work
