@@ -38,6 +38,8 @@ BF16_PEAK_TFLOPS = 2500.0
 
 DECODE = dict(name="decode L=1048320 B=4 12 layers, 16 q heads / 2 kv heads, head_dim 256, top-512 of 4-token blocks",
               config_id=3, ctx=1048320, batch=4, layers=12)
+SMALL_DECODES = (dict(name="decode L=8192 B=1 1 layer", config_id=1, ctx=8192, layers=1),
+                 dict(name="decode L=131072 B=1 12 layers run in sequence", config_id=2, ctx=131072, layers=12))
 MLA = dict(name="shared-latent variant: 64 q heads over one 576-wide bf16 latent row per token (V = first 512), "
                 "token indexer 4 heads x 64-d ReLU-weighted, top-2048 tokens, context 131072",
            config_id=5, ctx=131072, batch=8, chunk=2048, tiles=(131072, 32768))
@@ -155,6 +157,8 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
     ms, wall, graph = time_graph(torch, lambda: step(True), steps, warmup)
     ms_med, ms_mean_each = replay_median(torch, graph, steps)
     del graph
+    for bf in bufs:  # every bounded merge wait of the timed replays ended in time
+        pkg.check_decode_layer_error(bf.layer_ws)
     # the same step as separate calls (index_topk, sparse_decode, lse_merge)
     ms_sep, _, graph = time_graph(torch, lambda: step(False), max(10, steps // 2), warmup)
     del graph
@@ -239,6 +243,8 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
 
     ms_fp8, _, graph = time_graph(torch, step_fp8, steps, warmup)
     del graph
+    for bf in bufs:
+        pkg.check_decode_layer_error(bf.layer_ws)
     lists_fp8_ms = time_launches(torch, lists_fp8, reps) / len(layers)
     for lay in layers:
         del lay["pooled_fp8"]
@@ -266,6 +272,9 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
 
     ms_two, _, graph = time_graph(torch, step_two_streams, steps, warmup)
     del graph
+    for h in halves:
+        for bf in h[4]:
+            pkg.check_decode_layer_error(bf.layer_ws)
     step(True)  # the batch-4 step again (the FP8 leg above reused its buffers)
     torch.cuda.synchronize()
     for l, bf in enumerate(bufs):  # the same outputs as the batch-4 step, bit for bit
@@ -281,6 +290,49 @@ def run_decode(pkg, pipeline, bm, qi, torch, steps, warmup):
                 ms_fp8=ms_fp8, step_bytes_fp8=bm.decode_unit_bytes_fp8(L) * B * len(layers),
                 lists_fp8_ms=lists_fp8_ms, lists_fp8_gbs=scan_fp8_bytes / (lists_fp8_ms * 1e-3) / 1e9,
                 ms_two=ms_two, rcache=rcache, layers=layers, bufs=bufs)
+
+
+def run_small_decode(pkg, pipeline, bm, qi, torch, cfg, steps, warmup):
+    """A batch-1 decode workload (8,192 tokens and 1 layer, or 131,072 tokens
+    and 12 layers run in sequence): one qsa_decode_layer call per layer,
+    the step captured in a graph. These steps take tens of microseconds, so
+    they are replayed at least 500 times."""
+    L, NL = cfg["ctx"], cfg["layers"]
+    seed = qi.config_seed(cfg["config_id"])
+    layers = []
+    for l in range(NL):
+        raw = torch.empty(1, L, 128, dtype=torch.bfloat16, device="cuda")
+        k = torch.empty(1, L, 2, 256, dtype=torch.bfloat16, device="cuda")
+        v = torch.empty(1, L, 2, 256, dtype=torch.bfloat16, device="cuda")
+        q = torch.empty(1, 16, 256, dtype=torch.bfloat16, device="cuda")
+        q_idx = torch.empty(1, 1, 128, dtype=torch.bfloat16, device="cuda")
+        for t, kind in ((raw, "raw_key"), (k, "k"), (v, "v"), (q, "q"), (q_idx, "q_idx")):
+            fill(t[0], seed, qi.stream_id(l, 0, kind))
+        pooled = torch.empty(1, L // 4, 128, dtype=torch.bfloat16, device="cuda")
+        pkg.qsa_pool_keys(raw, pooled, block=4)
+        layers.append(dict(q=q, q_idx=q_idx, pooled=pooled, kv=pkg.make_kv(k, v), k=k, v=v))
+    q_ctx = torch.full((1,), L, dtype=torch.int32, device="cuda")
+    q_seq = torch.zeros(1, dtype=torch.int32, device="cuda")
+    bufs = [pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, 1, L) for _ in layers]
+
+    def step():
+        for lay, bf in zip(layers, bufs):
+            pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, L, lay["q_idx"], lay["pooled"], lay["q"], lay["kv"],
+                                  bf, q_seq=q_seq, fused=True)
+
+    reps = max(500, steps)
+    ms, _, graph = time_graph(torch, step, reps, max(20, warmup))
+    med, _ = replay_median(torch, graph, reps)
+    del graph
+    for bf in bufs:
+        pkg.check_decode_layer_error(bf.layer_ws)
+    step_bytes = bm.decode_unit_bytes(L) * NL
+    out = dict(workload=cfg["name"], ctx=L, batch=1, layers=NL, n_split=bufs[0].n_split, replays=reps,
+               ms_per_step=round(ms, 5), ms_per_step_median=round(med, 5), steps_s=round(1e3 / ms, 1),
+               step_bytes=step_bytes, hbm_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
+               hbm_frac=round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4))
+    log(f"{cfg['name']}: {ms * 1e3:.1f} us/step")
+    return out
 
 
 ROW_CACHE_SLOTS = 65536  # 128 MiB per layer: about 8 steps of batch-4 rows
@@ -500,10 +552,10 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
         def chunk():
             pipeline.prefill_chunk(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q_idx, pooled, q, kv, bufs)
 
-        ms, wall, g = time_graph(torch, chunk, max(3, steps // 5), max(1, warmup))
+        ms, wall, g = time_graph(torch, chunk, max(10, steps // 5), max(2, warmup))
         out[tile] = dict(ms=ms, tok_s=C / (ms * 1e-3), tflops=flops["total"] / (ms * 1e-3) / 1e12)
         if tile == PREFILL["tiles"][0]:
-            r = max(3, steps // 10)
+            r = max(10, steps // 10)
             t_sc = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_A, q_ctx, ctx_max, q_idx, pooled,
                                                                      bufs.scores), r)
             t_tk = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, ctx_max, bufs.scores, bufs.sel,
@@ -535,7 +587,7 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
     def chunk_c():
         pipeline.prefill_chunk(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q_idx_c, pooled, q, kv, bufs)
 
-    ms_c, _, g = time_graph(torch, chunk_c, max(3, steps // 5), max(1, warmup))
+    ms_c, _, g = time_graph(torch, chunk_c, max(10, steps // 5), max(2, warmup))
     del g
 
     def tiles_c():
@@ -543,7 +595,7 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
             pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, bufs.sel, bufs.n_sel, a0, a1,
                                    bufs.o_tiles[t], bufs.lse_tiles[t])
 
-    t_at_c = time_launches(torch, tiles_c, max(3, steps // 10))
+    t_at_c = time_launches(torch, tiles_c, max(10, steps // 10))
     sel = bufs.sel.cpu().numpy()
     ov = [np.intersect1d(sel[i], sel[i - 1]).size / 512 for i in range(1, C)]
     out["correlated"] = dict(workload=f"the same chunk with AR(1) indexer queries over positions (rho {rho})",
@@ -666,11 +718,11 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
         def chunk():
             pipeline.prefill_chunk(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, pb, w_idx=w)
 
-        ms_p, _, g = time_graph(torch, chunk, max(3, steps // 10), max(1, warmup // 2))
+        ms_p, _, g = time_graph(torch, chunk, max(10, steps // 10), max(2, warmup // 2))
         del g
         pre[tile] = dict(ms=ms_p, tok_s=C / (ms_p * 1e-3), tflops=flops["total"] / (ms_p * 1e-3) / 1e12)
         if tile == MLA["tiles"][0]:
-            r = max(3, steps // 20)
+            r = max(10, steps // 20)
             t_sc = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, pb.scores,
                                                                      w_idx=w), r)
             t_tk = time_launches(torch, lambda: pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, pb.scores, pb.sel, pb.n_sel,
@@ -693,7 +745,7 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
             def chunk8():
                 pipeline.prefill_chunk(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv8, pb, w_idx=w)
 
-            ms8, _, g = time_graph(torch, chunk8, max(3, steps // 10), max(1, warmup // 2))
+            ms8, _, g = time_graph(torch, chunk8, max(10, steps // 10), max(2, warmup // 2))
             del g
             a0, a1 = pb.tiles[0]
             t_at8 = time_launches(torch, lambda: pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv8, pb.sel,
@@ -741,79 +793,214 @@ def counter_traffic(kernel: str, groups: str):
     return None
 
 
-def cpu_baseline(qi, orc, bm):
-    """The oracle on one (layer, sequence) unit of the decode workload: scan of
-    262,080 pooled keys, top-512 selection, attention over the 2,048 selected
-    tokens (input generation and pooling excluded), repeated for about 10 s
-    (a step has 48 such units; steps/s is scaled accordingly)."""
+# ---------------------------------------------------------------- oracle --
+# The CPU oracle (oracle/qsa_oracle.py, float64 numpy, as it stands) timed on
+# the host cores: units of each workload (one query in one layer, which is
+# how the oracle computes) run in a pool of single-threaded worker processes,
+# one per core, each for a fixed time after building its inputs; throughput
+# is units per second of wall time over the pool, scaled to the metric's unit.
+
+ORACLE_UNITS = {
+    1: ("steps/s", 1, "one decode step: scan of 2,048 pooled keys, top-512, attention over 2,048 tokens"),
+    2: ("steps/s", 12, "one of the 12 layers of a step: scan of 32,768 pooled keys, top-512, attention over "
+                       "2,048 tokens"),
+    3: ("steps/s", 48, "one (layer, sequence) unit of the step: scan of 262,080 pooled keys, top-512, attention "
+                       "over 2,048 tokens"),
+    4: ("tok/s", 1, "one query of the chunk: scores of its 15,000..16,023 blocks, top-512, attention tile by tile "
+                    "(8,192-token tiles) and the log-sum-exp merge"),
+    "5a": ("tok/s", 1, "one query of the chunk: ReLU-weighted scores of its 129,025..131,072 tokens, top-2048, "
+                       "attention of 64 heads over 2,048 latent rows"),
+    "5b": ("steps/s", 8, "one query of the batch-8 step: scores of 131,072 tokens, top-2048, attention of 64 heads "
+                         "over 2,048 latent rows"),
+}
+
+
+def _gen_rows(qi, seed, stream, toks, width):
+    """Rows `toks` of a [tokens][width] bf16 tensor filled by the generator."""
     import numpy as np
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    L = DECODE["ctx"]
+    idx = (np.asarray(toks, dtype=np.int64)[:, None] * width + np.arange(width)[None, :]).reshape(-1)
+    return qi.normal_bf16(seed, stream, 0, index=idx.astype(np.uint64)).reshape(len(toks), width)
+
+
+def _one_thread():
+    """Limit this worker's numeric libraries to one thread (numpy and the
+    oracle are imported first, so their thread pools exist to be limited)."""
+    import numpy  # noqa: F401
+
+    from oracle import qsa_oracle  # noqa: F401
+    from threadpoolctl import threadpool_limits
+    return threadpool_limits(limits=1)
+
+
+def _pool_slice(task):
+    """Pool blocks [b0, b1) of the 1M-token decode workload's layer 0,
+    sequence 0 into the shared pooled-key array (input preparation)."""
+    shm_name, nb, b0, b1 = task
+    from multiprocessing import shared_memory
+
+    import numpy as np
+
+    import qsa_inputs as qi
+    from oracle import qsa_oracle as orc
+    keep = _one_thread()
     seed = qi.config_seed(DECODE["config_id"])
-    t0 = time.time()
-    raw = qi.normal_bf16(seed, qi.stream_id(0, 0, "raw_key"), 0, L * 128).reshape(L, 128)
-    pooled = orc.pool_keys(raw, 4)
-    del raw
-    q_idx = qi.normal_bf16(seed, qi.stream_id(0, 0, "q_idx"), 0, 128)
-    q = qi.normal_bf16(seed, qi.stream_id(0, 0, "q"), 0, 16 * 256).reshape(16, 256)
-    # the selection does not change between repetitions: generate the K/V rows it reads once
-    s0 = orc.index_scores(q_idx, pooled, L // 4)
-    toks0 = orc.selected_tokens(orc.select_blocks(s0, L, 4, 512), L, 4)
-    idx = (toks0[:, None, None] * 512 + np.arange(2)[None, :, None] * 256 + np.arange(256)[None, None, :])
-    k_rows = qi.normal_bf16(seed, qi.stream_id(0, 0, "k"), 0, index=idx.reshape(-1).astype(np.uint64))
-    v_rows = qi.normal_bf16(seed, qi.stream_id(0, 0, "v"), 0, index=idx.reshape(-1).astype(np.uint64))
-    k_rows, v_rows = k_rows.reshape(-1, 2, 256), v_rows.reshape(-1, 2, 256)
-    row_of = {int(t): r for r, t in enumerate(toks0)}
-    prep_s = time.time() - t0
-    # repeat the unit for about 10 s of CPU work (at least 16 times)
-    reps = 0
+    raw = qi.normal_bf16(seed, qi.stream_id(0, 0, "raw_key"), 4 * b0 * 128, 4 * (b1 - b0) * 128)
+    shm = shared_memory.SharedMemory(name=shm_name)
+    pooled = np.ndarray((nb, 128), dtype=np.uint16, buffer=shm.buf)
+    pooled[b0:b1] = orc.pool_keys(raw.reshape(-1, 128), 4)
+    del pooled, keep
+    shm.close()
+    return b1 - b0
+
+
+def _oracle_worker(task):
+    """One worker's share of an oracle measurement: build the inputs of its
+    units (not timed), then run units for `budget` seconds on one thread.
+    Returns (units, seconds, setup_seconds)."""
+    cfg, worker, n_workers, budget, shm_name = task
+    keep = _one_thread()
+    import numpy as np
+
+    import qsa_inputs as qi
+    from oracle import qsa_oracle as orc
+    t_setup = time.perf_counter()
+    units = []  # callables, run round-robin
+    max_units = 8  # distinct units a worker prepares (queries spread over the chunk)
+    shm = None
+
+    def gen(seed, stream, n):
+        return qi.normal_bf16(seed, stream, 0, n)
+
+    if cfg in (1, 2, 3):
+        L = {1: 8192, 2: 131072, 3: DECODE["ctx"]}[cfg]
+        seed = qi.config_seed(cfg)
+        layer, seq = {1: (0, 0), 2: (worker % 12, 0), 3: (0, 0)}[cfg]
+        S = lambda kind: qi.stream_id(layer, seq, kind)
+        if cfg == 3:  # pooled in parallel beforehand (_pool_slice), shared by the workers
+            from multiprocessing import shared_memory
+            shm = shared_memory.SharedMemory(name=shm_name)
+            pooled = np.ndarray((L // 4, 128), dtype=np.uint16, buffer=shm.buf)
+        else:
+            pooled = orc.pool_keys(gen(seed, S("raw_key"), L * 128).reshape(L, 128), 4)
+        q_idx = gen(seed, S("q_idx"), 128)
+        q = gen(seed, S("q"), 16 * 256).reshape(16, 256)
+        # the selection does not change between repetitions: the K/V rows it
+        # reads are generated once, by index
+        toks0 = orc.selected_tokens(orc.select_blocks(orc.index_scores(q_idx, pooled, L // 4), L, 4, 512), L, 4)
+        kr = _gen_rows(qi, seed, S("k"), toks0, 512).reshape(-1, 2, 256)
+        vr = _gen_rows(qi, seed, S("v"), toks0, 512).reshape(-1, 2, 256)
+        row_of = {int(t): r for r, t in enumerate(toks0)}
+
+        def unit():
+            sc = orc.index_scores(q_idx, pooled, L // 4)
+            toks = orc.selected_tokens(orc.select_blocks(sc, L, 4, 512), L, 4)
+            orc.attend(q, kr, vr, np.array([row_of[int(t)] for t in toks]), 1.0 / 16)
+
+        units.append(unit)
+    elif cfg == 4:
+        H, C = PREFILL["history"], PREFILL["chunk"]
+        n = H + C
+        seed = qi.config_seed(4)
+        S = lambda kind: qi.stream_id(0, 0, kind)
+        pooled = orc.pool_keys(gen(seed, S("raw_key"), n * 128).reshape(n, 128), 4)
+        k = gen(seed, S("k"), n * 512).reshape(n, 2, 256)
+        v = gen(seed, S("v"), n * 512).reshape(n, 2, 256)
+        for i in list(range(worker, C, n_workers))[::max(1, C // n_workers // max_units)][:max_units]:
+            ctx = H + i + 1
+            q_idx = qi.normal_bf16(seed, S("q_idx"), i * 128, 128)
+            q = qi.normal_bf16(seed, S("q"), i * 4096, 4096).reshape(16, 256)
+
+            def unit(ctx=ctx, q_idx=q_idx, q=q):
+                sc = orc.index_scores(q_idx, pooled, ctx // 4)
+                toks = orc.selected_tokens(orc.select_blocks(sc, ctx, 4, 512), ctx, 4)
+                orc.prefill_query_tiled(q, k, v, toks, n, PREFILL["tiles"][0], 1.0 / 16)
+
+            units.append(unit)
+    else:
+        L, C = MLA["ctx"], MLA["chunk"]
+        seed = qi.config_seed(5)
+        prefill = cfg == "5a"
+        layer, seq = (1, 0) if prefill else (0, worker % MLA["batch"])
+        S = lambda kind: qi.stream_id(layer, seq, kind)
+        keys = gen(seed, S("raw_key"), L * 64).reshape(L, 64)
+        qs = list(range(worker, C, n_workers))[::max(1, C // n_workers // max_units)][:max_units] if prefill else [0]
+        w_all = qi.uniform_f32(seed, S("w_idx"), (C if prefill else 1) * 4).reshape(-1, 4)
+        for i in qs:
+            ctx = L - C + i + 1 if prefill else L
+            q_idx = qi.normal_bf16(seed, S("q_idx"), i * 256, 256).reshape(4, 64)
+            q = qi.normal_bf16(seed, S("q"), i * 64 * 576, 64 * 576).reshape(64, 576)
+            w = w_all[i]
+            toks0 = orc.selected_tokens(orc.select_blocks(orc.index_scores_relu(q_idx, w, keys, ctx), ctx, 1, 2048),
+                                        ctx, 1)
+            lat = _gen_rows(qi, seed, S("latent"), toks0, 576)[:, None, :]
+            row_of = {int(t): r for r, t in enumerate(toks0)}
+
+            def unit(ctx=ctx, q_idx=q_idx, q=q, w=w, lat=lat, row_of=row_of):
+                sc = orc.index_scores_relu(q_idx, w, keys, ctx)
+                toks = orc.selected_tokens(orc.select_blocks(sc, ctx, 1, 2048), ctx, 1)
+                orc.attend(q, lat, lat, np.array([row_of[int(t)] for t in toks]), 1.0 / 24, dv=512)
+
+            units.append(unit)
+    setup = time.perf_counter() - t_setup
+    done = 0
     t0 = time.perf_counter()
-    while reps < 16 or (time.perf_counter() - t0 < 10.0 and reps < 2000):
-        reps += 1
-        s = orc.index_scores(q_idx, pooled, L // 4)
-        sel = orc.select_blocks(s, L, 4, 512)
-        toks = orc.selected_tokens(sel, L, 4)
-        rows = np.array([row_of[int(t)] for t in toks])
-        o, lse = orc.attend(q, k_rows, v_rows, rows, 1.0 / 16)
+    while done < 1 or time.perf_counter() - t0 < budget:
+        units[done % len(units)]()
+        done += 1
     dt = time.perf_counter() - t0
-    unit_s = dt / reps
+    if shm is not None:
+        del pooled, units
+        shm.close()
+    del keep
+    return done, dt, setup
 
-    def unit():
-        s = orc.index_scores(q_idx, pooled, L // 4)
-        toks = orc.selected_tokens(orc.select_blocks(s, L, 4, 512), L, 4)
-        orc.attend(q, k_rows, v_rows, np.array([row_of[int(t)] for t in toks]), 1.0 / 16)
 
-    # the same unit on one thread
-    unit_1t = None
+def cpu_baselines(budget=4.0, budget_headline=10.0):
+    """The oracle on every workload, timed over the host cores (see above).
+    Returns {config: dict(value, unit, cores, ...)}; config 3 is the
+    headline's baseline."""
+    import multiprocessing as mp
+    from multiprocessing import shared_memory
+    n_workers = max(1, min(16, os.cpu_count() or 1))
+    ctx = mp.get_context("spawn")  # fresh interpreters: the workers never touch the GPU
+    out = {}
+    nb = DECODE["ctx"] // 4
+    shm = shared_memory.SharedMemory(create=True, size=nb * 128 * 2)
     try:
-        from threadpoolctl import threadpool_limits
-        with threadpool_limits(limits=1):
-            t1 = time.perf_counter()
-            for _ in range(4):
-                unit()
-            unit_1t = (time.perf_counter() - t1) / 4
-    except Exception:  # pragma: no cover
-        pass
-    cpu_model = None
-    try:
-        for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                cpu_model = line.split(":", 1)[1].strip()
-                break
-    except OSError:  # pragma: no cover
-        pass
-    return dict(value=1.0 / (unit_s * DECODE["batch"] * DECODE["layers"]), unit="steps/s", cores=int(cores),
-                kind="oracle", cpu_model=cpu_model,
-                value_1thread=(round(1.0 / (unit_1t * DECODE["batch"] * DECODE["layers"]), 4) if unit_1t else None),
-                sample=(f"one (layer, sequence) unit of the 1M-context decode step (scan of 262,080 pooled keys, "
-                        f"top-512, attention over 2,048 tokens; K/V rows it reads are generated by index beforehand), "
-                        f"run {reps} times (a step has 48 such units); {unit_s * 1e3:.1f} ms per unit; "
-                        f"input generation and pooling excluded ({prep_s:.1f} s)"),
-                seconds=dt)
+        with ctx.Pool(n_workers) as pool:
+            t0 = time.perf_counter()
+            cuts = [nb * w // n_workers // 4 * 4 for w in range(n_workers)] + [nb]
+            pool.map(_pool_slice, [(shm.name, nb, cuts[w], cuts[w + 1]) for w in range(n_workers)])
+            log(f"oracle inputs: 262,080 pooled keys in {time.perf_counter() - t0:.1f} s")
+            for cfg, (unit, per_metric, what) in ORACLE_UNITS.items():
+                b = budget_headline if cfg == 3 else budget
+                t0 = time.perf_counter()
+                res = pool.map(_oracle_worker, [(cfg, w, n_workers, b, shm.name) for w in range(n_workers)])
+                wall = time.perf_counter() - t0
+                out[cfg] = _oracle_summary(res, n_workers, unit, per_metric, what, wall)
+                log(f"oracle config {cfg}: {out[cfg]['value']:.4g} {unit} on {n_workers} cores "
+                    f"({wall:.1f} s)")
+    finally:
+        shm.close()
+        shm.unlink()
+    return out
+
+
+def _oracle_summary(res, n_workers, unit, per_metric, what, wall):
+    """Pool throughput (units per second of the longest worker's timed
+    span) and the one-core figure (units per second of summed worker time),
+    both scaled to the metric's unit."""
+    units = sum(r[0] for r in res)
+    secs = max(r[1] for r in res)
+    setup = max(r[2] for r in res)
+    per_unit = sum(r[1] for r in res) / units  # seconds of one core per unit
+    value = units / secs / per_metric
+    return dict(value=round(value, 6), unit=unit, cores=n_workers, kind="oracle",
+                sample=(f"{what}; {units} units over {n_workers} single-threaded worker processes, "
+                        f"{secs:.1f} s each after {setup:.1f} s of input generation (not timed); "
+                        f"{per_unit * 1e3:.1f} ms of one core per unit; one {unit.split('/')[0][:-1]} is "
+                        f"{per_metric} unit(s)"),
+                value_1core=round(1.0 / per_unit / per_metric, 6), wall_s=round(wall, 1))
 
 
 def main():
@@ -847,14 +1034,23 @@ def main():
         f"scan {dec['lists_ms'] * 1e3:.1f} us/launch")
     del dec["layers"], dec["bufs"]
     torch.cuda.empty_cache()
+    small = [run_small_decode(pkg, pipeline, bm, qi, torch, c, args.steps, args.warmup) for c in SMALL_DECODES]
+    torch.cuda.empty_cache()
     pre, pflops = run_prefill(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
     torch.cuda.empty_cache()
     mla = run_mla(pkg, pipeline, bm, qi, torch, args.steps, args.warmup)
     torch.cuda.empty_cache()
 
-    from oracle import qsa_oracle as orc
-    cpu = cpu_baseline(qi, orc, bm)
-    log(f"cpu baseline: {cpu['value']:.4f} steps/s ({cpu['seconds']:.1f} s)")
+    cpu_all = cpu_baselines()
+    cpu = cpu_all[3]
+    cpu_model = None
+    try:
+        for line_ in open("/proc/cpuinfo"):
+            if line_.startswith("model name"):
+                cpu_model = line_.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
 
     steps_s = 1e3 / dec["ms"]
     hbm_gbs = dec["step_bytes"] / (dec["ms"] * 1e-3) / 1e9
@@ -914,15 +1110,21 @@ def main():
                     "useful_gflop": round(pflops["total"] / 1e9, 2),
                     "breakdown_us": pre["breakdown_us"], "attend_tflops": pre["attend_tflops"],
                     "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)},
-                    "correlated": pre["correlated"]},
-        "mla": mla,
+                    "correlated": pre["correlated"], "oracle_tok_s": cpu_all[4]["value"]},
+        "mla": dict(mla, decode=dict(mla["decode"], oracle_steps_s=cpu_all["5b"]["value"]),
+                    prefill=dict(mla["prefill"], oracle_tok_s=cpu_all["5a"]["value"])),
+        "decode_batch1": {f"config_{c['config_id']}": dict(r, oracle_steps_s=cpu_all[c["config_id"]]["value"])
+                          for c, r in zip(SMALL_DECODES, small)},
         "roofline": {"kernel": "index_lists_a (pooled-key scan + per-chunk candidate lists, first launch of "
                                "qsa_decode_layer)", "bound": "hbm",
                      "achieved": round(dec["lists_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(dec["lists_gbs"] / HBM_PEAK_GBS, 4),
                      "traffic": counter_traffic("index_lists_a<2, false>", "2048"),
                      "bytes_per_launch": dec["scan_launch_bytes"], "us_per_launch": round(dec["lists_ms"] * 1e3, 3)},
-        "cpu_baseline": {k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample", "value_1thread", "cpu_model")},
+        "cpu_baseline": {**{k: cpu[k] for k in ("value", "unit", "cores", "kind", "sample", "value_1core")},
+                         "cpu_model": cpu_model,
+                         "other_workloads": {str(c): {k: v for k, v in r.items() if k != "kind"}
+                                             for c, r in cpu_all.items() if c != 3}},
         "wall_s": round(time.time() - t_all, 1),
     }
     print(json.dumps(line), flush=True)
