@@ -22,6 +22,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   mla::attend_part<false>(a, split, i, sh);
 }
 
+// Transposed form with two tile buffers: two work-groups per CU, each
+// gathering its next tile while it computes the current one.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_b_t(AttendArgs a) {
+  __shared__ mla::LdsT sh;
+  const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
+  mla::attend_part_t<false>(a, split, i, sh);
+}
+
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) void attend_b_fp8(AttendArgs a) {
   __shared__ mla::LdsF8 sh;
   const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
@@ -48,10 +56,13 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     return hipGetLastError();
   }
   if (a.hq == mla::kH && a.hkv == 1 && a.dk == mla::kDK && a.dv == mla::kDV) {
+    const dim3 grid(unsigned(int64_t(a.nq) * a.n_split));
     if (a.kv_fp8)
-      hipLaunchKernelGGL(attend_b_fp8, dim3(unsigned(int64_t(a.nq) * a.n_split)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attend_b_fp8, grid, dim3(256), 0, s, a);
+    else if (a.block == 1)  // token-level selection (the indexer of this shape)
+      hipLaunchKernelGGL(attend_b_t, grid, dim3(256), 0, s, a);
     else
-      hipLaunchKernelGGL(attend_b, dim3(unsigned(int64_t(a.nq) * a.n_split)), dim3(256), 0, s, a);
+      hipLaunchKernelGGL(attend_b, grid, dim3(256), 0, s, a);
     return hipGetLastError();
   }
   return hipErrorInvalidValue;

@@ -190,6 +190,301 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
   }
 }
 
+// Barrier without a memory fence (a fence would wait for the gathers in
+// flight): each wait for data is an explicit s_waitcnt, and an empty asm with
+// a memory clobber keeps the compiler from moving LDS accesses across.
+__device__ __forceinline__ void pipe_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// wave instructions of one tile's gather: slots 64s .. 64s+63 of the
+// kTileC chunks
+constexpr int kTileSlots = (kTileC + 63) / 64;  // 37
+
+// ---- transposed form, two tile buffers: attend_part_t
+// S^T = K Q^T (K rows from LDS as the A operand, the wave's 16 queries as
+// the B operand), so after the MFMA lane (kq, r) holds the scores of head r
+// for tokens 4kq + e and 16 + 4kq + e (e < 4). The softmax of head r runs
+// on its lane column (row reductions across the four 16-lane rows with
+// permlane swaps), and the lane's eight probabilities are, as they stand,
+// the B operand of O^T += V^T P^T when the 32 tokens of the tile enter the
+// contraction in the order {4kq .. 4kq+3, 16+4kq .. 16+4kq+3} for k-group
+// kq; V^T is read in that order by the transposed LDS reads. P never goes
+// through LDS, so a work-group needs only its tile buffers: two (75 KB), one
+// tile gathered while the other is computed, and two work-groups per CU.
+// The selection entries of a tile also arrive by LDS DMA, two tiles ahead,
+// so no register load (and no wait for it) sits in the loop. Per tile t:
+// wait for everything this wave has in flight (tile t's rows, the entries of
+// tile t + 1), barrier (tile t visible to all; everyone done with tile
+// t - 1), gather tile t + 1 into the other buffer and the entries of tile
+// t + 2 into the entry slot tile t used, then compute tile t without
+// waiting for either.
+constexpr int kSelSlot = 64;  // selection entries per slot (one wave instruction)
+
+struct LdsT {
+  __attribute__((aligned(16))) unsigned char kv[2][kTileC * 16];
+  int selbuf[2][kSelSlot];
+  float lsum[kH];
+  int64_t range[2];
+};
+
+__device__ __forceinline__ float rows_max(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// A part's list for token-level selection (block 1: list entry p is the
+// selected token sel[p], no trailing tokens): its selection row from P0 on.
+struct TList {
+  const int* sel;  // the query's selection row (topk entries)
+  int topk, ctx, P0, n_list;
+  // token of row j of tile t, from the entries of the tile (clamped into the context)
+  __device__ __forceinline__ int tok(const int* ent, int j) const {
+    const int b = ent[j];
+    return b < 0 ? 0 : (b >= ctx ? ctx - 1 : b);
+  }
+  __device__ __forceinline__ int cnt(int t) const {
+    const int c = n_list - kTT * t;
+    return c <= 0 ? 0 : (c < kTT ? c : kTT);
+  }
+};
+
+struct TLane {
+  int wave, lane, r, kq;
+};
+
+// DMA of the selection entries of tile t into a slot (wave 0; the entries
+// past the row are clamped to its last one and never used).
+__device__ __forceinline__ void sel_dma(const TLane& tl, const TList& ls, int t, int* slot) {
+  if (tl.wave != 0 || ls.cnt(t) == 0) return;
+  int e = ls.P0 + kTT * t + tl.lane;
+  e = e < ls.topk ? e : ls.topk - 1;
+  __builtin_amdgcn_global_load_lds(ls.sel + e, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
+}
+
+// DMA of the latent rows of tile t into a buffer, tokens from its entries:
+// every lane first reads the token of each row it loads (all LDS reads
+// issued together), then issues its gathers. Slot s of wave w is s = w + 4j;
+// its chunks c = 64s + lane sit at (row, col) = (c / 73, c % 73), stepped
+// from slot to slot (256 chunks = 3 rows + 37 chunks). The lane index goes
+// through an opaque copy first, so that the compiler recomputes these
+// offsets per tile instead of keeping all of them live (and spilling) across
+// the tile loop.
+constexpr int kSlotsPerWave = (kTileSlots + 3) / 4;  // 10 (wave w: slots w, w + 4, ...)
+
+__device__ __forceinline__ void rows_dma(const TLane& tl, const TList& ls, int t, const int* __restrict__ ent,
+                                         unsigned char* __restrict__ buf, const uint16_t* kvbase,
+                                         int64_t tok_stride) {
+  const int n = ls.cnt(t);
+  if (n == 0) return;
+  int lane;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(tl.lane));
+  const int c0 = 64 * tl.wave + lane;
+  int row = c0 / kRowL, col = c0 % kRowL;
+  int tok[kSlotsPerWave], cc[kSlotsPerWave];
+#pragma unroll
+  for (int j = 0; j < kSlotsPerWave; j++) {
+    tok[j] = ls.tok(ent, row < n ? row : 0);  // rows past the tile's count (or the tile) repeat row 0
+    cc[j] = col < kRowC ? col : 0;             // the pad chunk takes a copy of chunk 0
+    col += 37;
+    row += 3;
+    if (col >= kRowL) {
+      col -= kRowL;
+      row += 1;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kSlotsPerWave; j++) {
+    const int s = tl.wave + 4 * j;
+    if (64 * s + tl.lane < kTileC)
+      __builtin_amdgcn_global_load_lds(kvbase + int64_t(tok[j]) * tok_stride + 8 * cc[j],
+                                       (__attribute__((address_space(3))) void*)(buf + 1024 * s), 16, 0, 0);
+  }
+}
+
+// One tile: the gathers of tile t + 1 (rows into `nxt`, from the entries in
+// `ent_next`) and of the entries of tile t + 2 (into `ent_free`), then the
+// tile in `cur`. Every LDS buffer arrives as a __restrict__ pointer, so the
+// compiler knows the DMA in flight does not write what this tile reads and
+// does not make the reads wait for it.
+__device__ __attribute__((always_inline)) inline void tile_t(
+    const TLane& tl, const TList& ls, int t, const unsigned char* __restrict__ cur,
+    unsigned char* __restrict__ nxt, const int* __restrict__ ent_next, int* __restrict__ ent_free,
+    const uint16_t* kvbase, int64_t tok_stride, float sl2, const bf16x8 (&qa)[kDK / 32], float& m, float& l,
+    f32x4 (&o)[kDV / 16]) {
+  const int r = tl.r, kq = tl.kq;
+  rows_dma(tl, ls, t + 1, ent_next, nxt, kvbase, tok_stride);
+  sel_dma(tl, ls, t + 2, ent_free);
+  const int cnt = ls.cnt(t);
+  // S^T for the two 16-token halves, K operands read one k-step ahead
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  const unsigned char* krow0 = cur + (r * kRowL + kq) * 16;
+  const unsigned char* krow1 = cur + ((16 + r) * kRowL + kq) * 16;
+  bf16x8 kb[2][2];
+#pragma unroll
+  for (int ks = 0; ks < kDK / 32 + 1; ks++) {
+    if (ks < kDK / 32) {
+      kb[0][ks % 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 64 * ks));
+      kb[1][ks % 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 64 * ks));
+    }
+    if (ks >= 1) {
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[0][(ks - 1) % 2], qa[ks - 1], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[1][(ks - 1) % 2], qa[ks - 1], acc[1], 0, 0, 0);
+    }
+  }
+  // online softmax of head r over the tile's tokens 4kq + e (acc[0]) and 16 + 4kq + e (acc[1])
+  float sv[8];
+#pragma unroll
+  for (int e = 0; e < 4; e++) {
+    sv[e] = 4 * kq + e < cnt ? acc[0][e] * sl2 : -INFINITY;
+    sv[4 + e] = 16 + 4 * kq + e < cnt ? acc[1][e] * sl2 : -INFINITY;
+  }
+  float tm = sv[0];
+#pragma unroll
+  for (int j = 1; j < 8; j++) tm = fmaxf(tm, sv[j]);
+  tm = rows_max(tm);
+  const float mn = fmaxf(m, tm);
+  // (exp2 of the hardware: results below 2^-126, weights negligible next to
+  // the row maximum's 1, may flush to zero)
+  float pv[8];
+  float alpha = 1.f, ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; j++) pv[j] = 0.f;
+  if (mn != -INFINITY) {
+    alpha = __builtin_amdgcn_exp2f(m - mn);
+#pragma unroll
+    for (int j = 0; j < 8; j++) {
+      pv[j] = __builtin_amdgcn_exp2f(sv[j] - mn);
+      ps += pv[j];
+    }
+  }
+  ps = rows_sum(ps);
+  l = l * alpha + ps;
+  m = mn;
+  // P^T as bf16 hi + lo parts (~16 significant bits; both rounded to
+  // nearest even by the hardware conversion), the B operands of P V
+  bf16x8 bh, bl;
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    bh[j] = (__bf16)pv[j];
+    bl[j] = (__bf16)(pv[j] - float(bh[j]));
+  }
+  // rescale (alpha belongs to the lane's head; it is 1 on every lane once
+  // the running maxima have settled, and then nothing is multiplied)
+  if (__ballot(alpha != 1.f)) {
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++)
+#pragma unroll
+      for (int e = 0; e < 4; e++) o[nt][e] *= alpha;
+  }
+  // O^T += V^T P^T: lane (kq, r) reads, for dims 16nt .. 16nt+15, rows
+  // 4kq + r/4 (first read) and 16 + 4kq + r/4 (second), dims 16nt + 4(r % 4)
+  // .. +3; after the transpose it holds V[rows 4kq .. 4kq+3, then 16+4kq ..
+  // 16+4kq+3][dim 16nt + r]
+  const unsigned char* va = cur + (4 * kq + (r >> 2)) * kRowL * 16 + 8 * (r & 3);
+  const unsigned char* vb = va + 16 * kRowL * 16;
+#pragma unroll
+  for (int nt = 0; nt < kDV / 16; nt++) {
+    const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 32 * nt));
+    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + 32 * nt));
+    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
+    o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, o[nt], 0, 0, 0);
+    o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, o[nt], 0, 0, 0);
+    if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // reads in flight: 4 n-tiles (registers)
+  }
+}
+
+template <bool kCoh>
+__device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
+  TLane tl;
+  const int tid = threadIdx.x;
+  tl.wave = tid >> 6;
+  tl.lane = tid & 63;
+  tl.r = tl.lane & 15;
+  tl.kq = tl.lane >> 4;
+  const int wave = tl.wave, r = tl.r, kq = tl.kq;
+
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
+  // block 1 (the host sends other block sizes to attend_part): the list is
+  // the ns selected tokens, no trailing ones
+  att::List<kCoh> lv;
+  lv.sel = a.sel + int64_t(i) * a.topk;
+  lv.block = 1;
+  lv.nblk = ctx;
+  const int ns_max = ctx < a.topk ? ctx : a.topk;
+  const int ns = kCoh ? ns_max : a.n_sel[i];
+  lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
+  lv.L = lv.ns;
+  if (tid == 0) {
+    const int lo = int(int64_t(split) * lv.L / a.n_split);
+    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int t0 = lv.count_below(a.tile_begin, ctx);
+    const int t1 = lv.count_below(a.tile_end, ctx);
+    sh.range[0] = lo > t0 ? lo : t0;
+    sh.range[1] = hi < t1 ? hi : t1;
+  }
+  __syncthreads();
+  TList ls;
+  ls.sel = lv.sel;
+  ls.topk = a.topk;
+  ls.ctx = ctx;
+  // the part's range is the same on every lane: keep it (and what derives
+  // from it) in scalar registers
+  ls.P0 = __builtin_amdgcn_readfirstlane(int(sh.range[0]));
+  ls.n_list = __builtin_amdgcn_readfirstlane(int(sh.range[1])) - ls.P0;
+  const int n_tiles = (ls.n_list + kTT - 1) / kTT;
+
+  const uint16_t* kvbase = a.k + int64_t(seq) * a.seq_stride;
+  const float sl2 = a.scale * kLog2e;
+
+  // B operands: Q[head 16w + r][32ks + 8kq .. +7]
+  bf16x8 qa[kDK / 32];
+  {
+    const uint16_t* qrow = a.q + (int64_t(i) * kH + 16 * wave + r) * kDK + 8 * kq;
+#pragma unroll
+    for (int ks = 0; ks < kDK / 32; ks++) qa[ks] = as_bf16x8(ld16(qrow + 32 * ks));
+  }
+  float m = -INFINITY, l = 0.f;
+  f32x4 o[kDV / 16];
+#pragma unroll
+  for (int nt = 0; nt < kDV / 16; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the entries of tiles 0 and 1, then tile 0's rows
+  sel_dma(tl, ls, 0, sh.selbuf[0]);
+  sel_dma(tl, ls, 1, sh.selbuf[1]);
+  wait_memory();
+  pipe_barrier();
+  rows_dma(tl, ls, 0, sh.selbuf[0], sh.kv[0], kvbase, a.tok_stride);
+  for (int t = 0; t < n_tiles; t++) {
+    // tile t's rows (this wave's share) and the entries of tile t + 1: all
+    // this wave has in flight
+    wait_memory();
+    pipe_barrier();  // every wave's share of tile t has landed; every wave is done with tile t - 1
+    tile_t(tl, ls, t, sh.kv[t & 1], sh.kv[(t + 1) & 1], sh.selbuf[(t + 1) & 1], sh.selbuf[t & 1], kvbase,
+           a.tok_stride, sl2, qa, m, l, o);
+  }
+
+  // normalise and write: lane (kq, r) holds O^T[dim 16nt + 4kq + e][head 16w + r]
+  const float inv = l > 0.f ? 1.f / l : 0.f;
+  const int64_t orow = (int64_t(split) * a.nq + i) * kH + 16 * wave + r;
+  float* op = a.o_part + orow * kDV + 4 * kq;
+#pragma unroll
+  for (int nt = 0; nt < kDV / 16; nt++)
+    *reinterpret_cast<f32x4*>(op + 16 * nt) = f32x4{o[nt][0] * inv, o[nt][1] * inv, o[nt][2] * inv, o[nt][3] * inv};
+  if (kq == 0) a.lse_part[orow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+}
+
 // ---- FP8 latent rows
 // "GLM-5.3 最適化 第2部", footnote 1: the FP8 sparse-MLA row is 656 bytes:
 // the 512 latent values as E4M3 codes in 4 groups of 128 with one fp32

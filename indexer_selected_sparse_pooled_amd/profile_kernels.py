@@ -18,6 +18,7 @@ Usage (one counter group per run):
 Summaries of rocprofv3 CSV output (host only, no GPU):
   python profile_kernels.py --trace OUT/run_kernel_trace.csv
   python profile_kernels.py --pmc FETCH/run_counter_collection.csv WRITE/run_counter_collection.csv
+  python profile_kernels.py --counters A/run_counter_collection.csv [B/...]   (MFMA, LDS, waits)
 The counter summary scales each memory counter by what it reads for the
 256 MiB copy, so its figures are bytes moved to and from memory.
 """
@@ -107,6 +108,44 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(out)
 
 
+def summarize_counters(paths) -> str:
+    """Per (kernel, grid): the per-dispatch average of every counter found in
+    the given counter_collection.csv files (one per rocprofv3 --pmc pass),
+    and, where present: MFMA busy % (AMD's MfmaUtil: MFMA-busy cycles of all
+    SIMDs over active cycles x SIMDs), executed bf16 MFMA work
+    (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 FLOP), the LDS bank-conflict share of
+    LDS-active cycles, and the share of wave cycles spent waiting."""
+    g = collections.OrderedDict()
+    names = []
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            wg = int(r["Workgroup_Size"])
+            key = (kernel_name(r["Kernel_Name"]), f'{int(r["Grid_Size"]) // wg}')
+            c = r["Counter_Name"]
+            if c not in names:
+                names.append(c)
+            g.setdefault(key, {}).setdefault(c, []).append(float(r["Counter_Value"]))
+    out = [f"source digest: {source_digest()}", "counters: " + " ".join(names)]
+    for (kern, grid), cs in g.items():
+        avg = {c: sum(v) / len(v) for c, v in cs.items()}
+        n = max(len(v) for v in cs.values())
+        parts = [f"{kern} [{grid} wgs, {n} dispatches]"]
+        parts += [f"  {c} {avg[c]:.6g}" for c in names if c in avg]
+        if "MfmaUtil" in avg:
+            parts.append(f"  => MFMA busy {avg['MfmaUtil']:.2f} %")
+        if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
+            parts.append(f"  => executed bf16 MFMA {avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.3f} GFLOP per dispatch")
+        if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
+            parts.append(f"  => LDS bank conflicts {100 * avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.1f} % "
+                         f"of LDS-active cycles")
+        if "SQ_WAIT_INST_ANY" in avg and avg.get("SQ_WAVE_CYCLES"):
+            parts.append(f"  => waiting on any instruction {100 * avg['SQ_WAIT_INST_ANY'] / avg['SQ_WAVE_CYCLES']:.1f} % "
+                         f"of wave cycles" + (f", on LDS {100 * avg['SQ_WAIT_INST_LDS'] / avg['SQ_WAVE_CYCLES']:.1f} %"
+                                              if "SQ_WAIT_INST_LDS" in avg else ""))
+        out.append("\n".join(parts))
+    return "\n".join(out)
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--reps", type=int, default=5)
@@ -114,9 +153,14 @@ def main() -> int:
     ap.add_argument("--trace", help="summarize a rocprofv3 kernel_trace.csv and exit")
     ap.add_argument("--pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="summarize two rocprofv3 counter_collection.csv files and exit")
+    ap.add_argument("--counters", nargs="+", metavar="CSV",
+                    help="summarize any rocprofv3 counter_collection.csv files (MFMA, LDS, waits) and exit")
     args = ap.parse_args()
     if args.trace:
         print(summarize_trace(args.trace))
+        return 0
+    if args.counters:
+        print(summarize_counters(args.counters))
         return 0
     if args.pmc:
         print(summarize_pmc(*args.pmc))
@@ -201,7 +245,8 @@ def prefill_tile(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
     kv = pkg.make_kv(k, v)
     q_ctx = torch.arange(H + 1, H + C + 1, dtype=torch.int32, device=dev)
     pb = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, C, ctx_max, 8192)
-    pkg.qsa_index_scores(pkg.SEL_A, q_ctx, ctx_max, q_idx, pooled, pb.scores)
+    for _ in range(reps):  # the indexer GEMM of the chunk (scores_gemm_a)
+        pkg.qsa_index_scores(pkg.SEL_A, q_ctx, ctx_max, q_idx, pooled, pb.scores)
     pkg.qsa_topk_blocks(pkg.SEL_A, q_ctx, ctx_max, pb.scores, pb.sel, pb.n_sel, pb.ws)
     a0, a1 = pb.tiles[3]
     for _ in range(reps):
@@ -229,8 +274,11 @@ def mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
     kv = pkg.make_kv(lat, lat)
     q_ctx = torch.tensor(np.arange(L - C + 1, L + 1, dtype=np.int32), device=dev)
     pb = pipeline.prefill_buffers(pkg.SEL_B, pkg.ATTN_B, C, L, L)
-    pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, pb.scores, w_idx=w)
+    for _ in range(reps):  # the indexer GEMM of the chunk (scores_gemm_b)
+        pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, pb.scores, w_idx=w)
     pkg.qsa_topk_blocks(pkg.SEL_B, q_ctx, L, pb.scores, pb.sel, pb.n_sel, pb.ws)
+    for _ in range(reps):  # the one-call selection (list-mode score GEMM, list select)
+        pkg.qsa_index_topk_prefill(pkg.SEL_B, q_ctx, L, q_idx, w, keys, pb.scores, pb.sel, pb.n_sel, pb.sel_ws)
     for _ in range(reps):
         pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv, pb.sel, pb.n_sel, 0, L, pb.o_tiles[0],
                                pb.lse_tiles[0])
