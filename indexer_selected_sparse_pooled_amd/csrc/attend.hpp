@@ -54,7 +54,6 @@ struct Lds {
   __attribute__((aligned(16))) uint16_t phi[kG * kPStr];
   __attribute__((aligned(16))) uint16_t plo[kG * kPStr];
   float alpha[kG], m[kG], l[kG];
-  int64_t range[2];
 };
 
 // sel may have been written earlier in the same launch by another
@@ -65,6 +64,11 @@ __device__ __forceinline__ int ld_sel(const int* p) {
   return *p;
 }
 
+// A pointer into LDS, typed as one: reads through it are ds_read (counted by
+// lgkmcnt alone). A generic pointer would make them flat loads, which also
+// count against vmcnt, so every read would wait for the loads in flight.
+typedef const __attribute__((address_space(3))) int* LdsIntPtr;
+
 template <bool kCoh>
 struct List {
   const int* sel;
@@ -72,8 +76,11 @@ struct List {
   int nblk;  // complete blocks
   int block;
   int L;     // list length
-  const int* cache = nullptr;  // LDS copy of sel[0 .. ns), or nullptr
-  __device__ __forceinline__ int sel_at(int j) const { return cache ? cache[j] : ld_sel<kCoh>(sel + j); }
+  // LDS copy of sel[0 .. ns) when has_cache (a flag, not a null test: LDS
+  // offset 0 is a valid address)
+  LdsIntPtr cache = nullptr;
+  bool has_cache = false;
+  __device__ __forceinline__ int sel_at(int j) const { return has_cache ? cache[j] : ld_sel<kCoh>(sel + j); }
   // token of list entry p (0 <= p < L)
   __device__ __forceinline__ int tok(int p) const {
     const int nb_tok = ns * block;
@@ -90,7 +97,7 @@ struct List {
     if (x >= ctx) return L;
     const int nb_tok = nblk * block;
     if (x >= nb_tok) return ns * block + int(x - nb_tok);
-    const int xb = int(x / block);
+    const int xb = int(x) / block;  // 0 < x < ctx here
     int lo = 0, hi = ns;  // first selected block >= xb
     while (lo < hi) {
       const int mid = (lo + hi) >> 1;
@@ -100,27 +107,37 @@ struct List {
   }
 };
 
+// First list position of part `split` of n_split over a list of L entries:
+// split * L / n_split. L < (topk + 1) * block <= 8196 and split <= n_split
+// <= 256, so the product fits 32-bit unsigned arithmetic (a 64-bit division
+// is a long emulated sequence).
+__device__ __forceinline__ int split_point(int split, int L, int n_split) {
+  return int(uint32_t(split) * uint32_t(L) / uint32_t(n_split));
+}
+
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
   const uint32_t lo = __shfl(uint32_t(v), src), hi = __shfl(uint32_t(v >> 32), src);
   return (uint64_t(hi) << 32) | lo;
 }
 
-// One part (split, kv head g, query i): see the file comment. sel_lds, when
-// given, holds the query's ns_lds selected blocks in LDS (ascending) and
-// replaces sel / n_sel. kCached: rows come from the HBM row cache on a hit
+// One part (split, kv head g, query i): see the file comment. With ns_lds >=
+// 0, sel_lds holds the query's ns_lds selected blocks in LDS (ascending) and
+// replaces sel / n_sel; ctx_in / seq_in, when >= 0, are the query's context
+// length and sequence (already loaded by the caller). kCached: rows come from the HBM row cache on a hit
 // (the plan in a.src) and from their home (host) memory otherwise, and the
 // rows this part may fill are written to the cache after the tile
 // (row_cache.hip).
 template <bool kCoh, int GT, bool kCached = false>
-__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT>& sh, const int* sel_lds = nullptr,
-                            int ns_lds = 0) {
+__device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT>& sh, LdsIntPtr sel_lds = nullptr,
+                            int ns_lds = -1, int ctx_in = -1, int seq_in = -1) {
+  const bool sel_lds_given = ns_lds >= 0;
   constexpr int kTok = Lds<GT>::kTok, kPStr = Lds<GT>::kPStr;
   constexpr int kRW = 16 * GT;  // token rows per wave
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int r = lane & 15, kq = lane >> 4;
 
-  const int seq = a.q_seq ? a.q_seq[i] : 0;
-  const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
+  const int seq = seq_in >= 0 ? seq_in : (a.q_seq ? a.q_seq[i] : 0);
+  const int ctx = ctx_in >= 0 ? ctx_in : clamp_ctx(a.q_ctx[i], a.max_ctx);
   List<kCoh> lv;
   lv.sel = a.sel + int64_t(i) * a.topk;
   lv.block = a.block;
@@ -128,25 +145,23 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
   const int ns_max = lv.nblk < a.topk ? lv.nblk : a.topk;
   // a selection made in this launch (sel_lds, or kCoh) always holds
   // min(complete blocks, topk) entries: no need to read n_sel
-  const int ns = sel_lds ? ns_lds : (kCoh ? ns_max : a.n_sel[i]);
+  const int ns = sel_lds_given ? ns_lds : (kCoh ? ns_max : a.n_sel[i]);
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.cache = sel_lds;
+  lv.has_cache = sel_lds_given;
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
 
-  if (tid == 0) {
-    const int lo = int(int64_t(split) * lv.L / a.n_split);
-    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
-    const int t0 = lv.count_below(a.tile_begin, ctx);
-    const int t1 = lv.count_below(a.tile_end, ctx);
-    sh.range[0] = lo > t0 ? lo : t0;
-    sh.range[1] = hi < t1 ? hi : t1;
-  }
+  // every thread computes the same range (uniform, no hand-off)
+  const int lo = split_point(split, lv.L, a.n_split);
+  const int hi = split_point(split + 1, lv.L, a.n_split);
+  const int t0 = lv.count_below(a.tile_begin, ctx);
+  const int t1 = lv.count_below(a.tile_end, ctx);
+  const int P0 = lo > t0 ? lo : t0, P1 = hi < t1 ? hi : t1;
   if (tid < kG) {
     sh.m[tid] = -INFINITY;
     sh.l[tid] = 0.f;
   }
   __syncthreads();
-  const int P0 = int(sh.range[0]), P1 = int(sh.range[1]);
 
   const int64_t kvs = int64_t(seq) * a.seq_stride + int64_t(g) * a.head_stride;
   const uint16_t* kbase = a.k + kvs;
@@ -204,17 +219,23 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
     // work-groups) the K rows are, so that S waits for them alone.
     auto load_v = [&]() {
       const int half = lane >> 5, c = lane & 31;
+      // every row address first (cross-lane moves, one wait), then the
+      // loads back to back
+      const uint16_t* vsrc[8 * GT];
+#pragma unroll
+      for (int j = 0; j < 8 * GT; j++) {
+        if constexpr (kCached) {
+          vsrc[j] = reinterpret_cast<const uint16_t*>(shfl64(vrow_l, 2 * j + half)) + 8 * c;
+        } else {
+          const int vt = __shfl(tokl, 2 * j + half);
+          vsrc[j] = vbase + int64_t(vt) * a.tok_stride + 8 * c;
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int j = 0; j < 8 * GT; j++) {
         const int p = 8 * GT * wave + j;
-        const uint16_t* vsrc;
-        if constexpr (kCached) {
-          vsrc = reinterpret_cast<const uint16_t*>(shfl64(vrow_l, 2 * j + half)) + 8 * c;
-        } else {
-          const int vt = __shfl(tokl, 2 * j + half);
-          vsrc = vbase + int64_t(vt) * a.tok_stride + 8 * c;
-        }
-        __builtin_amdgcn_global_load_lds(vsrc, (__attribute__((address_space(3))) void*)(sh.v + p * kPair), 16, 0,
+        __builtin_amdgcn_global_load_lds(vsrc[j], (__attribute__((address_space(3))) void*)(sh.v + p * kPair), 16, 0,
                                          0);
       }
     };

@@ -64,8 +64,8 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
   if (tid == 0) {
-    const int lo = int(int64_t(split) * lv.L / a.n_split);
-    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int lo = att::split_point(split, lv.L, a.n_split);
+    const int hi = att::split_point(split + 1, lv.L, a.n_split);
     const int t0 = lv.count_below(a.tile_begin, ctx);
     const int t1 = lv.count_below(a.tile_end, ctx);
     sh.range[0] = lo > t0 ? lo : t0;
@@ -427,8 +427,8 @@ __device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns;
   if (tid == 0) {
-    const int lo = int(int64_t(split) * lv.L / a.n_split);
-    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int lo = att::split_point(split, lv.L, a.n_split);
+    const int hi = att::split_point(split + 1, lv.L, a.n_split);
     const int t0 = lv.count_below(a.tile_begin, ctx);
     const int t1 = lv.count_below(a.tile_end, ctx);
     sh.range[0] = lo > t0 ? lo : t0;
@@ -531,8 +531,8 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
   if (tid == 0) {
-    const int lo = int(int64_t(split) * lv.L / a.n_split);
-    const int hi = int(int64_t(split + 1) * lv.L / a.n_split);
+    const int lo = att::split_point(split, lv.L, a.n_split);
+    const int hi = att::split_point(split + 1, lv.L, a.n_split);
     const int t0 = lv.count_below(a.tile_begin, ctx);
     const int t1 = lv.count_below(a.tile_end, ctx);
     sh.range[0] = lo > t0 ? lo : t0;

@@ -14,7 +14,7 @@
 // lists, into LDS (final_select, the same code the last chunk of
 // qsa_index_topk runs): the parts of a query repeat the same register
 // select side by side instead of waiting for one of them to publish it.
-// Part (kv head 0, split 0) also writes sel and n_sel. Each part then
+// Part (kv head 0, split 0) also copies it to sel and n_sel. Each part then
 // attends its split of the token list (attend.hpp) and stores its partial
 // result; the parts of a (query, kv head) wait for each other and merge,
 // each part one slice of the output dims. That wait needs every part
@@ -36,7 +36,7 @@ constexpr int kMaxTopk = 2048;
 constexpr int kLayerGT = 2;
 
 struct SelAttnLds {
-  int sel[kMaxTopk];  // the query's selected blocks, ascending
+  int sel[kMaxTopk + 64];  // the query's selected blocks, ascending (then one dummy slot per lane)
   union {
     itk::FinalLds f;
     att::Lds<kLayerGT> a;
@@ -79,19 +79,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const uint64_t b0 = tid < it.n_chunks ? bq[tid] : 0ull;
   const uint64_t b1 = tid + itk::kNT < it.n_chunks ? bq[tid + itk::kNT] : 0ull;
   const int n = clamp_ctx(it.q_ctx[i], it.max_ctx) / 4;
+  // the attention's own view of the query (loaded now, used after the select)
+  const int actx = clamp_ctx(at.q_ctx[i], at.max_ctx);
+  const int aseq = at.q_seq ? at.q_seq[i] : 0;
   const int topk = it.topk;
   const int ns = n < topk ? n : topk;
   const bool writer = g == 0 && split == 0;
   int* gsel = it.sel + int64_t(i) * topk;
   int* const lsel = sh.sel;
-  auto emit = [lsel, writer, gsel](int pos, int blk) {
-    lsel[pos] = blk;
-    if (writer) gsel[pos] = blk;
-  };
+  // selectors call emit(-1, block) for keys they leave out: those go to the
+  // lane's dummy slot
+  const int dummy = kMaxTopk + (tid & 63);
+  auto emit = [lsel, dummy](int pos, int blk) { lsel[pos >= 0 ? pos : dummy] = blk; };
   if (n <= topk) {  // every complete block
     for (int j = tid; j < ns; j += 256) sh.sel[j] = j;
-    if (writer)
-      for (int j = tid; j < topk; j += 256) gsel[j] = j < n ? j : -1;
   } else if (itk::use_union(it, n) && it.n_chunks <= 2 * itk::kNT) {
     const int nch = (n + it.chunk_blocks - 1) / it.chunk_blocks;
     const int u = nch * it.keep;
@@ -99,7 +100,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     int uidx[itk::kRegR];
 #pragma unroll
     for (int rr = 0; rr < itk::kRegR; rr++) {
-      const bool in = rr * itk::kNT + tid < u;
+      const bool in = tid * itk::kRegR + rr < u;
       ukey[rr] = in ? uint32_t(ent[rr] >> 32) : 0u;
       uidx[rr] = int(uint32_t(ent[rr]));
     }
@@ -110,9 +111,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   } else {
     itk::final_select(it, i, n, sh.u.f, emit);
   }
-  if (writer && tid == 0) it.n_sel[i] = ns;
   __syncthreads();
-  att::attend_part<false, kLayerGT>(at, split, g, i, sh.u.a, sh.sel, ns);
+  if (writer) {  // the query's selection, padded with -1
+    for (int j = tid; j < topk; j += 256) gsel[j] = j < ns ? sh.sel[j] : -1;
+    if (tid == 0) it.n_sel[i] = ns;
+  }
+  att::attend_part<false, kLayerGT>(at, split, g, i, sh.u.a, (att::LdsIntPtr)(sh.sel), ns, actx, aseq);
 }
 
 // Work-groups of attend_select_a the current device holds at once.

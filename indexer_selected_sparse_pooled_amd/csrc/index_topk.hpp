@@ -75,12 +75,17 @@ constexpr int kChunkKeep = 16;  // at most, per chunk (a.keep)
 constexpr int kRegR = 16;       // union / raw entries per thread in the final select
 constexpr int kRegCap = kNT * kRegR;
 
-struct FinalLds {
-  RegSelLds<kNT> rs;
-  StreamLds st;
+// One chunk's list step: every wave's candidates and bound.
+struct ListLds {
   uint32_t wkey[4 * kWaveKeep];
   int widx[4 * kWaveKeep];
   uint64_t wbound[4];
+};
+
+struct FinalLds {
+  RegSelLds<kNT> rs;
+  StreamLds st;
+  ListLds lst;
   int last;
 };
 
@@ -174,40 +179,92 @@ __device__ __forceinline__ bool use_union(const IndexTopkArgs& a, int n) {
 
 // Union entry e = chunk * keep + slot of query i (each list in ascending
 // block order, so entry order is block order), as (key << 32 | block), 0 =
-// empty; thread t holds entries r * kNT + t. Entries at or past u are 0.
-// kCoh: written by other work-groups of the same launch (else by an
-// earlier launch, and plain loads see it).
+// empty; thread t holds entries t * kRegR + r (thread-major). Entries at or
+// past u are 0. kCoh: written by other work-groups of the same launch (else
+// by an earlier launch, and plain 16-byte loads see it).
 template <bool kCoh = true>
 __device__ __forceinline__ void load_union(const IndexTopkArgs& a, int i, int u, uint64_t (&ent)[kRegR]) {
   const uint64_t* ul = a.list + size_t(i) * a.n_chunks * a.keep;
+  const int e0 = int(threadIdx.x) * kRegR;
+  if constexpr (kCoh) {
 #pragma unroll
-  for (int r = 0; r < kRegR; r++) {
-    const int e = r * kNT + int(threadIdx.x);
-    if constexpr (kCoh) ent[r] = e < u ? ld_coherent(ul + e) : 0ull;
-    else ent[r] = e < u ? ul[e] : 0ull;
+    for (int r = 0; r < kRegR; r++) ent[r] = e0 + r < u ? ld_coherent(ul + e0 + r) : 0ull;
+  } else {
+    // u is a multiple of the list length (8 or 16), so pairs are never split
+#pragma unroll
+    for (int r = 0; r < kRegR; r += 2) {
+      const u32x4 w = e0 + r < u ? ld16(ul + e0 + r) : u32x4{0u, 0u, 0u, 0u};
+      ent[r] = (uint64_t(w[1]) << 32) | w[0];
+      ent[r + 1] = (uint64_t(w[3]) << 32) | w[2];
+    }
   }
 }
 
-// The topk best of the keys in registers (element j = r * kNT + tid, in
-// block order): emit(position, block) for each, positions ascending, and
-// true; or false, emitting nothing, when in union mode a chunk's bound (the
-// best block it left out; my_bound is the largest this thread checked)
-// ranks above the union's topk-th, so the union may miss a better block.
+// The topk best of the keys in registers (element j = tid * kRegR + r, in
+// block order; 0 = empty): emit(position, block) with position in [0, topk)
+// for each selected key, positions ascending in element order, and
+// emit(-1, block) for every other key of the thread (emit must ignore or
+// redirect those: the loops carry no per-key branch); returns true. Returns
+// false, emitting nothing, when in union mode a chunk's bound (the best block
+// it left out; my_bound is the largest this thread checked) ranks above the
+// union's topk-th, so the union may miss a better block. Positions come from
+// one block-wide scan of the per-thread counts of keys above and equal to the
+// threshold (packed in one word); the bound check rides on the same
+// exchange: a bound key above the threshold fails at once, and only a bound
+// key equal to it needs the topk-th's block.
 template <class Emit>
-__device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, uint32_t (&ukey)[kRegR],
-                                 int (&uidx)[kRegR], uint64_t my_bound, FinalLds& sh, Emit emit) {
+__device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const uint32_t (&ukey)[kRegR],
+                                 const int (&uidx)[kRegR], uint64_t my_bound, FinalLds& sh, Emit emit) {
+  constexpr int NW = kNT / 64;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t kstar;
   int need;
   regsel_threshold<kNT, kRegR>(ukey, a.topk, sh.rs, kstar, need);
-  int pos[kRegR];
-  regsel_positions_rm<kNT, kRegR>(ukey, uidx, kstar, need, sh.rs, pos);
-  if (union_mode) {
+  int g = 0, e = 0;
+#pragma unroll
+  for (int r = 0; r < kRegR; r++) {
+    g += ukey[r] > kstar ? 1 : 0;
+    e += (ukey[r] == kstar && ukey[r] != 0u) ? 1 : 0;
+  }
+  const int v = g | (e << 16);  // at most kRegCap each: no carry between the halves
+  const int incl = wave_incl_sum(v);
+  const uint32_t bkey = uint32_t(my_bound >> 32);
+  const uint64_t bfail = __ballot(union_mode && bkey > kstar);
+  const uint64_t btie = __ballot(union_mode && my_bound != 0ull && bkey == kstar);
+  if (lane == 63) sh.rs.wg[wave] = incl;
+  if (lane == 0) sh.rs.we[wave] = (bfail ? 1 : 0) | (btie ? 2 : 0);
+  __syncthreads();
+  int off = incl - v, flags = 0;
+#pragma unroll
+  for (int w = 0; w < NW; w++) {
+    if (w < wave) off += sh.rs.wg[w];
+    flags |= sh.rs.we[w];
+  }
+  if (flags & 1) return false;
+  const int gb0 = off & 0xFFFF, eb0 = off >> 16;
+  if (flags & 2) {  // a bound ties with the threshold key: compare blocks
+    int eb = eb0;
+#pragma unroll
+    for (int r = 0; r < kRegR; r++) {
+      const bool eq = ukey[r] == kstar && ukey[r] != 0u;
+      if (eq && eb == need - 1) sh.rs.tau_val = uidx[r];
+      eb += eq ? 1 : 0;
+    }
+    __syncthreads();
     const uint64_t tau = rank64(kstar, sh.rs.tau_val);
     if (__syncthreads_or(my_bound > tau)) return false;
   }
+  // keys above kstar, then the first `need` keys equal to it, in element order
+  int gb = gb0, eb = eb0;
 #pragma unroll
-  for (int r = 0; r < kRegR; r++)
-    if (pos[r] >= 0) emit(pos[r], uidx[r]);
+  for (int r = 0; r < kRegR; r++) {
+    const bool gt = ukey[r] > kstar;
+    const bool eq = ukey[r] == kstar && ukey[r] != 0u;
+    const int p = gt ? gb + (eb < need ? eb : need) : ((eq && eb < need) ? gb + eb : -1);
+    emit(p, uidx[r]);
+    gb += gt ? 1 : 0;
+    eb += eq ? 1 : 0;
+  }
   return true;
 }
 
@@ -244,17 +301,77 @@ __device__ void final_select(const IndexTopkArgs& a, int i, int n, FinalLds& sh,
         my_bound = b > my_bound ? b : my_bound;
       }
     } else {
-      // register-major raw scores: element j = r * kNT + tid
+      // thread-major raw scores: element j = tid * kRegR + r
 #pragma unroll
       for (int r = 0; r < kRegR; r++) {
-        const int j = r * kNT + tid;
+        const int j = tid * kRegR + r;
         ukey[r] = j < n ? score_key(sc, j) : 0u;
         uidx[r] = j;
       }
     }
-    if (select_registers(a, union_mode, ukey, uidx, my_bound, sh, emit)) return;
+    if (select_registers(a, union_mode, ukey, uidx, my_bound, sh, [&](int pos, int blk) {
+          if (pos >= 0) emit(pos, blk);
+        }))
+      return;
   }
   select_streamed(sc, n, a.topk, sh, emit);
+}
+
+// The list of one chunk (union mode): every wave keeps its 8 best keys (a
+// register threshold search on their top 16 bits, no barrier) and the best
+// block it leaves out; wave 0 then keeps the chunk's `keep` best of the 32
+// and writes them (ascending block order, 0 past the kept ones) with the
+// chunk's bound: the best block it left out, at full precision. key[t] holds
+// the order key of block w0 + 64 t + lane (0 past n). One barrier; the caller
+// keeps L untouched until every wave has passed the next one. kCoh: the list
+// is read by another work-group of the same launch.
+template <int TPW, bool kCoh>
+__device__ void chunk_list(const IndexTopkArgs& a, int i, int chunk, int n, int64_t w0, const uint32_t (&key)[TPW],
+                           ListLds& L) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int keep = a.keep, wkeep = a.wkeep;
+  const int64_t m64 = int64_t(n) - w0;
+  const int m = m64 <= 0 ? 0 : (m64 >= TPW * 64 ? TPW * 64 : int(m64));
+  if (lane < kWaveKeep) {
+    L.wkey[wave * kWaveKeep + lane] = 0u;
+    L.widx[wave * kWaveKeep + lane] = -1;
+  }
+  uint32_t kh[TPW];  // top 16 bits (nonzero for every nonzero key)
+#pragma unroll
+  for (int t = 0; t < TPW; t++) kh[t] = key[t] >> 16;
+  uint32_t kstar = 0u;
+  int need = wkeep;
+  if (m > wkeep) wave_select<TPW, 16>(kh, wkeep, kstar, need);
+  wave_compact<TPW>(kh, kstar, need, [&](int pos, int r) {
+    L.wkey[wave * kWaveKeep + pos] = key[r];
+    L.widx[wave * kWaveKeep + pos] = int(w0) + 64 * r + lane;
+  });
+  const uint64_t wb = wave_best_excluded<TPW>(kh, key, kstar, need, [&](int j) { return int(w0) + j; });
+  if (lane == 0) L.wbound[wave] = wb;
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t k1[1] = {lane < 4 * kWaveKeep ? L.wkey[lane] : 0u};
+    const uint32_t h1[1] = {k1[0] >> 16};
+    const int i1 = lane < 4 * kWaveKeep ? L.widx[lane] : -1;
+    const int valid = __popcll(__ballot(k1[0] != 0u));
+    uint64_t bound = 0ull;
+#pragma unroll
+    for (int w = 0; w < 4; w++) bound = L.wbound[w] > bound ? L.wbound[w] : bound;
+    uint32_t ks = 0u;
+    int nd = keep;
+    if (valid > keep) wave_select<1, 16>(h1, keep, ks, nd);
+    const size_t base = (size_t(i) * a.n_chunks + chunk) * keep;
+    // kept entries (key << 32 | block) go to their list position; the
+    // positions past the kept count are cleared (0 = empty)
+    wave_compact<1>(h1, ks, nd, [&](int pos, int) {
+      put<kCoh>(a.list + base + pos, (uint64_t(k1[0]) << 32) | uint32_t(i1));
+    });
+    const int nkept = valid < keep ? valid : keep;
+    if (lane >= nkept && lane < keep) put<kCoh>(a.list + base + lane, 0ull);
+    const uint64_t b = wave_best_excluded<1>(h1, k1, ks, nd, [&](int) { return i1; });
+    bound = b > bound ? b : bound;
+    if (lane == 0) put<kCoh>(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
+  }
 }
 
 // One chunk of query i. Returns true in the one work-group that completed
@@ -335,54 +452,10 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
     }
     return false;
   }
-  const int keep = a.keep, wkeep = a.wkeep;
   const bool union_mode = use_union(a, n);
 
   // ---- chunk list: 8 best per wave, then 16 best of the 32
-  if (union_mode) {
-    const int64_t m64 = int64_t(n) - w0;
-    const int m = m64 <= 0 ? 0 : (m64 >= TPW * 64 ? TPW * 64 : int(m64));
-    if (lane < kWaveKeep) {
-      sh.wkey[wave * kWaveKeep + lane] = 0u;
-      sh.widx[wave * kWaveKeep + lane] = -1;
-    }
-    uint32_t kh[TPW];  // top 16 bits (nonzero for every nonzero key)
-#pragma unroll
-    for (int t = 0; t < TPW; t++) kh[t] = key[t] >> 16;
-    uint32_t kstar = 0u;
-    int need = wkeep;
-    if (m > wkeep) wave_select<TPW, 16>(kh, wkeep, kstar, need);
-    wave_compact<TPW>(kh, kstar, need, [&](int pos, int r) {
-      sh.wkey[wave * kWaveKeep + pos] = key[r];
-      sh.widx[wave * kWaveKeep + pos] = int(w0) + 64 * r + lane;
-    });
-    const uint64_t wb = wave_best_excluded<TPW>(kh, key, kstar, need, [&](int j) { return int(w0) + j; });
-    if (lane == 0) sh.wbound[wave] = wb;
-    __syncthreads();
-    if (wave == 0) {
-      const uint32_t k1[1] = {lane < 4 * kWaveKeep ? sh.wkey[lane] : 0u};
-      const uint32_t h1[1] = {k1[0] >> 16};
-      const int i1 = lane < 4 * kWaveKeep ? sh.widx[lane] : -1;
-      const int valid = __popcll(__ballot(k1[0] != 0u));
-      uint64_t bound = 0ull;
-#pragma unroll
-      for (int w = 0; w < 4; w++) bound = sh.wbound[w] > bound ? sh.wbound[w] : bound;
-      uint32_t ks = 0u;
-      int nd = keep;
-      if (valid > keep) wave_select<1, 16>(h1, keep, ks, nd);
-      const size_t base = (size_t(i) * a.n_chunks + chunk) * keep;
-      // kept entries (key << 32 | block) go to their list position; the
-      // positions past the kept count are cleared (0 = empty)
-      wave_compact<1>(h1, ks, nd, [&](int pos, int) {
-        put<kSelect>(a.list + base + pos, (uint64_t(k1[0]) << 32) | uint32_t(i1));
-      });
-      const int nkept = valid < keep ? valid : keep;
-      if (lane >= nkept && lane < keep) put<kSelect>(a.list + base + lane, 0ull);
-      const uint64_t b = wave_best_excluded<1>(h1, k1, ks, nd, [&](int) { return i1; });
-      bound = b > bound ? b : bound;
-      if (lane == 0) put<kSelect>(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);
-    }
-  }
+  if (union_mode) chunk_list<TPW, kSelect>(a, i, chunk, n, w0, key, sh.lst);
 
   if (!kSelect) return false;
   // ---- the last work-group of this query selects
@@ -400,7 +473,6 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   publish();
   return true;
 }
-
 
 }  // namespace itk
 }  // namespace qsa

@@ -115,18 +115,33 @@ __device__ __forceinline__ uint64_t wave_best_excluded(const uint32_t (&key)[R],
 // Element j = tid * R + r lives in key[r] of thread tid (so element order is
 // thread order, then register order). Empty slots hold 0.
 
+// Once the threshold digit's bin holds at most this many keys, they move
+// to LDS and one wave finds the exact threshold among them bit by bit (one
+// ballot per bit), instead of more histogram passes over every key.
+constexpr int kRegSelCand = 64;
+
+// Histogram bins 256 + lane and counters / slots past the candidates are
+// per-lane dummies: keys that take no part in a pass still issue their LDS
+// atomic or store (to a lane of their own, so no two lanes of one
+// instruction collide), which keeps the per-key loops free of branches.
 template <int NT>
 struct RegSelLds {
-  uint32_t hist[3][256];
+  uint32_t hist[3][256 + 64];
   uint32_t wmax[NT / 64], wmin[NT / 64];
   int wg[NT / 64], we[NT / 64];
   int pg[64], pe[64];  // register-major positions: counts per (register, wave)
+  uint32_t cand[kRegSelCand + 64];
+  uint32_t n_cand[1 + 64];
+  uint32_t res_key;
+  int res_need;
   int tau_slot;
   int tau_val;
 };
 
 // The k-th largest nonzero key (kstar) and need = k - #{key > kstar} >= 1.
-// Requires 1 <= k <= number of nonzero keys.
+// Requires 1 <= k <= number of nonzero keys. 8-bit radix passes narrow the
+// threshold to one bin; as soon as that bin holds at most kRegSelCand keys,
+// they are gathered in LDS and wave 0 settles the remaining low bits.
 template <int NT, int R>
 __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>& sh, uint32_t& kstar, int& need) {
   constexpr int NW = NT / 64;
@@ -146,6 +161,7 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
     sh.wmin[wave] = mn;
   }
   for (int b = threadIdx.x; b < 256; b += NT) sh.hist[0][b] = 0u;
+  if (threadIdx.x == 0) sh.n_cand[0] = 0u;
   __syncthreads();
 #pragma unroll
   for (int w = 0; w < NW; w++) {
@@ -163,6 +179,7 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
   uint32_t prefix = mx & mask;
   int remaining = k;
   int pass = 0;
+  int dcnt = 0;  // keys in the bin chosen last
   while (lo > 0) {
     const int width = lo < 8 ? lo : 8;
     const int shift = lo - width;
@@ -171,8 +188,10 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
     uint32_t* hz = sh.hist[(pass + 1) % 3];
     for (int b = threadIdx.x; b < 256; b += NT) hz[b] = 0u;
 #pragma unroll
-    for (int r = 0; r < R; r++)
-      if (key[r] != 0u && (key[r] & mask) == prefix) atomicAdd(&h[(key[r] >> shift) & dmask], 1u);
+    for (int r = 0; r < R; r++) {
+      const bool in = key[r] != 0u && (key[r] & mask) == prefix;
+      atomicAdd(&h[in ? (key[r] >> shift) & dmask : 256u + lane], 1u);
+    }
     __syncthreads();
     // every wave finds the digit (same result everywhere): lane holds the
     // bins 255 - 4*lane - e, e = 0..3, i.e. digits in descending order
@@ -184,12 +203,13 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
       lsum += cnt[e];
     }
     int above = wave_incl_sum(lsum) - lsum;
-    int my_digit = -1, my_above = 0;
+    int my_digit = -1, my_above = 0, my_cnt = 0;
 #pragma unroll
     for (int e = 0; e < 4; e++) {
       if (my_digit < 0 && above < remaining && remaining <= above + cnt[e]) {
         my_digit = 255 - (4 * lane + e);
         my_above = above;
+        my_cnt = cnt[e];
       }
       above += cnt[e];
     }
@@ -197,13 +217,47 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
     const int src = int(__ffsll(static_cast<unsigned long long>(hit)) - 1);
     const uint32_t digit = uint32_t(__builtin_amdgcn_readlane(my_digit, src));
     remaining -= __builtin_amdgcn_readlane(my_above, src);
+    dcnt = __builtin_amdgcn_readlane(my_cnt, src);
     prefix |= digit << shift;
     mask |= dmask << shift;
     lo = shift;
     pass++;
+    if (dcnt <= kRegSelCand) break;
   }
-  kstar = prefix;
-  need = remaining;
+  if (lo == 0) {  // every bit settled by the passes
+    kstar = prefix;
+    need = remaining;
+    return;
+  }
+  // the dcnt keys of the chosen bin (1 <= remaining <= dcnt of them are
+  // still needed): the largest t with #{bin keys >= t} >= remaining is the
+  // threshold, found from the top remaining bit down
+  uint32_t slot[R];
+#pragma unroll
+  for (int r = 0; r < R; r++) {
+    const bool in = key[r] != 0u && (key[r] & mask) == prefix;
+    slot[r] = atomicAdd(&sh.n_cand[in ? 0 : 1 + lane], 1u);
+    slot[r] = in ? slot[r] : uint32_t(kRegSelCand + lane);
+  }
+#pragma unroll
+  for (int r = 0; r < R; r++) sh.cand[slot[r]] = key[r];
+  __syncthreads();
+  if (wave == 0) {
+    const uint32_t c = lane < dcnt ? sh.cand[lane] : 0u;
+    uint32_t t = prefix;
+    for (int bit = lo - 1; bit >= 0; bit--) {
+      const uint32_t cd = t | (1u << bit);
+      if (__popcll(__ballot(c >= cd)) >= remaining) t = cd;
+    }
+    const int gt = __popcll(__ballot(c > t));
+    if (lane == 0) {
+      sh.res_key = t;
+      sh.res_need = remaining - gt;
+    }
+  }
+  __syncthreads();
+  kstar = sh.res_key;
+  need = sh.res_need;
 }
 
 // Output position of every element (-1 if not selected): keys > kstar and
