@@ -103,6 +103,64 @@ def decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: De
 
 
 @dataclass
+class MicroBatch:
+    """Sequences lo .. hi-1 of a decode batch, with their own buffers (one
+    set per layer) and their slices of the batch's q_ctx / q_seq."""
+    lo: int
+    hi: int
+    q_ctx: torch.Tensor
+    q_seq: torch.Tensor
+    bufs: list
+
+
+def micro_batches(sel_cfg, attn_cfg, q_ctx, q_seq, max_ctx, n_layers, n_micro, n_split=None, device="cuda"):
+    """Split a decode batch into n_micro contiguous micro-batches. Each keeps
+    the batch's max_ctx and n_split (the whole batch's default unless given),
+    so its layers run exactly the batch's kernels on its own sequences."""
+    nq = int(q_ctx.numel())
+    if not 1 <= n_micro <= nq:
+        raise ValueError(f"n_micro {n_micro} not in [1, {nq}]")
+    if n_split is None:
+        n_split = default_n_split(nq, attn_cfg.hkv, sel_cfg.topk * sel_cfg.block + sel_cfg.block - 1)
+    out = []
+    for m in range(n_micro):
+        lo, hi = m * nq // n_micro, (m + 1) * nq // n_micro
+        out.append(MicroBatch(lo, hi, q_ctx[lo:hi].contiguous(), q_seq[lo:hi].contiguous(),
+                              [decode_buffers(sel_cfg, attn_cfg, hi - lo, max_ctx, n_split=n_split, device=device)
+                               for _ in range(n_layers)]))
+    return out
+
+
+def decode_step_streams(sel_cfg, attn_cfg, max_ctx, layers, micro, side_streams) -> None:
+    """One decode step of a batch split into micro-batches: each micro-batch
+    goes through the layers in order (one qsa_decode_layer call per layer)
+    on a stream of its own, the first on the current stream and the others
+    on side_streams (default priority); the current stream then waits for
+    all of them. A micro-batch's layer l depends only on its own layer l - 1,
+    so the streams' scans and attention tails can overlap. layers: one
+    (q_idx, keys, q, kv) per layer, q_idx and q over the whole batch (their
+    rows lo .. hi-1 go to each micro-batch); keys and kv are addressed by
+    q_seq. Results land in each micro-batch's bufs[l]."""
+    if len(side_streams) < len(micro) - 1:
+        raise ValueError("need one side stream per micro-batch after the first")
+    cur = torch.cuda.current_stream()
+    for s in side_streams[:len(micro) - 1]:
+        s.wait_stream(cur)
+
+    def chain(mb):
+        for (q_idx, keys, q, kv), bf in zip(layers, mb.bufs):
+            decode_layer(sel_cfg, attn_cfg, mb.q_ctx, max_ctx, q_idx[mb.lo:mb.hi], keys, q[mb.lo:mb.hi], kv, bf,
+                         q_seq=mb.q_seq, fused=True)
+
+    chain(micro[0])
+    for s, mb in zip(side_streams, micro[1:]):
+        with torch.cuda.stream(s):
+            chain(mb)
+    for s in side_streams[:len(micro) - 1]:
+        cur.wait_stream(s)
+
+
+@dataclass
 class PrefillBuffers:
     scores: torch.Tensor      # [nq, max_ctx / block] fp32
     sel: torch.Tensor

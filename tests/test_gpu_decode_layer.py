@@ -234,3 +234,62 @@ def test_host_kv_must_be_pinned(Q):
     k = torch.zeros(1, 8, 2, 256, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         pkg.make_kv(k, k)
+
+
+def test_two_stream_schedule_is_the_batch_step(Q):
+    """The decode step as two micro-batches (sequences 0-1 and 2-3), each
+    going through its layers in order on a stream of its own
+    (pipeline.decode_step_streams), computes the batch-4 step: selections,
+    outputs (fp32 and bf16) and lse bit-identical to one qsa_decode_layer
+    call per layer over the whole batch. Checked eagerly and over graph
+    replays with eager work between them."""
+    pkg, pipeline = Q
+    ctxs = [70000, 41003, 70000, 9002]
+    cap = max(ctxs)
+    n_layers, nq = 3, len(ctxs)
+    layers, refs = [], []
+    q_ctx, q_seq = qc.i32(ctxs), qc.i32(range(nq))
+    for l in range(n_layers):
+        case = qc.DecodeCase(90 + l, ctxs, cap=cap)
+        pooled = torch.zeros(nq, case.cap // 4, 128, dtype=torch.bfloat16, device="cuda")
+        pkg.qsa_pool_keys(qc.to_dev(case.raw), pooled, block=4)
+        kv = pkg.make_kv(qc.to_dev(case.k), qc.to_dev(case.v))
+        q_idx, q = qc.to_dev(case.q_idx[:, None, :]), qc.to_dev(case.q)
+        layers.append((q_idx, pooled, q, kv))
+        bf = pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, nq, cap)
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, cap, q_idx, pooled, q, kv, bf, q_seq=q_seq, fused=True)
+        refs.append(bf)
+    torch.cuda.synchronize()
+    n_split = refs[0].n_split
+    micro = pipeline.micro_batches(pkg.SEL_A, pkg.ATTN_A, q_ctx, q_seq, cap, n_layers, 2, n_split=n_split)
+    side = [torch.cuda.Stream()]
+
+    def check(tag):
+        for l, ref in enumerate(refs):
+            for mb in micro:
+                bf = mb.bufs[l]
+                pkg.check_decode_layer_error(bf.layer_ws)
+                for name in ("sel", "n_sel", "o", "o_bf16", "lse"):
+                    got, want = getattr(bf, name), getattr(ref, name)[mb.lo:mb.hi]
+                    assert torch.equal(got, want), f"{tag}: layer {l}, sequences {mb.lo}-{mb.hi - 1}: {name}"
+
+    _print_case("two_stream_eager", ctxs=ctxs)
+    pipeline.decode_step_streams(pkg.SEL_A, pkg.ATTN_A, cap, layers, micro, side)
+    torch.cuda.synchronize()
+    check("eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pipeline.decode_step_streams(pkg.SEL_A, pkg.ATTN_A, cap, layers, micro, side)
+    for rep in range(3):
+        _print_case("two_stream_graph", rep=rep)
+        for mb in micro:
+            for bf in mb.bufs:
+                bf.o.zero_()
+                bf.lse.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        check(f"graph replay {rep}")
+        # eager work between replays: the batch call on layer 0 again
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, q_ctx, cap, *layers[0], refs[0], q_seq=q_seq, fused=True)
+        torch.cuda.synchronize()
+    del g
