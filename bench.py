@@ -564,8 +564,17 @@ def run_prefill(pkg, pipeline, bm, qi, torch, steps, warmup):
             t_at = time_launches(torch, tiles_only, r)
             t_mg = time_launches(torch, lambda: pkg.qsa_lse_merge(bufs.o_tiles, bufs.lse_tiles, o_out=bufs.o,
                                                                   o_out_bf16=bufs.o_bf16, lse_out=bufs.lse), r)
+
+            def tiles_running():
+                last = len(bufs.tiles) - 1
+                for t, (a0, a1) in enumerate(bufs.tiles):
+                    pkg.qsa_sparse_prefill_merge(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, bufs.sel, bufs.n_sel,
+                                                 a0, a1, t == 0, t == last, bufs.o, bufs.lse, o_out_bf16=bufs.o_bf16)
+
+            t_rm = time_launches(torch, tiles_running, r)
             out["breakdown_us"] = {"scores": round(t_sc * 1e3, 1), "topk": round(t_tk * 1e3, 1),
-                                   "attend_all_tiles": round(t_at * 1e3, 1), "merge": round(t_mg * 1e3, 1)}
+                                   "attend_all_tiles": round(t_at * 1e3, 1), "merge": round(t_mg * 1e3, 1),
+                                   "attend_all_tiles_running_merge": round(t_rm * 1e3, 1)}
             out["attend_tflops"] = round(flops["attention"] / (t_at * 1e-3) / 1e12, 1)
         del g, bufs
         log(f"prefill tile {tile}: {ms:.3f} ms/chunk")

@@ -484,6 +484,31 @@ qsa_status qsa_sparse_prefill(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* at
                               int64_t tile_begin, int64_t tile_end,
                               float* o_part, float* lse_part, qsa_stream_t stream);
 
+/* qsa_sparse_prefill_merge: qsa_sparse_prefill for one history tile, merged
+ * at once into the running result of the tiles before it (the same
+ * log-sum-exp combination as qsa_lse_merge, one tile at a time), so that no
+ * per-tile partials are kept and no final merge is needed (same sources as
+ * qsa_sparse_prefill; "GLM-5.3 最適化 第2部", section "DCP", for the merge).
+ *   o_run (device) fp32 [nq][hq][dv] and lse_run (device) fp32 [nq][hq]:
+ *     with first == 0, the merge of the earlier tiles (as this call left
+ *     it); with first != 0 their contents are ignored. On return they hold
+ *     the merge including this tile; a query with no token in any tile so
+ *     far has O = 0, lse = -inf.
+ *   last != 0 and o_out_bf16 (device, 16-byte aligned, [nq][hq][dv]) non-NULL:
+ *     the merged output is also written as bf16.
+ *   Tiles merge in call order: issue them on one stream. Equal to
+ *   qsa_sparse_prefill per tile followed by qsa_lse_merge up to rounding.
+ *   Pooled-block variant only (16 / 2 heads, head dim 256, bf16 K/V rows);
+ *   otherwise QSA_ERR_UNSUPPORTED. Other arguments and errors as
+ *   qsa_sparse_prefill. */
+qsa_status qsa_sparse_prefill_merge(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
+                                    int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
+                                    int32_t max_ctx, const qsa_bf16* q, const qsa_kv* kv,
+                                    const int32_t* sel, const int32_t* n_sel,
+                                    int64_t tile_begin, int64_t tile_end, int32_t first, int32_t last,
+                                    float* o_run, float* lse_run, qsa_bf16* o_out_bf16,
+                                    qsa_stream_t stream);
+
 /* ---------------------------------------------------------------- A5 ----
  * qsa_lse_merge: combine n_part partial softmax results per row.
  *   lse = M + ln sum_p exp(lse_p - M), M = max_p lse_p;

@@ -11,7 +11,8 @@ from .qsa import (  # noqa: F401
     qsa_quantize_latent,
     qsa_decode_layer, qsa_decode_layer_noalloc, qsa_decode_layer_workspace_bytes, qsa_index_scores,
     qsa_index_topk, qsa_index_topk_workspace_bytes, index_topk_workspace, qsa_index_lists,
-    qsa_kv_append, qsa_lse_merge, qsa_pool_keys, qsa_sparse_decode, qsa_sparse_prefill, qsa_topk_blocks,
+    qsa_kv_append, qsa_lse_merge, qsa_pool_keys, qsa_sparse_decode, qsa_sparse_prefill, qsa_sparse_prefill_merge,
+    qsa_topk_blocks,
     qsa_topk_workspace_bytes, qsa_version, topk_workspace, decode_layer_error, check_decode_layer_error,
     qsa_index_topk_prefill, qsa_index_topk_prefill_workspace_bytes, index_topk_prefill_workspace,
     qsa_row_cache_bytes, qsa_decode_cached_plan_bytes, row_cache_empty, qsa_row_cache_step, qsa_sparse_decode_cached,

@@ -850,6 +850,35 @@ qsa_status qsa_sparse_prefill(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* at
   return finish(qsa::launch_attend(a, s), s, "qsa_sparse_prefill");
 }
 
+qsa_status qsa_sparse_prefill_merge(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                    const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q,
+                                    const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel, int64_t tile_begin,
+                                    int64_t tile_end, int32_t first, int32_t last, float* o_run, float* lse_run,
+                                    qsa_bf16* o_out_bf16, qsa_stream_t stream) {
+  qsa_status st = check_attn(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel, o_run, lse_run);
+  if (st != QSA_OK) return st;
+  if (attn_cfg->hq != 16 || attn_cfg->hkv != 2 || attn_cfg->dk != 256 || attn_cfg->dv != 256 ||
+      kv->format != QSA_KV_BF16)
+    return fail(QSA_ERR_UNSUPPORTED, "the running tile merge covers the pooled-block variant (16 / 2 heads, "
+                                     "head dim 256, bf16 rows)");
+  if (tile_begin < 0 || tile_end < tile_begin) return fail(QSA_ERR_ARG, "bad tile range");
+  if (tile_begin % sel_cfg->block) return fail(QSA_ERR_ARG, "tile_begin must be a multiple of block");
+  if (tile_end % sel_cfg->block && tile_end < max_ctx)
+    return fail(QSA_ERR_ARG, "tile_end must be a multiple of block (or >= max_ctx)");
+  if (o_out_bf16 && !aligned16(o_out_bf16)) return fail(QSA_ERR_ARG, "o_out_bf16 must be 16-byte aligned");
+  if (nq == 0) return QSA_OK;
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::AttendArgs a = attend_args(sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q, kv, sel, n_sel, 1, tile_begin,
+                                  tile_end, o_run, lse_run);
+  a.acc = 4 | (first ? 1 : 0) | (last ? 2 : 0);
+  a.o_bf16 = last ? reinterpret_cast<uint16_t*>(o_out_bf16) : nullptr;
+  return finish(qsa::launch_attend(a, s), s, "qsa_sparse_prefill_merge");
+}
+
 qsa_status qsa_lse_merge(int32_t n_part, int64_t rows, int32_t dv, const float* o_parts, int64_t o_part_stride,
                          const float* lse_parts, int64_t lse_part_stride, float* o_out, qsa_bf16* o_out_bf16,
                          float* lse_out, qsa_stream_t stream) {

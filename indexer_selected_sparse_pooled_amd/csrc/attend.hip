@@ -36,6 +36,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   mla::attend_part_fp8<false>(a, split, i, sh);
 }
 
+// The pooled-block variant, one history tile merged into the running result
+// of the earlier tiles (AttendArgs::acc).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 8))) void attend_a_acc(AttendArgs a) {
+  __shared__ att::Lds<1> sh;
+  const int split = blockIdx.x % a.n_split, i = blockIdx.x / a.n_split;
+  att::attend_part<false, 1, false, true>(a, split, blockIdx.y, i, sh);
+}
+
 // The pooled-block variant over K/V in host memory with the HBM row cache.
 __global__ __launch_bounds__(256) void attend_a_cached(AttendArgs a) {
   __shared__ att::Lds<1> sh;
@@ -51,6 +59,8 @@ hipError_t launch_attend(const AttendArgs& a, hipStream_t s) {
     dim3 grid(unsigned(int64_t(a.nq) * a.n_split), unsigned(a.hkv));
     if (a.src)
       hipLaunchKernelGGL(attend_a_cached, grid, dim3(256), 0, s, a);
+    else if (a.acc)
+      hipLaunchKernelGGL(attend_a_acc, grid, dim3(256), 0, s, a);
     else
       hipLaunchKernelGGL(attend_a, grid, dim3(256), 0, s, a);
     return hipGetLastError();

@@ -54,6 +54,7 @@ struct Lds {
   __attribute__((aligned(16))) uint16_t phi[kG * kPStr];
   __attribute__((aligned(16))) uint16_t plo[kG * kPStr];
   float alpha[kG], m[kG], l[kG];
+  int cnt[4];
 };
 
 // sel may have been written earlier in the same launch by another
@@ -91,19 +92,24 @@ struct List {
     }
     return nblk * block + (p - nb_tok);
   }
-  // number of list entries whose token is < x (x a multiple of block, or >= ctx)
-  __device__ int count_below(int64_t x, int ctx) const {
-    if (x <= 0) return 0;
-    if (x >= ctx) return L;
-    const int nb_tok = nblk * block;
-    if (x >= nb_tok) return ns * block + int(x - nb_tok);
-    const int xb = int(x) / block;  // 0 < x < ctx here
-    int lo = 0, hi = ns;  // first selected block >= xb
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (sel_at(mid) < xb) lo = mid + 1; else hi = mid;
+  // the number of list entries whose token is < x (x a multiple of block,
+  // or >= ctx) when it follows from the sizes alone (true), else false: x
+  // falls among the selected blocks and their count below x / block decides
+  __device__ __forceinline__ bool below_known(int64_t x, int ctx, int& val) const {
+    if (x <= 0) {
+      val = 0;
+      return true;
     }
-    return lo * block;
+    if (x >= ctx) {
+      val = L;
+      return true;
+    }
+    const int nb_tok = nblk * block;
+    if (x >= nb_tok) {
+      val = ns * block + int(x - nb_tok);
+      return true;
+    }
+    return false;
   }
 };
 
@@ -113,6 +119,44 @@ struct List {
 // is a long emulated sequence).
 __device__ __forceinline__ int split_point(int split, int L, int n_split) {
   return int(uint32_t(split) * uint32_t(L) / uint32_t(n_split));
+}
+
+// The part's list range [P0, P1): its split of the list intersected with
+// the positions of the tokens in [tile_begin, tile_end), the same on every
+// thread of the work-group (NT threads, all calling). A tile bound that
+// falls among the selected blocks is settled by all threads at once: each
+// reads ns / NT entries of the (ascending) selection and counts those below
+// the bound's block, then one block sum (cnt: NT / 64 ints of LDS, one
+// barrier, only when a bound needs it), in place of a binary search of
+// dependent loads.
+template <bool kCoh, int NT>
+__device__ void part_range(const List<kCoh>& lv, const AttendArgs& a, int split, int ctx, int* cnt, int& P0,
+                           int& P1) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lo = split_point(split, lv.L, a.n_split);
+  const int hi = split_point(split + 1, lv.L, a.n_split);
+  int t0, t1;
+  const bool k0 = lv.below_known(a.tile_begin, ctx, t0);
+  const bool k1 = lv.below_known(a.tile_end, ctx, t1);
+  if (!(k0 && k1)) {  // uniform
+    const int xb0 = k0 ? 0 : int(a.tile_begin) / lv.block;
+    const int xb1 = k1 ? 0 : int(a.tile_end) / lv.block;
+    int c = 0;  // below bound 0 in the low half, below bound 1 in the high half (ns <= 2048)
+    for (int j = tid; j < lv.ns; j += NT) {
+      const int b = lv.sel_at(j);
+      c += (b < xb0 ? 1 : 0) + (b < xb1 ? 0x10000 : 0);
+    }
+    c = __builtin_amdgcn_readlane(wave_incl_sum(c), 63);
+    if (lane == 0) cnt[wave] = c;
+    __syncthreads();
+    int s = 0;
+#pragma unroll
+    for (int w = 0; w < NT / 64; w++) s += cnt[w];
+    if (!k0) t0 = (s & 0xFFFF) * lv.block;
+    if (!k1) t1 = (s >> 16) * lv.block;
+  }
+  P0 = lo > t0 ? lo : t0;
+  P1 = hi < t1 ? hi : t1;
 }
 
 __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
@@ -127,7 +171,7 @@ __device__ __forceinline__ uint64_t shfl64(uint64_t v, int src) {
 // (the plan in a.src) and from their home (host) memory otherwise, and the
 // rows this part may fill are written to the cache after the tile
 // (row_cache.hip).
-template <bool kCoh, int GT, bool kCached = false>
+template <bool kCoh, int GT, bool kCached = false, bool kAcc = false>
 __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT>& sh, LdsIntPtr sel_lds = nullptr,
                             int ns_lds = -1, int ctx_in = -1, int seq_in = -1) {
   const bool sel_lds_given = ns_lds >= 0;
@@ -151,12 +195,8 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
   lv.has_cache = sel_lds_given;
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
 
-  // every thread computes the same range (uniform, no hand-off)
-  const int lo = split_point(split, lv.L, a.n_split);
-  const int hi = split_point(split + 1, lv.L, a.n_split);
-  const int t0 = lv.count_below(a.tile_begin, ctx);
-  const int t1 = lv.count_below(a.tile_end, ctx);
-  const int P0 = lo > t0 ? lo : t0, P1 = hi < t1 ? hi : t1;
+  int P0, P1;
+  part_range<kCoh, 256>(lv, a, split, ctx, sh.cnt, P0, P1);
   if (tid < kG) {
     sh.m[tid] = -INFINITY;
     sh.l[tid] = 0.f;
@@ -183,6 +223,23 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
   f32x4 oacc[4];
 #pragma unroll
   for (int nt = 0; nt < 4; nt++) oacc[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // kAcc: the earlier tiles' merged result for this lane's elements (rows
+  // 4 kq + e < 8, dims 64 wave + 16 nt + r) and rows, loaded now so that the
+  // loads complete while the tile is attended
+  [[maybe_unused]] float run_o[4][4], run_lse[4];
+  if constexpr (kAcc) {
+    const bool first = a.acc & 1;
+    const int64_t row0 = int64_t(i) * a.hq + g * kG;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int row = 4 * kq + e;
+      const bool mine = !first && row < kG;
+      run_lse[e] = mine ? a.lse_part[row0 + row] : -INFINITY;
+#pragma unroll
+      for (int nt = 0; nt < 4; nt++)
+        run_o[e][nt] = mine ? a.o_part[(row0 + row) * kD + 64 * wave + 16 * nt + r] : 0.f;
+    }
+  }
 
   for (int pb = P0; pb < P1; pb += kTok) {
     const int cnt = (P1 - pb) < kTok ? (P1 - pb) : kTok;
@@ -378,6 +435,38 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
 
   // normalise and write the partial result
   const int64_t orow0 = (int64_t(split) * a.nq + i) * a.hq + g * kG;
+  if constexpr (kAcc) {
+    // merge with the earlier tiles (log-sum-exp weights; an empty side
+    // weighs 0) and write the running result in place
+    const bool last = a.acc & 2;
+#pragma unroll
+    for (int e = 0; e < 4; e++) {
+      const int row = 4 * kq + e;
+      if (row < kG) {
+        const float l = sh.l[row];
+        const float lse_t = l > 0.f ? (sh.m[row] + log2f(l)) * kLn2 : -INFINITY;
+        const float inv = l > 0.f ? 1.f / l : 0.f;
+        const float mx = fmaxf(run_lse[e], lse_t);
+        float w_run = 0.f, w_t = 0.f, lse = -INFINITY;
+        if (mx != -INFINITY) {
+          w_run = expf(run_lse[e] - mx);
+          w_t = expf(lse_t - mx);
+          lse = mx + logf(w_run + w_t);
+        }
+        const float norm = w_run + w_t > 0.f ? 1.f / (w_run + w_t) : 0.f;
+        const int64_t orow = orow0 + row;
+#pragma unroll
+        for (int nt = 0; nt < 4; nt++) {
+          const float o = (run_o[e][nt] * w_run + oacc[nt][e] * inv * w_t) * norm;
+          const int64_t idx = orow * kD + 64 * wave + 16 * nt + r;
+          a.o_part[idx] = o;
+          if (last && a.o_bf16) a.o_bf16[idx] = f32_to_bf16(o);
+        }
+        if (r == 0 && wave == 0) a.lse_part[orow] = lse;
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int e = 0; e < 4; e++) {
     const int row = 4 * kq + e;

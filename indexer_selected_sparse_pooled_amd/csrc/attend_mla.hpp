@@ -37,13 +37,14 @@ constexpr int kDV = 512;    // V columns (first kDV of the row)
 constexpr int kTT = 32;     // tokens per tile
 constexpr int kRowC = kDK / 8;          // 16-byte chunks per latent row (72)
 constexpr int kRowL = kRowC + 1;        // LDS chunks per row incl. one pad chunk (73)
+constexpr int kNTPART = 256;             // threads of every shared-latent attention work-group
 constexpr int kTileC = kTT * kRowL;     // LDS chunks per tile (2336)
 constexpr int kPStr = kTT + 8;          // LDS row of P in elements (80 bytes)
 
 struct Lds {
   __attribute__((aligned(16))) unsigned char kv[kTileC * 16];
   __attribute__((aligned(16))) uint16_t p[4][2][16 * kPStr];  // per wave: P hi, lo [head][token]
-  int64_t range[2];
+  int cnt[kNTPART / 64];
 };
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -63,16 +64,9 @@ __device__ void attend_part(const AttendArgs& a, int split, int i, Lds& sh) {
   const int ns = kCoh ? ns_max : a.n_sel[i];
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
-  if (tid == 0) {
-    const int lo = att::split_point(split, lv.L, a.n_split);
-    const int hi = att::split_point(split + 1, lv.L, a.n_split);
-    const int t0 = lv.count_below(a.tile_begin, ctx);
-    const int t1 = lv.count_below(a.tile_end, ctx);
-    sh.range[0] = lo > t0 ? lo : t0;
-    sh.range[1] = hi < t1 ? hi : t1;
-  }
-  __syncthreads();
-  const int P0 = int(sh.range[0]), P1 = int(sh.range[1]);
+  int P0_, P1_;
+  att::part_range<kCoh, kNTPART>(lv, a, split, ctx, sh.cnt, P0_, P1_);
+  const int P0 = P0_, P1 = P1_;
 
   const uint16_t* kvbase = a.k + int64_t(seq) * a.seq_stride;
   const float sl2 = a.scale * kLog2e;
@@ -227,7 +221,7 @@ struct LdsT {
   __attribute__((aligned(16))) unsigned char kv[2][kTileC * 16];
   int selbuf[2][kSelSlot];
   float lsum[kH];
-  int64_t range[2];
+  int cnt[kNTPART / 64];
 };
 
 __device__ __forceinline__ float rows_max(float v) {
@@ -426,23 +420,16 @@ __device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
   const int ns = kCoh ? ns_max : a.n_sel[i];
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns;
-  if (tid == 0) {
-    const int lo = att::split_point(split, lv.L, a.n_split);
-    const int hi = att::split_point(split + 1, lv.L, a.n_split);
-    const int t0 = lv.count_below(a.tile_begin, ctx);
-    const int t1 = lv.count_below(a.tile_end, ctx);
-    sh.range[0] = lo > t0 ? lo : t0;
-    sh.range[1] = hi < t1 ? hi : t1;
-  }
-  __syncthreads();
+  int P0_, P1_;
+  att::part_range<kCoh, kNTPART>(lv, a, split, ctx, sh.cnt, P0_, P1_);
   TList ls;
   ls.sel = lv.sel;
   ls.topk = a.topk;
   ls.ctx = ctx;
   // the part's range is the same on every lane: keep it (and what derives
   // from it) in scalar registers
-  ls.P0 = __builtin_amdgcn_readfirstlane(int(sh.range[0]));
-  ls.n_list = __builtin_amdgcn_readfirstlane(int(sh.range[1])) - ls.P0;
+  ls.P0 = __builtin_amdgcn_readfirstlane(P0_);
+  ls.n_list = __builtin_amdgcn_readfirstlane(P1_) - ls.P0;
   const int n_tiles = (ls.n_list + kTT - 1) / kTT;
 
   const uint16_t* kvbase = a.k + int64_t(seq) * a.seq_stride;
@@ -512,7 +499,7 @@ struct LdsF8 {
   __attribute__((aligned(16))) uint16_t p[4][2][16 * kPStr];
   __attribute__((aligned(16))) float pf[4][64][8];  // per wave and lane: the tile's P before scaling
   float sc[kTT][4];
-  int64_t range[2];
+  int cnt[kNTPART / 64];
 };
 
 template <bool kCoh>
@@ -530,16 +517,9 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
   const int ns = kCoh ? ns_max : a.n_sel[i];
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns * a.block + (ctx - lv.nblk * a.block);
-  if (tid == 0) {
-    const int lo = att::split_point(split, lv.L, a.n_split);
-    const int hi = att::split_point(split + 1, lv.L, a.n_split);
-    const int t0 = lv.count_below(a.tile_begin, ctx);
-    const int t1 = lv.count_below(a.tile_end, ctx);
-    sh.range[0] = lo > t0 ? lo : t0;
-    sh.range[1] = hi < t1 ? hi : t1;
-  }
-  __syncthreads();
-  const int P0 = int(sh.range[0]), P1 = int(sh.range[1]);
+  int P0_, P1_;
+  att::part_range<kCoh, kNTPART>(lv, a, split, ctx, sh.cnt, P0_, P1_);
+  const int P0 = P0_, P1 = P1_;
 
   // strides in bytes
   const unsigned char* kvbase = reinterpret_cast<const unsigned char*>(a.k) + int64_t(seq) * a.seq_stride;

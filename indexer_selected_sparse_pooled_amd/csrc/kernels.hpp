@@ -143,6 +143,12 @@ struct AttendArgs {
   float* o_out;       // [nq][hq][dv] or nullptr
   uint16_t* o_bf16;   // [nq][hq][dv] or nullptr
   float* lse_out;     // [nq][hq] or nullptr
+  // running merge over history tiles (n_split 1, pooled-block variant):
+  // o_part / lse_part hold the merge of the earlier tiles and receive the
+  // merge with this one. 0: off; else bit 2 set, bit 0: first tile (no
+  // earlier result), bit 1: last tile (the merged output also goes to
+  // o_bf16 when given)
+  int acc;
   // HBM row cache (qsa_sparse_decode_cached); src == nullptr: none
   const int* src;           // [nq][src_ld] per list position: -(slot + 1) for a hit, else the token
   int src_ld;

@@ -147,15 +147,15 @@ def decode_step_streams(sel_cfg, attn_cfg, max_ctx, layers, micro, side_streams)
     for s in side_streams[:len(micro) - 1]:
         s.wait_stream(cur)
 
-    def chain(mb):
-        for (q_idx, keys, q, kv), bf in zip(layers, mb.bufs):
-            decode_layer(sel_cfg, attn_cfg, mb.q_ctx, max_ctx, q_idx[mb.lo:mb.hi], keys, q[mb.lo:mb.hi], kv, bf,
-                         q_seq=mb.q_seq, fused=True)
-
-    chain(micro[0])
-    for s, mb in zip(side_streams, micro[1:]):
-        with torch.cuda.stream(s):
-            chain(mb)
+    streams = [cur] + list(side_streams[:len(micro) - 1])
+    # issued layer by layer, alternating between the micro-batches, so that
+    # the streams' work is submitted interleaved (a captured graph keeps
+    # this order) rather than one micro-batch's whole chain first
+    for l, (q_idx, keys, q, kv) in enumerate(layers):
+        for s, mb in zip(streams, micro):
+            with torch.cuda.stream(s):
+                decode_layer(sel_cfg, attn_cfg, mb.q_ctx, max_ctx, q_idx[mb.lo:mb.hi], keys, q[mb.lo:mb.hi], kv,
+                             mb.bufs[l], q_seq=mb.q_seq, fused=True)
     for s in side_streams[:len(micro) - 1]:
         cur.wait_stream(s)
 
@@ -180,17 +180,29 @@ def history_tiles(ctx_max: int, tile: int):
     return [(a, min(a + tile, ctx_max)) for a in range(0, ctx_max, tile)]
 
 
-def prefill_buffers(sel_cfg, attn_cfg, nq, max_ctx, tile, device="cuda") -> PrefillBuffers:
+def running_tile_merge(attn_cfg) -> bool:
+    """Whether qsa_sparse_prefill_merge covers this attention (the
+    pooled-block variant): a chunk can then merge its history tiles as they
+    complete instead of keeping per-tile partials (no partial buffers, no
+    final merge; each tile reads the running result back, so it takes longer
+    per tile)."""
+    return (attn_cfg.hq, attn_cfg.hkv, attn_cfg.dk, attn_cfg.dv) == (16, 2, 256, 256)
+
+
+def prefill_buffers(sel_cfg, attn_cfg, nq, max_ctx, tile, device="cuda", partials=True) -> PrefillBuffers:
+    """partials: allocate per-tile partial results (o_tiles, lse_tiles);
+    a chunk run with running_merge=True does without them."""
     nmax = max(1, max_ctx // sel_cfg.block)
     tiles = history_tiles(max_ctx, tile)
     f32 = dict(dtype=torch.float32, device=device)
+    n_part = len(tiles) if partials else 0
     return PrefillBuffers(
         scores=torch.empty(nq, nmax, **f32),
         sel=torch.empty(nq, sel_cfg.topk, dtype=torch.int32, device=device),
         n_sel=torch.empty(nq, dtype=torch.int32, device=device),
         ws=qsa.topk_workspace(sel_cfg, nq, max_ctx, device),
-        o_tiles=torch.empty(len(tiles), nq, attn_cfg.hq, attn_cfg.dv, **f32),
-        lse_tiles=torch.empty(len(tiles), nq, attn_cfg.hq, **f32),
+        o_tiles=torch.empty(n_part, nq, attn_cfg.hq, attn_cfg.dv, **f32),
+        lse_tiles=torch.empty(n_part, nq, attn_cfg.hq, **f32),
         o=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, **f32),
         o_bf16=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, dtype=torch.bfloat16, device=device),
         lse=torch.empty(nq, attn_cfg.hq, **f32),
@@ -201,9 +213,11 @@ def prefill_buffers(sel_cfg, attn_cfg, nq, max_ctx, tile, device="cuda") -> Pref
 
 
 def prefill_chunk(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: PrefillBuffers,
-                  w_idx=None, stream=None, fused_select=True) -> None:
+                  w_idx=None, stream=None, fused_select=True, running_merge=False) -> None:
     """A chunk of queries of one sequence: selection, then the history tiles
-    in the outer loop (one attention call per tile), then the merge. The
+    in the outer loop (one attention call per tile), then the merge of the
+    per-tile partials; with running_merge (pooled-block variant), each tile
+    is merged into the running result as it completes instead. The
     token-level indexer selects in one call (qsa_index_topk_prefill) unless
     fused_select is False."""
     if fused_select and bufs.sel_ws is not None:
@@ -213,6 +227,17 @@ def prefill_chunk(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: P
         qsa.qsa_index_scores(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, q_seq=None, w_idx=w_idx,
                              stream=stream)
         qsa.qsa_topk_blocks(sel_cfg, q_ctx, max_ctx, bufs.scores, bufs.sel, bufs.n_sel, bufs.ws, stream=stream)
+    if running_merge:
+        if not (running_tile_merge(attn_cfg) and kv.format == qsa.KV_BF16):
+            raise ValueError("the running tile merge covers the pooled-block variant with bf16 K/V rows")
+        # each tile merged into the running result as it completes
+        last = len(bufs.tiles) - 1
+        for t, (a, b) in enumerate(bufs.tiles):
+            qsa.qsa_sparse_prefill_merge(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, a, b,
+                                         t == 0, t == last, bufs.o, bufs.lse, o_out_bf16=bufs.o_bf16, stream=stream)
+        return
+    if bufs.o_tiles.shape[0] != len(bufs.tiles):
+        raise ValueError("prefill_buffers(..., partials=True) is needed for this attention")
     for t, (a, b) in enumerate(bufs.tiles):
         qsa.qsa_sparse_prefill(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, a, b,
                                bufs.o_tiles[t], bufs.lse_tiles[t], stream=stream)

@@ -91,6 +91,8 @@ _SIGS = {
     "qsa_sparse_decode_cached": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp, _sz,
                                  _i64, _vp, _sz, _vp],
     "qsa_sparse_prefill": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _vp, _vp, _vp],
+    "qsa_sparse_prefill_merge": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i64, _i64, _i32, _i32, _vp,
+                                 _vp, _vp, _vp],
     "qsa_lse_merge": [_i32, _i64, _i32, _vp, _i64, _vp, _i64, _vp, _vp, _vp, _vp],
     "qsa_status_string": [_i32],
     "qsa_last_error": [],
@@ -562,6 +564,25 @@ def qsa_sparse_prefill(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, til
         _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q, _BF16, "q"), ctypes.byref(kv),
         _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), tile_begin, tile_end,
         _dev(o_part, _F32, "o_part"), _dev(lse_part, _F32, "lse_part"), _stream(stream)))
+
+
+def qsa_sparse_prefill_merge(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, sel, n_sel, tile_begin, tile_end, first,
+                             last, o_run, lse_run, o_out_bf16=None, q_seq=None, stream=None):
+    """One history tile merged into the running result: o_run [nq, hq, dv] fp32, lse_run [nq, hq] fp32 (read
+    unless first, written); with last, the merged output also goes to o_out_bf16 [nq, hq, dv] bf16 if given."""
+    nq = q_ctx.shape[0]
+    if not q.is_contiguous() or not o_run.is_contiguous() or not lse_run.is_contiguous():
+        raise ValueError("q, o_run and lse_run must be contiguous")
+    if tuple(o_run.shape) != (nq, attn_cfg.hq, attn_cfg.dv) or tuple(lse_run.shape) != (nq, attn_cfg.hq):
+        raise ValueError("o_run must be [nq, hq, dv] and lse_run [nq, hq]")
+    if o_out_bf16 is not None and (tuple(o_out_bf16.shape) != tuple(o_run.shape) or not o_out_bf16.is_contiguous()):
+        raise ValueError("o_out_bf16 must be a contiguous [nq, hq, dv] tensor")
+    _check("qsa_sparse_prefill_merge", lib().qsa_sparse_prefill_merge(
+        ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"),
+        _dev(q_ctx, _I32, "q_ctx"), max_ctx, _dev(q, _BF16, "q"), ctypes.byref(kv),
+        _dev(sel, _I32, "sel"), _dev(n_sel, _I32, "n_sel"), tile_begin, tile_end, int(bool(first)),
+        int(bool(last)), _dev(o_run, _F32, "o_run"), _dev(lse_run, _F32, "lse_run"),
+        _dev(o_out_bf16, _BF16, "o_out_bf16"), _stream(stream)))
 
 
 def qsa_lse_merge(o_parts, lse_parts, o_out=None, o_out_bf16=None, lse_out=None, stream=None):

@@ -336,11 +336,12 @@ def test_decode_is_deterministic(Q):
 
 # ------------------------------------------------------------ A6 prefill --
 
-@pytest.mark.parametrize("tile", [8192, 1024, 332])
-def test_prefill_chunk_tiled(Q, tile):
+@pytest.mark.parametrize("tile,running", [(8192, False), (1024, False), (332, False), (1024, True), (332, True)])
+def test_prefill_chunk_tiled(Q, tile, running):
     """A prefill chunk of 48 queries after a 9000-token history: per-query
-    selection, tiles in the outer loop, log-sum-exp merge; every row equals
-    the oracle's decode at ctx = position + 1, whatever the tile size."""
+    selection, tiles in the outer loop, log-sum-exp merge (of the per-tile
+    partials, or running, tile by tile); every row equals the oracle's
+    decode at ctx = position + 1, whatever the tile size."""
     pkg, pipeline = Q
     hist, nq = 9000, 48
     ctx_max = hist + nq
@@ -355,9 +356,9 @@ def test_prefill_chunk_tiled(Q, tile):
     pooled = torch.zeros(1, ctx_max // 4, 128, dtype=torch.bfloat16, device="cuda")
     pkg.qsa_pool_keys(qc.to_dev(raw[None]), pooled, block=4)
     kv = pkg.make_kv(qc.to_dev(k[None]), qc.to_dev(v[None]))
-    bufs = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, nq, ctx_max, tile)
+    bufs = pipeline.prefill_buffers(pkg.SEL_A, pkg.ATTN_A, nq, ctx_max, tile, partials=not running)
     pipeline.prefill_chunk(pkg.SEL_A, pkg.ATTN_A, qc.i32(ctxs), ctx_max, qc.to_dev(q_idx), pooled, qc.to_dev(q),
-                           kv, bufs)
+                           kv, bufs, running_merge=running)
     torch.cuda.synchronize()
     pooled_np = orc.pool_keys(raw, 4)
     sel, n_sel = bufs.sel.cpu().numpy(), bufs.n_sel.cpu().numpy()
@@ -393,6 +394,61 @@ def test_prefill_tile_partials_match_oracle(Q):
         toks = orc.selected_tokens(sels[i], ctxs[i], 4)
         o_ref, l_ref = orc.prefill_tile(q[i], k, v, toks, a, b, 1.0 / 16)
         qc.check_attention(o_p[i], l_p[i], o_ref, l_ref)
+
+
+def test_prefill_running_merge_matches_partials(Q):
+    """qsa_sparse_prefill_merge over consecutive tiles (first / last flags,
+    the running result in place) against qsa_sparse_prefill per tile plus
+    qsa_lse_merge: equal within fp32 rounding of the merge order; lse
+    -inf and O = 0 for a query with no token in any tile so far; the bf16
+    output written by the last tile only."""
+    pkg, pipeline = Q
+    hist, nq = 9000, 24
+    ctx_max = hist + nq
+    k = qc.bits(54, 2, (ctx_max, 2, 256))
+    v = qc.bits(54, 3, (ctx_max, 2, 256))
+    q = qc.bits(54, 4, (nq, 16, 256))
+    rng = np.random.default_rng(11)
+    ctxs = [hist + i + 1 for i in range(nq)]
+    sels = [np.sort(rng.choice(c // 4, 512, replace=False)) for c in ctxs]
+    sels[5] = np.arange(1500, 2012)  # all inside one tile: empty before and after it
+    sel = torch.tensor(np.stack(sels).astype(np.int32), device="cuda")
+    n_sel = qc.i32([512] * nq)
+    kv = pkg.make_kv(qc.to_dev(k[None]), qc.to_dev(v[None]))
+    q_dev, q_ctx = qc.to_dev(q), qc.i32(ctxs)
+    tiles = pipeline.history_tiles(ctx_max, 2048)
+    o_p = torch.empty(len(tiles), nq, 16, 256, device="cuda")
+    l_p = torch.empty(len(tiles), nq, 16, device="cuda")
+    for t, (a, b) in enumerate(tiles):
+        pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q_dev, kv, sel, n_sel, a, b, o_p[t], l_p[t])
+    o_ref = torch.empty(nq, 16, 256, device="cuda")
+    l_ref = torch.empty(nq, 16, device="cuda")
+    pkg.qsa_lse_merge(o_p, l_p, o_out=o_ref, lse_out=l_ref)
+    o_run = torch.full((nq, 16, 256), float("nan"), device="cuda")
+    l_run = torch.full((nq, 16), float("nan"), device="cuda")
+    ob = torch.zeros(nq, 16, 256, dtype=torch.bfloat16, device="cuda")
+    for t, (a, b) in enumerate(tiles):
+        _print_case("prefill_running_merge", tile=t)
+        pkg.qsa_sparse_prefill_merge(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q_dev, kv, sel, n_sel, a, b, t == 0,
+                                     t == len(tiles) - 1, o_run, l_run, o_out_bf16=ob)
+        torch.cuda.synchronize()
+        if t == 0:
+            # query 5 has no token in the first tile yet
+            assert torch.all(torch.isneginf(l_run[5])) and torch.all(o_run[5] == 0)
+        if t < len(tiles) - 1:
+            assert torch.count_nonzero(ob.view(torch.int16)).item() == 0, "bf16 output before the last tile"
+    o_run, l_run, o_r, l_r = o_run.cpu().numpy(), l_run.cpu().numpy(), o_ref.cpu().numpy(), l_ref.cpu().numpy()
+    assert np.all(np.isfinite(l_run)) and np.max(np.abs(l_run - l_r)) <= 1e-5
+    for i in range(nq):
+        scale = np.max(np.abs(o_r[i]))
+        assert np.max(np.abs(o_run[i] - o_r[i])) <= 1e-5 * scale, f"query {i}"
+    obf = orc.bf16_to_f64(qc.from_dev_bits(ob))
+    assert np.max(np.abs(obf - o_run)) <= 2.0**-8 * np.max(np.abs(o_run))
+    # and against the oracle directly
+    for i in (0, 5, nq - 1):
+        toks = orc.selected_tokens(sels[i], ctxs[i], 4)
+        o_o, l_o = orc.attend(q[i], k, v, toks, 1.0 / 16)
+        qc.check_attention(o_run[i], l_run[i], o_o, l_o)
 
 
 # --------------------------------------------------------------- errors ---
