@@ -647,11 +647,26 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
     q_seq = torch.arange(B, dtype=torch.int32, device=dev)
     bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, B, L)
 
-    def dstep():
+    def dstep_sep():
         pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, w_idx=w)
+
+    ms_sep, _, g = time_graph(torch, dstep_sep, max(10, steps // 2), warmup)
+    del g
+    ref = [x.clone() for x in (bufs.sel, bufs.n_sel, bufs.o, bufs.o_bf16, bufs.lse)]
+    for x in (bufs.sel, bufs.o, bufs.o_bf16, bufs.lse):
+        x.zero_()
+
+    # the step as one qsa_decode_layer_latent call (the headline when its
+    # results are the separate calls' bit for bit)
+    def dstep():
+        pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, w_idx=w,
+                              fused=True)
 
     ms, _, g = time_graph(torch, dstep, max(10, steps // 2), warmup)
     del g
+    same = all(bool(torch.equal(a, b)) for a, b in zip(ref, (bufs.sel, bufs.n_sel, bufs.o, bufs.o_bf16, bufs.lse)))
+    if not same:
+        raise RuntimeError("shared-latent decode: the one-call layer's results differ from the separate calls'")
     reps = max(10, steps // 5)
     t_sc = time_launches(torch, lambda: pkg.qsa_index_scores(pkg.SEL_B, q_ctx, L, q_idx, keys, bufs.scores,
                                                              q_seq=q_seq, w_idx=w), reps)
@@ -663,10 +678,13 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
     step_bytes = B * bm.mla_decode_unit_bytes(L)
     out["decode"] = dict(workload=f"decode batch {B}, context {L}, one layer", steps_s=round(1e3 / ms, 1),
                          ms_per_step=round(ms, 5), hbm_gbs=round(step_bytes / (ms * 1e-3) / 1e9, 1),
-                         step_bytes=step_bytes, n_split=bufs.n_split,
-                         breakdown_us={"scores": round(t_sc * 1e3, 2), "topk": round(t_tk * 1e3, 2),
-                                       "attend": round(t_at * 1e3, 2)})
-    log(f"mla decode: {ms:.4f} ms/step")
+                         step_bytes=step_bytes, n_split=bufs.n_split, schedule="one qsa_decode_layer_latent call",
+                         separate_calls=dict(ms_per_step=round(ms_sep, 5), steps_s=round(1e3 / ms_sep, 1),
+                                             hbm_gbs=round(step_bytes / (ms_sep * 1e-3) / 1e9, 1),
+                                             breakdown_us={"scores": round(t_sc * 1e3, 2),
+                                                           "topk": round(t_tk * 1e3, 2),
+                                                           "attend": round(t_at * 1e3, 2)}))
+    log(f"mla decode: {ms:.4f} ms/step one call, {ms_sep:.4f} separate calls")
     # the same step over FP8 sparse-MLA rows (656 bytes per token)
     rows8 = torch.empty(B, L, 656, dtype=torch.uint8, device=dev)
     pkg.qsa_quantize_latent(lat, rows8)

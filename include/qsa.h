@@ -426,6 +426,41 @@ qsa_status qsa_decode_layer_noalloc(const qsa_sel_cfg* sel_cfg, const qsa_attn_c
                                     int32_t* sel, int32_t* n_sel, int32_t n_split, float* o_out,
                                     qsa_bf16* o_out_bf16, float* lse_out, qsa_stream_t stream);
 
+/* ------------------------------------ A2 + A3 + A4 + A5, shared latent ----
+ * qsa_decode_layer_latent: one decode layer of the token-level indexer over
+ * the shared 576-wide latent: exactly what qsa_index_scores, then
+ * qsa_topk_blocks, then qsa_sparse_decode with n_split parts, then
+ * qsa_lse_merge of those parts compute ("GLM-5.3 最適化 第2部", section
+ * "PCP": every earlier token is scored by the 4-head ReLU-weighted indexer
+ * and the best topk tokens feed the sparse MLA; section "DCP": the parts
+ * are merged by log-sum-exp). Three launches: the scan, which also keeps
+ * each 512-token chunk's 32 best tokens and the best one it left out; one
+ * work-group per (query, split) that selects the query's exact top-k itself
+ * (from the chunk lists, or from the scores when the lists cannot show it
+ * exact) and attends its part; the merge.
+ * Block 1, idx_dim 64, idx_heads 4 (bf16 or FP8 token keys), topk <= 2048;
+ * hq 64, hkv 1, dk 576, dv 512 with bf16 latent rows; other configurations
+ * return QSA_ERR_UNSUPPORTED. nq <= 65535.
+ *   q_seq, q_ctx, q_idx, w_idx, keys, keys_seq_stride: as qsa_index_scores
+ *          (w_idx required).
+ *   scores, ld_scores (>= max_ctx): written as qsa_index_scores writes them.
+ *   sel, n_sel: written as qsa_topk_blocks writes them.
+ *   q, kv, n_split: as qsa_sparse_decode (1 <= n_split <= 256).
+ *   o_out, o_out_bf16, lse_out: as qsa_decode_layer (at least one given).
+ *   ws (device) at least qsa_decode_layer_latent_workspace_bytes(...) bytes,
+ *      16-byte aligned, any contents (the call keeps no state in it between
+ *      calls); calls sharing a workspace must not overlap. */
+qsa_status qsa_decode_layer_latent(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                   const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                                   const qsa_bf16* q_idx, const float* w_idx, const void* keys,
+                                   int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv,
+                                   float* scores, int64_t ld_scores, int32_t* sel, int32_t* n_sel,
+                                   int32_t n_split, float* o_out, qsa_bf16* o_out_bf16, float* lse_out,
+                                   void* ws, size_t ws_bytes, qsa_stream_t stream);
+
+size_t qsa_decode_layer_latent_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
+                                               int32_t nq, int32_t max_ctx, int32_t n_split);
+
 /* ------------------------------------------- A4 with an HBM row cache ----
  * For K/V rows kept in host memory (pinned, read zero-copy): a direct-mapped
  * cache of rows in device memory that later decode steps read instead of

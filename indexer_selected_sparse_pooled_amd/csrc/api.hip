@@ -728,6 +728,76 @@ qsa_status qsa_decode_layer_noalloc(const qsa_sel_cfg* sel_cfg, const qsa_attn_c
                            nullptr, 0, true, stream);
 }
 
+size_t qsa_decode_layer_latent_workspace_bytes(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
+                                               int32_t nq, int32_t max_ctx, int32_t n_split) {
+  if (!sel_cfg || !attn_cfg || nq <= 0 || max_ctx < 0 || n_split < 1 || attn_cfg->hq <= 0 || attn_cfg->dv <= 0)
+    return 0;
+  return qsa::plan_decode_layer_b(nq, max_ctx, attn_cfg->hq, attn_cfg->dv, n_split).ws_bytes;
+}
+
+qsa_status qsa_decode_layer_latent(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
+                                   const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
+                                   const qsa_bf16* q_idx, const float* w_idx, const void* keys,
+                                   int64_t keys_seq_stride, const qsa_bf16* q, const qsa_kv* kv, float* scores,
+                                   int64_t ld_scores, int32_t* sel, int32_t* n_sel, int32_t n_split, float* o_out,
+                                   qsa_bf16* o_out_bf16, float* lse_out, void* ws, size_t ws_bytes,
+                                   qsa_stream_t stream) {
+  const char* fn = "qsa_decode_layer_latent";
+  qsa_status st = check_sel_cfg(sel_cfg);
+  if (st != QSA_OK) return st;
+  if (sel_cfg->block != 1 || sel_cfg->idx_dim != 64 || sel_cfg->idx_heads != 4)
+    return fail(QSA_ERR_UNSUPPORTED, "%s: only the token-level indexer (block 1, 4 heads of 64 dims)", fn);
+  if (sel_cfg->topk > 2048) return fail(QSA_ERR_UNSUPPORTED, "%s: topk %d > 2048", fn, sel_cfg->topk);
+  st = check_attn_inputs(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel);
+  if (st != QSA_OK) return st;
+  if (!(attn_cfg->hq == 64 && attn_cfg->hkv == 1 && attn_cfg->dk == 576 && attn_cfg->dv == 512))
+    return fail(QSA_ERR_UNSUPPORTED, "%s: only the 576-wide shared latent (hq 64, hkv 1, dk 576, dv 512)", fn);
+  if (kv->format != QSA_KV_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s: bf16 latent rows only", fn);
+  if (n_split < 1 || n_split > 256) return fail(QSA_ERR_ARG, "n_split %d not in [1, 256]", n_split);
+  if (nq == 0) return QSA_OK;
+  if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
+  if (!q_idx || !w_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!o_out && !o_out_bf16 && !lse_out) return fail(QSA_ERR_ARG, "no output requested");
+  if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
+  if ((o_out && !aligned16(o_out)) || (o_out_bf16 && !aligned16(o_out_bf16)))
+    return fail(QSA_ERR_ARG, "o_out and o_out_bf16 must be 16-byte aligned");
+  const int64_t nmax = int64_t(max_ctx);
+  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx = %lld", (long long)ld_scores, (long long)nmax);
+  st = check_keys(sel_cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
+  if (st != QSA_OK) return st;
+  const qsa::DecodeLayerBPlan plan = qsa::plan_decode_layer_b(nq, max_ctx, attn_cfg->hq, attn_cfg->dv, n_split);
+  if (int64_t(nq) * n_split > 0x7FFFFFFF) return fail(QSA_ERR_UNSUPPORTED, "nq * n_split too large");
+  if (!ws || ws_bytes < plan.ws_bytes)
+    return fail(QSA_ERR_WORKSPACE, "workspace %zu bytes < %zu required", ws_bytes, plan.ws_bytes);
+  if (!aligned16(ws)) return fail(QSA_ERR_ARG, "workspace must be 16-byte aligned");
+  st = check_device();
+  if (st != QSA_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  st = validate_queries(nq, q_seq, q_ctx, max_ctx, s);
+  if (st != QSA_OK) return st;
+  qsa::ScoreArgs sa{};
+  sa.q_seq = q_seq;
+  sa.q_ctx = q_ctx;
+  sa.max_ctx = max_ctx;
+  sa.nq = nq;
+  sa.block = 1;
+  sa.idx_dim = 64;
+  sa.idx_heads = 4;
+  sa.q_idx = q_idx;
+  sa.w_idx = w_idx;
+  sa.keys = keys;
+  sa.keys_ss = keys_seq_stride;
+  sa.key_fp8 = sel_cfg->key_format == QSA_KEYS_FP8;
+  sa.scores = scores;
+  sa.ld = ld_scores;
+  qsa::AttendArgs at = attend_args(sel_cfg, attn_cfg, nq, q_seq, q_ctx, max_ctx, q, kv, sel, n_sel, n_split, 0,
+                                   int64_t(max_ctx), nullptr, nullptr);
+  at.o_out = o_out;
+  at.o_bf16 = o_out_bf16;
+  at.lse_out = lse_out;
+  return finish(qsa::launch_decode_layer_b(sa, at, plan, ws, s), s, fn);
+}
+
 qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                              const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx, const qsa_bf16* q,
                              const qsa_kv* kv, const int32_t* sel, const int32_t* n_sel, int32_t n_split,

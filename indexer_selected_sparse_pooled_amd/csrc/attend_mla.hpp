@@ -242,6 +242,7 @@ __device__ __forceinline__ float rows_sum(float v) {
 struct TList {
   const int* sel;  // the query's selection row (topk entries)
   int topk, ctx, P0, n_list;
+  bool dma_sel = true;  // entries gathered by sel_dma (else already in LDS)
   // token of row j of tile t, from the entries of the tile (clamped into the context)
   __device__ __forceinline__ int tok(const int* ent, int j) const {
     const int b = ent[j];
@@ -260,7 +261,7 @@ struct TLane {
 // DMA of the selection entries of tile t into a slot (wave 0; the entries
 // past the row are clamped to its last one and never used).
 __device__ __forceinline__ void sel_dma(const TLane& tl, const TList& ls, int t, int* slot) {
-  if (tl.wave != 0 || ls.cnt(t) == 0) return;
+  if (!ls.dma_sel || tl.wave != 0 || ls.cnt(t) == 0) return;
   int e = ls.P0 + kTT * t + tl.lane;
   e = e < ls.topk ? e : ls.topk - 1;
   __builtin_amdgcn_global_load_lds(ls.sel + e, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
@@ -398,8 +399,14 @@ __device__ __attribute__((always_inline)) inline void tile_t(
   }
 }
 
-template <bool kCoh>
-__device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
+// kLdsList: the query's ns_lds selected tokens (ascending) are already in
+// LDS at sel_lds (the decode layer's own selection); the part takes its
+// tiles' entries from there instead of gathering them, and ctx_in / seq_in
+// are the query's context and sequence.
+template <bool kCoh, bool kLdsList = false>
+__device__ __attribute__((always_inline)) inline void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh,
+                                                                    const int* sel_lds = nullptr, int ns_lds = 0,
+                                                                    int ctx_in = -1, int seq_in = -1) {
   TLane tl;
   const int tid = threadIdx.x;
   tl.wave = tid >> 6;
@@ -408,8 +415,8 @@ __device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
   tl.kq = tl.lane >> 4;
   const int wave = tl.wave, r = tl.r, kq = tl.kq;
 
-  const int seq = a.q_seq ? a.q_seq[i] : 0;
-  const int ctx = clamp_ctx(a.q_ctx[i], a.max_ctx);
+  const int seq = kLdsList ? seq_in : (a.q_seq ? a.q_seq[i] : 0);
+  const int ctx = kLdsList ? ctx_in : clamp_ctx(a.q_ctx[i], a.max_ctx);
   // block 1 (the host sends other block sizes to attend_part): the list is
   // the ns selected tokens, no trailing ones
   att::List<kCoh> lv;
@@ -417,9 +424,13 @@ __device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
   lv.block = 1;
   lv.nblk = ctx;
   const int ns_max = ctx < a.topk ? ctx : a.topk;
-  const int ns = kCoh ? ns_max : a.n_sel[i];
+  const int ns = kLdsList ? ns_lds : (kCoh ? ns_max : a.n_sel[i]);
   lv.ns = ns < 0 ? 0 : (ns > ns_max ? ns_max : ns);
   lv.L = lv.ns;
+  if constexpr (kLdsList) {
+    lv.cache = (att::LdsIntPtr)sel_lds;
+    lv.has_cache = true;
+  }
   int P0_, P1_;
   att::part_range<kCoh, kNTPART>(lv, a, split, ctx, sh.cnt, P0_, P1_);
   TList ls;
@@ -430,6 +441,7 @@ __device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
   // from it) in scalar registers
   ls.P0 = __builtin_amdgcn_readfirstlane(P0_);
   ls.n_list = __builtin_amdgcn_readfirstlane(P1_) - ls.P0;
+  ls.dma_sel = !kLdsList;
   const int n_tiles = (ls.n_list + kTT - 1) / kTT;
 
   const uint16_t* kvbase = a.k + int64_t(seq) * a.seq_stride;
@@ -447,19 +459,32 @@ __device__ void attend_part_t(const AttendArgs& a, int split, int i, LdsT& sh) {
 #pragma unroll
   for (int nt = 0; nt < kDV / 16; nt++) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the entries of tiles 0 and 1, then tile 0's rows
-  sel_dma(tl, ls, 0, sh.selbuf[0]);
-  sel_dma(tl, ls, 1, sh.selbuf[1]);
-  wait_memory();
-  pipe_barrier();
-  rows_dma(tl, ls, 0, sh.selbuf[0], sh.kv[0], kvbase, a.tok_stride);
-  for (int t = 0; t < n_tiles; t++) {
-    // tile t's rows (this wave's share) and the entries of tile t + 1: all
-    // this wave has in flight
+  if constexpr (kLdsList) {
+    // the entries are in LDS: tile 0's rows at once; tile t + 1's entries
+    // start at list position P0 + kTT (t + 1)
+    const int* ents = sel_lds + ls.P0;
+    rows_dma(tl, ls, 0, ents, sh.kv[0], kvbase, a.tok_stride);
+    for (int t = 0; t < n_tiles; t++) {
+      wait_memory();
+      pipe_barrier();  // every wave's share of tile t has landed; every wave is done with tile t - 1
+      tile_t(tl, ls, t, sh.kv[t & 1], sh.kv[(t + 1) & 1], ents + kTT * (t + 1), sh.selbuf[t & 1], kvbase,
+             a.tok_stride, sl2, qa, m, l, o);
+    }
+  } else {
+    // the entries of tiles 0 and 1, then tile 0's rows
+    sel_dma(tl, ls, 0, sh.selbuf[0]);
+    sel_dma(tl, ls, 1, sh.selbuf[1]);
     wait_memory();
-    pipe_barrier();  // every wave's share of tile t has landed; every wave is done with tile t - 1
-    tile_t(tl, ls, t, sh.kv[t & 1], sh.kv[(t + 1) & 1], sh.selbuf[(t + 1) & 1], sh.selbuf[t & 1], kvbase,
-           a.tok_stride, sl2, qa, m, l, o);
+    pipe_barrier();
+    rows_dma(tl, ls, 0, sh.selbuf[0], sh.kv[0], kvbase, a.tok_stride);
+    for (int t = 0; t < n_tiles; t++) {
+      // tile t's rows (this wave's share) and the entries of tile t + 1: all
+      // this wave has in flight
+      wait_memory();
+      pipe_barrier();  // every wave's share of tile t has landed; every wave is done with tile t - 1
+      tile_t(tl, ls, t, sh.kv[t & 1], sh.kv[(t + 1) & 1], sh.selbuf[(t + 1) & 1], sh.selbuf[t & 1], kvbase,
+             a.tok_stride, sl2, qa, m, l, o);
+    }
   }
 
   // normalise and write: lane (kq, r) holds O^T[dim 16nt + 4kq + e][head 16w + r]

@@ -75,17 +75,18 @@ constexpr int kChunkKeep = 16;  // at most, per chunk (a.keep)
 constexpr int kRegR = 16;       // union / raw entries per thread in the final select
 constexpr int kRegCap = kNT * kRegR;
 
-// One chunk's list step: every wave's candidates and bound.
+// One chunk's list step: every wave's candidates (at most WK) and bound.
+template <int WK = kWaveKeep>
 struct ListLds {
-  uint32_t wkey[4 * kWaveKeep];
-  int widx[4 * kWaveKeep];
+  uint32_t wkey[4 * WK];
+  int widx[4 * WK];
   uint64_t wbound[4];
 };
 
 struct FinalLds {
   RegSelLds<kNT> rs;
   StreamLds st;
-  ListLds lst;
+  ListLds<> lst;
   int last;
 };
 
@@ -200,7 +201,7 @@ __device__ __forceinline__ void load_union(const IndexTopkArgs& a, int i, int u,
   }
 }
 
-// The topk best of the keys in registers (element j = tid * kRegR + r, in
+// The topk best of the keys in registers (element j = tid * R + r, in
 // block order; 0 = empty): emit(position, block) with position in [0, topk)
 // for each selected key, positions ascending in element order, and
 // emit(-1, block) for every other key of the thread (emit must ignore or
@@ -212,21 +213,32 @@ __device__ __forceinline__ void load_union(const IndexTopkArgs& a, int i, int u,
 // threshold (packed in one word); the bound check rides on the same
 // exchange: a bound key above the threshold fails at once, and only a bound
 // key equal to it needs the topk-th's block.
-template <class Emit>
-__device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const uint32_t (&ukey)[kRegR],
-                                 const int (&uidx)[kRegR], uint64_t my_bound, FinalLds& sh, Emit emit) {
+// What select_registers found when it returns false on a tie (no bound key
+// above the threshold, but one equal to it that ranks above the topk-th):
+// the threshold key and need are then the whole row's, and every key above
+// the threshold is in the union (n_gt of them).
+struct RegSelOut {
+  bool tie_fail;
+  uint32_t kstar;
+  int need, n_gt;
+};
+
+template <int R, class Emit>
+__device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const uint32_t (&ukey)[R],
+                                 const int (&uidx)[R], uint64_t my_bound, FinalLds& sh, Emit emit, RegSelOut& out) {
   constexpr int NW = kNT / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t kstar;
   int need;
-  regsel_threshold<kNT, kRegR>(ukey, a.topk, sh.rs, kstar, need);
+  regsel_threshold<kNT, R>(ukey, a.topk, sh.rs, kstar, need);
   int g = 0, e = 0;
 #pragma unroll
-  for (int r = 0; r < kRegR; r++) {
+  for (int r = 0; r < R; r++) {
     g += ukey[r] > kstar ? 1 : 0;
     e += (ukey[r] == kstar && ukey[r] != 0u) ? 1 : 0;
   }
-  const int v = g | (e << 16);  // at most kRegCap each: no carry between the halves
+  static_assert(kNT * R < 65536, "two 16-bit counts in one word");
+  const int v = g | (e << 16);  // at most kNT * R each: no carry between the halves
   const int incl = wave_incl_sum(v);
   const uint32_t bkey = uint32_t(my_bound >> 32);
   const uint64_t bfail = __ballot(union_mode && bkey > kstar);
@@ -234,30 +246,38 @@ __device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const 
   if (lane == 63) sh.rs.wg[wave] = incl;
   if (lane == 0) sh.rs.we[wave] = (bfail ? 1 : 0) | (btie ? 2 : 0);
   __syncthreads();
-  int off = incl - v, flags = 0;
+  int off = incl - v, flags = 0, tot = 0;
 #pragma unroll
   for (int w = 0; w < NW; w++) {
     if (w < wave) off += sh.rs.wg[w];
+    tot += sh.rs.wg[w];
     flags |= sh.rs.we[w];
   }
+  out.tie_fail = false;
   if (flags & 1) return false;
   const int gb0 = off & 0xFFFF, eb0 = off >> 16;
   if (flags & 2) {  // a bound ties with the threshold key: compare blocks
     int eb = eb0;
 #pragma unroll
-    for (int r = 0; r < kRegR; r++) {
+    for (int r = 0; r < R; r++) {
       const bool eq = ukey[r] == kstar && ukey[r] != 0u;
       if (eq && eb == need - 1) sh.rs.tau_val = uidx[r];
       eb += eq ? 1 : 0;
     }
     __syncthreads();
     const uint64_t tau = rank64(kstar, sh.rs.tau_val);
-    if (__syncthreads_or(my_bound > tau)) return false;
+    if (__syncthreads_or(my_bound > tau)) {
+      out.tie_fail = true;
+      out.kstar = kstar;
+      out.need = need;
+      out.n_gt = tot & 0xFFFF;
+      return false;
+    }
   }
   // keys above kstar, then the first `need` keys equal to it, in element order
   int gb = gb0, eb = eb0;
 #pragma unroll
-  for (int r = 0; r < kRegR; r++) {
+  for (int r = 0; r < R; r++) {
     const bool gt = ukey[r] > kstar;
     const bool eq = ukey[r] == kstar && ukey[r] != 0u;
     const int p = gt ? gb + (eb < need ? eb : need) : ((eq && eb < need) ? gb + eb : -1);
@@ -266,6 +286,13 @@ __device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const 
     eb += eq ? 1 : 0;
   }
   return true;
+}
+
+template <int R = kRegR, class Emit>
+__device__ __forceinline__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const uint32_t (&ukey)[R],
+                                                 const int (&uidx)[R], uint64_t my_bound, FinalLds& sh, Emit emit) {
+  RegSelOut out;
+  return select_registers<R>(a, union_mode, ukey, uidx, my_bound, sh, emit, out);
 }
 
 // The exact top-k of query i (n > topk candidates), once every chunk of the
@@ -317,24 +344,29 @@ __device__ void final_select(const IndexTopkArgs& a, int i, int n, FinalLds& sh,
   select_streamed(sc, n, a.topk, sh, emit);
 }
 
-// The list of one chunk (union mode): every wave keeps its 8 best keys (a
-// register threshold search on their top 16 bits, no barrier) and the best
-// block it leaves out; wave 0 then keeps the chunk's `keep` best of the 32
-// and writes them (ascending block order, 0 past the kept ones) with the
-// chunk's bound: the best block it left out, at full precision. key[t] holds
-// the order key of block w0 + 64 t + lane (0 past n). One barrier; the caller
-// keeps L untouched until every wave has passed the next one. kCoh: the list
-// is read by another work-group of the same launch.
-template <int TPW, bool kCoh>
+// The list of one chunk (union mode): every wave keeps its a.wkeep (<= WK)
+// best keys (a register threshold search on their top 16 bits, no barrier)
+// and the best block it leaves out; wave 0 then keeps the chunk's `keep`
+// best of the 4 WK and writes them (ascending block order, 0 past the kept
+// ones) with the chunk's bound: the best block it left out, at full
+// precision. key[t] holds the order key of block w0 + 64 t + lane (0 past
+// n). One barrier; the caller keeps L untouched until every wave has passed
+// the next one. kCoh: the list is read by another work-group of the same
+// launch. kPairMajor: the query's lists are stored pair-major (entry
+// (chunk c, slot s) at ((s / 2) * n_chunks + c) * 2 + s % 2 of the query's
+// region), so that thread c loading list c's pairs reads contiguously
+// across lanes; otherwise list by list.
+template <int TPW, bool kCoh, int WK = kWaveKeep, bool kPairMajor = false>
 __device__ void chunk_list(const IndexTopkArgs& a, int i, int chunk, int n, int64_t w0, const uint32_t (&key)[TPW],
-                           ListLds& L) {
+                           ListLds<WK>& L) {
+  static_assert(4 * WK <= 64, "wave 0 holds the 4 WK candidates one per lane");
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int keep = a.keep, wkeep = a.wkeep;
   const int64_t m64 = int64_t(n) - w0;
   const int m = m64 <= 0 ? 0 : (m64 >= TPW * 64 ? TPW * 64 : int(m64));
-  if (lane < kWaveKeep) {
-    L.wkey[wave * kWaveKeep + lane] = 0u;
-    L.widx[wave * kWaveKeep + lane] = -1;
+  if (lane < WK) {
+    L.wkey[wave * WK + lane] = 0u;
+    L.widx[wave * WK + lane] = -1;
   }
   uint32_t kh[TPW];  // top 16 bits (nonzero for every nonzero key)
 #pragma unroll
@@ -343,16 +375,16 @@ __device__ void chunk_list(const IndexTopkArgs& a, int i, int chunk, int n, int6
   int need = wkeep;
   if (m > wkeep) wave_select<TPW, 16>(kh, wkeep, kstar, need);
   wave_compact<TPW>(kh, kstar, need, [&](int pos, int r) {
-    L.wkey[wave * kWaveKeep + pos] = key[r];
-    L.widx[wave * kWaveKeep + pos] = int(w0) + 64 * r + lane;
+    L.wkey[wave * WK + pos] = key[r];
+    L.widx[wave * WK + pos] = int(w0) + 64 * r + lane;
   });
   const uint64_t wb = wave_best_excluded<TPW>(kh, key, kstar, need, [&](int j) { return int(w0) + j; });
   if (lane == 0) L.wbound[wave] = wb;
   __syncthreads();
   if (wave == 0) {
-    const uint32_t k1[1] = {lane < 4 * kWaveKeep ? L.wkey[lane] : 0u};
+    const uint32_t k1[1] = {lane < 4 * WK ? L.wkey[lane] : 0u};
     const uint32_t h1[1] = {k1[0] >> 16};
-    const int i1 = lane < 4 * kWaveKeep ? L.widx[lane] : -1;
+    const int i1 = lane < 4 * WK ? L.widx[lane] : -1;
     const int valid = __popcll(__ballot(k1[0] != 0u));
     uint64_t bound = 0ull;
 #pragma unroll
@@ -360,14 +392,18 @@ __device__ void chunk_list(const IndexTopkArgs& a, int i, int chunk, int n, int6
     uint32_t ks = 0u;
     int nd = keep;
     if (valid > keep) wave_select<1, 16>(h1, keep, ks, nd);
-    const size_t base = (size_t(i) * a.n_chunks + chunk) * keep;
+    const size_t qbase = size_t(i) * a.n_chunks * keep;
+    auto slot = [&](int pos) -> size_t {
+      return kPairMajor ? qbase + (size_t(pos >> 1) * a.n_chunks + chunk) * 2 + (pos & 1)
+                        : qbase + size_t(chunk) * keep + pos;
+    };
     // kept entries (key << 32 | block) go to their list position; the
     // positions past the kept count are cleared (0 = empty)
     wave_compact<1>(h1, ks, nd, [&](int pos, int) {
-      put<kCoh>(a.list + base + pos, (uint64_t(k1[0]) << 32) | uint32_t(i1));
+      put<kCoh>(a.list + slot(pos), (uint64_t(k1[0]) << 32) | uint32_t(i1));
     });
     const int nkept = valid < keep ? valid : keep;
-    if (lane >= nkept && lane < keep) put<kCoh>(a.list + base + lane, 0ull);
+    if (lane >= nkept && lane < keep) put<kCoh>(a.list + slot(lane), 0ull);
     const uint64_t b = wave_best_excluded<1>(h1, k1, ks, nd, [&](int) { return i1; });
     bound = b > bound ? b : bound;
     if (lane == 0) put<kCoh>(a.list_bound + size_t(i) * a.n_chunks + chunk, bound);

@@ -228,6 +228,22 @@ DecodeLayerPlan plan_decode_layer(int nq, int max_ctx, int topk, int hq, int hkv
 hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLayerPlan& p, void* ws,
                                hipStream_t s, bool clear_control = false);
 
+// One decode layer of the shared-latent variant (token-level indexer, top-k
+// of single tokens, 64 heads over one latent row): scan with chunk lists,
+// then attention whose work-groups select their query's tokens themselves,
+// then the merge (three launches).
+struct DecodeLayerBPlan {
+  int n_chunks;  // 512-key chunks per query at max_ctx
+  size_t off_list, off_bound, off_o, off_lse, ws_bytes;
+};
+constexpr int kDecodeBChunk = 512;     // keys per chunk
+constexpr int kDecodeBKeep = 32;       // candidates kept per chunk
+constexpr int kDecodeBMaxChunks = 256;  // most chunks per query whose lists the select holds (one per thread)
+DecodeLayerBPlan plan_decode_layer_b(int nq, int max_ctx, int hq, int dv, int n_split);
+// sa: the scan's arguments (scores, q_idx, w_idx, keys ...); att: the
+// attention's (sel, n_sel, the outputs) without the workspace views.
+hipError_t launch_decode_layer_b(ScoreArgs sa, AttendArgs att, const DecodeLayerBPlan& p, void* ws, hipStream_t s);
+
 hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, int64_t o_ps,
                         const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,
                         float* lse_out, hipStream_t s);

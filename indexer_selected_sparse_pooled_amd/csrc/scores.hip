@@ -14,6 +14,7 @@
 #include "common.hpp"
 #include "fp8.hpp"
 #include "kernels.hpp"
+#include "scores_b.hpp"
 #include "select.hpp"
 
 namespace qsa {
@@ -113,86 +114,22 @@ __global__ __launch_bounds__(256) void scores_gemv_a_fp8(ScoreArgs a) {
   }
 }
 
-// Variant B decode: 64-d token keys, 4 indexer heads, ReLU-weighted sum.
-// A wave owns 128 consecutive keys (16 KiB); lane (g = lane/8, c = lane%8)
-// loads dims [8c, 8c+8) of keys 8k+g; after the butterfly over the 8 lanes
-// of a group it holds the 4 head dots of keys 8(2c+j)+g, j = 0, 1.
-// kFp8: FP8 token keys (pages of 64 keys of 64 codes + scales): each lane
-// reads its 8 codes, converts them to bf16 exactly, and the key's scale
-// multiplies the final score (ReLU commutes with a non-negative scale).
+// Variant B decode: one wave per 128 consecutive keys (scores_b.hpp).
 template <bool kFp8>
 __global__ __launch_bounds__(256) void scores_gemv_b(ScoreArgs a) {
   const int i = blockIdx.y;
   const int seq = a.q_seq ? a.q_seq[i] : 0;
   const int64_t n = clamp_ctx(a.q_ctx[i], a.max_ctx) / a.block;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 3, c = lane & 7;
   const int64_t tile0 = (int64_t(blockIdx.x) * 4 + wave) * 128;
   if (tile0 >= n) return;
-  u32x4 qv[4];
-  float w[4];
-#pragma unroll
-  for (int h = 0; h < 4; h++) {
-    qv[h] = ld16(a.q_idx + (int64_t(i) * 4 + h) * 64 + 8 * c);
-    w[h] = a.w_idx[int64_t(i) * 4 + h];
-  }
-  const uint16_t* kb = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss;
-  const uint8_t* kb8 = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
-  float p[16][4];
-#pragma unroll
-  for (int k = 0; k < 16; k++) {
-    const int64_t tok = tile0 + 8 * k + g;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if constexpr (kFp8) {
-      if (tok < n)
-        v = __builtin_bit_cast(u32x4, e4m3x8_bf16(*reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(tok, 64) + 8 * c)));
-    } else {
-      if (tok < n) v = ld16_nt(kb + tok * 64 + 8 * c);
-    }
-#pragma unroll
-    for (int h = 0; h < 4; h++) p[k][h] = dot8(v, qv[h]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const bool up = c & 4;
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      const float keep = up ? p[j + 8][h] : p[j][h];
-      const float send = up ? p[j][h] : p[j + 8][h];
-      p[j][h] = keep + __shfl_xor(send, 4);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 4; j++) {
-    const bool up = c & 2;
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      const float keep = up ? p[j + 4][h] : p[j][h];
-      const float send = up ? p[j][h] : p[j + 4][h];
-      p[j][h] = keep + __shfl_xor(send, 2);
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < 2; j++) {
-    const bool up = c & 1;
-#pragma unroll
-    for (int h = 0; h < 4; h++) {
-      const float keep = up ? p[j + 2][h] : p[j][h];
-      const float send = up ? p[j][h] : p[j + 2][h];
-      p[j][h] = keep + __shfl_xor(send, 1);
-    }
-  }
+  float s[2];
+  sb::tile_scores<kFp8>(a, i, seq, n, tile0, s);
   float* out = a.scores + int64_t(i) * a.ld;
 #pragma unroll
   for (int j = 0; j < 2; j++) {
-    const int64_t tok = tile0 + 8 * (2 * c + j) + g;
-    float s = 0.f;
-#pragma unroll
-    for (int h = 0; h < 4; h++) s += w[h] * fmaxf(p[j][h], 0.f);
-    if constexpr (kFp8) {
-      if (tok < n) s *= *reinterpret_cast<const float*>(kb8 + fp8_scale_off(tok, 64));
-    }
-    if (tok < n) out[tok] = s;
+    const int64_t tok = sb::tile_token(tile0, lane, j);
+    if (tok < n) out[tok] = s[j];
   }
 }
 

@@ -120,6 +120,23 @@ __device__ __forceinline__ uint64_t wave_best_excluded(const uint32_t (&key)[R],
 // ballot per bit), instead of more histogram passes over every key.
 constexpr int kRegSelCand = 64;
 
+// LDS histogram increment of bin b (< 256) for the lanes with `in`: the
+// lanes that share the first such lane's bin add their count in one atomic
+// (scores cluster, and identical keys all fall in one bin, so one bin often
+// takes most of a wave and would otherwise serialize on one address); every
+// other lane adds to its own bin, or to its dummy bin 256 + lane, so the
+// instruction carries no branch.
+__device__ __forceinline__ void hist_add(uint32_t* h, bool in, uint32_t b) {
+  const int lane = threadIdx.x & 63;
+  const uint64_t act = __ballot(in);
+  const int first = act ? int(__ffsll(static_cast<unsigned long long>(act))) - 1 : 0;
+  const uint32_t b0 = uint32_t(__builtin_amdgcn_readlane(int(b), first));
+  const uint64_t same = __ballot(in && b == b0);
+  const bool lead = in && lane == first;
+  const bool own = lead || (in && b != b0);
+  atomicAdd(&h[own ? b : 256u + lane], lead ? uint32_t(__popcll(same)) : 1u);
+}
+
 // Histogram bins 256 + lane and counters / slots past the candidates are
 // per-lane dummies: keys that take no part in a pass still issue their LDS
 // atomic or store (to a lane of their own, so no two lanes of one
@@ -190,7 +207,7 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
 #pragma unroll
     for (int r = 0; r < R; r++) {
       const bool in = key[r] != 0u && (key[r] & mask) == prefix;
-      atomicAdd(&h[in ? (key[r] >> shift) & dmask : 256u + lane], 1u);
+      hist_add(h, in, (key[r] >> shift) & dmask);
     }
     __syncthreads();
     // every wave finds the digit (same result everywhere): lane holds the

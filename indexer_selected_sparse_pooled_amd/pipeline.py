@@ -1,8 +1,8 @@
 """The hot path as a chain of libqsa calls.
 
 A decode layer is A2 -> A3 -> A4 -> A5 (scores, top-k, split attention,
-merge): one qsa_decode_layer call for the pooled-block variant, or the
-separate calls; a prefill chunk is A2 -> A3 -> A6 per history tile -> A5. Buffers
+merge): one qsa_decode_layer call for the pooled-block variant, one
+qsa_decode_layer_latent call for the shared latent, or the separate calls; a prefill chunk is A2 -> A3 -> A6 per history tile -> A5. Buffers
 are allocated once with torch and reused; every step runs in libqsa's
 kernels, enqueued on one stream with no host synchronisation, so a whole
 layer or chunk can be captured in a HIP graph.
@@ -30,6 +30,7 @@ class DecodeBuffers:
     o_bf16: torch.Tensor    # [nq, hq, dv] bf16
     lse: torch.Tensor       # [nq, hq] fp32
     n_split: int
+    latent_ws: torch.Tensor = None  # workspace of qsa_decode_layer_latent (or None)
 
 
 def default_n_split(nq: int, hkv: int, budget_tokens: int) -> int:
@@ -55,6 +56,13 @@ def fused_layer(sel_cfg, attn_cfg) -> bool:
     return fused_select(sel_cfg) and (attn_cfg.hq, attn_cfg.hkv, attn_cfg.dk, attn_cfg.dv) == (16, 2, 256, 256)
 
 
+def latent_layer(sel_cfg, attn_cfg) -> bool:
+    """Whether qsa_decode_layer_latent covers this configuration (with bf16
+    latent rows): the token-level 4-head indexer over the shared latent."""
+    return ((sel_cfg.block, sel_cfg.idx_dim, sel_cfg.idx_heads) == (1, 64, 4) and sel_cfg.topk <= 2048
+            and (attn_cfg.hq, attn_cfg.hkv, attn_cfg.dk, attn_cfg.dv) == (64, 1, 576, 512))
+
+
 def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") -> DecodeBuffers:
     nmax = max(1, max_ctx // sel_cfg.block)
     if n_split is None:
@@ -74,20 +82,27 @@ def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") 
         o_bf16=torch.empty(nq, attn_cfg.hq, attn_cfg.dv, dtype=torch.bfloat16, device=device),
         lse=torch.empty(nq, attn_cfg.hq, **f32),
         n_split=n_split,
+        latent_ws=(qsa.decode_layer_latent_workspace(sel_cfg, attn_cfg, nq, max_ctx, n_split, device)
+                   if latent_layer(sel_cfg, attn_cfg) else None),
     )
 
 
 def decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: DecodeBuffers,
                  q_seq=None, w_idx=None, stream=None, fused=False) -> None:
     """One decode layer for nq queries (one per sequence): results in bufs.o / o_bf16 / lse.
-    fused=True issues the layer as one qsa_decode_layer call (same results;
-    two launches instead of three, and the attention work-groups select
-    their query's blocks themselves, so no selection is written and re-read
-    in between)."""
-    if fused and bufs.layer_ws is not None and w_idx is None:
+    fused=True issues the layer as one qsa_decode_layer call, or one
+    qsa_decode_layer_latent call for the shared latent with bf16 rows (same
+    results; the attention work-groups select their query's tokens
+    themselves, so no selection is re-read in between)."""
+    if fused and bufs.layer_ws is not None and w_idx is None and fused_layer(sel_cfg, attn_cfg):
         qsa.qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs.scores, bufs.sel,
                              bufs.n_sel, bufs.n_split, bufs.layer_ws, o_out=bufs.o, o_out_bf16=bufs.o_bf16,
                              lse_out=bufs.lse, q_seq=q_seq, stream=stream)
+        return
+    if fused and bufs.latent_ws is not None and w_idx is not None and kv.format == qsa.KV_BF16:
+        qsa.qsa_decode_layer_latent(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, w_idx, keys, q, kv, bufs.scores,
+                                    bufs.sel, bufs.n_sel, bufs.n_split, bufs.latent_ws, o_out=bufs.o,
+                                    o_out_bf16=bufs.o_bf16, lse_out=bufs.lse, q_seq=q_seq, stream=stream)
         return
     if bufs.itk_ws is not None and w_idx is None:
         qsa.qsa_index_topk(sel_cfg, q_ctx, max_ctx, q_idx, keys, bufs.scores, bufs.sel, bufs.n_sel, bufs.itk_ws,

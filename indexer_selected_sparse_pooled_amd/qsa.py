@@ -82,6 +82,9 @@ _SIGS = {
     "qsa_decode_layer": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp, _i32,
                          _vp, _vp, _vp, _vp, _sz, _vp],
     "qsa_decode_layer_workspace_bytes": [_vp, _vp, _i32, _i32, _i32],
+    "qsa_decode_layer_latent": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
+                                _i32, _vp, _vp, _vp, _vp, _sz, _vp],
+    "qsa_decode_layer_latent_workspace_bytes": [_vp, _vp, _i32, _i32, _i32],
     "qsa_decode_layer_noalloc": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _i64, _vp, _vp, _vp, _i64, _vp, _vp,
                                  _i32, _vp, _vp, _vp, _vp],
     "qsa_sparse_decode": [_vp, _vp, _i32, _vp, _vp, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _vp, _vp],
@@ -99,7 +102,7 @@ _SIGS = {
     "qsa_version": [],
 }
 _RES = {"qsa_topk_workspace_bytes": _sz, "qsa_index_topk_workspace_bytes": _sz, "qsa_index_topk_prefill_workspace_bytes": _sz, "qsa_fp8_keys_bytes": _i64,
-        "qsa_decode_layer_workspace_bytes": _sz,
+        "qsa_decode_layer_workspace_bytes": _sz, "qsa_decode_layer_latent_workspace_bytes": _sz,
         "qsa_row_cache_bytes": _sz, "qsa_decode_cached_plan_bytes": _sz, "qsa_status_string": ctypes.c_char_p,
         "qsa_last_error": ctypes.c_char_p, "qsa_version": _i32}
 EXPORTS = tuple(_SIGS)
@@ -404,6 +407,36 @@ def qsa_decode_layer_noalloc(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, 
     args = _decode_layer_args("qsa_decode_layer_noalloc", sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv,
                               scores, sel, n_sel, n_split, o_out, o_out_bf16, lse_out, q_seq)
     _check("qsa_decode_layer_noalloc", lib().qsa_decode_layer_noalloc(*args, _stream(stream)))
+
+
+def qsa_decode_layer_latent_workspace_bytes(sel_cfg, attn_cfg, nq, max_ctx, n_split) -> int:
+    return int(lib().qsa_decode_layer_latent_workspace_bytes(ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq,
+                                                             max_ctx, n_split))
+
+
+def decode_layer_latent_workspace(sel_cfg, attn_cfg, nq, max_ctx, n_split, device="cuda"):
+    """A workspace tensor for qsa_decode_layer_latent (no state is kept in it
+    between calls)."""
+    n = qsa_decode_layer_latent_workspace_bytes(sel_cfg, attn_cfg, nq, max_ctx, n_split)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def qsa_decode_layer_latent(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, w_idx, keys, q, kv, scores, sel, n_sel,
+                            n_split, ws, o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
+    """One decode layer of the shared-latent variant (three launches):
+    qsa_index_scores, qsa_topk_blocks, qsa_sparse_decode and qsa_lse_merge.
+    q_idx: [nq, 4, 64] bf16; w_idx: [nq, 4] fp32; keys: [n_seq, n_keys, 64]
+    bf16 (or FP8 pages); q: [nq, 64, 576] bf16; kv: bf16 latent rows;
+    scores/sel/n_sel as qsa_index_scores / qsa_topk_blocks write them;
+    outputs as qsa_decode_layer; ws: decode_layer_latent_workspace(...)."""
+    fn = "qsa_decode_layer_latent"
+    args = _decode_layer_args(fn, sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel, n_sel,
+                              n_split, o_out, o_out_bf16, lse_out, q_seq)
+    if w_idx is None or tuple(w_idx.shape) != (q_ctx.shape[0], 4) or not w_idx.is_contiguous():
+        raise ValueError(f"{fn}: w_idx must be a contiguous [nq, 4] tensor")
+    args.insert(7, _dev(w_idx, _F32, "w_idx"))
+    _check(fn, lib().qsa_decode_layer_latent(
+        *args, ctypes.c_void_p(ws.data_ptr()), ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def qsa_kv_append(sel_cfg, attn_cfg, q_pos, k_new, kv, v_new=None, raw_new=None, raw_keys=None, pooled=None,

@@ -142,10 +142,13 @@ def test_mla_prefill_full_size_sampled(Q):
         qc.check_row_with(sel[i], n_sel[i], o[i], lse[i], ob[i], sc, ctx, 1, 2048, attend_ref)
 
 
-def test_mla_decode_full_size(Q):
+@pytest.mark.parametrize("fused", [False, True], ids=["separate_calls", "one_call"])
+def test_mla_decode_full_size(Q, fused):
     """The shared-latent decode step as the benchmark times it: batch 8 at
-    context 131,072, layer 0 of the workload's inputs, one call chain per
-    step in its launch configuration (32 splits). Every query is checked
+    context 131,072, layer 0 of the workload's inputs, in its launch
+    configuration (32 splits): the separate calls, or one
+    qsa_decode_layer_latent call (which selects from the union of its
+    512-token chunk lists). Every query is checked
     against the oracle: the whole score row (131,072 tokens) and the top-2048
     from the oracle's own scores, then the attention over the selected latent
     rows regenerated by index. Query 5's indexer head weights are all
@@ -155,7 +158,7 @@ def test_mla_decode_full_size(Q):
     from qsa_inputs.gpu import fill_normal_bf16
     L, B = 131072, 8
     seed = qi.config_seed(5)
-    _print_case("mla_decode_full", ctx=L, batch=B)
+    _print_case("mla_decode_full", ctx=L, batch=B, fused=fused)
     S = lambda s, kind: qi.stream_id(0, s, kind)
     lat = torch.empty(B, L, 1, 576, dtype=torch.bfloat16, device="cuda")
     keys = torch.empty(B, L, 64, dtype=torch.bfloat16, device="cuda")
@@ -170,11 +173,10 @@ def test_mla_decode_full_size(Q):
     q_ctx, q_seq = qc.i32([L] * B), qc.i32(range(B))
     bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, B, L)
     assert bufs.n_split == 32
+    assert bufs.latent_ws is not None
     pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq,
-                          w_idx=torch.tensor(w_np, device="cuda"))
+                          w_idx=torch.tensor(w_np, device="cuda"), fused=fused)
     torch.cuda.synchronize()
-    if bufs.layer_ws is not None:
-        pkg.check_decode_layer_error(bufs.layer_ws)
     sel, n_sel = bufs.sel.cpu().numpy(), bufs.n_sel.cpu().numpy()
     o, lse, ob = bufs.o.cpu().numpy(), bufs.lse.cpu().numpy(), qc.from_dev_bits(bufs.o_bf16)
     got_sc = bufs.scores.cpu().numpy()

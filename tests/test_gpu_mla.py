@@ -5,7 +5,8 @@ the C ABI, against the oracle.
 
 Cases: attention on given selections with several split counts (full
 attention at ctx <= 2048, one token, an empty context), the decode layer end
-to end (scores, top-2048, attention, merge), and a tiled prefill chunk whose
+to end (scores, top-2048, attention, merge) through the separate calls and
+through one qsa_decode_layer_latent call, and a tiled prefill chunk whose
 result must not depend on the tile size.
 """
 import numpy as np
@@ -94,7 +95,7 @@ def test_mla_decode_layer_end_to_end(Q):
     lat = qc.to_dev(case.latent)
     kv = pkg.make_kv(lat, lat)
     bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, nq, case.cap)
-    assert bufs.layer_ws is None
+    assert bufs.layer_ws is None and bufs.latent_ws is not None
     pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, qc.i32(ctxs), case.cap, qc.to_dev(case.q_idx), qc.to_dev(case.keys),
                           qc.to_dev(case.q), kv, bufs, q_seq=qc.i32(range(nq)),
                           w_idx=torch.tensor(case.w, device="cuda"))
@@ -105,6 +106,55 @@ def test_mla_decode_layer_end_to_end(Q):
         r = case.oracle(i)
         qc.check_row(sel[i], n_sel[i], o[i], lse[i], ob[i], r, ctxs[i], 1, 2048, case.q[i], case.latent[i],
                      case.latent[i], SCALE, dv=512)
+
+
+def _layer_both_ways(pkg, pipeline, case, n_split):
+    """The decode layer through the separate calls and through one
+    qsa_decode_layer_latent call, on the same inputs: both results."""
+    nq = case.nq
+    lat = qc.to_dev(case.latent)
+    kv = pkg.make_kv(lat, lat)
+    args = (qc.i32(case.ctxs), case.cap, qc.to_dev(case.q_idx), qc.to_dev(case.keys), qc.to_dev(case.q), kv)
+    w = torch.tensor(case.w, device="cuda")
+    out = []
+    for fused in (False, True):
+        bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, nq, case.cap, n_split=n_split)
+        assert bufs.latent_ws is not None
+        pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, *args, bufs, q_seq=qc.i32(range(nq)), w_idx=w, fused=fused)
+        torch.cuda.synchronize()
+        out.append(dict(sel=bufs.sel.cpu().numpy(), n_sel=bufs.n_sel.cpu().numpy(), o=bufs.o.cpu().numpy(),
+                        lse=bufs.lse.cpu().numpy(), ob=qc.from_dev_bits(bufs.o_bf16),
+                        scores=bufs.scores.cpu().numpy()))
+    return out
+
+
+@pytest.mark.parametrize("n_split", [None, 3])
+@pytest.mark.parametrize("which", ["short", "long"])
+def test_mla_decode_layer_one_call(Q, which, n_split):
+    """qsa_decode_layer_latent against the oracle and, bit for bit, against
+    the separate calls, over every way its attention work-groups select:
+    every token (ctx <= 2048), the register select straight over the scores
+    (ctx <= 8192), the streamed select (too few chunk lists for the union),
+    the union of the chunk lists (ctx > 65,024; one query ragged), and the
+    fallback when a chunk's bound ranks above the union's 2048th (query with
+    all-negative indexer weights: every score 0, ties decided by index)."""
+    pkg, pipeline = Q
+    ctxs = [0, 1, 2048, 2049, 8192, 8193, 20000] if which == "short" else [65536, 70001, 70001]
+    _print_case("mla_decode_one_call", ctxs=ctxs, n_split=n_split)
+    case = MlaCase(63, ctxs)
+    if which == "long":
+        case.w[2] = -np.abs(case.w[2]) - 0.125  # every score of query 2 is 0
+    sep, one = _layer_both_ways(pkg, pipeline, case, n_split)
+    for i, ctx in enumerate(ctxs):
+        r = case.oracle(i)
+        qc.check_row(one["sel"][i], one["n_sel"][i], one["o"][i], one["lse"][i], one["ob"][i], r, ctx, 1, 2048,
+                     case.q[i], case.latent[i], case.latent[i], SCALE, dv=512)
+        if which == "long" and i == 2:
+            assert np.all(r["scores"][one["sel"][i, :2048]] == 0.0)
+    for k in ("sel", "n_sel", "o", "lse", "ob"):
+        assert np.array_equal(sep[k], one[k]), k
+    for i, ctx in enumerate(ctxs):
+        assert np.array_equal(sep["scores"][i, :ctx].view(np.uint32), one["scores"][i, :ctx].view(np.uint32))
 
 
 @pytest.mark.parametrize("tile", [16384, 4096, 777])
