@@ -376,7 +376,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       }
     }
     itk::RegSelOut ro;
-    if (!itk::select_registers<kRegRB>(la, um, ukey, uidx, my_bound, sh.u.f, emit, ro)) {
+    if (!itk::select_registers<kRegRB, true>(la, um, ukey, uidx, my_bound, sh.u.f, emit, ro)) {
       // the union cannot show the top-k exact: from the scores (when only a
       // tie failed, the threshold is known and one pass settles it)
       __syncthreads();  // the select's LDS is free

@@ -181,20 +181,26 @@ __device__ __forceinline__ bool use_union(const IndexTopkArgs& a, int n) {
 // Union entry e = chunk * keep + slot of query i (each list in ascending
 // block order, so entry order is block order), as (key << 32 | block), 0 =
 // empty; thread t holds entries t * kRegR + r (thread-major). Entries at or
-// past u are 0. kCoh: written by other work-groups of the same launch (else
-// by an earlier launch, and plain 16-byte loads see it).
+// past u are 0. The lists are stored pair-major (chunk_list), so the 16-byte
+// pair loads of neighbouring threads are neighbours in memory. kCoh: written
+// by other work-groups of the same launch (else by an earlier launch, and
+// plain 16-byte loads see it).
 template <bool kCoh = true>
 __device__ __forceinline__ void load_union(const IndexTopkArgs& a, int i, int u, uint64_t (&ent)[kRegR]) {
   const uint64_t* ul = a.list + size_t(i) * a.n_chunks * a.keep;
   const int e0 = int(threadIdx.x) * kRegR;
-  if constexpr (kCoh) {
+  const int lk = a.keep == 16 ? 4 : 3;  // the list length is 8 or 16
+  // u is a multiple of the list length, so pairs are never split
 #pragma unroll
-    for (int r = 0; r < kRegR; r++) ent[r] = e0 + r < u ? ld_coherent(ul + e0 + r) : 0ull;
-  } else {
-    // u is a multiple of the list length (8 or 16), so pairs are never split
-#pragma unroll
-    for (int r = 0; r < kRegR; r += 2) {
-      const u32x4 w = e0 + r < u ? ld16(ul + e0 + r) : u32x4{0u, 0u, 0u, 0u};
+  for (int r = 0; r < kRegR; r += 2) {
+    const int e = e0 + r;
+    const int c = e >> lk, s = e & (a.keep - 1);
+    const size_t at = (size_t(s >> 1) * a.n_chunks + c) * 2;
+    if constexpr (kCoh) {
+      ent[r] = e < u ? ld_coherent(ul + at) : 0ull;
+      ent[r + 1] = e < u ? ld_coherent(ul + at + 1) : 0ull;
+    } else {
+      const u32x4 w = e < u ? ld16(ul + at) : u32x4{0u, 0u, 0u, 0u};
       ent[r] = (uint64_t(w[1]) << 32) | w[0];
       ent[r + 1] = (uint64_t(w[3]) << 32) | w[2];
     }
@@ -223,14 +229,14 @@ struct RegSelOut {
   int need, n_gt;
 };
 
-template <int R, class Emit>
+template <int R, bool kAgg = false, class Emit>
 __device__ bool select_registers(const IndexTopkArgs& a, bool union_mode, const uint32_t (&ukey)[R],
                                  const int (&uidx)[R], uint64_t my_bound, FinalLds& sh, Emit emit, RegSelOut& out) {
   constexpr int NW = kNT / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   uint32_t kstar;
   int need;
-  regsel_threshold<kNT, R>(ukey, a.topk, sh.rs, kstar, need);
+  regsel_threshold<kNT, R, kAgg>(ukey, a.topk, sh.rs, kstar, need);
   int g = 0, e = 0;
 #pragma unroll
   for (int r = 0; r < R; r++) {
@@ -491,7 +497,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   const bool union_mode = use_union(a, n);
 
   // ---- chunk list: 8 best per wave, then 16 best of the 32
-  if (union_mode) chunk_list<TPW, kSelect>(a, i, chunk, n, w0, key, sh.lst);
+  if (union_mode) chunk_list<TPW, kSelect, kWaveKeep, true>(a, i, chunk, n, w0, key, sh.lst);
 
   if (!kSelect) return false;
   // ---- the last work-group of this query selects

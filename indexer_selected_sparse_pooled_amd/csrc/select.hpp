@@ -159,7 +159,9 @@ struct RegSelLds {
 // Requires 1 <= k <= number of nonzero keys. 8-bit radix passes narrow the
 // threshold to one bin; as soon as that bin holds at most kRegSelCand keys,
 // they are gathered in LDS and wave 0 settles the remaining low bits.
-template <int NT, int R>
+// kAgg: histogram increments go through hist_add (worth its extra
+// instructions where many keys are equal, e.g. scores that are exact zeros).
+template <int NT, int R, bool kAgg = false>
 __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>& sh, uint32_t& kstar, int& need) {
   constexpr int NW = NT / 64;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -207,7 +209,10 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
 #pragma unroll
     for (int r = 0; r < R; r++) {
       const bool in = key[r] != 0u && (key[r] & mask) == prefix;
-      hist_add(h, in, (key[r] >> shift) & dmask);
+      if constexpr (kAgg)
+        hist_add(h, in, (key[r] >> shift) & dmask);
+      else
+        atomicAdd(&h[in ? (key[r] >> shift) & dmask : 256u + lane], 1u);
     }
     __syncthreads();
     // every wave finds the digit (same result everywhere): lane holds the
