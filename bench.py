@@ -30,6 +30,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -788,6 +789,8 @@ def run_mla(pkg, pipeline, bm, qi, torch, steps, warmup):
                           useful_gflop=round(flops["total"] / 1e9, 1), history_tile=t0,
                           attend_tflops=pre["attend_tflops"],
                           attend_mfma_frac=round(pre["attend_tflops"] / BF16_PEAK_TFLOPS, 4),
+                          attend_counters=counter_mfma("attend_b_t"),
+                          select_gemm_counters=counter_mfma("scores_gemm_b<false, true>"),
                           breakdown_us=pre["breakdown_us"], fp8_rows=pre["fp8_rows"],
                           **{f"tile_{t}": {"tok_s": round(pre[t]["tok_s"], 1), "ms_per_chunk": round(pre[t]["ms"], 4)}
                              for t in MLA["tiles"][1:]})
@@ -813,6 +816,33 @@ def counter_traffic(kernel: str, groups: str):
         if len(f) == 6 and l[:40].strip() == kernel and f[0] == groups:
             return int(f[4]) + int(f[5])
     return None
+
+
+MFMA_COUNTERS = os.path.join(ROOT, "profiles", "mfma_lds_counters_prefill_4096q_tile_mla_2048q_131k.txt")
+
+
+def counter_mfma(kernel: str):
+    """Counter-measured MFMA busy % (AMD's MfmaUtil) and executed / useful
+    MFMA work of `kernel` from the committed rocprofv3 summary, or None if
+    the kernel sources changed since (or no summary exists)."""
+    from indexer_selected_sparse_pooled_amd.profile_kernels import source_digest
+    if not os.path.exists(MFMA_COUNTERS):
+        return None
+    text = open(MFMA_COUNTERS).read()
+    digest = re.findall(r"^source digest: (\S+)", text, re.M)
+    if not digest or digest[0] != source_digest():
+        return None
+    m = re.search(r"^" + re.escape(kernel) + r" \[.*?\n(.*?)(?=^\S|\Z)", text, re.M | re.S)
+    if not m:
+        return None
+    busy = re.search(r"MFMA busy ([0-9.]+) %", m.group(1))
+    ratio = re.search(r"executed / useful = ([0-9.]+)", m.group(1))
+    out = {}
+    if busy:
+        out["mfma_busy_pct"] = float(busy.group(1))
+    if ratio:
+        out["executed_over_useful"] = float(ratio.group(1))
+    return out or None
 
 
 # ---------------------------------------------------------------- oracle --
@@ -1136,6 +1166,7 @@ def main():
                     "tflops": round(t8["tflops"], 2), "mfma_frac": round(t8["tflops"] / BF16_PEAK_TFLOPS, 5),
                     "useful_gflop": round(pflops["total"] / 1e9, 2),
                     "breakdown_us": pre["breakdown_us"], "attend_tflops": pre["attend_tflops"],
+                    "attend_counters": counter_mfma("attend_a"), "scores_gemm_counters": counter_mfma("scores_gemm_a"),
                     "tile_1024": {"tok_s": round(pre[1024]["tok_s"], 1), "ms_per_chunk": round(pre[1024]["ms"], 4)},
                     "correlated": pre["correlated"], "oracle_tok_s": cpu_all[4]["value"]},
         "mla": dict(mla, decode=dict(mla["decode"], oracle_steps_s=cpu_all["5b"]["value"]),

@@ -8,8 +8,15 @@ Runs, each `--reps` times, on seeded synthetic inputs already in HBM:
     and the same layer as one qsa_decode_layer call (two launches);
   * one history tile of the 4096-query prefill chunk (qsa_sparse_prefill);
   * the shared-latent prefill attention of 2048 queries at context 131,072
-    (one qsa_sparse_prefill over the whole history).
-`--parts` picks a subset (copy, decode, prefill, mla).
+    (one qsa_sparse_prefill over the whole history);
+  * the shared-latent decode step at batch 8, context 131,072, as one
+    qsa_decode_layer_latent call.
+`--parts` picks a subset (copy, decode, prefill, mla, mladecode).
+`--useful-out FILE` writes, per MFMA kernel of these workloads, the useful
+FLOPs of one dispatch (the contraction the method needs: selected tokens
+only, causal keys only), computed on the host from the run's own
+selections; `--counters ... --useful FILE` then reports executed bf16 MFMA
+work (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512) over it.
 
 Usage (one counter group per run):
   rocprofv3 --pmc FETCH_SIZE --output-format csv -d OUT -o run -- \
@@ -18,7 +25,7 @@ Usage (one counter group per run):
 Summaries of rocprofv3 CSV output (host only, no GPU):
   python profile_kernels.py --trace OUT/run_kernel_trace.csv
   python profile_kernels.py --pmc FETCH/run_counter_collection.csv WRITE/run_counter_collection.csv
-  python profile_kernels.py --counters A/run_counter_collection.csv [B/...]   (MFMA, LDS, waits)
+  python profile_kernels.py --counters A/run_counter_collection.csv [B/...] [--useful FILE]   (MFMA, LDS, waits)
 The counter summary scales each memory counter by what it reads for the
 256 MiB copy, so its figures are bytes moved to and from memory.
 """
@@ -108,7 +115,7 @@ def summarize_pmc(fetch_csv: str, write_csv: str) -> str:
     return "\n".join(out)
 
 
-def summarize_counters(paths) -> str:
+def summarize_counters(paths, useful=None) -> str:
     """Per (kernel, grid): the per-dispatch average of every counter found in
     the given counter_collection.csv files (one per rocprofv3 --pmc pass),
     and, where present: MFMA busy % (AMD's MfmaUtil: MFMA-busy cycles of all
@@ -134,7 +141,11 @@ def summarize_counters(paths) -> str:
         if "MfmaUtil" in avg:
             parts.append(f"  => MFMA busy {avg['MfmaUtil']:.2f} %")
         if "SQ_INSTS_VALU_MFMA_MOPS_BF16" in avg:
-            parts.append(f"  => executed bf16 MFMA {avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512 / 1e9:.3f} GFLOP per dispatch")
+            ex = avg['SQ_INSTS_VALU_MFMA_MOPS_BF16'] * 512
+            parts.append(f"  => executed bf16 MFMA {ex / 1e9:.3f} GFLOP per dispatch")
+            u = (useful or {}).get(kern)
+            if u:
+                parts.append(f"  => useful {u / 1e9:.3f} GFLOP per dispatch: executed / useful = {ex / u:.2f}")
         if "SQ_LDS_BANK_CONFLICT" in avg and avg.get("SQ_LDS_IDX_ACTIVE"):
             parts.append(f"  => LDS bank conflicts {100 * avg['SQ_LDS_BANK_CONFLICT'] / avg['SQ_LDS_IDX_ACTIVE']:.1f} % "
                          f"of LDS-active cycles")
@@ -155,12 +166,16 @@ def main() -> int:
                     help="summarize two rocprofv3 counter_collection.csv files and exit")
     ap.add_argument("--counters", nargs="+", metavar="CSV",
                     help="summarize any rocprofv3 counter_collection.csv files (MFMA, LDS, waits) and exit")
+    ap.add_argument("--useful", help="with --counters: the useful-FLOP file a run wrote (--useful-out)")
+    ap.add_argument("--useful-out", help="write the useful FLOPs per dispatch of the MFMA kernels run here")
     args = ap.parse_args()
     if args.trace:
         print(summarize_trace(args.trace))
         return 0
     if args.counters:
-        print(summarize_counters(args.counters))
+        import json
+        useful = json.load(open(args.useful)) if args.useful else None
+        print(summarize_counters(args.counters, useful))
         return 0
     if args.pmc:
         print(summarize_pmc(*args.pmc))
@@ -173,17 +188,22 @@ def main() -> int:
     from qsa_inputs.gpu import fill_normal_bf16
 
     pkg.qsa.lib()
-    dev = "cuda"
     parts = set(args.parts.split(","))
+    useful = {}
     if "copy" in parts:
         copy_reference(torch, fill_normal_bf16, args.reps)
     if "decode" in parts:
         decode_layer(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
     if "prefill" in parts:
-        prefill_tile(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
+        useful.update(prefill_tile(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps))
     if "mla" in parts:
-        mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
+        useful.update(mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps))
+    if "mladecode" in parts:
+        mla_decode(torch, pkg, qi, pipeline, fill_normal_bf16, args.reps)
     torch.cuda.synchronize()
+    if args.useful_out:
+        import json
+        json.dump(useful, open(args.useful_out, "w"), indent=1)
     print("profile_kernels: done", flush=True)
     return 0
 
@@ -253,8 +273,23 @@ def prefill_tile(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
         pkg.qsa_sparse_prefill(pkg.SEL_A, pkg.ATTN_A, q_ctx, ctx_max, q, kv, pb.sel, pb.n_sel, a0, a1,
                                pb.o_tiles[3], pb.lse_tiles[3])
     torch.cuda.synchronize()
+    # useful work: the indexer dot of every complete block before each query;
+    # QK and PV (16 heads, 256 + 256 dims) over the query's selected tokens
+    # inside the tile: its selected blocks' 4 tokens and its trailing tokens
+    import numpy as np
+    ctx = q_ctx.cpu().numpy().astype(np.int64)
+    sel, ns = pb.sel.cpu().numpy(), pb.n_sel.cpu().numpy()
+    att = 0
+    for i in range(C):
+        blk = sel[i, :ns[i]].astype(np.int64)
+        att += int((np.clip(4 * blk + 4, a0, a1) - np.clip(4 * blk, a0, a1)).sum())
+        tr0, tr1 = 4 * (ctx[i] // 4), ctx[i]  # the trailing tokens
+        att += max(0, min(tr1, a1) - max(tr0, a0))
+    useful = {"scores_gemm_a": float((ctx // 4).sum() * 128 * 2),
+              "attend_a": float(att * 16 * (256 + 256) * 2)}
     del pb, k, v, kv
     torch.cuda.empty_cache()
+    return useful
 
 
 def mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
@@ -289,6 +324,42 @@ def mla_prefill(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
     for _ in range(reps):
         pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q, kv8, pb.sel, pb.n_sel, 0, L, pb.o_tiles[0],
                                pb.lse_tiles[0])
+    torch.cuda.synchronize()
+    # useful work: the 4-head indexer over every earlier token; QK (576
+    # dims) and PV (512) of 64 heads over each query's selected tokens
+    ctx = q_ctx.cpu().numpy().astype(np.int64)
+    ns = pb.n_sel.cpu().numpy().astype(np.int64)
+    att = float(ns.sum() * 64 * (576 + 512) * 2)
+    # (scores_gemm_b<false, true>: the list-mode GEMM of qsa_index_topk_prefill, one dispatch per call)
+    useful = {"scores_gemm_b<false, true>": float(ctx.sum() * 4 * 64 * 2), "attend_b_t": att, "attend_b_fp8": att}
+    del pb, lat, keys, kv, rows, kv8
+    torch.cuda.empty_cache()
+    return useful
+
+
+def mla_decode(torch, pkg, qi, pipeline, fill_normal_bf16, reps):
+    """The shared-latent decode step: batch 8 at context 131,072, one
+    qsa_decode_layer_latent call (scan with chunk lists, then select and
+    attend)."""
+    import numpy as np
+    dev = "cuda"
+    L, B = 131072, 8
+    seed = qi.config_seed(5)
+    lat = torch.empty(B, L, 1, 576, dtype=torch.bfloat16, device=dev)
+    keys = torch.empty(B, L, 64, dtype=torch.bfloat16, device=dev)
+    q = torch.empty(B, 64, 576, dtype=torch.bfloat16, device=dev)
+    q_idx = torch.empty(B, 4, 64, dtype=torch.bfloat16, device=dev)
+    for s in range(B):
+        for t, kind in ((lat, "latent"), (keys, "raw_key"), (q, "q"), (q_idx, "q_idx")):
+            fill_normal_bf16(t[s], seed, qi.stream_id(0, s, kind))
+    w = torch.tensor(np.stack([qi.uniform_f32(seed, qi.stream_id(0, s, "w_idx"), 4) for s in range(B)]), device=dev)
+    kv = pkg.make_kv(lat, lat)
+    q_ctx = torch.full((B,), L, dtype=torch.int32, device=dev)
+    q_seq = torch.arange(B, dtype=torch.int32, device=dev)
+    bufs = pipeline.decode_buffers(pkg.SEL_B, pkg.ATTN_B, B, L)
+    for _ in range(reps):
+        pipeline.decode_layer(pkg.SEL_B, pkg.ATTN_B, q_ctx, L, q_idx, keys, q, kv, bufs, q_seq=q_seq, w_idx=w,
+                              fused=True)
     torch.cuda.synchronize()
 
 
