@@ -385,9 +385,12 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
  *      The parts of a (query, kv head) wait for each other before they
  *      merge; the wait is bounded: if it runs out (which only a corrupted
  *      workspace or a device shared with other work can cause) a sticky
- *      error word in the workspace is set, results are unspecified, and
- *      with QSA_SYNC_CHECK=1 the call returns QSA_ERR_LAUNCH; zero the
- *      workspace to clear it. */
+ *      error word in the workspace is set and results are unspecified. The
+ *      error word is the workspace's first 4 bytes (uint32, device memory):
+ *      once the stream has completed the call, a nonzero value means a wait
+ *      ran out (callers that run layers concurrently on several streams
+ *      read it after their step). With QSA_SYNC_CHECK=1 the call itself
+ *      returns QSA_ERR_LAUNCH. Zero the workspace to clear it. */
 qsa_status qsa_decode_layer(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg, int32_t nq,
                             const int32_t* q_seq, const int32_t* q_ctx, int32_t max_ctx,
                             const qsa_bf16* q_idx, const void* keys, int64_t keys_seq_stride,
