@@ -324,7 +324,8 @@ size_t qsa_index_topk_prefill_workspace_bytes(const qsa_sel_cfg* cfg, int32_t nq
  * scan on its own. ("3090x3で 314 万コンテキスト", "VRAM に残す必要があるもの":
  * every pooled key is scored at every step.)
  * Variant A only (block 4, idx_dim 128, idx_heads 1; bf16 or FP8 keys).
- *   q_seq, q_ctx, q_idx, keys, scores, ld_scores: as qsa_index_scores.
+ *   q_seq, q_ctx, q_idx, keys, scores, ld_scores: as qsa_index_scores;
+ *          scores may be NULL (no scores written, ld_scores ignored).
  *   ws (device) workspace of at least qsa_index_topk_workspace_bytes(cfg,
  *      nq, max_ctx) bytes; contents ignored on entry, list layout internal.
  *      Calls that share a workspace must not run concurrently. */
@@ -374,6 +375,13 @@ qsa_status qsa_sparse_decode(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* att
  * QSA_ERR_UNSUPPORTED. nq <= 4096.
  *   q_seq, q_ctx, q_idx, keys, scores, ld_scores, sel, n_sel: as
  *          qsa_index_topk (scores, sel and n_sel are written as there).
+ *          scores may be NULL (ld_scores is then ignored): the scan writes
+ *          no scores (4 bytes per block less traffic), and a query whose
+ *          selection cannot come from the chunk lists (at most 4096 blocks,
+ *          too few or too many chunks, or a chunk's bound ranking above
+ *          the 512th) recomputes its scores from the keys inside the exact
+ *          streamed select, bit for bit the scan's: same selection, much
+ *          slower for such queries (every pass reads the query's keys).
  *   q, kv, n_split: as qsa_sparse_decode (1 <= n_split <= 256).
  *   o_out      (device) fp32 [nq][hq][dv], or NULL;
  *   o_out_bf16 (device) bf16 [nq][hq][dv] (nearest-even of o_out), or NULL;

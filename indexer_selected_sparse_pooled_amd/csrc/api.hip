@@ -554,10 +554,12 @@ qsa_status qsa_index_lists(const qsa_sel_cfg* cfg, int32_t nq, const int32_t* q_
   if (nq < 0 || max_ctx < 0) return fail(QSA_ERR_ARG, "negative nq or max_ctx");
   if (nq == 0) return QSA_OK;
   if (nq > 65535) return fail(QSA_ERR_UNSUPPORTED, "nq > 65535");
-  if (!q_ctx || !q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
-  if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
+  if (!q_ctx || !q_idx) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!aligned16(q_idx) || (scores && !aligned16(scores)))
+    return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
   const int64_t nmax = int64_t(max_ctx) / 4;
-  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
+  if (scores && ld_scores < nmax)
+    return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
   st = check_keys(cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
   if (st != QSA_OK) return st;
   const qsa::IndexTopkPlan plan = qsa::plan_index_topk(nq, max_ctx, cfg->topk);
@@ -643,13 +645,15 @@ qsa_status decode_layer_call(const char* fn, const qsa_sel_cfg* sel_cfg, const q
   if (nq == 0) return QSA_OK;
   if (nq > 4096) return fail(QSA_ERR_UNSUPPORTED, "nq > 4096");
   if (kv->format != QSA_KV_BF16) return fail(QSA_ERR_UNSUPPORTED, "%s: bf16 K/V rows only", fn);
-  if (!q_idx || !scores) return fail(QSA_ERR_ARG, "NULL pointer argument");
+  if (!q_idx) return fail(QSA_ERR_ARG, "NULL pointer argument");
   if (!o_out && !o_out_bf16 && !lse_out) return fail(QSA_ERR_ARG, "no output requested");
-  if (!aligned16(q_idx) || !aligned16(scores)) return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
+  if (!aligned16(q_idx) || (scores && !aligned16(scores)))
+    return fail(QSA_ERR_ARG, "q_idx and scores must be 16-byte aligned");
   if ((o_out && !aligned16(o_out)) || (o_out_bf16 && !aligned16(o_out_bf16)))
     return fail(QSA_ERR_ARG, "o_out and o_out_bf16 must be 16-byte aligned");
   const int64_t nmax = int64_t(max_ctx) / 4;
-  if (ld_scores < nmax) return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
+  if (scores && ld_scores < nmax)
+    return fail(QSA_ERR_ARG, "ld_scores %lld < max_ctx / 4 = %lld", (long long)ld_scores, (long long)nmax);
   st = check_keys(sel_cfg, keys, keys_seq_stride, nmax, q_seq != nullptr);
   if (st != QSA_OK) return st;
   const qsa::DecodeLayerPlan plan = qsa::plan_decode_layer(nq, max_ctx, sel_cfg->topk, attn_cfg->hq, attn_cfg->hkv,

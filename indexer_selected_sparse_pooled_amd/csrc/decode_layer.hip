@@ -106,10 +106,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
     uint64_t my_bound = tid < nch ? b0 : 0ull;
     if (tid + itk::kNT < nch) my_bound = b1 > my_bound ? b1 : my_bound;
-    if (!itk::select_registers(it, true, ukey, uidx, my_bound, sh.u.f, emit))
-      itk::select_streamed(it.scores + int64_t(i) * it.ld, n, topk, sh.u.f, emit);
-  } else {
+    if (!itk::select_registers(it, true, ukey, uidx, my_bound, sh.u.f, emit)) {
+      if (it.scores)
+        itk::select_streamed(it.scores + int64_t(i) * it.ld, n, topk, sh.u.f, emit);
+      else
+        itk::select_streamed_keys(it, i, n, sh.u.f, emit);
+    }
+  } else if (it.scores) {
     itk::final_select(it, i, n, sh.u.f, emit);
+  } else {  // no score buffer: the scores are recomputed from the keys
+    itk::select_streamed_keys(it, i, n, sh.u.f, emit);
   }
   __syncthreads();
   if (writer) {  // the query's selection, padded with -1

@@ -160,6 +160,75 @@ __device__ __forceinline__ float tile_scores(const u32x4 (&v)[16], int64_t tile0
   return __shfl(p[0], 16 * (lane & 3) + (lane >> 2));
 }
 
+// The score of pooled key b of query i computed by one thread, bit for bit
+// the scan's (tile_scores / fp8::tile_scores): the same 16-byte chunk dots
+// (dot2 chains for bf16 keys, fp32 FMA chains over exact E4M3 values for
+// FP8 keys) and the same pairwise tree over the chunks as the scan's
+// butterfly (fp32 addition is commutative, so only the pairing matters).
+__device__ __noinline__ float key_score(const IndexTopkArgs& a, int i, int seq, int b) {
+  const uint16_t* q = a.q_idx + int64_t(i) * 128;
+  if (a.key_fp8) {
+    const uint8_t* kb = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
+    const uint8_t* row = kb + fp8_code_off(b, 128);
+    float p[8];
+#pragma unroll
+    for (int c = 0; c < 8; c++) {  // chunk c: codes 16c .. 16c+15
+      const u32x4 v = ld16(row + 16 * c);
+      const u32x4 qa = ld16(q + 16 * c), qb = ld16(q + 16 * c + 8);
+      float qf[16];
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        qf[2 * j] = bf16_lo(qa[j]);
+        qf[2 * j + 1] = bf16_hi(qa[j]);
+        qf[8 + 2 * j] = bf16_lo(qb[j]);
+        qf[8 + 2 * j + 1] = bf16_hi(qb[j]);
+      }
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; w++) {
+        float x0, x1, x2, x3;
+        e4m3x4(v[w], x0, x1, x2, x3);
+        acc = fmaf(x0, qf[4 * w], acc);
+        acc = fmaf(x1, qf[4 * w + 1], acc);
+        acc = fmaf(x2, qf[4 * w + 2], acc);
+        acc = fmaf(x3, qf[4 * w + 3], acc);
+      }
+      p[c] = acc;
+    }
+#pragma unroll
+    for (int c = 0; c < 4; c++) p[c] = p[c] + p[c + 4];
+#pragma unroll
+    for (int c = 0; c < 2; c++) p[c] = p[c] + p[c + 2];
+    const float sc = *reinterpret_cast<const float*>(kb + fp8_scale_off(b, 128));
+    return (p[0] + p[1]) * sc;
+  }
+  const uint16_t* row = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss + int64_t(b) * 128;
+  float p[16];
+#pragma unroll
+  for (int c = 0; c < 16; c++) p[c] = dot8(ld16(row + 8 * c), ld16(q + 8 * c));
+#pragma unroll
+  for (int c = 0; c < 8; c++) p[c] = p[c] + p[c + 8];
+#pragma unroll
+  for (int c = 0; c < 4; c++) p[c] = p[c] + p[c + 4];
+#pragma unroll
+  for (int c = 0; c < 2; c++) p[c] = p[c] + p[c + 2];
+  return p[0] + p[1];
+}
+
+// Exact selection over the scores of query i recomputed from its keys (for
+// calls given no score buffer): the streamed select with each key's score
+// computed where it is read. Slow (every pass reads the query's keys), but
+// only taken where the chunk lists cannot show the selection exact.
+template <class Emit>
+__device__ void select_streamed_keys(const IndexTopkArgs& a, int i, int n, FinalLds& sh, Emit emit) {
+  const int seq = a.q_seq ? a.q_seq[i] : 0;
+  auto key_at = [&](int j) { return order_key(key_score(a, i, seq, j)); };
+  uint32_t kstar;
+  int need;
+  stream_select<kNT>(key_at, n, a.topk, sh.st, kstar, need);
+  stream_compact<kNT>(key_at, n, kstar, need, sh.st, emit);
+}
+
 // Exact selection over the scores of one query, streamed from memory.
 template <class Emit>
 __device__ void select_streamed(const float* sc, int n, int topk, FinalLds& sh, Emit emit) {
@@ -442,8 +511,10 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   }
   const int nch = (n + C - 1) / C;
 
-  // ---- scan: scores of this chunk
-  float* out = a.scores + int64_t(i) * a.ld;
+  // ---- scan: scores of this chunk (the lists-only scan writes them only
+  // when given a score buffer)
+  const bool store = kSelect || a.scores != nullptr;
+  float* out = store ? a.scores + int64_t(i) * a.ld : nullptr;
   const int64_t w0 = lo + int64_t(wave) * TPW * 64;
   uint32_t key[TPW];
   // two tiles in flight per wave: the next tile's loads are issued before
@@ -453,7 +524,7 @@ __device__ bool chunk_step(const IndexTopkArgs& a, int i, int chunk, FinalLds& s
   auto keep_score = [&](int t, int64_t tile0, float s) {
     const int64_t blk = tile0 + lane;
     if (blk < n) {
-      put<kSelect>(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
+      if (store) put<kSelect>(reinterpret_cast<uint32_t*>(out) + blk, __float_as_uint(s));
       key[t] = order_key(s);
     }
   };

@@ -18,7 +18,7 @@ from . import qsa
 
 @dataclass
 class DecodeBuffers:
-    scores: torch.Tensor    # [nq, max_ctx / block] fp32
+    scores: torch.Tensor    # [nq, max_ctx / block] fp32 (or None: see decode_buffers)
     sel: torch.Tensor       # [nq, topk] int32
     n_sel: torch.Tensor     # [nq] int32
     ws: torch.Tensor        # top-k workspace (or None)
@@ -63,13 +63,16 @@ def latent_layer(sel_cfg, attn_cfg) -> bool:
             and (attn_cfg.hq, attn_cfg.hkv, attn_cfg.dk, attn_cfg.dv) == (64, 1, 576, 512))
 
 
-def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda") -> DecodeBuffers:
+def decode_buffers(sel_cfg, attn_cfg, nq, max_ctx, n_split=None, device="cuda", keep_scores=True) -> DecodeBuffers:
+    """Buffers of one decode layer. keep_scores=False: no score buffer (the
+    one-call pooled-block layer then writes no scores; the separate calls
+    need one)."""
     nmax = max(1, max_ctx // sel_cfg.block)
     if n_split is None:
         n_split = default_n_split(nq, attn_cfg.hkv, sel_cfg.topk * sel_cfg.block + sel_cfg.block - 1)
     f32 = dict(dtype=torch.float32, device=device)
     return DecodeBuffers(
-        scores=torch.empty(nq, nmax, **f32),
+        scores=torch.empty(nq, nmax, **f32) if keep_scores else None,
         sel=torch.empty(nq, sel_cfg.topk, dtype=torch.int32, device=device),
         n_sel=torch.empty(nq, dtype=torch.int32, device=device),
         ws=qsa.topk_workspace(sel_cfg, nq, max_ctx, device),
@@ -128,10 +131,12 @@ class MicroBatch:
     bufs: list
 
 
-def micro_batches(sel_cfg, attn_cfg, q_ctx, q_seq, max_ctx, n_layers, n_micro, n_split=None, device="cuda"):
+def micro_batches(sel_cfg, attn_cfg, q_ctx, q_seq, max_ctx, n_layers, n_micro, n_split=None, device="cuda",
+                  keep_scores=True):
     """Split a decode batch into n_micro contiguous micro-batches. Each keeps
     the batch's max_ctx and n_split (the whole batch's default unless given),
-    so its layers run exactly the batch's kernels on its own sequences."""
+    so its layers run exactly the batch's kernels on its own sequences.
+    keep_scores: as decode_buffers."""
     nq = int(q_ctx.numel())
     if not 1 <= n_micro <= nq:
         raise ValueError(f"n_micro {n_micro} not in [1, {nq}]")
@@ -141,7 +146,8 @@ def micro_batches(sel_cfg, attn_cfg, q_ctx, q_seq, max_ctx, n_layers, n_micro, n
     for m in range(n_micro):
         lo, hi = m * nq // n_micro, (m + 1) * nq // n_micro
         out.append(MicroBatch(lo, hi, q_ctx[lo:hi].contiguous(), q_seq[lo:hi].contiguous(),
-                              [decode_buffers(sel_cfg, attn_cfg, hi - lo, max_ctx, n_split=n_split, device=device)
+                              [decode_buffers(sel_cfg, attn_cfg, hi - lo, max_ctx, n_split=n_split, device=device,
+                                              keep_scores=keep_scores)
                                for _ in range(n_layers)]))
     return out
 

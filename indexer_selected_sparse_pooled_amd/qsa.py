@@ -323,16 +323,18 @@ def qsa_index_topk(cfg, q_ctx, max_ctx, q_idx, keys, scores, sel, n_sel, ws, q_s
 
 
 def qsa_index_lists(cfg, q_ctx, max_ctx, q_idx, keys, scores, ws, q_seq=None, stream=None):
-    """The scan qsa_decode_layer issues first, on its own: scores and the
-    chunk candidate lists (in ws: index_topk_workspace(...)); no selection."""
+    """The scan qsa_decode_layer issues first, on its own: scores (unless
+    scores is None) and the chunk candidate lists (in ws:
+    index_topk_workspace(...)); no selection."""
     nq = q_ctx.shape[0]
     _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(scores, "scores", 1)
+    if scores is not None:
+        _rowmajor_tail(scores, "scores", 1)
     kp, kss = _keys_arg(cfg, keys, max_ctx, "qsa_index_lists")
     _check("qsa_index_lists", lib().qsa_index_lists(
         ctypes.byref(cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"), max_ctx,
         _dev(q_idx, _BF16, "q_idx"), kp, kss,
-        _dev(scores, _F32, "scores"), scores.stride(0), ctypes.c_void_p(ws.data_ptr()),
+        _dev(scores, _F32, "scores"), scores.stride(0) if scores is not None else 0, ctypes.c_void_p(ws.data_ptr()),
         ws.numel() * ws.element_size(), _stream(stream)))
 
 
@@ -368,7 +370,8 @@ def _decode_layer_args(fn, sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv
                        o_out, o_out_bf16, lse_out, q_seq):
     nq = q_ctx.shape[0]
     _rowmajor_tail(q_idx, "q_idx", 3)
-    _rowmajor_tail(scores, "scores", 1)
+    if scores is not None:
+        _rowmajor_tail(scores, "scores", 1)
     kp, kss = _keys_arg(sel_cfg, keys, max_ctx, fn)
     if sel.shape != (nq, sel_cfg.topk) or not sel.is_contiguous():
         raise ValueError(f"{fn}: sel must be a contiguous [nq, topk] tensor")
@@ -381,7 +384,8 @@ def _decode_layer_args(fn, sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv
             raise ValueError(f"{fn}: {name} must be a contiguous {list(shp)} tensor")
     return [ctypes.byref(sel_cfg), ctypes.byref(attn_cfg), nq, _dev(q_seq, _I32, "q_seq"), _dev(q_ctx, _I32, "q_ctx"),
             max_ctx, _dev(q_idx, _BF16, "q_idx"), kp, kss, _dev(q, _BF16, "q"),
-            ctypes.byref(kv), _dev(scores, _F32, "scores"), scores.stride(0), _dev(sel, _I32, "sel"),
+            ctypes.byref(kv), _dev(scores, _F32, "scores"), scores.stride(0) if scores is not None else 0,
+            _dev(sel, _I32, "sel"),
             _dev(n_sel, _I32, "n_sel"), n_split, _dev(o_out, _F32, "o_out"), _dev(o_out_bf16, _BF16, "o_out_bf16"),
             _dev(lse_out, _F32, "lse_out")]
 
@@ -390,7 +394,8 @@ def qsa_decode_layer(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scor
                      o_out=None, o_out_bf16=None, lse_out=None, q_seq=None, stream=None):
     """One decode layer (two launches): qsa_index_topk, then qsa_sparse_decode
     and qsa_lse_merge. q_idx: [nq, 1, 128] bf16; keys: [n_seq, n_blocks, 128]
-    bf16 (or FP8 pages, see qsa_index_scores); q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk;
+    bf16 (or FP8 pages, see qsa_index_scores); q: [nq, hq, dk] bf16; scores/sel/n_sel as qsa_index_topk
+    (scores may be None: no scores are written, see include/qsa.h);
     o_out: [nq, hq, dv] fp32, o_out_bf16: [nq, hq, dv] bf16, lse_out: [nq, hq]
     fp32 (each optional); ws: decode_layer_workspace(...)."""
     args = _decode_layer_args("qsa_decode_layer", sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, scores, sel,

@@ -101,6 +101,85 @@ def test_decode_layer_mixed_contexts(Q, n_split):
     assert torch.count_nonzero(fused.layer_ws[:64]).item() == 0, "control words not reset"
 
 
+def _same_bits(a, b):
+    for name in ("sel", "n_sel", "o", "o_bf16", "lse"):
+        assert torch.equal(getattr(a, name), getattr(b, name)), name
+
+
+@pytest.mark.parametrize("fp8", [False, True], ids=["bf16_keys", "fp8_keys"])
+def test_decode_layer_without_scores(Q, fp8):
+    """qsa_decode_layer with no score buffer: the scan writes no scores, and
+    every query whose selection does not come from the chunk lists (full
+    attention, too few chunks for the union, ragged lengths) recomputes its
+    scores from the keys, bit for bit the scan's. Results identical to the
+    call with a score buffer; selections and outputs against the oracle
+    (bf16 keys)."""
+    pkg, pipeline = Q
+    ctxs = [8195, 2051, 2052, 3, 0, 40000, 8192, 131071]
+    _print_case("decode_layer_no_scores", ctxs=ctxs, fp8=fp8)
+    case = qc.DecodeCase(51, ctxs)
+    nq = case.nq
+    pooled = torch.zeros(nq, case.cap // 4, 128, dtype=torch.bfloat16, device="cuda")
+    pkg.qsa_pool_keys(qc.to_dev(case.raw), pooled, block=4)
+    cfg = pkg.SEL_A_FP8 if fp8 else pkg.SEL_A
+    keys = pooled
+    if fp8:
+        keys = pkg.fp8_keys_empty(nq, case.cap // 4, 128)
+        pkg.qsa_quantize_keys(pooled, keys)
+    kv = pkg.make_kv(qc.to_dev(case.k), qc.to_dev(case.v))
+    q_idx, q = qc.to_dev(case.q_idx[:, None, :]), qc.to_dev(case.q)
+    max_ctx = max(ctxs)
+    out = []
+    for keep in (True, False):
+        bufs = pipeline.decode_buffers(cfg, pkg.ATTN_A, nq, max_ctx, keep_scores=keep)
+        assert (bufs.scores is None) != keep
+        pipeline.decode_layer(cfg, pkg.ATTN_A, qc.i32(ctxs), max_ctx, q_idx, keys, q, kv, bufs,
+                              q_seq=qc.i32(range(nq)), fused=True)
+        torch.cuda.synchronize()
+        pkg.check_decode_layer_error(bufs.layer_ws)
+        out.append(bufs)
+    _same_bits(out[0], out[1])
+    if not fp8:
+        _check_against_oracle(out[1], case.oracle(), ctxs, case.q, lambda i, t: case.k[i][t],
+                              lambda i, t: case.v[i][t])
+
+
+@pytest.mark.parametrize("kind", ["tied_run", "graded_run"])
+def test_decode_layer_without_scores_overflowing_lists(Q, kind):
+    """Top blocks packed into a few chunks, so that a chunk's bound ranks
+    above the 512th and the union check fails: with no score buffer the
+    exact fallback recomputes the query's scores from the keys. Same bits as
+    the call with a score buffer; the selection is the oracle's on the exact
+    scores (the score is key dimension 0)."""
+    pkg, pipeline = Q
+    n_blk = 40000
+    runs = {"tied_run": [(10003, 700, 8.0, 0.0)], "graded_run": [(5000, 600, 6.0, 2.0**-6)]}[kind]
+    _print_case("decode_layer_no_scores_overflow", kind=kind)
+    keys_np = qc.bits(47, 3, (n_blk, 128))
+    for (b0, length, val, step) in runs:
+        keys_np[b0:b0 + length, 0] = orc.f64_to_bf16(val + step * np.arange(length))
+    keys = qc.to_dev(keys_np).unsqueeze(0)
+    qv = np.zeros((1, 1, 128), dtype=np.uint16)
+    qv[0, 0, 0] = 0x3F80  # 1.0: score = key dimension 0, exactly
+    L = 4 * n_blk
+    k = qc.to_dev(qc.bits(48, 1, (1, L, 2, 256)))
+    v = qc.to_dev(qc.bits(48, 2, (1, L, 2, 256)))
+    kv = pkg.make_kv(k, v)
+    q = qc.to_dev(qc.bits(48, 3, (1, 16, 256)))
+    out = []
+    for keep in (True, False):
+        bufs = pipeline.decode_buffers(pkg.SEL_A, pkg.ATTN_A, 1, L, keep_scores=keep)
+        pipeline.decode_layer(pkg.SEL_A, pkg.ATTN_A, qc.i32([L]), L, qc.to_dev(qv), keys, q, kv, bufs,
+                              q_seq=qc.i32([0]), fused=True)
+        torch.cuda.synchronize()
+        pkg.check_decode_layer_error(bufs.layer_ws)
+        out.append(bufs)
+    _same_bits(out[0], out[1])
+    exact = orc.bf16_to_f64(keys_np[:, 0])
+    want = orc.select_blocks(exact, L, 4, 512)
+    assert np.array_equal(out[1].sel.cpu().numpy()[0], want)
+
+
 def test_decode_layer_full_size_batch4(Q):
     """The 1,048,320-token, batch-4 workload in the benchmark's launch
     configuration (default split count). The layer's inputs (pooled keys,
