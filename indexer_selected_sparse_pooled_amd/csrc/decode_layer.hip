@@ -62,6 +62,11 @@ void launch_lists_tpw(const IndexTopkArgs& a, int tpw, dim3 grid, hipStream_t s)
   }
 }
 
+// kKeys: the call gave no score buffer, so a query whose selection cannot
+// come from the chunk lists recomputes its scores from the keys (a separate
+// instance, so that the code of that fallback does not weigh on the
+// register allocation of the instance that reads stored scores).
+template <bool kKeys>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void attend_select_a(IndexTopkArgs it,
                                                                                        AttendArgs at) {
   __shared__ SelAttnLds sh;
@@ -107,15 +112,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     uint64_t my_bound = tid < nch ? b0 : 0ull;
     if (tid + itk::kNT < nch) my_bound = b1 > my_bound ? b1 : my_bound;
     if (!itk::select_registers(it, true, ukey, uidx, my_bound, sh.u.f, emit)) {
-      if (it.scores)
-        itk::select_streamed(it.scores + int64_t(i) * it.ld, n, topk, sh.u.f, emit);
-      else
+      if constexpr (kKeys)
         itk::select_streamed_keys(it, i, n, sh.u.f, emit);
+      else
+        itk::select_streamed(it.scores + int64_t(i) * it.ld, n, topk, sh.u.f, emit);
     }
-  } else if (it.scores) {
-    itk::final_select(it, i, n, sh.u.f, emit);
-  } else {  // no score buffer: the scores are recomputed from the keys
+  } else if constexpr (kKeys) {  // no score buffer: the scores are recomputed from the keys
     itk::select_streamed_keys(it, i, n, sh.u.f, emit);
+  } else {
+    itk::final_select(it, i, n, sh.u.f, emit);
   }
   __syncthreads();
   if (writer) {  // the query's selection, padded with -1
@@ -125,14 +130,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   att::attend_part<false, kLayerGT>(at, split, g, i, sh.u.a, (att::LdsIntPtr)(sh.sel), ns, actx, aseq);
 }
 
-// Work-groups of attend_select_a the current device holds at once.
+template __global__ void attend_select_a<false>(IndexTopkArgs, AttendArgs);
+template __global__ void attend_select_a<true>(IndexTopkArgs, AttendArgs);
+
+// Work-groups of attend_select_a (either instance) the current device holds
+// at once.
 int resident_groups() {
   static int cache[64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (cache[dev] == 0) {
-    int per_cu = 0, cus = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_select_a, 256, 0) != hipSuccess) per_cu = 0;
+    int per_cu = 0, per_cu_keys = 0, cus = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attend_select_a<false>, 256, 0) != hipSuccess) per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu_keys, attend_select_a<true>, 256, 0) != hipSuccess)
+      per_cu_keys = 0;
+    if (per_cu_keys < per_cu) per_cu = per_cu_keys;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) cus = 0;
     cache[dev] = per_cu * cus > 0 ? per_cu * cus : -1;
   }
@@ -203,7 +215,10 @@ hipError_t launch_decode_layer(IndexTopkArgs itk, AttendArgs att, const DecodeLa
   itk.chunk_blocks = 256 * p.itk.tpw;
   itk.keep = p.itk.keep;
   itk.wkeep = p.itk.wkeep;
-  hipLaunchKernelGGL(attend_select_a, dim3(unsigned(n_att_all)), dim3(256), 0, s, itk, att);
+  if (itk.scores)
+    hipLaunchKernelGGL(attend_select_a<false>, dim3(unsigned(n_att_all)), dim3(256), 0, s, itk, att);
+  else
+    hipLaunchKernelGGL(attend_select_a<true>, dim3(unsigned(n_att_all)), dim3(256), 0, s, itk, att);
   e = hipGetLastError();
   if (e != hipSuccess || merge_in) return e;
   // too many parts to be resident together: merge in a third launch

@@ -165,10 +165,13 @@ __device__ __forceinline__ float tile_scores(const u32x4 (&v)[16], int64_t tile0
 // (dot2 chains for bf16 keys, fp32 FMA chains over exact E4M3 values for
 // FP8 keys) and the same pairwise tree over the chunks as the scan's
 // butterfly (fp32 addition is commutative, so only the pairing matters).
-__device__ __noinline__ float key_score(const IndexTopkArgs& a, int i, int seq, int b) {
-  const uint16_t* q = a.q_idx + int64_t(i) * 128;
-  if (a.key_fp8) {
-    const uint8_t* kb = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
+// q: the query's 128 bf16 indexer values; keys: its sequence's key rows
+// (bf16) or FP8 pages (fp8). Plain values, not the argument struct: a
+// reference to the kernel's argument struct would make the caller copy it
+// to private memory.
+__device__ __noinline__ float key_score(const uint16_t* q, const void* keys, int fp8, int b) {
+  if (fp8) {
+    const uint8_t* kb = static_cast<const uint8_t*>(keys);
     const uint8_t* row = kb + fp8_code_off(b, 128);
     float p[8];
 #pragma unroll
@@ -202,7 +205,7 @@ __device__ __noinline__ float key_score(const IndexTopkArgs& a, int i, int seq, 
     const float sc = *reinterpret_cast<const float*>(kb + fp8_scale_off(b, 128));
     return (p[0] + p[1]) * sc;
   }
-  const uint16_t* row = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss + int64_t(b) * 128;
+  const uint16_t* row = static_cast<const uint16_t*>(keys) + int64_t(b) * 128;
   float p[16];
 #pragma unroll
   for (int c = 0; c < 16; c++) p[c] = dot8(ld16(row + 8 * c), ld16(q + 8 * c));
@@ -222,7 +225,11 @@ __device__ __noinline__ float key_score(const IndexTopkArgs& a, int i, int seq, 
 template <class Emit>
 __device__ void select_streamed_keys(const IndexTopkArgs& a, int i, int n, FinalLds& sh, Emit emit) {
   const int seq = a.q_seq ? a.q_seq[i] : 0;
-  auto key_at = [&](int j) { return order_key(key_score(a, i, seq, j)); };
+  const uint16_t* q = a.q_idx + int64_t(i) * 128;
+  const int64_t off = a.key_fp8 ? int64_t(seq) * a.keys_ss : int64_t(seq) * a.keys_ss * 2;
+  const void* keys = static_cast<const uint8_t*>(a.keys) + off;
+  const int fp8 = a.key_fp8;
+  auto key_at = [q, keys, fp8](int j) { return order_key(key_score(q, keys, fp8, j)); };
   uint32_t kstar;
   int need;
   stream_select<kNT>(key_at, n, a.topk, sh.st, kstar, need);
