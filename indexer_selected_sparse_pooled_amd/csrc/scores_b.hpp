@@ -34,7 +34,9 @@ __device__ __forceinline__ float dot8(u32x4 k, u32x4 q) {
 }
 
 // s[j]: the score of key tile_token(tile0, lane, j) of query i (sequence
-// seq, n keys); keys past n score 0.
+// seq, n keys, tile0 < n); keys past n score 0. Lanes whose key is past n
+// load key n - 1 instead (no branch per load, so all 16 loads are in
+// flight together) and their scores are dropped at the end.
 template <bool kFp8>
 __device__ __forceinline__ void tile_scores(const ScoreArgs& a, int i, int seq, int64_t n, int64_t tile0,
                                             float (&s)[2]) {
@@ -49,17 +51,26 @@ __device__ __forceinline__ void tile_scores(const ScoreArgs& a, int i, int seq, 
   }
   const uint16_t* kb = static_cast<const uint16_t*>(a.keys) + int64_t(seq) * a.keys_ss;
   const uint8_t* kb8 = static_cast<const uint8_t*>(a.keys) + int64_t(seq) * a.keys_ss;
-  float p[16][4];
+  const int64_t last = n - 1;
+  u32x4 kv[16];
+  u32x2 kc[16];
 #pragma unroll
   for (int k = 0; k < 16; k++) {
     const int64_t tok = tile0 + 8 * k + g;
-    u32x4 v = u32x4{0u, 0u, 0u, 0u};
-    if constexpr (kFp8) {
-      if (tok < n)
-        v = __builtin_bit_cast(u32x4, e4m3x8_bf16(*reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(tok, 64) + 8 * c)));
-    } else {
-      if (tok < n) v = ld16_nt(kb + tok * 64 + 8 * c);
-    }
+    const int64_t tc = tok < n ? tok : last;
+    if constexpr (kFp8)
+      kc[k] = *reinterpret_cast<const u32x2*>(kb8 + fp8_code_off(tc, 64) + 8 * c);
+    else
+      kv[k] = ld16_nt(kb + tc * 64 + 8 * c);
+  }
+  float p[16][4];
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    u32x4 v;
+    if constexpr (kFp8)
+      v = __builtin_bit_cast(u32x4, e4m3x8_bf16(kc[k]));
+    else
+      v = kv[k];
 #pragma unroll
     for (int h = 0; h < 4; h++) p[k][h] = dot8(v, qv[h]);
   }
@@ -99,9 +110,7 @@ __device__ __forceinline__ void tile_scores(const ScoreArgs& a, int i, int seq, 
     float v = 0.f;
 #pragma unroll
     for (int h = 0; h < 4; h++) v += w[h] * fmaxf(p[j][h], 0.f);
-    if constexpr (kFp8) {
-      if (tok < n) v *= *reinterpret_cast<const float*>(kb8 + fp8_scale_off(tok, 64));
-    }
+    if constexpr (kFp8) v *= *reinterpret_cast<const float*>(kb8 + fp8_scale_off(tok < n ? tok : last, 64));
     s[j] = tok < n ? v : 0.f;
   }
 }
