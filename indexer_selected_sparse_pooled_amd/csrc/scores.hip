@@ -11,6 +11,8 @@
 // is the weighted sum of the heads' ReLU'd dot products.
 // A prefill chunk (all queries in one sequence) uses MFMA 16x16x32 bf16
 // tiles: 16 queries x 16 keys x 32 dims per instruction.
+#include <cfloat>
+
 #include "common.hpp"
 #include "fp8.hpp"
 #include "kernels.hpp"
@@ -257,7 +259,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     __syncthreads();
     if (red[1] == 0) return;
   }
-  const int64_t step = a.tok_step > 0 ? a.tok_step : 1;
+  // (list mode never strides)
+  const int64_t step = kList ? 1 : (a.tok_step > 0 ? a.tok_step : 1);
   // a work-group covers 128 columns, or kListBatches x 128 in list mode
   const int64_t b00 = int64_t(blockIdx.x) * 128 * (kList ? kListBatches : 1);
   const int64_t nmax = (wg_max_n(a, q0, red) + step - 1) / step;  // in units of tok_step
@@ -330,8 +333,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][0], kb[0], acc, 0, 0, 0);
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[h][1], kb[1], acc, 0, 0, 0);
+      // ReLU as one med3 clamp to [0, FLT_MAX] (fmaxf would first
+      // canonicalise the MFMA result; the same for every finite dot); the
+      // sum starts at +0, so the sign of a zero never reaches a score
 #pragma unroll
-      for (int e = 0; e < 4; e++) acc_s[e] += wr[e][h] * fmaxf(acc[e], 0.f);
+      for (int e = 0; e < 4; e++) acc_s[e] += wr[e][h] * __builtin_amdgcn_fmed3f(acc[e], 0.f, FLT_MAX);
     }
 #pragma unroll
     for (int e = 0; e < 4; e++) sc[e] = acc_s[e] * k.sc;
@@ -343,8 +349,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   // lane group's ballot masks
   [[maybe_unused]] float thf[4];
   [[maybe_unused]] int thi[4], nrow32[4];
-  [[maybe_unused]] const uint64_t gmask = 0xFFFFull << (16 * kq);
-  [[maybe_unused]] const uint64_t gbelow = kq == 0 ? 0ull : (~0ull >> (64 - 16 * kq));
+  [[maybe_unused]] const uint32_t below16 = (1u << r) - 1u;  // lanes of the group below this one
+  [[maybe_unused]] const uint32_t gshift = 16u * kq;         // the group's bits in a ballot
   if constexpr (kList) {
 #pragma unroll
     for (int e = 0; e < 4; e++) {
@@ -360,8 +366,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   }
   // list mode: query row 16 wave + 4 kq + e belongs to the 16 lanes of group
   // kq of one wave; they stage its kept entries in LDS (ballot prefix, no
-  // atomics) and, when the stage is full and after the span, reserve list
-  // slots with one atomic and copy
+  // atomics) and, when the stage might not hold another tile's entries and
+  // after the span, reserve list slots with one atomic and copy
   [[maybe_unused]] auto flush = [&](int e) {
     const int q = q0 + 16 * wave + 4 * kq + e;
     const int row = 16 * wave + 4 * kq + e;
@@ -385,13 +391,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     for (int e = 0; e < 4; e++) {
       if constexpr (kList) {
         // keep the scores ranked at least as high as the query's threshold
-        // (score descending, index ascending; float order equals key order)
+        // (score descending, index ascending; float order equals key order);
+        // bitwise, not short-circuit, so no branch per test
+        // a tile adds at most 16 entries to the row; the test comes first so
+        // that no branch separates the ballot from the stores
+        if (staged[e] > kStage - 16) flush(e);  // rare; uniform in the group
         const int tk32 = int(tok);
-        const bool keep = tk32 < nrow32[e] && (sc[e] > thf[e] || (sc[e] == thf[e] && tk32 <= thi[e]));
-        const uint64_t bal = __ballot(keep);
-        const int c = __popcll(bal & gmask);                          // kept in the lane's group
-        const int before = __popcll(bal & lanes_below()) - __popcll(bal & gbelow);  // ... ahead of the lane
-        if (staged[e] + c > kStage) flush(e);  // rare; uniform in the group
+        const bool keep = (tk32 < nrow32[e]) & ((sc[e] > thf[e]) | ((sc[e] == thf[e]) & (tk32 <= thi[e])));
+        const uint64_t bal = __builtin_amdgcn_ballot_w64(keep);
+        const uint32_t g16 = uint32_t(bal >> gshift) & 0xFFFFu;  // the 16 ballot bits of the lane's group
+        const int c = __popc(g16);                                // kept in the lane's group
+        const int before = __popc(g16 & below16);                 // ... ahead of the lane
         if (keep)
           stage[16 * wave + 4 * kq + e][staged[e] + before] =
               (uint64_t(__float_as_uint(sc[e])) << 32) | uint64_t(uint32_t(tk32));
