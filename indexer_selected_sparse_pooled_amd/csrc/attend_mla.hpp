@@ -12,7 +12,7 @@
 // their 576-d queries in registers as MFMA A operands. The part's token list
 // is walked in tiles of 32 tokens:
 //   * the 32 latent rows go straight from global memory to LDS
-//     (global_load_lds_dwordx4) with a row stride of 73 x 16 bytes, so rows
+//     (global_load_lds_dwordx4) with a row stride of 74 x 16 bytes, so rows
 //     that are read together fall on different banks;
 //   * S = Q K^T on MFMA 16x16x32 bf16, B operands read from LDS (18 k-steps
 //     of 32 per 16-token half);
@@ -36,9 +36,17 @@ constexpr int kDK = 576;    // latent row (QK)
 constexpr int kDV = 512;    // V columns (first kDV of the row)
 constexpr int kTT = 32;     // tokens per tile
 constexpr int kRowC = kDK / 8;          // 16-byte chunks per latent row (72)
-constexpr int kRowL = kRowC + 1;        // LDS chunks per row incl. one pad chunk (73)
+// LDS chunks per row incl. two pad chunks (74). gfx950's LDS serves a
+// 16-byte read of 32 lanes per cycle from 128 four-byte banks: the 32
+// chunks must fall on distinct (chunk mod 32). The MFMA operand reads take
+// rows r = 0..15 at chunks c and c + 1 in one half-wave, and 74 r mod 32
+// (= 10 r) runs over 16 distinct even values, so the two columns never
+// meet; the transposed V reads (rows 4kq + r/4, 32 bytes each) land on 16
+// distinct multiples of 4 eight-byte units. With 73 both were 2-way
+// conflicts (measured: 49.6% of LDS cycles).
+constexpr int kRowL = kRowC + 2;
 constexpr int kNTPART = 256;             // threads of every shared-latent attention work-group
-constexpr int kTileC = kTT * kRowL;     // LDS chunks per tile (2336)
+constexpr int kTileC = kTT * kRowL;     // LDS chunks per tile (2368)
 constexpr int kPStr = kTT + 8;          // LDS row of P in elements (80 bytes)
 
 struct Lds {
@@ -270,8 +278,8 @@ __device__ __forceinline__ void sel_dma(const TLane& tl, const TList& ls, int t,
 // DMA of the latent rows of tile t into a buffer, tokens from its entries:
 // every lane first reads the token of each row it loads (all LDS reads
 // issued together), then issues its gathers. Slot s of wave w is s = w + 4j;
-// its chunks c = 64s + lane sit at (row, col) = (c / 73, c % 73), stepped
-// from slot to slot (256 chunks = 3 rows + 37 chunks). The lane index goes
+// its chunks c = 64s + lane sit at (row, col) = (c / kRowL, c % kRowL),
+// stepped from slot to slot (256 chunks = 3 rows + 34 chunks). The lane index goes
 // through an opaque copy first, so that the compiler recomputes these
 // offsets per tile instead of keeping all of them live (and spilling) across
 // the tile loop.
@@ -290,9 +298,9 @@ __device__ __forceinline__ void rows_dma(const TLane& tl, const TList& ls, int t
 #pragma unroll
   for (int j = 0; j < kSlotsPerWave; j++) {
     tok[j] = ls.tok(ent, row < n ? row : 0);  // rows past the tile's count (or the tile) repeat row 0
-    cc[j] = col < kRowC ? col : 0;             // the pad chunk takes a copy of chunk 0
-    col += 37;
-    row += 3;
+    cc[j] = col < kRowC ? col : 0;             // the pad chunks take a copy of chunk 0
+    col += 256 % kRowL;
+    row += 256 / kRowL;
     if (col >= kRowL) {
       col -= kRowL;
       row += 1;
