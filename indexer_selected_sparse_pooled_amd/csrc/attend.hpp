@@ -39,7 +39,17 @@ namespace att {
 constexpr int kTT = 64;          // token positions per tile
 constexpr int kG = 8;            // query heads per kv head
 constexpr int kD = 256;          // head dim of K and V
-constexpr int kPair = 1040;      // LDS bytes per pair of V rows (2 x 512 + 16: pairs 4 apart hit other banks)
+// LDS bytes per pair of V rows (2 x 512 + 32). gfx950's LDS has 128
+// four-byte banks; a transposed V read takes one row of each of 16
+// consecutive pairs (32 bytes each), and at 1056 bytes (132 eight-byte
+// units, 4 mod 64) the 16 pairs start on 16 distinct multiples of 4 units:
+// no conflicts. (The two rows of a pair, 512 bytes apart, always share
+// banks, so they are never read by the same instruction.)
+constexpr int kPair = 1056;
+// LDS position of token t of a tile in S and P: within each group of 8
+// tokens the even ones first (0 2 4 6 1 3 5 7), the order in which the
+// P V contraction takes them (see the V reads)
+__device__ __forceinline__ int tok_pos(int t) { return (t & ~7) | ((t & 7) >> 1) | ((t & 1) << 2); }
 constexpr unsigned kMergeSpinLimit = 1u << 24;  // polls while the parts of a merge arrive
 
 typedef short s16x4 __attribute__((ext_vector_type(4)));
@@ -321,11 +331,11 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
       const int rr = kRW * wave + 16 * b + r;
       if (kq < 2) {
 #pragma unroll
-        for (int e = 0; e < 4; e++) sh.s[4 * kq + e][rr] = rr < cnt ? acc[e] * sl2 : -INFINITY;
+        for (int e = 0; e < 4; e++) sh.s[4 * kq + e][tok_pos(rr)] = rr < cnt ? acc[e] * sl2 : -INFINITY;
       }
     }
     __syncthreads();
-    // online softmax: head h = tid / 32, 2 * GT consecutive tokens per thread
+    // online softmax: head h = tid / 32, 2 * GT consecutive positions per thread
     {
       constexpr int kE = 2 * GT;
       const int h = tid >> 5;
@@ -380,19 +390,21 @@ __device__ void attend_part(const AttendArgs& a, int split, int g, int i, Lds<GT
       }
 #pragma unroll
       for (int k2 = 0; k2 < kTok / 32; k2++) {
-        // A: P[head r][tokens 32*k2 + 8*kq .. +7] (rows 8..15 are zero)
+        // A: P[head r][positions 32*k2 + 8*kq .. +7] (rows 8..15 are zero)
         const bf16x8 ah = r < kG ? as_bf16x8(ld16(sh.phi + r * kPStr + 32 * k2 + 8 * kq)) : bf16x8{};
         const bf16x8 al8 = r < kG ? as_bf16x8(ld16(sh.plo + r * kPStr + 32 * k2 + 8 * kq)) : bf16x8{};
 #pragma unroll
         for (int nt = 0; nt < 4; nt++) {
-          // B: V[token 32*k2 + 8*kq + j][dim 64*wave + 16*nt + r], j = 0..7, as two
-          // transposed reads: lane (kq, r') addresses row 32*k2 + 8*kq + 4*h + r'/4,
-          // dims 64*wave + 16*nt + 4*(r'%4) .. +3
+          // B: V[token at position 32*k2 + 8*kq + j][dim 64*wave + 16*nt + r],
+          // j = 0..7, as two transposed reads: lane (kq, r') addresses row
+          // 32*k2 + 8*kq + 2*(r'/4) + h (the even tokens of the group, then
+          // the odd ones: the positions' order), dims 64*wave + 16*nt +
+          // 4*(r'%4) .. +3
           const int d0 = 64 * wave + 16 * nt + 4 * (r & 3);
           s16x4 t[2];
 #pragma unroll
           for (int hh = 0; hh < 2; hh++) {
-            const int row = 32 * k2 + 8 * kq + 4 * hh + (r >> 2);
+            const int row = 32 * k2 + 8 * kq + 2 * (r >> 2) + hh;
             const unsigned char* pa = sh.v + (row >> 1) * kPair + (row & 1) * 512 + 2 * d0;
             t[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)pa);
           }
