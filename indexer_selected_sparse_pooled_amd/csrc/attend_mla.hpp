@@ -48,6 +48,7 @@ constexpr int kRowL = kRowC + 2;
 constexpr int kNTPART = 256;             // threads of every shared-latent attention work-group
 constexpr int kTileC = kTT * kRowL;     // LDS chunks per tile (2368)
 constexpr int kPStr = kTT + 8;          // LDS row of P in elements (80 bytes)
+constexpr float kLazyMax = 8.f;         // log2 headroom of the transposed form's softmax reference
 
 struct Lds {
   __attribute__((aligned(16))) unsigned char kv[kTileC * 16];
@@ -356,9 +357,14 @@ __device__ __attribute__((always_inline)) inline void tile_t(
 #pragma unroll
   for (int j = 1; j < 8; j++) tm = fmaxf(tm, sv[j]);
   tm = rows_max(tm);
-  const float mn = fmaxf(m, tm);
+  // The reference m (the exponent offset of P, l and O) is raised only when
+  // the tile's maximum exceeds it by more than kLazyMax, so the rescale of
+  // O below is rare once a head's scores have been seen (weights up to
+  // 2^kLazyMax: fp32 sums and the hi + lo split of P are relative, so
+  // nothing is lost; the result O / l is independent of the reference).
+  const float mn = tm > m + kLazyMax ? tm : m;
   // (exp2 of the hardware: results below 2^-126, weights negligible next to
-  // the row maximum's 1, may flush to zero)
+  // the row maximum's, may flush to zero)
   float pv[8];
   float alpha = 1.f, ps = 0.f;
 #pragma unroll
@@ -382,8 +388,8 @@ __device__ __attribute__((always_inline)) inline void tile_t(
     bh[j] = (__bf16)pv[j];
     bl[j] = (__bf16)(pv[j] - float(bh[j]));
   }
-  // rescale (alpha belongs to the lane's head; it is 1 on every lane once
-  // the running maxima have settled, and then nothing is multiplied)
+  // rescale (alpha belongs to the lane's head; it is 1 on every lane unless
+  // some head's reference was raised, and then nothing is multiplied)
   if (__ballot(alpha != 1.f)) {
 #pragma unroll
     for (int nt = 0; nt < kDV / 16; nt++)
