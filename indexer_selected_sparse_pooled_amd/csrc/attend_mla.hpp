@@ -279,12 +279,21 @@ __device__ __forceinline__ void sel_dma(const TLane& tl, const TList& ls, int t,
 // DMA of the latent rows of tile t into a buffer, tokens from its entries:
 // every lane first reads the token of each row it loads (all LDS reads
 // issued together), then issues its gathers. Slot s of wave w is s = w + 4j;
-// its chunks c = 64s + lane sit at (row, col) = (c / kRowL, c % kRowL),
-// stepped from slot to slot (256 chunks = 3 rows + 34 chunks). The lane index goes
-// through an opaque copy first, so that the compiler recomputes these
-// offsets per tile instead of keeping all of them live (and spilling) across
-// the tile loop.
+// its chunk c = 64s + lane sits at (row, col) = (c / kRowL, c % kRowL), the
+// division by a multiply and shift (exact for every c used). Rows past the
+// tile's count repeat its last row and the pad chunks copy chunk 71 (both
+// are never read). The address is an unsigned 32 x 32 + 64 multiply-add
+// (tokens are clamped into [0, ctx) first). The lane index goes through an
+// opaque copy first, so that the compiler recomputes these offsets per tile
+// instead of keeping all of them live (and spilling) across the tile loop.
 constexpr int kSlotsPerWave = (kTileSlots + 3) / 4;  // 10 (wave w: slots w, w + 4, ...)
+constexpr uint32_t kRowDivM = (1u << 20) / kRowL + 1;
+constexpr bool row_div_exact() {
+  for (uint32_t c = 0; c < 4096; c++)
+    if (((c * kRowDivM) >> 20) != c / kRowL) return false;
+  return true;
+}
+static_assert(row_div_exact() && 64 * 4 * kSlotsPerWave <= 4096, "chunk index / kRowL by multiply and shift");
 
 __device__ __forceinline__ void rows_dma(const TLane& tl, const TList& ls, int t, const int* __restrict__ ent,
                                          unsigned char* __restrict__ buf, const uint16_t* kvbase,
@@ -293,25 +302,26 @@ __device__ __forceinline__ void rows_dma(const TLane& tl, const TList& ls, int t
   if (n == 0) return;
   int lane;
   asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(tl.lane));
-  const int c0 = 64 * tl.wave + lane;
-  int row = c0 / kRowL, col = c0 % kRowL;
-  int tok[kSlotsPerWave], cc[kSlotsPerWave];
+  const uint32_t c0 = uint32_t(64 * tl.wave + lane);
+  const unsigned char* gb = reinterpret_cast<const unsigned char*>(kvbase);
+  const uint32_t row_bytes = uint32_t(tok_stride) * 2u;
+  const int hi = ls.ctx - 1;
+  uint32_t tok[kSlotsPerWave], cb[kSlotsPerWave];
 #pragma unroll
   for (int j = 0; j < kSlotsPerWave; j++) {
-    tok[j] = ls.tok(ent, row < n ? row : 0);  // rows past the tile's count (or the tile) repeat row 0
-    cc[j] = col < kRowC ? col : 0;             // the pad chunks take a copy of chunk 0
-    col += 256 % kRowL;
-    row += 256 / kRowL;
-    if (col >= kRowL) {
-      col -= kRowL;
-      row += 1;
-    }
+    const uint32_t c = c0 + 256u * uint32_t(j);
+    const uint32_t row = (c * kRowDivM) >> 20;
+    const uint32_t col = c - uint32_t(kRowL) * row;
+    const int b = ent[int(row) < n - 1 ? int(row) : n - 1];
+    const int b0 = b > 0 ? b : 0;
+    tok[j] = uint32_t(b0 < hi ? b0 : hi);
+    cb[j] = 16u * (col < uint32_t(kRowC) ? col : uint32_t(kRowC - 1));
   }
 #pragma unroll
   for (int j = 0; j < kSlotsPerWave; j++) {
     const int s = tl.wave + 4 * j;
     if (64 * s + tl.lane < kTileC)
-      __builtin_amdgcn_global_load_lds(kvbase + int64_t(tok[j]) * tok_stride + 8 * cc[j],
+      __builtin_amdgcn_global_load_lds(gb + (uint64_t(tok[j]) * row_bytes + cb[j]),
                                        (__attribute__((address_space(3))) void*)(buf + 1024 * s), 16, 0, 0);
   }
 }
