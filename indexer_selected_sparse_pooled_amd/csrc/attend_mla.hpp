@@ -25,6 +25,8 @@
 // Output: normalised partial O (fp32) and natural-log lse per head.
 #pragma once
 
+#include <cfloat>
+
 #include "attend.hpp"
 #include "fp8.hpp"
 
@@ -233,11 +235,14 @@ struct LdsT {
   int cnt[kNTPART / 64];
 };
 
+// max of a and b, both finite or -inf, as one med3 against FLT_MAX (fmaxf
+// would first canonicalise both operands of the lane swap)
+__device__ __forceinline__ float max2(float a, float b) { return __builtin_amdgcn_fmed3f(a, b, FLT_MAX); }
 __device__ __forceinline__ float rows_max(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  v = max2(__uint_as_float(a[0]), __uint_as_float(a[1]));
   auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  return max2(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 __device__ __forceinline__ float rows_sum(float v) {
   auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -356,17 +361,28 @@ __device__ __attribute__((always_inline)) inline void tile_t(
       acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[1][(ks - 1) % 2], qa[ks - 1], acc[1], 0, 0, 0);
     }
   }
-  // online softmax of head r over the tile's tokens 4kq + e (acc[0]) and 16 + 4kq + e (acc[1])
+  // online softmax of head r over the tile's tokens 4kq + e (acc[0]) and
+  // 16 + 4kq + e (acc[1]); the scores stay unscaled until the exponent
+  // (exp2(s * sl2 - m) as one fma; sl2 > 0, so the maximum commutes with
+  // the scaling), and positions past the list are masked in the query's
+  // last tile only
   float sv[8];
 #pragma unroll
   for (int e = 0; e < 4; e++) {
-    sv[e] = 4 * kq + e < cnt ? acc[0][e] * sl2 : -INFINITY;
-    sv[4 + e] = 16 + 4 * kq + e < cnt ? acc[1][e] * sl2 : -INFINITY;
+    sv[e] = acc[0][e];
+    sv[4 + e] = acc[1][e];
   }
-  float tm = sv[0];
+  if (cnt < kTT) {
 #pragma unroll
-  for (int j = 1; j < 8; j++) tm = fmaxf(tm, sv[j]);
-  tm = rows_max(tm);
+    for (int e = 0; e < 4; e++) {
+      sv[e] = 4 * kq + e < cnt ? sv[e] : -INFINITY;
+      sv[4 + e] = 16 + 4 * kq + e < cnt ? sv[4 + e] : -INFINITY;
+    }
+  }
+  float tm = max2(sv[0], sv[1]);
+#pragma unroll
+  for (int j = 2; j < 8; j++) tm = max2(tm, sv[j]);
+  tm = rows_max(tm) * sl2;
   // The reference m (the exponent offset of P, l and O) is raised only when
   // the tile's maximum exceeds it by more than kLazyMax, so the rescale of
   // O below is rare once a head's scores have been seen (weights up to
@@ -383,7 +399,7 @@ __device__ __attribute__((always_inline)) inline void tile_t(
     alpha = __builtin_amdgcn_exp2f(m - mn);
 #pragma unroll
     for (int j = 0; j < 8; j++) {
-      pv[j] = __builtin_amdgcn_exp2f(sv[j] - mn);
+      pv[j] = __builtin_amdgcn_exp2f(fmaf(sv[j], sl2, -mn));
       ps += pv[j];
     }
   }
