@@ -3,11 +3,13 @@
 // context is computed separately and the partial results are combined with
 // log-sum-exp; "3090x3で 314 万コンテキスト", section "ちなみにこの欠点":
 // prefill merges the softmax partials of consecutive history tiles.
-// One wave per output row; each lane owns 4 consecutive dims per 256. The
-// row's lse values are wave-uniform (scalar loads), so every lane computes
-// the partials' weights itself, with no cross-lane step, and a batch of PB
-// partials (O rows and lse values) is loaded before any of it is used: a
-// merge of up to PB partials costs one memory round trip.
+// One wave per 256 dims of an output row (a row of dv dims is `pieces` =
+// ceil(dv / 256) waves, so a small merge still spreads over the chip); each
+// lane owns 4 consecutive dims. The row's lse values are wave-uniform
+// (scalar loads), so every lane computes the partials' weights itself, with
+// no cross-lane step, and a batch of PB partials (O pieces and lse values)
+// is loaded before any of it is used: a merge of up to PB partials costs
+// one memory round trip. The first piece of a row writes its lse.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -15,18 +17,21 @@ namespace qsa {
 namespace {
 
 template <int ND, int PB>
-__global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, int dv,
+__global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, int dv, int pieces,
                                                     const float* __restrict__ o, int64_t ops,
                                                     const float* __restrict__ l, int64_t lps,
                                                     float* __restrict__ oo, uint16_t* __restrict__ ob,
                                                     float* __restrict__ lo) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = int64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int64_t w = int64_t(blockIdx.x) * 4 + __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+  const int64_t row = w / pieces;
+  const int piece = int(w - row * pieces);
   if (row >= rows) return;
+  const int dbase = 256 * ND * piece;  // the wave's first dim
   bool in[ND];
 #pragma unroll
-  for (int c = 0; c < ND; c++) in[c] = 256 * c + 4 * lane < dv;
-  const float* src0 = o + row * dv + 4 * lane;
+  for (int c = 0; c < ND; c++) in[c] = dbase + 256 * c + 4 * lane < dv;
+  const float* src0 = o + row * dv + dbase + 4 * lane;
   f32x4 acc[ND];
 #pragma unroll
   for (int c = 0; c < ND; c++) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -66,7 +71,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, in
   const float inv = tot > 0.f ? 1.f / tot : 0.f;
 #pragma unroll
   for (int c = 0; c < ND; c++) {
-    const int d0 = 256 * c + 4 * lane;
+    const int d0 = dbase + 256 * c + 4 * lane;
     if (!in[c]) continue;
     const f32x4 r = acc[c] * inv;
     if (oo) *reinterpret_cast<f32x4*>(oo + row * dv + d0) = r;
@@ -77,7 +82,7 @@ __global__ __launch_bounds__(256) void merge_kernel(int n_part, int64_t rows, in
       *reinterpret_cast<u32x2*>(ob + row * dv + d0) = pk;
     }
   }
-  if (lane == 0 && lo) lo[row] = tot > 0.f ? mx + logf(tot) : -INFINITY;
+  if (lane == 0 && piece == 0 && lo) lo[row] = tot > 0.f ? mx + logf(tot) : -INFINITY;
 }
 
 }  // namespace
@@ -86,17 +91,10 @@ hipError_t launch_merge(int n_part, int64_t rows, int dv, const float* o_parts, 
                         const float* lse_parts, int64_t l_ps, float* o_out, uint16_t* o_bf16,
                         float* lse_out, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
-  const dim3 grid(unsigned((rows + 3) / 4));
-  const int nd = (dv + 255) / 256;
-  if (nd == 1)
-    hipLaunchKernelGGL((merge_kernel<1, 16>), grid, dim3(256), 0, s, n_part, rows, dv, o_parts, o_ps, lse_parts,
-                       l_ps, o_out, o_bf16, lse_out);
-  else if (nd == 2)
-    hipLaunchKernelGGL((merge_kernel<2, 8>), grid, dim3(256), 0, s, n_part, rows, dv, o_parts, o_ps, lse_parts,
-                       l_ps, o_out, o_bf16, lse_out);
-  else
-    hipLaunchKernelGGL((merge_kernel<4, 4>), grid, dim3(256), 0, s, n_part, rows, dv, o_parts, o_ps, lse_parts,
-                       l_ps, o_out, o_bf16, lse_out);
+  const int pieces = (dv + 255) / 256;
+  const dim3 grid(unsigned((rows * pieces + 3) / 4));
+  hipLaunchKernelGGL((merge_kernel<1, 16>), grid, dim3(256), 0, s, n_part, rows, dv, pieces, o_parts, o_ps,
+                     lse_parts, l_ps, o_out, o_bf16, lse_out);
   return hipGetLastError();
 }
 
