@@ -149,6 +149,7 @@ struct RegSelLds {
   int pg[64], pe[64];  // register-major positions: counts per (register, wave)
   uint32_t cand[kRegSelCand + 64];
   uint32_t n_cand[1 + 64];
+  int eqmx[NT / 64];  // (kAgg) per wave: keys equal to the largest
   uint32_t res_key;
   int res_need;
   int tau_slot;
@@ -160,7 +161,9 @@ struct RegSelLds {
 // threshold to one bin; as soon as that bin holds at most kRegSelCand keys,
 // they are gathered in LDS and wave 0 settles the remaining low bits.
 // kAgg: histogram increments go through hist_add (worth its extra
-// instructions where many keys are equal, e.g. scores that are exact zeros).
+// instructions where many keys are equal, e.g. scores that are exact zeros),
+// and the first pass also counts the keys equal to the largest: with k or
+// more of them the threshold is found without further passes.
 template <int NT, int R, bool kAgg = false>
 __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>& sh, uint32_t& kstar, int& need) {
   constexpr int NW = NT / 64;
@@ -214,7 +217,28 @@ __device__ void regsel_threshold(const uint32_t (&key)[R], int k, RegSelLds<NT>&
       else
         atomicAdd(&h[in ? (key[r] >> shift) & dmask : 256u + lane], 1u);
     }
+    if constexpr (kAgg) {
+      if (pass == 0) {  // keys equal to the largest (many equal keys: e.g. exact-zero scores)
+        int eq = 0;
+#pragma unroll
+        for (int r = 0; r < R; r++) eq += key[r] == mx ? 1 : 0;
+        eq = wave_incl_sum(eq);
+        if (lane == 63) sh.eqmx[wave] = eq;
+      }
+    }
     __syncthreads();
+    if constexpr (kAgg) {
+      if (pass == 0) {  // at least k of them: the threshold is the largest key itself
+        int te = 0;
+#pragma unroll
+        for (int w = 0; w < NW; w++) te += sh.eqmx[w];
+        if (te >= k) {
+          kstar = mx;
+          need = k;
+          return;
+        }
+      }
+    }
     // every wave finds the digit (same result everywhere): lane holds the
     // bins 255 - 4*lane - e, e = 0..3, i.e. digits in descending order
     int cnt[4];
