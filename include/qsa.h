@@ -544,9 +544,13 @@ qsa_status qsa_sparse_prefill(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* at
  *     the merged output is also written as bf16.
  *   Tiles merge in call order: issue them on one stream. Equal to
  *   qsa_sparse_prefill per tile followed by qsa_lse_merge up to rounding.
- *   Pooled-block variant only (16 / 2 heads, head dim 256, bf16 K/V rows);
- *   otherwise QSA_ERR_UNSUPPORTED. Other arguments and errors as
- *   qsa_sparse_prefill. */
+ *   Pooled-block variant (16 / 2 heads, head dim 256, bf16 K/V rows); and
+ *   the shared latent (64 heads, dk 576, dv 512, block 1, bf16 rows) for a
+ *   call that is both first and last (the whole history in one tile: the
+ *   attention's result is final, written with its bf16 copy in the same
+ *   launch, identical to qsa_sparse_prefill followed by a one-partial
+ *   qsa_lse_merge); otherwise QSA_ERR_UNSUPPORTED. Other arguments and
+ *   errors as qsa_sparse_prefill. */
 qsa_status qsa_sparse_prefill_merge(const qsa_sel_cfg* sel_cfg, const qsa_attn_cfg* attn_cfg,
                                     int32_t nq, const int32_t* q_seq, const int32_t* q_ctx,
                                     int32_t max_ctx, const qsa_bf16* q, const qsa_kv* kv,

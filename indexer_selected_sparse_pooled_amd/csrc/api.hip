@@ -931,10 +931,14 @@ qsa_status qsa_sparse_prefill_merge(const qsa_sel_cfg* sel_cfg, const qsa_attn_c
                                     qsa_bf16* o_out_bf16, qsa_stream_t stream) {
   qsa_status st = check_attn(sel_cfg, attn_cfg, nq, q_ctx, max_ctx, q, kv, sel, n_sel, o_run, lse_run);
   if (st != QSA_OK) return st;
-  if (attn_cfg->hq != 16 || attn_cfg->hkv != 2 || attn_cfg->dk != 256 || attn_cfg->dv != 256 ||
-      kv->format != QSA_KV_BF16)
+  const bool pooled = attn_cfg->hq == 16 && attn_cfg->hkv == 2 && attn_cfg->dk == 256 && attn_cfg->dv == 256;
+  // the shared latent (token-level selection, bf16 rows): a single tile only
+  const bool latent_single = attn_cfg->hq == 64 && attn_cfg->hkv == 1 && attn_cfg->dk == 576 &&
+                             attn_cfg->dv == 512 && sel_cfg->block == 1 && first && last;
+  if (!(pooled || latent_single) || kv->format != QSA_KV_BF16)
     return fail(QSA_ERR_UNSUPPORTED, "the running tile merge covers the pooled-block variant (16 / 2 heads, "
-                                     "head dim 256, bf16 rows)");
+                                     "head dim 256) and a single-tile call of the shared latent (64 heads, "
+                                     "576 / 512, token-level selection), with bf16 rows");
   if (tile_begin < 0 || tile_end < tile_begin) return fail(QSA_ERR_ARG, "bad tile range");
   if (tile_begin % sel_cfg->block) return fail(QSA_ERR_ARG, "tile_begin must be a multiple of block");
   if (tile_end % sel_cfg->block && tile_end < max_ctx)

@@ -535,6 +535,19 @@ __device__ __attribute__((always_inline)) inline void attend_part_t(const Attend
   for (int nt = 0; nt < kDV / 16; nt++)
     *reinterpret_cast<f32x4*>(op + 16 * nt) = f32x4{o[nt][0] * inv, o[nt][1] * inv, o[nt][2] * inv, o[nt][3] * inv};
   if (kq == 0) a.lse_part[orow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+  // the only tile of a prefill (first and last of a running merge): the
+  // result is final, and its bf16 copy is written here (what a merge of
+  // this single partial would produce: the same value, rounded the same way)
+  if (a.acc == 7 && a.o_bf16) {
+    uint16_t* ob = a.o_bf16 + orow * kDV + 4 * kq;
+#pragma unroll
+    for (int nt = 0; nt < kDV / 16; nt++) {
+      u32x2 pk;
+      pk[0] = uint32_t(f32_to_bf16(o[nt][0] * inv)) | (uint32_t(f32_to_bf16(o[nt][1] * inv)) << 16);
+      pk[1] = uint32_t(f32_to_bf16(o[nt][2] * inv)) | (uint32_t(f32_to_bf16(o[nt][3] * inv)) << 16);
+      *reinterpret_cast<u32x2*>(ob + 16 * nt) = pk;
+    }
+  }
 }
 
 // ---- FP8 latent rows

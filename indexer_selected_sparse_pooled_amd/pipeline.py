@@ -201,6 +201,15 @@ def history_tiles(ctx_max: int, tile: int):
     return [(a, min(a + tile, ctx_max)) for a in range(0, ctx_max, tile)]
 
 
+def single_tile_final(sel_cfg, attn_cfg, kv, n_tiles) -> bool:
+    """Whether a chunk whose whole history is one tile takes its final
+    result (O, lse and the bf16 copy) straight from the attention launch
+    (qsa_sparse_prefill_merge as first and last tile): the shared latent with
+    token-level selection and bf16 rows. No partials and no merge pass."""
+    return (n_tiles == 1 and (attn_cfg.hq, attn_cfg.hkv, attn_cfg.dk, attn_cfg.dv) == (64, 1, 576, 512)
+            and sel_cfg.block == 1 and kv.format == qsa.KV_BF16)
+
+
 def running_tile_merge(attn_cfg) -> bool:
     """Whether qsa_sparse_prefill_merge covers this attention (the
     pooled-block variant): a chunk can then merge its history tiles as they
@@ -238,7 +247,9 @@ def prefill_chunk(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: P
     """A chunk of queries of one sequence: selection, then the history tiles
     in the outer loop (one attention call per tile), then the merge of the
     per-tile partials; with running_merge (pooled-block variant), each tile
-    is merged into the running result as it completes instead. The
+    is merged into the running result as it completes instead; a
+    shared-latent chunk with one tile writes its result from the attention
+    (single_tile_final). The
     token-level indexer selects in one call (qsa_index_topk_prefill) unless
     fused_select is False."""
     if fused_select and bufs.sel_ws is not None:
@@ -256,6 +267,11 @@ def prefill_chunk(sel_cfg, attn_cfg, q_ctx, max_ctx, q_idx, keys, q, kv, bufs: P
         for t, (a, b) in enumerate(bufs.tiles):
             qsa.qsa_sparse_prefill_merge(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, a, b,
                                          t == 0, t == last, bufs.o, bufs.lse, o_out_bf16=bufs.o_bf16, stream=stream)
+        return
+    if single_tile_final(sel_cfg, attn_cfg, kv, len(bufs.tiles)):
+        a, b = bufs.tiles[0]
+        qsa.qsa_sparse_prefill_merge(sel_cfg, attn_cfg, q_ctx, max_ctx, q, kv, bufs.sel, bufs.n_sel, a, b,
+                                     True, True, bufs.o, bufs.lse, o_out_bf16=bufs.o_bf16, stream=stream)
         return
     if bufs.o_tiles.shape[0] != len(bufs.tiles):
         raise ValueError("prefill_buffers(..., partials=True) is needed for this attention")

@@ -6,8 +6,9 @@ the C ABI, against the oracle.
 Cases: attention on given selections with several split counts (full
 attention at ctx <= 2048, one token, an empty context), the decode layer end
 to end (scores, top-2048, attention, merge) through the separate calls and
-through one qsa_decode_layer_latent call, and a tiled prefill chunk whose
-result must not depend on the tile size.
+through one qsa_decode_layer_latent call, a tiled prefill chunk whose
+result must not depend on the tile size, and the single-tile chunk whose
+result comes straight from the attention launch.
 """
 import numpy as np
 import pytest
@@ -186,3 +187,39 @@ def test_mla_prefill_chunk_tiled(Q, tile):
         r = orc.decode_query(q[i], q_idx[i], keys, latent, latent, ctxs[i], block=1, topk=2048, scale=SCALE,
                              w_idx=w[i], dv=512)
         qc.check_row(sel[i], n_sel[i], o[i], lse[i], ob[i], r, ctxs[i], 1, 2048, q[i], latent, latent, SCALE, dv=512)
+
+
+def test_mla_prefill_single_tile_final(Q):
+    """A chunk whose history is one tile takes O, lse and the bf16 copy
+    straight from the attention (qsa_sparse_prefill_merge, first and last):
+    bit for bit the result of qsa_sparse_prefill followed by a one-partial
+    qsa_lse_merge. A shared-latent call that is not both first and last is
+    refused."""
+    pkg, pipeline = Q
+    hist, nq = 5000, 24
+    ctx_max = hist + nq
+    _print_case("mla_prefill_single_tile", hist=hist, nq=nq)
+    seed = 64
+    latent = qc.bits(seed, 1, (ctx_max, 1, 576))
+    keys = qc.bits(seed, 2, (ctx_max, 64))
+    q = qc.to_dev(qc.bits(seed, 3, (nq, 64, 576)))
+    q_idx = qc.to_dev(qc.bits(seed, 4, (nq, 4, 64)))
+    w = torch.tensor(np.stack([qi.uniform_f32(seed, 100 + i, 4) for i in range(nq)]), device="cuda")
+    q_ctx = qc.i32([hist + i + 1 for i in range(nq)])
+    lat = qc.to_dev(latent[None])
+    kv = pkg.make_kv(lat, lat)
+    bufs = pipeline.prefill_buffers(pkg.SEL_B, pkg.ATTN_B, nq, ctx_max, ctx_max)
+    assert len(bufs.tiles) == 1 and pipeline.single_tile_final(pkg.SEL_B, pkg.ATTN_B, kv, 1)
+    pipeline.prefill_chunk(pkg.SEL_B, pkg.ATTN_B, q_ctx, ctx_max, q_idx, qc.to_dev(keys[None]), q, kv, bufs, w_idx=w)
+    torch.cuda.synchronize()
+    one = {k: getattr(bufs, k).clone() for k in ("o", "lse", "o_bf16")}
+    a0, a1 = bufs.tiles[0]
+    pkg.qsa_sparse_prefill(pkg.SEL_B, pkg.ATTN_B, q_ctx, ctx_max, q, kv, bufs.sel, bufs.n_sel, a0, a1,
+                           bufs.o_tiles[0], bufs.lse_tiles[0])
+    pkg.qsa_lse_merge(bufs.o_tiles, bufs.lse_tiles, o_out=bufs.o, o_out_bf16=bufs.o_bf16, lse_out=bufs.lse)
+    torch.cuda.synchronize()
+    for k, v in one.items():
+        assert torch.equal(v, getattr(bufs, k)), k
+    with pytest.raises(pkg.QsaError):
+        pkg.qsa_sparse_prefill_merge(pkg.SEL_B, pkg.ATTN_B, q_ctx, ctx_max, q, kv, bufs.sel, bufs.n_sel, a0, a1,
+                                     True, False, bufs.o, bufs.lse)
