@@ -261,10 +261,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   }
   // (list mode never strides)
   const int64_t step = kList ? 1 : (a.tok_step > 0 ? a.tok_step : 1);
-  // a work-group covers 128 columns, or kListBatches x 128 in list mode
-  const int64_t b00 = int64_t(blockIdx.x) * 128 * (kList ? kListBatches : 1);
+  // a span is 128 columns, or kListBatches x 128 in list mode; work-group x
+  // covers spans x, x + gridDim.x, ... (one span each unless the launch
+  // narrows the grid)
+  const int64_t span = 128 * (kList ? kListBatches : 1);
   const int64_t nmax = (wg_max_n(a, q0, red) + step - 1) / step;  // in units of tok_step
-  if (b00 >= nmax) return;
+  if (int64_t(blockIdx.x) * span >= nmax) return;
   [[maybe_unused]] __shared__ uint64_t stage[kList ? 64 : 1][kList ? kStage : 1];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int r = lane & 15, kq = lane >> 4;
@@ -291,6 +293,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     for (int h = 0; h < 4; h++) wr[e][h] = q < a.nq ? a.w_idx[int64_t(q) * 4 + h] : 0.f;
     if constexpr (kList) th[e] = q < a.nq ? a.theta[q] : ~0ull;
   }
+  for (int64_t b00 = int64_t(blockIdx.x) * span; b00 < nmax; b00 += int64_t(gridDim.x) * span) {
   // Column tiles t = 0 .. T-1 of the span (tokens b00 + 16 t + r); the key
   // rows of tile t + 2 are fetched before tile t is computed, so loads stay
   // two tiles ahead of the MFMAs. Columns past nmax read a valid row (the
@@ -433,6 +436,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     for (int e = 0; e < 4; e++)
       if (staged[e] > 0) flush(e);
   }
+  }  // spans
 }
 
 }  // namespace
@@ -441,6 +445,10 @@ hipError_t launch_scores_gemm_b(const ScoreArgs& a, int64_t n_cols, bool lists, 
   if (a.nq <= 0 || n_cols <= 0) return hipSuccess;
   const int64_t span = 128 * (lists ? kListBatches : 1);
   dim3 grid(unsigned((n_cols + span - 1) / span), unsigned((a.nq + 63) / 64));
+  // a pass over flagged queries only: few work-groups per query tile, each
+  // walking many spans, so that a pass with nothing flagged (the usual case)
+  // costs a small grid of work-groups that exit at once
+  if (a.only && grid.x > 64) grid.x = 64;
   if (lists) {
     if (a.key_fp8)
       hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<true, true>), grid, dim3(256), 0, s, a);
@@ -491,11 +499,7 @@ hipError_t launch_scores(const ScoreArgs& a, hipStream_t s) {
     }
   } else {
     if (chunk) {
-      dim3 grid(unsigned((nmax + 127) / 128), unsigned((a.nq + 63) / 64));
-      if (a.key_fp8)
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<true, false>), grid, dim3(256), 0, s, a);
-      else
-        hipLaunchKernelGGL(HIP_KERNEL_NAME(scores_gemm_b<false, false>), grid, dim3(256), 0, s, a);
+      return launch_scores_gemm_b(a, nmax, false, s);
     } else {
       dim3 grid(unsigned((nmax + 511) / 512), unsigned(a.nq));
       if (a.key_fp8)
