@@ -345,20 +345,27 @@ __device__ __attribute__((always_inline)) inline void tile_t(
   rows_dma(tl, ls, t + 1, ent_next, nxt, kvbase, tok_stride);
   sel_dma(tl, ls, t + 2, ent_free);
   const int cnt = ls.cnt(t);
-  // S^T for the two 16-token halves, K operands read one k-step ahead
+  // S^T for the two 16-token halves, K operands read two k-steps ahead (the
+  // group barriers keep the reads ahead of the MFMAs; left to itself the
+  // compiler, short of registers, reads each operand just before its MFMA
+  // and waits a full LDS latency at every k-step)
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   const unsigned char* krow0 = cur + (r * kRowL + kq) * 16;
   const unsigned char* krow1 = cur + ((16 + r) * kRowL + kq) * 16;
-  bf16x8 kb[2][2];
+  constexpr int kPD = 2;
+  bf16x8 kb[2][kPD + 1];
 #pragma unroll
-  for (int ks = 0; ks < kDK / 32 + 1; ks++) {
+  for (int ks = 0; ks < kDK / 32 + kPD; ks++) {
     if (ks < kDK / 32) {
-      kb[0][ks % 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 64 * ks));
-      kb[1][ks % 2] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 64 * ks));
+      kb[0][ks % (kPD + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 64 * ks));
+      kb[1][ks % (kPD + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 64 * ks));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
-    if (ks >= 1) {
-      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[0][(ks - 1) % 2], qa[ks - 1], acc[0], 0, 0, 0);
-      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[1][(ks - 1) % 2], qa[ks - 1], acc[1], 0, 0, 0);
+    if (ks >= kPD) {
+      const int k = ks - kPD;
+      acc[0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[0][k % (kPD + 1)], qa[k], acc[0], 0, 0, 0);
+      acc[1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb[1][k % (kPD + 1)], qa[k], acc[1], 0, 0, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
     }
   }
   // online softmax of head r over the tile's tokens 4kq + e (acc[0]) and
@@ -428,14 +435,35 @@ __device__ __attribute__((always_inline)) inline void tile_t(
   // 16+4kq+3][dim 16nt + r]
   const unsigned char* va = cur + (4 * kq + (r >> 2)) * kRowL * 16 + 8 * (r & 3);
   const unsigned char* vb = va + 16 * kRowL * 16;
+  // two n-tiles at a time; the next pair's reads are issued before this
+  // pair's MFMAs, so they complete while those run
+  constexpr int kNP = kDV / 32;  // pairs of n-tiles
+  s16x4 tv[2][2][2];             // [buffer][n-tile of the pair][read]
+  auto load_pair = [&](int np, s16x4 (&t)[2][2]) {
 #pragma unroll
-  for (int nt = 0; nt < kDV / 16; nt++) {
-    const s16x4 t0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 32 * nt));
-    const s16x4 t1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + 32 * nt));
-    const bf16x8 av = __builtin_bit_cast(bf16x8, __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7));
-    o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, o[nt], 0, 0, 0);
-    o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, o[nt], 0, 0, 0);
-    if (nt % 4 == 3) __builtin_amdgcn_sched_barrier(0);  // reads in flight: 4 n-tiles (registers)
+    for (int j = 0; j < 2; j++) {
+      const int nt = 2 * np + j;
+      t[j][0] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(va + 32 * nt));
+      t[j][1] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4*)(vb + 32 * nt));
+    }
+  };
+#pragma unroll
+  for (int np = 0; np < kNP + 1; np++) {
+    if (np < kNP) {
+      load_pair(np, tv[np & 1]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+    }
+    if (np >= 1) {
+#pragma unroll
+      for (int j = 0; j < 2; j++) {
+        const int nt = 2 * (np - 1) + j;
+        const bf16x8 av = __builtin_bit_cast(
+            bf16x8, __builtin_shufflevector(tv[(np - 1) & 1][j][0], tv[(np - 1) & 1][j][1], 0, 1, 2, 3, 4, 5, 6, 7));
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl, o[nt], 0, 0, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+    }
   }
 }
 
