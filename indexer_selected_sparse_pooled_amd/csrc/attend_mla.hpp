@@ -50,7 +50,7 @@ constexpr int kRowL = kRowC + 2;
 constexpr int kNTPART = 256;             // threads of every shared-latent attention work-group
 constexpr int kTileC = kTT * kRowL;     // LDS chunks per tile (2368)
 constexpr int kPStr = kTT + 8;          // LDS row of P in elements (80 bytes)
-constexpr float kLazyMax = 8.f;         // log2 headroom of the transposed form's softmax reference
+constexpr float kLazyMax = 8.f;         // log2 headroom of a head's softmax reference (bf16 and FP8 rows)
 
 struct Lds {
   __attribute__((aligned(16))) unsigned char kv[kTileC * 16];
@@ -728,7 +728,8 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
       const float s0 = r < cnt ? acc[0][e] * sl2 : -INFINITY;
       const float s1 = 16 + r < cnt ? acc[1][e] * sl2 : -INFINITY;
       const float tm = row16_max(fmaxf(s0, s1));
-      const float mn = fmaxf(m[e], tm);
+      // the reference is raised only past kLazyMax (as in the bf16 form)
+      const float mn = tm > m[e] + kLazyMax ? tm : m[e];
       float p0 = 0.f, p1 = 0.f;
       alpha[e] = 1.f;
       if (mn != -INFINITY) {
@@ -742,10 +743,12 @@ __device__ void attend_part_fp8(const AttendArgs& a, int split, int i, LdsF8& sh
       pl[2 * e] = p0;  // kept in LDS (the lane's own slot) for the four groups below
       pl[2 * e + 1] = p1;
     }
+    if (__ballot(alpha[0] != 1.f || alpha[1] != 1.f || alpha[2] != 1.f || alpha[3] != 1.f)) {
 #pragma unroll
-    for (int nt = 0; nt < kDV / 16; nt++)
+      for (int nt = 0; nt < kDV / 16; nt++)
 #pragma unroll
-      for (int e = 0; e < 4; e++) o[nt][e] *= alpha[e];
+        for (int e = 0; e < 4; e++) o[nt][e] *= alpha[e];
+    }
     // O += P' V, one 128-column group at a time
     const unsigned char* vb0 = sh.kv + (8 * kq + (r >> 2)) * kRowL * 16 + 8 * (r & 3);
 #pragma unroll
