@@ -268,9 +268,14 @@ def test_decode_splits_match_oracle_partials(Q):
         qc.check_attention(o_part[j, 0].cpu().numpy(), lse_part[j, 0].cpu().numpy(), o_ref, lse_ref)
 
 
-def test_merge_against_oracle(Q):
+@pytest.mark.parametrize("P,dv", [(7, 256), (33, 512), (7, 300), (20, 36)])
+def test_merge_against_oracle(Q, P, dv):
+    """Rows of 256, 512 (two 256-dim pieces per row), 300 (a partial second
+    piece) and 36 dims; more partials than one batch of 16; an all-empty
+    row; the bf16 copy equals the fp32 result rounded to bf16."""
     pkg, _ = Q
-    P, rows, dv = 7, 33, 256
+    rows = 33
+    _print_case("merge", P=P, dv=dv)
     rng = np.random.default_rng(3)
     o = rng.standard_normal((P, rows, dv)).astype(np.float32)
     lse = (rng.standard_normal((P, rows)) * 3).astype(np.float32)
@@ -278,10 +283,13 @@ def test_merge_against_oracle(Q):
     lse[:, 5] = -np.inf
     o[:, 5] = 0
     out = torch.empty(rows, dv, device="cuda")
+    out_b = torch.empty(rows, dv, dtype=torch.bfloat16, device="cuda")
     out_l = torch.empty(rows, device="cuda")
-    pkg.qsa_lse_merge(torch.tensor(o, device="cuda"), torch.tensor(lse, device="cuda"), o_out=out, lse_out=out_l)
+    pkg.qsa_lse_merge(torch.tensor(o, device="cuda"), torch.tensor(lse, device="cuda"), o_out=out, o_out_bf16=out_b,
+                      lse_out=out_l)
     ref_o, ref_l = orc.lse_merge(o, lse)
     got_o, got_l = out.cpu().numpy(), out_l.cpu().numpy()
+    assert torch.equal(out_b, out.to(torch.bfloat16))
     assert np.isneginf(got_l[5]) and np.all(got_o[5] == 0)
     live = ~np.isneginf(ref_l)
     assert np.max(np.abs(got_o[live] - ref_o[live])) <= 1e-5 * np.max(np.abs(ref_o))
