@@ -13,7 +13,9 @@
 // is walked in tiles of 32 tokens:
 //   * the 32 latent rows go straight from global memory to LDS
 //     (global_load_lds_dwordx4) with a row stride of 74 x 16 bytes, so rows
-//     that are read together fall on different banks;
+//     that are read together fall on different banks (the two-buffer form
+//     below: 66 x 16-byte rows of the first 512 columns and a separate
+//     region for the 64 rotary columns);
 //   * S = Q K^T on MFMA 16x16x32 bf16, B operands read from LDS (18 k-steps
 //     of 32 per 16-token half);
 //   * online softmax per head on the MFMA result layout (each wave its own
@@ -204,10 +206,6 @@ __device__ __forceinline__ void pipe_barrier() {
   asm volatile("" ::: "memory");
 }
 
-// wave instructions of one tile's gather: slots 64s .. 64s+63 of the
-// kTileC chunks
-constexpr int kTileSlots = (kTileC + 63) / 64;  // 37
-
 // ---- transposed form, two tile buffers: attend_part_t
 // S^T = K Q^T (K rows from LDS as the A operand, the wave's 16 queries as
 // the B operand), so after the MFMA lane (kq, r) holds the scores of head r
@@ -281,53 +279,56 @@ __device__ __forceinline__ void sel_dma(const TLane& tl, const TList& ls, int t,
   __builtin_amdgcn_global_load_lds(ls.sel + e, (__attribute__((address_space(3))) void*)slot, 4, 0, 0);
 }
 
-// DMA of the latent rows of tile t into a buffer, tokens from its entries:
-// every lane first reads the token of each row it loads (all LDS reads
-// issued together), then issues its gathers. Slot s of wave w is s = w + 4j;
-// its chunk c = 64s + lane sits at (row, col) = (c / kRowL, c % kRowL), the
-// division by a multiply and shift (exact for every c used). Rows past the
-// tile's count repeat its last row and the pad chunks copy chunk 71 (both
-// are never read). The address is an unsigned 32 x 32 + 64 multiply-add
-// (tokens are clamped into [0, ctx) first). The lane index goes through an
-// opaque copy first, so that the compiler recomputes these offsets per tile
-// instead of keeping all of them live (and spilling) across the tile loop.
-constexpr int kSlotsPerWave = (kTileSlots + 3) / 4;  // 10 (wave w: slots w, w + 4, ...)
-constexpr uint32_t kRowDivM = (1u << 20) / kRowL + 1;
-constexpr bool row_div_exact() {
-  for (uint32_t c = 0; c < 4096; c++)
-    if (((c * kRowDivM) >> 20) != c / kRowL) return false;
-  return true;
-}
-static_assert(row_div_exact() && 64 * 4 * kSlotsPerWave <= 4096, "chunk index / kRowL by multiply and shift");
+// Tile layout of the two-buffer form: the first 512 columns (64 chunks, V
+// and the first 16 k-steps of K) of row j at j * kRowM chunks, then the
+// rotary tails (chunks 64 .. 71) of all 32 rows, 8 chunks per row, chunk c
+// of row j at position c ^ tail_swz(j). Bank model as above: 66 j mod 32 =
+// 2 j, so the K reads of rows r = 0..15 at chunks c and c + 1 fall on 32
+// distinct (chunk mod 32), and the transposed V reads of rows 4kq + r/4 on
+// 16 distinct multiples of 4 eight-byte units; in the tail region the
+// swizzle spreads the 4 rows that share (8 j mod 32) over 4 chunk pairs.
+// The buffer is exactly as large as 32 rows at kRowL chunks.
+constexpr int kMainC = 64;                     // chunks of columns 0 .. 511
+constexpr int kRowM = kMainC + 2;              // LDS chunks per row in the main region (1056 bytes)
+constexpr int kTailC = kRowC - kMainC;         // 8 chunks of columns 512 .. 575
+constexpr int kTailOff = kTT * kRowM * 16;     // byte offset of the tail region
+static_assert(kTailOff + kTT * kTailC * 16 <= kTileC * 16, "main rows and tails fit one tile buffer");
+__device__ __forceinline__ int tail_swz(int j) { return 2 * ((j >> 2) & 3); }
 
+// DMA of the latent rows of tile t into a buffer, tokens from its entries.
+// Wave w gathers rows 8w .. 8w+7: per row, the first 1024 bytes in one wave
+// instruction whose token is the same on every lane (lane l loads chunk l),
+// so the address is a scalar base plus the lane's offset; then the 8 rows'
+// tails in one more instruction (lane l: row 8w + l / 8, tail position
+// l % 8). Rows past the tile's count repeat its last row (they are never
+// weighted, but their values must be finite); tokens are clamped into
+// [0, ctx).
 __device__ __forceinline__ void rows_dma(const TLane& tl, const TList& ls, int t, const int* __restrict__ ent,
                                          unsigned char* __restrict__ buf, const uint16_t* kvbase,
                                          int64_t tok_stride) {
   const int n = ls.cnt(t);
   if (n == 0) return;
-  int lane;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(lane) : "v"(tl.lane));
-  const uint32_t c0 = uint32_t(64 * tl.wave + lane);
   const unsigned char* gb = reinterpret_cast<const unsigned char*>(kvbase);
-  const uint32_t row_bytes = uint32_t(tok_stride) * 2u;
-  const int hi = ls.ctx - 1;
-  uint32_t tok[kSlotsPerWave], cb[kSlotsPerWave];
+  const uint64_t row_bytes = uint64_t(tok_stride) * 2u;
+  // (the wave index through readfirstlane: the compiler then keeps the LDS
+  // destinations, which the instruction takes from a scalar register, in
+  // scalar arithmetic)
+  const int lane = tl.lane, r8 = 8 * __builtin_amdgcn_readfirstlane(tl.wave);
+  const int ra = r8 + (lane & 7) < n - 1 ? r8 + (lane & 7) : n - 1;  // rows of the row loads
+  const int rb = r8 + (lane >> 3) < n - 1 ? r8 + (lane >> 3) : n - 1;  // row of the lane's tail chunk
+  const int ta = ls.tok(ent, ra), tb = ls.tok(ent, rb);
+  const int cb = kMainC + ((lane & 7) ^ tail_swz(r8 + (lane >> 3)));
+  __builtin_amdgcn_global_load_lds(gb + (uint64_t(uint32_t(tb)) * row_bytes + 16u * uint32_t(cb)),
+                                   (__attribute__((address_space(3))) void*)(buf + kTailOff + 128 * r8), 16, 0, 0);
 #pragma unroll
-  for (int j = 0; j < kSlotsPerWave; j++) {
-    const uint32_t c = c0 + 256u * uint32_t(j);
-    const uint32_t row = (c * kRowDivM) >> 20;
-    const uint32_t col = c - uint32_t(kRowL) * row;
-    const int b = ent[int(row) < n - 1 ? int(row) : n - 1];
-    const int b0 = b > 0 ? b : 0;
-    tok[j] = uint32_t(b0 < hi ? b0 : hi);
-    cb[j] = 16u * (col < uint32_t(kRowC) ? col : uint32_t(kRowC - 1));
-  }
-#pragma unroll
-  for (int j = 0; j < kSlotsPerWave; j++) {
-    const int s = tl.wave + 4 * j;
-    if (64 * s + tl.lane < kTileC)
-      __builtin_amdgcn_global_load_lds(gb + (uint64_t(tok[j]) * row_bytes + cb[j]),
-                                       (__attribute__((address_space(3))) void*)(buf + 1024 * s), 16, 0, 0);
+  for (int k = 0; k < 8; k++) {
+    const uint32_t tk = uint32_t(__builtin_amdgcn_readlane(ta, k));
+    const uint64_t rp = reinterpret_cast<uint64_t>(gb) + uint64_t(tk) * row_bytes;
+    const uint64_t rs = uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(rp)))) |
+                        (uint64_t(uint32_t(__builtin_amdgcn_readfirstlane(uint32_t(rp >> 32)))) << 32);
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const unsigned char*>(rs) + 16u * uint32_t(lane),
+                                     (__attribute__((address_space(3))) void*)(buf + (r8 + k) * (kRowM * 16)), 16, 0,
+                                     0);
   }
 }
 
@@ -350,15 +351,25 @@ __device__ __attribute__((always_inline)) inline void tile_t(
   // compiler, short of registers, reads each operand just before its MFMA
   // and waits a full LDS latency at every k-step)
   f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  const unsigned char* krow0 = cur + (r * kRowL + kq) * 16;
-  const unsigned char* krow1 = cur + ((16 + r) * kRowL + kq) * 16;
+  // k-steps 0 .. 15 from the main rows, 16 and 17 from the tails (chunks
+  // kq and 4 + kq of rows r and 16 + r, which share tail_swz)
+  const unsigned char* krow0 = cur + (r * kRowM + kq) * 16;
+  const unsigned char* krow1 = cur + ((16 + r) * kRowM + kq) * 16;
+  const int tq = kq ^ tail_swz(r);
+  const unsigned char* ktail0 = cur + kTailOff + (r * kTailC) * 16;
+  const unsigned char* ktail1 = ktail0 + 16 * kTailC * 16;
   constexpr int kPD = 2;
   bf16x8 kb[2][kPD + 1];
 #pragma unroll
   for (int ks = 0; ks < kDK / 32 + kPD; ks++) {
-    if (ks < kDK / 32) {
+    if (ks < kMainC / 4) {
       kb[0][ks % (kPD + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow0 + 64 * ks));
       kb[1][ks % (kPD + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(krow1 + 64 * ks));
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    } else if (ks < kDK / 32) {
+      const int tc = 16 * (tq ^ (4 * (ks - kMainC / 4)));
+      kb[0][ks % (kPD + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(ktail0 + tc));
+      kb[1][ks % (kPD + 1)] = as_bf16x8(*reinterpret_cast<const u32x4*>(ktail1 + tc));
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     if (ks >= kPD) {
@@ -433,8 +444,8 @@ __device__ __attribute__((always_inline)) inline void tile_t(
   // 4kq + r/4 (first read) and 16 + 4kq + r/4 (second), dims 16nt + 4(r % 4)
   // .. +3; after the transpose it holds V[rows 4kq .. 4kq+3, then 16+4kq ..
   // 16+4kq+3][dim 16nt + r]
-  const unsigned char* va = cur + (4 * kq + (r >> 2)) * kRowL * 16 + 8 * (r & 3);
-  const unsigned char* vb = va + 16 * kRowL * 16;
+  const unsigned char* va = cur + (4 * kq + (r >> 2)) * kRowM * 16 + 8 * (r & 3);
+  const unsigned char* vb = va + 16 * kRowM * 16;
   // two n-tiles at a time; the next pair's reads are issued before this
   // pair's MFMAs, so they complete while those run
   constexpr int kNP = kDV / 32;  // pairs of n-tiles
