@@ -418,8 +418,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   // two fetch buffers with fixed roles (unrolled by two, no copies of
   // registers still being loaded); with T odd the last step computes the
   // tile past the span's keys, whose columns are all past nmax and ignored
+  // (in this order: the waits at the loop head count the loads issued
+  // after a tile's keys, on the way in as on the way round)
   KRaw ka = fetch(0);
+  __builtin_amdgcn_sched_barrier(0);
   KRaw kb = fetch(T > 1 ? 1 : 0);
+  __builtin_amdgcn_sched_barrier(0);
   for (int t = 0; t < T; t += 2) {
     float sc[4];
     compute(ka, sc);
